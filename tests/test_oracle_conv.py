@@ -1,0 +1,248 @@
+"""Pins of the edge-convolution oracle (forward, VJP, VJP-of-VJP)."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from cartesian_tensor_product_amd import inputs
+from oracle import conv, tensors as T
+from tests.test_oracle_tensors import rand_rotation, rotate_full
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def tiny(l=1, r_cut=6.0, seed=0, channels=8):
+    spec = conv.ConvSpec(l, l, l, r_cut)
+    d = inputs.edge_conv_inputs(seed, 32, 8, 6.0, channels, spec.n_in, spec.n_paths, spec.n_out)
+    f = {k: (v.astype(np.float64) if isinstance(v, np.ndarray) and v.dtype == np.float32 else v)
+         for k, v in d.items()}
+    return spec, f
+
+
+def stored_rotation(l, R):
+    """Matrix D(R) acting on stored components: select o R^(x)l o recon."""
+    return T.select_matrix(l) @ rotate_full(l, T.recon_matrix(l).T, R).T
+
+
+def rotate_rows(spec_rows_l, arr, R, contra=False):
+    out = arr.copy()
+    for rows, l in spec_rows_l:
+        D = stored_rotation(l, R)
+        if contra:
+            D = np.linalg.inv(D).T
+        out[:, rows, :] = np.einsum('ab,ubk->uak', D, arr[:, rows, :])
+    return out
+
+
+def in_rows(spec):
+    return [(np.arange(spec.in_off[l], spec.in_off[l + 1]), l) for l in range(spec.l_in + 1)]
+
+
+def out_rows(spec):
+    return [(spec.rows[p], p_[2]) for p, p_ in enumerate(spec.paths)]
+
+
+def call(spec, d, **kw):
+    return dict(spec=spec, pos=d["pos"], rowptr=d["rowptr"], sender=d["sender"], x=d["x"], W=d["W"], **kw)
+
+
+# ----------------------------------------------------------------- radial --
+
+def test_radial_closed_form():
+    rc = 5.0
+    r = np.array([rc / 2, rc / 4, rc, rc * 1.3])
+    R = conv.radial(r, 8, rc)
+    b = np.arange(1, 9)
+    # r = rc/2: sin(b pi/2)/(rc/2) * (1 + cos(pi/2))/2 = sin(b pi/2)/rc
+    assert np.allclose(R[0], np.sin(b * np.pi / 2) / rc)
+    # r = rc/4: sin(b pi/4)/(rc/4) * (1 + cos(pi/4))/2
+    assert np.allclose(R[1], np.sin(b * np.pi / 4) / (rc / 4) * (1 + np.sqrt(0.5)) / 2)
+    # zero at and beyond the cutoff
+    assert np.all(R[2:] == 0)
+    rr = np.linspace(0.3, 4.9, 17)
+    h = 1e-6
+    fd = (conv.radial(rr + h, 8, rc) - conv.radial(rr - h, 8, rc)) / (2 * h)
+    assert np.allclose(conv.radial_deriv(rr, 8, rc), fd, atol=1e-7)
+
+
+# ---------------------------------------------------------------- forward --
+
+@pytest.mark.parametrize("l", [1, 2])
+def test_explicit_full_tensor_mode_matches_probed(l):
+    spec, d = tiny(l, channels=4 if l == 2 else 8)
+    z1 = conv.edge_conv_fwd(spec, d["pos"], d["rowptr"], d["sender"], d["x"], d["W"])
+    z2 = conv.edge_conv_fwd(spec, d["pos"], d["rowptr"], d["sender"], d["x"], d["W"], mode="explicit")
+    assert np.abs(z1 - z2).max() < 1e-12 * np.abs(z1).max()
+
+
+def test_tiny_paths_and_layout():
+    spec, _ = tiny(1)
+    # natural parity only: (0,0)->0, (1,1)->0, (0,1)->1, (1,0)->1
+    assert spec.paths == [(0, 0, 0), (1, 1, 0), (0, 1, 1), (1, 0, 1)]
+    assert spec.n_out == 2 * 1 + 2 * 3
+
+
+def test_receiver_sum_brute_force():
+    # one receiver, summed edge by edge with the explicit coupling
+    spec, d = tiny(1)
+    z = conv.edge_conv_fwd(spec, d["pos"], d["rowptr"], d["sender"], d["x"], d["W"])
+    u = 5
+    acc = np.zeros((spec.n_out, d["x"].shape[-1]))
+    for e in range(d["rowptr"][u], d["rowptr"][u + 1]):
+        v = d["sender"][e]
+        r = d["pos"][v] - d["pos"][u]
+        rn = np.linalg.norm(r)
+        Rb = [np.sin(b * np.pi * rn / 6) / rn * 0.5 * (1 + np.cos(np.pi * rn / 6)) if rn < 6 else 0
+              for b in range(1, 9)]
+        for p, (l1, l2, L) in enumerate(spec.paths):
+            y = T.direction_tensor(l2, r / rn)
+            for k in range(acc.shape[1]):
+                w = sum(Rb[b] * d["W"][b, p, k] for b in range(8))
+                xs = d["x"][v, spec.in_off[l1]:spec.in_off[l1 + 1], k]
+                acc[spec.rows[p], k] += w * T.coupling(l1, l2, L, xs, y)
+    assert np.allclose(z[u], acc, atol=1e-12)
+
+
+@pytest.mark.parametrize("l", [1, 2, 3])
+def test_forward_equivariance(l):
+    spec, d = tiny(l, r_cut=12.0, channels=3)
+    rng = np.random.default_rng(7)
+    for reflect in (False, True):
+        R = rand_rotation(rng, reflect)
+        z = conv.edge_conv_fwd(spec, d["pos"], d["rowptr"], d["sender"], d["x"], d["W"])
+        xr = rotate_rows(in_rows(spec), d["x"], R)
+        zr = conv.edge_conv_fwd(spec, d["pos"] @ R.T, d["rowptr"], d["sender"], xr, d["W"])
+        assert np.abs(zr - rotate_rows(out_rows(spec), z, R)).max() < 1e-10 * np.abs(z).max()
+
+
+# -------------------------------------------------------------------- VJP --
+
+@pytest.mark.parametrize("l", [1, 2])
+def test_vjp_against_complex_step_and_fd(l):
+    spec, d = tiny(l, channels=3)
+    args = (spec, d["pos"], d["rowptr"], d["sender"])
+    g = d["g"]
+    xb, pb, Wb = conv.edge_conv_vjp(*args, d["x"], d["W"], g, want_W=True)
+    loss = lambda pos, x, W: np.sum(g * conv.edge_conv_fwd(spec, pos, d["rowptr"], d["sender"], x, W))
+    # every position coordinate by complex step
+    for i in range(d["pos"].shape[0]):
+        for j in range(3):
+            pc = d["pos"].astype(complex)
+            pc[i, j] += 1e-20j
+            assert abs(loss(pc, d["x"], d["W"]).imag / 1e-20 - pb[i, j]) < 1e-9 * max(1, abs(pb).max())
+    # sampled features and weights by central differences
+    rng = np.random.default_rng(3)
+    h = 1e-6
+    for _ in range(6):
+        idx = tuple(rng.integers(0, s) for s in d["x"].shape)
+        xp, xm = d["x"].copy(), d["x"].copy()
+        xp[idx] += h
+        xm[idx] -= h
+        fd = (loss(d["pos"], xp, d["W"]) - loss(d["pos"], xm, d["W"])) / (2 * h)
+        assert fd == pytest.approx(xb[idx], rel=1e-6, abs=1e-7)
+        idw = tuple(rng.integers(0, s) for s in d["W"].shape)
+        Wp, Wm = d["W"].copy(), d["W"].copy()
+        Wp[idw] += h
+        Wm[idw] -= h
+        fd = (loss(d["pos"], d["x"], Wp) - loss(d["pos"], d["x"], Wm)) / (2 * h)
+        assert fd == pytest.approx(Wb[idw], rel=1e-6, abs=1e-7)
+
+
+def test_vjp_translation_and_rotation():
+    spec, d = tiny(2, r_cut=12.0, channels=3)
+    g = d["g"]
+    xb, pb, _ = conv.edge_conv_vjp(spec, d["pos"], d["rowptr"], d["sender"], d["x"], d["W"], g)
+    assert np.abs(pb.sum(0)).max() < 1e-10 * np.abs(pb).max()
+    R = rand_rotation(np.random.default_rng(11), reflect=True)
+    xr = rotate_rows(in_rows(spec), d["x"], R)
+    gr = rotate_rows(out_rows(spec), g, R, contra=True)   # cotangents transform contragrediently
+    xbr, pbr, _ = conv.edge_conv_vjp(spec, d["pos"] @ R.T, d["rowptr"], d["sender"], xr, d["W"], gr)
+    assert np.abs(pbr - pb @ R.T).max() < 1e-10 * np.abs(pb).max()
+    assert np.abs(xbr - rotate_rows(in_rows(spec), xb, R, contra=True)).max() < 1e-10 * np.abs(xb).max()
+
+
+@pytest.mark.parametrize("path", [(1, 1, 2), (2, 1, 1), (2, 2, 2), (3, 2, 1), (2, 3, 3)])
+def test_bilinear_vjp_identities(path):
+    # <g, f(x,y)> = <x, VJP1(g,y)> = <y, VJP2(g,x)>  (Eq. C1, f bilinear)
+    K = T.coupling_tensor(*path)
+    rng = np.random.default_rng(5)
+    x, y, g = rng.standard_normal(K.shape[1]), rng.standard_normal(K.shape[2]), rng.standard_normal(K.shape[0])
+    f = np.einsum('abc,b,c->a', K, x, y)
+    v1 = np.einsum('abc,a,c->b', K, g, y)
+    v2 = np.einsum('abc,a,b->c', K, g, x)
+    assert g @ f == pytest.approx(x @ v1, rel=1e-12) and g @ f == pytest.approx(y @ v2, rel=1e-12)
+
+
+# ------------------------------------------------------------ VJP-of-VJP --
+
+@pytest.mark.parametrize("path", [(1, 1, 2), (2, 1, 1), (2, 2, 0), (1, 2, 3)])
+def test_eq_c2_identities(path):
+    """Eq. C2 for one weighted product c = w f(x, y), against complex step."""
+    K = T.coupling_tensor(*path)
+    rng = np.random.default_rng(9)
+    x, y, g = rng.standard_normal(K.shape[1]), rng.standard_normal(K.shape[2]), rng.standard_normal(K.shape[0])
+    w = rng.standard_normal()
+    vx, vy, vw = rng.standard_normal(K.shape[1]), rng.standard_normal(K.shape[2]), rng.standard_normal()
+    f = lambda a, b: np.einsum('abc,b,c->a', K, a, b)
+    vjp1 = lambda gg, b: np.einsum('abc,a,c->b', K, gg, b)
+    vjp2 = lambda gg, a: np.einsum('abc,a,b->c', K, gg, a)
+
+    def s(gg, xx, yy, ww):        # <v_x, x_bar> + <v_y, y_bar> + v_w w_bar  (Eq. C1)
+        return vx @ (ww * vjp1(gg, yy)) + vy @ (ww * vjp2(gg, xx)) + vw * (gg @ f(xx, yy))
+
+    def grad(which, n):
+        out = np.zeros(n)
+        for i in range(n):
+            a = [g.astype(complex), x.astype(complex), y.astype(complex), complex(w)]
+            if which == 3:
+                a[3] += 1e-20j
+            else:
+                a[which][i] += 1e-20j
+            out[i] = s(*a).imag / 1e-20
+        return out
+
+    g_hat = w * (f(vx, y) + f(x, vy)) + vw * f(x, y)
+    x_hat = vjp1(g, w * vy + vw * y)
+    y_hat = vjp2(g, w * vx + vw * x)
+    w_hat = g @ (f(vx, y) + f(x, vy))
+    assert np.allclose(grad(0, len(g)), g_hat, atol=1e-12)
+    assert np.allclose(grad(1, len(x)), x_hat, atol=1e-12)
+    assert np.allclose(grad(2, len(y)), y_hat, atol=1e-12)
+    assert np.allclose(grad(3, 1), w_hat, atol=1e-12)
+
+
+def test_vjp_vjp_against_fd_and_symmetry():
+    spec, d = tiny(2, channels=3)
+    rng = np.random.default_rng(21)
+    v_pos = rng.standard_normal(d["pos"].shape)
+    v_x = rng.standard_normal(d["x"].shape)
+    base = (spec, d["pos"], d["rowptr"], d["sender"], d["x"], d["W"], d["g"])
+    gh, xh, ph, Wh = conv.edge_conv_vjp_vjp(*base, v_x=v_x, v_pos=v_pos, want_W=True)
+    h = 1e-5
+    fp = conv.edge_conv_vjp(spec, d["pos"] + h * v_pos, d["rowptr"], d["sender"], d["x"] + h * v_x, d["W"], d["g"], want_W=True)
+    fm = conv.edge_conv_vjp(spec, d["pos"] - h * v_pos, d["rowptr"], d["sender"], d["x"] - h * v_x, d["W"], d["g"], want_W=True)
+    for got, a, b in zip((xh, ph, Wh), fp, fm):
+        fd = (a - b) / (2 * h)
+        assert np.abs(got - fd).max() < 1e-6 * max(1.0, np.abs(got).max())
+    zp = conv.edge_conv_fwd(spec, d["pos"] + h * v_pos, d["rowptr"], d["sender"], d["x"] + h * v_x, d["W"])
+    zm = conv.edge_conv_fwd(spec, d["pos"] - h * v_pos, d["rowptr"], d["sender"], d["x"] - h * v_x, d["W"])
+    assert np.abs(gh - (zp - zm) / (2 * h)).max() < 1e-6 * np.abs(gh).max()
+    # Hessian symmetry: <v2, H v1> = <v1, H v2>
+    v2p, v2x = rng.standard_normal(d["pos"].shape), rng.standard_normal(d["x"].shape)
+    _, xh2, ph2, _ = conv.edge_conv_vjp_vjp(*base, v_x=v2x, v_pos=v2p, outputs=("x", "pos"))
+    lhs = np.sum(v2p * ph) + np.sum(v2x * xh)
+    rhs = np.sum(v_pos * ph2) + np.sum(v_x * xh2)
+    assert lhs == pytest.approx(rhs, rel=1e-10)
+
+
+# ---------------------------------------------------------------- diamond --
+
+def test_diamond_neighbour_counts():
+    c = json.load(open(os.path.join(GOLDEN, "counts.json")))["diamond_neighbours"]
+    pos, box = inputs.diamond_positions(5, c["lattice_constant"])
+    rowptr, sender, shift = inputs.periodic_neighbours(pos, box, c["cutoff"])
+    assert np.all(np.diff(rowptr) == c["edges_per_atom"])
+    # the shell sum at the 5 A cutoff used by the diamond workload
+    rowptr5, _, _ = inputs.periodic_neighbours(pos, box, 5.0)
+    assert np.all(np.diff(rowptr5) == 86)

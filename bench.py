@@ -1,0 +1,168 @@
+"""Benchmark of the FlashCart edge convolution on one MI355X.
+
+One step = forward (Eq. 1) + VJP (feature and position gradients) of the
+edge convolution on the 1024-node microbenchmark: positions uniform in a
+20 A cube, 128 neighbours per node (E = 131072), 128 channels, ranks <= 2
+(11 paths), Bessel-8 radial weights with r_c = 5 A; synthetic, seeded inputs
+resident in HBM before timing starts.
+
+Prints one JSON line: edge-channels/s = E*C / (t_fwd + t_vjp), the roofline
+of the dominant kernel (algorithmic bytes per launch / its mean duration,
+HIP events on the launch stream), and the oracle timed on a bounded sample
+on the host CPU.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+N_NODES, K_NBR, BOX, CHANNELS, LMAX, R_CUT, SEED = 1024, 128, 20.0, 128, 2, 5.0, 1
+
+
+def algorithmic_bytes(N, E, C, n_in, n_out, P):
+    """Bytes each launch must move if every per-edge gather goes to memory.
+
+    forward: gather x[v] (n_in C floats) per edge, write z once per node,
+             sender id + sender position per edge, rowptr + receiver position
+             per node, radial weights once.
+    VJP:     gather g[u] (n_out C floats) per edge, read x[v] and write x_bar[v]
+             once per node, per edge the edge id, receiver id, receiver
+             position, and the edge position cotangent (written, then read by
+             the receiver pass), positions/row pointers and pos_bar per node,
+             radial weights once.
+    """
+    f = 4
+    fwd = E * C * n_in * f + N * n_out * C * f + E * (4 + 12) + N * (8 + 12) + 8 * P * C * f
+    vjp = (E * C * n_out * f + 2 * N * n_in * C * f + E * (4 + 4 + 12 + 12 + 12) + N * (8 + 8 + 12 + 12 + 12)
+           + 8 * P * C * f)
+    return fwd, vjp
+
+
+def cpu_baseline(d, spec, n_recv=384):
+    """Oracle (numpy fp64, one thread) on the edges into the first n_recv receivers."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import conv
+    f = lambda a: a.astype(np.float64)
+    edges = np.arange(int(d["rowptr"][n_recv]))
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        conv.edge_conv_fwd(spec, f(d["pos"]), d["rowptr"], d["sender"], f(d["x"]), f(d["W"]), edges=edges)
+        conv.edge_conv_vjp(spec, f(d["pos"]), d["rowptr"], d["sender"], f(d["x"]), f(d["W"]), f(d["g"]),
+                           edges=edges)
+        dt = time.perf_counter() - t0
+    units = len(edges) * d["x"].shape[-1]
+    return {"value": units / dt, "unit": "edge-channels/s", "cores": 1, "kind": "oracle",
+            "sample": f"fwd+VJP over the {len(edges)} edges into {n_recv} of {N_NODES} receivers "
+                      f"({units} edge-channels, {dt:.1f} s, numpy fp64 single thread)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from cartesian_tensor_product_amd import flashcart as fc
+    from cartesian_tensor_product_amd import inputs
+
+    dev = torch.device("cuda:0")
+    desc = fc.conv_desc(N_NODES, N_NODES * K_NBR, CHANNELS, LMAX, LMAX, LMAX, R_CUT)
+    P, n_in, n_out = fc.fc_conv_layout(desc)
+    d = inputs.edge_conv_inputs(SEED, N_NODES, K_NBR, BOX, CHANNELS, n_in, P, n_out)
+    E = len(d["sender"])
+    graph = fc.DeviceGraph(d["rowptr"], d["sender"], N_NODES, device=dev)
+    t = lambda a: torch.from_numpy(a).to(dev)
+    pos, x, W, g = t(d["pos"]), t(d["x"]), t(d["W"]), t(d["g"])
+    z = torch.empty((N_NODES, n_out, CHANNELS), device=dev)
+    xb = torch.empty_like(x)
+    pb = torch.empty((N_NODES, 3), device=dev)
+    ws = fc.workspace(fc.fc_edge_conv_workspace_bytes(desc, 1), dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fc.fc_edge_conv_fwd(desc, graph, pos, None, x, W, z, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        fc.fc_edge_conv_vjp(desc, graph, pos, None, x, W, g, xb, pb, None, ws, stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_fwd = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    t_vjp = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    ms_step = float(evs[0][0].elapsed_time(evs[-1][2]) / args.steps)
+
+    b_fwd, b_vjp = algorithmic_bytes(N_NODES, E, CHANNELS, n_in, n_out, P)
+    f_mean, v_mean = float(t_fwd.mean()), float(t_vjp.mean())
+    if v_mean >= f_mean:
+        dom, dom_ms, dom_bytes = "conv_vjp_sender_kernel (+ receiver pass)", v_mean, b_vjp
+    else:
+        dom, dom_ms, dom_bytes = "conv_fwd_kernel", f_mean, b_fwd
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    value = E * CHANNELS / (ms_step * 1e-3)
+
+    out = {
+        "metric": "edge-conv fwd+VJP edge-channels/s (1024n,128c,128nbr); % HBM roofline",
+        "value": value,
+        "unit": "edge-channels/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "edge conv fwd+VJP, 1024 nodes, 128 neighbours (E=131072), 128 channels, "
+                               "ranks<=2 (11 paths), Bessel-8 r_c=5 A, seed 1",
+                   "nodes": N_NODES, "neighbours": K_NBR, "channels": CHANNELS, "l_max": LMAX,
+                   "edges": E},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": dom_bytes},
+        "breakdown": {"fwd_ms": f_mean, "vjp_ms": v_mean, "fwd_GBs_alg": b_fwd / (f_mean * 1e-3) / 1e9,
+                      "vjp_GBs_alg": b_vjp / (v_mean * 1e-3) / 1e9,
+                      "fwd_plus_vjp_frac_hbm": (b_fwd + b_vjp) / ((f_mean + v_mean) * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                      "wall_s": wall},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import conv
+        spec = conv.ConvSpec(LMAX, LMAX, LMAX, R_CUT)
+        out["cpu_baseline"] = cpu_baseline(d, spec)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

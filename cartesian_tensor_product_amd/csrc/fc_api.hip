@@ -1,0 +1,266 @@
+// C ABI of the FlashCart gfx950 library: argument checks on the host, then
+// stream-ordered kernel launches.  See include/flashcart.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/flashcart.h"
+#include "fc_conv.h"
+#include "fc_graph.h"
+
+namespace {
+
+thread_local std::string g_msg;
+
+fc_status fail(fc_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_msg = buf;
+  return s;
+}
+
+fc_status ok() {
+  g_msg.clear();
+  return FC_OK;
+}
+
+fc_status check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(FC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool misaligned(const void* p, size_t a) { return p && (reinterpret_cast<uintptr_t>(p) % a) != 0; }
+
+int conv_paths_L(const fc_conv_desc* d, int L) {
+  int c = 0;
+  for (int l1 = 0; l1 <= d->l_in; ++l1)
+    for (int l2 = 0; l2 <= d->l_edge; ++l2)
+      if (fc::admissible(l1, l2, L)) ++c;
+  return c;
+}
+
+fc_status check_desc(const fc_conv_desc* d) {
+  if (!d) return fail(FC_ERR_INVALID_ARGUMENT, "descriptor is NULL");
+  if (d->n_nodes < 1) return fail(FC_ERR_INVALID_ARGUMENT, "n_nodes must be >= 1 (got %d)", d->n_nodes);
+  if (d->n_edges < 0) return fail(FC_ERR_INVALID_ARGUMENT, "n_edges must be >= 0 (got %d)", d->n_edges);
+  if (d->channels < 1) return fail(FC_ERR_INVALID_ARGUMENT, "channels must be >= 1 (got %d)", d->channels);
+  if (d->l_in < 0 || d->l_edge < 0 || d->l_out < 0)
+    return fail(FC_ERR_INVALID_ARGUMENT, "ranks must be >= 0");
+  if (d->l_in > 4 || d->l_edge > 4 || d->l_out > 4)
+    return fail(FC_ERR_UNSUPPORTED, "ranks above 4 are not supported (l_in=%d l_edge=%d l_out=%d)", d->l_in,
+                d->l_edge, d->l_out);
+  if (!(d->r_cut > 0.f) || !std::isfinite(d->r_cut))
+    return fail(FC_ERR_INVALID_ARGUMENT, "r_cut must be positive and finite");
+  if (d->n_basis != fc::kNB) return fail(FC_ERR_UNSUPPORTED, "n_basis must be 8 (got %d)", d->n_basis);
+  if (d->flags != 0) return fail(FC_ERR_UNSUPPORTED, "flags must be 0 (natural parity, paths separate)");
+  int P = 0;
+  for (int L = 0; L <= d->l_out; ++L) P += conv_paths_L(d, L);
+  if (P == 0) return fail(FC_ERR_INVALID_ARGUMENT, "no admissible path for these ranks");
+  if (d->channels > 256) return fail(FC_ERR_UNSUPPORTED, "channels above 256 are not supported");
+  if (!fc::conv_supported(d->l_in, d->l_edge, d->l_out))
+    return fail(FC_ERR_UNSUPPORTED, "(l_in, l_edge, l_out) = (%d, %d, %d) is not instantiated in this build",
+                d->l_in, d->l_edge, d->l_out);
+  return FC_OK;
+}
+
+void layout(const fc_conv_desc* d, int* P, int* nin, int* nout) {
+  int p = 0, o = 0;
+  for (int L = 0; L <= d->l_out; ++L) {
+    const int c = conv_paths_L(d, L);
+    p += c;
+    o += (2 * L + 1) * c;
+  }
+  *P = p;
+  *nin = (d->l_in + 1) * (d->l_in + 1);
+  *nout = o;
+}
+
+fc::ConvArgs make_args(const fc_conv_desc* d, const fc_graph* g, const float* pos, const float* shift,
+                       const float* x, const float* W) {
+  fc::ConvArgs a{};
+  a.N = d->n_nodes;
+  a.E = d->n_edges;
+  a.C = d->channels;
+  a.rc = d->r_cut;
+  a.rowptr = g->rowptr;
+  a.sender = g->sender;
+  a.receiver = g->receiver;
+  a.t_rowptr = g->t_rowptr;
+  a.t_edge = g->t_edge;
+  a.pos = pos;
+  a.shift = shift;
+  a.x = x;
+  a.W = W;
+  return a;
+}
+
+size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+}  // namespace
+
+extern "C" {
+
+const char* fc_status_string(fc_status s) {
+  switch (s) {
+    case FC_OK: return "FC_OK";
+    case FC_ERR_INVALID_ARGUMENT: return "FC_ERR_INVALID_ARGUMENT";
+    case FC_ERR_UNSUPPORTED: return "FC_ERR_UNSUPPORTED";
+    case FC_ERR_WORKSPACE: return "FC_ERR_WORKSPACE";
+    case FC_ERR_HIP: return "FC_ERR_HIP";
+  }
+  return "FC_UNKNOWN_STATUS";
+}
+
+const char* fc_last_error_message(void) { return g_msg.c_str(); }
+
+int32_t fc_abi_version(void) { return FC_ABI_VERSION; }
+
+fc_status fc_conv_layout(const fc_conv_desc* d, int32_t* n_paths, int32_t* in_rows, int32_t* out_rows) {
+  if (fc_status s = check_desc(d)) return s;
+  int P, nin, nout;
+  layout(d, &P, &nin, &nout);
+  if (n_paths) *n_paths = P;
+  if (in_rows) *in_rows = nin;
+  if (out_rows) *out_rows = nout;
+  return ok();
+}
+
+fc_status fc_conv_path(const fc_conv_desc* d, int32_t i, int32_t* l1, int32_t* l2, int32_t* L) {
+  if (fc_status s = check_desc(d)) return s;
+  int idx = 0;
+  for (int LL = 0; LL <= d->l_out; ++LL)
+    for (int a = 0; a <= d->l_in; ++a)
+      for (int b = 0; b <= d->l_edge; ++b)
+        if (fc::admissible(a, b, LL)) {
+          if (idx == i) {
+            if (l1) *l1 = a;
+            if (l2) *l2 = b;
+            if (L) *L = LL;
+            return ok();
+          }
+          ++idx;
+        }
+  return fail(FC_ERR_INVALID_ARGUMENT, "path index %d out of range [0, %d)", i, idx);
+}
+
+size_t fc_graph_transpose_workspace_bytes(int32_t n_nodes) {
+  return n_nodes > 0 ? fc::graph_transpose_ws(n_nodes) : 0;
+}
+
+fc_status fc_graph_transpose(int32_t n_nodes, int32_t n_edges, const int32_t* rowptr, const int32_t* sender,
+                             int32_t* receiver, int32_t* t_rowptr, int32_t* t_edge, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  if (n_nodes < 1 || n_edges < 0) return fail(FC_ERR_INVALID_ARGUMENT, "need n_nodes >= 1, n_edges >= 0");
+  if (!rowptr || !t_rowptr || (n_edges > 0 && (!sender || !receiver || !t_edge)))
+    return fail(FC_ERR_INVALID_ARGUMENT, "graph transpose: NULL array");
+  if (!workspace || workspace_bytes < fc::graph_transpose_ws(n_nodes))
+    return fail(FC_ERR_WORKSPACE, "graph transpose needs %zu workspace bytes", fc::graph_transpose_ws(n_nodes));
+  fc::graph_transpose(n_nodes, n_edges, rowptr, sender, receiver, t_rowptr, t_edge, workspace, stream);
+  return check_launch("graph transpose");
+}
+
+fc_status fc_graph_validate(int32_t n_nodes, int32_t n_edges, const int32_t* h_rowptr, const int32_t* h_sender) {
+  if (n_nodes < 1 || n_edges < 0) return fail(FC_ERR_INVALID_ARGUMENT, "need n_nodes >= 1, n_edges >= 0");
+  if (!h_rowptr || (n_edges > 0 && !h_sender)) return fail(FC_ERR_INVALID_ARGUMENT, "NULL array");
+  if (h_rowptr[0] != 0) return fail(FC_ERR_INVALID_ARGUMENT, "rowptr[0] = %d, expected 0", h_rowptr[0]);
+  for (int u = 0; u < n_nodes; ++u)
+    if (h_rowptr[u + 1] < h_rowptr[u])
+      return fail(FC_ERR_INVALID_ARGUMENT, "rowptr decreases at node %d", u);
+  if (h_rowptr[n_nodes] != n_edges)
+    return fail(FC_ERR_INVALID_ARGUMENT, "rowptr[N] = %d, expected E = %d", h_rowptr[n_nodes], n_edges);
+  for (int e = 0; e < n_edges; ++e)
+    if (h_sender[e] < 0 || h_sender[e] >= n_nodes)
+      return fail(FC_ERR_INVALID_ARGUMENT, "sender[%d] = %d out of range", e, h_sender[e]);
+  return ok();
+}
+
+size_t fc_edge_conv_workspace_bytes(const fc_conv_desc* d, int32_t op) {
+  if (check_desc(d) != FC_OK) return 0;
+  if (op == 1) return round256((size_t)3 * d->n_edges * sizeof(float));
+  return 0;
+}
+
+fc_status fc_edge_conv_fwd(const fc_conv_desc* d, const fc_graph* g, const float* pos, const float* shift,
+                           const float* x, const float* radial_w, float* z, hipStream_t stream) {
+  if (fc_status s = check_desc(d)) return s;
+  if (!g || !g->rowptr || (d->n_edges > 0 && !g->sender))
+    return fail(FC_ERR_INVALID_ARGUMENT, "forward needs graph rowptr and sender");
+  if (!pos || !x || !radial_w || !z) return fail(FC_ERR_INVALID_ARGUMENT, "forward: NULL pos, x, radial_w or z");
+  if (misaligned(pos, 4) || misaligned(x, 4) || misaligned(radial_w, 4) || misaligned(z, 4) ||
+      misaligned(shift, 4))
+    return fail(FC_ERR_INVALID_ARGUMENT, "forward: arrays must be 4-byte aligned");
+  fc::ConvArgs a = make_args(d, g, pos, shift, x, radial_w);
+  a.z = z;
+  fc::conv_dispatch(0, d->l_in, d->l_edge, d->l_out, a, stream);
+  return check_launch("edge conv forward");
+}
+
+fc_status fc_edge_conv_vjp(const fc_conv_desc* d, const fc_graph* g, const float* pos, const float* shift,
+                           const float* x, const float* radial_w, const float* g_z, float* x_grad,
+                           float* pos_grad, float* radial_w_grad, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  if (fc_status s = check_desc(d)) return s;
+  if (!g || !g->rowptr || !g->t_rowptr || (d->n_edges > 0 && (!g->sender || !g->receiver || !g->t_edge)))
+    return fail(FC_ERR_INVALID_ARGUMENT, "VJP needs the full graph (run fc_graph_transpose first)");
+  if (!pos || !x || !radial_w || !g_z) return fail(FC_ERR_INVALID_ARGUMENT, "VJP: NULL pos, x, radial_w or g_z");
+  if (!x_grad && !pos_grad && !radial_w_grad) return fail(FC_ERR_INVALID_ARGUMENT, "VJP: no output requested");
+  if (radial_w_grad) return fail(FC_ERR_UNSUPPORTED, "VJP: radial_w_grad is not implemented in this build");
+  if (misaligned(pos, 4) || misaligned(x, 4) || misaligned(radial_w, 4) || misaligned(g_z, 4) ||
+      misaligned(x_grad, 4) || misaligned(pos_grad, 4) || misaligned(shift, 4))
+    return fail(FC_ERR_INVALID_ARGUMENT, "VJP: arrays must be 4-byte aligned");
+  const size_t need = fc_edge_conv_workspace_bytes(d, 1);
+  if (pos_grad && (!workspace || workspace_bytes < need))
+    return fail(FC_ERR_WORKSPACE, "VJP needs %zu workspace bytes", need);
+  fc::ConvArgs a = make_args(d, g, pos, shift, x, radial_w);
+  a.g = g_z;
+  a.x_bar = x_grad;
+  a.pos_bar = pos_grad;
+  a.rbar = static_cast<float*>(workspace);
+  fc::conv_dispatch(1, d->l_in, d->l_edge, d->l_out, a, stream);
+  return check_launch("edge conv VJP");
+}
+
+fc_status fc_edge_conv_vjp_vjp(const fc_conv_desc* d, const fc_graph* g, const float* pos, const float* shift,
+                               const float* x, const float* radial_w, const float* g_z, const float* v_x,
+                               const float* v_pos, float* g_hat, float* x_hat, float* pos_hat,
+                               float* radial_w_hat, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  if (fc_status s = check_desc(d)) return s;
+  (void)g; (void)pos; (void)shift; (void)x; (void)radial_w; (void)g_z; (void)v_x; (void)v_pos;
+  (void)g_hat; (void)x_hat; (void)pos_hat; (void)radial_w_hat; (void)workspace; (void)workspace_bytes;
+  (void)stream;
+  return fail(FC_ERR_UNSUPPORTED, "VJP-of-VJP is not implemented in this build");
+}
+
+fc_status fc_ladder_layout(const fc_ladder_desc* d, size_t* n_weight_floats, size_t* n_saved_floats) {
+  (void)d; (void)n_weight_floats; (void)n_saved_floats;
+  return fail(FC_ERR_UNSUPPORTED, "ladder is not implemented in this build");
+}
+
+size_t fc_ladder_workspace_bytes(const fc_ladder_desc* d, int32_t op) {
+  (void)d; (void)op;
+  return 0;
+}
+
+fc_status fc_node_ladder_fwd(const fc_ladder_desc* d, const float* A, const float* weights, float* z,
+                             float* saved, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  (void)d; (void)A; (void)weights; (void)z; (void)saved; (void)workspace; (void)workspace_bytes; (void)stream;
+  return fail(FC_ERR_UNSUPPORTED, "ladder is not implemented in this build");
+}
+
+fc_status fc_node_ladder_vjp(const fc_ladder_desc* d, const float* A, const float* weights, const float* saved,
+                             const float* g_z, float* A_grad, float* weights_grad, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  (void)d; (void)A; (void)weights; (void)saved; (void)g_z; (void)A_grad; (void)weights_grad; (void)workspace;
+  (void)workspace_bytes; (void)stream;
+  return fail(FC_ERR_UNSUPPORTED, "ladder is not implemented in this build");
+}
+
+}  // extern "C"

@@ -1,0 +1,213 @@
+// Shared device helpers for the FlashCart gfx950 kernels.
+//
+// * compile-time path configuration of a convolution (path list, output rows);
+// * direction tensors T_l(n) and their n-gradients from the generated
+//   monomial tables (FlashCart paper, App. B direction-tensor formula);
+// * the Bessel radial basis with cosine cutoff and its r-derivatives;
+// * static_for, so that every register-array index is a compile-time constant.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <array>
+#include <cstdint>
+#include <type_traits>
+#include <utility>
+
+#include "generated/fc_tables.h"
+
+namespace fc {
+
+inline constexpr int kWave = 64;
+inline constexpr int kNB = 8;          // radial basis functions
+inline constexpr float kPi = 3.14159265358979323846f;
+
+// ---------------------------------------------------------------- static_for
+template <class F, int... Is>
+__host__ __device__ __forceinline__ constexpr void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, class F>
+__host__ __device__ __forceinline__ constexpr void static_for(F&& f) {
+  if constexpr (N > 0) static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// ------------------------------------------------------------ rank bookkeeping
+__host__ __device__ constexpr int ncomp(int l) { return 2 * l + 1; }
+__host__ __device__ constexpr int nrank(int l) { return (l + 1) * (l + 1); }   // sum_{l'<=l} (2l'+1)
+__host__ __device__ constexpr int rank_off(int l) { return l * l; }         // sum_{l'<l} (2l'+1)
+__host__ __device__ constexpr bool admissible(int l1, int l2, int L) {
+  int d = l1 > l2 ? l1 - l2 : l2 - l1;
+  return d <= L && L <= l1 + l2 && ((l1 + l2 + L) % 2 == 0);
+}
+__host__ __device__ constexpr int path_type(int l1, int l2, int L) {
+  for (int t = 0; t < tab::kNumPathTypes; ++t)
+    if (tab::kPathL1[t] == l1 && tab::kPathL2[t] == l2 && tab::kPathL[t] == L) return t;
+  return -1;
+}
+
+struct PathInfo {
+  int type, l1, l2, L;
+  int eta;   // position among the paths with the same L
+  int PL;    // number of paths with this L
+  int off;   // first row of the L block
+};
+
+// Paths (l1 <= LIN, l2 <= LEDGE, L <= LOUT), ordered by L then (l1, l2).
+template <int LIN, int LEDGE, int LOUT>
+struct ConvCfg {
+  static constexpr int NIN = nrank(LIN);
+  static constexpr int NE = nrank(LEDGE);
+
+  static constexpr int count_L(int L) {
+    int c = 0;
+    for (int l1 = 0; l1 <= LIN; ++l1)
+      for (int l2 = 0; l2 <= LEDGE; ++l2)
+        if (admissible(l1, l2, L)) ++c;
+    return c;
+  }
+  static constexpr int count_all() {
+    int c = 0;
+    for (int L = 0; L <= LOUT; ++L) c += count_L(L);
+    return c;
+  }
+  static constexpr int P = count_all();
+  static constexpr int off_L(int L) {
+    int o = 0;
+    for (int l = 0; l < L; ++l) o += ncomp(l) * count_L(l);
+    return o;
+  }
+  static constexpr int NOUT = off_L(LOUT + 1);
+
+  static constexpr std::array<PathInfo, (P > 0 ? P : 1)> build() {
+    std::array<PathInfo, (P > 0 ? P : 1)> a{};
+    int i = 0;
+    for (int L = 0; L <= LOUT; ++L) {
+      int eta = 0;
+      for (int l1 = 0; l1 <= LIN; ++l1)
+        for (int l2 = 0; l2 <= LEDGE; ++l2)
+          if (admissible(l1, l2, L)) {
+            a[i] = PathInfo{path_type(l1, l2, L), l1, l2, L, eta, count_L(L), off_L(L)};
+            ++eta;
+            ++i;
+          }
+    }
+    return a;
+  }
+  static constexpr std::array<PathInfo, (P > 0 ? P : 1)> paths = build();
+
+  static constexpr int row(int p, int c) { return paths[p].off + c * paths[p].PL + paths[p].eta; }
+  static constexpr int first_path_of(int L) {
+    int i = 0;
+    for (int l = 0; l < L; ++l) i += count_L(l);
+    return i;
+  }
+};
+
+// Paths of a rank group [LLO, LHI] of a configuration.
+template <class Cfg, int LLO, int LHI>
+struct Group {
+  static constexpr int p0 = Cfg::first_path_of(LLO);
+  static constexpr int p1 = Cfg::first_path_of(LHI + 1);
+  static constexpr int NP = p1 - p0;
+  static constexpr int r0 = Cfg::off_L(LLO);
+  static constexpr int r1 = Cfg::off_L(LHI + 1);
+  static constexpr int NR = r1 - r0;
+};
+
+// ----------------------------------------------------------- direction tensors
+// y[g], g = l^2 + c, for all ranks l <= LE; n is a unit vector.
+template <int LE>
+__device__ __forceinline__ void direction_tensors(float nx, float ny, float nz, float* y) {
+  float px[LE + 1], py[LE + 1], pz[LE + 1];
+  px[0] = py[0] = pz[0] = 1.f;
+  static_for<LE>([&](auto i) {
+    px[i + 1] = px[i] * nx;
+    py[i + 1] = py[i] * ny;
+    pz[i + 1] = pz[i] * nz;
+  });
+  static_for<nrank(LE)>([&](auto gi) {
+    constexpr int g = gi;
+    constexpr int mb = tab::kMonoBegin[g], me = tab::kMonoBegin[g + 1];
+    float v = 0.f;
+    static_for<me - mb>([&](auto mi) {
+      constexpr tab::Mono m = tab::kMono[mb + mi];
+      v = fmaf(m.c, px[m.ex] * py[m.ey] * pz[m.ez], v);
+    });
+    y[g] = v;
+  });
+}
+
+// d y[g] / d n_j as polynomials (n treated as free variables).
+template <int LE>
+__device__ __forceinline__ void direction_tensor_grads(float nx, float ny, float nz, float* dy /*[NE][3]*/) {
+  float px[LE + 1], py[LE + 1], pz[LE + 1];
+  px[0] = py[0] = pz[0] = 1.f;
+  static_for<LE>([&](auto i) {
+    px[i + 1] = px[i] * nx;
+    py[i + 1] = py[i] * ny;
+    pz[i + 1] = pz[i] * nz;
+  });
+  static_for<nrank(LE)>([&](auto gi) {
+    constexpr int g = gi;
+    constexpr int mb = tab::kMonoBegin[g], me = tab::kMonoBegin[g + 1];
+    float gx = 0.f, gy = 0.f, gz = 0.f;
+    static_for<me - mb>([&](auto mi) {
+      constexpr tab::Mono m = tab::kMono[mb + mi];
+      if constexpr (m.ex > 0) gx = fmaf(m.c * float(m.ex), px[m.ex - 1] * py[m.ey] * pz[m.ez], gx);
+      if constexpr (m.ey > 0) gy = fmaf(m.c * float(m.ey), px[m.ex] * py[m.ey - 1] * pz[m.ez], gy);
+      if constexpr (m.ez > 0) gz = fmaf(m.c * float(m.ez), px[m.ex] * py[m.ey] * pz[m.ez - 1], gz);
+    });
+    dy[3 * g + 0] = gx;
+    dy[3 * g + 1] = gy;
+    dy[3 * g + 2] = gz;
+  });
+}
+
+// ------------------------------------------------------------------- radial
+// R_b(r) = sin(b pi r/rc)/r * (1 + cos(pi r/rc))/2, b = 1..8, 0 for r >= rc
+// (and for r == 0, where no direction exists).  sin(b t) and cos(b t) follow
+// from sin t, cos t by the angle-addition recurrences.
+struct Radial {
+  float R[kNB];
+  float dR[kNB];   // dR_b/dr (only when requested)
+};
+
+template <bool DERIV>
+__device__ __forceinline__ void radial(float r, float rc, float* R, float* dR) {
+  if (!(r < rc) || !(r > 0.f)) {
+#pragma unroll
+    for (int b = 0; b < kNB; ++b) {
+      R[b] = 0.f;
+      if constexpr (DERIV) dR[b] = 0.f;
+    }
+    return;
+  }
+  const float th = kPi * r / rc;
+  float s1, c1;
+  sincosf(th, &s1, &c1);
+  const float inv_r = 1.f / r;
+  const float env = 0.5f * (1.f + c1);
+  const float denv = -0.5f * s1 * (kPi / rc);
+  float sp = 0.f, s = s1;      // sin((b-1)t), sin(b t)
+  float cp = 1.f, c = c1;      // cos((b-1)t), cos(b t)
+#pragma unroll
+  for (int b = 0; b < kNB; ++b) {
+    R[b] = s * inv_r * env;
+    if constexpr (DERIV) {
+      const float kb = float(b + 1) * (kPi / rc);
+      dR[b] = (kb * c * inv_r - s * inv_r * inv_r) * env + s * inv_r * denv;
+    }
+    const float sn = 2.f * c1 * s - sp;
+    const float cn = 2.f * c1 * c - cp;
+    sp = s;
+    s = sn;
+    cp = c;
+    c = cn;
+  }
+}
+
+// ------------------------------------------------------------- misc device
+__device__ __forceinline__ int uniform_int(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+}  // namespace fc

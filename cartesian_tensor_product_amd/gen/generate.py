@@ -1,0 +1,373 @@
+"""Coupling-table generator for the HIP kernels.
+
+Expands every natural-parity Cartesian coupling path (l1, l2) -> L with
+l1, l2, L <= MAX_RANK into an exact bilinear polynomial over the 2l+1 stored
+components of each operand, and every direction tensor T_l(n) into a
+polynomial in (n_x, n_y, n_z), using exact rational arithmetic (stdlib
+``fractions``).  The result is emitted as constexpr C++ tables in
+``csrc/generated/fc_tables.h``, which the hand-written kernels iterate over
+with fully unrolled loops.
+
+Mathematics (FlashCart paper, arXiv 2610.06409):
+
+* stored components: the 2l+1 entries with at most one z index, labelled by
+  their index counts (p_x, p_y, p_z); every other entry follows from the
+  trace relation (x)_{px,py,pz} = -(x)_{px+2,py,pz-2} - (x)_{px,py+2,pz-2}
+  (§3 "Symbolic construction").
+* coupling: App. B Eq. B1 evaluated literally, i.e.
+      sum_{m=0}^{min(l1,l2)-n} (-2)^m (2L-2m-1)!!/(2L-1)!!
+          {(x .(n+m). y) (x) I^m},
+  the braces summing over distinct placements of the free indices (those
+  left from x, those left from y, and the m identity factors), times a path
+  constant.
+* path constant: the pages leave C_{l1 l2 L} to another reference.  It is
+  fixed here by requiring (T_l1(n) (x) T_l2(n))_L = T_L(n); at n = e_x the
+  x...x entry of T_L(e_x) is T_L : e_x^L = 1, which fixes the constant exactly.
+* direction tensors: App. B, T_l = (2l-1)!!/l! sum_m (-1)^m
+  (2l-2m-1)!!/(2l-1)!! {n^(l-2m) (x) I^m}.
+
+Run as a script to (re)write the header; ``build()`` in the package does so.
+"""
+
+from __future__ import annotations
+
+import itertools
+import math
+import os
+import sys
+from fractions import Fraction
+
+MAX_RANK = 4
+
+
+# ----------------------------------------------------------------------------
+# index bookkeeping
+# ----------------------------------------------------------------------------
+
+def dfact(n: int) -> int:
+    out = 1
+    while n > 1:
+        out *= n
+        n -= 2
+    return out
+
+
+def stored(l: int):
+    """(p_x, p_y, p_z) of the stored components, in storage order."""
+    return ([(px, l - px, 0) for px in range(l, -1, -1)]
+            + [(px, l - 1 - px, 1) for px in range(l - 1, -1, -1)])
+
+
+def rep_index(p):
+    return (0,) * p[0] + (1,) * p[1] + (2,) * p[2]
+
+
+def index_counts(idx):
+    c = [0, 0, 0]
+    for i in idx:
+        c[i] += 1
+    return tuple(c)
+
+
+def entry_in_stored(l: int):
+    """Map counts (p_x,p_y,p_z) -> {stored comp: Fraction} via the trace relation."""
+    pos = {p: i for i, p in enumerate(stored(l))}
+    memo = {}
+
+    def rec(p):
+        if p in memo:
+            return memo[p]
+        if p[2] <= 1:
+            out = {pos[p]: Fraction(1)}
+        else:
+            out = {}
+            for q in ((p[0] + 2, p[1], p[2] - 2), (p[0], p[1] + 2, p[2] - 2)):
+                for k, v in rec(q).items():
+                    out[k] = out.get(k, Fraction(0)) - v
+            out = {k: v for k, v in out.items() if v != 0}
+        memo[p] = out
+        return out
+
+    return rec
+
+
+def full_tensor(l: int, vec):
+    """Dict index tuple -> Fraction of the STF tensor with stored comps ``vec``."""
+    rec = entry_in_stored(l)
+    out = {}
+    for idx in itertools.product(range(3), repeat=l):
+        val = Fraction(0)
+        for k, c in rec(index_counts(idx)).items():
+            val += c * vec[k]
+        out[idx] = val
+    return out
+
+
+def matchings(slots):
+    if not slots:
+        yield ()
+        return
+    first, others = slots[0], slots[1:]
+    for i, partner in enumerate(others):
+        for rest in matchings(others[:i] + others[i + 1:]):
+            yield ((first, partner),) + rest
+
+
+# ----------------------------------------------------------------------------
+# Eq. B1
+# ----------------------------------------------------------------------------
+
+def admissible(l1, l2, L):
+    return abs(l1 - l2) <= L <= l1 + l2 and (l1 + l2 + L) % 2 == 0
+
+
+def b1_entry(l1, l2, L, X, Y, out_idx):
+    """Entry ``out_idx`` of Eq. B1 without its path constant."""
+    n = (l1 + l2 - L) // 2
+    total = Fraction(0)
+    for m in range(0, min(l1, l2) - n + 1):
+        k = n + m
+        fx, fy = l1 - k, l2 - k                # free indices left on x and y
+        coef = Fraction((-2) ** m * dfact(2 * L - 2 * m - 1), dfact(2 * L - 1))
+        acc = Fraction(0)
+        slots = tuple(range(L))
+        for sx in itertools.combinations(slots, fx):
+            rest = tuple(s for s in slots if s not in sx)
+            for sy in itertools.combinations(rest, fy):
+                pair_slots = tuple(s for s in rest if s not in sy)
+                for pairs in matchings(pair_slots):
+                    if any(out_idx[a] != out_idx[b] for a, b in pairs):
+                        continue
+                    xi = tuple(out_idx[s] for s in sx)
+                    yi = tuple(out_idx[s] for s in sy)
+                    q = Fraction(0)
+                    for c in itertools.product(range(3), repeat=k):
+                        q += X[xi + c] * Y[c + yi]
+                    acc += q
+        total += coef * acc
+    return total
+
+
+# ----------------------------------------------------------------------------
+# direction tensors as polynomials in n
+# ----------------------------------------------------------------------------
+
+def direction_poly(l: int, p):
+    """T_l(n) stored comp with counts p as {(ex,ey,ez): Fraction}."""
+    idx = rep_index(p)
+    out = {}
+    pref = Fraction(dfact(2 * l - 1), math.factorial(l))
+    for m in range(l // 2 + 1):
+        coef = pref * Fraction((-1) ** m * dfact(2 * l - 2 * m - 1), dfact(2 * l - 1))
+        for chosen in itertools.combinations(range(l), 2 * m):
+            rest = [s for s in range(l) if s not in chosen]
+            for pairs in matchings(chosen):
+                if any(idx[a] != idx[b] for a, b in pairs):
+                    continue
+                e = [0, 0, 0]
+                for s in rest:
+                    e[idx[s]] += 1
+                key = tuple(e)
+                out[key] = out.get(key, Fraction(0)) + coef
+    return {k: v for k, v in out.items() if v != 0}
+
+
+def direction_full_at_ex(l: int):
+    """T_l(e_x) as a full tensor of Fractions (n = (1, 0, 0))."""
+    out = {}
+    for idx in itertools.product(range(3), repeat=l):
+        poly = direction_poly_idx(l, idx)
+        out[idx] = sum((c for (ex, ey, ez), c in poly.items() if ey == 0 and ez == 0),
+                       Fraction(0))
+    return out
+
+
+def direction_poly_idx(l, idx):
+    out = {}
+    pref = Fraction(dfact(2 * l - 1), math.factorial(l))
+    for m in range(l // 2 + 1):
+        coef = pref * Fraction((-1) ** m * dfact(2 * l - 2 * m - 1), dfact(2 * l - 1))
+        for chosen in itertools.combinations(range(l), 2 * m):
+            rest = [s for s in range(l) if s not in chosen]
+            for pairs in matchings(chosen):
+                if any(idx[a] != idx[b] for a, b in pairs):
+                    continue
+                e = [0, 0, 0]
+                for s in rest:
+                    e[idx[s]] += 1
+                out[tuple(e)] = out.get(tuple(e), Fraction(0)) + coef
+    return out
+
+
+# ----------------------------------------------------------------------------
+# tables
+# ----------------------------------------------------------------------------
+
+def path_constant(l1, l2, L):
+    X, Y = direction_full_at_ex(l1), direction_full_at_ex(l2)
+    v = b1_entry(l1, l2, L, X, Y, (0,) * L)
+    assert v != 0
+    return 1 / v
+
+
+def coupling_terms(l1, l2, L):
+    """[(a, b1, b2, Fraction)] with f_a(x, y) = sum c x_b1 y_b2."""
+    c = path_constant(l1, l2, L)
+    n1, n2 = 2 * l1 + 1, 2 * l2 + 1
+    basis = lambda n, i: [Fraction(int(j == i)) for j in range(n)]
+    fullx = [full_tensor(l1, basis(n1, i)) for i in range(n1)]
+    fully = [full_tensor(l2, basis(n2, i)) for i in range(n2)]
+    terms = []
+    for a, p in enumerate(stored(L)):
+        oi = rep_index(p)
+        for b1 in range(n1):
+            for b2 in range(n2):
+                v = c * b1_entry(l1, l2, L, fullx[b1], fully[b2], oi)
+                if v != 0:
+                    terms.append((a, b1, b2, v))
+    return terms
+
+
+def all_paths(max_rank=MAX_RANK):
+    return [(l1, l2, L) for l1 in range(max_rank + 1) for l2 in range(max_rank + 1)
+            for L in range(max_rank + 1) if admissible(l1, l2, L)]
+
+
+def build_tables(max_rank=MAX_RANK):
+    paths = all_paths(max_rank)
+    cache = {}
+    tables = {}
+    for (l1, l2, L) in paths:
+        if (l2, l1, L) in cache:           # exchange symmetry: swap operands
+            tables[(l1, l2, L)] = [(a, b2, b1, c) for (a, b1, b2, c) in cache[(l2, l1, L)]]
+        else:
+            cache[(l1, l2, L)] = coupling_terms(l1, l2, L)
+            tables[(l1, l2, L)] = cache[(l1, l2, L)]
+    tpoly = {l: [direction_poly(l, p) for p in stored(l)] for l in range(max_rank + 1)}
+    return paths, tables, tpoly
+
+
+# ----------------------------------------------------------------------------
+# emission
+# ----------------------------------------------------------------------------
+
+def cfloat(fr: Fraction) -> str:
+    if fr.denominator == 1:
+        return f"{fr.numerator}.0f"
+    return f"float({fr.numerator}.0 / {fr.denominator}.0)"
+
+
+def emit(path: str, max_rank=MAX_RANK) -> None:
+    paths, tables, tpoly = build_tables(max_rank)
+    lines = []
+    w = lines.append
+    w("// Generated by cartesian_tensor_product_amd/gen/generate.py -- do not edit.")
+    w("// Exact rational coupling and direction-tensor tables (FlashCart paper,")
+    w("// §3 'Symbolic construction', App. B Eq. B1 and the direction-tensor formula).")
+    w("#pragma once")
+    w("")
+    w("namespace fc {")
+    w("namespace tab {")
+    w("")
+    w(f"inline constexpr int kMaxRank = {max_rank};")
+    w("")
+    w("struct Term { int a, b1, b2; float c; };")
+    w("struct Mono { int ex, ey, ez; float c; };")
+    w("")
+    w("// coupling path types (l1, l2 -> L), natural parity, lexicographic")
+    w(f"inline constexpr int kNumPathTypes = {len(paths)};")
+    w("inline constexpr int kPathL1[] = {" + ", ".join(str(p[0]) for p in paths) + "};")
+    w("inline constexpr int kPathL2[] = {" + ", ".join(str(p[1]) for p in paths) + "};")
+    w("inline constexpr int kPathL[] = {" + ", ".join(str(p[2]) for p in paths) + "};")
+    begins, allterms = [], []
+    for p in paths:
+        begins.append(len(allterms))
+        allterms.extend(tables[p])
+    begins.append(len(allterms))
+    w("inline constexpr int kTermBegin[] = {" + ", ".join(map(str, begins)) + "};")
+    w(f"inline constexpr int kNumTerms = {len(allterms)};")
+    w("inline constexpr Term kTerms[] = {")
+    for p in paths:
+        w(f"  // ({p[0]},{p[1]})->{p[2]}: {len(tables[p])} terms")
+        for (a, b1, b2, c) in tables[p]:
+            w(f"  {{{a}, {b1}, {b2}, {cfloat(c)}}},")
+    w("};")
+    w("")
+    w("// direction tensors T_l(n): stored component c of rank l is")
+    w("// sum over monomials c * n_x^ex n_y^ey n_z^ez")
+    mb, allmono = [], []
+    for l in range(max_rank + 1):
+        for poly in tpoly[l]:
+            mb.append(len(allmono))
+            for (ex, ey, ez), c in sorted(poly.items(), reverse=True):
+                allmono.append((ex, ey, ez, c))
+    mb.append(len(allmono))
+    w("inline constexpr int kMonoBegin[] = {" + ", ".join(map(str, mb)) + "};")
+    w("inline constexpr Mono kMono[] = {")
+    for (ex, ey, ez, c) in allmono:
+        w(f"  {{{ex}, {ey}, {ez}, {cfloat(c)}}},")
+    w("};")
+    w("")
+    w("}  // namespace tab")
+    w("}  // namespace fc")
+    _write(path, "\n".join(lines) + "\n")
+
+
+# (l_in, l_edge, l_out) instantiated in the library: equal ranks 0..4 (the
+# microbenchmark grid of the pages) and (l_prop, l_e, l_e) with
+# l_prop <= min(l_e, 3) (model blocks; the first convolution has scalar
+# senders, later ones propagate rank l_prop).
+def conv_configs():
+    out = [(L, L, L) for L in range(MAX_RANK + 1)]
+    for le in range(1, MAX_RANK + 1):
+        for lp in range(0, 4):
+            if lp <= le and (lp, le, le) not in out:
+                out.append((lp, le, le))
+    return out
+
+
+def emit_instances(gen_dir: str) -> list:
+    """One translation unit per convolution configuration, plus the list."""
+    cfgs = conv_configs()
+    lines = ["// Generated by cartesian_tensor_product_amd/gen/generate.py -- do not edit.",
+             "// (l_in, l_edge, l_out) instantiated in this build.", "#pragma once", "",
+             "#define FC_CONV_CONFIGS(X) \\"]
+    lines += [f"  X({a}, {b}, {c}) \\" for a, b, c in cfgs]
+    lines += ["", ""]
+    _write(os.path.join(gen_dir, "fc_conv_configs.h"), "\n".join(lines))
+    files = []
+    for a, b, c in cfgs:
+        src = (f"// Generated by cartesian_tensor_product_amd/gen/generate.py -- do not edit.\n"
+               f"#include \"../fc_conv_kernels.h\"\n\n"
+               f"namespace fc {{\n\n"
+               f"bool conv_run_{a}{b}{c}(int op, const ConvArgs& args, hipStream_t stream) {{\n"
+               f"  if (op == 0) launch_fwd_groups<{a}, {b}, {c}, 0>(args, stream);\n"
+               f"  else launch_vjp<{a}, {b}, {c}>(args, stream);\n"
+               f"  return true;\n}}\n\n}}  // namespace fc\n")
+        f = os.path.join(gen_dir, f"conv_inst_{a}{b}{c}.hip")
+        _write(f, src)
+        files.append(f)
+    return files
+
+
+def _write(path: str, text: str) -> None:
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    if os.path.exists(path) and open(path).read() == text:
+        return
+    tmp = path + ".tmp"
+    with open(tmp, "w") as f:
+        f.write(text)
+    os.replace(tmp, path)
+
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "csrc", "generated", "fc_tables.h")
+
+
+def emit_all() -> None:
+    emit(HEADER)
+    emit_instances(os.path.dirname(HEADER))
+
+
+if __name__ == "__main__":
+    emit_all()

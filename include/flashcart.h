@@ -1,0 +1,213 @@
+/*
+ * flashcart.h -- C ABI of the MI355X (gfx950) FlashCart hot path.
+ *
+ * Operations follow "FlashCart: Fast Cartesian Tensor Products for
+ * Equivariant Interatomic Potentials" (arXiv 2610.06409):
+ *   - edge convolution, §4 Eq. 1 (receiver-sorted sum over incoming edges),
+ *     with path-separated outputs and the layout of App. D ("Data layout",
+ *     Fig. D1);
+ *   - its VJP, App. C Eq. C1, carried through the direction tensors and the
+ *     radial weights to the positions (forces);
+ *   - its VJP-of-VJP for position cotangents, App. C Eq. C2;
+ *   - the node-local correlation ladder, §5 Eq. 2 (full) and App. E
+ *     "Path-reduced products", and its VJP.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Precision: fp32 storage and arithmetic.
+ * Memory: every array argument is a DEVICE pointer into caller-owned memory.
+ *   The library allocates nothing inside any call and keeps no pointer after
+ *   return; scratch comes from a caller workspace sized by the matching
+ *   *_workspace_bytes query.  Inputs and outputs must not alias.
+ * Streams: calls are asynchronous and ordered on the given hipStream_t
+ *   (pass 0 for the null stream).  Host-side argument checks happen before
+ *   any launch; on error nothing is launched.
+ * Outputs are overwritten, never accumulated into.
+ * Determinism: no atomics touch floating-point data; results are bitwise
+ *   reproducible for fixed inputs and launch configuration.
+ * Errors: every call returns an fc_status; fc_last_error_message() gives a
+ *   thread-local detail string for the last failing call on this thread.
+ *
+ * Layouts (row-major, channels contiguous)
+ * ----------------------------------------
+ * Stored components of a rank-l tensor: the 2l+1 entries with at most one z
+ * index, ordered (p_x descending with p_z = 0), then (p_x descending with
+ * p_z = 1); e.g. l = 2: xx, xy, yy, xz, yz (§3 "Symbolic construction").
+ * Node features x: [N][(l_in+1)^2][C]; rank block l starts at row l^2.
+ * Path-separated outputs z (and g, g_hat): [N][n_out][C] with
+ *   row(path p, component c) = off(L) + c * P_L + eta_L,
+ *   off(L) = sum_{L'<L} (2L'+1) P_L',
+ * where P_L counts the paths with output rank L and eta_L is the position of
+ * p among them.  Paths are the natural-parity triples (l1, l2, L),
+ * l1 <= l_in, l2 <= l_edge, L <= l_out, |l1-l2| <= L <= l1+l2, l1+l2+L even,
+ * ordered by L and then (l1, l2) lexicographically (fc_conv_path).
+ * Radial weights W: [n_basis][P][C]; the weight of edge e, path p, channel k
+ *   is w = sum_b R_b(r_e) W[b][p][k] with
+ *   R_b(r) = sin(b pi r / r_cut) / r * (1 + cos(pi r / r_cut)) / 2 for
+ *   r < r_cut and 0 beyond, b = 1..n_basis (n_basis = 8 supported).
+ * Graph: receiver-sorted CSR (rowptr[N+1], sender[E]); edge e has receiver
+ *   u_e (rowptr[u] <= e < rowptr[u+1]), sender v_e = sender[e] and vector
+ *   r_e = pos[v_e] - pos[u_e] + shift[e] (shift may be NULL), pointing from
+ *   the receiver to its neighbour (§2).  The sender-sorted transpose
+ *   (t_rowptr[N+1], t_edge[E], with receiver[E]) is built by
+ *   fc_graph_transpose and lets the VJP run without atomics.
+ */
+#ifndef FLASHCART_H_
+#define FLASHCART_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FC_ABI_VERSION 1
+
+typedef enum {
+  FC_OK = 0,
+  FC_ERR_INVALID_ARGUMENT = 1, /* bad descriptor, NULL required pointer, bad size */
+  FC_ERR_UNSUPPORTED = 2,      /* valid request this build does not implement    */
+  FC_ERR_WORKSPACE = 3,        /* workspace NULL or smaller than required        */
+  FC_ERR_HIP = 4               /* a HIP runtime call or launch failed            */
+} fc_status;
+
+/* Human-readable name of a status code (static string). */
+const char* fc_status_string(fc_status s);
+/* Detail of the last failing call on the calling thread ("" if none). */
+const char* fc_last_error_message(void);
+/* Returns FC_ABI_VERSION. */
+int32_t fc_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * Edge convolution descriptor.
+ * n_nodes >= 1, n_edges >= 0, 1 <= channels <= 4096,
+ * 0 <= l_in, l_edge, l_out <= 4 with at least one admissible path,
+ * n_basis == 8, r_cut > 0, flags == 0 (natural parity, paths separate).
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t n_nodes, n_edges, channels;
+  int32_t l_in, l_edge, l_out;
+  int32_t n_basis;
+  float r_cut;
+  uint32_t flags;
+} fc_conv_desc;
+
+typedef struct {
+  const int32_t* rowptr;   /* [N+1] receiver-sorted row pointer              */
+  const int32_t* sender;   /* [E]   sender of each receiver-sorted edge       */
+  const int32_t* receiver; /* [E]   receiver of each edge (fc_graph_transpose) */
+  const int32_t* t_rowptr; /* [N+1] sender-sorted row pointer                 */
+  const int32_t* t_edge;   /* [E]   edge ids grouped by sender, ascending     */
+} fc_graph;
+
+/* Number of paths and row counts (in units of C floats) of x and z.
+ * Implements the path enumeration of §2 "Irreducible Cartesian tensors"
+ * (admissible = triangle + even J).  Host only. */
+fc_status fc_conv_layout(const fc_conv_desc* d, int32_t* n_paths, int32_t* in_rows,
+                         int32_t* out_rows);
+/* The i-th path (l1, l2, L) in storage order.  Host only. */
+fc_status fc_conv_path(const fc_conv_desc* d, int32_t i, int32_t* l1, int32_t* l2,
+                       int32_t* L);
+
+/* Builds receiver[E], t_rowptr[N+1] and t_edge[E] on the device from the
+ * receiver-sorted CSR.  Within each sender, edge ids are ascending, so the
+ * result is unique.  Workspace: fc_graph_transpose_workspace_bytes(N). */
+size_t fc_graph_transpose_workspace_bytes(int32_t n_nodes);
+fc_status fc_graph_transpose(int32_t n_nodes, int32_t n_edges, const int32_t* rowptr,
+                             const int32_t* sender, int32_t* receiver, int32_t* t_rowptr,
+                             int32_t* t_edge, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+/* Host-side check of a receiver-sorted CSR given in HOST memory: rowptr[0]
+ * == 0, non-decreasing, rowptr[N] == E, 0 <= sender < N. */
+fc_status fc_graph_validate(int32_t n_nodes, int32_t n_edges, const int32_t* h_rowptr,
+                            const int32_t* h_sender);
+
+/* Workspace bytes for op = 0 (forward), 1 (VJP), 2 (VJP-of-VJP). */
+size_t fc_edge_conv_workspace_bytes(const fc_conv_desc* d, int32_t op);
+
+/* Forward, Eq. 1: z[u, eta, k] = sum_{e: u_e = u} w[e, eta, k] f_eta(x[v_e, k], T(r_hat_e)).
+ * pos [N][3], shift [E][3] or NULL, x [N][in_rows][C], radial_w [8][P][C],
+ * z [N][out_rows][C] (written).  Needs rowptr and sender of g. */
+fc_status fc_edge_conv_fwd(const fc_conv_desc* d, const fc_graph* g, const float* pos,
+                           const float* shift, const float* x, const float* radial_w,
+                           float* z, hipStream_t stream);
+
+/* VJP of L = <g_z, z> (Eq. C1 and the chain rule through T_l and R_b).
+ * x_grad [N][in_rows][C] and pos_grad [N][3] are written when non-NULL;
+ * radial_w_grad [8][P][C] is written when non-NULL.  At least one output
+ * must be requested.  Needs the full graph (transpose included) and a
+ * workspace of fc_edge_conv_workspace_bytes(d, 1) bytes. */
+fc_status fc_edge_conv_vjp(const fc_conv_desc* d, const fc_graph* g, const float* pos,
+                           const float* shift, const float* x, const float* radial_w,
+                           const float* g_z, float* x_grad, float* pos_grad,
+                           float* radial_w_grad, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/* VJP-of-VJP (Eq. C2 with the position derivatives of T_l and R_b): for
+ * s = <v_x, x_grad> + <v_pos, pos_grad> (NULL cotangent = zero), writes
+ * g_hat = ds/dg_z [N][out_rows][C], x_hat = ds/dx [N][in_rows][C] and
+ * pos_hat = ds/dpos [N][3] (each when non-NULL).  radial_w_hat must be NULL
+ * in this build (FC_ERR_UNSUPPORTED otherwise). */
+fc_status fc_edge_conv_vjp_vjp(const fc_conv_desc* d, const fc_graph* g, const float* pos,
+                               const float* shift, const float* x, const float* radial_w,
+                               const float* g_z, const float* v_x, const float* v_pos,
+                               float* g_hat, float* x_hat, float* pos_hat,
+                               float* radial_w_hat, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Node-local correlation ladder (§5 Eq. 2; App. E "Path-reduced products").
+ * A [N][(l_a+1)^2][C]; z [N][(l_out+1)^2][C].  Steps q = 1..order; the
+ * product at step q >= 2 couples phi^{q-1} (ranks <= l_{q-1}) with A (ranks
+ * <= l_a) to ranks <= l_q, with l_q = l_prod for q < order and l_q = l_out
+ * for q = order (phi^1 keeps ranks <= min(l_a, l_1)).  Paths of a step are
+ * ordered like the convolution paths.
+ * variant FC_LADDER_FULL: phi^1_l = W1_l A_l; phi^q_L = W^q_L B^q_L with
+ *   B^q_L [(2L+1) rows][P_{q,L} * C] the path-separated products;
+ *   z = sum_q Pi_{<= l_out} phi^q.
+ *   Flat weights: W1_l [C][C] for l = 0..l_1, then for q = 2..order and
+ *   L = 0..l_q with P_{q,L} > 0: W^q_L [C][P_{q,L} C], element
+ *   [k_out][eta * C + k_in].
+ * variant FC_LADDER_PATH_REDUCED: phi^1_l = a1[l][k] A_l;
+ *   phi^q_L = P_{q,L}^{-1/2} sum_{eta -> L} a^q[eta][k] (phi^{q-1} (x) A)_eta;
+ *   z_L = W_L sum_q phi^q_L.
+ *   Flat weights: a1 [l_1+1][C], a^q [P_q][C] for q = 2..order,
+ *   W_L [C][C] for L = 0..l_out.
+ * Constraints: 1 <= order <= 8, ranks <= 4, C a multiple of 32 and <= 512.
+ * ---------------------------------------------------------------------- */
+enum { FC_LADDER_FULL = 0, FC_LADDER_PATH_REDUCED = 1 };
+
+typedef struct {
+  int32_t n_nodes, channels;
+  int32_t l_a, l_prod, l_out, order;
+  int32_t variant;
+} fc_ladder_desc;
+
+/* Sizes in floats of the flat weight buffer and of the saved-state buffer
+ * the forward fills for the VJP.  Host only. */
+fc_status fc_ladder_layout(const fc_ladder_desc* d, size_t* n_weight_floats,
+                           size_t* n_saved_floats);
+size_t fc_ladder_workspace_bytes(const fc_ladder_desc* d, int32_t op /*0 fwd, 1 vjp*/);
+
+/* Forward.  saved may be NULL when no VJP follows; otherwise it receives
+ * n_saved_floats floats of intermediate states. */
+fc_status fc_node_ladder_fwd(const fc_ladder_desc* d, const float* A, const float* weights,
+                             float* z, float* saved, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/* VJP of L = <g_z, z>: A_grad [N][(l_a+1)^2][C] and, when non-NULL, the
+ * weight gradient in the flat weight layout.  saved must come from
+ * fc_node_ladder_fwd with the same A and weights. */
+fc_status fc_node_ladder_vjp(const fc_ladder_desc* d, const float* A, const float* weights,
+                             const float* saved, const float* g_z, float* A_grad,
+                             float* weights_grad, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASHCART_H_ */

@@ -1,0 +1,101 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point declared in include/flashcart.h, and its layout queries and
+argument checks behave as documented."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+from cartesian_tensor_product_amd import flashcart as fc
+from oracle import conv, ladder
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pytestmark = pytest.mark.skipif(not os.path.exists(fc.LIB_PATH), reason="libflashcart.so not built")
+
+
+def declared_symbols():
+    src = open(os.path.join(ROOT, "include", "flashcart.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fc_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_symbols()
+    assert len(names) >= 16
+    L = fc.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    out = os.popen(f"nm -D --defined-only {fc.LIB_PATH}").read()
+    for n in names:
+        assert re.search(rf"\bT {n}\b", out), f"{n} not exported"
+
+
+def test_abi_version_and_status_strings():
+    assert fc.fc_abi_version() == 1
+    L = fc.lib()
+    assert L.fc_status_string(0) == b"FC_OK"
+    assert L.fc_status_string(3) == b"FC_ERR_WORKSPACE"
+
+
+@pytest.mark.parametrize("ranks", [(1, 1, 1), (2, 2, 2), (3, 3, 3), (4, 4, 4), (0, 3, 3), (2, 3, 3)])
+def test_layout_and_path_order_match_oracle(ranks):
+    spec = conv.ConvSpec(*ranks, 5.0)
+    d = fc.conv_desc(10, 20, 16, *ranks, 5.0)
+    P, nin, nout = fc.fc_conv_layout(d)
+    assert (P, nin, nout) == (spec.n_paths, spec.n_in, spec.n_out)
+    assert [fc.fc_conv_path(d, i) for i in range(P)] == spec.paths
+    with pytest.raises(fc.FlashCartError):
+        fc.fc_conv_path(d, P)
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(n_nodes=0), fc.FC_ERR_INVALID_ARGUMENT),
+    (dict(n_edges=-1), fc.FC_ERR_INVALID_ARGUMENT),
+    (dict(channels=0), fc.FC_ERR_INVALID_ARGUMENT),
+    (dict(channels=300), fc.FC_ERR_UNSUPPORTED),
+    (dict(l_in=5), fc.FC_ERR_UNSUPPORTED),
+    (dict(l_in=-1), fc.FC_ERR_INVALID_ARGUMENT),
+    (dict(n_basis=6), fc.FC_ERR_UNSUPPORTED),
+    (dict(r_cut=0.0), fc.FC_ERR_INVALID_ARGUMENT),
+    (dict(r_cut=float("inf")), fc.FC_ERR_INVALID_ARGUMENT),
+    (dict(flags=1), fc.FC_ERR_UNSUPPORTED),
+])
+def test_descriptor_errors(bad, status):
+    kw = dict(n_nodes=4, n_edges=8, channels=8, l_in=1, l_edge=1, l_out=1, r_cut=5.0, n_basis=8, flags=0)
+    kw.update(bad)
+    d = fc.conv_desc(**kw)
+    with pytest.raises(fc.FlashCartError) as ei:
+        fc.fc_conv_layout(d)
+    assert ei.value.status == status
+    # calls fail on the host before anything touches a GPU
+    assert fc.fc_edge_conv_workspace_bytes(d, 1) == 0
+
+
+def test_null_pointers_rejected_before_launch():
+    d = fc.conv_desc(4, 8, 8, 1, 1, 1, 5.0)
+    g = fc.Graph()
+    L = fc.lib()
+    import ctypes
+    st = L.fc_edge_conv_fwd(ctypes.byref(d), ctypes.byref(g), None, None, None, None, None, None)
+    assert st == fc.FC_ERR_INVALID_ARGUMENT
+    assert b"rowptr" in L.fc_last_error_message()
+    st = L.fc_edge_conv_vjp(ctypes.byref(d), ctypes.byref(g), None, None, None, None, None, None, None, None,
+                            None, 0, None)
+    assert st == fc.FC_ERR_INVALID_ARGUMENT
+
+
+def test_graph_validate():
+    fc.fc_graph_validate(3, 4, [0, 2, 3, 4], [1, 2, 0, 1])
+    for rp, sd in [([1, 2, 3, 4], [1, 2, 0, 1]), ([0, 3, 2, 4], [1, 2, 0, 1]), ([0, 2, 3, 5], [1, 2, 0, 1]),
+                   ([0, 2, 3, 4], [1, 2, 0, 3])]:
+        with pytest.raises(fc.FlashCartError) as ei:
+            fc.fc_graph_validate(3, 4, rp, sd)
+        assert ei.value.status == fc.FC_ERR_INVALID_ARGUMENT
+
+
+def test_workspace_sizes():
+    d = fc.conv_desc(1024, 131072, 128, 2, 2, 2, 5.0)
+    assert fc.fc_edge_conv_workspace_bytes(d, 0) == 0
+    assert fc.fc_edge_conv_workspace_bytes(d, 1) >= 131072 * 3 * 4

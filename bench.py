@@ -75,6 +75,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-only", type=int, default=0, metavar="MB",
+                    help="only run 5 device-to-device copies of MB megabytes (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
@@ -82,6 +84,15 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_only:
+        src = torch.ones(args.copy_only * (1 << 20) // 4, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": src.numel() * 4, "copies": 5}))
+        return
 
     from cartesian_tensor_product_amd import flashcart as fc
     from cartesian_tensor_product_amd import inputs

@@ -101,7 +101,6 @@ fc::ConvArgs make_args(const fc_conv_desc* d, const fc_graph* g, const float* po
   return a;
 }
 
-size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
 }  // namespace
 
@@ -183,7 +182,10 @@ fc_status fc_graph_validate(int32_t n_nodes, int32_t n_edges, const int32_t* h_r
 
 size_t fc_edge_conv_workspace_bytes(const fc_conv_desc* d, int32_t op) {
   if (check_desc(d) != FC_OK) return 0;
-  if (op == 1) return round256((size_t)3 * d->n_edges * sizeof(float));
+  if (op == 1) {
+    const fc::VjpWorkspace w(d->n_nodes, d->n_edges, d->channels, (d->l_in + 1) * (d->l_in + 1), nullptr);
+    return w.bytes;
+  }
   return 0;
 }
 
@@ -216,7 +218,7 @@ fc_status fc_edge_conv_vjp(const fc_conv_desc* d, const fc_graph* g, const float
       misaligned(x_grad, 4) || misaligned(pos_grad, 4) || misaligned(shift, 4))
     return fail(FC_ERR_INVALID_ARGUMENT, "VJP: arrays must be 4-byte aligned");
   const size_t need = fc_edge_conv_workspace_bytes(d, 1);
-  if (pos_grad && (!workspace || workspace_bytes < need))
+  if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(FC_ERR_WORKSPACE, "VJP needs %zu workspace bytes", need);
   fc::ConvArgs a = make_args(d, g, pos, shift, x, radial_w);
   a.g = g_z;

@@ -210,4 +210,16 @@ __device__ __forceinline__ void radial(float r, float rc, float* R, float* dR) {
 // ------------------------------------------------------------- misc device
 __device__ __forceinline__ int uniform_int(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Raw buffer access: a row gather becomes one buffer_load with the row
+// offset in an SGPR (soffset) and the lane's channel offset in a VGPR
+// (voffset), so no per-load 64-bit address arithmetic runs on the VALU.
+// Out-of-range offsets read 0.  dword3 0x00020000 is the gfx9-family
+// (CDNA) raw-buffer format word.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ float buf_load(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+
 }  // namespace fc

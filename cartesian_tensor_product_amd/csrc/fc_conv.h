@@ -21,7 +21,38 @@ bool conv_supported(int l_in, int l_edge, int l_out);
 // op 0: forward (needs rowptr, sender, pos, shift, x, W, z);
 // op 1: VJP (additionally receiver, t_rowptr, t_edge, g, rbar, and x_bar
 //       and/or pos_bar).
-void launch_vjp_receiver(const ConvArgs& a, hipStream_t st);
+// Outgoing edges of a sender are split into S contiguous slices (about 32
+// edges each on average) processed by separate blocks.
+inline int vjp_slices(int N, int E) {
+  const int avg = N > 0 ? E / N : 0;
+  int s = (avg + 16) / 32;
+  return s < 1 ? 1 : (s > 8 ? 8 : s);
+}
+
+inline size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+
+// VJP workspace: per-edge position cotangents, then (S > 1) per-slice
+// partial position sums and partial x_bar.
+struct VjpWorkspace {
+  int S;
+  float *rbar, *p_part, *x_part;
+  size_t bytes;
+  VjpWorkspace(int N, int E, int C, int nin, void* base) {
+    S = vjp_slices(N, E);
+    char* p = static_cast<char*>(base);
+    size_t off = 0;
+    rbar = reinterpret_cast<float*>(p + off);
+    off += align256((size_t)3 * E * sizeof(float));
+    p_part = reinterpret_cast<float*>(p + off);
+    if (S > 1) off += align256((size_t)3 * N * S * sizeof(float));
+    x_part = reinterpret_cast<float*>(p + off);
+    if (S > 1) off += align256((size_t)N * S * nin * C * sizeof(float));
+    bytes = off;
+    if (!base) rbar = p_part = x_part = nullptr;
+  }
+};
+
+void launch_vjp_combine(const ConvArgs& a, const VjpWorkspace& w, int nin, hipStream_t st);
 bool conv_dispatch(int op, int l_in, int l_edge, int l_out, const ConvArgs& args, hipStream_t stream);
 
 }  // namespace fc

@@ -5,38 +5,58 @@
 
 namespace fc {
 
-// Receiver pass: pos_bar[u] -= sum of r_bar over the incoming edges of u
-// (one wave per node, fixed per-lane order and a fixed butterfly, so the
-// result is deterministic).
-__global__ __launch_bounds__(256) void conv_vjp_receiver_kernel(int N, const int* __restrict__ rowptr,
-                                                                const float* __restrict__ rbar,
-                                                                float* __restrict__ pos_bar) {
-  const int u = blockIdx.x * 4 + threadIdx.x / kWave;
-  const int lane = threadIdx.x % kWave;
-  if (u >= N) return;
-  const int e0 = rowptr[u], e1 = rowptr[u + 1];
-  float sx = 0.f, sy = 0.f, sz = 0.f;
-  for (int e = e0 + lane; e < e1; e += kWave) {
-    sx += rbar[3 * (size_t)e];
-    sy += rbar[3 * (size_t)e + 1];
-    sz += rbar[3 * (size_t)e + 2];
+// Combine pass, one block per node v, fixed summation order (deterministic):
+//   x_bar[v]   = sum_s x_part[v, s]                         (when S > 1)
+//   pos_bar[v] = sum_s p_part[v, s] - sum_{e: u_e = v} r_bar_e
+// With S == 1 the sender kernel wrote x_bar and the sender part of pos_bar
+// directly and only the receiver sum is applied.
+__global__ __launch_bounds__(256) void conv_vjp_combine_kernel(int S, int row, const int* __restrict__ rowptr,
+                                                               const float* __restrict__ rbar,
+                                                               const float* __restrict__ p_part,
+                                                               const float* __restrict__ x_part,
+                                                               float* __restrict__ x_bar, float* __restrict__ pos_bar) {
+  const int v = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (x_part && S > 1) {
+    for (int i = tid; i < row; i += blockDim.x) {
+      float t = 0.f;
+      for (int s = 0; s < S; ++s) t += x_part[((size_t)v * S + s) * row + i];
+      x_bar[(size_t)v * row + i] = t;
+    }
   }
+  if (pos_bar && tid < kWave) {
+    const int e0 = rowptr[v], e1 = rowptr[v + 1];
+    float sx = 0.f, sy = 0.f, sz = 0.f;
+    for (int e = e0 + tid; e < e1; e += kWave) {
+      sx += rbar[3 * (size_t)e];
+      sy += rbar[3 * (size_t)e + 1];
+      sz += rbar[3 * (size_t)e + 2];
+    }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    sx += __shfl_xor(sx, o);
-    sy += __shfl_xor(sy, o);
-    sz += __shfl_xor(sz, o);
-  }
-  if (lane == 0) {
-    pos_bar[3 * u] -= sx;
-    pos_bar[3 * u + 1] -= sy;
-    pos_bar[3 * u + 2] -= sz;
+    for (int o = 32; o > 0; o >>= 1) {
+      sx += __shfl_xor(sx, o);
+      sy += __shfl_xor(sy, o);
+      sz += __shfl_xor(sz, o);
+    }
+    if (tid == 0) {
+      const float* pp = S > 1 ? p_part + (size_t)3 * v * S : pos_bar + 3 * (size_t)v;
+      float px = 0.f, py = 0.f, pz = 0.f;
+      for (int s = 0; s < (S > 1 ? S : 1); ++s) {
+        px += pp[3 * s];
+        py += pp[3 * s + 1];
+        pz += pp[3 * s + 2];
+      }
+      pos_bar[3 * (size_t)v] = px - sx;
+      pos_bar[3 * (size_t)v + 1] = py - sy;
+      pos_bar[3 * (size_t)v + 2] = pz - sz;
+    }
   }
 }
 
-void launch_vjp_receiver(const ConvArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(conv_vjp_receiver_kernel, dim3((a.N + 3) / 4), dim3(256), 0, st, a.N, a.rowptr, a.rbar,
-                     a.pos_bar);
+void launch_vjp_combine(const ConvArgs& a, const VjpWorkspace& w, int nin, hipStream_t st) {
+  if (w.S == 1 && !a.pos_bar) return;
+  hipLaunchKernelGGL(conv_vjp_combine_kernel, dim3(a.N), dim3(256), 0, st, w.S, nin * a.C, a.rowptr, w.rbar,
+                     w.p_part, a.x_bar ? w.x_part : nullptr, a.x_bar, a.pos_bar);
 }
 
 #define FC_CONV_DECL(A, B, Cc) bool conv_run_##A##B##Cc(int op, const ConvArgs& args, hipStream_t stream);

@@ -4,12 +4,12 @@
 //
 // Mapping: one wavefront per (node, 64-channel tile); channel k lives in lane
 // k % 64, so every gather of a neighbour row is one coalesced 256-byte
-// transaction per stored component.  Per-edge geometry (direction tensor
-// components, Bessel radial values, neighbour id) is computed once per edge
-// by a lane of its own (lane j <-> edge j of a 64-edge chunk), parked in LDS
-// and read back by all 64 lanes as a broadcast, so it is shared by all
-// channels.  The coupling polynomials come from the generated tables and are
-// fully unrolled; all accumulators stay in VGPRs.
+// buffer load per stored component.  Per-edge geometry (direction tensor
+// components or their coefficient products, Bessel radial values, neighbour
+// id) is computed once per edge by a lane of its own (lane j <-> edge j of a
+// 64-edge chunk), parked in LDS and read back by all 64 lanes as a broadcast,
+// so it is shared by all channels.  The coupling polynomials come from the
+// generated tables and are fully unrolled; all accumulators stay in VGPRs.
 #pragma once
 
 #include "fc_conv.h"
@@ -21,6 +21,11 @@ namespace fc {
 inline constexpr int kGroupRows = 100;
 // Channels of one VJP block: up to 4 waves (C <= 256).
 inline constexpr int kMaxVjpWaves = 4;
+// Per-edge products |c| y[g] are broadcast from LDS when a configuration uses
+// at most this many; larger tables multiply inline from y.
+inline constexpr int kCYMax = 48;
+// Per-sender products |c| x[g] stay in registers up to this many.
+inline constexpr int kCXMax = 20;
 
 template <class Cfg, int LOUT>
 constexpr int group_end(int lo) {
@@ -34,16 +39,53 @@ constexpr int group_end(int lo) {
   return hi;
 }
 
+// Per-edge coefficient products of one configuration.
+template <int LIN, int LEDGE, int LOUT>
+struct EdgeProducts {
+  using CYt = tab::CY<LIN, LEDGE, LOUT>;
+  using CXt = tab::CX<LIN, LEDGE, LOUT>;
+  static constexpr int NE = nrank(LEDGE);
+  static constexpr bool kLDS = CYt::n <= kCYMax;
+  static constexpr bool kCXReg = CXt::n <= kCXMax;
+  static constexpr int NY = kLDS ? CYt::n : NE;   // record floats holding y (first NE) and products
+
+  // record entries from y (lane-per-edge stage)
+  __device__ __forceinline__ static void fill(const float* y, float* rec) {
+    if constexpr (kLDS) {
+      static_for<CYt::n>([&](auto i) {
+        constexpr int ii = i;
+        constexpr float c = CYt::c[ii];
+        if constexpr (c == 1.f) rec[ii] = y[CYt::g[ii]];
+        else rec[ii] = c * y[CYt::g[ii]];
+      });
+    } else {
+      static_for<NE>([&](auto i) { rec[i] = y[i]; });
+    }
+  }
+  // signed c * y[g2] of global term TERM (g2 = l2^2 + b2)
+  template <int TERM, int G2>
+  __device__ __forceinline__ static float cy(const float* rec) {
+    constexpr tab::Term T = tab::kTerms[TERM];
+    constexpr float ac = T.c < 0.f ? -T.c : T.c;
+    float v;
+    if constexpr (kLDS) v = rec[CYt::term[TERM]];
+    else if constexpr (ac == 1.f) v = rec[G2];
+    else v = ac * rec[G2];
+    return T.c < 0.f ? -v : v;
+  }
+};
+
 // ============================================================== forward ====
 template <int LIN, int LEDGE, int LOUT, int LLO, int LHI>
 __global__ __launch_bounds__(kWave) void conv_fwd_kernel(
-    int C, const int* __restrict__ rowptr, const int* __restrict__ sender,
+    int N, int C, const int* __restrict__ rowptr, const int* __restrict__ sender,
     const float* __restrict__ pos, const float* __restrict__ shift,
     const float* __restrict__ x, const float* __restrict__ W, float* __restrict__ z, float rc) {
   using Cfg = ConvCfg<LIN, LEDGE, LOUT>;
   using G = Group<Cfg, LLO, LHI>;
+  using EP = EdgeProducts<LIN, LEDGE, LOUT>;
   constexpr int NIN = Cfg::NIN, NE = Cfg::NE, P = Cfg::P, NOUT = Cfg::NOUT;
-  constexpr int REC = NE + kNB + 1;
+  constexpr int REC = EP::NY + kNB + 1;
   constexpr bool WREG = kNB * G::NP <= 128;
   __shared__ float geo[kWave * REC];
 
@@ -52,6 +94,8 @@ __global__ __launch_bounds__(kWave) void conv_fwd_kernel(
   const int k = blockIdx.y * kWave + lane;
   const bool act = k < C;
   const int kk = act ? k : 0;
+  const int voff = kk * 4;
+  const auto xr = make_rsrc(x, (uint32_t)((size_t)N * NIN * C * 4));
 
   float Wr[WREG ? kNB * G::NP : 1];
   if constexpr (WREG) {
@@ -82,39 +126,37 @@ __global__ __launch_bounds__(kWave) void conv_fwd_kernel(
       direction_tensors<LEDGE>(rx * inv, ry * inv, rz * inv, y);
       radial<false>(r, rc, R, nullptr);
       float* rec = geo + lane * REC;
-      static_for<NE>([&](auto c) { rec[c] = y[c]; });
-      static_for<kNB>([&](auto b) { rec[NE + b] = R[b]; });
-      rec[NE + kNB] = __int_as_float(s);
+      EP::fill(y, rec);
+      static_for<kNB>([&](auto b) { rec[EP::NY + b] = R[b]; });
+      rec[EP::NY + kNB] = __int_as_float(s);
     }
     __syncthreads();
     for (int j = 0; j < cnt; ++j) {
       const float* rec = geo + j * REC;
-      const int s = uniform_int(__float_as_int(rec[NE + kNB]));
-      const float* xs = x + (size_t)s * NIN * C + kk;
-      float xv[NIN], y[NE], R[kNB];
-      static_for<NIN>([&](auto c) { xv[c] = xs[(size_t)c * C]; });
-      static_for<NE>([&](auto c) { y[c] = rec[c]; });
-      static_for<kNB>([&](auto b) { R[b] = rec[NE + b]; });
+      const int s = uniform_int(__float_as_int(rec[EP::NY + kNB]));
+      const int sbase = s * NIN * C * 4;
+      float xv[NIN];
+      static_for<NIN>([&](auto c) { xv[c] = buf_load(xr, voff, sbase + c * C * 4); });
       static_for<G::NP>([&](auto pi) {
         constexpr int p = G::p0 + pi;
         constexpr PathInfo PI = Cfg::paths[p];
+        constexpr int n1 = ncomp(PI.l1), o1 = rank_off(PI.l1), o2 = rank_off(PI.l2);
         float w = 0.f;
         static_for<kNB>([&](auto b) {
+          constexpr int bb = b;
           float wb;
-          if constexpr (WREG) wb = Wr[b * G::NP + pi];
-          else wb = W[(size_t)(b * P + p) * C + kk];
-          w = fmaf(R[b], wb, w);
+          if constexpr (WREG) wb = Wr[bb * G::NP + pi];
+          else wb = W[(size_t)(bb * P + p) * C + kk];
+          w = fmaf(rec[EP::NY + bb], wb, w);
         });
+        float xw[n1];
+        static_for<n1>([&](auto c) { xw[c] = w * xv[o1 + c]; });
         constexpr int tb = tab::kTermBegin[PI.type], te = tab::kTermBegin[PI.type + 1];
-        float t[ncomp(PI.L)];
-        static_for<ncomp(PI.L)>([&](auto a) { t[a] = 0.f; });
         static_for<te - tb>([&](auto ti) {
-          constexpr tab::Term T = tab::kTerms[tb + ti];
-          t[T.a] = fmaf(T.c * y[rank_off(PI.l2) + T.b2], xv[rank_off(PI.l1) + T.b1], t[T.a]);
-        });
-        static_for<ncomp(PI.L)>([&](auto a) {
-          constexpr int row = Cfg::row(p, a) - G::r0;
-          acc[row] = fmaf(w, t[a], acc[row]);
+          constexpr int tt = tb + ti;
+          constexpr tab::Term T = tab::kTerms[tt];
+          constexpr int row = Cfg::row(p, T.a) - G::r0;
+          acc[row] = fmaf(EP::template cy<tt, o2 + T.b2>(rec), xw[T.b1], acc[row]);
         });
       });
     }
@@ -132,57 +174,99 @@ void launch_fwd_groups(const ConvArgs& a, hipStream_t st) {
   constexpr int LHI = group_end<Cfg, LOUT>(LLO);
   dim3 grid(a.N, (a.C + kWave - 1) / kWave);
   hipLaunchKernelGGL((conv_fwd_kernel<LIN, LEDGE, LOUT, LLO, LHI>), grid, dim3(kWave), 0, st,
-                     a.C, a.rowptr, a.sender, a.pos, a.shift, a.x, a.W, a.z, a.rc);
+                     a.N, a.C, a.rowptr, a.sender, a.pos, a.shift, a.x, a.W, a.z, a.rc);
   if constexpr (LHI < LOUT) launch_fwd_groups<LIN, LEDGE, LOUT, LHI + 1>(a, st);
 }
 
 // ================================================================== VJP ====
-// Sender-sorted pass: block = NW = ceil(C/64) waves covering all C channels
-// of sender v (C <= 256).
-// For every outgoing edge e = (v -> u): gather g[u], then
-//   x_bar[v]  += sum_p w_p VJP1_p(g_p, y)                  (per lane)
-//   y_bar_e   = sum_{p,k} w_p VJP2_p(g_p, x_v)             (across lanes)
-//   rho_e[b]  = sum_{p,k} <g_p, f_p(x_v, y)> W[b,p,k]      (across lanes)
-// and the edge's position cotangent
-//   r_bar_e = (sum_b dR_b/dr rho_b) r_hat + (I - r_hat r_hat^T)/r (sum_c y_bar_c grad_n y_c),
-// which is added to the sender here and stored per edge for the receiver pass.
+// Sender-sorted pass: a block of NW = ceil(C/64) waves holds all C channels
+// of sender v (C <= 256) and one of S contiguous slices of v's outgoing
+// edges (slices balance the unequal out-degrees; their partial x_bar and
+// position sums are combined in a fixed order by conv_vjp_combine_kernel).
+// For every outgoing edge e = (v -> u), gather g[u] and accumulate
+//   x_bar[v]  += sum_p w_p VJP1_p(g_p, y)                       (per lane)
+//   y_bar_e    = sum_{p,k} w_p VJP2_p(g_p, x_v)                 (over lanes)
+//   s_e        = sum_{p,k} <g_p, f_p(x_v, y)> dw_p/dr            (over lanes)
+// with w_p = sum_b R_b W[b,p] and dw_p/dr = sum_b R'_b W[b,p].  The edge's
+// position cotangent is
+//   r_bar_e = s_e r_hat + (I - r_hat r_hat^T)/r (sum_c y_bar_c grad_n y_c);
+// it is added to the sender and stored per edge for the combine pass.
+// The NE+1 per-edge sums over lanes use DPP row rotations (16 lanes) and the
+// four row totals of every wave are combined from LDS once per 64-edge chunk.
+template <int LIN, int LEDGE, int LOUT>
+struct VjpShape {
+  using EP = EdgeProducts<LIN, LEDGE, LOUT>;
+  static constexpr int NE = nrank(LEDGE);
+  static constexpr int NRED = NE + 1;                      // y_bar components, s
+  static constexpr int REC = EP::NY + 2 * kNB + 1;         // y / products, R, R', receiver
+  static constexpr size_t lds_bytes(int nw) {
+    return sizeof(float) * ((size_t)kWave * REC + (size_t)nw * kWave * NRED * 4);
+  }
+};
+
+__device__ __forceinline__ float row_sum16(float v) {
+  // every lane of a 16-lane row ends with the row total
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x122, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x121, 0xF, 0xF, false));
+  return v;
+}
+
 template <int LIN, int LEDGE, int LOUT, bool NEED_X, bool NEED_POS>
 __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
-    int C, const int* __restrict__ t_rowptr, const int* __restrict__ t_edge,
+    int N, int C, const int* __restrict__ t_rowptr, const int* __restrict__ t_edge,
     const int* __restrict__ receiver, const float* __restrict__ pos,
     const float* __restrict__ shift, const float* __restrict__ x,
-    const float* __restrict__ W, const float* __restrict__ g, float* __restrict__ x_bar,
-    float* __restrict__ pos_bar, float* __restrict__ rbar, float rc) {
+    const float* __restrict__ W, const float* __restrict__ g, float* __restrict__ x_out,
+    float* __restrict__ p_out, float* __restrict__ rbar, float rc) {
   using Cfg = ConvCfg<LIN, LEDGE, LOUT>;
+  using Sh = VjpShape<LIN, LEDGE, LOUT>;
+  using EP = typename Sh::EP;
+  using CXt = typename EP::CXt;
   constexpr int NIN = Cfg::NIN, NE = Cfg::NE, P = Cfg::P, NOUT = Cfg::NOUT;
-  constexpr int REC = NE + kNB + 1;
-  constexpr int NRED = NE + kNB;
+  constexpr int REC = Sh::REC, NRED = Sh::NRED, NY = EP::NY;
   constexpr bool WREG = kNB * P <= 128;
-  __shared__ float geo[kWave * REC];
-  __shared__ float red[NEED_POS ? kMaxVjpWaves * kWave * NRED : 1];
+  extern __shared__ float lds[];
+  float* geo = lds;                      // [64][REC]
+  float* part = lds + kWave * REC;       // [NW][64 edges][NRED][4 rows]
   const int NW = blockDim.x / kWave;
 
   const int v = blockIdx.x;
+  const int S = gridDim.y, sl = blockIdx.y;   // slice sl of S of v's outgoing edges
   const int tid = threadIdx.x;
   const int wv = tid / kWave, lane = tid % kWave;
   const int k = tid;
   const bool act = k < C;
   const int kk = act ? k : 0;
+  const int voff = kk * 4;
+  const auto gr = make_rsrc(g, (uint32_t)((size_t)N * NOUT * C * 4));
 
+  // radial weights of this lane's channel (zero for idle lanes, so their
+  // contributions to the sums over lanes vanish)
   float Wr[WREG ? kNB * P : 1];
   if constexpr (WREG) {
     static_for<kNB * P>([&](auto i) { Wr[i] = act ? W[(size_t)i * C + kk] : 0.f; });
   }
+#define FC_WGET(B, PP) (WREG ? Wr[WREG ? (B) * P + (PP) : 0] : (act ? W[(size_t)((B) * P + (PP)) * C + kk] : 0.f))
   float xv[NIN];
   {
     const float* xs = x + (size_t)v * NIN * C + kk;
-    static_for<NIN>([&](auto c) { xv[c] = act ? xs[(size_t)c * C] : 0.f; });
+    static_for<NIN>([&](auto c) { xv[c] = xs[(size_t)c * C]; });
+  }
+  float cxr[EP::kCXReg && CXt::n > 0 ? CXt::n : 1];
+  if constexpr (EP::kCXReg) {
+    static_for<CXt::n>([&](auto i) {
+      constexpr int ii = i;
+      cxr[ii] = CXt::c[ii] * xv[CXt::g[ii]];
+    });
   }
   float xb[NIN];
   static_for<NIN>([&](auto c) { xb[c] = 0.f; });
   float psum[3] = {0.f, 0.f, 0.f};
 
-  const int e0 = t_rowptr[v], e1 = t_rowptr[v + 1];
+  const int v0 = t_rowptr[v], deg = t_rowptr[v + 1] - v0;
+  const int e0 = v0 + (int)(((long long)sl * deg) / S), e1 = v0 + (int)(((long long)(sl + 1) * deg) / S);
   const float pvx = pos[3 * v], pvy = pos[3 * v + 1], pvz = pos[3 * v + 2];
   for (int base = e0; base < e1; base += kWave) {
     const int cnt = min(kWave, e1 - base);
@@ -197,84 +281,88 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
       }
       const float r = sqrtf(rx * rx + ry * ry + rz * rz);
       const float inv = r > 0.f ? 1.f / r : 0.f;
-      float y[NE], R[kNB];
+      float y[NE], R[kNB], dR[kNB];
       direction_tensors<LEDGE>(rx * inv, ry * inv, rz * inv, y);
-      radial<false>(r, rc, R, nullptr);
+      radial<true>(r, rc, R, dR);
       float* rec = geo + lane * REC;
-      static_for<NE>([&](auto c) { rec[c] = y[c]; });
-      static_for<kNB>([&](auto b) { rec[NE + b] = R[b]; });
-      rec[NE + kNB] = __int_as_float(u);
+      EP::fill(y, rec);
+      static_for<kNB>([&](auto b) {
+        rec[NY + b] = R[b];
+        rec[NY + kNB + b] = dR[b];
+      });
+      rec[NY + 2 * kNB] = __int_as_float(u);
     }
     __syncthreads();
     for (int j = 0; j < cnt; ++j) {
       const float* rec = geo + j * REC;
-      const int u = uniform_int(__float_as_int(rec[NE + kNB]));
-      const float* gs = g + (size_t)u * NOUT * C + kk;
-      float y[NE], R[kNB];
-      static_for<NE>([&](auto c) { y[c] = rec[c]; });
-      static_for<kNB>([&](auto b) { R[b] = rec[NE + b]; });
-      float yb[NE], rho[kNB];
+      const int u = uniform_int(__float_as_int(rec[NY + 2 * kNB]));
+      const int ubase = u * NOUT * C * 4;
+      float gv[NOUT];
+      static_for<NOUT>([&](auto a) { gv[a] = buf_load(gr, voff, ubase + a * C * 4); });
+      float yb[NE];
       static_for<NE>([&](auto c) { yb[c] = 0.f; });
-      static_for<kNB>([&](auto b) { rho[b] = 0.f; });
+      float sacc = 0.f;
       static_for<P>([&](auto pc) {
         constexpr int p = pc;
         constexpr PathInfo PI = Cfg::paths[p];
-        constexpr int na = ncomp(PI.L), n1 = ncomp(PI.l1), n2 = ncomp(PI.l2);
+        constexpr int na = ncomp(PI.L), n2 = ncomp(PI.l2);
         constexpr int o1 = rank_off(PI.l1), o2 = rank_off(PI.l2);
-        float gp[na];
-        static_for<na>([&](auto a) { gp[a] = act ? gs[(size_t)Cfg::row(p, a) * C] : 0.f; });
+        constexpr int tb = tab::kTermBegin[PI.type], te = tab::kTermBegin[PI.type + 1];
         float w = 0.f;
         static_for<kNB>([&](auto b) {
-          float wb;
-          if constexpr (WREG) wb = Wr[b * P + p];
-          else wb = act ? W[(size_t)(b * P + p) * C + kk] : 0.f;
-          w = fmaf(R[b], wb, w);
+          constexpr int bb = b;
+          w = fmaf(rec[NY + bb], FC_WGET(bb, p), w);
         });
-        constexpr int tb = tab::kTermBegin[PI.type], te = tab::kTermBegin[PI.type + 1];
         if constexpr (NEED_X) {
-          float v1[n1];
-          static_for<n1>([&](auto c) { v1[c] = 0.f; });
-          static_for<te - tb>([&](auto ti) {
-            constexpr tab::Term T = tab::kTerms[tb + ti];
-            v1[T.b1] = fmaf(T.c * y[o2 + T.b2], gp[T.a], v1[T.b1]);
+          // x_bar[b1] += sum_terms c y[b2] (w g[a])
+          float gw[na];
+          static_for<na>([&](auto a) {
+            constexpr int ra = Cfg::row(p, a);
+            gw[a] = w * gv[ra];
           });
-          static_for<n1>([&](auto c) { xb[o1 + c] = fmaf(w, v1[c], xb[o1 + c]); });
+          static_for<te - tb>([&](auto ti) {
+            constexpr int tt = tb + ti;
+            constexpr tab::Term T = tab::kTerms[tt];
+            xb[o1 + T.b1] = fmaf(EP::template cy<tt, o2 + T.b2>(rec), gw[T.a], xb[o1 + T.b1]);
+          });
         }
         if constexpr (NEED_POS) {
+          // v2[b2] = sum_terms c g[a] x[b1]  (VJP_2(g, x), unweighted)
           float v2[n2];
-          static_for<n2>([&](auto c) { v2[c] = 0.f; });
           static_for<te - tb>([&](auto ti) {
-            constexpr tab::Term T = tab::kTerms[tb + ti];
-            v2[T.b2] = fmaf(T.c * gp[T.a], xv[o1 + T.b1], v2[T.b2]);
+            constexpr int tt = tb + ti;
+            constexpr tab::Term T = tab::kTerms[tt];
+            constexpr int ra = Cfg::row(p, T.a);
+            constexpr float ac = T.c < 0.f ? -T.c : T.c;
+            float cx;
+            if constexpr (ac == 1.f) cx = xv[o1 + T.b1];
+            else if constexpr (EP::kCXReg) cx = cxr[CXt::term[tt]];
+            else cx = ac * xv[o1 + T.b1];
+            if constexpr (T.c < 0.f) cx = -cx;
+            if constexpr (T.f2) v2[T.b2] = gv[ra] * cx;
+            else v2[T.b2] = fmaf(gv[ra], cx, v2[T.b2]);
           });
           float wbar = 0.f;
           static_for<n2>([&](auto c) {
             yb[o2 + c] = fmaf(w, v2[c], yb[o2 + c]);
-            wbar = fmaf(v2[c], y[o2 + c], wbar);
+            wbar = fmaf(v2[c], rec[o2 + c], wbar);
           });
+          float dw = 0.f;
           static_for<kNB>([&](auto b) {
-            float wb;
-            if constexpr (WREG) wb = Wr[b * P + p];
-            else wb = act ? W[(size_t)(b * P + p) * C + kk] : 0.f;
-            rho[b] = fmaf(wbar, wb, rho[b]);
+            constexpr int bb = b;
+            dw = fmaf(rec[NY + kNB + bb], FC_WGET(bb, p), dw);
           });
+          sacc = fmaf(wbar, dw, sacc);
         }
       });
       if constexpr (NEED_POS) {
-        // wave reduction of the per-lane partials, then park them in LDS
-        float* dst = red + ((size_t)wv * kWave + j) * NRED;
+        float* dst = part + ((size_t)(wv * kWave + j) * NRED) * 4 + (lane >> 4);
         static_for<NE>([&](auto c) {
-          float t = yb[c];
-#pragma unroll
-          for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o);
-          if (lane == 0) dst[c] = t;
+          const float t = row_sum16(yb[c]);
+          if ((lane & 15) == 0) dst[c * 4] = t;
         });
-        static_for<kNB>([&](auto b) {
-          float t = rho[b];
-#pragma unroll
-          for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o);
-          if (lane == 0) dst[NE + b] = t;
-        });
+        const float t = row_sum16(sacc);
+        if ((lane & 15) == 0) dst[NE * 4] = t;
       }
     }
     __syncthreads();
@@ -285,8 +373,11 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
         float tot[NRED];
         static_for<NRED>([&](auto i) { tot[i] = 0.f; });
         for (int w2 = 0; w2 < NW; ++w2) {
-          const float* src = red + ((size_t)w2 * kWave + lane) * NRED;
-          static_for<NRED>([&](auto i) { tot[i] += src[i]; });
+          const float4* src = reinterpret_cast<const float4*>(part + ((size_t)(w2 * kWave + lane) * NRED) * 4);
+          static_for<NRED>([&](auto i) {
+            const float4 q = src[i];
+            tot[i] += (q.x + q.y) + (q.z + q.w);
+          });
         }
         float rx = pvx - pos[3 * u], ry = pvy - pos[3 * u + 1], rz = pvz - pos[3 * u + 2];
         if (shift) {
@@ -299,10 +390,7 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
         if (r > 0.f) {
           const float inv = 1.f / r;
           const float nx = rx * inv, ny = ry * inv, nz = rz * inv;
-          float R[kNB], dR[kNB];
-          radial<true>(r, rc, R, dR);
-          float srad = 0.f;
-          static_for<kNB>([&](auto b) { srad = fmaf(dR[b], tot[NE + b], srad); });
+          const float srad = tot[NE];
           float dy[3 * NE];
           direction_tensor_grads<LEDGE>(nx, ny, nz, dy);
           float gx = 0.f, gy = 0.f, gz = 0.f;
@@ -326,8 +414,10 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
       __syncthreads();
     }
   }
-  if (NEED_X && x_bar && act) {
-    float* xo = x_bar + (size_t)v * NIN * C + k;
+#undef FC_WGET
+  const size_t slot = (size_t)v * S + sl;
+  if (NEED_X && act) {
+    float* xo = x_out + slot * NIN * C + k;
     static_for<NIN>([&](auto c) { xo[(size_t)c * C] = xb[c]; });
   }
   if constexpr (NEED_POS) {
@@ -340,9 +430,9 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
         psum[i] = t;
       }
       if (lane == 0) {
-        pos_bar[3 * v] = psum[0];
-        pos_bar[3 * v + 1] = psum[1];
-        pos_bar[3 * v + 2] = psum[2];
+        p_out[3 * slot] = psum[0];
+        p_out[3 * slot + 1] = psum[1];
+        p_out[3 * slot + 2] = psum[2];
       }
     }
   }
@@ -352,20 +442,21 @@ template <int LIN, int LEDGE, int LOUT>
 void launch_vjp(const ConvArgs& a, hipStream_t st) {
   const bool nx = a.x_bar != nullptr, np = a.pos_bar != nullptr;
   const int nw = (a.C + kWave - 1) / kWave;
-  dim3 grid(a.N), block(nw * kWave);
+  const VjpWorkspace wsl(a.N, a.E, a.C, nrank(LIN), a.rbar);
+  float* xo = wsl.S == 1 ? a.x_bar : wsl.x_part;
+  float* po = wsl.S == 1 ? a.pos_bar : wsl.p_part;
+  dim3 grid(a.N, wsl.S), block(nw * kWave);
+  const size_t lds = VjpShape<LIN, LEDGE, LOUT>::lds_bytes(np ? nw : 0);
   if (nx && np)
-    hipLaunchKernelGGL((conv_vjp_sender_kernel<LIN, LEDGE, LOUT, true, true>), grid, block, 0, st, a.C,
-                       a.t_rowptr, a.t_edge, a.receiver, a.pos, a.shift, a.x, a.W, a.g, a.x_bar, a.pos_bar,
-                       a.rbar, a.rc);
+    hipLaunchKernelGGL((conv_vjp_sender_kernel<LIN, LEDGE, LOUT, true, true>), grid, block, lds, st, a.N, a.C,
+                       a.t_rowptr, a.t_edge, a.receiver, a.pos, a.shift, a.x, a.W, a.g, xo, po, wsl.rbar, a.rc);
   else if (nx)
-    hipLaunchKernelGGL((conv_vjp_sender_kernel<LIN, LEDGE, LOUT, true, false>), grid, block, 0, st, a.C,
-                       a.t_rowptr, a.t_edge, a.receiver, a.pos, a.shift, a.x, a.W, a.g, a.x_bar, a.pos_bar,
-                       a.rbar, a.rc);
+    hipLaunchKernelGGL((conv_vjp_sender_kernel<LIN, LEDGE, LOUT, true, false>), grid, block, lds, st, a.N, a.C,
+                       a.t_rowptr, a.t_edge, a.receiver, a.pos, a.shift, a.x, a.W, a.g, xo, po, wsl.rbar, a.rc);
   else
-    hipLaunchKernelGGL((conv_vjp_sender_kernel<LIN, LEDGE, LOUT, false, true>), grid, block, 0, st, a.C,
-                       a.t_rowptr, a.t_edge, a.receiver, a.pos, a.shift, a.x, a.W, a.g, a.x_bar, a.pos_bar,
-                       a.rbar, a.rc);
-  if (np) launch_vjp_receiver(a, st);
+    hipLaunchKernelGGL((conv_vjp_sender_kernel<LIN, LEDGE, LOUT, false, true>), grid, block, lds, st, a.N, a.C,
+                       a.t_rowptr, a.t_edge, a.receiver, a.pos, a.shift, a.x, a.W, a.g, xo, po, wsl.rbar, a.rc);
+  launch_vjp_combine(a, wsl, nrank(LIN), st);
 }
 
 }  // namespace fc

@@ -257,6 +257,49 @@ def cfloat(fr: Fraction) -> str:
     return f"float({fr.numerator}.0 / {fr.denominator}.0)"
 
 
+def first_flags(terms):
+    """Per term: is it the first term of its path writing output a, VJP-1 slot
+    b1, VJP-2 slot b2?  Lets the kernels start each sum with a product."""
+    seen_a, seen_1, seen_2, out = set(), set(), set(), []
+    for (a, b1, b2, c) in terms:
+        out.append((a not in seen_a, b1 not in seen_1, b2 not in seen_2))
+        seen_a.add(a)
+        seen_1.add(b1)
+        seen_2.add(b2)
+    return out
+
+
+def product_table(paths, tables, cfg, operand):
+    """Distinct products |c| * v[g] used by the paths of one configuration.
+
+    ``operand`` 2: v = edge tensor y, g = l2^2 + b2; the list starts with
+    (g, 1) for every edge-tensor row, so y itself is its first entries.
+    ``operand`` 1: v = node features x, g = l1^2 + b1; only |c| != 1 entries.
+    Returns the list of (g, |c|) and, for every term of every path type, its
+    index in the list (-1 when the path type is not part of the
+    configuration, or for operand 1 when |c| = 1).
+    """
+    l_in, l_edge, l_out = cfg
+    used = {p for p in paths if p[0] <= l_in and p[1] <= l_edge and p[2] <= l_out}
+    keys, index = [], {}
+    if operand == 2:
+        for g in range((l_edge + 1) ** 2):
+            index[(g, Fraction(1))] = len(keys)
+            keys.append((g, Fraction(1)))
+    term_idx = []
+    for p in paths:
+        for (a, b1, b2, c) in tables[p]:
+            if p not in used or (operand == 1 and abs(c) == 1):
+                term_idx.append(-1)
+                continue
+            key = (p[1] * p[1] + b2, abs(c)) if operand == 2 else (p[0] * p[0] + b1, abs(c))
+            if key not in index:
+                index[key] = len(keys)
+                keys.append(key)
+            term_idx.append(index[key])
+    return keys, term_idx
+
+
 def emit(path: str, max_rank=MAX_RANK) -> None:
     paths, tables, tpoly = build_tables(max_rank)
     lines = []
@@ -271,7 +314,9 @@ def emit(path: str, max_rank=MAX_RANK) -> None:
     w("")
     w(f"inline constexpr int kMaxRank = {max_rank};")
     w("")
-    w("struct Term { int a, b1, b2; float c; };")
+    w("// f_a(x, y) = sum over terms c * x[b1] * y[b2]; fa/f1/f2 mark the first term of")
+    w("// the path that writes output a / VJP-1 slot b1 / VJP-2 slot b2")
+    w("struct Term { int a, b1, b2; float c; bool fa, f1, f2; };")
     w("struct Mono { int ex, ey, ez; float c; };")
     w("")
     w("// coupling path types (l1, l2 -> L), natural parity, lexicographic")
@@ -282,15 +327,20 @@ def emit(path: str, max_rank=MAX_RANK) -> None:
     begins, allterms = [], []
     for p in paths:
         begins.append(len(allterms))
-        allterms.extend(tables[p])
+        for t, f in zip(tables[p], first_flags(tables[p])):
+            allterms.append(t + f)
     begins.append(len(allterms))
     w("inline constexpr int kTermBegin[] = {" + ", ".join(map(str, begins)) + "};")
     w(f"inline constexpr int kNumTerms = {len(allterms)};")
     w("inline constexpr Term kTerms[] = {")
+    k = 0
     for p in paths:
         w(f"  // ({p[0]},{p[1]})->{p[2]}: {len(tables[p])} terms")
-        for (a, b1, b2, c) in tables[p]:
-            w(f"  {{{a}, {b1}, {b2}, {cfloat(c)}}},")
+        for _ in tables[p]:
+            (a, b1, b2, c, fa, f1, f2) = allterms[k]
+            k += 1
+            bl = lambda v: "true" if v else "false"
+            w(f"  {{{a}, {b1}, {b2}, {cfloat(c)}, {bl(fa)}, {bl(f1)}, {bl(f2)}}},")
     w("};")
     w("")
     w("// direction tensors T_l(n): stored component c of rank l is")
@@ -307,6 +357,21 @@ def emit(path: str, max_rank=MAX_RANK) -> None:
     for (ex, ey, ez, c) in allmono:
         w(f"  {{{ex}, {ey}, {ez}, {cfloat(c)}}},")
     w("};")
+    w("")
+    w("// per configuration (l_in, l_edge, l_out): the distinct products |c| * y[g]")
+    w("// (CY, g = l2^2 + b2; y itself first) and |c| * x[g] with |c| != 1")
+    w("// (CX, g = l1^2 + b1) its paths use, and for every term the product's index")
+    w("template <int LIN, int LEDGE, int LOUT> struct CY;")
+    w("template <int LIN, int LEDGE, int LOUT> struct CX;")
+    for cfg in conv_configs():
+        for name, op in (("CY", 2), ("CX", 1)):
+            keys, tidx = product_table(paths, tables, cfg, op)
+            w(f"template <> struct {name}<{cfg[0]}, {cfg[1]}, {cfg[2]}> {{")
+            w(f"  static constexpr int n = {len(keys)};")
+            w("  static constexpr int g[] = {" + ", ".join(str(g) for g, _ in keys or [(0, 0)]) + "};")
+            w("  static constexpr float c[] = {" + ", ".join(cfloat(c) for _, c in keys or [(0, Fraction(0))]) + "};")
+            w("  static constexpr int term[] = {" + ", ".join(map(str, tidx)) + "};")
+            w("};")
     w("")
     w("}  // namespace tab")
     w("}  // namespace fc")

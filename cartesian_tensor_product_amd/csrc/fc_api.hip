@@ -10,6 +10,7 @@
 #include "../../include/flashcart.h"
 #include "fc_conv.h"
 #include "fc_graph.h"
+#include "fc_ladder.h"
 
 namespace {
 
@@ -101,6 +102,22 @@ fc::ConvArgs make_args(const fc_conv_desc* d, const fc_graph* g, const float* po
   return a;
 }
 
+
+fc_status ladder_plan(const fc_ladder_desc* d, fc::LadderPlan* p) {
+  if (!d) return fail(FC_ERR_INVALID_ARGUMENT, "ladder descriptor is NULL");
+  if (d->n_nodes < 1) return fail(FC_ERR_INVALID_ARGUMENT, "ladder: n_nodes must be >= 1");
+  if (d->channels < 32 || d->channels > 512 || d->channels % 32 != 0)
+    return fail(FC_ERR_UNSUPPORTED, "ladder: channels must be a multiple of 32 in [32, 512] (got %d)", d->channels);
+  if (d->variant != FC_LADDER_FULL && d->variant != FC_LADDER_PATH_REDUCED)
+    return fail(FC_ERR_INVALID_ARGUMENT, "ladder: unknown variant %d", d->variant);
+  if (d->order < 1) return fail(FC_ERR_INVALID_ARGUMENT, "ladder: order must be >= 1");
+  if (d->order > 8) return fail(FC_ERR_UNSUPPORTED, "ladder: order above 8 is not supported");
+  if (d->l_a < 0 || d->l_prod < 0 || d->l_out < 0) return fail(FC_ERR_INVALID_ARGUMENT, "ladder: negative rank");
+  if (d->l_a != d->l_prod || d->l_prod < 1 || d->l_prod > 4 || d->l_out > d->l_prod)
+    return fail(FC_ERR_UNSUPPORTED, "ladder: this build needs l_a == l_prod in 1..4 and l_out <= l_prod");
+  *p = fc::LadderPlan{d->n_nodes, d->channels, d->l_a, d->l_prod, d->l_out, d->order, d->variant};
+  return FC_OK;
+}
 
 }  // namespace
 
@@ -242,27 +259,50 @@ fc_status fc_edge_conv_vjp_vjp(const fc_conv_desc* d, const fc_graph* g, const f
 }
 
 fc_status fc_ladder_layout(const fc_ladder_desc* d, size_t* n_weight_floats, size_t* n_saved_floats) {
-  (void)d; (void)n_weight_floats; (void)n_saved_floats;
-  return fail(FC_ERR_UNSUPPORTED, "ladder is not implemented in this build");
+  fc::LadderPlan p;
+  if (fc_status s = ladder_plan(d, &p)) return s;
+  if (n_weight_floats) *n_weight_floats = p.weight_floats();
+  if (n_saved_floats) *n_saved_floats = p.saved_floats();
+  return ok();
 }
 
 size_t fc_ladder_workspace_bytes(const fc_ladder_desc* d, int32_t op) {
-  (void)d; (void)op;
-  return 0;
+  fc::LadderPlan p;
+  if (ladder_plan(d, &p) != FC_OK) return 0;
+  return sizeof(float) * (op == 1 ? p.vjp_ws_floats() : p.fwd_ws_floats());
 }
 
 fc_status fc_node_ladder_fwd(const fc_ladder_desc* d, const float* A, const float* weights, float* z,
                              float* saved, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  (void)d; (void)A; (void)weights; (void)z; (void)saved; (void)workspace; (void)workspace_bytes; (void)stream;
-  return fail(FC_ERR_UNSUPPORTED, "ladder is not implemented in this build");
+  fc::LadderPlan p;
+  if (fc_status s = ladder_plan(d, &p)) return s;
+  if (!A || !weights || !z) return fail(FC_ERR_INVALID_ARGUMENT, "ladder forward: NULL A, weights or z");
+  if (misaligned(A, 4) || misaligned(weights, 4) || misaligned(z, 4) || misaligned(saved, 4) ||
+      misaligned(workspace, 4))
+    return fail(FC_ERR_INVALID_ARGUMENT, "ladder forward: arrays must be 4-byte aligned");
+  const size_t need = fc_ladder_workspace_bytes(d, 0);
+  if (!workspace || workspace_bytes < need)
+    return fail(FC_ERR_WORKSPACE, "ladder forward needs %zu workspace bytes", need);
+  fc::ladder_forward(p, A, weights, z, saved, static_cast<float*>(workspace), stream);
+  return check_launch("ladder forward");
 }
 
 fc_status fc_node_ladder_vjp(const fc_ladder_desc* d, const float* A, const float* weights, const float* saved,
                              const float* g_z, float* A_grad, float* weights_grad, void* workspace,
                              size_t workspace_bytes, hipStream_t stream) {
-  (void)d; (void)A; (void)weights; (void)saved; (void)g_z; (void)A_grad; (void)weights_grad; (void)workspace;
-  (void)workspace_bytes; (void)stream;
-  return fail(FC_ERR_UNSUPPORTED, "ladder is not implemented in this build");
+  fc::LadderPlan p;
+  if (fc_status s = ladder_plan(d, &p)) return s;
+  if (!A || !weights || !g_z || !A_grad)
+    return fail(FC_ERR_INVALID_ARGUMENT, "ladder VJP: NULL A, weights, g_z or A_grad");
+  if (p.order > 1 && !saved) return fail(FC_ERR_INVALID_ARGUMENT, "ladder VJP: saved states required (order > 1)");
+  if (misaligned(A, 4) || misaligned(weights, 4) || misaligned(saved, 4) || misaligned(g_z, 4) ||
+      misaligned(A_grad, 4) || misaligned(weights_grad, 4) || misaligned(workspace, 4))
+    return fail(FC_ERR_INVALID_ARGUMENT, "ladder VJP: arrays must be 4-byte aligned");
+  const size_t need = fc_ladder_workspace_bytes(d, 1);
+  if (!workspace || workspace_bytes < need)
+    return fail(FC_ERR_WORKSPACE, "ladder VJP needs %zu workspace bytes", need);
+  fc::ladder_vjp(p, A, weights, saved, g_z, A_grad, weights_grad, static_cast<float*>(workspace), stream);
+  return check_launch("ladder VJP");
 }
 
 }  // extern "C"

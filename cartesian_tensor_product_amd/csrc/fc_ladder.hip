@@ -1,0 +1,780 @@
+// Node-local correlation ladder for gfx950 (FlashCart paper §5 Eq. 2 and
+// App. E "Path-reduced products").
+//
+// Full ladder, per step q >= 2: a VALU kernel forms the channel-diagonal
+// products B_eta = (phi^{q-1}_{l1} (x) A_{l2})_L for every path eta of the
+// step (lanes = channels, coalesced) into a GEMM-ready buffer, one row
+// (u, component) per output rank and columns (eta, channel); the path/channel
+// mixing phi^q_L = B_L W^q_L^T then runs on the matrix cores as a grouped
+// FP32 MFMA GEMM whose epilogue also adds phi^q into the output sum z.
+// Path-reduced products: every step runs in registers per (node, channel)
+// with the per-path weights a^q, and one grouped GEMM applies the final
+// rank-wise maps W_L.
+//
+// Supported shapes: l_a = l_prod in 1..4, 0 <= l_out <= l_prod, 1 <= order
+// <= 8, C a multiple of 32 in [32, 512].
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+
+#include "fc_common.h"
+#include "fc_gemm.h"
+#include "fc_ladder.h"
+
+namespace fc {
+
+// ------------------------------------------------------- product kernels --
+
+// One step of the full ladder: B rows for all paths of ConvCfg<LP, LA, LQ>.
+// phi [N][phi_rows][C], A [N][a_rows][C]; B block of rank L starts at
+// N * off(L) * C floats, row (u (2L+1) + a), column (eta_L C + k).
+template <int LP, int LA, int LQ>
+__global__ __launch_bounds__(kWave) void ladder_prod_kernel(int N, int C, const float* __restrict__ phi,
+                                                            int phi_rows, const float* __restrict__ A,
+                                                            int a_rows, float* __restrict__ B) {
+  using Cfg = ConvCfg<LP, LA, LQ>;
+  const int u = blockIdx.x;
+  const int k = blockIdx.y * kWave + threadIdx.x;
+  if (k >= C) return;
+  float x[nrank(LP)], y[nrank(LA)];
+  static_for<nrank(LP)>([&](auto c) { x[c] = phi[((size_t)u * phi_rows + c) * C + k]; });
+  static_for<nrank(LA)>([&](auto c) { y[c] = A[((size_t)u * a_rows + c) * C + k]; });
+  static_for<Cfg::P>([&](auto pc) {
+    constexpr int p = pc;
+    constexpr PathInfo PI = Cfg::paths[p];
+    constexpr int na = ncomp(PI.L), o1 = rank_off(PI.l1), o2 = rank_off(PI.l2);
+    constexpr int tb = tab::kTermBegin[PI.type], te = tab::kTermBegin[PI.type + 1];
+    float t[na];
+    static_for<te - tb>([&](auto ti) {
+      constexpr tab::Term T = tab::kTerms[tb + ti];
+      float xy = x[o1 + T.b1] * y[o2 + T.b2];
+      if constexpr (T.fa) t[T.a] = T.c * xy;
+      else t[T.a] = fmaf(T.c, xy, t[T.a]);
+    });
+    float* dst = B + (size_t)N * PI.off * C + (size_t)PI.eta * C + k;
+    const size_t ld = (size_t)PI.PL * C;
+    static_for<na>([&](auto a) { dst[((size_t)u * na + a) * ld] = t[a]; });
+  });
+}
+
+// One step of the path-reduced products in registers:
+// new_L = P_L^{-1/2} sum_{eta -> L} a[eta][k] (x_{l1} (x) y_{l2})_L.
+template <int LP, int LA, int LQ>
+__device__ __forceinline__ void reduced_step(const float* x, const float* y, const float* __restrict__ aw, int C,
+                                             int k, float* nw) {
+  using Cfg = ConvCfg<LP, LA, LQ>;
+  static_for<nrank(LQ)>([&](auto c) { nw[c] = 0.f; });
+  static_for<Cfg::P>([&](auto pc) {
+    constexpr int p = pc;
+    constexpr PathInfo PI = Cfg::paths[p];
+    constexpr int na = ncomp(PI.L), o1 = rank_off(PI.l1), o2 = rank_off(PI.l2), oL = rank_off(PI.L);
+    constexpr int tb = tab::kTermBegin[PI.type], te = tab::kTermBegin[PI.type + 1];
+    const float a = aw[(size_t)p * C + k];
+    float t[na];
+    static_for<te - tb>([&](auto ti) {
+      constexpr tab::Term T = tab::kTerms[tb + ti];
+      float xy = x[o1 + T.b1] * y[o2 + T.b2];
+      if constexpr (T.fa) t[T.a] = T.c * xy;
+      else t[T.a] = fmaf(T.c, xy, t[T.a]);
+    });
+    static_for<na>([&](auto c) { nw[oL + c] = fmaf(a, t[c], nw[oL + c]); });
+  });
+  static_for<LQ + 1>([&](auto Lc) {
+    constexpr int L = Lc;
+    if constexpr (Cfg::count_L(L) > 1) {
+      const float s = 1.0f / sqrtf(float(Cfg::count_L(L)));
+      static_for<ncomp(L)>([&](auto c) { nw[rank_off(L) + c] *= s; });
+    }
+  });
+}
+
+// All steps of the path-reduced ladder for one (node, channel); writes the
+// step sum S = sum_q Pi_{<= LO} phi^q and (saved != nullptr) phi^q for
+// q = 1 .. order-1.
+template <int LP, int LO>
+__global__ __launch_bounds__(kWave) void ladder_reduced_kernel(int N, int C, int order, const float* __restrict__ A,
+                                                               const float* __restrict__ a1,
+                                                               const float* __restrict__ amid, int pmid,
+                                                               const float* __restrict__ alast,
+                                                               float* __restrict__ S, float* __restrict__ saved) {
+  constexpr int NP = nrank(LP), NO = nrank(LO);
+  const int u = blockIdx.x;
+  const int k = blockIdx.y * kWave + threadIdx.x;
+  if (k >= C) return;
+  float y[NP], x[NP], s[NO];
+  static_for<NP>([&](auto c) { y[c] = A[((size_t)u * NP + c) * C + k]; });
+  // phi^1 = a1[l] * A_l for l <= l_1 (l_1 = LO when order == 1)
+  const int l1max = order == 1 ? LO : LP;
+  static_for<LP + 1>([&](auto lc) {
+    constexpr int l = lc;
+    const float a = l <= l1max ? a1[(size_t)l * C + k] : 0.f;
+    static_for<ncomp(l)>([&](auto c) { x[rank_off(l) + c] = a * y[rank_off(l) + c]; });
+  });
+  static_for<NO>([&](auto c) { s[c] = x[c]; });
+  if (saved && order > 1) static_for<NP>([&](auto c) { saved[((size_t)u * NP + c) * C + k] = x[c]; });
+  for (int q = 2; q < order; ++q) {
+    float nw[NP];
+    reduced_step<LP, LP, LP>(x, y, amid + (size_t)(q - 2) * pmid * C, C, k, nw);
+    static_for<NO>([&](auto c) { s[c] += nw[c]; });
+    static_for<NP>([&](auto c) { x[c] = nw[c]; });
+    if (saved)
+      static_for<NP>([&](auto c) { saved[(((size_t)(q - 1) * N + u) * NP + c) * C + k] = x[c]; });
+  }
+  if (order > 1) {
+    float nw[NO];
+    reduced_step<LP, LP, LO>(x, y, alast, C, k, nw);
+    static_for<NO>([&](auto c) { s[c] += nw[c]; });
+  }
+  static_for<NO>([&](auto c) { S[((size_t)u * NO + c) * C + k] = s[c]; });
+}
+
+
+// ------------------------------------------------------------ VJP kernels --
+
+// Full ladder, reverse of one product step: given Bbar (layout of B),
+// phi^{q-1} and A, write G^{q-1} = g_z (ranks <= l_out) + sum_eta VJP1 and
+// add sum_eta VJP2 into A_bar.
+template <int LP, int LA, int LQ>
+__global__ __launch_bounds__(kWave) void ladder_prod_vjp_kernel(int N, int C, const float* __restrict__ Bbar,
+                                                                const float* __restrict__ phi,
+                                                                const float* __restrict__ A,
+                                                                const float* __restrict__ gz, int gz_rows,
+                                                                float* __restrict__ Gprev,
+                                                                float* __restrict__ Abar) {
+  using Cfg = ConvCfg<LP, LA, LQ>;
+  constexpr int NP = nrank(LP), NA = nrank(LA);
+  const int u = blockIdx.x;
+  const int k = blockIdx.y * kWave + threadIdx.x;
+  if (k >= C) return;
+  float x[NP], y[NA], gp[NP], ab[NA];
+  static_for<NP>([&](auto c) {
+    x[c] = phi[((size_t)u * NP + c) * C + k];
+    gp[c] = c < gz_rows ? gz[((size_t)u * gz_rows + c) * C + k] : 0.f;
+  });
+  static_for<NA>([&](auto c) {
+    y[c] = A[((size_t)u * NA + c) * C + k];
+    ab[c] = 0.f;
+  });
+  static_for<Cfg::P>([&](auto pc) {
+    constexpr int p = pc;
+    constexpr PathInfo PI = Cfg::paths[p];
+    constexpr int na = ncomp(PI.L), o1 = rank_off(PI.l1), o2 = rank_off(PI.l2);
+    constexpr int tb = tab::kTermBegin[PI.type], te = tab::kTermBegin[PI.type + 1];
+    const float* src = Bbar + (size_t)N * PI.off * C + (size_t)PI.eta * C + k;
+    const size_t ld = (size_t)PI.PL * C;
+    float bb[na];
+    static_for<na>([&](auto a) { bb[a] = src[((size_t)u * na + a) * ld]; });
+    static_for<te - tb>([&](auto ti) {
+      constexpr tab::Term T = tab::kTerms[tb + ti];
+      const float cb = T.c * bb[T.a];
+      gp[o1 + T.b1] = fmaf(cb, y[o2 + T.b2], gp[o1 + T.b1]);
+      ab[o2 + T.b2] = fmaf(cb, x[o1 + T.b1], ab[o2 + T.b2]);
+    });
+  });
+  static_for<NP>([&](auto c) { Gprev[((size_t)u * NP + c) * C + k] = gp[c]; });
+  static_for<NA>([&](auto c) { Abar[((size_t)u * NA + c) * C + k] += ab[c]; });
+}
+
+// Path-reduced ladder, reverse of step q for a tile of nodes: G = dL/dphi^q
+// (ranks <= LQ), phi^{q-1}, A and Sbar = dL/dS.  Writes
+//   G^{q-1} = Sbar (ranks <= l_out) + sum_eta s_eta a_eta VJP1(G_L, A_l2)
+// (or, for q == 2, applies phi^1 = a1 A directly: A_bar += a1 G^1 and the
+// a1 gradient), adds sum_eta s_eta a_eta VJP2(G_L, phi_l1) into A_bar and
+// writes per-block partial gradients of a^q (and a1) summed over the tile.
+template <int LP, int LA, int LQ, bool FIRST>
+__global__ __launch_bounds__(kWave) void ladder_reduced_vjp_kernel(
+    int N, int C, int ntile, const float* __restrict__ G, int g_rows, const float* __restrict__ phi,
+    const float* __restrict__ A, const float* __restrict__ Sbar, int s_rows, const float* __restrict__ aw,
+    const float* __restrict__ a1, float* __restrict__ Gprev, float* __restrict__ Abar,
+    float* __restrict__ apart, float* __restrict__ a1part) {
+  using Cfg = ConvCfg<LP, LA, LQ>;
+  constexpr int NP = nrank(LP), NA = nrank(LA), NQ = nrank(LQ);
+  const int k = blockIdx.y * kWave + threadIdx.x;
+  if (k >= C) return;
+  float aacc[Cfg::P], a1acc[LP + 1];
+  static_for<Cfg::P>([&](auto i) { aacc[i] = 0.f; });
+  static_for<LP + 1>([&](auto i) { a1acc[i] = 0.f; });
+  float aq[Cfg::P];
+  static_for<Cfg::P>([&](auto i) { aq[i] = aw[(size_t)i * C + k]; });
+  const int u0 = blockIdx.x * ntile, u1 = min(N, u0 + ntile);
+  for (int u = u0; u < u1; ++u) {
+    float g[NQ], x[NP], y[NA], gp[NP], ab[NA];
+    static_for<NQ>([&](auto c) { g[c] = c < g_rows ? G[((size_t)u * g_rows + c) * C + k] : 0.f; });
+    static_for<NP>([&](auto c) {
+      x[c] = phi[((size_t)u * NP + c) * C + k];
+      gp[c] = c < s_rows ? Sbar[((size_t)u * s_rows + c) * C + k] : 0.f;
+    });
+    static_for<NA>([&](auto c) {
+      y[c] = A[((size_t)u * NA + c) * C + k];
+      ab[c] = 0.f;
+    });
+    static_for<Cfg::P>([&](auto pc) {
+      constexpr int p = pc;
+      constexpr PathInfo PI = Cfg::paths[p];
+      constexpr int na = ncomp(PI.L), o1 = rank_off(PI.l1), o2 = rank_off(PI.l2), oL = rank_off(PI.L);
+      constexpr int tb = tab::kTermBegin[PI.type], te = tab::kTermBegin[PI.type + 1];
+      const float sc = 1.0f / sqrtf(float(PI.PL));
+      float t[na];
+      static_for<te - tb>([&](auto ti) {
+        constexpr tab::Term T = tab::kTerms[tb + ti];
+        const float xy = x[o1 + T.b1] * y[o2 + T.b2];
+        if constexpr (T.fa) t[T.a] = T.c * xy;
+        else t[T.a] = fmaf(T.c, xy, t[T.a]);
+      });
+      float dot = 0.f;
+      static_for<na>([&](auto a) { dot = fmaf(g[oL + a], t[a], dot); });
+      aacc[p] = fmaf(sc, dot, aacc[p]);
+      const float sa = sc * aq[p];
+      static_for<te - tb>([&](auto ti) {
+        constexpr tab::Term T = tab::kTerms[tb + ti];
+        const float cg = (T.c * sa) * g[oL + T.a];
+        gp[o1 + T.b1] = fmaf(cg, y[o2 + T.b2], gp[o1 + T.b1]);
+        ab[o2 + T.b2] = fmaf(cg, x[o1 + T.b1], ab[o2 + T.b2]);
+      });
+    });
+    if constexpr (FIRST) {
+      // phi^1_l = a1[l] A_l
+      static_for<LP + 1>([&](auto lc) {
+        constexpr int l = lc;
+        const float a = a1[(size_t)l * C + k];
+        float d = 0.f;
+        static_for<ncomp(l)>([&](auto c) {
+          ab[rank_off(l) + c] = fmaf(a, gp[rank_off(l) + c], ab[rank_off(l) + c]);
+          d = fmaf(gp[rank_off(l) + c], y[rank_off(l) + c], d);
+        });
+        a1acc[l] += d;
+      });
+    } else {
+      static_for<NP>([&](auto c) { Gprev[((size_t)u * NP + c) * C + k] = gp[c]; });
+    }
+    static_for<NA>([&](auto c) { Abar[((size_t)u * NA + c) * C + k] += ab[c]; });
+  }
+  static_for<Cfg::P>([&](auto i) { apart[((size_t)blockIdx.x * Cfg::P + i) * C + k] = aacc[i]; });
+  if constexpr (FIRST)
+    static_for<LP + 1>([&](auto i) { a1part[((size_t)blockIdx.x * (LP + 1) + i) * C + k] = a1acc[i]; });
+}
+
+// Path-reduced ladder of order 1: z = W (a1 A), so A_bar = a1 Sbar and the
+// a1 gradient is <Sbar, A> per rank (ranks <= l_out only).
+__global__ __launch_bounds__(kWave) void ladder_reduced_first_kernel(int N, int C, int ntile, int lout, int a_rows,
+                                                                     const float* __restrict__ Sbar,
+                                                                     const float* __restrict__ A,
+                                                                     const float* __restrict__ a1,
+                                                                     float* __restrict__ Abar,
+                                                                     float* __restrict__ a1part) {
+  const int k = blockIdx.y * kWave + threadIdx.x;
+  if (k >= C) return;
+  const int ro = (lout + 1) * (lout + 1);
+  float acc[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+  const int u0 = blockIdx.x * ntile, u1 = min(N, u0 + ntile);
+  for (int u = u0; u < u1; ++u)
+    for (int c = 0; c < ro; ++c) {
+      int l = 0;
+      while ((l + 1) * (l + 1) <= c) ++l;
+      const float sb = Sbar[((size_t)u * ro + c) * C + k];
+      Abar[((size_t)u * a_rows + c) * C + k] += a1[(size_t)l * C + k] * sb;
+      acc[l] = fmaf(sb, A[((size_t)u * a_rows + c) * C + k], acc[l]);
+    }
+  for (int l = 0; l <= lout; ++l) a1part[((size_t)blockIdx.x * (lout + 1) + l) * C + k] = acc[l];
+}
+
+// out[i] = sum_b part[b][i], fixed order.
+__global__ __launch_bounds__(256) void block_sum_kernel(int nblk, int n, const float* __restrict__ part,
+                                                        float* __restrict__ out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float t = 0.f;
+  for (int b = 0; b < nblk; ++b) t += part[(size_t)b * n + i];
+  out[i] = t;
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(size_t n, float* __restrict__ p) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.f;
+}
+
+// ----------------------------------------------------------------- host --
+
+namespace {
+
+int nr(int l) { return (l + 1) * (l + 1); }
+
+}  // namespace
+
+int LadderPlan::lq(int q) const {
+  if (q == 1) return order == 1 ? lout : lprod;
+  return q == order ? lout : lprod;
+}
+
+int LadderPlan::paths(int q, int L) const {
+  int c = 0;
+  for (int l1 = 0; l1 <= lq(q - 1); ++l1)
+    for (int l2 = 0; l2 <= la; ++l2)
+      if (admissible(l1, l2, L)) ++c;
+  return c;
+}
+
+int LadderPlan::paths(int q) const {
+  int c = 0;
+  for (int L = 0; L <= lq(q); ++L) c += paths(q, L);
+  return c;
+}
+
+// rows of the product buffer of step q: sum_L (2L+1) P_{q,L}
+int LadderPlan::prod_rows(int q) const {
+  int r = 0;
+  for (int L = 0; L <= lq(q); ++L) r += (2 * L + 1) * paths(q, L);
+  return r;
+}
+
+size_t LadderPlan::weight_floats() const {
+  const size_t C2 = (size_t)C * C;
+  size_t n = 0;
+  if (variant == 0) {
+    n += (size_t)(lq(1) + 1) * C2;
+    for (int q = 2; q <= order; ++q)
+      for (int L = 0; L <= lq(q); ++L) n += (size_t)paths(q, L) * C2;
+  } else {
+    n += (size_t)(lq(1) + 1) * C;
+    for (int q = 2; q <= order; ++q) n += (size_t)paths(q) * C;
+    n += (size_t)(lout + 1) * C2;
+  }
+  return n;
+}
+
+size_t LadderPlan::saved_floats() const { return (size_t)(order - 1) * N * nr(lprod) * C; }
+
+size_t LadderPlan::state_floats() const { return (size_t)N * nr(lprod) * C; }
+
+size_t LadderPlan::fwd_ws_floats() const {
+  if (variant == 1) return (size_t)N * nr(lout) * C;
+  size_t b = 0;
+  for (int q = 2; q <= order; ++q) b = std::max(b, (size_t)N * prod_rows(q) * C);
+  return b + 2 * state_floats();
+}
+
+namespace {
+constexpr int kNTile = 16;          // nodes per block in the path-reduced reverse kernels
+constexpr int kSplitTarget = 512;   // blocks per split-K weight-gradient GEMM
+}  // namespace
+
+size_t LadderPlan::vjp_ws_floats() const {
+  const size_t st = state_floats();
+  const size_t C2 = (size_t)C * C;
+  size_t part = 0;
+  if (variant == 0) {
+    size_t b = 0;
+    for (int q = 2; q <= order; ++q) {
+      b = std::max(b, (size_t)N * prod_rows(q) * C);
+      size_t g = 0;
+      for (int L = 0; L <= lq(q); ++L) {
+        const int P = paths(q, L);
+        if (P) g += (size_t)gemm_ksplit(C, P * C, N * (2 * L + 1), kSplitTarget) * P * C2;
+      }
+      part = std::max(part, g);
+    }
+    size_t g1 = 0;
+    for (int l = 0; l <= lq(1); ++l) g1 += (size_t)gemm_ksplit(C, C, N * (2 * l + 1), kSplitTarget) * C2;
+    part = std::max(part, g1);
+    return 2 * b + 2 * st + part;
+  }
+  const int nblk = (N + kNTile - 1) / kNTile;
+  int pmax = 0;
+  for (int q = 2; q <= order; ++q) pmax = std::max(pmax, paths(q));
+  for (int L = 0; L <= lout; ++L) part += (size_t)gemm_ksplit(C, C, N * (2 * L + 1), kSplitTarget) * C2;
+  return 2 * (size_t)N * nr(lout) * C + 2 * st + (size_t)nblk * (pmax + lprod + 1) * C + part;
+}
+
+// offset (floats) of W^q_L (full) in the flat weights
+size_t LadderPlan::w_full(int q, int L) const {
+  const size_t C2 = (size_t)C * C;
+  if (q == 1) return (size_t)L * C2;
+  size_t n = (size_t)(lq(1) + 1) * C2;
+  for (int qq = 2; qq <= order; ++qq)
+    for (int LL = 0; LL <= lq(qq); ++LL) {
+      if (qq == q && LL == L) return n;
+      n += (size_t)paths(qq, LL) * C2;
+    }
+  return n;
+}
+
+size_t LadderPlan::w_a(int q) const {
+  if (q == 1) return 0;
+  size_t n = (size_t)(lq(1) + 1) * C;
+  for (int qq = 2; qq < q; ++qq) n += (size_t)paths(qq) * C;
+  return n;
+}
+
+size_t LadderPlan::w_final(int L) const {
+  size_t n = w_a(order + 1);
+  return n + (size_t)L * C * C;
+}
+
+namespace {
+
+template <int LP, int LQ>
+void launch_prod(const LadderPlan& p, const float* phi, const float* A, float* B, hipStream_t st) {
+  dim3 grid(p.N, (p.C + kWave - 1) / kWave);
+  hipLaunchKernelGGL((ladder_prod_kernel<LP, LP, LQ>), grid, dim3(kWave), 0, st, p.N, p.C, phi, nr(p.lprod), A,
+                     nr(p.la), B);
+}
+
+template <int LP>
+void dispatch_prod(const LadderPlan& p, int LQ, const float* phi, const float* A, float* B, hipStream_t st) {
+  switch (LQ) {
+    case 0: launch_prod<LP, 0>(p, phi, A, B, st); break;
+    case 1: if constexpr (LP >= 1) launch_prod<LP, 1>(p, phi, A, B, st); break;
+    case 2: if constexpr (LP >= 2) launch_prod<LP, 2>(p, phi, A, B, st); break;
+    case 3: if constexpr (LP >= 3) launch_prod<LP, 3>(p, phi, A, B, st); break;
+    case 4: if constexpr (LP >= 4) launch_prod<LP, 4>(p, phi, A, B, st); break;
+  }
+}
+
+void prod(const LadderPlan& p, int LQ, const float* phi, const float* A, float* B, hipStream_t st) {
+  switch (p.lprod) {
+    case 1: dispatch_prod<1>(p, LQ, phi, A, B, st); break;
+    case 2: dispatch_prod<2>(p, LQ, phi, A, B, st); break;
+    case 3: dispatch_prod<3>(p, LQ, phi, A, B, st); break;
+    case 4: dispatch_prod<4>(p, LQ, phi, A, B, st); break;
+  }
+}
+
+template <int LP, int LO>
+void launch_reduced(const LadderPlan& p, const float* A, const float* w, float* S, float* saved, hipStream_t st) {
+  dim3 grid(p.N, (p.C + kWave - 1) / kWave);
+  const float* amid = w + p.w_a(2);
+  const int pmid = p.order > 2 ? p.paths(2) : 0;
+  const float* alast = w + p.w_a(p.order);
+  hipLaunchKernelGGL((ladder_reduced_kernel<LP, LO>), grid, dim3(kWave), 0, st, p.N, p.C, p.order, A, w, amid,
+                     pmid, alast, S, saved);
+}
+
+template <int LP>
+void dispatch_reduced(const LadderPlan& p, const float* A, const float* w, float* S, float* saved, hipStream_t st) {
+  switch (p.lout) {
+    case 0: launch_reduced<LP, 0>(p, A, w, S, saved, st); break;
+    case 1: if constexpr (LP >= 1) launch_reduced<LP, 1>(p, A, w, S, saved, st); break;
+    case 2: if constexpr (LP >= 2) launch_reduced<LP, 2>(p, A, w, S, saved, st); break;
+    case 3: if constexpr (LP >= 3) launch_reduced<LP, 3>(p, A, w, S, saved, st); break;
+    case 4: if constexpr (LP >= 4) launch_reduced<LP, 4>(p, A, w, S, saved, st); break;
+  }
+}
+
+// Rank block L of a node array [N][rows][C] as a matrix: row (u, c), column k.
+GView node_view(const float* base, int rows, int L, int C) {
+  return GView{base + (size_t)L * L * C, 2 * L + 1, (long long)rows * C, (long long)C, 1, 1, 0, 0, 0};
+}
+// Its transpose: element (k, m) with m = (u, c) the reduction index.
+GView node_view_t(const float* base, int rows, int L, int C) {
+  return GView{base + (size_t)L * L * C, 1, 1, 0, 2 * L + 1, (long long)rows * C, (long long)C, 0, 0};
+}
+GOut node_out(float* base, int rows, int L, int C, int acc) {
+  if (!base) return no_out();
+  return GOut{base + (size_t)L * L * C, 2 * L + 1, (long long)rows * C, (long long)C, acc, 0};
+}
+
+}  // namespace
+
+void ladder_forward(const LadderPlan& p, const float* A, const float* w, float* z, float* saved, float* ws,
+                    hipStream_t st) {
+  const int C = p.C;
+  const int ra = nr(p.la), rp = nr(p.lprod), ro = nr(p.lout);
+  if (p.variant == 1) {
+    float* S = ws;
+    switch (p.lprod) {
+      case 1: dispatch_reduced<1>(p, A, w, S, saved, st); break;
+      case 2: dispatch_reduced<2>(p, A, w, S, saved, st); break;
+      case 3: dispatch_reduced<3>(p, A, w, S, saved, st); break;
+      case 4: dispatch_reduced<4>(p, A, w, S, saved, st); break;
+    }
+    GemmGroup g{};
+    for (int L = 0; L <= p.lout; ++L) {
+      GemmProblem& pr = g.prob[g.count++];
+      pr.M = p.N * (2 * L + 1);
+      pr.N = C;
+      pr.K = C;
+      pr.alpha = 1.f;
+      pr.A = node_view(S, ro, L, C);
+      pr.Bt = plain_view(w + p.w_final(L), C);
+      pr.C = node_out(z, ro, L, C, 0);
+      pr.C2 = no_out();
+    }
+    gemm_group(g, st);
+    return;
+  }
+  // full ladder
+  float* B = ws;
+  size_t bmax = 0;
+  for (int q = 2; q <= p.order; ++q) bmax = std::max(bmax, (size_t)p.N * p.prod_rows(q) * C);
+  float* tmp[2] = {ws + bmax, ws + bmax + p.state_floats()};
+  auto state = [&](int q) -> float* {
+    if (q >= p.order) return nullptr;
+    return saved ? saved + (size_t)(q - 1) * p.state_floats() : tmp[q % 2];
+  };
+  // step 1: phi^1_l = W1_l A_l
+  {
+    GemmGroup g{};
+    for (int L = 0; L <= p.lq(1); ++L) {
+      GemmProblem& pr = g.prob[g.count++];
+      pr.M = p.N * (2 * L + 1);
+      pr.N = C;
+      pr.K = C;
+      pr.alpha = 1.f;
+      pr.A = node_view(A, ra, L, C);
+      pr.Bt = plain_view(w + p.w_full(1, L), C);
+      pr.C = node_out(state(1), rp, L, C, 0);
+      pr.C2 = L <= p.lout ? node_out(z, ro, L, C, 0) : no_out();
+    }
+    gemm_group(g, st);
+  }
+  for (int q = 2; q <= p.order; ++q) {
+    const float* phi = state(q - 1);
+    prod(p, p.lq(q), phi, A, B, st);
+    GemmGroup g{};
+    size_t boff = 0;
+    for (int L = 0; L <= p.lq(q); ++L) {
+      const int P = p.paths(q, L);
+      if (P == 0) continue;
+      GemmProblem& pr = g.prob[g.count++];
+      pr.M = p.N * (2 * L + 1);
+      pr.N = C;
+      pr.K = P * C;
+      pr.alpha = 1.f;
+      pr.A = plain_view(B + boff, (long long)P * C);
+      pr.Bt = plain_view(w + p.w_full(q, L), (long long)P * C);
+      pr.C = node_out(state(q), rp, L, C, 0);
+      pr.C2 = L <= p.lout ? node_out(z, ro, L, C, 1) : no_out();
+      boff += (size_t)p.N * (2 * L + 1) * P * C;
+    }
+    gemm_group(g, st);
+  }
+}
+
+
+namespace {
+
+template <int LP, int LQ>
+void launch_prod_vjp(const LadderPlan& p, const float* Bbar, const float* phi, const float* A, const float* gz,
+                     float* Gprev, float* Abar, hipStream_t st) {
+  dim3 grid(p.N, (p.C + kWave - 1) / kWave);
+  hipLaunchKernelGGL((ladder_prod_vjp_kernel<LP, LP, LQ>), grid, dim3(kWave), 0, st, p.N, p.C, Bbar, phi, A, gz,
+                     nr(p.lout), Gprev, Abar);
+}
+
+template <int LP, int LQ>
+void launch_red_vjp(const LadderPlan& p, bool first, const float* G, int g_rows, const float* phi, const float* A,
+                    const float* Sbar, const float* aw, const float* a1, float* Gprev, float* Abar, float* apart,
+                    float* a1part, hipStream_t st) {
+  dim3 grid((p.N + kNTile - 1) / kNTile, (p.C + kWave - 1) / kWave);
+  if (first)
+    hipLaunchKernelGGL((ladder_reduced_vjp_kernel<LP, LP, LQ, true>), grid, dim3(kWave), 0, st, p.N, p.C, kNTile,
+                       G, g_rows, phi, A, Sbar, nr(p.lout), aw, a1, Gprev, Abar, apart, a1part);
+  else
+    hipLaunchKernelGGL((ladder_reduced_vjp_kernel<LP, LP, LQ, false>), grid, dim3(kWave), 0, st, p.N, p.C, kNTile,
+                       G, g_rows, phi, A, Sbar, nr(p.lout), aw, a1, Gprev, Abar, apart, a1part);
+}
+
+// dispatch (lprod, LQ) -> F<LP, LQ>
+template <template <int, int> class F, class... Args>
+void by_ranks(int lp, int lq, Args&&... args) {
+#define FC_LQ(LPV)                                                   \
+  switch (lq) {                                                      \
+    case 0: F<LPV, 0>::run(args...); break;                          \
+    case 1: if constexpr (LPV >= 1) F<LPV, 1>::run(args...); break;  \
+    case 2: if constexpr (LPV >= 2) F<LPV, 2>::run(args...); break;  \
+    case 3: if constexpr (LPV >= 3) F<LPV, 3>::run(args...); break;  \
+    case 4: if constexpr (LPV >= 4) F<LPV, 4>::run(args...); break;  \
+  }
+  switch (lp) {
+    case 1: FC_LQ(1) break;
+    case 2: FC_LQ(2) break;
+    case 3: FC_LQ(3) break;
+    case 4: FC_LQ(4) break;
+  }
+#undef FC_LQ
+}
+
+template <int LP, int LQ>
+struct ProdVjp {
+  template <class... A>
+  static void run(A&&... a) { launch_prod_vjp<LP, LQ>(a...); }
+};
+template <int LP, int LQ>
+struct RedVjp {
+  template <class... A>
+  static void run(A&&... a) { launch_red_vjp<LP, LQ>(a...); }
+};
+
+void fill_zero(float* p, size_t n, hipStream_t st) {
+  if (n) hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, n, p);
+}
+
+void block_sum(int nblk, int n, const float* part, float* out, hipStream_t st) {
+  hipLaunchKernelGGL(block_sum_kernel, dim3((n + 255) / 256), dim3(256), 0, st, nblk, n, part, out);
+}
+
+// element (n, k) = W[k * ld + n]: the weight matrix used untransposed
+GView weight_t(const float* W, long long ld) { return GView{W, 1, 1, 0, 1, ld, 0, 0, 0}; }
+
+}  // namespace
+
+void ladder_vjp(const LadderPlan& p, const float* A, const float* w, const float* saved, const float* gz,
+                float* A_grad, float* w_grad, float* ws, hipStream_t st) {
+  const int C = p.C;
+  const int ra = nr(p.la), rp = nr(p.lprod), ro = nr(p.lout);
+  const size_t stf = p.state_floats();
+  fill_zero(A_grad, (size_t)p.N * ra * C, st);
+  if (p.variant == 0) {
+    size_t bmax = 0;
+    for (int q = 2; q <= p.order; ++q) bmax = std::max(bmax, (size_t)p.N * p.prod_rows(q) * C);
+    float* B = ws;
+    float* Bbar = B + bmax;
+    float* Gbuf[2] = {Bbar + bmax, Bbar + bmax + stf};
+    float* part = Gbuf[1] + stf;
+    const float* G = gz;
+    int grows = ro;
+    for (int q = p.order; q >= 2; --q) {
+      const float* phi = saved + (size_t)(q - 2) * stf;
+      prod(p, p.lq(q), phi, A, B, st);
+      GemmGroup g{};
+      size_t boff = 0, poff = 0;
+      for (int L = 0; L <= p.lq(q); ++L) {
+        const int P = p.paths(q, L);
+        if (P == 0) continue;
+        const long long PC = (long long)P * C;
+        const float* W = w + p.w_full(q, L);
+        GemmProblem& b = g.prob[g.count++];
+        b.M = p.N * (2 * L + 1);
+        b.N = (int)PC;
+        b.K = C;
+        b.alpha = 1.f;
+        b.A = node_view(G, grows, L, C);
+        b.Bt = weight_t(W, PC);
+        b.C = plain_out(Bbar + boff, PC, 0);
+        b.C2 = no_out();
+        if (w_grad) {
+          GemmProblem& d = g.prob[g.count++];
+          d.M = C;
+          d.N = (int)PC;
+          d.K = p.N * (2 * L + 1);
+          d.alpha = 1.f;
+          d.A = node_view_t(G, grows, L, C);
+          d.Bt = weight_t(B + boff, PC);
+          d.C = plain_out(w_grad + p.w_full(q, L), PC, 0);
+          d.C2 = no_out();
+          d.ksplit = gemm_ksplit(d.M, d.N, d.K, kSplitTarget);
+          d.part = part + poff;
+          poff += (size_t)d.ksplit * d.M * d.N;
+        }
+        boff += (size_t)p.N * (2 * L + 1) * PC;
+      }
+      gemm_group(g, st);
+      float* Gprev = Gbuf[q % 2];
+      by_ranks<ProdVjp>(p.lprod, p.lq(q), p, (const float*)Bbar, phi, A, gz, Gprev, A_grad, st);
+      G = Gprev;
+      grows = rp;
+    }
+    GemmGroup g{};
+    size_t poff = 0;
+    for (int l = 0; l <= p.lq(1); ++l) {
+      const float* W1 = w + p.w_full(1, l);
+      GemmProblem& b = g.prob[g.count++];
+      b.M = p.N * (2 * l + 1);
+      b.N = C;
+      b.K = C;
+      b.alpha = 1.f;
+      b.A = node_view(G, grows, l, C);
+      b.Bt = weight_t(W1, C);
+      b.C = node_out(A_grad, ra, l, C, 1);
+      b.C2 = no_out();
+      if (w_grad) {
+        GemmProblem& d = g.prob[g.count++];
+        d.M = C;
+        d.N = C;
+        d.K = p.N * (2 * l + 1);
+        d.alpha = 1.f;
+        d.A = node_view_t(G, grows, l, C);
+        d.Bt = node_view_t(A, ra, l, C);
+        d.C = plain_out(w_grad + p.w_full(1, l), C, 0);
+        d.C2 = no_out();
+        d.ksplit = gemm_ksplit(d.M, d.N, d.K, kSplitTarget);
+        d.part = part + poff;
+        poff += (size_t)d.ksplit * d.M * d.N;
+      }
+    }
+    gemm_group(g, st);
+    return;
+  }
+  // path-reduced
+  float* S = ws;
+  float* Sbar = S + (size_t)p.N * ro * C;
+  float* Gbuf[2] = {Sbar + (size_t)p.N * ro * C, Sbar + (size_t)p.N * ro * C + stf};
+  const int nblk = (p.N + kNTile - 1) / kNTile;
+  int pmax = 0;
+  for (int q = 2; q <= p.order; ++q) pmax = std::max(pmax, p.paths(q));
+  float* apart = Gbuf[1] + stf;
+  float* a1part = apart + (size_t)nblk * pmax * C;
+  float* part = a1part + (size_t)nblk * (p.lprod + 1) * C;
+  switch (p.lprod) {
+    case 1: dispatch_reduced<1>(p, A, w, S, nullptr, st); break;
+    case 2: dispatch_reduced<2>(p, A, w, S, nullptr, st); break;
+    case 3: dispatch_reduced<3>(p, A, w, S, nullptr, st); break;
+    case 4: dispatch_reduced<4>(p, A, w, S, nullptr, st); break;
+  }
+  {
+    GemmGroup g{};
+    size_t poff = 0;
+    for (int L = 0; L <= p.lout; ++L) {
+      const float* WL = w + p.w_final(L);
+      GemmProblem& b = g.prob[g.count++];
+      b.M = p.N * (2 * L + 1);
+      b.N = C;
+      b.K = C;
+      b.alpha = 1.f;
+      b.A = node_view(gz, ro, L, C);
+      b.Bt = weight_t(WL, C);
+      b.C = node_out(Sbar, ro, L, C, 0);
+      b.C2 = no_out();
+      if (w_grad) {
+        GemmProblem& d = g.prob[g.count++];
+        d.M = C;
+        d.N = C;
+        d.K = p.N * (2 * L + 1);
+        d.alpha = 1.f;
+        d.A = node_view_t(gz, ro, L, C);
+        d.Bt = node_view_t(S, ro, L, C);
+        d.C = plain_out(w_grad + p.w_final(L), C, 0);
+        d.C2 = no_out();
+        d.ksplit = gemm_ksplit(d.M, d.N, d.K, kSplitTarget);
+        d.part = part + poff;
+        poff += (size_t)d.ksplit * d.M * d.N;
+      }
+    }
+    gemm_group(g, st);
+  }
+  const float* a1 = w + p.w_a(1);
+  if (p.order == 1) {
+    dim3 grid(nblk, (C + kWave - 1) / kWave);
+    hipLaunchKernelGGL(ladder_reduced_first_kernel, grid, dim3(kWave), 0, st, p.N, C, kNTile, p.lout, ra,
+                       (const float*)Sbar, A, a1, A_grad, a1part);
+    if (w_grad) block_sum(nblk, (p.lout + 1) * C, a1part, w_grad + p.w_a(1), st);
+    return;
+  }
+  const float* G = Sbar;
+  int grows = ro;
+  for (int q = p.order; q >= 2; --q) {
+    const float* phi = saved + (size_t)(q - 2) * stf;
+    float* Gprev = Gbuf[q % 2];
+    by_ranks<RedVjp>(p.lprod, p.lq(q), p, q == 2, G, grows, phi, A, (const float*)Sbar,
+                     (const float*)(w + p.w_a(q)), a1, Gprev, A_grad, apart, a1part, st);
+    if (w_grad) {
+      block_sum(nblk, p.paths(q) * C, apart, w_grad + p.w_a(q), st);
+      if (q == 2) block_sum(nblk, (p.lprod + 1) * C, a1part, w_grad + p.w_a(1), st);
+    }
+    G = Gprev;
+    grows = rp;
+  }
+}
+
+}  // namespace fc

@@ -207,6 +207,72 @@ __device__ __forceinline__ void radial(float r, float rc, float* R, float* dR) {
   }
 }
 
+// R_b, R'_b and R''_b (second derivatives for the VJP-of-VJP).
+__device__ __forceinline__ void radial2(float r, float rc, float* R, float* dR, float* d2R) {
+  if (!(r < rc) || !(r > 0.f)) {
+#pragma unroll
+    for (int b = 0; b < kNB; ++b) R[b] = dR[b] = d2R[b] = 0.f;
+    return;
+  }
+  const float a = kPi / rc;
+  float s1, c1;
+  sincosf(a * r, &s1, &c1);
+  const float ir = 1.f / r;
+  const float e = 0.5f * (1.f + c1), de = -0.5f * a * s1, d2e = -0.5f * a * a * c1;
+  float sp = 0.f, s = s1, cp = 1.f, c = c1;
+#pragma unroll
+  for (int b = 0; b < kNB; ++b) {
+    const float k = float(b + 1) * a;
+    const float h = s * ir;
+    const float dh = (k * c - h) * ir;                               // (k cos)/r - s/r^2
+    const float d2h = (-k * k * s - 2.f * dh) * ir;                  // -k^2 s/r - 2k cos/r^2 + 2 s/r^3
+    R[b] = h * e;
+    dR[b] = dh * e + h * de;
+    d2R[b] = d2h * e + 2.f * dh * de + h * d2e;
+    const float sn = 2.f * c1 * s - sp, cn = 2.f * c1 * c - cp;
+    sp = s;
+    s = sn;
+    cp = c;
+    c = cn;
+  }
+}
+
+// Gradient g = dG/dn and Hessian H (xx, yy, zz, xy, xz, yz) of the
+// polynomial G(n) = sum_c coef[c] y_c(n) over all ranks <= LE.
+template <int LE>
+__device__ __forceinline__ void direction_contract_d2(const float* coef, float nx, float ny, float nz, float* g,
+                                                      float* H) {
+  float px[LE + 1], py[LE + 1], pz[LE + 1];
+  px[0] = py[0] = pz[0] = 1.f;
+  static_for<LE>([&](auto i) {
+    px[i + 1] = px[i] * nx;
+    py[i + 1] = py[i] * ny;
+    pz[i + 1] = pz[i] * nz;
+  });
+  auto P = [&](int a, int b, int c) -> float { return (a < 0 || b < 0 || c < 0) ? 0.f : px[a] * py[b] * pz[c]; };
+  g[0] = g[1] = g[2] = 0.f;
+  for (int i = 0; i < 6; ++i) H[i] = 0.f;
+  static_for<nrank(LE)>([&](auto gi) {
+    constexpr int gg = gi;
+    constexpr int mb = tab::kMonoBegin[gg], me = tab::kMonoBegin[gg + 1];
+    const float cf = coef[gg];
+    static_for<me - mb>([&](auto mi) {
+      constexpr tab::Mono m = tab::kMono[mb + mi];
+      constexpr int a = m.ex, b = m.ey, c = m.ez;
+      const float w = cf * m.c;
+      if constexpr (a > 0) g[0] = fmaf(w * a, P(a - 1, b, c), g[0]);
+      if constexpr (b > 0) g[1] = fmaf(w * b, P(a, b - 1, c), g[1]);
+      if constexpr (c > 0) g[2] = fmaf(w * c, P(a, b, c - 1), g[2]);
+      if constexpr (a > 1) H[0] = fmaf(w * (a * (a - 1)), P(a - 2, b, c), H[0]);
+      if constexpr (b > 1) H[1] = fmaf(w * (b * (b - 1)), P(a, b - 2, c), H[1]);
+      if constexpr (c > 1) H[2] = fmaf(w * (c * (c - 1)), P(a, b, c - 2), H[2]);
+      if constexpr (a > 0 && b > 0) H[3] = fmaf(w * (a * b), P(a - 1, b - 1, c), H[3]);
+      if constexpr (a > 0 && c > 0) H[4] = fmaf(w * (a * c), P(a - 1, b, c - 1), H[4]);
+      if constexpr (b > 0 && c > 0) H[5] = fmaf(w * (b * c), P(a, b - 1, c - 1), H[5]);
+    });
+  });
+}
+
 // ------------------------------------------------------------- misc device
 __device__ __forceinline__ int uniform_int(int v) { return __builtin_amdgcn_readfirstlane(v); }
 

@@ -13,6 +13,10 @@ struct ConvArgs {
   const int *rowptr, *sender, *receiver, *t_rowptr, *t_edge;
   const float *pos, *shift, *x, *W, *g;
   float *z, *x_bar, *pos_bar, *rbar;
+  // VJP-of-VJP: cotangents of x_bar / pos_bar (nullable) and the g_hat output;
+  // x_hat and pos_hat reuse x_bar and pos_bar, the per-edge term reuses rbar
+  const float *v_x, *v_pos;
+  float* g_hat;
 };
 
 #include "generated/fc_conv_configs.h"
@@ -20,7 +24,9 @@ struct ConvArgs {
 bool conv_supported(int l_in, int l_edge, int l_out);
 // op 0: forward (needs rowptr, sender, pos, shift, x, W, z);
 // op 1: VJP (additionally receiver, t_rowptr, t_edge, g, rbar, and x_bar
-//       and/or pos_bar).
+//       and/or pos_bar);
+// op 2: VJP-of-VJP (g, v_x / v_pos, and g_hat, x_bar (= x_hat) and/or
+//       pos_bar (= pos_hat)).
 // Outgoing edges of a sender are split into S contiguous slices (about 32
 // edges each on average) processed by separate blocks.
 inline int vjp_slices(int N, int E) {

@@ -1,0 +1,475 @@
+// VJP-of-VJP of the edge convolution for gfx950 (FlashCart paper, App. C
+// Eq. C2, carried through the direction tensors and radial weights).
+//
+// For s = <v_x, x_bar> + <v_pos, pos_bar>, with per edge e = (u <- v)
+//   dv_e = v_pos[v] - v_pos[u],   ydot = J_y dv_e,   wdot = w'(r) (r_hat . dv_e),
+// the outputs are
+//   g_hat[u]  = sum_{e into u} w (f(v_x, y) + f(x, ydot)) + wdot f(x, y)
+//   x_hat[v]  = sum_{e out of v} VJP1(g_u, w ydot + wdot y)
+//   pos_hat  += q_e at v, -= q_e at u, with q_e = d psi_e / d r_e,
+//   q_e = S1 r_hat + J_y^T (Ya + nd Yd) + H_y[Yb] dv + S2 nd r_hat + S3 (dv - nd r_hat) / r,
+// nd = r_hat . dv, and per-edge channel sums (beta = VJP2(g, x),
+// alpha = VJP2(g, v_x)):
+//   Ya = sum w alpha, Yb = sum w beta, Yd = sum w' beta,
+//   S1 = sum w' (<alpha, y> + <beta, ydot>), S2 = sum w'' <beta, y>,
+//   S3 = sum w' <beta, y>.
+// g_hat runs receiver-sorted like the forward; x_hat and q_e run
+// sender-sorted like the VJP and share its slice/combine passes.
+#pragma once
+
+#include "fc_conv_kernels.h"
+
+namespace fc {
+
+// Geometry of one edge: unit direction, length, dv and its derived terms.
+struct VVGeo {
+  float nx, ny, nz, r, inv, dvx, dvy, dvz, nd, ndx, ndy, ndz;   // ndot = (dv - nd n) / r
+};
+
+__device__ __forceinline__ VVGeo vv_geo(float rx, float ry, float rz, float dvx, float dvy, float dvz) {
+  VVGeo G;
+  G.r = sqrtf(rx * rx + ry * ry + rz * rz);
+  G.inv = G.r > 0.f ? 1.f / G.r : 0.f;
+  G.nx = rx * G.inv;
+  G.ny = ry * G.inv;
+  G.nz = rz * G.inv;
+  G.dvx = dvx;
+  G.dvy = dvy;
+  G.dvz = dvz;
+  G.nd = G.nx * dvx + G.ny * dvy + G.nz * dvz;
+  G.ndx = (dvx - G.nd * G.nx) * G.inv;
+  G.ndy = (dvy - G.nd * G.ny) * G.inv;
+  G.ndz = (dvz - G.nd * G.nz) * G.inv;
+  return G;
+}
+
+// y and ydot = J_y dv (= grad_n y . ndot) for all ranks <= LE.
+template <int LE>
+__device__ __forceinline__ void vv_tensors(const VVGeo& G, float* y, float* yd) {
+  constexpr int NE = nrank(LE);
+  direction_tensors<LE>(G.nx, G.ny, G.nz, y);
+  float dy[3 * NE];
+  direction_tensor_grads<LE>(G.nx, G.ny, G.nz, dy);
+  static_for<NE>([&](auto c) { yd[c] = dy[3 * c] * G.ndx + dy[3 * c + 1] * G.ndy + dy[3 * c + 2] * G.ndz; });
+}
+
+// ------------------------------------------------------------ g_hat pass --
+template <int LIN, int LEDGE, int LOUT, int LLO, int LHI, bool HAS_VX>
+__global__ __launch_bounds__(kWave) void conv_vv_recv_kernel(
+    int N, int C, const int* __restrict__ rowptr, const int* __restrict__ sender, const float* __restrict__ pos,
+    const float* __restrict__ shift, const float* __restrict__ x, const float* __restrict__ W,
+    const float* __restrict__ v_x, const float* __restrict__ v_pos, float* __restrict__ g_hat, float rc) {
+  using Cfg = ConvCfg<LIN, LEDGE, LOUT>;
+  using G = Group<Cfg, LLO, LHI>;
+  constexpr int NIN = Cfg::NIN, NE = Cfg::NE, P = Cfg::P, NOUT = Cfg::NOUT;
+  constexpr int REC = 2 * NE + 2 * kNB + 2;   // y, ydot, R, R', nd, sender
+  constexpr bool WREG = 2 * kNB * G::NP <= 128;
+  __shared__ float geo[kWave * REC];
+
+  const int u = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int k = blockIdx.y * kWave + lane;
+  const bool act = k < C;
+  const int kk = act ? k : 0;
+  const int voff = kk * 4;
+  const auto xr = make_rsrc(x, (uint32_t)((size_t)N * NIN * C * 4));
+  const auto vr = make_rsrc(HAS_VX ? v_x : x, (uint32_t)((size_t)N * NIN * C * 4));
+
+  float Wr[WREG ? kNB * G::NP : 1];
+  if constexpr (WREG) {
+    static_for<kNB * G::NP>([&](auto i) {
+      constexpr int b = i / G::NP, p = i % G::NP;
+      Wr[i] = W[(size_t)(b * P + G::p0 + p) * C + kk];
+    });
+  }
+  float acc[G::NR];
+  static_for<G::NR>([&](auto i) { acc[i] = 0.f; });
+
+  const int e0 = rowptr[u], e1 = rowptr[u + 1];
+  const float pux = pos[3 * u], puy = pos[3 * u + 1], puz = pos[3 * u + 2];
+  const float vux = v_pos ? v_pos[3 * u] : 0.f, vuy = v_pos ? v_pos[3 * u + 1] : 0.f,
+              vuz = v_pos ? v_pos[3 * u + 2] : 0.f;
+  for (int base = e0; base < e1; base += kWave) {
+    const int cnt = min(kWave, e1 - base);
+    if (lane < cnt) {
+      const int e = base + lane;
+      const int s = sender[e];
+      float rx = pos[3 * s] - pux, ry = pos[3 * s + 1] - puy, rz = pos[3 * s + 2] - puz;
+      if (shift) {
+        rx += shift[3 * e];
+        ry += shift[3 * e + 1];
+        rz += shift[3 * e + 2];
+      }
+      float dvx = 0.f, dvy = 0.f, dvz = 0.f;
+      if (v_pos) {
+        dvx = v_pos[3 * s] - vux;
+        dvy = v_pos[3 * s + 1] - vuy;
+        dvz = v_pos[3 * s + 2] - vuz;
+      }
+      const VVGeo Gm = vv_geo(rx, ry, rz, dvx, dvy, dvz);
+      float y[NE], yd[NE], R[kNB], dR[kNB];
+      vv_tensors<LEDGE>(Gm, y, yd);
+      radial<true>(Gm.r, rc, R, dR);
+      float* rec = geo + lane * REC;
+      static_for<NE>([&](auto c) {
+        rec[c] = y[c];
+        rec[NE + c] = yd[c];
+      });
+      static_for<kNB>([&](auto b) {
+        rec[2 * NE + b] = R[b];
+        rec[2 * NE + kNB + b] = dR[b];
+      });
+      rec[2 * NE + 2 * kNB] = Gm.nd;
+      rec[2 * NE + 2 * kNB + 1] = __int_as_float(s);
+    }
+    __syncthreads();
+    for (int j = 0; j < cnt; ++j) {
+      const float* rec = geo + j * REC;
+      const int s = uniform_int(__float_as_int(rec[2 * NE + 2 * kNB + 1]));
+      const float nd = rec[2 * NE + 2 * kNB];
+      const int sbase = s * NIN * C * 4;
+      float xv[NIN], vx[HAS_VX ? NIN : 1];
+      static_for<NIN>([&](auto c) { xv[c] = buf_load(xr, voff, sbase + c * C * 4); });
+      if constexpr (HAS_VX) static_for<NIN>([&](auto c) { vx[c] = buf_load(vr, voff, sbase + c * C * 4); });
+      static_for<G::NP>([&](auto pi) {
+        constexpr int p = G::p0 + pi;
+        constexpr PathInfo PI = Cfg::paths[p];
+        constexpr int n1 = ncomp(PI.l1), o1 = rank_off(PI.l1), o2 = rank_off(PI.l2);
+        float w = 0.f, w1 = 0.f;
+        static_for<kNB>([&](auto b) {
+          constexpr int bb = b;
+          float wb;
+          if constexpr (WREG) wb = Wr[bb * G::NP + pi];
+          else wb = W[(size_t)(bb * P + p) * C + kk];
+          w = fmaf(rec[2 * NE + bb], wb, w);
+          w1 = fmaf(rec[2 * NE + kNB + bb], wb, w1);
+        });
+        const float wd = w1 * nd;
+        float xw[n1], xd[n1], vw[HAS_VX ? n1 : 1];
+        static_for<n1>([&](auto c) {
+          xw[c] = w * xv[o1 + c];
+          xd[c] = wd * xv[o1 + c];
+          if constexpr (HAS_VX) vw[c] = w * vx[o1 + c];
+        });
+        constexpr int tb = tab::kTermBegin[PI.type], te = tab::kTermBegin[PI.type + 1];
+        static_for<te - tb>([&](auto ti) {
+          constexpr tab::Term T = tab::kTerms[tb + ti];
+          constexpr int row = Cfg::row(p, T.a) - G::r0;
+          const float cy = T.c * rec[o2 + T.b2];
+          const float cyd = T.c * rec[NE + o2 + T.b2];
+          float a = fmaf(cy, xd[T.b1], acc[row]);
+          a = fmaf(cyd, xw[T.b1], a);
+          if constexpr (HAS_VX) a = fmaf(cy, vw[T.b1], a);
+          acc[row] = a;
+        });
+      });
+    }
+    __syncthreads();
+  }
+  if (act) {
+    float* zo = g_hat + (size_t)u * NOUT * C + k;
+    static_for<G::NR>([&](auto i) { zo[(size_t)(G::r0 + i) * C] = acc[i]; });
+  }
+}
+
+template <int LIN, int LEDGE, int LOUT, int LLO>
+void launch_vv_recv(const ConvArgs& a, hipStream_t st) {
+  using Cfg = ConvCfg<LIN, LEDGE, LOUT>;
+  constexpr int LHI = group_end<Cfg, LOUT>(LLO);
+  dim3 grid(a.N, (a.C + kWave - 1) / kWave);
+  if (a.v_x)
+    hipLaunchKernelGGL((conv_vv_recv_kernel<LIN, LEDGE, LOUT, LLO, LHI, true>), grid, dim3(kWave), 0, st, a.N,
+                       a.C, a.rowptr, a.sender, a.pos, a.shift, a.x, a.W, a.v_x, a.v_pos, a.g_hat, a.rc);
+  else
+    hipLaunchKernelGGL((conv_vv_recv_kernel<LIN, LEDGE, LOUT, LLO, LHI, false>), grid, dim3(kWave), 0, st, a.N,
+                       a.C, a.rowptr, a.sender, a.pos, a.shift, a.x, a.W, a.v_x, a.v_pos, a.g_hat, a.rc);
+  if constexpr (LHI < LOUT) launch_vv_recv<LIN, LEDGE, LOUT, LHI + 1>(a, st);
+}
+
+// ------------------------------------------------- x_hat / pos_hat pass --
+template <int LIN, int LEDGE, int LOUT, bool HAS_VX>
+struct VVShape {
+  static constexpr int NE = nrank(LEDGE);
+  // reductions: Yb, Yd, [Ya], S1, S2, S3
+  static constexpr int NRED = (HAS_VX ? 3 : 2) * NE + 3;
+  static constexpr int REC = 2 * NE + 3 * kNB + 2;   // y, ydot, R, R', R'', nd, receiver
+  static constexpr size_t lds_bytes(int nw) {
+    return sizeof(float) * ((size_t)kWave * REC + (size_t)nw * kWave * NRED * 4);
+  }
+};
+
+template <int LIN, int LEDGE, int LOUT, bool HAS_VX, bool NEED_X, bool NEED_POS>
+__global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vv_sender_kernel(
+    int N, int C, const int* __restrict__ t_rowptr, const int* __restrict__ t_edge,
+    const int* __restrict__ receiver, const float* __restrict__ pos, const float* __restrict__ shift,
+    const float* __restrict__ x, const float* __restrict__ W, const float* __restrict__ g,
+    const float* __restrict__ v_x, const float* __restrict__ v_pos, float* __restrict__ x_out,
+    float* __restrict__ p_out, float* __restrict__ qbar, float rc) {
+  using Cfg = ConvCfg<LIN, LEDGE, LOUT>;
+  using Sh = VVShape<LIN, LEDGE, LOUT, HAS_VX>;
+  constexpr int NIN = Cfg::NIN, NE = Cfg::NE, P = Cfg::P, NOUT = Cfg::NOUT;
+  constexpr int REC = Sh::REC, NRED = Sh::NRED;
+  constexpr int IYB = 0, IYD = NE, IYA = 2 * NE, IS = (HAS_VX ? 3 : 2) * NE;
+  constexpr bool WREG = kNB * P <= 96;
+  extern __shared__ float lds[];
+  float* geo = lds;
+  float* part = lds + kWave * REC;
+  const int NW = blockDim.x / kWave;
+
+  const int v = blockIdx.x;
+  const int S = gridDim.y, sl = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int wv = tid / kWave, lane = tid % kWave;
+  const int k = tid;
+  const bool act = k < C;
+  const int kk = act ? k : 0;
+  const int voff = kk * 4;
+  const auto gr = make_rsrc(g, (uint32_t)((size_t)N * NOUT * C * 4));
+
+  float Wr[WREG ? kNB * P : 1];
+  if constexpr (WREG) {
+    static_for<kNB * P>([&](auto i) { Wr[i] = act ? W[(size_t)i * C + kk] : 0.f; });
+  }
+#define FC_WGET(B, PP) (WREG ? Wr[WREG ? (B) * P + (PP) : 0] : (act ? W[(size_t)((B) * P + (PP)) * C + kk] : 0.f))
+  float xv[NIN], vx[HAS_VX ? NIN : 1];
+  {
+    const float* xs = x + (size_t)v * NIN * C + kk;
+    static_for<NIN>([&](auto c) { xv[c] = xs[(size_t)c * C]; });
+    if constexpr (HAS_VX) {
+      const float* vs = v_x + (size_t)v * NIN * C + kk;
+      static_for<NIN>([&](auto c) { vx[c] = vs[(size_t)c * C]; });
+    }
+  }
+  float xh[NIN];
+  static_for<NIN>([&](auto c) { xh[c] = 0.f; });
+  float psum[3] = {0.f, 0.f, 0.f};
+
+  const int v0 = t_rowptr[v], deg = t_rowptr[v + 1] - v0;
+  const int e0 = v0 + (int)(((long long)sl * deg) / S), e1 = v0 + (int)(((long long)(sl + 1) * deg) / S);
+  const float pvx = pos[3 * v], pvy = pos[3 * v + 1], pvz = pos[3 * v + 2];
+  const float vvx = v_pos ? v_pos[3 * v] : 0.f, vvy = v_pos ? v_pos[3 * v + 1] : 0.f,
+              vvz = v_pos ? v_pos[3 * v + 2] : 0.f;
+  auto edge_geo = [&](int e, int u) -> VVGeo {
+    float rx = pvx - pos[3 * u], ry = pvy - pos[3 * u + 1], rz = pvz - pos[3 * u + 2];
+    if (shift) {
+      rx += shift[3 * e];
+      ry += shift[3 * e + 1];
+      rz += shift[3 * e + 2];
+    }
+    float dvx = 0.f, dvy = 0.f, dvz = 0.f;
+    if (v_pos) {
+      dvx = vvx - v_pos[3 * u];
+      dvy = vvy - v_pos[3 * u + 1];
+      dvz = vvz - v_pos[3 * u + 2];
+    }
+    return vv_geo(rx, ry, rz, dvx, dvy, dvz);
+  };
+  for (int base = e0; base < e1; base += kWave) {
+    const int cnt = min(kWave, e1 - base);
+    if (wv == 0 && lane < cnt) {
+      const int e = t_edge[base + lane];
+      const int u = receiver[e];
+      const VVGeo Gm = edge_geo(e, u);
+      float y[NE], yd[NE], R[kNB], dR[kNB], d2R[kNB];
+      vv_tensors<LEDGE>(Gm, y, yd);
+      radial2(Gm.r, rc, R, dR, d2R);
+      float* rec = geo + lane * REC;
+      static_for<NE>([&](auto c) {
+        rec[c] = y[c];
+        rec[NE + c] = yd[c];
+      });
+      static_for<kNB>([&](auto b) {
+        rec[2 * NE + b] = R[b];
+        rec[2 * NE + kNB + b] = dR[b];
+        rec[2 * NE + 2 * kNB + b] = d2R[b];
+      });
+      rec[2 * NE + 3 * kNB] = Gm.nd;
+      rec[2 * NE + 3 * kNB + 1] = __int_as_float(u);
+    }
+    __syncthreads();
+    for (int j = 0; j < cnt; ++j) {
+      const float* rec = geo + j * REC;
+      const int u = uniform_int(__float_as_int(rec[2 * NE + 3 * kNB + 1]));
+      const float nd = rec[2 * NE + 3 * kNB];
+      const int ubase = u * NOUT * C * 4;
+      float gv[NOUT];
+      static_for<NOUT>([&](auto a) { gv[a] = buf_load(gr, voff, ubase + a * C * 4); });
+      float red[NRED];
+      static_for<NRED>([&](auto i) { red[i] = 0.f; });
+      static_for<P>([&](auto pc) {
+        constexpr int p = pc;
+        constexpr PathInfo PI = Cfg::paths[p];
+        constexpr int na = ncomp(PI.L), n2 = ncomp(PI.l2);
+        constexpr int o1 = rank_off(PI.l1), o2 = rank_off(PI.l2);
+        constexpr int tb = tab::kTermBegin[PI.type], te = tab::kTermBegin[PI.type + 1];
+        float w = 0.f, w1 = 0.f, w2 = 0.f;
+        static_for<kNB>([&](auto b) {
+          constexpr int bb = b;
+          const float wb = FC_WGET(bb, p);
+          w = fmaf(rec[2 * NE + bb], wb, w);
+          w1 = fmaf(rec[2 * NE + kNB + bb], wb, w1);
+          if constexpr (NEED_POS) w2 = fmaf(rec[2 * NE + 2 * kNB + bb], wb, w2);
+        });
+        const float wd = w1 * nd;
+        if constexpr (NEED_X) {
+          // x_hat[b1] += sum c g[a] (w ydot[b2] + wdot y[b2])
+          float gw[na], gd[na];
+          static_for<na>([&](auto a) {
+            constexpr int ra = Cfg::row(p, a);
+            gw[a] = w * gv[ra];
+            gd[a] = wd * gv[ra];
+          });
+          static_for<te - tb>([&](auto ti) {
+            constexpr tab::Term T = tab::kTerms[tb + ti];
+            float t = fmaf(T.c * rec[NE + o2 + T.b2], gw[T.a], xh[o1 + T.b1]);
+            xh[o1 + T.b1] = fmaf(T.c * rec[o2 + T.b2], gd[T.a], t);
+          });
+        }
+        if constexpr (NEED_POS) {
+          float be[n2], al[HAS_VX ? n2 : 1];
+          static_for<n2>([&](auto c) {
+            be[c] = 0.f;
+            if constexpr (HAS_VX) al[c] = 0.f;
+          });
+          static_for<te - tb>([&](auto ti) {
+            constexpr tab::Term T = tab::kTerms[tb + ti];
+            constexpr int ra = Cfg::row(p, T.a);
+            const float cg = T.c * gv[ra];
+            be[T.b2] = fmaf(cg, xv[o1 + T.b1], be[T.b2]);
+            if constexpr (HAS_VX) al[T.b2] = fmaf(cg, vx[o1 + T.b1], al[T.b2]);
+          });
+          float by = 0.f, bd = 0.f, ay = 0.f;
+          static_for<n2>([&](auto c) {
+            by = fmaf(be[c], rec[o2 + c], by);
+            bd = fmaf(be[c], rec[NE + o2 + c], bd);
+            red[IYB + o2 + c] = fmaf(w, be[c], red[IYB + o2 + c]);
+            red[IYD + o2 + c] = fmaf(w1, be[c], red[IYD + o2 + c]);
+            if constexpr (HAS_VX) {
+              ay = fmaf(al[c], rec[o2 + c], ay);
+              red[IYA + o2 + c] = fmaf(w, al[c], red[IYA + o2 + c]);
+            }
+          });
+          red[IS] = fmaf(w1, ay + bd, red[IS]);
+          red[IS + 1] = fmaf(w2, by, red[IS + 1]);
+          red[IS + 2] = fmaf(w1, by, red[IS + 2]);
+        }
+      });
+      if constexpr (NEED_POS) {
+        float* dst = part + ((size_t)(wv * kWave + j) * NRED) * 4 + (lane >> 4);
+        static_for<NRED>([&](auto i) {
+          const float t = row_sum16(red[i]);
+          if ((lane & 15) == 0) dst[i * 4] = t;
+        });
+      }
+    }
+    __syncthreads();
+    if constexpr (NEED_POS) {
+      if (wv == 0 && lane < cnt) {
+        const int e = t_edge[base + lane];
+        const int u = receiver[e];
+        float tot[NRED];
+        static_for<NRED>([&](auto i) { tot[i] = 0.f; });
+        for (int w2 = 0; w2 < NW; ++w2) {
+          const float4* src = reinterpret_cast<const float4*>(part + ((size_t)(w2 * kWave + lane) * NRED) * 4);
+          static_for<NRED>([&](auto i) {
+            const float4 q = src[i];
+            tot[i] += (q.x + q.y) + (q.z + q.w);
+          });
+        }
+        const VVGeo Gm = edge_geo(e, u);
+        float ox = 0.f, oy = 0.f, oz = 0.f;
+        if (Gm.r > 0.f) {
+          // J_y^T (Ya + nd Yd) = (gA - n (n.gA)) / r, gA = grad_n of (Ya + nd Yd) . y
+          float cA[NE];
+          static_for<NE>([&](auto c) {
+            cA[c] = Gm.nd * tot[IYD + c];
+            if constexpr (HAS_VX) cA[c] += tot[IYA + c];
+          });
+          float gA[3], HA[6], gB[3], HB[6];
+          direction_contract_d2<LEDGE>(cA, Gm.nx, Gm.ny, Gm.nz, gA, HA);
+          direction_contract_d2<LEDGE>(tot + IYB, Gm.nx, Gm.ny, Gm.nz, gB, HB);
+          const float ngA = Gm.nx * gA[0] + Gm.ny * gA[1] + Gm.nz * gA[2];
+          ox = (gA[0] - Gm.nx * ngA) * Gm.inv;
+          oy = (gA[1] - Gm.ny * ngA) * Gm.inv;
+          oz = (gA[2] - Gm.nz * ngA) * Gm.inv;
+          // H_y[Yb] dv = [gdot - ndot (n.g) - n (ndot.g + n.gdot)] / r - nd (g - n (n.g)) / r^2
+          const float gdx = HB[0] * Gm.ndx + HB[3] * Gm.ndy + HB[4] * Gm.ndz;
+          const float gdy = HB[3] * Gm.ndx + HB[1] * Gm.ndy + HB[5] * Gm.ndz;
+          const float gdz = HB[4] * Gm.ndx + HB[5] * Gm.ndy + HB[2] * Gm.ndz;
+          const float ng = Gm.nx * gB[0] + Gm.ny * gB[1] + Gm.nz * gB[2];
+          const float ndg = Gm.ndx * gB[0] + Gm.ndy * gB[1] + Gm.ndz * gB[2];
+          const float ngd = Gm.nx * gdx + Gm.ny * gdy + Gm.nz * gdz;
+          const float t1 = ndg + ngd;
+          ox += (gdx - Gm.ndx * ng - Gm.nx * t1) * Gm.inv - Gm.nd * (gB[0] - Gm.nx * ng) * Gm.inv * Gm.inv;
+          oy += (gdy - Gm.ndy * ng - Gm.ny * t1) * Gm.inv - Gm.nd * (gB[1] - Gm.ny * ng) * Gm.inv * Gm.inv;
+          oz += (gdz - Gm.ndz * ng - Gm.nz * t1) * Gm.inv - Gm.nd * (gB[2] - Gm.nz * ng) * Gm.inv * Gm.inv;
+          // radial terms
+          const float sn = tot[IS] + tot[IS + 1] * Gm.nd;
+          ox += sn * Gm.nx + tot[IS + 2] * Gm.ndx;
+          oy += sn * Gm.ny + tot[IS + 2] * Gm.ndy;
+          oz += sn * Gm.nz + tot[IS + 2] * Gm.ndz;
+        }
+        qbar[3 * (size_t)e] = ox;
+        qbar[3 * (size_t)e + 1] = oy;
+        qbar[3 * (size_t)e + 2] = oz;
+        psum[0] += ox;
+        psum[1] += oy;
+        psum[2] += oz;
+      }
+      __syncthreads();
+    }
+  }
+#undef FC_WGET
+  const size_t slot = (size_t)v * S + sl;
+  if (NEED_X && act) {
+    float* xo = x_out + slot * NIN * C + k;
+    static_for<NIN>([&](auto c) { xo[(size_t)c * C] = xh[c]; });
+  }
+  if constexpr (NEED_POS) {
+    if (wv == 0) {
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        float t = psum[i];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o);
+        psum[i] = t;
+      }
+      if (lane == 0) {
+        p_out[3 * slot] = psum[0];
+        p_out[3 * slot + 1] = psum[1];
+        p_out[3 * slot + 2] = psum[2];
+      }
+    }
+  }
+}
+
+template <int LIN, int LEDGE, int LOUT, bool HAS_VX>
+void launch_vv_sender_vx(const ConvArgs& a, const VjpWorkspace& wsl, hipStream_t st) {
+  const bool nx = a.x_bar != nullptr, np = a.pos_bar != nullptr;
+  const int nw = (a.C + kWave - 1) / kWave;
+  float* xo = wsl.S == 1 ? a.x_bar : wsl.x_part;
+  float* po = wsl.S == 1 ? a.pos_bar : wsl.p_part;
+  dim3 grid(a.N, wsl.S), block(nw * kWave);
+  const size_t lds = VVShape<LIN, LEDGE, LOUT, HAS_VX>::lds_bytes(np ? nw : 0);
+#define FC_VV(NX, NP)                                                                                         \
+  hipLaunchKernelGGL((conv_vv_sender_kernel<LIN, LEDGE, LOUT, HAS_VX, NX, NP>), grid, block, lds, st, a.N, a.C, \
+                     a.t_rowptr, a.t_edge, a.receiver, a.pos, a.shift, a.x, a.W, a.g, a.v_x, a.v_pos, xo, po,   \
+                     wsl.rbar, a.rc)
+  if (nx && np) FC_VV(true, true);
+  else if (nx) FC_VV(true, false);
+  else FC_VV(false, true);
+#undef FC_VV
+}
+
+// g_hat (when requested), then x_hat / pos_hat (when requested).
+template <int LIN, int LEDGE, int LOUT>
+void launch_vjp_vjp(const ConvArgs& a, hipStream_t st) {
+  if (a.g_hat) launch_vv_recv<LIN, LEDGE, LOUT, 0>(a, st);
+  if (!a.x_bar && !a.pos_bar) return;
+  const VjpWorkspace wsl(a.N, a.E, a.C, nrank(LIN), a.rbar);
+  if (a.v_x) launch_vv_sender_vx<LIN, LEDGE, LOUT, true>(a, wsl, st);
+  else launch_vv_sender_vx<LIN, LEDGE, LOUT, false>(a, wsl, st);
+  launch_vjp_combine(a, wsl, nrank(LIN), st);
+}
+
+}  // namespace fc

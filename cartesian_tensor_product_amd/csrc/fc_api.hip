@@ -2,6 +2,7 @@
 // stream-ordered kernel launches.  See include/flashcart.h for the contract.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -10,6 +11,7 @@
 #include "../../include/flashcart.h"
 #include "fc_conv.h"
 #include "fc_graph.h"
+#include "fc_block.h"
 #include "fc_ladder.h"
 
 namespace {
@@ -324,6 +326,83 @@ fc_status fc_node_ladder_vjp(const fc_ladder_desc* d, const float* A, const floa
     return fail(FC_ERR_WORKSPACE, "ladder VJP needs %zu workspace bytes", need);
   fc::ladder_vjp(p, A, weights, saved, g_z, A_grad, weights_grad, static_cast<float*>(workspace), stream);
   return check_launch("ladder VJP");
+}
+
+}  // extern "C"
+
+namespace {
+
+struct BlockLayout {
+  size_t A, z, saved, lws, gz, Ab, cws, parts, total;   // byte offsets / total
+};
+
+fc_status block_layout(const fc_conv_desc* cd, const fc_ladder_desc* ld, BlockLayout* L) {
+  if (fc_status s = check_desc(cd)) return s;
+  fc::LadderPlan p;
+  if (fc_status s = ladder_plan(ld, &p)) return s;
+  if (cd->l_in != 0) return fail(FC_ERR_UNSUPPORTED, "block: the convolution needs scalar senders (l_in == 0)");
+  if (cd->l_out != ld->l_a || cd->channels != ld->channels || cd->n_nodes != ld->n_nodes)
+    return fail(FC_ERR_INVALID_ARGUMENT, "block: conv l_out/channels/nodes must match ladder l_a/channels/nodes");
+  auto al = [](size_t b) { return (b + 255) / 256 * 256; };
+  const size_t N = cd->n_nodes, C = cd->channels;
+  const size_t nA = (size_t)(cd->l_out + 1) * (cd->l_out + 1), nz = (size_t)(ld->l_out + 1) * (ld->l_out + 1);
+  size_t o = 0;
+  L->A = o;      o += al(N * nA * C * 4);
+  L->z = o;      o += al(N * nz * C * 4);
+  L->saved = o;  o += al(p.saved_floats() * 4);
+  L->lws = o;    o += al(std::max(p.fwd_ws_floats(), p.vjp_ws_floats()) * 4);
+  L->gz = o;     o += al(N * nz * C * 4);
+  L->Ab = o;     o += al(N * nA * C * 4);
+  L->cws = o;    o += al(fc_edge_conv_workspace_bytes(cd, 1));
+  L->parts = o;  o += al((size_t)fc::block_energy_parts(cd->n_nodes) * 8);
+  L->total = o;
+  return FC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fc_block_workspace_bytes(const fc_conv_desc* conv, const fc_ladder_desc* lad) {
+  BlockLayout L;
+  return block_layout(conv, lad, &L) == FC_OK ? L.total : 0;
+}
+
+fc_status fc_block_energy_forces(const fc_conv_desc* cd, const fc_graph* g, const float* pos, const float* shift,
+                                 const float* x, const float* radial_w, const fc_ladder_desc* ld,
+                                 const float* ladder_w, float conv_scale, double* energy, float* e_atom,
+                                 float* forces, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  BlockLayout L;
+  if (fc_status s = block_layout(cd, ld, &L)) return s;
+  if (!energy || !ladder_w) return fail(FC_ERR_INVALID_ARGUMENT, "block: NULL energy or ladder weights");
+  if (!workspace || workspace_bytes < L.total)
+    return fail(FC_ERR_WORKSPACE, "block needs %zu workspace bytes", L.total);
+  char* w = static_cast<char*>(workspace);
+  float* A = reinterpret_cast<float*>(w + L.A);
+  float* z = reinterpret_cast<float*>(w + L.z);
+  float* saved = reinterpret_cast<float*>(w + L.saved);
+  float* lws = reinterpret_cast<float*>(w + L.lws);
+  float* gz = reinterpret_cast<float*>(w + L.gz);
+  float* Ab = reinterpret_cast<float*>(w + L.Ab);
+  double* parts = reinterpret_cast<double*>(w + L.parts);
+  fc::LadderPlan p;
+  ladder_plan(ld, &p);
+  const int N = cd->n_nodes, C = cd->channels;
+  const int nA = (cd->l_out + 1) * (cd->l_out + 1), nz = (ld->l_out + 1) * (ld->l_out + 1);
+  if (fc_status s = fc_edge_conv_fwd(cd, g, pos, shift, x, radial_w, A, stream)) return s;
+  fc::block_scale(A, (size_t)N * nA * C, conv_scale, stream);
+  fc::ladder_forward(p, A, ladder_w, z, saved, lws, stream);
+  fc::block_energy(z, N, nz, C, e_atom, parts, energy, stream);
+  if (forces) {
+    fc::block_unit_cotangent(gz, N, nz, C, stream);
+    fc::ladder_vjp(p, A, ladder_w, saved, gz, Ab, nullptr, lws, stream);
+    fc::block_scale(Ab, (size_t)N * nA * C, conv_scale, stream);
+    if (fc_status s = fc_edge_conv_vjp(cd, g, pos, shift, x, radial_w, Ab, nullptr, forces, nullptr,
+                                       w + L.cws, L.parts - L.cws, stream))
+      return s;
+    fc::block_scale(forces, (size_t)N * 3, -1.f, stream);
+  }
+  return check_launch("block energy/forces");
 }
 
 }  // extern "C"

@@ -68,6 +68,8 @@ _SIGS = {
     "fc_ladder_workspace_bytes": (_SZ, [_PL, _I]),
     "fc_node_ladder_fwd": (_I, [_PL, _P, _P, _P, _P, _P, _SZ, _P]),
     "fc_node_ladder_vjp": (_I, [_PL, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "fc_block_workspace_bytes": (_SZ, [_PD, _PL]),
+    "fc_block_energy_forces": (_I, [_PD, _PG, _P, _P, _P, _P, _PL, _P, ctypes.c_float, _P, _P, _P, _P, _SZ, _P]),
 }
 
 
@@ -251,6 +253,22 @@ def fc_node_ladder_vjp(d: LadderDesc, A, weights, saved, g_z, A_grad, weights_gr
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().fc_node_ladder_vjp(ctypes.byref(d), _f32(A), _f32(weights), _f32(saved), _f32(g_z),
                                     _f32(A_grad), _f32(weights_grad), _ptr(workspace), nbytes, _stream(stream)))
+
+
+# ------------------------------------------------------------------- block --
+
+def fc_block_workspace_bytes(conv: ConvDesc, lad: LadderDesc) -> int:
+    return lib().fc_block_workspace_bytes(ctypes.byref(conv), ctypes.byref(lad))
+
+
+def fc_block_energy_forces(conv: ConvDesc, graph: DeviceGraph, pos, shift, x, radial_w, lad: LadderDesc, ladder_w,
+                           conv_scale: float, energy, e_atom, forces, workspace, stream=None):
+    import torch
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().fc_block_energy_forces(ctypes.byref(conv), ctypes.byref(graph.struct), _f32(pos), _f32(shift),
+                                        _f32(x), _f32(radial_w), ctypes.byref(lad), _f32(ladder_w),
+                                        ctypes.c_float(conv_scale), _ptr(energy, torch.float64), _f32(e_atom),
+                                        _f32(forces), _ptr(workspace), nbytes, _stream(stream)))
 
 
 def workspace(nbytes: int, device="cuda"):

@@ -83,7 +83,7 @@ int32_t fc_abi_version(void);
 
 /* ------------------------------------------------------------------------
  * Edge convolution descriptor.
- * n_nodes >= 1, n_edges >= 0, 1 <= channels <= 4096,
+ * n_nodes >= 1, n_edges >= 0, 1 <= channels <= 256,
  * 0 <= l_in, l_edge, l_out <= 4 with at least one admissible path,
  * n_basis == 8, r_cut > 0, flags == 0 (natural parity, paths separate).
  * ---------------------------------------------------------------------- */
@@ -205,6 +205,25 @@ fc_status fc_node_ladder_vjp(const fc_ladder_desc* d, const float* A, const floa
                              const float* saved, const float* g_z, float* A_grad,
                              float* weights_grad, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * One message-passing block for energy and forces (App. E "Model
+ * architecture" and Eq. E1; §2 for F = -grad E):
+ *   A = conv_scale * edge_conv(x) ,  z = ladder(A),
+ *   E = sum_u sum_k z[u, 0, k],      forces = -dE/dpos.
+ * Needs conv.l_in == 0 (scalar senders: one path per output rank, so the
+ * convolution output has the node-feature layout), conv.l_out == lad.l_a,
+ * equal channels and node counts.  energy: DEVICE double[1] (summed in
+ * fp64 in a fixed order); e_atom: DEVICE float[N] or NULL (per-atom sums);
+ * forces: DEVICE float[N][3] or NULL (skips the backward pass).  Residual
+ * updates, normalisation, gates and the readout are not included.
+ * ---------------------------------------------------------------------- */
+size_t fc_block_workspace_bytes(const fc_conv_desc* conv, const fc_ladder_desc* lad);
+fc_status fc_block_energy_forces(const fc_conv_desc* conv, const fc_graph* g, const float* pos,
+                                 const float* shift, const float* x, const float* radial_w,
+                                 const fc_ladder_desc* lad, const float* ladder_w, float conv_scale,
+                                 double* energy, float* e_atom, float* forces, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

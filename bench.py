@@ -28,7 +28,128 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_F32_PEAK_TFS = 157.3
 N_NODES, K_NBR, BOX, CHANNELS, LMAX, R_CUT, SEED = 1024, 128, 20.0, 128, 2, 5.0, 1
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_conv_vjp_sender_micro.json")
+KERNEL_SOURCES = ["cartesian_tensor_product_amd/csrc/fc_conv_kernels.h", "cartesian_tensor_product_amd/csrc/fc_common.h",
+                  "cartesian_tensor_product_amd/csrc/fc_conv.hip", "cartesian_tensor_product_amd/csrc/generated/fc_tables.h"]
+
+
+def kernel_source_sha() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the VJP sender kernel from the committed
+    rocprofv3 FETCH_SIZE/WRITE_SIZE runs, if the kernel is unchanged since."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except OSError:
+        return None
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return t["bytes_per_launch"]
+
+
+def timed(fn, iters=10, warmup=2):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(st)
+    for _ in range(iters):
+        fn()
+    b.record(st)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / iters
+
+
+def extras(dev):
+    """Secondary workloads (reported beside the headline, not part of it)."""
+    import torch
+
+    from cartesian_tensor_product_amd import flashcart as fc
+    from cartesian_tensor_product_amd import inputs
+    out = {}
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    # high-rank microbenchmark: fwd, VJP, VJP-of-VJP (position cotangent)
+    for l in (3, 4):
+        desc = fc.conv_desc(N_NODES, N_NODES * K_NBR, CHANNELS, l, l, l, R_CUT)
+        P, n_in, n_out = fc.fc_conv_layout(desc)
+        d = inputs.edge_conv_inputs(2, N_NODES, K_NBR, BOX, CHANNELS, n_in, P, n_out, with_vpos=True)
+        graph = fc.DeviceGraph(d["rowptr"], d["sender"], N_NODES, device=dev)
+        pos, x, W, g, vp = t(d["pos"]), t(d["x"]), t(d["W"]), t(d["g"]), t(d["v_pos"])
+        z = torch.empty((N_NODES, n_out, CHANNELS), device=dev)
+        xb, pb = torch.empty_like(x), torch.empty((N_NODES, 3), device=dev)
+        gh, xh, ph = torch.empty_like(z), torch.empty_like(x), torch.empty_like(pb)
+        ws = fc.workspace(max(fc.fc_edge_conv_workspace_bytes(desc, 1), fc.fc_edge_conv_workspace_bytes(desc, 2)), dev)
+        E = N_NODES * K_NBR
+        r = {"fwd_ms": timed(lambda: fc.fc_edge_conv_fwd(desc, graph, pos, None, x, W, z)),
+             "vjp_ms": timed(lambda: fc.fc_edge_conv_vjp(desc, graph, pos, None, x, W, g, xb, pb, None, ws)),
+             "vjp_vjp_ms": timed(lambda: fc.fc_edge_conv_vjp_vjp(desc, graph, pos, None, x, W, g, None, vp, gh, xh,
+                                                                 ph, None, ws), iters=5)}
+        r["fwd_plus_vjp_edge_channels_per_s"] = E * CHANNELS / ((r["fwd_ms"] + r["vjp_ms"]) * 1e-3)
+        out[f"conv_rank{l}_1024n_128c_128nbr"] = r
+        del z, xb, pb, gh, xh, ph, ws
+    # node-local ladder, 4096 nodes, 128 channels, ranks <= 3, order 4, both variants
+    for name, var in (("full", fc.FC_LADDER_FULL), ("path_reduced", fc.FC_LADDER_PATH_REDUCED)):
+        ld = fc.ladder_desc(4096, CHANNELS, 3, 3, 3, 4, var)
+        blocks = fc.ladder_weight_blocks(ld)
+        shapes = [((r, c), "normal" if kind == 0 else "one_plus", c) for (_, r, c, kind) in blocks]
+        rng, A, ws = inputs.ladder_inputs(3, 4096, CHANNELS, 16, shapes)
+        gz = inputs.ladder_cotangent(rng, 4096, 16, CHANNELS)
+        dA, dW, dg = t(A), t(np.concatenate([w.ravel() for w in ws])), t(gz)
+        nw, ns = fc.fc_ladder_layout(ld)
+        saved = torch.empty(ns, device=dev)
+        z = torch.empty((4096, 16, CHANNELS), device=dev)
+        Ab, Wb = torch.empty_like(dA), torch.empty_like(dW)
+        wsf = fc.workspace(fc.fc_ladder_workspace_bytes(ld, 0), dev)
+        wsb = fc.workspace(fc.fc_ladder_workspace_bytes(ld, 1), dev)
+        r = {"fwd_ms": timed(lambda: fc.fc_node_ladder_fwd(ld, dA, dW, z, saved, wsf)),
+             "vjp_ms": timed(lambda: fc.fc_node_ladder_vjp(ld, dA, dW, saved, dg, Ab, Wb, wsb))}
+        r["node_channels_per_s_fwd"] = 4096 * CHANNELS / (r["fwd_ms"] * 1e-3)
+        out[f"ladder_{name}_4096n_128c_rank3_order4"] = r
+        del saved, z, Ab, Wb, wsf, wsb
+    out["ladder_full_4096n_128c_rank3_order4"]["mixing_gemm_gflop_fwd"] = ladder_gemm_gflop(4096, CHANNELS, 3, 4)
+    lf = out["ladder_full_4096n_128c_rank3_order4"]
+    lf["mixing_gemm_tflops_fwd_lower_bound"] = lf["mixing_gemm_gflop_fwd"] / lf["fwd_ms"]
+    # 1000-atom diamond block: energy and forces
+    from cartesian_tensor_product_amd import inputs as inp
+    cd_l = fc.ladder_desc(1000, CHANNELS, 3, 3, 0, 5, fc.FC_LADDER_PATH_REDUCED)
+    blocks = fc.ladder_weight_blocks(cd_l)
+    shapes = [((r_, c_), "normal" if k_ == 0 else "one_plus", c_) for (_, r_, c_, k_) in blocks]
+    dd = inp.diamond_inputs(channels=CHANNELS, r_cut=5.0, rattle=0.05, n_paths=4, ladder_weight_shapes=shapes)
+    Nd, Ed = dd["pos"].shape[0], len(dd["sender"])
+    cd = fc.conv_desc(Nd, Ed, CHANNELS, 0, 3, 3, 5.0)
+    graph = fc.DeviceGraph(dd["rowptr"], dd["sender"], Nd, device=dev)
+    lw = t(np.concatenate([w.ravel() for w in dd["ladder_weights"]]))
+    en = torch.zeros(1, dtype=torch.float64, device=dev)
+    F = torch.empty((Nd, 3), device=dev)
+    wsd = fc.workspace(fc.fc_block_workspace_bytes(cd, cd_l), dev)
+    args = (cd, graph, t(dd["pos"]), t(dd["shift"]), t(dd["x"]), t(dd["W"]), cd_l, lw, 1.0 / np.sqrt(Ed / Nd))
+    ms = timed(lambda: fc.fc_block_energy_forces(*args, en, None, F, wsd))
+    out["diamond_1000_atoms_energy_forces"] = {"ms": ms, "us_per_atom": ms * 1e3 / Nd, "edges": Ed}
+    return out
+
+
+def ladder_gemm_gflop(N, C, l, order):
+    """Flops of the full ladder's mixing GEMMs in one forward: W1 on every
+    rank, then per step sum_L 2 N (2L+1) (P_L C) C with P_L the admissible
+    paths (l1 <= l, l2 <= l) -> L."""
+    def paths(L):
+        return sum(1 for a in range(l + 1) for b in range(l + 1)
+                   if abs(a - b) <= L <= a + b and (a + b + L) % 2 == 0)
+    f = sum(2.0 * N * (2 * L + 1) * C * C for L in range(l + 1))
+    f += (order - 1) * sum(2.0 * N * (2 * L + 1) * paths(L) * C * C for L in range(l + 1))
+    return f / 1e9
 
 
 def algorithmic_bytes(N, E, C, n_in, n_out, P):
@@ -75,6 +196,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--copy-only", type=int, default=0, metavar="MB",
                     help="only run 5 device-to-device copies of MB megabytes (counter calibration)")
     args = ap.parse_args()
@@ -161,13 +283,16 @@ def main():
                    "nodes": N_NODES, "neighbours": K_NBR, "channels": CHANNELS, "l_max": LMAX,
                    "edges": E},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic() if dom.startswith("conv_vjp") else None,
                      "algorithmic_bytes_per_launch": dom_bytes},
         "breakdown": {"fwd_ms": f_mean, "vjp_ms": v_mean, "fwd_GBs_alg": b_fwd / (f_mean * 1e-3) / 1e9,
                       "vjp_GBs_alg": b_vjp / (v_mean * 1e-3) / 1e9,
                       "fwd_plus_vjp_frac_hbm": (b_fwd + b_vjp) / ((f_mean + v_mean) * 1e-3) / 1e9 / HBM_PEAK_GBS,
                       "wall_s": wall},
     }
+    if not args.no_extras:
+        out["extras"] = extras(dev)
     if not args.no_cpu_baseline:
         from oracle import conv
         spec = conv.ConvSpec(LMAX, LMAX, LMAX, R_CUT)

@@ -289,6 +289,32 @@ fc_status fc_ladder_layout(const fc_ladder_desc* d, size_t* n_weight_floats, siz
   return ok();
 }
 
+fc_status fc_ladder_weight_block(const fc_ladder_desc* d, int32_t i, size_t* offset, int32_t* rows, int32_t* cols,
+                                 int32_t* kind) {
+  fc::LadderPlan p;
+  if (fc_status s = ladder_plan(d, &p)) return s;
+  struct Blk { size_t off; int r, c, k; };
+  Blk blk[64];
+  int n = 0;
+  const int C = p.C;
+  if (p.variant == FC_LADDER_FULL) {
+    for (int l = 0; l <= p.lq(1); ++l) blk[n++] = {p.w_full(1, l), C, C, 0};
+    for (int q = 2; q <= p.order; ++q)
+      for (int L = 0; L <= p.lq(q); ++L)
+        if (p.paths(q, L)) blk[n++] = {p.w_full(q, L), C, p.paths(q, L) * C, 0};
+  } else {
+    blk[n++] = {p.w_a(1), p.lq(1) + 1, C, 1};
+    for (int q = 2; q <= p.order; ++q) blk[n++] = {p.w_a(q), p.paths(q), C, 1};
+    for (int L = 0; L <= p.lout; ++L) blk[n++] = {p.w_final(L), C, C, 0};
+  }
+  if (i < 0 || i >= n) return fail(FC_ERR_INVALID_ARGUMENT, "weight block %d out of range [0, %d)", i, n);
+  if (offset) *offset = blk[i].off;
+  if (rows) *rows = blk[i].r;
+  if (cols) *cols = blk[i].c;
+  if (kind) *kind = blk[i].k;
+  return ok();
+}
+
 size_t fc_ladder_workspace_bytes(const fc_ladder_desc* d, int32_t op) {
   fc::LadderPlan p;
   if (ladder_plan(d, &p) != FC_OK) return 0;

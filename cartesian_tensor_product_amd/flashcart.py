@@ -66,6 +66,7 @@ _SIGS = {
     "fc_edge_conv_vjp_vjp": (_I, [_PD, _PG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "fc_ladder_layout": (_I, [_PL, _PSZ, _PSZ]),
     "fc_ladder_workspace_bytes": (_SZ, [_PL, _I]),
+    "fc_ladder_weight_block": (_I, [_PL, _I, _PSZ, _PI, _PI, _PI]),
     "fc_node_ladder_fwd": (_I, [_PL, _P, _P, _P, _P, _P, _SZ, _P]),
     "fc_node_ladder_vjp": (_I, [_PL, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "fc_block_workspace_bytes": (_SZ, [_PD, _PL]),
@@ -179,6 +180,24 @@ def fc_ladder_layout(d: LadderDesc):
 
 def fc_ladder_workspace_bytes(d: LadderDesc, op: int) -> int:
     return lib().fc_ladder_workspace_bytes(ctypes.byref(d), op)
+
+
+def fc_ladder_weight_block(d: LadderDesc, i: int):
+    """(offset, rows, cols, kind) of block i of the flat weight buffer."""
+    off, r, c, k = ctypes.c_size_t(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().fc_ladder_weight_block(ctypes.byref(d), i, ctypes.byref(off), ctypes.byref(r), ctypes.byref(c),
+                                        ctypes.byref(k)))
+    return off.value, r.value, c.value, k.value
+
+
+def ladder_weight_blocks(d: LadderDesc):
+    out, i = [], 0
+    while True:
+        try:
+            out.append(fc_ladder_weight_block(d, i))
+        except FlashCartError:
+            return out
+        i += 1
 
 
 # ------------------------------------------------------------------- graph --

@@ -191,6 +191,12 @@ typedef struct {
 fc_status fc_ladder_layout(const fc_ladder_desc* d, size_t* n_weight_floats,
                            size_t* n_saved_floats);
 size_t fc_ladder_workspace_bytes(const fc_ladder_desc* d, int32_t op /*0 fwd, 1 vjp*/);
+/* Block i (0-based, in flat order) of the weight buffer: its offset in
+ * floats, its shape rows x cols, and kind 0 (a mixing matrix, fan-in =
+ * cols) or 1 (per-rank or per-path channel weights a, shape [rows][C]).
+ * FC_ERR_INVALID_ARGUMENT past the last block.  Host only. */
+fc_status fc_ladder_weight_block(const fc_ladder_desc* d, int32_t i, size_t* offset, int32_t* rows,
+                                 int32_t* cols, int32_t* kind);
 
 /* Forward.  saved may be NULL when no VJP follows; otherwise it receives
  * n_saved_floats floats of intermediate states. */

@@ -104,15 +104,69 @@ struct ConvCfg {
   }
 };
 
-// Paths of a rank group [LLO, LHI] of a configuration.
-template <class Cfg, int LLO, int LHI>
-struct Group {
-  static constexpr int p0 = Cfg::first_path_of(LLO);
-  static constexpr int p1 = Cfg::first_path_of(LHI + 1);
-  static constexpr int NP = p1 - p0;
-  static constexpr int r0 = Cfg::off_L(LLO);
-  static constexpr int r1 = Cfg::off_L(LHI + 1);
-  static constexpr int NR = r1 - r0;
+// A path group: the contiguous paths [P0, P1) of a configuration, handled by
+// one kernel launch (forward) or one sweep over the edges (VJP).  The rows of
+// the group's paths are held path-major in registers: component c of path p
+// sits at loff(p) + c; its row in the node-feature layout is Cfg::row(p, c).
+template <class Cfg, int P0, int P1>
+struct PathGroup {
+  static constexpr int p0 = P0, p1 = P1, NP = P1 - P0;
+  static constexpr int loff(int p) {
+    int o = 0;
+    for (int q = P0; q < p; ++q) o += ncomp(Cfg::paths[q].L);
+    return o;
+  }
+  static constexpr int NR = loff(P1);
+  // whether some path of the group has edge rank l2
+  static constexpr bool uses_l2(int l2) {
+    for (int q = P0; q < P1; ++q)
+      if (Cfg::paths[q].l2 == l2) return true;
+    return false;
+  }
+  // whether stored direction component g (= l2^2 + c) enters the group
+  static constexpr bool uses_comp(int g) {
+    int l = 0;
+    while ((l + 1) * (l + 1) <= g) ++l;
+    return uses_l2(l);
+  }
+  // bit g set for every direction component that enters the group
+  static constexpr uint64_t comp_mask() {
+    uint64_t m = 0;
+    for (int g = 0; g < Cfg::NE; ++g)
+      if (uses_comp(g)) m |= uint64_t(1) << g;
+    return m;
+  }
+};
+
+// Split of the paths into groups whose register cost stays within BUDGET:
+// every path costs its 2L+1 output rows plus its kNB radial weights.  Greedy
+// in path order; a group holds at least one path.
+template <class Cfg, int BUDGET>
+struct PathGroups {
+  static constexpr int cost(int p) { return ncomp(Cfg::paths[p].L) + kNB; }
+  static constexpr std::array<int, Cfg::P + 1> build() {
+    std::array<int, Cfg::P + 1> s{};
+    int n = 0, used = 0;
+    s[0] = 0;
+    for (int p = 0; p < Cfg::P; ++p) {
+      if (p > s[n] && used + cost(p) > BUDGET) {
+        s[++n] = p;
+        used = 0;
+      }
+      used += cost(p);
+    }
+    s[++n] = Cfg::P;
+    return s;
+  }
+  static constexpr std::array<int, Cfg::P + 1> start = build();
+  static constexpr int count() {
+    int n = 0;
+    while (start[n] != Cfg::P) ++n;
+    return n;
+  }
+  static constexpr int n = count();
+  template <int I>
+  using group = PathGroup<Cfg, start[I], start[I + 1]>;
 };
 
 // ----------------------------------------------------------- direction tensors
@@ -238,8 +292,9 @@ __device__ __forceinline__ void radial2(float r, float rc, float* R, float* dR, 
 }
 
 // Gradient g = dG/dn and Hessian H (xx, yy, zz, xy, xz, yz) of the
-// polynomial G(n) = sum_c coef[c] y_c(n) over all ranks <= LE.
-template <int LE>
+// polynomial G(n) = sum_c coef[c] y_c(n) over all ranks <= LE; components
+// whose bit is clear in MASK are taken as zero.
+template <int LE, uint64_t MASK = ~uint64_t(0)>
 __device__ __forceinline__ void direction_contract_d2(const float* coef, float nx, float ny, float nz, float* g,
                                                       float* H) {
   float px[LE + 1], py[LE + 1], pz[LE + 1];
@@ -255,6 +310,7 @@ __device__ __forceinline__ void direction_contract_d2(const float* coef, float n
   static_for<nrank(LE)>([&](auto gi) {
     constexpr int gg = gi;
     constexpr int mb = tab::kMonoBegin[gg], me = tab::kMonoBegin[gg + 1];
+    if constexpr (((MASK >> gg) & 1) == 0) return;
     const float cf = coef[gg];
     static_for<me - mb>([&](auto mi) {
       constexpr tab::Mono m = tab::kMono[mb + mi];

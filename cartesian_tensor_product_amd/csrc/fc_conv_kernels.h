@@ -16,9 +16,12 @@
 
 namespace fc {
 
-// Largest number of output rows one launch accumulates per lane (the pages
-// group output ranks to about 100 stored components per channel).
-inline constexpr int kGroupRows = 100;
+// Register budgets of the path groups (see PathGroups): what is left of
+// about 200 VGPRs per lane once the per-lane arrays that do not depend on the
+// group (gathered features, their weighted copies, accumulated cotangents)
+// are counted.
+__host__ __device__ constexpr int fwd_budget(int nin) { return 200 - 2 * nin; }
+__host__ __device__ constexpr int vjp_budget(int nin, int ne) { return 200 - 2 * nin - ne; }
 // Channels of one VJP block: up to 4 waves (C <= 256).
 inline constexpr int kMaxVjpWaves = 4;
 // Per-edge products |c| y[g] are broadcast from LDS when a configuration uses
@@ -26,18 +29,6 @@ inline constexpr int kMaxVjpWaves = 4;
 inline constexpr int kCYMax = 48;
 // Per-sender products |c| x[g] stay in registers up to this many.
 inline constexpr int kCXMax = 20;
-
-template <class Cfg, int LOUT>
-constexpr int group_end(int lo) {
-  int rows = 0, hi = lo;
-  for (int L = lo; L <= LOUT; ++L) {
-    const int r = ncomp(L) * Cfg::count_L(L);
-    if (L > lo && rows + r > kGroupRows) break;
-    rows += r;
-    hi = L;
-  }
-  return hi;
-}
 
 // Per-edge coefficient products of one configuration.
 template <int LIN, int LEDGE, int LOUT>
@@ -76,17 +67,17 @@ struct EdgeProducts {
 };
 
 // ============================================================== forward ====
-template <int LIN, int LEDGE, int LOUT, int LLO, int LHI>
+// One launch per path group G: z rows of G's paths for node u and 64 channels.
+template <int LIN, int LEDGE, int LOUT, int P0, int P1>
 __global__ __launch_bounds__(kWave) void conv_fwd_kernel(
     int N, int C, const int* __restrict__ rowptr, const int* __restrict__ sender,
     const float* __restrict__ pos, const float* __restrict__ shift,
     const float* __restrict__ x, const float* __restrict__ W, float* __restrict__ z, float rc) {
   using Cfg = ConvCfg<LIN, LEDGE, LOUT>;
-  using G = Group<Cfg, LLO, LHI>;
+  using G = PathGroup<Cfg, P0, P1>;
   using EP = EdgeProducts<LIN, LEDGE, LOUT>;
   constexpr int NIN = Cfg::NIN, NE = Cfg::NE, P = Cfg::P, NOUT = Cfg::NOUT;
   constexpr int REC = EP::NY + kNB + 1;
-  constexpr bool WREG = kNB * G::NP <= 128;
   __shared__ float geo[kWave * REC];
 
   const int u = blockIdx.x;
@@ -97,13 +88,11 @@ __global__ __launch_bounds__(kWave) void conv_fwd_kernel(
   const int voff = kk * 4;
   const auto xr = make_rsrc(x, (uint32_t)((size_t)N * NIN * C * 4));
 
-  float Wr[WREG ? kNB * G::NP : 1];
-  if constexpr (WREG) {
-    static_for<kNB * G::NP>([&](auto i) {
-      constexpr int b = i / G::NP, p = i % G::NP;
-      Wr[i] = W[(size_t)(b * P + G::p0 + p) * C + kk];
-    });
-  }
+  float Wr[kNB * G::NP];
+  static_for<kNB * G::NP>([&](auto i) {
+    constexpr int b = i / G::NP, p = i % G::NP;
+    Wr[i] = W[(size_t)(b * P + P0 + p) * C + kk];
+  });
   float acc[G::NR];
   static_for<G::NR>([&](auto i) { acc[i] = 0.f; });
 
@@ -138,16 +127,14 @@ __global__ __launch_bounds__(kWave) void conv_fwd_kernel(
       float xv[NIN];
       static_for<NIN>([&](auto c) { xv[c] = buf_load(xr, voff, sbase + c * C * 4); });
       static_for<G::NP>([&](auto pi) {
-        constexpr int p = G::p0 + pi;
+        constexpr int p = P0 + pi;
         constexpr PathInfo PI = Cfg::paths[p];
         constexpr int n1 = ncomp(PI.l1), o1 = rank_off(PI.l1), o2 = rank_off(PI.l2);
+        constexpr int lo = G::loff(p);
         float w = 0.f;
         static_for<kNB>([&](auto b) {
           constexpr int bb = b;
-          float wb;
-          if constexpr (WREG) wb = Wr[bb * G::NP + pi];
-          else wb = W[(size_t)(bb * P + p) * C + kk];
-          w = fmaf(rec[EP::NY + bb], wb, w);
+          w = fmaf(rec[EP::NY + bb], Wr[bb * G::NP + pi], w);
         });
         float xw[n1];
         static_for<n1>([&](auto c) { xw[c] = w * xv[o1 + c]; });
@@ -155,8 +142,7 @@ __global__ __launch_bounds__(kWave) void conv_fwd_kernel(
         static_for<te - tb>([&](auto ti) {
           constexpr int tt = tb + ti;
           constexpr tab::Term T = tab::kTerms[tt];
-          constexpr int row = Cfg::row(p, T.a) - G::r0;
-          acc[row] = fmaf(EP::template cy<tt, o2 + T.b2>(rec), xw[T.b1], acc[row]);
+          acc[lo + T.a] = fmaf(EP::template cy<tt, o2 + T.b2>(rec), xw[T.b1], acc[lo + T.a]);
         });
       });
     }
@@ -164,18 +150,26 @@ __global__ __launch_bounds__(kWave) void conv_fwd_kernel(
   }
   if (act) {
     float* zo = z + (size_t)u * NOUT * C + k;
-    static_for<G::NR>([&](auto i) { zo[(size_t)(G::r0 + i) * C] = acc[i]; });
+    static_for<G::NP>([&](auto pi) {
+      constexpr int p = P0 + pi;
+      static_for<ncomp(Cfg::paths[p].L)>([&](auto c) {
+        constexpr int row = Cfg::row(p, c), li = G::loff(p) + c;
+        zo[(size_t)row * C] = acc[li];
+      });
+    });
   }
 }
 
-template <int LIN, int LEDGE, int LOUT, int LLO>
-void launch_fwd_groups(const ConvArgs& a, hipStream_t st) {
+template <int LIN, int LEDGE, int LOUT>
+void launch_fwd(const ConvArgs& a, hipStream_t st) {
   using Cfg = ConvCfg<LIN, LEDGE, LOUT>;
-  constexpr int LHI = group_end<Cfg, LOUT>(LLO);
+  using GS = PathGroups<Cfg, fwd_budget(Cfg::NIN)>;
   dim3 grid(a.N, (a.C + kWave - 1) / kWave);
-  hipLaunchKernelGGL((conv_fwd_kernel<LIN, LEDGE, LOUT, LLO, LHI>), grid, dim3(kWave), 0, st,
-                     a.N, a.C, a.rowptr, a.sender, a.pos, a.shift, a.x, a.W, a.z, a.rc);
-  if constexpr (LHI < LOUT) launch_fwd_groups<LIN, LEDGE, LOUT, LHI + 1>(a, st);
+  static_for<GS::n>([&](auto gi) {
+    constexpr int p0 = GS::start[gi], p1 = GS::start[gi + 1];
+    hipLaunchKernelGGL((conv_fwd_kernel<LIN, LEDGE, LOUT, p0, p1>), grid, dim3(kWave), 0, st, a.N, a.C, a.rowptr,
+                       a.sender, a.pos, a.shift, a.x, a.W, a.z, a.rc);
+  });
 }
 
 // ================================================================== VJP ====
@@ -199,6 +193,7 @@ struct VjpShape {
   static constexpr int NE = nrank(LEDGE);
   static constexpr int NRED = NE + 1;                      // y_bar components, s
   static constexpr int REC = EP::NY + 2 * kNB + 1;         // y / products, R, R', receiver
+  static constexpr int budget = vjp_budget(nrank(LIN), NE) - (EP::kCXReg ? EP::CXt::n : 0);
   static constexpr size_t lds_bytes(int nw) {
     return sizeof(float) * ((size_t)kWave * REC + (size_t)nw * kWave * NRED * 4);
   }
@@ -226,7 +221,7 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
   using CXt = typename EP::CXt;
   constexpr int NIN = Cfg::NIN, NE = Cfg::NE, P = Cfg::P, NOUT = Cfg::NOUT;
   constexpr int REC = Sh::REC, NRED = Sh::NRED, NY = EP::NY;
-  constexpr bool WREG = kNB * P <= 128;
+  using GS = PathGroups<Cfg, Sh::budget>;
   extern __shared__ float lds[];
   float* geo = lds;                      // [64][REC]
   float* part = lds + kWave * REC;       // [NW][64 edges][NRED][4 rows]
@@ -242,13 +237,6 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
   const int voff = kk * 4;
   const auto gr = make_rsrc(g, (uint32_t)((size_t)N * NOUT * C * 4));
 
-  // radial weights of this lane's channel (zero for idle lanes, so their
-  // contributions to the sums over lanes vanish)
-  float Wr[WREG ? kNB * P : 1];
-  if constexpr (WREG) {
-    static_for<kNB * P>([&](auto i) { Wr[i] = act ? W[(size_t)i * C + kk] : 0.f; });
-  }
-#define FC_WGET(B, PP) (WREG ? Wr[WREG ? (B) * P + (PP) : 0] : (act ? W[(size_t)((B) * P + (PP)) * C + kk] : 0.f))
   float xv[NIN];
   {
     const float* xs = x + (size_t)v * NIN * C + kk;
@@ -268,117 +256,25 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
   const int v0 = t_rowptr[v], deg = t_rowptr[v + 1] - v0;
   const int e0 = v0 + (int)(((long long)sl * deg) / S), e1 = v0 + (int)(((long long)(sl + 1) * deg) / S);
   const float pvx = pos[3 * v], pvy = pos[3 * v + 1], pvz = pos[3 * v + 2];
-  for (int base = e0; base < e1; base += kWave) {
-    const int cnt = min(kWave, e1 - base);
-    if (wv == 0 && lane < cnt) {
-      const int e = t_edge[base + lane];
-      const int u = receiver[e];
-      float rx = pvx - pos[3 * u], ry = pvy - pos[3 * u + 1], rz = pvz - pos[3 * u + 2];
-      if (shift) {
-        rx += shift[3 * e];
-        ry += shift[3 * e + 1];
-        rz += shift[3 * e + 2];
-      }
-      const float r = sqrtf(rx * rx + ry * ry + rz * rz);
-      const float inv = r > 0.f ? 1.f / r : 0.f;
-      float y[NE], R[kNB], dR[kNB];
-      direction_tensors<LEDGE>(rx * inv, ry * inv, rz * inv, y);
-      radial<true>(r, rc, R, dR);
-      float* rec = geo + lane * REC;
-      EP::fill(y, rec);
-      static_for<kNB>([&](auto b) {
-        rec[NY + b] = R[b];
-        rec[NY + kNB + b] = dR[b];
-      });
-      rec[NY + 2 * kNB] = __int_as_float(u);
-    }
-    __syncthreads();
-    for (int j = 0; j < cnt; ++j) {
-      const float* rec = geo + j * REC;
-      const int u = uniform_int(__float_as_int(rec[NY + 2 * kNB]));
-      const int ubase = u * NOUT * C * 4;
-      float gv[NOUT];
-      static_for<NOUT>([&](auto a) { gv[a] = buf_load(gr, voff, ubase + a * C * 4); });
-      float yb[NE];
-      static_for<NE>([&](auto c) { yb[c] = 0.f; });
-      float sacc = 0.f;
-      static_for<P>([&](auto pc) {
-        constexpr int p = pc;
-        constexpr PathInfo PI = Cfg::paths[p];
-        constexpr int na = ncomp(PI.L), n2 = ncomp(PI.l2);
-        constexpr int o1 = rank_off(PI.l1), o2 = rank_off(PI.l2);
-        constexpr int tb = tab::kTermBegin[PI.type], te = tab::kTermBegin[PI.type + 1];
-        float w = 0.f;
-        static_for<kNB>([&](auto b) {
-          constexpr int bb = b;
-          w = fmaf(rec[NY + bb], FC_WGET(bb, p), w);
-        });
-        if constexpr (NEED_X) {
-          // x_bar[b1] += sum_terms c y[b2] (w g[a])
-          float gw[na];
-          static_for<na>([&](auto a) {
-            constexpr int ra = Cfg::row(p, a);
-            gw[a] = w * gv[ra];
-          });
-          static_for<te - tb>([&](auto ti) {
-            constexpr int tt = tb + ti;
-            constexpr tab::Term T = tab::kTerms[tt];
-            xb[o1 + T.b1] = fmaf(EP::template cy<tt, o2 + T.b2>(rec), gw[T.a], xb[o1 + T.b1]);
-          });
-        }
-        if constexpr (NEED_POS) {
-          // v2[b2] = sum_terms c g[a] x[b1]  (VJP_2(g, x), unweighted)
-          float v2[n2];
-          static_for<te - tb>([&](auto ti) {
-            constexpr int tt = tb + ti;
-            constexpr tab::Term T = tab::kTerms[tt];
-            constexpr int ra = Cfg::row(p, T.a);
-            constexpr float ac = T.c < 0.f ? -T.c : T.c;
-            float cx;
-            if constexpr (ac == 1.f) cx = xv[o1 + T.b1];
-            else if constexpr (EP::kCXReg) cx = cxr[CXt::term[tt]];
-            else cx = ac * xv[o1 + T.b1];
-            if constexpr (T.c < 0.f) cx = -cx;
-            if constexpr (T.f2) v2[T.b2] = gv[ra] * cx;
-            else v2[T.b2] = fmaf(gv[ra], cx, v2[T.b2]);
-          });
-          float wbar = 0.f;
-          static_for<n2>([&](auto c) {
-            yb[o2 + c] = fmaf(w, v2[c], yb[o2 + c]);
-            wbar = fmaf(v2[c], rec[o2 + c], wbar);
-          });
-          float dw = 0.f;
-          static_for<kNB>([&](auto b) {
-            constexpr int bb = b;
-            dw = fmaf(rec[NY + kNB + bb], FC_WGET(bb, p), dw);
-          });
-          sacc = fmaf(wbar, dw, sacc);
-        }
-      });
-      if constexpr (NEED_POS) {
-        float* dst = part + ((size_t)(wv * kWave + j) * NRED) * 4 + (lane >> 4);
-        static_for<NE>([&](auto c) {
-          const float t = row_sum16(yb[c]);
-          if ((lane & 15) == 0) dst[c * 4] = t;
-        });
-        const float t = row_sum16(sacc);
-        if ((lane & 15) == 0) dst[NE * 4] = t;
-      }
-    }
-    __syncthreads();
-    if constexpr (NEED_POS) {
+
+  // One sweep over the slice per path group; x_bar accumulates in registers
+  // across the sweeps, and each edge's position cotangent (linear in the
+  // per-edge sums) is the sum of the sweeps' parts, added in group order.
+  static_for<GS::n>([&](auto gi) {
+    using G = typename GS::template group<gi>;
+    constexpr bool FIRST = gi == 0;
+    // radial weights of this lane's channel for the group's paths (zero for
+    // idle lanes, so their contributions to the sums over lanes vanish)
+    float Wr[kNB * G::NP];
+    static_for<kNB * G::NP>([&](auto i) {
+      constexpr int b = i / G::NP, pi = i % G::NP;
+      Wr[i] = act ? W[(size_t)(b * P + G::p0 + pi) * C + kk] : 0.f;
+    });
+    for (int base = e0; base < e1; base += kWave) {
+      const int cnt = min(kWave, e1 - base);
       if (wv == 0 && lane < cnt) {
         const int e = t_edge[base + lane];
         const int u = receiver[e];
-        float tot[NRED];
-        static_for<NRED>([&](auto i) { tot[i] = 0.f; });
-        for (int w2 = 0; w2 < NW; ++w2) {
-          const float4* src = reinterpret_cast<const float4*>(part + ((size_t)(w2 * kWave + lane) * NRED) * 4);
-          static_for<NRED>([&](auto i) {
-            const float4 q = src[i];
-            tot[i] += (q.x + q.y) + (q.z + q.w);
-          });
-        }
         float rx = pvx - pos[3 * u], ry = pvy - pos[3 * u + 1], rz = pvz - pos[3 * u + 2];
         if (shift) {
           rx += shift[3 * e];
@@ -386,35 +282,157 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
           rz += shift[3 * e + 2];
         }
         const float r = sqrtf(rx * rx + ry * ry + rz * rz);
-        float ox = 0.f, oy = 0.f, oz = 0.f;
-        if (r > 0.f) {
-          const float inv = 1.f / r;
-          const float nx = rx * inv, ny = ry * inv, nz = rz * inv;
-          const float srad = tot[NE];
-          float dy[3 * NE];
-          direction_tensor_grads<LEDGE>(nx, ny, nz, dy);
-          float gx = 0.f, gy = 0.f, gz = 0.f;
-          static_for<NE>([&](auto c) {
-            gx = fmaf(tot[c], dy[3 * c], gx);
-            gy = fmaf(tot[c], dy[3 * c + 1], gy);
-            gz = fmaf(tot[c], dy[3 * c + 2], gz);
-          });
-          const float gn = gx * nx + gy * ny + gz * nz;
-          ox = srad * nx + (gx - gn * nx) * inv;
-          oy = srad * ny + (gy - gn * ny) * inv;
-          oz = srad * nz + (gz - gn * nz) * inv;
-        }
-        rbar[3 * (size_t)e] = ox;
-        rbar[3 * (size_t)e + 1] = oy;
-        rbar[3 * (size_t)e + 2] = oz;
-        psum[0] += ox;
-        psum[1] += oy;
-        psum[2] += oz;
+        const float inv = r > 0.f ? 1.f / r : 0.f;
+        float y[NE], R[kNB], dR[kNB];
+        direction_tensors<LEDGE>(rx * inv, ry * inv, rz * inv, y);
+        radial<true>(r, rc, R, dR);
+        float* rec = geo + lane * REC;
+        EP::fill(y, rec);
+        static_for<kNB>([&](auto b) {
+          rec[NY + b] = R[b];
+          rec[NY + kNB + b] = dR[b];
+        });
+        rec[NY + 2 * kNB] = __int_as_float(u);
       }
       __syncthreads();
+      for (int j = 0; j < cnt; ++j) {
+        const float* rec = geo + j * REC;
+        const int u = uniform_int(__float_as_int(rec[NY + 2 * kNB]));
+        const int ubase = u * NOUT * C * 4;
+        float gv[G::NR];
+        static_for<G::NP>([&](auto pi) {
+          constexpr int p = G::p0 + pi;
+          static_for<ncomp(Cfg::paths[p].L)>([&](auto c) {
+            constexpr int row = Cfg::row(p, c), li = G::loff(p) + c;
+            gv[li] = buf_load(gr, voff, ubase + row * C * 4);
+          });
+        });
+        float yb[NE];
+        static_for<NE>([&](auto c) { yb[c] = 0.f; });
+        float sacc = 0.f;
+        static_for<G::NP>([&](auto pi) {
+          constexpr int p = G::p0 + pi;
+          constexpr PathInfo PI = Cfg::paths[p];
+          constexpr int na = ncomp(PI.L), n2 = ncomp(PI.l2);
+          constexpr int o1 = rank_off(PI.l1), o2 = rank_off(PI.l2);
+          constexpr int lo = G::loff(p);
+          constexpr int tb = tab::kTermBegin[PI.type], te = tab::kTermBegin[PI.type + 1];
+          float w = 0.f;
+          static_for<kNB>([&](auto b) {
+            constexpr int bb = b;
+            w = fmaf(rec[NY + bb], Wr[bb * G::NP + pi], w);
+          });
+          if constexpr (NEED_X) {
+            // x_bar[b1] += sum_terms c y[b2] (w g[a])
+            float gw[na];
+            static_for<na>([&](auto a) { gw[a] = w * gv[lo + a]; });
+            static_for<te - tb>([&](auto ti) {
+              constexpr int tt = tb + ti;
+              constexpr tab::Term T = tab::kTerms[tt];
+              xb[o1 + T.b1] = fmaf(EP::template cy<tt, o2 + T.b2>(rec), gw[T.a], xb[o1 + T.b1]);
+            });
+          }
+          if constexpr (NEED_POS) {
+            // v2[b2] = sum_terms c g[a] x[b1]  (VJP_2(g, x), unweighted)
+            float v2[n2];
+            static_for<te - tb>([&](auto ti) {
+              constexpr int tt = tb + ti;
+              constexpr tab::Term T = tab::kTerms[tt];
+              constexpr float ac = T.c < 0.f ? -T.c : T.c;
+              float cx;
+              if constexpr (ac == 1.f) cx = xv[o1 + T.b1];
+              else if constexpr (EP::kCXReg) cx = cxr[CXt::term[tt]];
+              else cx = ac * xv[o1 + T.b1];
+              if constexpr (T.c < 0.f) cx = -cx;
+              if constexpr (T.f2) v2[T.b2] = gv[lo + T.a] * cx;
+              else v2[T.b2] = fmaf(gv[lo + T.a], cx, v2[T.b2]);
+            });
+            float wbar = 0.f;
+            static_for<n2>([&](auto c) {
+              yb[o2 + c] = fmaf(w, v2[c], yb[o2 + c]);
+              wbar = fmaf(v2[c], rec[o2 + c], wbar);
+            });
+            float dw = 0.f;
+            static_for<kNB>([&](auto b) {
+              constexpr int bb = b;
+              dw = fmaf(rec[NY + kNB + bb], Wr[bb * G::NP + pi], dw);
+            });
+            sacc = fmaf(wbar, dw, sacc);
+          }
+        });
+        if constexpr (NEED_POS) {
+          float* dst = part + ((size_t)(wv * kWave + j) * NRED) * 4 + (lane >> 4);
+          static_for<NE>([&](auto c) {
+            if constexpr (G::uses_comp(c)) {
+              const float t = row_sum16(yb[c]);
+              if ((lane & 15) == 0) dst[c * 4] = t;
+            }
+          });
+          const float t = row_sum16(sacc);
+          if ((lane & 15) == 0) dst[NE * 4] = t;
+        }
+      }
+      __syncthreads();
+      if constexpr (NEED_POS) {
+        if (wv == 0 && lane < cnt) {
+          const int e = t_edge[base + lane];
+          const int u = receiver[e];
+          float tot[NRED];
+          static_for<NRED>([&](auto i) { tot[i] = 0.f; });
+          for (int w2 = 0; w2 < NW; ++w2) {
+            const float4* src = reinterpret_cast<const float4*>(part + ((size_t)(w2 * kWave + lane) * NRED) * 4);
+            static_for<NRED>([&](auto i) {
+              if constexpr (i == NE || G::uses_comp(i)) {
+                const float4 q = src[i];
+                tot[i] += (q.x + q.y) + (q.z + q.w);
+              }
+            });
+          }
+          float rx = pvx - pos[3 * u], ry = pvy - pos[3 * u + 1], rz = pvz - pos[3 * u + 2];
+          if (shift) {
+            rx += shift[3 * e];
+            ry += shift[3 * e + 1];
+            rz += shift[3 * e + 2];
+          }
+          const float r = sqrtf(rx * rx + ry * ry + rz * rz);
+          float ox = 0.f, oy = 0.f, oz = 0.f;
+          if (r > 0.f) {
+            const float inv = 1.f / r;
+            const float nx = rx * inv, ny = ry * inv, nz = rz * inv;
+            const float srad = tot[NE];
+            float dy[3 * NE];
+            direction_tensor_grads<LEDGE>(nx, ny, nz, dy);
+            float gx = 0.f, gy = 0.f, gz = 0.f;
+            static_for<NE>([&](auto c) {
+              if constexpr (G::uses_comp(c)) {
+                gx = fmaf(tot[c], dy[3 * c], gx);
+                gy = fmaf(tot[c], dy[3 * c + 1], gy);
+                gz = fmaf(tot[c], dy[3 * c + 2], gz);
+              }
+            });
+            const float gn = gx * nx + gy * ny + gz * nz;
+            ox = srad * nx + (gx - gn * nx) * inv;
+            oy = srad * ny + (gy - gn * ny) * inv;
+            oz = srad * nz + (gz - gn * nz) * inv;
+          }
+          float* re = rbar + 3 * (size_t)e;
+          if constexpr (FIRST) {
+            re[0] = ox;
+            re[1] = oy;
+            re[2] = oz;
+          } else {
+            re[0] += ox;
+            re[1] += oy;
+            re[2] += oz;
+          }
+          psum[0] += ox;
+          psum[1] += oy;
+          psum[2] += oz;
+        }
+        __syncthreads();
+      }
     }
-  }
-#undef FC_WGET
+  });
   const size_t slot = (size_t)v * S + sl;
   if (NEED_X && act) {
     float* xo = x_out + slot * NIN * C + k;

@@ -54,16 +54,17 @@ __device__ __forceinline__ void vv_tensors(const VVGeo& G, float* y, float* yd) 
 }
 
 // ------------------------------------------------------------ g_hat pass --
-template <int LIN, int LEDGE, int LOUT, int LLO, int LHI, bool HAS_VX>
+__host__ __device__ constexpr int vv_recv_budget(int nin) { return 200 - 3 * nin; }
+
+template <int LIN, int LEDGE, int LOUT, int P0, int P1, bool HAS_VX>
 __global__ __launch_bounds__(kWave) void conv_vv_recv_kernel(
     int N, int C, const int* __restrict__ rowptr, const int* __restrict__ sender, const float* __restrict__ pos,
     const float* __restrict__ shift, const float* __restrict__ x, const float* __restrict__ W,
     const float* __restrict__ v_x, const float* __restrict__ v_pos, float* __restrict__ g_hat, float rc) {
   using Cfg = ConvCfg<LIN, LEDGE, LOUT>;
-  using G = Group<Cfg, LLO, LHI>;
+  using G = PathGroup<Cfg, P0, P1>;
   constexpr int NIN = Cfg::NIN, NE = Cfg::NE, P = Cfg::P, NOUT = Cfg::NOUT;
   constexpr int REC = 2 * NE + 2 * kNB + 2;   // y, ydot, R, R', nd, sender
-  constexpr bool WREG = 2 * kNB * G::NP <= 128;
   __shared__ float geo[kWave * REC];
 
   const int u = blockIdx.x;
@@ -75,13 +76,11 @@ __global__ __launch_bounds__(kWave) void conv_vv_recv_kernel(
   const auto xr = make_rsrc(x, (uint32_t)((size_t)N * NIN * C * 4));
   const auto vr = make_rsrc(HAS_VX ? v_x : x, (uint32_t)((size_t)N * NIN * C * 4));
 
-  float Wr[WREG ? kNB * G::NP : 1];
-  if constexpr (WREG) {
-    static_for<kNB * G::NP>([&](auto i) {
-      constexpr int b = i / G::NP, p = i % G::NP;
-      Wr[i] = W[(size_t)(b * P + G::p0 + p) * C + kk];
-    });
-  }
+  float Wr[kNB * G::NP];
+  static_for<kNB * G::NP>([&](auto i) {
+    constexpr int b = i / G::NP, p = i % G::NP;
+    Wr[i] = W[(size_t)(b * P + P0 + p) * C + kk];
+  });
   float acc[G::NR];
   static_for<G::NR>([&](auto i) { acc[i] = 0.f; });
 
@@ -132,15 +131,14 @@ __global__ __launch_bounds__(kWave) void conv_vv_recv_kernel(
       static_for<NIN>([&](auto c) { xv[c] = buf_load(xr, voff, sbase + c * C * 4); });
       if constexpr (HAS_VX) static_for<NIN>([&](auto c) { vx[c] = buf_load(vr, voff, sbase + c * C * 4); });
       static_for<G::NP>([&](auto pi) {
-        constexpr int p = G::p0 + pi;
+        constexpr int p = P0 + pi;
         constexpr PathInfo PI = Cfg::paths[p];
         constexpr int n1 = ncomp(PI.l1), o1 = rank_off(PI.l1), o2 = rank_off(PI.l2);
+        constexpr int lo = G::loff(p);
         float w = 0.f, w1 = 0.f;
         static_for<kNB>([&](auto b) {
           constexpr int bb = b;
-          float wb;
-          if constexpr (WREG) wb = Wr[bb * G::NP + pi];
-          else wb = W[(size_t)(bb * P + p) * C + kk];
+          const float wb = Wr[bb * G::NP + pi];
           w = fmaf(rec[2 * NE + bb], wb, w);
           w1 = fmaf(rec[2 * NE + kNB + bb], wb, w1);
         });
@@ -154,13 +152,12 @@ __global__ __launch_bounds__(kWave) void conv_vv_recv_kernel(
         constexpr int tb = tab::kTermBegin[PI.type], te = tab::kTermBegin[PI.type + 1];
         static_for<te - tb>([&](auto ti) {
           constexpr tab::Term T = tab::kTerms[tb + ti];
-          constexpr int row = Cfg::row(p, T.a) - G::r0;
           const float cy = T.c * rec[o2 + T.b2];
           const float cyd = T.c * rec[NE + o2 + T.b2];
-          float a = fmaf(cy, xd[T.b1], acc[row]);
+          float a = fmaf(cy, xd[T.b1], acc[lo + T.a]);
           a = fmaf(cyd, xw[T.b1], a);
           if constexpr (HAS_VX) a = fmaf(cy, vw[T.b1], a);
-          acc[row] = a;
+          acc[lo + T.a] = a;
         });
       });
     }
@@ -168,31 +165,41 @@ __global__ __launch_bounds__(kWave) void conv_vv_recv_kernel(
   }
   if (act) {
     float* zo = g_hat + (size_t)u * NOUT * C + k;
-    static_for<G::NR>([&](auto i) { zo[(size_t)(G::r0 + i) * C] = acc[i]; });
+    static_for<G::NP>([&](auto pi) {
+      constexpr int p = P0 + pi;
+      static_for<ncomp(Cfg::paths[p].L)>([&](auto c) {
+        constexpr int row = Cfg::row(p, c), li = G::loff(p) + c;
+        zo[(size_t)row * C] = acc[li];
+      });
+    });
   }
 }
 
-template <int LIN, int LEDGE, int LOUT, int LLO>
+template <int LIN, int LEDGE, int LOUT>
 void launch_vv_recv(const ConvArgs& a, hipStream_t st) {
   using Cfg = ConvCfg<LIN, LEDGE, LOUT>;
-  constexpr int LHI = group_end<Cfg, LOUT>(LLO);
+  using GS = PathGroups<Cfg, vv_recv_budget(Cfg::NIN)>;
   dim3 grid(a.N, (a.C + kWave - 1) / kWave);
-  if (a.v_x)
-    hipLaunchKernelGGL((conv_vv_recv_kernel<LIN, LEDGE, LOUT, LLO, LHI, true>), grid, dim3(kWave), 0, st, a.N,
-                       a.C, a.rowptr, a.sender, a.pos, a.shift, a.x, a.W, a.v_x, a.v_pos, a.g_hat, a.rc);
-  else
-    hipLaunchKernelGGL((conv_vv_recv_kernel<LIN, LEDGE, LOUT, LLO, LHI, false>), grid, dim3(kWave), 0, st, a.N,
-                       a.C, a.rowptr, a.sender, a.pos, a.shift, a.x, a.W, a.v_x, a.v_pos, a.g_hat, a.rc);
-  if constexpr (LHI < LOUT) launch_vv_recv<LIN, LEDGE, LOUT, LHI + 1>(a, st);
+  static_for<GS::n>([&](auto gi) {
+    constexpr int p0 = GS::start[gi], p1 = GS::start[gi + 1];
+    if (a.v_x)
+      hipLaunchKernelGGL((conv_vv_recv_kernel<LIN, LEDGE, LOUT, p0, p1, true>), grid, dim3(kWave), 0, st, a.N, a.C,
+                         a.rowptr, a.sender, a.pos, a.shift, a.x, a.W, a.v_x, a.v_pos, a.g_hat, a.rc);
+    else
+      hipLaunchKernelGGL((conv_vv_recv_kernel<LIN, LEDGE, LOUT, p0, p1, false>), grid, dim3(kWave), 0, st, a.N,
+                         a.C, a.rowptr, a.sender, a.pos, a.shift, a.x, a.W, a.v_x, a.v_pos, a.g_hat, a.rc);
+  });
 }
 
 // ------------------------------------------------- x_hat / pos_hat pass --
 template <int LIN, int LEDGE, int LOUT, bool HAS_VX>
 struct VVShape {
+  static constexpr int NIN = nrank(LIN);
   static constexpr int NE = nrank(LEDGE);
   // reductions: Yb, Yd, [Ya], S1, S2, S3
   static constexpr int NRED = (HAS_VX ? 3 : 2) * NE + 3;
   static constexpr int REC = 2 * NE + 3 * kNB + 2;   // y, ydot, R, R', R'', nd, receiver
+  static constexpr int budget = 200 - (HAS_VX ? 3 : 2) * (NIN + NE);
   static constexpr size_t lds_bytes(int nw) {
     return sizeof(float) * ((size_t)kWave * REC + (size_t)nw * kWave * NRED * 4);
   }
@@ -207,10 +214,10 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vv_sender_kernel(
     float* __restrict__ p_out, float* __restrict__ qbar, float rc) {
   using Cfg = ConvCfg<LIN, LEDGE, LOUT>;
   using Sh = VVShape<LIN, LEDGE, LOUT, HAS_VX>;
+  using GS = PathGroups<Cfg, Sh::budget>;
   constexpr int NIN = Cfg::NIN, NE = Cfg::NE, P = Cfg::P, NOUT = Cfg::NOUT;
   constexpr int REC = Sh::REC, NRED = Sh::NRED;
   constexpr int IYB = 0, IYD = NE, IYA = 2 * NE, IS = (HAS_VX ? 3 : 2) * NE;
-  constexpr bool WREG = kNB * P <= 96;
   extern __shared__ float lds[];
   float* geo = lds;
   float* part = lds + kWave * REC;
@@ -226,11 +233,6 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vv_sender_kernel(
   const int voff = kk * 4;
   const auto gr = make_rsrc(g, (uint32_t)((size_t)N * NOUT * C * 4));
 
-  float Wr[WREG ? kNB * P : 1];
-  if constexpr (WREG) {
-    static_for<kNB * P>([&](auto i) { Wr[i] = act ? W[(size_t)i * C + kk] : 0.f; });
-  }
-#define FC_WGET(B, PP) (WREG ? Wr[WREG ? (B) * P + (PP) : 0] : (act ? W[(size_t)((B) * P + (PP)) * C + kk] : 0.f))
   float xv[NIN], vx[HAS_VX ? NIN : 1];
   {
     const float* xs = x + (size_t)v * NIN * C + kk;
@@ -264,162 +266,189 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vv_sender_kernel(
     }
     return vv_geo(rx, ry, rz, dvx, dvy, dvz);
   };
-  for (int base = e0; base < e1; base += kWave) {
-    const int cnt = min(kWave, e1 - base);
-    if (wv == 0 && lane < cnt) {
-      const int e = t_edge[base + lane];
-      const int u = receiver[e];
-      const VVGeo Gm = edge_geo(e, u);
-      float y[NE], yd[NE], R[kNB], dR[kNB], d2R[kNB];
-      vv_tensors<LEDGE>(Gm, y, yd);
-      radial2(Gm.r, rc, R, dR, d2R);
-      float* rec = geo + lane * REC;
-      static_for<NE>([&](auto c) {
-        rec[c] = y[c];
-        rec[NE + c] = yd[c];
-      });
-      static_for<kNB>([&](auto b) {
-        rec[2 * NE + b] = R[b];
-        rec[2 * NE + kNB + b] = dR[b];
-        rec[2 * NE + 2 * kNB + b] = d2R[b];
-      });
-      rec[2 * NE + 3 * kNB] = Gm.nd;
-      rec[2 * NE + 3 * kNB + 1] = __int_as_float(u);
-    }
-    __syncthreads();
-    for (int j = 0; j < cnt; ++j) {
-      const float* rec = geo + j * REC;
-      const int u = uniform_int(__float_as_int(rec[2 * NE + 3 * kNB + 1]));
-      const float nd = rec[2 * NE + 3 * kNB];
-      const int ubase = u * NOUT * C * 4;
-      float gv[NOUT];
-      static_for<NOUT>([&](auto a) { gv[a] = buf_load(gr, voff, ubase + a * C * 4); });
-      float red[NRED];
-      static_for<NRED>([&](auto i) { red[i] = 0.f; });
-      static_for<P>([&](auto pc) {
-        constexpr int p = pc;
-        constexpr PathInfo PI = Cfg::paths[p];
-        constexpr int na = ncomp(PI.L), n2 = ncomp(PI.l2);
-        constexpr int o1 = rank_off(PI.l1), o2 = rank_off(PI.l2);
-        constexpr int tb = tab::kTermBegin[PI.type], te = tab::kTermBegin[PI.type + 1];
-        float w = 0.f, w1 = 0.f, w2 = 0.f;
-        static_for<kNB>([&](auto b) {
-          constexpr int bb = b;
-          const float wb = FC_WGET(bb, p);
-          w = fmaf(rec[2 * NE + bb], wb, w);
-          w1 = fmaf(rec[2 * NE + kNB + bb], wb, w1);
-          if constexpr (NEED_POS) w2 = fmaf(rec[2 * NE + 2 * kNB + bb], wb, w2);
-        });
-        const float wd = w1 * nd;
-        if constexpr (NEED_X) {
-          // x_hat[b1] += sum c g[a] (w ydot[b2] + wdot y[b2])
-          float gw[na], gd[na];
-          static_for<na>([&](auto a) {
-            constexpr int ra = Cfg::row(p, a);
-            gw[a] = w * gv[ra];
-            gd[a] = wd * gv[ra];
-          });
-          static_for<te - tb>([&](auto ti) {
-            constexpr tab::Term T = tab::kTerms[tb + ti];
-            float t = fmaf(T.c * rec[NE + o2 + T.b2], gw[T.a], xh[o1 + T.b1]);
-            xh[o1 + T.b1] = fmaf(T.c * rec[o2 + T.b2], gd[T.a], t);
-          });
-        }
-        if constexpr (NEED_POS) {
-          float be[n2], al[HAS_VX ? n2 : 1];
-          static_for<n2>([&](auto c) {
-            be[c] = 0.f;
-            if constexpr (HAS_VX) al[c] = 0.f;
-          });
-          static_for<te - tb>([&](auto ti) {
-            constexpr tab::Term T = tab::kTerms[tb + ti];
-            constexpr int ra = Cfg::row(p, T.a);
-            const float cg = T.c * gv[ra];
-            be[T.b2] = fmaf(cg, xv[o1 + T.b1], be[T.b2]);
-            if constexpr (HAS_VX) al[T.b2] = fmaf(cg, vx[o1 + T.b1], al[T.b2]);
-          });
-          float by = 0.f, bd = 0.f, ay = 0.f;
-          static_for<n2>([&](auto c) {
-            by = fmaf(be[c], rec[o2 + c], by);
-            bd = fmaf(be[c], rec[NE + o2 + c], bd);
-            red[IYB + o2 + c] = fmaf(w, be[c], red[IYB + o2 + c]);
-            red[IYD + o2 + c] = fmaf(w1, be[c], red[IYD + o2 + c]);
-            if constexpr (HAS_VX) {
-              ay = fmaf(al[c], rec[o2 + c], ay);
-              red[IYA + o2 + c] = fmaf(w, al[c], red[IYA + o2 + c]);
-            }
-          });
-          red[IS] = fmaf(w1, ay + bd, red[IS]);
-          red[IS + 1] = fmaf(w2, by, red[IS + 1]);
-          red[IS + 2] = fmaf(w1, by, red[IS + 2]);
-        }
-      });
-      if constexpr (NEED_POS) {
-        float* dst = part + ((size_t)(wv * kWave + j) * NRED) * 4 + (lane >> 4);
-        static_for<NRED>([&](auto i) {
-          const float t = row_sum16(red[i]);
-          if ((lane & 15) == 0) dst[i * 4] = t;
-        });
-      }
-    }
-    __syncthreads();
-    if constexpr (NEED_POS) {
+  // One sweep over the slice per path group, as in the VJP: x_hat stays in
+  // registers, q_e (linear in the per-edge sums) is summed over the sweeps.
+  static_for<GS::n>([&](auto gi) {
+    using G = typename GS::template group<gi>;
+    constexpr bool FIRST = gi == 0;
+    constexpr uint64_t MASK = G::comp_mask();
+    float Wr[kNB * G::NP];
+    static_for<kNB * G::NP>([&](auto i) {
+      constexpr int b = i / G::NP, pi = i % G::NP;
+      Wr[i] = act ? W[(size_t)(b * P + G::p0 + pi) * C + kk] : 0.f;
+    });
+    for (int base = e0; base < e1; base += kWave) {
+      const int cnt = min(kWave, e1 - base);
       if (wv == 0 && lane < cnt) {
         const int e = t_edge[base + lane];
         const int u = receiver[e];
-        float tot[NRED];
-        static_for<NRED>([&](auto i) { tot[i] = 0.f; });
-        for (int w2 = 0; w2 < NW; ++w2) {
-          const float4* src = reinterpret_cast<const float4*>(part + ((size_t)(w2 * kWave + lane) * NRED) * 4);
-          static_for<NRED>([&](auto i) {
-            const float4 q = src[i];
-            tot[i] += (q.x + q.y) + (q.z + q.w);
-          });
-        }
         const VVGeo Gm = edge_geo(e, u);
-        float ox = 0.f, oy = 0.f, oz = 0.f;
-        if (Gm.r > 0.f) {
-          // J_y^T (Ya + nd Yd) = (gA - n (n.gA)) / r, gA = grad_n of (Ya + nd Yd) . y
-          float cA[NE];
-          static_for<NE>([&](auto c) {
-            cA[c] = Gm.nd * tot[IYD + c];
-            if constexpr (HAS_VX) cA[c] += tot[IYA + c];
-          });
-          float gA[3], HA[6], gB[3], HB[6];
-          direction_contract_d2<LEDGE>(cA, Gm.nx, Gm.ny, Gm.nz, gA, HA);
-          direction_contract_d2<LEDGE>(tot + IYB, Gm.nx, Gm.ny, Gm.nz, gB, HB);
-          const float ngA = Gm.nx * gA[0] + Gm.ny * gA[1] + Gm.nz * gA[2];
-          ox = (gA[0] - Gm.nx * ngA) * Gm.inv;
-          oy = (gA[1] - Gm.ny * ngA) * Gm.inv;
-          oz = (gA[2] - Gm.nz * ngA) * Gm.inv;
-          // H_y[Yb] dv = [gdot - ndot (n.g) - n (ndot.g + n.gdot)] / r - nd (g - n (n.g)) / r^2
-          const float gdx = HB[0] * Gm.ndx + HB[3] * Gm.ndy + HB[4] * Gm.ndz;
-          const float gdy = HB[3] * Gm.ndx + HB[1] * Gm.ndy + HB[5] * Gm.ndz;
-          const float gdz = HB[4] * Gm.ndx + HB[5] * Gm.ndy + HB[2] * Gm.ndz;
-          const float ng = Gm.nx * gB[0] + Gm.ny * gB[1] + Gm.nz * gB[2];
-          const float ndg = Gm.ndx * gB[0] + Gm.ndy * gB[1] + Gm.ndz * gB[2];
-          const float ngd = Gm.nx * gdx + Gm.ny * gdy + Gm.nz * gdz;
-          const float t1 = ndg + ngd;
-          ox += (gdx - Gm.ndx * ng - Gm.nx * t1) * Gm.inv - Gm.nd * (gB[0] - Gm.nx * ng) * Gm.inv * Gm.inv;
-          oy += (gdy - Gm.ndy * ng - Gm.ny * t1) * Gm.inv - Gm.nd * (gB[1] - Gm.ny * ng) * Gm.inv * Gm.inv;
-          oz += (gdz - Gm.ndz * ng - Gm.nz * t1) * Gm.inv - Gm.nd * (gB[2] - Gm.nz * ng) * Gm.inv * Gm.inv;
-          // radial terms
-          const float sn = tot[IS] + tot[IS + 1] * Gm.nd;
-          ox += sn * Gm.nx + tot[IS + 2] * Gm.ndx;
-          oy += sn * Gm.ny + tot[IS + 2] * Gm.ndy;
-          oz += sn * Gm.nz + tot[IS + 2] * Gm.ndz;
-        }
-        qbar[3 * (size_t)e] = ox;
-        qbar[3 * (size_t)e + 1] = oy;
-        qbar[3 * (size_t)e + 2] = oz;
-        psum[0] += ox;
-        psum[1] += oy;
-        psum[2] += oz;
+        float y[NE], yd[NE], R[kNB], dR[kNB], d2R[kNB];
+        vv_tensors<LEDGE>(Gm, y, yd);
+        radial2(Gm.r, rc, R, dR, d2R);
+        float* rec = geo + lane * REC;
+        static_for<NE>([&](auto c) {
+          rec[c] = y[c];
+          rec[NE + c] = yd[c];
+        });
+        static_for<kNB>([&](auto b) {
+          rec[2 * NE + b] = R[b];
+          rec[2 * NE + kNB + b] = dR[b];
+          rec[2 * NE + 2 * kNB + b] = d2R[b];
+        });
+        rec[2 * NE + 3 * kNB] = Gm.nd;
+        rec[2 * NE + 3 * kNB + 1] = __int_as_float(u);
       }
       __syncthreads();
+      for (int j = 0; j < cnt; ++j) {
+        const float* rec = geo + j * REC;
+        const int u = uniform_int(__float_as_int(rec[2 * NE + 3 * kNB + 1]));
+        const float nd = rec[2 * NE + 3 * kNB];
+        const int ubase = u * NOUT * C * 4;
+        float gv[G::NR];
+        static_for<G::NP>([&](auto pi) {
+          constexpr int p = G::p0 + pi;
+          static_for<ncomp(Cfg::paths[p].L)>([&](auto c) {
+            constexpr int row = Cfg::row(p, c), li = G::loff(p) + c;
+            gv[li] = buf_load(gr, voff, ubase + row * C * 4);
+          });
+        });
+        float red[NRED];
+        static_for<NRED>([&](auto i) { red[i] = 0.f; });
+        static_for<G::NP>([&](auto pi) {
+          constexpr int p = G::p0 + pi;
+          constexpr PathInfo PI = Cfg::paths[p];
+          constexpr int na = ncomp(PI.L), n2 = ncomp(PI.l2);
+          constexpr int o1 = rank_off(PI.l1), o2 = rank_off(PI.l2);
+          constexpr int lo = G::loff(p);
+          constexpr int tb = tab::kTermBegin[PI.type], te = tab::kTermBegin[PI.type + 1];
+          float w = 0.f, w1 = 0.f, w2 = 0.f;
+          static_for<kNB>([&](auto b) {
+            constexpr int bb = b;
+            const float wb = Wr[bb * G::NP + pi];
+            w = fmaf(rec[2 * NE + bb], wb, w);
+            w1 = fmaf(rec[2 * NE + kNB + bb], wb, w1);
+            if constexpr (NEED_POS) w2 = fmaf(rec[2 * NE + 2 * kNB + bb], wb, w2);
+          });
+          const float wd = w1 * nd;
+          if constexpr (NEED_X) {
+            // x_hat[b1] += sum c g[a] (w ydot[b2] + wdot y[b2])
+            float gw[na], gd[na];
+            static_for<na>([&](auto a) {
+              gw[a] = w * gv[lo + a];
+              gd[a] = wd * gv[lo + a];
+            });
+            static_for<te - tb>([&](auto ti) {
+              constexpr tab::Term T = tab::kTerms[tb + ti];
+              float t = fmaf(T.c * rec[NE + o2 + T.b2], gw[T.a], xh[o1 + T.b1]);
+              xh[o1 + T.b1] = fmaf(T.c * rec[o2 + T.b2], gd[T.a], t);
+            });
+          }
+          if constexpr (NEED_POS) {
+            float be[n2], al[HAS_VX ? n2 : 1];
+            static_for<n2>([&](auto c) {
+              be[c] = 0.f;
+              if constexpr (HAS_VX) al[c] = 0.f;
+            });
+            static_for<te - tb>([&](auto ti) {
+              constexpr tab::Term T = tab::kTerms[tb + ti];
+              const float cg = T.c * gv[lo + T.a];
+              be[T.b2] = fmaf(cg, xv[o1 + T.b1], be[T.b2]);
+              if constexpr (HAS_VX) al[T.b2] = fmaf(cg, vx[o1 + T.b1], al[T.b2]);
+            });
+            float by = 0.f, bd = 0.f, ay = 0.f;
+            static_for<n2>([&](auto c) {
+              by = fmaf(be[c], rec[o2 + c], by);
+              bd = fmaf(be[c], rec[NE + o2 + c], bd);
+              red[IYB + o2 + c] = fmaf(w, be[c], red[IYB + o2 + c]);
+              red[IYD + o2 + c] = fmaf(w1, be[c], red[IYD + o2 + c]);
+              if constexpr (HAS_VX) {
+                ay = fmaf(al[c], rec[o2 + c], ay);
+                red[IYA + o2 + c] = fmaf(w, al[c], red[IYA + o2 + c]);
+              }
+            });
+            red[IS] = fmaf(w1, ay + bd, red[IS]);
+            red[IS + 1] = fmaf(w2, by, red[IS + 1]);
+            red[IS + 2] = fmaf(w1, by, red[IS + 2]);
+          }
+        });
+        if constexpr (NEED_POS) {
+          float* dst = part + ((size_t)(wv * kWave + j) * NRED) * 4 + (lane >> 4);
+          static_for<NRED>([&](auto i) {
+            if constexpr (i >= IS || ((MASK >> (i % NE)) & 1)) {
+              const float t = row_sum16(red[i]);
+              if ((lane & 15) == 0) dst[i * 4] = t;
+            }
+          });
+        }
+      }
+      __syncthreads();
+      if constexpr (NEED_POS) {
+        if (wv == 0 && lane < cnt) {
+          const int e = t_edge[base + lane];
+          const int u = receiver[e];
+          float tot[NRED];
+          static_for<NRED>([&](auto i) { tot[i] = 0.f; });
+          for (int w2 = 0; w2 < NW; ++w2) {
+            const float4* src = reinterpret_cast<const float4*>(part + ((size_t)(w2 * kWave + lane) * NRED) * 4);
+            static_for<NRED>([&](auto i) {
+              if constexpr (i >= IS || ((MASK >> (i % NE)) & 1)) {
+                const float4 q = src[i];
+                tot[i] += (q.x + q.y) + (q.z + q.w);
+              }
+            });
+          }
+          const VVGeo Gm = edge_geo(e, u);
+          float ox = 0.f, oy = 0.f, oz = 0.f;
+          if (Gm.r > 0.f) {
+            // J_y^T (Ya + nd Yd) = (gA - n (n.gA)) / r, gA = grad_n of (Ya + nd Yd) . y
+            float cA[NE];
+            static_for<NE>([&](auto c) {
+              cA[c] = Gm.nd * tot[IYD + c];
+              if constexpr (HAS_VX) cA[c] += tot[IYA + c];
+            });
+            float gA[3], HA[6], gB[3], HB[6];
+            direction_contract_d2<LEDGE, MASK>(cA, Gm.nx, Gm.ny, Gm.nz, gA, HA);
+            direction_contract_d2<LEDGE, MASK>(tot + IYB, Gm.nx, Gm.ny, Gm.nz, gB, HB);
+            const float ngA = Gm.nx * gA[0] + Gm.ny * gA[1] + Gm.nz * gA[2];
+            ox = (gA[0] - Gm.nx * ngA) * Gm.inv;
+            oy = (gA[1] - Gm.ny * ngA) * Gm.inv;
+            oz = (gA[2] - Gm.nz * ngA) * Gm.inv;
+            // H_y[Yb] dv = [gdot - ndot (n.g) - n (ndot.g + n.gdot)] / r - nd (g - n (n.g)) / r^2
+            const float gdx = HB[0] * Gm.ndx + HB[3] * Gm.ndy + HB[4] * Gm.ndz;
+            const float gdy = HB[3] * Gm.ndx + HB[1] * Gm.ndy + HB[5] * Gm.ndz;
+            const float gdz = HB[4] * Gm.ndx + HB[5] * Gm.ndy + HB[2] * Gm.ndz;
+            const float ng = Gm.nx * gB[0] + Gm.ny * gB[1] + Gm.nz * gB[2];
+            const float ndg = Gm.ndx * gB[0] + Gm.ndy * gB[1] + Gm.ndz * gB[2];
+            const float ngd = Gm.nx * gdx + Gm.ny * gdy + Gm.nz * gdz;
+            const float t1 = ndg + ngd;
+            ox += (gdx - Gm.ndx * ng - Gm.nx * t1) * Gm.inv - Gm.nd * (gB[0] - Gm.nx * ng) * Gm.inv * Gm.inv;
+            oy += (gdy - Gm.ndy * ng - Gm.ny * t1) * Gm.inv - Gm.nd * (gB[1] - Gm.ny * ng) * Gm.inv * Gm.inv;
+            oz += (gdz - Gm.ndz * ng - Gm.nz * t1) * Gm.inv - Gm.nd * (gB[2] - Gm.nz * ng) * Gm.inv * Gm.inv;
+            // radial terms
+            const float sn = tot[IS] + tot[IS + 1] * Gm.nd;
+            ox += sn * Gm.nx + tot[IS + 2] * Gm.ndx;
+            oy += sn * Gm.ny + tot[IS + 2] * Gm.ndy;
+            oz += sn * Gm.nz + tot[IS + 2] * Gm.ndz;
+          }
+          float* qe = qbar + 3 * (size_t)e;
+          if constexpr (FIRST) {
+            qe[0] = ox;
+            qe[1] = oy;
+            qe[2] = oz;
+          } else {
+            qe[0] += ox;
+            qe[1] += oy;
+            qe[2] += oz;
+          }
+          psum[0] += ox;
+          psum[1] += oy;
+          psum[2] += oz;
+        }
+        __syncthreads();
+      }
     }
-  }
-#undef FC_WGET
+  });
   const size_t slot = (size_t)v * S + sl;
   if (NEED_X && act) {
     float* xo = x_out + slot * NIN * C + k;
@@ -464,7 +493,7 @@ void launch_vv_sender_vx(const ConvArgs& a, const VjpWorkspace& wsl, hipStream_t
 // g_hat (when requested), then x_hat / pos_hat (when requested).
 template <int LIN, int LEDGE, int LOUT>
 void launch_vjp_vjp(const ConvArgs& a, hipStream_t st) {
-  if (a.g_hat) launch_vv_recv<LIN, LEDGE, LOUT, 0>(a, st);
+  if (a.g_hat) launch_vv_recv<LIN, LEDGE, LOUT>(a, st);
   if (!a.x_bar && !a.pos_bar) return;
   const VjpWorkspace wsl(a.N, a.E, a.C, nrank(LIN), a.rbar);
   if (a.v_x) launch_vv_sender_vx<LIN, LEDGE, LOUT, true>(a, wsl, st);

@@ -406,7 +406,7 @@ def emit_instances(gen_dir: str) -> list:
                f"#include \"../fc_conv_vv.h\"\n\n"
                f"namespace fc {{\n\n"
                f"bool conv_run_{a}{b}{c}(int op, const ConvArgs& args, hipStream_t stream) {{\n"
-               f"  if (op == 0) launch_fwd_groups<{a}, {b}, {c}, 0>(args, stream);\n"
+               f"  if (op == 0) launch_fwd<{a}, {b}, {c}>(args, stream);\n"
                f"  else if (op == 1) launch_vjp<{a}, {b}, {c}>(args, stream);\n"
                f"  else launch_vjp_vjp<{a}, {b}, {c}>(args, stream);\n"
                f"  return true;\n}}\n\n}}  // namespace fc\n")

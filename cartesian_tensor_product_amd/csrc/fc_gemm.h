@@ -52,10 +52,11 @@ struct GemmGroup {
   int tiles_m[kMaxGemmGroup];
   int tiles_n[kMaxGemmGroup];
   int kchunk[kMaxGemmGroup];
+  int mode[kMaxGemmGroup];   // operand staging modes (filled by gemm_group)
   GemmProblem prob[kMaxGemmGroup];
 };
 
-// Launches all problems of the group in one grid (block tile 32 x 128),
+// Launches all problems of the group in one grid (block tile 128 x 128),
 // then the split-K reductions if any problem uses them.
 void gemm_group(const GemmGroup& g, hipStream_t st);
 

@@ -1,21 +1,40 @@
 // Grouped FP32 GEMM on the gfx950 matrix cores.
 //
-// Block tile 32 (M) x 128 (N) x 32 (K), four waves; wave w owns output
-// columns [32w, 32w + 32) of the block tile and accumulates one 32x32 tile
-// with v_mfma_f32_32x32x2f32 (K = 2 per instruction).  Operand layout of that
-// instruction: lane l supplies A[l % 32][l / 32] and B[l / 32][l % 32]; the
-// sixteen accumulator registers r of lane l hold
-// D[8 (r / 4) + 4 (l / 32) + r % 4][l % 32].  Tiles are staged through LDS
-// k-major, so both operand reads are bank-conflict free.
+// Block tile 128 (M) x 128 (N) x 32 (K), four waves in a 2 x 2 grid; each
+// wave owns a 64 x 64 sub-tile held as 2 x 2 accumulators of
+// v_mfma_f32_32x32x2f32.  Operand layout of that instruction: lane l
+// supplies A[l % 32][l / 32] and B[l / 32][l % 32]; the sixteen accumulator
+// registers r of lane l hold D[8 (r / 4) + 4 (l / 32) + r % 4][l % 32].
+//
+// Reduction order inside a K tile: at MFMA step s (0..15) the lanes of half
+// h = l / 32 supply reduction index k = 16 h + s for both operands, so a
+// lane's sixteen A (or B) values of the tile are contiguous in a k-major
+// LDS row and come in four 128-bit LDS reads.
+//
+// Staging: a K tile is loaded into registers one tile ahead (global loads
+// in flight while the matrix cores work on the previous tile), then written
+// to LDS.  Each operand is staged in one of three ways, chosen per problem
+// on the host from its strides:
+//   kK  k contiguous:    128-bit loads along k, LDS rows [row][BK + 4];
+//   kR  rows contiguous: 128-bit loads along rows, LDS [k][rows + 4];
+//   kG  anything else:   scalar loads into the kK layout.
+// The paddings make the 128-bit LDS writes and the operand reads
+// conflict-free.
 #include "fc_gemm.h"
 
 namespace fc {
 
 namespace {
 
-constexpr int BM = 32, BN = 128, BK = 32, NT = 256;
+constexpr int BM = 128, BN = 128, BK = 32, NT = 256;
+constexpr int KPAD = BK + 4;     // kK / kG row length (floats)
+constexpr int RPAD = BM + 4;     // kR row length (floats)
+constexpr int SMEM = (BM * KPAD > BK * RPAD ? BM * KPAD : BK * RPAD);
+
+enum StageMode { kK = 0, kR = 1, kG = 2 };
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 // x / d for d <= 64, x < 2^26: q = umulhi(x, ceil(2^32 / d)) is exact.
 __device__ __forceinline__ int fdiv(int x, int d, uint32_t m) {
@@ -28,34 +47,109 @@ __device__ __forceinline__ long long two_level(int i, int d, uint32_t m, long lo
   return (long long)q * s1 + (long long)(i - q * d) * s2;
 }
 
-// Stage rows [r0, r0 + R) x cols [k0, k0 + BK) of a view into S[BK][R]
-// (k-major), zero outside [0, rows) x [k_lo, k_hi).
-template <int R>
-__device__ __forceinline__ void stage(const GView& v, int rows, int k_hi, int r0, int k0, float* S) {
-  constexpr int ELEMS = R * BK;
-  const bool k_contig = v.kdiv == 1 && v.sk1 == 1;
-  if (k_contig) {
-    // consecutive threads walk k of one row (contiguous in memory)
+__device__ __forceinline__ long long row_off(const GView& v, int r) { return two_level(r, v.div, v.mdiv, v.s1, v.s2); }
+__device__ __forceinline__ long long col_off(const GView& v, int k) {
+  return two_level(k, v.kdiv, v.mkdiv, v.sk1, v.sk2);
+}
+
+// Per-thread staging state of one operand (rows [r0, r0 + 128) of a view).
+// Elements per thread per K tile: 4 x float4 (kK, kR) or 16 scalars (kG).
+template <int MODE>
+struct Stager {
+  floatx4 reg[4];
+  long long base[4];   // kK: row offsets of the thread's four rows
+  bool rok[4];
+
+  __device__ __forceinline__ void init(const GView& v, int rows, int r0) {
+    if constexpr (MODE == kK) {
 #pragma unroll
-    for (int i = 0; i < ELEMS / NT; ++i) {
-      const int e = threadIdx.x + i * NT;
-      const int r = e / BK, kk = e % BK;
-      const int gr = r0 + r, gk = k0 + kk;
-      float val = 0.f;
-      if (gr < rows && gk < k_hi) val = v.p[two_level(gr, v.div, v.mdiv, v.s1, v.s2) + gk];
-      S[kk * R + r] = val;
+      for (int i = 0; i < 4; ++i) {
+        const int e = threadIdx.x + i * NT;
+        const int r = r0 + e / (BK / 4);
+        rok[i] = r < rows;
+        base[i] = rok[i] ? row_off(v, r) : 0;
+      }
+    } else if constexpr (MODE == kR) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = threadIdx.x + i * NT;
+        const int r = r0 + 4 * (e % (BM / 4));
+        rok[i] = r < rows;   // rows is a multiple of 4
+        base[i] = r;
+      }
     }
-  } else {
-    // consecutive threads walk rows
+  }
+
+  __device__ __forceinline__ void load(const GView& v, int rows, int r0, int k0, int k_hi) {
+    if constexpr (MODE == kK) {
 #pragma unroll
-    for (int i = 0; i < ELEMS / NT; ++i) {
-      const int e = threadIdx.x + i * NT;
-      const int kk = e / R, r = e % R;
-      const int gr = r0 + r, gk = k0 + kk;
-      float val = 0.f;
-      if (gr < rows && gk < k_hi)
-        val = v.p[two_level(gr, v.div, v.mdiv, v.s1, v.s2) + two_level(gk, v.kdiv, v.mkdiv, v.sk1, v.sk2)];
-      S[kk * R + r] = val;
+      for (int i = 0; i < 4; ++i) {
+        const int e = threadIdx.x + i * NT;
+        const int k = k0 + 4 * (e % (BK / 4));
+        if (rok[i] && k < k_hi) reg[i] = *reinterpret_cast<const floatx4*>(v.p + base[i] + k);
+        else reg[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+    } else if constexpr (MODE == kR) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = threadIdx.x + i * NT;
+        const int k = k0 + e / (BM / 4);
+        if (rok[i] && k < k_hi) reg[i] = *reinterpret_cast<const floatx4*>(v.p + col_off(v, k) + base[i]);
+        else reg[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+    } else {
+      // consecutive threads walk k of one row
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int e = threadIdx.x + i * NT;
+        const int r = r0 + e / BK, k = k0 + e % BK;
+        float val = 0.f;
+        if (r < rows && k < k_hi) val = v.p[row_off(v, r) + col_off(v, k)];
+        reg[i / 4][i % 4] = val;
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(float* S) const {
+    if constexpr (MODE == kK) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = threadIdx.x + i * NT;
+        *reinterpret_cast<floatx4*>(S + (e / (BK / 4)) * KPAD + 4 * (e % (BK / 4))) = reg[i];
+      }
+    } else if constexpr (MODE == kR) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = threadIdx.x + i * NT;
+        *reinterpret_cast<floatx4*>(S + (e / (BM / 4)) * RPAD + 4 * (e % (BM / 4))) = reg[i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int e = threadIdx.x + i * NT;
+        S[(e / BK) * KPAD + e % BK] = reg[i / 4][i % 4];
+      }
+    }
+  }
+};
+
+// The sixteen operand values (s = 0..15) of lane l for the 32-row block at
+// row offset t0 of the staged tile.
+template <int MODE>
+__device__ __forceinline__ void fetch(const float* S, int t0, int lane, float* o) {
+  const int m = t0 + lane % 32, h = lane / 32;
+  if constexpr (MODE == kR) {
+#pragma unroll
+    for (int s = 0; s < 16; ++s) o[s] = S[(16 * h + s) * RPAD + m];
+  } else {
+    const floatx4* src = reinterpret_cast<const floatx4*>(S + m * KPAD + 16 * h);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const floatx4 q = src[j];
+      o[4 * j] = q[0];
+      o[4 * j + 1] = q[1];
+      o[4 * j + 2] = q[2];
+      o[4 * j + 3] = q[3];
     }
   }
 }
@@ -67,9 +161,75 @@ __device__ __forceinline__ void store_out(const GOut& o, int m, int n, float val
   else *dst = val;
 }
 
+template <int MA, int MB>
+__device__ __forceinline__ void gemm_tile(const GemmProblem& P, int m0, int n0, int k_lo, int k_hi, int ks, float* As,
+                                          float* Bs) {
+  const int wv = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int wm = wv % 2, wn = wv / 2;
+  Stager<MA> sa;
+  Stager<MB> sb;
+  sa.init(P.A, P.M, m0);
+  sb.init(P.Bt, P.N, n0);
+  floatx16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  if (k_lo < k_hi) {
+    sa.load(P.A, P.M, m0, k_lo, k_hi);
+    sb.load(P.Bt, P.N, n0, k_lo, k_hi);
+  }
+  for (int k0 = k_lo; k0 < k_hi; k0 += BK) {
+    sa.store(As);
+    sb.store(Bs);
+    __syncthreads();
+    if (k0 + BK < k_hi) {
+      sa.load(P.A, P.M, m0, k0 + BK, k_hi);
+      sb.load(P.Bt, P.N, n0, k0 + BK, k_hi);
+    }
+    float a[2][16], b[2][16];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      fetch<MA>(As, wm * 64 + i * 32, lane, a[i]);
+      fetch<MB>(Bs, wn * 64 + i * 32, lane, b[i]);
+    }
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][s], b[j][s], acc[i][j], 0, 0, 0);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = n0 + wn * 64 + j * 32 + lane % 32;
+    if (n >= P.N) continue;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * 64 + i * 32 + 8 * (r / 4) + 4 * (lane / 32) + r % 4;
+        if (m >= P.M) continue;
+        if (P.ksplit > 1) {
+          P.part[(size_t)ks * P.M * P.N + (size_t)m * P.N + n] = acc[i][j][r];
+        } else {
+          const float val = P.alpha * acc[i][j][r];
+          store_out(P.C, m, n, val);
+          store_out(P.C2, m, n, val);
+        }
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(NT) void gemm_kernel(GemmGroup g) {
-  __shared__ float As[BK * BM];
-  __shared__ float Bs[BK * BN];
+  __shared__ __attribute__((aligned(16))) float As[SMEM];
+  __shared__ __attribute__((aligned(16))) float Bs[SMEM];
   int b = blockIdx.x, pi = 0;
   while (pi < g.count - 1 && b >= g.tiles_m[pi] * g.tiles_n[pi] * g.prob[pi].ksplit) {
     b -= g.tiles_m[pi] * g.tiles_n[pi] * g.prob[pi].ksplit;
@@ -83,42 +243,12 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmGroup g) {
   const int m0 = tm * BM, n0 = tn * BN;
   const int k_lo = ks * g.kchunk[pi];
   const int k_hi = min(P.K, k_lo + g.kchunk[pi]);
-  const int wv = threadIdx.x / 64, lane = threadIdx.x % 64;
-  floatx16 acc;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-
-  for (int k0 = k_lo; k0 < k_hi; k0 += BK) {
-    stage<BM>(P.A, P.M, k_hi, m0, k0, As);
-    stage<BN>(P.Bt, P.N, k_hi, n0, k0, Bs);
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 2) {
-      const float a = As[(kk + lane / 32) * BM + lane % 32];
-      const float bb = Bs[(kk + lane / 32) * BN + wv * 32 + lane % 32];
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bb, acc, 0, 0, 0);
-    }
-    __syncthreads();
-  }
-  const int n = n0 + wv * 32 + lane % 32;
-  if (n >= P.N) return;
-  if (P.ksplit > 1) {
-    float* part = P.part + (size_t)ks * P.M * P.N;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = m0 + 8 * (r / 4) + 4 * (lane / 32) + r % 4;
-      if (m < P.M) part[(size_t)m * P.N + n] = acc[r];
-    }
-    return;
-  }
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int m = m0 + 8 * (r / 4) + 4 * (lane / 32) + r % 4;
-    if (m < P.M) {
-      const float val = P.alpha * acc[r];
-      store_out(P.C, m, n, val);
-      store_out(P.C2, m, n, val);
-    }
+  switch (g.mode[pi]) {
+    case kK * 3 + kK: gemm_tile<kK, kK>(P, m0, n0, k_lo, k_hi, ks, As, Bs); break;
+    case kK * 3 + kR: gemm_tile<kK, kR>(P, m0, n0, k_lo, k_hi, ks, As, Bs); break;
+    case kR * 3 + kR: gemm_tile<kR, kR>(P, m0, n0, k_lo, k_hi, ks, As, Bs); break;
+    case kR * 3 + kK: gemm_tile<kR, kK>(P, m0, n0, k_lo, k_hi, ks, As, Bs); break;
+    default: gemm_tile<kG, kG>(P, m0, n0, k_lo, k_hi, ks, As, Bs); break;
   }
 }
 
@@ -135,6 +265,16 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(GemmProblem P) {
 }
 
 uint32_t magic(int d) { return d <= 1 ? 0u : (uint32_t)((0x100000000ull + d - 1) / d); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// Staging mode of a view with `rows` rows and reduction length K.
+int stage_mode(const GView& v, int rows, int K) {
+  if (!aligned16(v.p)) return kG;
+  if (v.kdiv == 1 && v.sk1 == 1 && K % 4 == 0 && v.s1 % 4 == 0 && (v.div == 1 || v.s2 % 4 == 0)) return kK;
+  if (v.div == 1 && v.s1 == 1 && rows % 4 == 0 && v.sk1 % 4 == 0 && (v.kdiv == 1 || v.sk2 % 4 == 0)) return kR;
+  return kG;
+}
 
 }  // namespace
 
@@ -162,6 +302,8 @@ void gemm_group(const GemmGroup& g0, hipStream_t st) {
     P.Bt.mkdiv = magic(P.Bt.kdiv);
     P.C.mdiv = magic(P.C.div);
     P.C2.mdiv = magic(P.C2.div);
+    const int ma = stage_mode(P.A, P.M, P.K), mb = stage_mode(P.Bt, P.N, P.K);
+    g.mode[i] = (ma == kG || mb == kG) ? kG * 3 + kG : ma * 3 + mb;
     total += g.tiles_m[i] * g.tiles_n[i] * P.ksplit;
   }
   if (total == 0) return;

@@ -106,3 +106,21 @@ def test_ladder_determinism():
     torch.cuda.synchronize()
     for u, v in zip(a, b):
         assert torch.equal(u, v)
+
+
+@pytest.mark.parametrize("C", [32, 160, 288])
+@pytest.mark.parametrize("l,l_out,order,variant", [(2, 2, 3, "full"), (3, 3, 2, "reduced")])
+def test_ladder_channel_tiles(l, l_out, order, variant, C):
+    """Channel counts that leave the 128-wide GEMM tiles partly filled (32),
+    or add a ragged last tile (160, 288), with a ragged node count."""
+    g = GpuLadder(l, l_out, order, variant, C=C, N=45, seed=11)
+    z = g.fwd()
+    Ab, Wb = g.vjp()
+    torch.cuda.synchronize()
+    f = lambda a: a.astype(np.float64)
+    zo = ladder.ladder_fwd(g.spec, f(g.A), [f(w) for w in g.ws])
+    Ao, Wo = ladder.ladder_vjp(g.spec, f(g.A), [f(w) for w in g.ws], f(g.gz))
+    assert_close("z", z.cpu().numpy(), zo)
+    assert_close("A_grad", Ab.cpu().numpy(), Ao)
+    for i, (got, want) in enumerate(zip(g.split(Wb.cpu().numpy()), Wo)):
+        assert_close(f"w_grad[{i}]", got, want)

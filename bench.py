@@ -31,17 +31,6 @@ HBM_PEAK_GBS = 8000.0
 MFMA_F32_PEAK_TFS = 157.3
 N_NODES, K_NBR, BOX, CHANNELS, LMAX, R_CUT, SEED = 1024, 128, 20.0, 128, 2, 5.0, 1
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_conv_vjp_sender_micro.json")
-KERNEL_SOURCES = ["cartesian_tensor_product_amd/csrc/fc_conv_kernels.h", "cartesian_tensor_product_amd/csrc/fc_common.h",
-                  "cartesian_tensor_product_amd/csrc/fc_conv.hip", "cartesian_tensor_product_amd/csrc/generated/fc_tables.h"]
-
-
-def kernel_source_sha() -> str:
-    import hashlib
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
 
 
 def measured_traffic():
@@ -52,7 +41,8 @@ def measured_traffic():
             t = json.load(fh)
     except OSError:
         return None
-    if t.get("kernel_source_sha") != kernel_source_sha():
+    from cartesian_tensor_product_amd.pmc import edge_kernel_source_sha
+    if t.get("kernel_source_sha") != edge_kernel_source_sha():
         return None
     return t["bytes_per_launch"]
 
@@ -72,7 +62,7 @@ def timed(fn, iters=10, warmup=2):
     return a.elapsed_time(b) / iters
 
 
-def extras(dev):
+def extras(dev, only_ladder=False):
     """Secondary workloads (reported beside the headline, not part of it)."""
     import torch
 
@@ -81,7 +71,7 @@ def extras(dev):
     out = {}
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     # high-rank microbenchmark: fwd, VJP, VJP-of-VJP (position cotangent)
-    for l in (3, 4):
+    for l in (() if only_ladder else (3, 4)):
         desc = fc.conv_desc(N_NODES, N_NODES * K_NBR, CHANNELS, l, l, l, R_CUT)
         P, n_in, n_out = fc.fc_conv_layout(desc)
         d = inputs.edge_conv_inputs(2, N_NODES, K_NBR, BOX, CHANNELS, n_in, P, n_out, with_vpos=True)
@@ -121,6 +111,8 @@ def extras(dev):
     out["ladder_full_4096n_128c_rank3_order4"]["mixing_gemm_gflop_fwd"] = ladder_gemm_gflop(4096, CHANNELS, 3, 4)
     lf = out["ladder_full_4096n_128c_rank3_order4"]
     lf["mixing_gemm_tflops_fwd_lower_bound"] = lf["mixing_gemm_gflop_fwd"] / lf["fwd_ms"]
+    if only_ladder:
+        return out
     # 1000-atom diamond block: energy and forces
     from cartesian_tensor_product_amd import inputs as inp
     cd_l = fc.ladder_desc(1000, CHANNELS, 3, 3, 0, 5, fc.FC_LADDER_PATH_REDUCED)
@@ -171,7 +163,7 @@ def algorithmic_bytes(N, E, C, n_in, n_out, P):
     return fwd, vjp
 
 
-def cpu_baseline(d, spec, n_recv=384):
+def cpu_baseline(d, spec, n_recv=768):
     """Oracle (numpy fp64, one thread) on the edges into the first n_recv receivers."""
     from threadpoolctl import threadpool_limits
 
@@ -197,6 +189,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the secondary workloads")
+    ap.add_argument("--ladder-only", action="store_true",
+                    help="only run the 4096-node ladder workloads (for counter runs) and print their timings")
     ap.add_argument("--copy-only", type=int, default=0, metavar="MB",
                     help="only run 5 device-to-device copies of MB megabytes (counter calibration)")
     args = ap.parse_args()
@@ -220,6 +214,9 @@ def main():
     from cartesian_tensor_product_amd import inputs
 
     dev = torch.device("cuda:0")
+    if args.ladder_only:
+        print(json.dumps(extras(dev, only_ladder=True)), flush=True)
+        return
     desc = fc.conv_desc(N_NODES, N_NODES * K_NBR, CHANNELS, LMAX, LMAX, LMAX, R_CUT)
     P, n_in, n_out = fc.fc_conv_layout(desc)
     d = inputs.edge_conv_inputs(SEED, N_NODES, K_NBR, BOX, CHANNELS, n_in, P, n_out)

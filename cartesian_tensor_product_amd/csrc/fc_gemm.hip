@@ -27,6 +27,7 @@ namespace fc {
 namespace {
 
 constexpr int BM = 128, BN = 128, BK = 32, NT = 256;
+constexpr int kMinSplitTiles = 16;   // K tiles per split-K block, at least
 constexpr int KPAD = BK + 4;     // kK / kG row length (floats)
 constexpr int RPAD = BM + 4;     // kR row length (floats)
 constexpr int SMEM = (BM * KPAD > BK * RPAD ? BM * KPAD : BK * RPAD);
@@ -252,13 +253,23 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmGroup g) {
   }
 }
 
-// Sum the ksplit partial tiles in split order, then store/add.
+// Sum the ksplit partial tiles in split order, then store/add.  Loads are
+// issued eight at a time; the additions stay in split order.
 __global__ __launch_bounds__(256) void split_reduce_kernel(GemmProblem P) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t MN = (size_t)P.M * P.N;
   if (i >= MN) return;
+  const float* src = P.part + i;
   float t = 0.f;
-  for (int s = 0; s < P.ksplit; ++s) t += P.part[(size_t)s * MN + i];
+  int s = 0;
+  for (; s + 8 <= P.ksplit; s += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = src[(size_t)(s + j) * MN];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t += v[j];
+  }
+  for (; s < P.ksplit; ++s) t += src[(size_t)s * MN];
   const int m = (int)(i / P.N), n = (int)(i % P.N);
   store_out(P.C, m, n, P.alpha * t);
   store_out(P.C2, m, n, P.alpha * t);
@@ -281,8 +292,11 @@ int stage_mode(const GView& v, int rows, int K) {
 int gemm_ksplit(int M, int N, int K, int target) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   int s = target / (tiles > 0 ? tiles : 1);
+  // every split covers at least kMinSplitTiles K tiles: short splits would
+  // spend more on writing their partial tile than on the products
   const int kt = (K + BK - 1) / BK;
-  if (s > kt) s = kt;
+  const int smax = (kt + kMinSplitTiles - 1) / kMinSplitTiles;
+  if (s > smax) s = smax;
   return s < 1 ? 1 : s;
 }
 

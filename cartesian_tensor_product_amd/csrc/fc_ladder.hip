@@ -24,6 +24,8 @@
 
 namespace fc {
 
+constexpr int kRedWaves = 4;   // waves per block of the path-reduced reverse kernel
+
 // ------------------------------------------------------- product kernels --
 
 // One step of the full ladder: B rows for all paths of ConvCfg<LP, LA, LQ>.
@@ -182,23 +184,29 @@ __global__ __launch_bounds__(kWave) void ladder_prod_vjp_kernel(int N, int C, co
 // (or, for q == 2, applies phi^1 = a1 A directly: A_bar += a1 G^1 and the
 // a1 gradient), adds sum_eta s_eta a_eta VJP2(G_L, phi_l1) into A_bar and
 // writes per-block partial gradients of a^q (and a1) summed over the tile.
+// A block holds kRedWaves waves over the same 64 channels; wave w takes the
+// nodes u0 + w, u0 + w + kRedWaves, ... of the tile, and the waves' partial
+// weight gradients are added in wave order through LDS.
 template <int LP, int LA, int LQ, bool FIRST>
-__global__ __launch_bounds__(kWave) void ladder_reduced_vjp_kernel(
+__global__ __launch_bounds__(kRedWaves * kWave) void ladder_reduced_vjp_kernel(
     int N, int C, int ntile, const float* __restrict__ G, int g_rows, const float* __restrict__ phi,
     const float* __restrict__ A, const float* __restrict__ Sbar, int s_rows, const float* __restrict__ aw,
     const float* __restrict__ a1, float* __restrict__ Gprev, float* __restrict__ Abar,
     float* __restrict__ apart, float* __restrict__ a1part) {
   using Cfg = ConvCfg<LP, LA, LQ>;
   constexpr int NP = nrank(LP), NA = nrank(LA), NQ = nrank(LQ);
-  const int k = blockIdx.y * kWave + threadIdx.x;
-  if (k >= C) return;
+  constexpr int NR = Cfg::P + (FIRST ? LP + 1 : 0);   // partial sums per lane
+  __shared__ float red[kRedWaves - 1][NR][kWave];
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int k = blockIdx.y * kWave + lane;
+  const bool active = k < C;
   float aacc[Cfg::P], a1acc[LP + 1];
   static_for<Cfg::P>([&](auto i) { aacc[i] = 0.f; });
   static_for<LP + 1>([&](auto i) { a1acc[i] = 0.f; });
   float aq[Cfg::P];
-  static_for<Cfg::P>([&](auto i) { aq[i] = aw[(size_t)i * C + k]; });
+  static_for<Cfg::P>([&](auto i) { aq[i] = active ? aw[(size_t)i * C + k] : 0.f; });
   const int u0 = blockIdx.x * ntile, u1 = min(N, u0 + ntile);
-  for (int u = u0; u < u1; ++u) {
+  for (int u = u0 + wave; active && u < u1; u += kRedWaves) {
     float g[NQ], x[NP], y[NA], gp[NP], ab[NA];
     static_for<NQ>([&](auto c) { g[c] = c < g_rows ? G[((size_t)u * g_rows + c) * C + k] : 0.f; });
     static_for<NP>([&](auto c) {
@@ -250,9 +258,20 @@ __global__ __launch_bounds__(kWave) void ladder_reduced_vjp_kernel(
     }
     static_for<NA>([&](auto c) { Abar[((size_t)u * NA + c) * C + k] += ab[c]; });
   }
-  static_for<Cfg::P>([&](auto i) { apart[((size_t)blockIdx.x * Cfg::P + i) * C + k] = aacc[i]; });
-  if constexpr (FIRST)
-    static_for<LP + 1>([&](auto i) { a1part[((size_t)blockIdx.x * (LP + 1) + i) * C + k] = a1acc[i]; });
+  if (wave > 0) {
+    static_for<Cfg::P>([&](auto i) { red[wave - 1][i][lane] = aacc[i]; });
+    if constexpr (FIRST) static_for<LP + 1>([&](auto i) { red[wave - 1][Cfg::P + i][lane] = a1acc[i]; });
+  }
+  __syncthreads();
+  if (wave == 0 && active) {
+    for (int w = 0; w < kRedWaves - 1; ++w) {
+      static_for<Cfg::P>([&](auto i) { aacc[i] += red[w][i][lane]; });
+      if constexpr (FIRST) static_for<LP + 1>([&](auto i) { a1acc[i] += red[w][Cfg::P + i][lane]; });
+    }
+    static_for<Cfg::P>([&](auto i) { apart[((size_t)blockIdx.x * Cfg::P + i) * C + k] = aacc[i]; });
+    if constexpr (FIRST)
+      static_for<LP + 1>([&](auto i) { a1part[((size_t)blockIdx.x * (LP + 1) + i) * C + k] = a1acc[i]; });
+  }
 }
 
 // Path-reduced ladder of order 1: z = W (a1 A), so A_bar = a1 Sbar and the
@@ -279,14 +298,32 @@ __global__ __launch_bounds__(kWave) void ladder_reduced_first_kernel(int N, int 
   for (int l = 0; l <= lout; ++l) a1part[((size_t)blockIdx.x * (lout + 1) + l) * C + k] = acc[l];
 }
 
-// out[i] = sum_b part[b][i], fixed order.
+// out[i] = sum_b part[b][i] in a fixed order: a block of four waves covers
+// 64 consecutive i, wave w sums the w-th quarter of the b range in b order,
+// and the four quarter sums are added in wave order.
 __global__ __launch_bounds__(256) void block_sum_kernel(int nblk, int n, const float* __restrict__ part,
                                                         float* __restrict__ out) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
+  __shared__ float red[3][kWave];
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int i = blockIdx.x * kWave + lane;
+  const int per = (nblk + 3) / 4;
+  const int b0 = min(nblk, wave * per), b1 = min(nblk, b0 + per);
   float t = 0.f;
-  for (int b = 0; b < nblk; ++b) t += part[(size_t)b * n + i];
-  out[i] = t;
+  if (i < n) {
+    const float* src = part + i;
+    int b = b0;
+    for (; b + 8 <= b1; b += 8) {
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = src[(size_t)(b + j) * n];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) t += v[j];
+    }
+    for (; b < b1; ++b) t += src[(size_t)b * n];
+  }
+  if (wave > 0) red[wave - 1][lane] = t;
+  __syncthreads();
+  if (wave == 0 && i < n) out[i] = ((t + red[0][lane]) + red[1][lane]) + red[2][lane];
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(size_t n, float* __restrict__ p) {
@@ -568,10 +605,10 @@ void launch_red_vjp(const LadderPlan& p, bool first, const float* G, int g_rows,
                     float* a1part, hipStream_t st) {
   dim3 grid((p.N + kNTile - 1) / kNTile, (p.C + kWave - 1) / kWave);
   if (first)
-    hipLaunchKernelGGL((ladder_reduced_vjp_kernel<LP, LP, LQ, true>), grid, dim3(kWave), 0, st, p.N, p.C, kNTile,
+    hipLaunchKernelGGL((ladder_reduced_vjp_kernel<LP, LP, LQ, true>), grid, dim3(kRedWaves * kWave), 0, st, p.N, p.C, kNTile,
                        G, g_rows, phi, A, Sbar, nr(p.lout), aw, a1, Gprev, Abar, apart, a1part);
   else
-    hipLaunchKernelGGL((ladder_reduced_vjp_kernel<LP, LP, LQ, false>), grid, dim3(kWave), 0, st, p.N, p.C, kNTile,
+    hipLaunchKernelGGL((ladder_reduced_vjp_kernel<LP, LP, LQ, false>), grid, dim3(kRedWaves * kWave), 0, st, p.N, p.C, kNTile,
                        G, g_rows, phi, A, Sbar, nr(p.lout), aw, a1, Gprev, Abar, apart, a1part);
 }
 
@@ -611,7 +648,7 @@ void fill_zero(float* p, size_t n, hipStream_t st) {
 }
 
 void block_sum(int nblk, int n, const float* part, float* out, hipStream_t st) {
-  hipLaunchKernelGGL(block_sum_kernel, dim3((n + 255) / 256), dim3(256), 0, st, nblk, n, part, out);
+  hipLaunchKernelGGL(block_sum_kernel, dim3((n + kWave - 1) / kWave), dim3(4 * kWave), 0, st, nblk, n, part, out);
 }
 
 // element (n, k) = W[k * ld + n]: the weight matrix used untransposed

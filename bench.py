@@ -82,13 +82,16 @@ def extras(dev, only_ladder=False):
         gh, xh, ph = torch.empty_like(z), torch.empty_like(x), torch.empty_like(pb)
         ws = fc.workspace(max(fc.fc_edge_conv_workspace_bytes(desc, 1), fc.fc_edge_conv_workspace_bytes(desc, 2)), dev)
         E = N_NODES * K_NBR
+        Wb = torch.empty_like(W)
         r = {"fwd_ms": timed(lambda: fc.fc_edge_conv_fwd(desc, graph, pos, None, x, W, z)),
              "vjp_ms": timed(lambda: fc.fc_edge_conv_vjp(desc, graph, pos, None, x, W, g, xb, pb, None, ws)),
+             "radial_w_grad_ms": timed(lambda: fc.fc_edge_conv_vjp(desc, graph, pos, None, x, W, g, None, None, Wb,
+                                                                   ws)),
              "vjp_vjp_ms": timed(lambda: fc.fc_edge_conv_vjp_vjp(desc, graph, pos, None, x, W, g, None, vp, gh, xh,
                                                                  ph, None, ws), iters=5)}
         r["fwd_plus_vjp_edge_channels_per_s"] = E * CHANNELS / ((r["fwd_ms"] + r["vjp_ms"]) * 1e-3)
         out[f"conv_rank{l}_1024n_128c_128nbr"] = r
-        del z, xb, pb, gh, xh, ph, ws
+        del z, xb, pb, gh, xh, ph, ws, Wb
     # node-local ladder, 4096 nodes, 128 channels, ranks <= 3, order 4, both variants
     for name, var in (("full", fc.FC_LADDER_FULL), ("path_reduced", fc.FC_LADDER_PATH_REDUCED)):
         ld = fc.ladder_desc(4096, CHANNELS, 3, 3, 3, 4, var)
@@ -289,6 +292,13 @@ def main():
                       "wall_s": wall},
     }
     if not args.no_extras:
+        # the radial-weight gradient (optional VJP output, a receiver-sorted
+        # pass of its own), timed alone and with the rest of the VJP
+        Wb = torch.empty_like(W)
+        out["breakdown"]["radial_w_grad_ms"] = timed(
+            lambda: fc.fc_edge_conv_vjp(desc, graph, pos, None, x, W, g, None, None, Wb, ws))
+        out["breakdown"]["vjp_with_radial_w_grad_ms"] = timed(
+            lambda: fc.fc_edge_conv_vjp(desc, graph, pos, None, x, W, g, xb, pb, Wb, ws))
         out["extras"] = extras(dev)
     if not args.no_cpu_baseline:
         from oracle import conv

@@ -202,7 +202,9 @@ fc_status fc_graph_validate(int32_t n_nodes, int32_t n_edges, const int32_t* h_r
 size_t fc_edge_conv_workspace_bytes(const fc_conv_desc* d, int32_t op) {
   if (check_desc(d) != FC_OK) return 0;
   if (op == 1 || op == 2) {
-    const fc::VjpWorkspace w(d->n_nodes, d->n_edges, d->channels, (d->l_in + 1) * (d->l_in + 1), nullptr);
+    int P, nin, nout;
+    layout(d, &P, &nin, &nout);
+    const fc::VjpWorkspace w(d->n_nodes, d->n_edges, d->channels, nin, P, op == 1, nullptr);
     return w.bytes;
   }
   return 0;
@@ -232,9 +234,8 @@ fc_status fc_edge_conv_vjp(const fc_conv_desc* d, const fc_graph* g, const float
     return fail(FC_ERR_INVALID_ARGUMENT, "VJP needs the full graph (run fc_graph_transpose first)");
   if (!pos || !x || !radial_w || !g_z) return fail(FC_ERR_INVALID_ARGUMENT, "VJP: NULL pos, x, radial_w or g_z");
   if (!x_grad && !pos_grad && !radial_w_grad) return fail(FC_ERR_INVALID_ARGUMENT, "VJP: no output requested");
-  if (radial_w_grad) return fail(FC_ERR_UNSUPPORTED, "VJP: radial_w_grad is not implemented in this build");
   if (misaligned(pos, 4) || misaligned(x, 4) || misaligned(radial_w, 4) || misaligned(g_z, 4) ||
-      misaligned(x_grad, 4) || misaligned(pos_grad, 4) || misaligned(shift, 4))
+      misaligned(x_grad, 4) || misaligned(pos_grad, 4) || misaligned(radial_w_grad, 4) || misaligned(shift, 4))
     return fail(FC_ERR_INVALID_ARGUMENT, "VJP: arrays must be 4-byte aligned");
   const size_t need = fc_edge_conv_workspace_bytes(d, 1);
   if (need > 0 && (!workspace || workspace_bytes < need))
@@ -243,6 +244,7 @@ fc_status fc_edge_conv_vjp(const fc_conv_desc* d, const fc_graph* g, const float
   a.g = g_z;
   a.x_bar = x_grad;
   a.pos_bar = pos_grad;
+  a.W_bar = radial_w_grad;
   a.rbar = static_cast<float*>(workspace);
   fc::conv_dispatch(1, d->l_in, d->l_edge, d->l_out, a, stream);
   return check_launch("edge conv VJP");

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include "fc_common.h"
+#include "fc_reduce.h"
 
 namespace fc {
 
@@ -17,6 +18,8 @@ struct ConvArgs {
   // x_hat and pos_hat reuse x_bar and pos_bar, the per-edge term reuses rbar
   const float *v_x, *v_pos;
   float* g_hat;
+  // VJP: gradient of the radial weights W [8][P][C] (nullable)
+  float* W_bar;
 };
 
 #include "generated/fc_conv_configs.h"
@@ -37,13 +40,18 @@ inline int vjp_slices(int N, int E) {
 
 inline size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
+// Receivers (one per wave) of a block of the radial-weight gradient pass.
+inline constexpr int kWgWaves = 4;
+inline int wgrad_blocks(int N) { return (N + kWgWaves - 1) / kWgWaves; }
+
 // VJP workspace: per-edge position cotangents, then (S > 1) per-slice
-// partial position sums and partial x_bar.
+// partial position sums and partial x_bar, then (with_w) the per-block
+// partial radial-weight gradients [wgrad_blocks(N)][8][P][C].
 struct VjpWorkspace {
   int S;
-  float *rbar, *p_part, *x_part;
+  float *rbar, *p_part, *x_part, *w_part;
   size_t bytes;
-  VjpWorkspace(int N, int E, int C, int nin, void* base) {
+  VjpWorkspace(int N, int E, int C, int nin, int P, bool with_w, void* base) {
     S = vjp_slices(N, E);
     char* p = static_cast<char*>(base);
     size_t off = 0;
@@ -53,8 +61,10 @@ struct VjpWorkspace {
     if (S > 1) off += align256((size_t)3 * N * S * sizeof(float));
     x_part = reinterpret_cast<float*>(p + off);
     if (S > 1) off += align256((size_t)N * S * nin * C * sizeof(float));
+    w_part = reinterpret_cast<float*>(p + off);
+    if (with_w) off += align256((size_t)wgrad_blocks(N) * kNB * P * C * sizeof(float));
     bytes = off;
-    if (!base) rbar = p_part = x_part = nullptr;
+    if (!base) rbar = p_part = x_part = w_part = nullptr;
   }
 };
 

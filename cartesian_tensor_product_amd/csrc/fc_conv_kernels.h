@@ -66,6 +66,31 @@ struct EdgeProducts {
   }
 };
 
+// Receiver-sorted edge record: direction-tensor entries (or their coefficient
+// products), the eight radial values and the sender id of edge e into u.
+template <int LIN, int LEDGE, int LOUT>
+__device__ __forceinline__ void recv_edge_record(int e, const int* __restrict__ sender, const float* __restrict__ pos,
+                                                 const float* __restrict__ shift, float pux, float puy, float puz,
+                                                 float rc, float* rec) {
+  using EP = EdgeProducts<LIN, LEDGE, LOUT>;
+  constexpr int NE = nrank(LEDGE);
+  const int s = sender[e];
+  float rx = pos[3 * s] - pux, ry = pos[3 * s + 1] - puy, rz = pos[3 * s + 2] - puz;
+  if (shift) {
+    rx += shift[3 * e];
+    ry += shift[3 * e + 1];
+    rz += shift[3 * e + 2];
+  }
+  const float r = sqrtf(rx * rx + ry * ry + rz * rz);
+  const float inv = r > 0.f ? 1.f / r : 0.f;
+  float y[NE], R[kNB];
+  direction_tensors<LEDGE>(rx * inv, ry * inv, rz * inv, y);
+  radial<false>(r, rc, R, nullptr);
+  EP::fill(y, rec);
+  static_for<kNB>([&](auto b) { rec[EP::NY + b] = R[b]; });
+  rec[EP::NY + kNB] = __int_as_float(s);
+}
+
 // ============================================================== forward ====
 // One launch per path group G: z rows of G's paths for node u and 64 channels.
 template <int LIN, int LEDGE, int LOUT, int P0, int P1>
@@ -100,25 +125,8 @@ __global__ __launch_bounds__(kWave) void conv_fwd_kernel(
   const float pux = pos[3 * u], puy = pos[3 * u + 1], puz = pos[3 * u + 2];
   for (int base = e0; base < e1; base += kWave) {
     const int cnt = min(kWave, e1 - base);
-    if (lane < cnt) {
-      const int e = base + lane;
-      const int s = sender[e];
-      float rx = pos[3 * s] - pux, ry = pos[3 * s + 1] - puy, rz = pos[3 * s + 2] - puz;
-      if (shift) {
-        rx += shift[3 * e];
-        ry += shift[3 * e + 1];
-        rz += shift[3 * e + 2];
-      }
-      const float r = sqrtf(rx * rx + ry * ry + rz * rz);
-      const float inv = r > 0.f ? 1.f / r : 0.f;
-      float y[NE], R[kNB];
-      direction_tensors<LEDGE>(rx * inv, ry * inv, rz * inv, y);
-      radial<false>(r, rc, R, nullptr);
-      float* rec = geo + lane * REC;
-      EP::fill(y, rec);
-      static_for<kNB>([&](auto b) { rec[EP::NY + b] = R[b]; });
-      rec[EP::NY + kNB] = __int_as_float(s);
-    }
+    if (lane < cnt)
+      recv_edge_record<LIN, LEDGE, LOUT>(base + lane, sender, pos, shift, pux, puy, puz, rc, geo + lane * REC);
     __syncthreads();
     for (int j = 0; j < cnt; ++j) {
       const float* rec = geo + j * REC;
@@ -170,6 +178,124 @@ void launch_fwd(const ConvArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((conv_fwd_kernel<LIN, LEDGE, LOUT, p0, p1>), grid, dim3(kWave), 0, st, a.N, a.C, a.rowptr,
                        a.sender, a.pos, a.shift, a.x, a.W, a.z, a.rc);
   });
+}
+
+// ============================================ radial-weight gradient ====
+// W_bar[b, p, k] = sum_e R_b(r_e) <g[u_e, p, k], f_p(x[v_e, k], y_e)>, the
+// weight-gradient line of Eq. C1 carried through w = R W.  Receiver-sorted
+// like the forward: a block of kWgWaves waves covers kWgWaves consecutive
+// receivers (one each) and 64 channels; wave w keeps g[u_w] of the group's
+// paths in registers, evaluates f_p(x_v, y_e) for every incoming edge from
+// the broadcast edge record, and accumulates R_b w_bar_p in kNB x NP
+// registers.  The waves' sums are added in wave order through LDS and the
+// block writes one partial [kNB][P][C] slab; launch_block_sum adds the slabs
+// in block order.  One launch per path group.
+template <int LIN, int LEDGE, int LOUT, int P0, int P1>
+__global__ __launch_bounds__(kWgWaves * kWave) void conv_wgrad_kernel(
+    int N, int C, const int* __restrict__ rowptr, const int* __restrict__ sender,
+    const float* __restrict__ pos, const float* __restrict__ shift, const float* __restrict__ x,
+    const float* __restrict__ g, float* __restrict__ wpart, float rc) {
+  using Cfg = ConvCfg<LIN, LEDGE, LOUT>;
+  using G = PathGroup<Cfg, P0, P1>;
+  using EP = EdgeProducts<LIN, LEDGE, LOUT>;
+  constexpr int NIN = Cfg::NIN, P = Cfg::P, NOUT = Cfg::NOUT;
+  constexpr int REC = EP::NY + kNB + 1;
+  constexpr int NACC = kNB * G::NP;
+  // edge records of every wave; reused afterwards for the cross-wave sums
+  constexpr int LDS = (kWgWaves * kWave * REC > kWave * NACC) ? kWgWaves * kWave * REC : kWave * NACC;
+  __shared__ float lds[LDS];
+
+  const int wv = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int u0 = blockIdx.x * kWgWaves, u = u0 + wv;
+  const bool has_u = u < N;
+  const int k = blockIdx.y * kWave + lane;
+  const bool act = k < C;
+  const int kk = act ? k : 0;
+  const int voff = kk * 4;
+  const auto xr = make_rsrc(x, (uint32_t)((size_t)N * NIN * C * 4));
+  float* geo = lds + wv * kWave * REC;
+
+  float gv[G::NR];
+  static_for<G::NP>([&](auto pi) {
+    constexpr int p = P0 + pi;
+    static_for<ncomp(Cfg::paths[p].L)>([&](auto c) {
+      constexpr int row = Cfg::row(p, c), li = G::loff(p) + c;
+      gv[li] = (act && has_u) ? g[((size_t)u * NOUT + row) * C + k] : 0.f;
+    });
+  });
+  float acc[NACC];
+  static_for<NACC>([&](auto i) { acc[i] = 0.f; });
+
+  // chunk count shared by the block's waves (they meet at every barrier)
+  int nch = 0;
+  for (int i = 0; i < kWgWaves; ++i)
+    if (u0 + i < N) nch = max(nch, (rowptr[u0 + i + 1] - rowptr[u0 + i] + kWave - 1) / kWave);
+  const int e0 = has_u ? rowptr[u] : 0, e1 = has_u ? rowptr[u + 1] : 0;
+  const float pux = has_u ? pos[3 * u] : 0.f, puy = has_u ? pos[3 * u + 1] : 0.f, puz = has_u ? pos[3 * u + 2] : 0.f;
+  for (int ch = 0; ch < nch; ++ch) {
+    const int base = e0 + ch * kWave;
+    const int cnt = max(0, min(kWave, e1 - base));
+    if (lane < cnt)
+      recv_edge_record<LIN, LEDGE, LOUT>(base + lane, sender, pos, shift, pux, puy, puz, rc, geo + lane * REC);
+    __syncthreads();
+    for (int j = 0; j < cnt; ++j) {
+      const float* rec = geo + j * REC;
+      const int s = uniform_int(__float_as_int(rec[EP::NY + kNB]));
+      const int sbase = s * NIN * C * 4;
+      float xv[NIN];
+      static_for<NIN>([&](auto c) { xv[c] = buf_load(xr, voff, sbase + c * C * 4); });
+      static_for<G::NP>([&](auto pi) {
+        constexpr int p = P0 + pi;
+        constexpr PathInfo PI = Cfg::paths[p];
+        constexpr int na = ncomp(PI.L), o1 = rank_off(PI.l1), o2 = rank_off(PI.l2);
+        constexpr int lo = G::loff(p);
+        constexpr int tb = tab::kTermBegin[PI.type], te = tab::kTermBegin[PI.type + 1];
+        float f[na];
+        static_for<te - tb>([&](auto ti) {
+          constexpr int tt = tb + ti;
+          constexpr tab::Term T = tab::kTerms[tt];
+          const float cy = EP::template cy<tt, o2 + T.b2>(rec);
+          if constexpr (T.fa) f[T.a] = cy * xv[o1 + T.b1];
+          else f[T.a] = fmaf(cy, xv[o1 + T.b1], f[T.a]);
+        });
+        float wb = 0.f;
+        static_for<na>([&](auto a) { wb = fmaf(gv[lo + a], f[a], wb); });
+        static_for<kNB>([&](auto b) {
+          constexpr int bb = b;
+          acc[bb * G::NP + pi] = fmaf(rec[EP::NY + bb], wb, acc[bb * G::NP + pi]);
+        });
+      });
+    }
+    __syncthreads();
+  }
+  // wave 0 adds the other waves' sums in wave order
+  for (int w = 1; w < kWgWaves; ++w) {
+    if (wv == w) static_for<NACC>([&](auto i) { lds[i * kWave + lane] = acc[i]; });
+    __syncthreads();
+    if (wv == 0) static_for<NACC>([&](auto i) { acc[i] += lds[i * kWave + lane]; });
+    __syncthreads();
+  }
+  if (wv == 0 && act) {
+    float* dst = wpart + (size_t)blockIdx.x * kNB * P * C + k;
+    static_for<NACC>([&](auto i) {
+      constexpr int b = i / G::NP, pi = i % G::NP;
+      dst[((size_t)b * P + P0 + pi) * C] = acc[i];
+    });
+  }
+}
+
+template <int LIN, int LEDGE, int LOUT>
+void launch_wgrad(const ConvArgs& a, float* wpart, hipStream_t st) {
+  using Cfg = ConvCfg<LIN, LEDGE, LOUT>;
+  using GS = PathGroups<Cfg, fwd_budget(Cfg::NIN)>;
+  const int nblk = wgrad_blocks(a.N);
+  dim3 grid(nblk, (a.C + kWave - 1) / kWave);
+  static_for<GS::n>([&](auto gi) {
+    constexpr int p0 = GS::start[gi], p1 = GS::start[gi + 1];
+    hipLaunchKernelGGL((conv_wgrad_kernel<LIN, LEDGE, LOUT, p0, p1>), grid, dim3(kWgWaves * kWave), 0, st, a.N, a.C,
+                       a.rowptr, a.sender, a.pos, a.shift, a.x, a.g, wpart, a.rc);
+  });
+  launch_block_sum(nblk, kNB * Cfg::P * a.C, wpart, a.W_bar, st);
 }
 
 // ================================================================== VJP ====
@@ -460,7 +586,9 @@ template <int LIN, int LEDGE, int LOUT>
 void launch_vjp(const ConvArgs& a, hipStream_t st) {
   const bool nx = a.x_bar != nullptr, np = a.pos_bar != nullptr;
   const int nw = (a.C + kWave - 1) / kWave;
-  const VjpWorkspace wsl(a.N, a.E, a.C, nrank(LIN), a.rbar);
+  const VjpWorkspace wsl(a.N, a.E, a.C, nrank(LIN), ConvCfg<LIN, LEDGE, LOUT>::P, true, a.rbar);
+  if (a.W_bar) launch_wgrad<LIN, LEDGE, LOUT>(a, wsl.w_part, st);
+  if (!nx && !np) return;
   float* xo = wsl.S == 1 ? a.x_bar : wsl.x_part;
   float* po = wsl.S == 1 ? a.pos_bar : wsl.p_part;
   dim3 grid(a.N, wsl.S), block(nw * kWave);

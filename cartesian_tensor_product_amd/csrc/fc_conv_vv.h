@@ -495,7 +495,7 @@ template <int LIN, int LEDGE, int LOUT>
 void launch_vjp_vjp(const ConvArgs& a, hipStream_t st) {
   if (a.g_hat) launch_vv_recv<LIN, LEDGE, LOUT>(a, st);
   if (!a.x_bar && !a.pos_bar) return;
-  const VjpWorkspace wsl(a.N, a.E, a.C, nrank(LIN), a.rbar);
+  const VjpWorkspace wsl(a.N, a.E, a.C, nrank(LIN), ConvCfg<LIN, LEDGE, LOUT>::P, false, a.rbar);
   if (a.v_x) launch_vv_sender_vx<LIN, LEDGE, LOUT, true>(a, wsl, st);
   else launch_vv_sender_vx<LIN, LEDGE, LOUT, false>(a, wsl, st);
   launch_vjp_combine(a, wsl, nrank(LIN), st);

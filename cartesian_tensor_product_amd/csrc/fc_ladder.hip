@@ -21,6 +21,7 @@
 #include "fc_common.h"
 #include "fc_gemm.h"
 #include "fc_ladder.h"
+#include "fc_reduce.h"
 
 namespace fc {
 
@@ -296,34 +297,6 @@ __global__ __launch_bounds__(kWave) void ladder_reduced_first_kernel(int N, int 
       acc[l] = fmaf(sb, A[((size_t)u * a_rows + c) * C + k], acc[l]);
     }
   for (int l = 0; l <= lout; ++l) a1part[((size_t)blockIdx.x * (lout + 1) + l) * C + k] = acc[l];
-}
-
-// out[i] = sum_b part[b][i] in a fixed order: a block of four waves covers
-// 64 consecutive i, wave w sums the w-th quarter of the b range in b order,
-// and the four quarter sums are added in wave order.
-__global__ __launch_bounds__(256) void block_sum_kernel(int nblk, int n, const float* __restrict__ part,
-                                                        float* __restrict__ out) {
-  __shared__ float red[3][kWave];
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int i = blockIdx.x * kWave + lane;
-  const int per = (nblk + 3) / 4;
-  const int b0 = min(nblk, wave * per), b1 = min(nblk, b0 + per);
-  float t = 0.f;
-  if (i < n) {
-    const float* src = part + i;
-    int b = b0;
-    for (; b + 8 <= b1; b += 8) {
-      float v[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = src[(size_t)(b + j) * n];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) t += v[j];
-    }
-    for (; b < b1; ++b) t += src[(size_t)b * n];
-  }
-  if (wave > 0) red[wave - 1][lane] = t;
-  __syncthreads();
-  if (wave == 0 && i < n) out[i] = ((t + red[0][lane]) + red[1][lane]) + red[2][lane];
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(size_t n, float* __restrict__ p) {
@@ -648,7 +621,7 @@ void fill_zero(float* p, size_t n, hipStream_t st) {
 }
 
 void block_sum(int nblk, int n, const float* part, float* out, hipStream_t st) {
-  hipLaunchKernelGGL(block_sum_kernel, dim3((n + kWave - 1) / kWave), dim3(4 * kWave), 0, st, nblk, n, part, out);
+  launch_block_sum(nblk, n, part, out, st);
 }
 
 // element (n, k) = W[k * ld + n]: the weight matrix used untransposed

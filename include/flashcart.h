@@ -137,9 +137,12 @@ fc_status fc_edge_conv_fwd(const fc_conv_desc* d, const fc_graph* g, const float
 
 /* VJP of L = <g_z, z> (Eq. C1 and the chain rule through T_l and R_b).
  * x_grad [N][in_rows][C] and pos_grad [N][3] are written when non-NULL;
- * radial_w_grad [8][P][C] is written when non-NULL.  At least one output
- * must be requested.  Needs the full graph (transpose included) and a
- * workspace of fc_edge_conv_workspace_bytes(d, 1) bytes. */
+ * radial_w_grad [8][P][C] is written when non-NULL: the weight-gradient
+ * line of Eq. C1 carried through w = R W, i.e.
+ * radial_w_grad[b, eta, k] = sum_e R_b(r_e) <g_z[u_e, eta, k], f_eta(x[v_e, k], T(r_hat_e))>,
+ * computed by a separate receiver-sorted pass and reduced in a fixed order.
+ * At least one output must be requested.  Needs the full graph (transpose
+ * included) and a workspace of fc_edge_conv_workspace_bytes(d, 1) bytes. */
 fc_status fc_edge_conv_vjp(const fc_conv_desc* d, const fc_graph* g, const float* pos,
                            const float* shift, const float* x, const float* radial_w,
                            const float* g_z, float* x_grad, float* pos_grad,

@@ -55,13 +55,15 @@ class GpuConv:
                                      dv(v_pos), gh, xh, ph, None, ws)
         return gh, xh, ph
 
-    def vjp(self, g=None, want_x=True, want_pos=True):
+    def vjp(self, g=None, want_x=True, want_pos=True, want_W=False):
+        """(x_grad, pos_grad), or (x_grad, pos_grad, radial_w_grad) with want_W."""
         g = self.g if g is None else g
         xb = self.torch.empty_like(self.x) if want_x else None
         pb = self.torch.empty((self.N, 3), device=self.device) if want_pos else None
-        self.fc.fc_edge_conv_vjp(self.desc, self.graph, self.pos, self.shift, self.x, self.W, g, xb, pb, None,
+        Wb = self.torch.empty_like(self.W) if want_W else None
+        self.fc.fc_edge_conv_vjp(self.desc, self.graph, self.pos, self.shift, self.x, self.W, g, xb, pb, Wb,
                                  self.ws)
-        return xb, pb
+        return (xb, pb, Wb) if want_W else (xb, pb)
 
 
 def sample_edges(rowptr, sender, nodes):

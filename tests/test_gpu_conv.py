@@ -16,23 +16,25 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 
-def oracle_all(spec, d, edges=None):
+def oracle_all(spec, d, edges=None, g=None):
     a = (spec, f64(d["pos"]), d["rowptr"], d["sender"], f64(d["x"]), f64(d["W"]))
     z = conv.edge_conv_fwd(*a, shift=f64(d.get("shift")), edges=edges)
-    xb, pb, _ = conv.edge_conv_vjp(*a, f64(d["g"]), shift=f64(d.get("shift")), edges=edges)
-    return z, xb, pb
+    g = d["g"] if g is None else g
+    xb, pb, Wb = conv.edge_conv_vjp(*a, f64(g), shift=f64(d.get("shift")), edges=edges, want_W=True)
+    return z, xb, pb, Wb
 
 
 def check_full(ranks, rc, d, C):
     spec = conv.ConvSpec(*ranks, rc)
     gc = GpuConv(ranks, rc, d, C)
     z = gc.fwd()
-    xb, pb = gc.vjp()
+    xb, pb, Wb = gc.vjp(want_W=True)
     torch.cuda.synchronize()
-    zo, xo, po = oracle_all(spec, d)
+    zo, xo, po, Wo = oracle_all(spec, d)
     assert_close("z", z.cpu().numpy(), zo)
     assert_close("x_grad", xb.cpu().numpy(), xo)
     assert_close("pos_grad", pb.cpu().numpy(), po)
+    assert_close("radial_w_grad", Wb.cpu().numpy(), Wo)
 
 
 def tiny_inputs(ranks, C, seed=0, n=32, k=8, box=6.0, rc=6.0):
@@ -86,9 +88,21 @@ def test_empty_graph():
              W=inputs.normal(rng, (8, spec.n_paths, C)), g=inputs.normal(rng, (N, spec.n_out, C)))
     gc = GpuConv((2, 2, 2), 5.0, d, C)
     z = gc.fwd()
-    xb, pb = gc.vjp()
+    xb, pb, Wb = gc.vjp(want_W=True)
     torch.cuda.synchronize()
     assert torch.count_nonzero(z) == 0 and torch.count_nonzero(xb) == 0 and torch.count_nonzero(pb) == 0
+    assert torch.count_nonzero(Wb) == 0
+
+
+@pytest.mark.parametrize("ranks", [(1, 1, 1), (2, 2, 2), (0, 3, 3)])
+def test_radial_weight_grad_alone(ranks):
+    """radial_w_grad requested without x_grad and pos_grad (receiver pass only)."""
+    spec, d = tiny_inputs(ranks, 40, seed=8, n=70, k=30, box=7.0, rc=6.0)
+    gc = GpuConv(ranks, 6.0, d, 40)
+    _, _, Wb = gc.vjp(want_x=False, want_pos=False, want_W=True)
+    torch.cuda.synchronize()
+    Wo = oracle_all(spec, d)[3]
+    assert_close("radial_w_grad", Wb.cpu().numpy(), Wo)
 
 
 def test_graph_transpose_matches_stable_sort():
@@ -130,13 +144,22 @@ def test_microbenchmark_sampled(ranks, seed, rc):
     gc = GpuConv(ranks, rc, d, 128)
     z = gc.fwd()
     xb, pb = gc.vjp()
-    torch.cuda.synchronize()
+    # radial-weight gradient of a cotangent that vanishes off the sampled
+    # receivers: only their incoming edges contribute, so the oracle sums
+    # exactly those
     nodes = np.random.default_rng(99).choice(1024, size=12, replace=False)
+    gm = np.zeros_like(d["g"])
+    gm[nodes] = d["g"][nodes]
+    _, _, Wb = gc.vjp(g=torch.from_numpy(gm).cuda(), want_x=False, want_pos=False, want_W=True)
+    torch.cuda.synchronize()
     edges = sample_edges(d["rowptr"], d["sender"], nodes)
-    zo, xo, po = oracle_all(spec, d, edges=edges)
+    zo, xo, po, _ = oracle_all(spec, d, edges=edges)
+    recv = np.repeat(np.arange(1024), np.diff(d["rowptr"]))
+    Wo = oracle_all(spec, d, edges=np.nonzero(np.isin(recv, nodes))[0], g=gm)[3]
     assert_close("z", z.cpu().numpy()[nodes], zo[nodes])
     assert_close("x_grad", xb.cpu().numpy()[nodes], xo[nodes])
     assert_close("pos_grad", pb.cpu().numpy()[nodes], po[nodes])
+    assert_close("radial_w_grad", Wb.cpu().numpy(), Wo)
     # properties that hold at any size: translation invariance of the forces
     p = pb.double().cpu().numpy()
     assert np.abs(p.sum(0)).max() < 1e-4 * np.abs(p).max() * np.sqrt(1024)
@@ -145,8 +168,8 @@ def test_microbenchmark_sampled(ranks, seed, rc):
 def test_bitwise_determinism():
     spec, d = micro((2, 2, 2), 1, 5.0)
     gc = GpuConv((2, 2, 2), 5.0, d, 128)
-    a = [gc.fwd(), *gc.vjp()]
-    b = [gc.fwd(), *gc.vjp()]
+    a = [gc.fwd(), *gc.vjp(want_W=True)]
+    b = [gc.fwd(), *gc.vjp(want_W=True)]
     torch.cuda.synchronize()
     for u, v in zip(a, b):
         assert torch.equal(u, v)

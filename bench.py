@@ -88,7 +88,9 @@ def extras(dev, only_ladder=False):
              "radial_w_grad_ms": timed(lambda: fc.fc_edge_conv_vjp(desc, graph, pos, None, x, W, g, None, None, Wb,
                                                                    ws)),
              "vjp_vjp_ms": timed(lambda: fc.fc_edge_conv_vjp_vjp(desc, graph, pos, None, x, W, g, None, vp, gh, xh,
-                                                                 ph, None, ws), iters=5)}
+                                                                 ph, None, ws), iters=5),
+             "radial_w_hat_ms": timed(lambda: fc.fc_edge_conv_vjp_vjp(desc, graph, pos, None, x, W, g, None, vp,
+                                                                      None, None, None, Wb, ws), iters=5)}
         r["fwd_plus_vjp_edge_channels_per_s"] = E * CHANNELS / ((r["fwd_ms"] + r["vjp_ms"]) * 1e-3)
         out[f"conv_rank{l}_1024n_128c_128nbr"] = r
         del z, xb, pb, gh, xh, ph, ws, Wb

@@ -204,7 +204,7 @@ size_t fc_edge_conv_workspace_bytes(const fc_conv_desc* d, int32_t op) {
   if (op == 1 || op == 2) {
     int P, nin, nout;
     layout(d, &P, &nin, &nout);
-    const fc::VjpWorkspace w(d->n_nodes, d->n_edges, d->channels, nin, P, op == 1, nullptr);
+    const fc::VjpWorkspace w(d->n_nodes, d->n_edges, d->channels, nin, P, true, nullptr);
     return w.bytes;
   }
   return 0;
@@ -256,20 +256,20 @@ fc_status fc_edge_conv_vjp_vjp(const fc_conv_desc* d, const fc_graph* g, const f
                                float* radial_w_hat, void* workspace, size_t workspace_bytes,
                                hipStream_t stream) {
   if (fc_status s = check_desc(d)) return s;
-  if (radial_w_hat) return fail(FC_ERR_UNSUPPORTED, "VJP-of-VJP: radial_w_hat is not implemented in this build");
-  if (!g_hat && !x_hat && !pos_hat) return fail(FC_ERR_INVALID_ARGUMENT, "VJP-of-VJP: no output requested");
+  if (!g_hat && !x_hat && !pos_hat && !radial_w_hat)
+    return fail(FC_ERR_INVALID_ARGUMENT, "VJP-of-VJP: no output requested");
   if (!g || !g->rowptr || (d->n_edges > 0 && !g->sender))
     return fail(FC_ERR_INVALID_ARGUMENT, "VJP-of-VJP needs graph rowptr and sender");
   if ((x_hat || pos_hat) && (!g->t_rowptr || (d->n_edges > 0 && (!g->receiver || !g->t_edge))))
     return fail(FC_ERR_INVALID_ARGUMENT, "VJP-of-VJP: x_hat/pos_hat need the graph transpose");
-  if (!pos || !x || !radial_w || ((x_hat || pos_hat) && !g_z))
+  if (!pos || !x || !radial_w || ((x_hat || pos_hat || radial_w_hat) && !g_z))
     return fail(FC_ERR_INVALID_ARGUMENT, "VJP-of-VJP: NULL pos, x, radial_w or g_z");
   if (misaligned(pos, 4) || misaligned(x, 4) || misaligned(radial_w, 4) || misaligned(g_z, 4) ||
       misaligned(v_x, 4) || misaligned(v_pos, 4) || misaligned(g_hat, 4) || misaligned(x_hat, 4) ||
-      misaligned(pos_hat, 4) || misaligned(shift, 4))
+      misaligned(pos_hat, 4) || misaligned(radial_w_hat, 4) || misaligned(shift, 4))
     return fail(FC_ERR_INVALID_ARGUMENT, "VJP-of-VJP: arrays must be 4-byte aligned");
   const size_t need = fc_edge_conv_workspace_bytes(d, 2);
-  if ((x_hat || pos_hat) && need > 0 && (!workspace || workspace_bytes < need))
+  if ((x_hat || pos_hat || radial_w_hat) && need > 0 && (!workspace || workspace_bytes < need))
     return fail(FC_ERR_WORKSPACE, "VJP-of-VJP needs %zu workspace bytes", need);
   fc::ConvArgs a = make_args(d, g, pos, shift, x, radial_w);
   a.g = g_z;
@@ -278,6 +278,7 @@ fc_status fc_edge_conv_vjp_vjp(const fc_conv_desc* d, const fc_graph* g, const f
   a.g_hat = g_hat;
   a.x_bar = x_hat;
   a.pos_bar = pos_hat;
+  a.W_bar = radial_w_hat;
   a.rbar = static_cast<float*>(workspace);
   fc::conv_dispatch(2, d->l_in, d->l_edge, d->l_out, a, stream);
   return check_launch("edge conv VJP-of-VJP");

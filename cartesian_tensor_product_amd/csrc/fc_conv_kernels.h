@@ -190,6 +190,28 @@ void launch_fwd(const ConvArgs& a, hipStream_t st) {
 // registers.  The waves' sums are added in wave order through LDS and the
 // block writes one partial [kNB][P][C] slab; launch_block_sum adds the slabs
 // in block order.  One launch per path group.
+// Adds the kWgWaves waves' accumulators acc[b * NP + pi] in wave order
+// (through `red`, kWave * kNB * NP floats that every wave may overwrite)
+// and stores the block's slab rows b, P0 + pi of wpart [blocks][kNB][P][C].
+template <int NP, int P0, int P>
+__device__ __forceinline__ void wgrad_block_store(float* acc, float* red, int wv, int lane, int k, bool act, int C,
+                                                  float* __restrict__ wpart) {
+  constexpr int NACC = kNB * NP;
+  for (int w = 1; w < kWgWaves; ++w) {
+    __syncthreads();
+    if (wv == w) static_for<NACC>([&](auto i) { red[i * kWave + lane] = acc[i]; });
+    __syncthreads();
+    if (wv == 0) static_for<NACC>([&](auto i) { acc[i] += red[i * kWave + lane]; });
+  }
+  if (wv == 0 && act) {
+    float* dst = wpart + (size_t)blockIdx.x * kNB * P * C + k;
+    static_for<NACC>([&](auto i) {
+      constexpr int b = i / NP, pi = i % NP;
+      dst[((size_t)b * P + P0 + pi) * C] = acc[i];
+    });
+  }
+}
+
 template <int LIN, int LEDGE, int LOUT, int P0, int P1>
 __global__ __launch_bounds__(kWgWaves * kWave) void conv_wgrad_kernel(
     int N, int C, const int* __restrict__ rowptr, const int* __restrict__ sender,
@@ -268,20 +290,7 @@ __global__ __launch_bounds__(kWgWaves * kWave) void conv_wgrad_kernel(
     }
     __syncthreads();
   }
-  // wave 0 adds the other waves' sums in wave order
-  for (int w = 1; w < kWgWaves; ++w) {
-    if (wv == w) static_for<NACC>([&](auto i) { lds[i * kWave + lane] = acc[i]; });
-    __syncthreads();
-    if (wv == 0) static_for<NACC>([&](auto i) { acc[i] += lds[i * kWave + lane]; });
-    __syncthreads();
-  }
-  if (wv == 0 && act) {
-    float* dst = wpart + (size_t)blockIdx.x * kNB * P * C + k;
-    static_for<NACC>([&](auto i) {
-      constexpr int b = i / G::NP, pi = i % G::NP;
-      dst[((size_t)b * P + P0 + pi) * C] = acc[i];
-    });
-  }
+  wgrad_block_store<G::NP, P0, P>(acc, lds, wv, lane, k, act, C, wpart);
 }
 
 template <int LIN, int LEDGE, int LOUT>

@@ -191,6 +191,156 @@ void launch_vv_recv(const ConvArgs& a, hipStream_t st) {
   });
 }
 
+// --------------------------------------------------------- W_hat pass --
+// W_hat[b, p, k] = d W_bar[b, p, k] / d eps along (v_x, v_pos):
+//   sum_e R'_b nd <g_u, f_p(x_v, y)> + R_b <g_u, f_p(x_v, ydot) + f_p(v_x[v], y)>,
+// nd = r_hat . dv_e, ydot = J_y dv_e.  Same block shape and fixed-order
+// reduction as the W_bar pass; edges are staged 32 per chunk so that the
+// four waves' records (y, ydot, R, R' nd, sender) fit in LDS at rank 4.
+inline constexpr int kWhChunk = 32;
+// path-group budget: g (2L+1) and kNB accumulators per path, below the g_hat
+// pass's budget by the per-path f and f-dot temporaries
+__host__ __device__ constexpr int wgrad_vv_budget(int nin) { return 176 - 3 * nin; }
+
+template <int LIN, int LEDGE, int LOUT, int P0, int P1, bool HAS_VX>
+__global__ __launch_bounds__(kWgWaves * kWave) void conv_wgrad_vv_kernel(
+    int N, int C, const int* __restrict__ rowptr, const int* __restrict__ sender, const float* __restrict__ pos,
+    const float* __restrict__ shift, const float* __restrict__ x, const float* __restrict__ g,
+    const float* __restrict__ v_x, const float* __restrict__ v_pos, float* __restrict__ wpart, float rc) {
+  using Cfg = ConvCfg<LIN, LEDGE, LOUT>;
+  using G = PathGroup<Cfg, P0, P1>;
+  constexpr int NIN = Cfg::NIN, NE = Cfg::NE, P = Cfg::P, NOUT = Cfg::NOUT;
+  constexpr int REC = 2 * NE + 2 * kNB + 1;   // y, ydot, R, R' nd, sender
+  constexpr int NACC = kNB * G::NP;
+  constexpr int LDS = (kWgWaves * kWhChunk * REC > kWave * NACC) ? kWgWaves * kWhChunk * REC : kWave * NACC;
+  __shared__ float lds[LDS];
+
+  const int wv = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int u0 = blockIdx.x * kWgWaves, u = u0 + wv;
+  const bool has_u = u < N;
+  const int k = blockIdx.y * kWave + lane;
+  const bool act = k < C;
+  const int kk = act ? k : 0;
+  const int voff = kk * 4;
+  const auto xr = make_rsrc(x, (uint32_t)((size_t)N * NIN * C * 4));
+  const auto vr = make_rsrc(HAS_VX ? v_x : x, (uint32_t)((size_t)N * NIN * C * 4));
+  float* geo = lds + wv * kWhChunk * REC;
+
+  float gv[G::NR];
+  static_for<G::NP>([&](auto pi) {
+    constexpr int p = P0 + pi;
+    static_for<ncomp(Cfg::paths[p].L)>([&](auto c) {
+      constexpr int row = Cfg::row(p, c), li = G::loff(p) + c;
+      gv[li] = (act && has_u) ? g[((size_t)u * NOUT + row) * C + k] : 0.f;
+    });
+  });
+  float acc[NACC];
+  static_for<NACC>([&](auto i) { acc[i] = 0.f; });
+
+  int nch = 0;
+  for (int i = 0; i < kWgWaves; ++i)
+    if (u0 + i < N) nch = max(nch, (rowptr[u0 + i + 1] - rowptr[u0 + i] + kWhChunk - 1) / kWhChunk);
+  const int e0 = has_u ? rowptr[u] : 0, e1 = has_u ? rowptr[u + 1] : 0;
+  const float pux = has_u ? pos[3 * u] : 0.f, puy = has_u ? pos[3 * u + 1] : 0.f, puz = has_u ? pos[3 * u + 2] : 0.f;
+  const bool vp = v_pos != nullptr && has_u;
+  const float vux = vp ? v_pos[3 * u] : 0.f, vuy = vp ? v_pos[3 * u + 1] : 0.f, vuz = vp ? v_pos[3 * u + 2] : 0.f;
+  for (int ch = 0; ch < nch; ++ch) {
+    const int base = e0 + ch * kWhChunk;
+    const int cnt = max(0, min(kWhChunk, e1 - base));
+    if (lane < cnt) {
+      const int e = base + lane;
+      const int s = sender[e];
+      float rx = pos[3 * s] - pux, ry = pos[3 * s + 1] - puy, rz = pos[3 * s + 2] - puz;
+      if (shift) {
+        rx += shift[3 * e];
+        ry += shift[3 * e + 1];
+        rz += shift[3 * e + 2];
+      }
+      float dvx = 0.f, dvy = 0.f, dvz = 0.f;
+      if (vp) {
+        dvx = v_pos[3 * s] - vux;
+        dvy = v_pos[3 * s + 1] - vuy;
+        dvz = v_pos[3 * s + 2] - vuz;
+      }
+      const VVGeo Gm = vv_geo(rx, ry, rz, dvx, dvy, dvz);
+      float y[NE], yd[NE], R[kNB], dR[kNB];
+      vv_tensors<LEDGE>(Gm, y, yd);
+      radial<true>(Gm.r, rc, R, dR);
+      float* rec = geo + lane * REC;
+      static_for<NE>([&](auto c) {
+        rec[c] = y[c];
+        rec[NE + c] = yd[c];
+      });
+      static_for<kNB>([&](auto b) {
+        rec[2 * NE + b] = R[b];
+        rec[2 * NE + kNB + b] = dR[b] * Gm.nd;
+      });
+      rec[2 * NE + 2 * kNB] = __int_as_float(s);
+    }
+    __syncthreads();
+    for (int j = 0; j < cnt; ++j) {
+      const float* rec = geo + j * REC;
+      const int s = uniform_int(__float_as_int(rec[2 * NE + 2 * kNB]));
+      const int sbase = s * NIN * C * 4;
+      float xv[NIN], vx[HAS_VX ? NIN : 1];
+      static_for<NIN>([&](auto c) { xv[c] = buf_load(xr, voff, sbase + c * C * 4); });
+      if constexpr (HAS_VX) static_for<NIN>([&](auto c) { vx[c] = buf_load(vr, voff, sbase + c * C * 4); });
+      static_for<G::NP>([&](auto pi) {
+        constexpr int p = P0 + pi;
+        constexpr PathInfo PI = Cfg::paths[p];
+        constexpr int na = ncomp(PI.L), o1 = rank_off(PI.l1), o2 = rank_off(PI.l2);
+        constexpr int lo = G::loff(p);
+        constexpr int tb = tab::kTermBegin[PI.type], te = tab::kTermBegin[PI.type + 1];
+        float f[na], fd[na];
+        static_for<te - tb>([&](auto ti) {
+          constexpr tab::Term T = tab::kTerms[tb + ti];
+          const float cy = T.c * rec[o2 + T.b2];
+          const float cyd = T.c * rec[NE + o2 + T.b2];
+          float d = cyd * xv[o1 + T.b1];
+          if constexpr (HAS_VX) d = fmaf(cy, vx[o1 + T.b1], d);
+          if constexpr (T.fa) {
+            f[T.a] = cy * xv[o1 + T.b1];
+            fd[T.a] = d;
+          } else {
+            f[T.a] = fmaf(cy, xv[o1 + T.b1], f[T.a]);
+            fd[T.a] += d;
+          }
+        });
+        float wb = 0.f, wbd = 0.f;
+        static_for<na>([&](auto a) {
+          wb = fmaf(gv[lo + a], f[a], wb);
+          wbd = fmaf(gv[lo + a], fd[a], wbd);
+        });
+        static_for<kNB>([&](auto b) {
+          constexpr int bb = b;
+          float t = fmaf(rec[2 * NE + kNB + bb], wb, acc[bb * G::NP + pi]);
+          acc[bb * G::NP + pi] = fmaf(rec[2 * NE + bb], wbd, t);
+        });
+      });
+    }
+    __syncthreads();
+  }
+  wgrad_block_store<G::NP, P0, P>(acc, lds, wv, lane, k, act, C, wpart);
+}
+
+template <int LIN, int LEDGE, int LOUT>
+void launch_wgrad_vv(const ConvArgs& a, float* wpart, hipStream_t st) {
+  using Cfg = ConvCfg<LIN, LEDGE, LOUT>;
+  using GS = PathGroups<Cfg, wgrad_vv_budget(Cfg::NIN)>;
+  const int nblk = wgrad_blocks(a.N);
+  dim3 grid(nblk, (a.C + kWave - 1) / kWave);
+  static_for<GS::n>([&](auto gi) {
+    constexpr int p0 = GS::start[gi], p1 = GS::start[gi + 1];
+    if (a.v_x)
+      hipLaunchKernelGGL((conv_wgrad_vv_kernel<LIN, LEDGE, LOUT, p0, p1, true>), grid, dim3(kWgWaves * kWave), 0, st,
+                         a.N, a.C, a.rowptr, a.sender, a.pos, a.shift, a.x, a.g, a.v_x, a.v_pos, wpart, a.rc);
+    else
+      hipLaunchKernelGGL((conv_wgrad_vv_kernel<LIN, LEDGE, LOUT, p0, p1, false>), grid, dim3(kWgWaves * kWave), 0,
+                         st, a.N, a.C, a.rowptr, a.sender, a.pos, a.shift, a.x, a.g, a.v_x, a.v_pos, wpart, a.rc);
+  });
+  launch_block_sum(nblk, kNB * Cfg::P * a.C, wpart, a.W_bar, st);
+}
+
 // ------------------------------------------------- x_hat / pos_hat pass --
 template <int LIN, int LEDGE, int LOUT, bool HAS_VX>
 struct VVShape {
@@ -490,12 +640,14 @@ void launch_vv_sender_vx(const ConvArgs& a, const VjpWorkspace& wsl, hipStream_t
 #undef FC_VV
 }
 
-// g_hat (when requested), then x_hat / pos_hat (when requested).
+// g_hat, W_hat (W_bar of the arguments), then x_hat / pos_hat, each when
+// requested.
 template <int LIN, int LEDGE, int LOUT>
 void launch_vjp_vjp(const ConvArgs& a, hipStream_t st) {
   if (a.g_hat) launch_vv_recv<LIN, LEDGE, LOUT>(a, st);
+  const VjpWorkspace wsl(a.N, a.E, a.C, nrank(LIN), ConvCfg<LIN, LEDGE, LOUT>::P, true, a.rbar);
+  if (a.W_bar) launch_wgrad_vv<LIN, LEDGE, LOUT>(a, wsl.w_part, st);
   if (!a.x_bar && !a.pos_bar) return;
-  const VjpWorkspace wsl(a.N, a.E, a.C, nrank(LIN), ConvCfg<LIN, LEDGE, LOUT>::P, false, a.rbar);
   if (a.v_x) launch_vv_sender_vx<LIN, LEDGE, LOUT, true>(a, wsl, st);
   else launch_vv_sender_vx<LIN, LEDGE, LOUT, false>(a, wsl, st);
   launch_vjp_combine(a, wsl, nrank(LIN), st);

@@ -151,9 +151,12 @@ fc_status fc_edge_conv_vjp(const fc_conv_desc* d, const fc_graph* g, const float
 
 /* VJP-of-VJP (Eq. C2 with the position derivatives of T_l and R_b): for
  * s = <v_x, x_grad> + <v_pos, pos_grad> (NULL cotangent = zero), writes
- * g_hat = ds/dg_z [N][out_rows][C], x_hat = ds/dx [N][in_rows][C] and
- * pos_hat = ds/dpos [N][3] (each when non-NULL).  radial_w_hat must be NULL
- * in this build (FC_ERR_UNSUPPORTED otherwise). */
+ * g_hat = ds/dg_z [N][out_rows][C], x_hat = ds/dx [N][in_rows][C],
+ * pos_hat = ds/dpos [N][3] and radial_w_hat = ds/dradial_w [8][P][C] (each
+ * when non-NULL; at least one).  The weight cotangent of Eq. C2 is zero.
+ * Needs g_z unless only g_hat is requested, the graph transpose for x_hat
+ * and pos_hat, and a workspace of fc_edge_conv_workspace_bytes(d, 2) bytes
+ * unless only g_hat is requested. */
 fc_status fc_edge_conv_vjp_vjp(const fc_conv_desc* d, const fc_graph* g, const float* pos,
                                const float* shift, const float* x, const float* radial_w,
                                const float* g_z, const float* v_x, const float* v_pos,

@@ -11,10 +11,11 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 
-def oracle_vv(spec, d, v_x, v_pos, edges=None):
+def oracle_vv(spec, d, v_x, v_pos, edges=None, g=None):
+    g = d["g"] if g is None else g
     return conv.edge_conv_vjp_vjp(spec, f64(d["pos"]), d["rowptr"], d["sender"], f64(d["x"]), f64(d["W"]),
-                                  f64(d["g"]), v_x=f64(v_x), v_pos=f64(v_pos), shift=f64(d.get("shift")),
-                                  edges=edges)
+                                  f64(g), v_x=f64(v_x), v_pos=f64(v_pos), shift=f64(d.get("shift")),
+                                  edges=edges, want_W=True)
 
 
 @pytest.mark.parametrize("ranks", [(1, 1, 1), (2, 2, 2), (3, 3, 3), (4, 4, 4), (0, 3, 3), (2, 3, 3)])
@@ -26,12 +27,29 @@ def test_vjp_vjp_small(ranks, with_vx):
     rng = np.random.default_rng(8)
     v_x = inputs.normal(rng, d["x"].shape) if with_vx else None
     gc = GpuConv(ranks, 6.0, d, C)
-    gh, xh, ph = gc.vjp_vjp(v_x=v_x, v_pos=d["v_pos"])
+    gh, xh, ph, Wh = gc.vjp_vjp(v_x=v_x, v_pos=d["v_pos"], want=("g", "x", "pos", "W"))
     torch.cuda.synchronize()
-    go, xo, po, _ = oracle_vv(spec, d, v_x, d["v_pos"])
+    go, xo, po, Wo = oracle_vv(spec, d, v_x, d["v_pos"])
     assert_close("g_hat", gh.cpu().numpy(), go)
     assert_close("x_hat", xh.cpu().numpy(), xo)
     assert_close("pos_hat", ph.cpu().numpy(), po)
+    assert_close("radial_w_hat", Wh.cpu().numpy(), Wo)
+
+
+@pytest.mark.parametrize("ranks", [(2, 2, 2), (4, 4, 4)])
+def test_radial_w_hat_ragged_receivers(ranks):
+    """Receiver counts that leave the last four-receiver block partly empty,
+    degrees above one 32-edge chunk, radial_w_hat requested alone."""
+    spec = conv.ConvSpec(*ranks, 6.0)
+    C = 40
+    d = inputs.edge_conv_inputs(9, 43, 37, 6.0, C, spec.n_in, spec.n_paths, spec.n_out, with_vpos=True)
+    rng = np.random.default_rng(10)
+    v_x = inputs.normal(rng, d["x"].shape)
+    gc = GpuConv(ranks, 6.0, d, C)
+    Wh = gc.vjp_vjp(v_x=v_x, v_pos=d["v_pos"], want=("W",))[3]
+    torch.cuda.synchronize()
+    Wo = oracle_vv(spec, d, v_x, d["v_pos"])[3]
+    assert_close("radial_w_hat", Wh.cpu().numpy(), Wo)
 
 
 @pytest.mark.parametrize("ranks", [(3, 3, 3), (4, 4, 4)])
@@ -41,14 +59,22 @@ def test_vjp_vjp_microbenchmark_sampled(ranks):
     spec = conv.ConvSpec(*ranks, 5.0)
     d = inputs.edge_conv_inputs(2, 1024, 128, 20.0, 128, spec.n_in, spec.n_paths, spec.n_out, with_vpos=True)
     gc = GpuConv(ranks, 5.0, d, 128)
-    gh, xh, ph = gc.vjp_vjp(v_pos=d["v_pos"])
-    torch.cuda.synchronize()
+    gh, xh, ph, _ = gc.vjp_vjp(v_pos=d["v_pos"])
+    # radial_w_hat through a cotangent that vanishes off the sampled
+    # receivers: only their incoming edges contribute
     nodes = np.random.default_rng(5).choice(1024, size=10, replace=False)
+    gm = np.zeros_like(d["g"])
+    gm[nodes] = d["g"][nodes]
+    Wh = gc.vjp_vjp(v_pos=d["v_pos"], want=("W",), g=gm)[3]
+    torch.cuda.synchronize()
     edges = sample_edges(d["rowptr"], d["sender"], nodes)
     go, xo, po, _ = oracle_vv(spec, d, None, d["v_pos"], edges=edges)
+    recv = np.repeat(np.arange(1024), np.diff(d["rowptr"]))
+    Wo = oracle_vv(spec, d, None, d["v_pos"], edges=np.nonzero(np.isin(recv, nodes))[0], g=gm)[3]
     assert_close("g_hat", gh.cpu().numpy()[nodes], go[nodes])
     assert_close("x_hat", xh.cpu().numpy()[nodes], xo[nodes])
     assert_close("pos_hat", ph.cpu().numpy()[nodes], po[nodes])
+    assert_close("radial_w_hat", Wh.cpu().numpy(), Wo)
 
 
 def test_vjp_vjp_periodic_and_subsets():
@@ -59,8 +85,8 @@ def test_vjp_vjp_periodic_and_subsets():
     d["g"] = inputs.normal(rng, (d["pos"].shape[0], spec.n_out, 32))
     vp = inputs.normal(rng, d["pos"].shape)
     gc = GpuConv((0, 3, 3), 5.0, d, 32)
-    go, xo, po, _ = oracle_vv(spec, d, None, vp)
-    for want, ref, idx in ((("g",), go, 0), (("x",), xo, 1), (("pos",), po, 2)):
+    go, xo, po, Wo = oracle_vv(spec, d, None, vp)
+    for want, ref, idx in ((("g",), go, 0), (("x",), xo, 1), (("pos",), po, 2), (("W",), Wo, 3)):
         out = gc.vjp_vjp(v_pos=vp, want=want)
         torch.cuda.synchronize()
         assert_close(want[0], out[idx].cpu().numpy(), ref)

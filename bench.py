@@ -62,7 +62,7 @@ def timed(fn, iters=10, warmup=2):
     return a.elapsed_time(b) / iters
 
 
-def extras(dev, only_ladder=False):
+def extras(dev, only_ladder=False, conv_ranks=(3, 4), only_conv=False):
     """Secondary workloads (reported beside the headline, not part of it)."""
     import torch
 
@@ -71,7 +71,7 @@ def extras(dev, only_ladder=False):
     out = {}
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     # high-rank microbenchmark: fwd, VJP, VJP-of-VJP (position cotangent)
-    for l in (() if only_ladder else (3, 4)):
+    for l in (() if only_ladder else conv_ranks):
         desc = fc.conv_desc(N_NODES, N_NODES * K_NBR, CHANNELS, l, l, l, R_CUT)
         P, n_in, n_out = fc.fc_conv_layout(desc)
         d = inputs.edge_conv_inputs(2, N_NODES, K_NBR, BOX, CHANNELS, n_in, P, n_out, with_vpos=True)
@@ -95,7 +95,7 @@ def extras(dev, only_ladder=False):
         out[f"conv_rank{l}_1024n_128c_128nbr"] = r
         del z, xb, pb, gh, xh, ph, ws, Wb
     # node-local ladder, 4096 nodes, 128 channels, ranks <= 3, order 4, both variants
-    for name, var in (("full", fc.FC_LADDER_FULL), ("path_reduced", fc.FC_LADDER_PATH_REDUCED)):
+    for name, var in (() if only_conv else (("full", fc.FC_LADDER_FULL), ("path_reduced", fc.FC_LADDER_PATH_REDUCED))):
         ld = fc.ladder_desc(4096, CHANNELS, 3, 3, 3, 4, var)
         blocks = fc.ladder_weight_blocks(ld)
         shapes = [((r, c), "normal" if kind == 0 else "one_plus", c) for (_, r, c, kind) in blocks]
@@ -113,6 +113,8 @@ def extras(dev, only_ladder=False):
         r["node_channels_per_s_fwd"] = 4096 * CHANNELS / (r["fwd_ms"] * 1e-3)
         out[f"ladder_{name}_4096n_128c_rank3_order4"] = r
         del saved, z, Ab, Wb, wsf, wsb
+    if only_conv:
+        return out
     out["ladder_full_4096n_128c_rank3_order4"]["mixing_gemm_gflop_fwd"] = ladder_gemm_gflop(4096, CHANNELS, 3, 4)
     lf = out["ladder_full_4096n_128c_rank3_order4"]
     lf["mixing_gemm_tflops_fwd_lower_bound"] = lf["mixing_gemm_gflop_fwd"] / lf["fwd_ms"]
@@ -196,6 +198,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--ladder-only", action="store_true",
                     help="only run the 4096-node ladder workloads (for counter runs) and print their timings")
+    ap.add_argument("--conv-rank", type=int, default=0, metavar="L",
+                    help="only run the 1024-node edge-conv workload at ranks <= L (3 or 4; for counter runs)")
     ap.add_argument("--copy-only", type=int, default=0, metavar="MB",
                     help="only run 5 device-to-device copies of MB megabytes (counter calibration)")
     args = ap.parse_args()
@@ -221,6 +225,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.ladder_only:
         print(json.dumps(extras(dev, only_ladder=True)), flush=True)
+        return
+    if args.conv_rank:
+        print(json.dumps(extras(dev, conv_ranks=(args.conv_rank,), only_conv=True)), flush=True)
         return
     desc = fc.conv_desc(N_NODES, N_NODES * K_NBR, CHANNELS, LMAX, LMAX, LMAX, R_CUT)
     P, n_in, n_out = fc.fc_conv_layout(desc)

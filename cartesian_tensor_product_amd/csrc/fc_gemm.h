@@ -53,6 +53,7 @@ struct GemmGroup {
   int tiles_n[kMaxGemmGroup];
   int kchunk[kMaxGemmGroup];
   int mode[kMaxGemmGroup];   // operand staging modes (filled by gemm_group)
+  int vec_out[kMaxGemmGroup];   // float4 output rows allowed (filled by gemm_group)
   GemmProblem prob[kMaxGemmGroup];
 };
 

@@ -11,9 +11,10 @@
 // lane's sixteen A (or B) values of the tile are contiguous in a k-major
 // LDS row and come in four 128-bit LDS reads.
 //
-// Staging: a K tile is loaded into registers one tile ahead (global loads
-// in flight while the matrix cores work on the previous tile), then written
-// to LDS.  Each operand is staged in one of three ways, chosen per problem
+// Staging: K tiles go through registers into two LDS buffers; a tile is
+// loaded two steps ahead of its use and stored one step ahead, so global
+// loads stay in flight while the matrix cores work on the current tile and
+// one barrier per K tile suffices.  Each operand is staged in one of three ways, chosen per problem
 // on the host from its strides:
 //   kK  k contiguous:    128-bit loads along k, LDS rows [row][BK + 4];
 //   kR  rows contiguous: 128-bit loads along rows, LDS [k][rows + 4];
@@ -31,6 +32,8 @@ constexpr int kMinSplitTiles = 16;   // K tiles per split-K block, at least
 constexpr int KPAD = BK + 4;     // kK / kG row length (floats)
 constexpr int RPAD = BM + 4;     // kR row length (floats)
 constexpr int SMEM = (BM * KPAD > BK * RPAD ? BM * KPAD : BK * RPAD);
+constexpr int TPAD = BN + 4;     // epilogue tile row length (floats)
+static_assert(BM * TPAD <= 4 * SMEM, "the epilogue tile reuses the operand buffers");
 
 enum StageMode { kK = 0, kR = 1, kG = 2 };
 
@@ -155,6 +158,44 @@ __device__ __forceinline__ void fetch(const float* S, int t0, int lane, float* o
   }
 }
 
+// Problem fields pinned in scalar registers: read once from the kernel
+// arguments (the problem index is only known at run time, and reloading the
+// fields inside the K loop would make every step wait on scalar loads).
+__device__ __forceinline__ int sreg(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ uint32_t sreg(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
+__device__ __forceinline__ float sreg(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+__device__ __forceinline__ long long sreg(long long v) {
+  const uint32_t lo = sreg((uint32_t)(unsigned long long)v), hi = sreg((uint32_t)((unsigned long long)v >> 32));
+  return (long long)(((unsigned long long)hi << 32) | lo);
+}
+template <class T>
+__device__ __forceinline__ T* sreg(T* p) {
+  return reinterpret_cast<T*>(sreg((long long)reinterpret_cast<uintptr_t>(p)));
+}
+__device__ __forceinline__ GView pin(const GView& v) {
+  return GView{sreg(v.p), sreg(v.div), sreg(v.s1), sreg(v.s2), sreg(v.kdiv), sreg(v.sk1), sreg(v.sk2),
+               sreg(v.mdiv), sreg(v.mkdiv)};
+}
+__device__ __forceinline__ GOut pin(const GOut& o) {
+  return GOut{sreg(o.p), sreg(o.div), sreg(o.s1), sreg(o.s2), sreg(o.accumulate), sreg(o.mdiv)};
+}
+__device__ __forceinline__ GemmProblem pin(const GemmProblem& q) {
+  GemmProblem r;
+  r.M = sreg(q.M);
+  r.N = sreg(q.N);
+  r.K = sreg(q.K);
+  r.alpha = sreg(q.alpha);
+  r.A = pin(q.A);
+  r.Bt = pin(q.Bt);
+  r.C = pin(q.C);
+  r.C2 = pin(q.C2);
+  r.ksplit = sreg(q.ksplit);
+  r.part = sreg(q.part);
+  return r;
+}
+
 __device__ __forceinline__ void store_out(const GOut& o, int m, int n, float val) {
   if (!o.p) return;
   float* dst = o.p + two_level(m, o.div, o.mdiv, o.s1, o.s2) + n;
@@ -164,7 +205,7 @@ __device__ __forceinline__ void store_out(const GOut& o, int m, int n, float val
 
 template <int MA, int MB>
 __device__ __forceinline__ void gemm_tile(const GemmProblem& P, int m0, int n0, int k_lo, int k_hi, int ks, float* As,
-                                          float* Bs) {
+                                          float* Bs, bool vec_out) {
   const int wv = threadIdx.x / 64, lane = threadIdx.x % 64;
   const int wm = wv % 2, wn = wv / 2;
   Stager<MA> sa;
@@ -179,23 +220,30 @@ __device__ __forceinline__ void gemm_tile(const GemmProblem& P, int m0, int n0, 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // Two LDS buffers: step t computes on buffer t % 2 while the registers
+  // holding tile t + 1 go to the other buffer and tile t + 2 is loaded.  The
+  // single barrier per step orders both the stores (read next step) and the
+  // reads of this step (overwritten by the next step's stores).
   if (k_lo < k_hi) {
     sa.load(P.A, P.M, m0, k_lo, k_hi);
     sb.load(P.Bt, P.N, n0, k_lo, k_hi);
-  }
-  for (int k0 = k_lo; k0 < k_hi; k0 += BK) {
     sa.store(As);
     sb.store(Bs);
-    __syncthreads();
-    if (k0 + BK < k_hi) {
-      sa.load(P.A, P.M, m0, k0 + BK, k_hi);
-      sb.load(P.Bt, P.N, n0, k0 + BK, k_hi);
+    if (k_lo + BK < k_hi) {
+      sa.load(P.A, P.M, m0, k_lo + BK, k_hi);
+      sb.load(P.Bt, P.N, n0, k_lo + BK, k_hi);
     }
+    __syncthreads();
+  }
+  int buf = 0;
+  for (int k0 = k_lo; k0 < k_hi; k0 += BK) {
+    const float* Ac = As + buf * SMEM;
+    const float* Bc = Bs + buf * SMEM;
     float a[2][16], b[2][16];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      fetch<MA>(As, wm * 64 + i * 32, lane, a[i]);
-      fetch<MB>(Bs, wn * 64 + i * 32, lane, b[i]);
+      fetch<MA>(Ac, wm * 64 + i * 32, lane, a[i]);
+      fetch<MB>(Bc, wn * 64 + i * 32, lane, b[i]);
     }
 #pragma unroll
     for (int s = 0; s < 16; ++s)
@@ -203,40 +251,77 @@ __device__ __forceinline__ void gemm_tile(const GemmProblem& P, int m0, int n0, 
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][s], b[j][s], acc[i][j], 0, 0, 0);
-    __syncthreads();
-  }
-
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = n0 + wn * 64 + j * 32 + lane % 32;
-    if (n >= P.N) continue;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * 64 + i * 32 + 8 * (r / 4) + 4 * (lane / 32) + r % 4;
-        if (m >= P.M) continue;
-        if (P.ksplit > 1) {
-          P.part[(size_t)ks * P.M * P.N + (size_t)m * P.N + n] = acc[i][j][r];
-        } else {
-          const float val = P.alpha * acc[i][j][r];
-          store_out(P.C, m, n, val);
-          store_out(P.C2, m, n, val);
-        }
+    if (k0 + BK < k_hi) {
+      sa.store(As + (buf ^ 1) * SMEM);
+      sb.store(Bs + (buf ^ 1) * SMEM);
+      if (k0 + 2 * BK < k_hi) {
+        sa.load(P.A, P.M, m0, k0 + 2 * BK, k_hi);
+        sb.load(P.Bt, P.N, n0, k0 + 2 * BK, k_hi);
       }
     }
+    __syncthreads();
+    buf ^= 1;
+  }
+
+  // Epilogue: the 128 x 128 tile goes through LDS (the operand buffers are
+  // free after the loop's last barrier), then every thread writes rows of
+  // it as float4 (or scalars when the output is not 16-byte aligned or N is
+  // not a multiple of 4): one two-level row offset per row instead of one
+  // per element, and whole 512-byte row segments per wave.
+  float* T = As;   // [BM][TPAD]
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * 64 + i * 32 + 8 * (r / 4) + 4 * (lane / 32) + r % 4;
+        T[row * TPAD + wn * 64 + j * 32 + lane % 32] = acc[i][j][r];
+      }
+  __syncthreads();
+  const int c4 = 4 * (threadIdx.x % 32);
+  const int n = n0 + c4;
+  const bool split = P.ksplit > 1;
+#pragma unroll 1
+  for (int it = 0; it < BM / 8; ++it) {
+    const int row = it * 8 + threadIdx.x / 32;
+    const int m = m0 + row;
+    if (m >= P.M || n >= P.N) continue;
+    floatx4 v = *reinterpret_cast<const floatx4*>(T + row * TPAD + c4);
+    if (split) {
+      float* dst = P.part + (size_t)ks * P.M * P.N + (size_t)m * P.N + n;
+      if (vec_out) *reinterpret_cast<floatx4*>(dst) = v;
+      else
+        for (int e = 0; e < 4 && n + e < P.N; ++e) dst[e] = v[e];
+      continue;
+    }
+    v *= P.alpha;
+    auto put = [&](const GOut& O) {
+      if (!O.p) return;
+      float* dst = O.p + two_level(m, O.div, O.mdiv, O.s1, O.s2) + n;
+      if (vec_out) {
+        floatx4 w = v;
+        if (O.accumulate) w += *reinterpret_cast<const floatx4*>(dst);
+        *reinterpret_cast<floatx4*>(dst) = w;
+      } else {
+        for (int e = 0; e < 4 && n + e < P.N; ++e) dst[e] = O.accumulate ? dst[e] + v[e] : v[e];
+      }
+    };
+    put(P.C);
+    put(P.C2);
   }
 }
 
-__global__ __launch_bounds__(NT) void gemm_kernel(GemmGroup g) {
-  __shared__ __attribute__((aligned(16))) float As[SMEM];
-  __shared__ __attribute__((aligned(16))) float Bs[SMEM];
+__global__ __launch_bounds__(NT, 2) void gemm_kernel(GemmGroup g) {
+  __shared__ __attribute__((aligned(16))) float smem[4 * SMEM];   // A and B, two buffers each
+  float* As = smem;
+  float* Bs = smem + 2 * SMEM;
   int b = blockIdx.x, pi = 0;
   while (pi < g.count - 1 && b >= g.tiles_m[pi] * g.tiles_n[pi] * g.prob[pi].ksplit) {
     b -= g.tiles_m[pi] * g.tiles_n[pi] * g.prob[pi].ksplit;
     ++pi;
   }
-  const GemmProblem& P = g.prob[pi];
+  const GemmProblem P = pin(g.prob[pi]);
   const int tiles = g.tiles_m[pi] * g.tiles_n[pi];
   const int ks = b / tiles;
   b %= tiles;
@@ -244,12 +329,13 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmGroup g) {
   const int m0 = tm * BM, n0 = tn * BN;
   const int k_lo = ks * g.kchunk[pi];
   const int k_hi = min(P.K, k_lo + g.kchunk[pi]);
+  const bool vec_out = g.vec_out[pi] != 0;
   switch (g.mode[pi]) {
-    case kK * 3 + kK: gemm_tile<kK, kK>(P, m0, n0, k_lo, k_hi, ks, As, Bs); break;
-    case kK * 3 + kR: gemm_tile<kK, kR>(P, m0, n0, k_lo, k_hi, ks, As, Bs); break;
-    case kR * 3 + kR: gemm_tile<kR, kR>(P, m0, n0, k_lo, k_hi, ks, As, Bs); break;
-    case kR * 3 + kK: gemm_tile<kR, kK>(P, m0, n0, k_lo, k_hi, ks, As, Bs); break;
-    default: gemm_tile<kG, kG>(P, m0, n0, k_lo, k_hi, ks, As, Bs); break;
+    case kK * 3 + kK: gemm_tile<kK, kK>(P, m0, n0, k_lo, k_hi, ks, As, Bs, vec_out); break;
+    case kK * 3 + kR: gemm_tile<kK, kR>(P, m0, n0, k_lo, k_hi, ks, As, Bs, vec_out); break;
+    case kR * 3 + kR: gemm_tile<kR, kR>(P, m0, n0, k_lo, k_hi, ks, As, Bs, vec_out); break;
+    case kR * 3 + kK: gemm_tile<kR, kK>(P, m0, n0, k_lo, k_hi, ks, As, Bs, vec_out); break;
+    default: gemm_tile<kG, kG>(P, m0, n0, k_lo, k_hi, ks, As, Bs, vec_out); break;
   }
 }
 
@@ -318,6 +404,10 @@ void gemm_group(const GemmGroup& g0, hipStream_t st) {
     P.C2.mdiv = magic(P.C2.div);
     const int ma = stage_mode(P.A, P.M, P.K), mb = stage_mode(P.Bt, P.N, P.K);
     g.mode[i] = (ma == kG || mb == kG) ? kG * 3 + kG : ma * 3 + mb;
+    auto out_vec = [&](const GOut& o) {
+      return !o.p || (aligned16(o.p) && o.s1 % 4 == 0 && (o.div == 1 || o.s2 % 4 == 0));
+    };
+    g.vec_out[i] = P.N % 4 == 0 && (P.ksplit > 1 ? aligned16(P.part) : (out_vec(P.C) && out_vec(P.C2)));
     total += g.tiles_m[i] * g.tiles_n[i] * P.ksplit;
   }
   if (total == 0) return;

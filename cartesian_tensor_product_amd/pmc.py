@@ -6,6 +6,12 @@
     python -m cartesian_tensor_product_amd.pmc stats DIR
         per-kernel durations from a ``--kernel-trace --stats`` run (markdown)
 
+    python -m cartesian_tensor_product_amd.pmc issue DIR [DIR ...]
+        per-kernel instruction mix from runs holding SQ_WAVES, SQ_INSTS_VALU,
+        SQ_INSTS_VALU_FMA_F32, SQ_INSTS_VALU_MUL_F32, SQ_INSTS_LDS,
+        SQ_INSTS_SALU, SQ_INSTS_VMEM_RD, SQ_WAIT_INST_ANY (any subset; the
+        runs are merged by kernel name)
+
     python -m cartesian_tensor_product_amd.pmc traffic --fetch DIR --write DIR \
         --copy-fetch DIR --copy-write DIR --copy-mib 512 --kernel NAME --out FILE
         HBM-side bytes per launch of one kernel: FETCH_SIZE and WRITE_SIZE
@@ -86,6 +92,26 @@ def table(dirs):
     return "\n".join(out)
 
 
+def issue(dirs) -> str:
+    merged: dict = collections.defaultdict(dict)
+    for d in dirs:
+        for k, cs in load(d).items():
+            for c, v in cs.items():
+                merged[k][c] = mean(v)
+    cols = [("SQ_INSTS_VALU", "VALU"), ("SQ_INSTS_VALU_FMA_F32", "FMA_F32"), ("SQ_INSTS_VALU_MUL_F32", "MUL_F32"),
+            ("SQ_INSTS_LDS", "LDS"), ("SQ_INSTS_SALU", "SALU"), ("SQ_INSTS_VMEM_RD", "VMEM_RD"),
+            ("SQ_WAIT_INST_ANY", "WAIT_INST_ANY")]
+    out = ["| kernel | waves | " + " | ".join(f"{n} / wave" for _, n in cols) + " | VALU total |",
+           "|---|---|" + "---|" * (len(cols) + 1)]
+    for k, cs in sorted(merged.items()):
+        w = cs.get("SQ_WAVES")
+        if not w or "SQ_INSTS_VALU" not in cs:
+            continue
+        vals = [f"{cs[c] / w:.0f}" if c in cs else "" for c, _ in cols]
+        out.append(f"| `{k[:80]}` | {w:.0f} | " + " | ".join(vals) + f" | {cs['SQ_INSTS_VALU']:.4g} |")
+    return "\n".join(out)
+
+
 def kernel_name(raw: str) -> str:
     return raw.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
 
@@ -131,6 +157,7 @@ def main(argv=None):
     t = sub.add_parser("table")
     t.add_argument("dirs", nargs="+")
     sub.add_parser("stats").add_argument("dir")
+    sub.add_parser("issue").add_argument("dirs", nargs="+")
     r = sub.add_parser("traffic")
     for k in ("fetch", "write", "copy_fetch", "copy_write"):
         r.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
@@ -145,6 +172,9 @@ def main(argv=None):
         return 0
     if a.cmd == "stats":
         print(stats(a.dir))
+        return 0
+    if a.cmd == "issue":
+        print(issue(a.dirs))
         return 0
     rec = traffic(a)
     with open(a.out, "w") as fh:

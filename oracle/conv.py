@@ -17,6 +17,10 @@ FlashCart paper:
   chain rule through T_l(r_hat) and R_b(r) to the positions (App. C
   "Symbolic derivatives": direction-tensor derivatives).  Gradients are taken
   with respect to the stored independent components (§3).
+* explicit per-edge weights (the pages' own interface of Eq. 1 and Eq. C1):
+  the same forward and VJP with w [E, P, C] given instead of formed from the
+  radial basis; its gradient w_bar [E, P, C] is returned per edge and the
+  position gradient runs through the direction tensors only (w held fixed).
 * VJP-of-VJP: with s = <v_x, x_bar> + <v_pos, pos_bar>, g_hat = ds/dg is the
   directional derivative of the forward along (v_x, v_pos), and
   (x_hat, pos_hat, W_hat) is the directional derivative of the VJP along the
@@ -207,6 +211,71 @@ def edge_conv_vjp(spec: ConvSpec, pos, rowptr, sender, x, W, g, shift=None,
         if want_W:
             W_bar += np.einsum('eb,epk->bpk', R, w_bar)
     return x_bar, pos_bar, W_bar
+
+
+# ----------------------------------------------------------------------------
+# explicit per-edge weights (Eq. 1 and Eq. C1 as the pages state them)
+# ----------------------------------------------------------------------------
+
+def edge_conv_fwd_w(spec: ConvSpec, pos, rowptr, sender, x, w, shift=None,
+                    edges=None, chunk: int = 4096):
+    """Eq. 1 with the per-edge weights given: w [E, P, C] in receiver-sorted
+    edge order; z [N, n_out, C] as in edge_conv_fwd."""
+    N, C = pos.shape[0], x.shape[-1]
+    recv = receivers(rowptr)
+    idx = np.arange(len(sender)) if edges is None else np.asarray(edges)
+    dt = np.result_type(pos.dtype, x.dtype, w.dtype, np.float64)
+    z = np.zeros((N, spec.n_out, C), dtype=dt)
+    for ch in _chunks(idx, chunk):
+        s, u = sender[ch], recv[ch]
+        rv, rn = _geometry(pos, shift, s, u, ch)
+        n = rv / rn[:, None]
+        ys = [T.direction_tensor(l, n) for l in range(spec.l_edge + 1)]
+        for p, (l1, l2, L) in enumerate(spec.paths):
+            K = T.coupling_tensor(l1, l2, L)
+            xs = x[s, spec.in_off[l1]:spec.in_off[l1 + 1], :]
+            f = np.matmul(np.einsum('abc,ec->eab', K, ys[l2]), xs)
+            z[:, spec.rows[p], :] += segment_sum(w[ch, p, None, :] * f, u, N)
+    return z
+
+
+def edge_conv_vjp_w(spec: ConvSpec, pos, rowptr, sender, x, w, g, shift=None,
+                    edges=None, chunk: int = 4096):
+    """Gradients of L = <g, z> for the explicit-weight forward, with w held
+    fixed: x_bar [N, n_in, C], w_bar [E, P, C] (Eq. C1: w_bar = <g, f>), and
+    pos_bar [N, 3] through the direction tensors only."""
+    N, C = pos.shape[0], x.shape[-1]
+    recv = receivers(rowptr)
+    idx = np.arange(len(sender)) if edges is None else np.asarray(edges)
+    dt = np.result_type(pos.dtype, x.dtype, w.dtype, g.dtype, np.float64)
+    x_bar = np.zeros((N, spec.n_in, C), dtype=dt)
+    pos_bar = np.zeros((N, 3), dtype=dt)
+    w_bar = np.zeros(w.shape, dtype=dt)
+    for ch in _chunks(idx, chunk):
+        s, u = sender[ch], recv[ch]
+        Ec = len(ch)
+        rv, rn = _geometry(pos, shift, s, u, ch)
+        n = rv / rn[:, None]
+        ys = [T.direction_tensor(l, n) for l in range(spec.l_edge + 1)]
+        jac = [T.direction_tensor_jac(l, rv) for l in range(spec.l_edge + 1)]
+        y_bar = [np.zeros((Ec, T.n_comp(l)), dtype=dt) for l in range(spec.l_edge + 1)]
+        xb_edge = np.zeros((Ec, spec.n_in, C), dtype=dt)
+        wc = w[ch]
+        for p, (l1, l2, L) in enumerate(spec.paths):
+            K = T.coupling_tensor(l1, l2, L)
+            gp = g[u][:, spec.rows[p], :]
+            xs = x[s, spec.in_off[l1]:spec.in_off[l1 + 1], :]
+            v1 = np.einsum('abc,eak,ec->ebk', K, gp, ys[l2], optimize=True)
+            xb_edge[:, spec.in_off[l1]:spec.in_off[l1 + 1], :] += wc[:, p, None, :] * v1
+            v2 = np.einsum('abc,eak,ebk->eck', K, gp, xs, optimize=True)
+            y_bar[l2] += np.einsum('eck,ek->ec', v2, wc[:, p, :])
+            w_bar[ch, p, :] = np.einsum('eck,ec->ek', v2, ys[l2])
+        x_bar += segment_sum(xb_edge, s, N)
+        r_bar = np.zeros((Ec, 3), dtype=dt)
+        for l in range(spec.l_edge + 1):
+            r_bar = r_bar + np.einsum('ec,ecj->ej', y_bar[l], jac[l])
+        pos_bar += segment_sum(r_bar, s, N) - segment_sum(r_bar, u, N)
+    return x_bar, pos_bar, w_bar
 
 
 # ----------------------------------------------------------------------------

@@ -246,3 +246,43 @@ def test_diamond_neighbour_counts():
     # the shell sum at the 5 A cutoff used by the diamond workload
     rowptr5, _, _ = inputs.periodic_neighbours(pos, box, 5.0)
     assert np.all(np.diff(rowptr5) == 86)
+
+
+# --------------------------------------------------- explicit edge weights --
+
+@pytest.mark.parametrize("l", [1, 2])
+def test_explicit_weights_forward_and_vjp(l):
+    """Eq. 1 / Eq. C1 with w [E, P, C] given: equals the fused forward when
+    w = R W; bilinear identities <g, z> = <w, w_bar> = <x, x_bar>; x_bar,
+    w_bar and the position gradient (w held fixed) against complex steps."""
+    spec, d = tiny(l, channels=3)
+    args = (spec, d["pos"], d["rowptr"], d["sender"])
+    recv = conv.receivers(d["rowptr"])
+    rv = d["pos"][d["sender"]] - d["pos"][recv]
+    R = conv.radial(np.sqrt((rv * rv).sum(1)), spec.n_basis, spec.r_cut)
+    w_fused = np.einsum('eb,bpk->epk', R, d["W"])
+    z_fused = conv.edge_conv_fwd(*args, d["x"], d["W"])
+    assert np.abs(conv.edge_conv_fwd_w(*args, d["x"], w_fused) - z_fused).max() < 1e-12 * np.abs(z_fused).max()
+    rng = np.random.default_rng(12)
+    w = rng.normal(size=(len(d["sender"]), spec.n_paths, 3))
+    g = d["g"]
+    z = conv.edge_conv_fwd_w(*args, d["x"], w)
+    xb, pb, wb = conv.edge_conv_vjp_w(*args, d["x"], w, g)
+    L0 = np.sum(g * z)
+    assert np.sum(w * wb) == pytest.approx(L0, rel=1e-12)
+    assert np.sum(d["x"] * xb) == pytest.approx(L0, rel=1e-12)
+    loss = lambda pos, x, ww: np.sum(g * conv.edge_conv_fwd_w(spec, pos, d["rowptr"], d["sender"], x, ww))
+    for i in range(d["pos"].shape[0]):
+        for j in range(3):
+            pc = d["pos"].astype(complex)
+            pc[i, j] += 1e-20j
+            assert abs(loss(pc, d["x"], w).imag / 1e-20 - pb[i, j]) < 1e-9 * max(1, abs(pb).max())
+    for _ in range(6):
+        idx = tuple(rng.integers(0, s_) for s_ in d["x"].shape)
+        xc = d["x"].astype(complex)
+        xc[idx] += 1e-20j
+        assert loss(d["pos"], xc, w).imag / 1e-20 == pytest.approx(xb[idx], rel=1e-10, abs=1e-12)
+        idw = tuple(rng.integers(0, s_) for s_ in w.shape)
+        wc = w.astype(complex)
+        wc[idw] += 1e-20j
+        assert loss(d["pos"], d["x"], wc).imag / 1e-20 == pytest.approx(wb[idw], rel=1e-10, abs=1e-12)

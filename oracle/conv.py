@@ -220,7 +220,8 @@ def edge_conv_vjp(spec: ConvSpec, pos, rowptr, sender, x, W, g, shift=None,
 def edge_conv_fwd_w(spec: ConvSpec, pos, rowptr, sender, x, w, shift=None,
                     edges=None, chunk: int = 4096):
     """Eq. 1 with the per-edge weights given: w [E, P, C] in receiver-sorted
-    edge order; z [N, n_out, C] as in edge_conv_fwd."""
+    edge order; z [N, n_out, C] as in edge_conv_fwd.  Edges of zero length
+    take no part (their direction is undefined)."""
     N, C = pos.shape[0], x.shape[-1]
     recv = receivers(rowptr)
     idx = np.arange(len(sender)) if edges is None else np.asarray(edges)
@@ -229,13 +230,15 @@ def edge_conv_fwd_w(spec: ConvSpec, pos, rowptr, sender, x, w, shift=None,
     for ch in _chunks(idx, chunk):
         s, u = sender[ch], recv[ch]
         rv, rn = _geometry(pos, shift, s, u, ch)
-        n = rv / rn[:, None]
+        keep = np.real(rn) > 0          # an edge of zero length has no direction
+        n = rv / np.where(keep, rn, 1.0)[:, None]
         ys = [T.direction_tensor(l, n) for l in range(spec.l_edge + 1)]
+        wc = w[ch] * keep[:, None, None]
         for p, (l1, l2, L) in enumerate(spec.paths):
             K = T.coupling_tensor(l1, l2, L)
             xs = x[s, spec.in_off[l1]:spec.in_off[l1 + 1], :]
             f = np.matmul(np.einsum('abc,ec->eab', K, ys[l2]), xs)
-            z[:, spec.rows[p], :] += segment_sum(w[ch, p, None, :] * f, u, N)
+            z[:, spec.rows[p], :] += segment_sum(wc[:, p, None, :] * f, u, N)
     return z
 
 
@@ -243,7 +246,8 @@ def edge_conv_vjp_w(spec: ConvSpec, pos, rowptr, sender, x, w, g, shift=None,
                     edges=None, chunk: int = 4096):
     """Gradients of L = <g, z> for the explicit-weight forward, with w held
     fixed: x_bar [N, n_in, C], w_bar [E, P, C] (Eq. C1: w_bar = <g, f>), and
-    pos_bar [N, 3] through the direction tensors only."""
+    pos_bar [N, 3] through the direction tensors only.  Edges of zero length
+    take no part (their direction is undefined; w_bar is 0 there)."""
     N, C = pos.shape[0], x.shape[-1]
     recv = receivers(rowptr)
     idx = np.arange(len(sender)) if edges is None else np.asarray(edges)
@@ -255,12 +259,14 @@ def edge_conv_vjp_w(spec: ConvSpec, pos, rowptr, sender, x, w, g, shift=None,
         s, u = sender[ch], recv[ch]
         Ec = len(ch)
         rv, rn = _geometry(pos, shift, s, u, ch)
-        n = rv / rn[:, None]
+        keep = np.real(rn) > 0          # an edge of zero length has no direction
+        rv = np.where(keep[:, None], rv, 1.0)
+        n = rv / np.where(keep, rn, np.sqrt(3.0))[:, None]
         ys = [T.direction_tensor(l, n) for l in range(spec.l_edge + 1)]
         jac = [T.direction_tensor_jac(l, rv) for l in range(spec.l_edge + 1)]
         y_bar = [np.zeros((Ec, T.n_comp(l)), dtype=dt) for l in range(spec.l_edge + 1)]
         xb_edge = np.zeros((Ec, spec.n_in, C), dtype=dt)
-        wc = w[ch]
+        wc = w[ch] * keep[:, None, None]
         for p, (l1, l2, L) in enumerate(spec.paths):
             K = T.coupling_tensor(l1, l2, L)
             gp = g[u][:, spec.rows[p], :]
@@ -269,7 +275,7 @@ def edge_conv_vjp_w(spec: ConvSpec, pos, rowptr, sender, x, w, g, shift=None,
             xb_edge[:, spec.in_off[l1]:spec.in_off[l1 + 1], :] += wc[:, p, None, :] * v1
             v2 = np.einsum('abc,eak,ebk->eck', K, gp, xs, optimize=True)
             y_bar[l2] += np.einsum('eck,ek->ec', v2, wc[:, p, :])
-            w_bar[ch, p, :] = np.einsum('eck,ec->ek', v2, ys[l2])
+            w_bar[ch, p, :] = np.einsum('eck,ec->ek', v2, ys[l2]) * keep[:, None]
         x_bar += segment_sum(xb_edge, s, N)
         r_bar = np.zeros((Ec, 3), dtype=dt)
         for l in range(spec.l_edge + 1):

@@ -286,3 +286,23 @@ def test_explicit_weights_forward_and_vjp(l):
         wc = w.astype(complex)
         wc[idw] += 1e-20j
         assert loss(d["pos"], d["x"], wc).imag / 1e-20 == pytest.approx(wb[idw], rel=1e-10, abs=1e-12)
+
+
+def test_explicit_weights_zero_length_edge():
+    """An edge of zero length (coincident atoms) takes no part: removing it
+    from the graph gives the same z, x_bar and pos_bar, and its w_bar is 0."""
+    spec, d = tiny(2, channels=3)
+    pos = d["pos"].copy()
+    recv = conv.receivers(d["rowptr"])
+    e0 = 5
+    pos[d["sender"][e0]] = pos[recv[e0]]          # make edge e0 zero length
+    w = np.random.default_rng(4).normal(size=(len(d["sender"]), spec.n_paths, 3))
+    z = conv.edge_conv_fwd_w(spec, pos, d["rowptr"], d["sender"], d["x"], w)
+    xb, pb, wb = conv.edge_conv_vjp_w(spec, pos, d["rowptr"], d["sender"], d["x"], w, d["g"])
+    keep = np.arange(len(d["sender"])) != e0
+    z2 = conv.edge_conv_fwd_w(spec, pos, d["rowptr"], d["sender"], d["x"], w, edges=np.nonzero(keep)[0])
+    xb2, pb2, _ = conv.edge_conv_vjp_w(spec, pos, d["rowptr"], d["sender"], d["x"], w, d["g"],
+                                       edges=np.nonzero(keep)[0])
+    assert np.all(np.isfinite(z)) and np.all(np.isfinite(pb))
+    assert np.abs(z - z2).max() == 0 and np.abs(xb - xb2).max() == 0 and np.abs(pb - pb2).max() < 1e-14
+    assert np.all(wb[e0] == 0)

@@ -170,6 +170,62 @@ def algorithmic_bytes(N, E, C, n_in, n_out, P):
     return fwd, vjp
 
 
+def explicit_bytes(N, E, C, n_in, n_out, P):
+    """Algorithmic bytes of the explicit-weight calls: the fused traffic plus
+    streaming w [E, P, C] (forward and VJP) and writing w_bar (VJP)."""
+    f, v = algorithmic_bytes(N, E, C, n_in, n_out, P)
+    wb = E * P * C * 4
+    return f + wb - 8 * P * C * 4, v + 2 * wb - 8 * P * C * 4
+
+
+def grid(dev, steps):
+    """The pages' microbenchmark grid (1024 nodes x {64, 128} neighbours x
+    {64, 128, 256} channels x ranks 1-4; rank 5 is not built here): forward,
+    VJP and VJP-of-VJP (position cotangent) with fused Bessel radial weights,
+    and forward + VJP with explicit per-edge weights drawn on the device."""
+    import torch
+
+    from cartesian_tensor_product_amd import flashcart as fc
+    from cartesian_tensor_product_amd import inputs
+    rows = []
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    for k in (64, 128):
+        rng, pos_h, rowptr, sender = inputs.random_cloud(SEED, N_NODES, k, BOX)
+        graph = fc.DeviceGraph(rowptr, sender, N_NODES, device=dev)
+        pos = t(pos_h)
+        E = len(sender)
+        for C in (64, 128, 256):
+            for l in (1, 2, 3, 4):
+                desc = fc.conv_desc(N_NODES, E, C, l, l, l, R_CUT)
+                P, n_in, n_out = fc.fc_conv_layout(desc)
+                gen = torch.Generator(device=dev).manual_seed(1000 * k + 10 * C + l)
+                rn = lambda shape, std=1.0: torch.randn(shape, device=dev, generator=gen) * std
+                x, g = rn((N_NODES, n_in, C)), rn((N_NODES, n_out, C))
+                W, vp = rn((8, P, C), 8 ** -0.5), rn((N_NODES, 3))
+                z, xb, pb = torch.empty_like(g), torch.empty_like(x), torch.empty_like(pos)
+                ws = fc.workspace(max(fc.fc_edge_conv_workspace_bytes(desc, 1),
+                                      fc.fc_edge_conv_workspace_bytes(desc, 2)), dev)
+                r = {"neighbours": k, "channels": C, "l_max": l, "paths": P,
+                     "fwd_ms": timed(lambda: fc.fc_edge_conv_fwd(desc, graph, pos, None, x, W, z), steps),
+                     "vjp_ms": timed(lambda: fc.fc_edge_conv_vjp(desc, graph, pos, None, x, W, g, xb, pb, None, ws),
+                                     steps),
+                     "vjp_vjp_ms": timed(lambda: fc.fc_edge_conv_vjp_vjp(desc, graph, pos, None, x, W, g, None, vp,
+                                                                         z, xb, pb, None, ws), max(2, steps // 4))}
+                w = rn((E, P, C))
+                wb = torch.empty_like(w)
+                r["explicit_fwd_ms"] = timed(lambda: fc.fc_edge_conv_fwd_w(desc, graph, pos, None, x, w, z), steps)
+                r["explicit_vjp_ms"] = timed(
+                    lambda: fc.fc_edge_conv_vjp_w(desc, graph, pos, None, x, w, g, xb, pb, wb, ws), steps)
+                bf, bv = explicit_bytes(N_NODES, E, C, n_in, n_out, P)
+                r["explicit_fwd_plus_vjp_frac_hbm"] = ((bf + bv) / ((r["explicit_fwd_ms"] + r["explicit_vjp_ms"])
+                                                                   * 1e-3) / 1e9 / HBM_PEAK_GBS)
+                r["fwd_plus_vjp_edge_channels_per_s"] = E * C / ((r["fwd_ms"] + r["vjp_ms"]) * 1e-3)
+                rows.append(r)
+                print(json.dumps(r), file=sys.stderr, flush=True)
+                del x, g, W, vp, z, xb, pb, ws, w, wb
+    return rows
+
+
 def cpu_baseline(d, spec, n_recv=768):
     """Oracle (numpy fp64, one thread) on the edges into the first n_recv receivers."""
     from threadpoolctl import threadpool_limits
@@ -200,6 +256,8 @@ def main():
                     help="only run the 4096-node ladder workloads (for counter runs) and print their timings")
     ap.add_argument("--conv-rank", type=int, default=0, metavar="L",
                     help="only run the 1024-node edge-conv workload at ranks <= L (3 or 4; for counter runs)")
+    ap.add_argument("--grid", action="store_true",
+                    help="only run the pages' microbenchmark grid (ranks 1-4) and print it as one JSON line")
     ap.add_argument("--copy-only", type=int, default=0, metavar="MB",
                     help="only run 5 device-to-device copies of MB megabytes (counter calibration)")
     args = ap.parse_args()
@@ -225,6 +283,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.ladder_only:
         print(json.dumps(extras(dev, only_ladder=True)), flush=True)
+        return
+    if args.grid:
+        print(json.dumps({"grid": grid(dev, 10)}), flush=True)
         return
     if args.conv_rank:
         print(json.dumps(extras(dev, conv_ranks=(args.conv_rank,), only_conv=True)), flush=True)
@@ -301,6 +362,20 @@ def main():
                       "wall_s": wall},
     }
     if not args.no_extras:
+        # explicit per-edge weights w [E, P, C] (the pages' own interface),
+        # same workload; w drawn on the device from a seeded generator
+        gen = torch.Generator(device=dev).manual_seed(SEED)
+        w_e = torch.randn((E, P, CHANNELS), device=dev, generator=gen)
+        wb_e = torch.empty_like(w_e)
+        fw = timed(lambda: fc.fc_edge_conv_fwd_w(desc, graph, pos, None, x, w_e, z))
+        vw = timed(lambda: fc.fc_edge_conv_vjp_w(desc, graph, pos, None, x, w_e, g, xb, pb, wb_e, ws))
+        bw_f, bw_v = explicit_bytes(N_NODES, E, CHANNELS, n_in, n_out, P)
+        out["explicit_weights"] = {
+            "fwd_ms": fw, "vjp_ms": vw, "edge_channels_per_s": E * CHANNELS / ((fw + vw) * 1e-3),
+            "fwd_GBs_alg": bw_f / (fw * 1e-3) / 1e9, "vjp_GBs_alg": bw_v / (vw * 1e-3) / 1e9,
+            "fwd_plus_vjp_frac_hbm": (bw_f + bw_v) / ((fw + vw) * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "w_bytes": E * P * CHANNELS * 4}
+        del w_e, wb_e
         # the radial-weight gradient (optional VJP output, a receiver-sorted
         # pass of its own), timed alone and with the rest of the VJP
         Wb = torch.empty_like(W)

@@ -250,6 +250,52 @@ fc_status fc_edge_conv_vjp(const fc_conv_desc* d, const fc_graph* g, const float
   return check_launch("edge conv VJP");
 }
 
+fc_status fc_edge_conv_fwd_w(const fc_conv_desc* d, const fc_graph* g, const float* pos, const float* shift,
+                             const float* x, const float* w, float* z, hipStream_t stream) {
+  if (fc_status s = check_desc(d)) return s;
+  if (!g || !g->rowptr || (d->n_edges > 0 && !g->sender))
+    return fail(FC_ERR_INVALID_ARGUMENT, "explicit-weight forward needs graph rowptr and sender");
+  if (!pos || !x || !z || (d->n_edges > 0 && !w))
+    return fail(FC_ERR_INVALID_ARGUMENT, "explicit-weight forward: NULL pos, x, w or z");
+  if (misaligned(pos, 4) || misaligned(x, 4) || misaligned(w, 4) || misaligned(z, 4) || misaligned(shift, 4))
+    return fail(FC_ERR_INVALID_ARGUMENT, "explicit-weight forward: arrays must be 4-byte aligned");
+  fc::ConvArgs a = make_args(d, g, pos, shift, x, nullptr);
+  a.w_edge = w;
+  a.z = z;
+  if (d->n_edges == 0) {
+    // no edge: z is zero (launch with a dummy weight pointer, nothing reads it)
+    a.w_edge = x;
+  }
+  fc::conv_dispatch(0, d->l_in, d->l_edge, d->l_out, a, stream);
+  return check_launch("explicit-weight edge conv forward");
+}
+
+fc_status fc_edge_conv_vjp_w(const fc_conv_desc* d, const fc_graph* g, const float* pos, const float* shift,
+                             const float* x, const float* w, const float* g_z, float* x_grad, float* pos_grad,
+                             float* w_grad, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (fc_status s = check_desc(d)) return s;
+  if (!g || !g->rowptr || !g->t_rowptr || (d->n_edges > 0 && (!g->sender || !g->receiver || !g->t_edge)))
+    return fail(FC_ERR_INVALID_ARGUMENT, "VJP needs the full graph (run fc_graph_transpose first)");
+  if (!pos || !x || !g_z || (d->n_edges > 0 && !w))
+    return fail(FC_ERR_INVALID_ARGUMENT, "explicit-weight VJP: NULL pos, x, w or g_z");
+  if (!x_grad && !pos_grad && !w_grad) return fail(FC_ERR_INVALID_ARGUMENT, "explicit-weight VJP: no output requested");
+  if (misaligned(pos, 4) || misaligned(x, 4) || misaligned(w, 4) || misaligned(g_z, 4) || misaligned(x_grad, 4) ||
+      misaligned(pos_grad, 4) || misaligned(w_grad, 4) || misaligned(shift, 4))
+    return fail(FC_ERR_INVALID_ARGUMENT, "explicit-weight VJP: arrays must be 4-byte aligned");
+  const size_t need = fc_edge_conv_workspace_bytes(d, 1);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(FC_ERR_WORKSPACE, "explicit-weight VJP needs %zu workspace bytes", need);
+  fc::ConvArgs a = make_args(d, g, pos, shift, x, nullptr);
+  a.w_edge = d->n_edges > 0 ? w : x;   // never read without edges
+  a.w_edge_bar = d->n_edges > 0 ? w_grad : nullptr;
+  a.g = g_z;
+  a.x_bar = x_grad;
+  a.pos_bar = pos_grad;
+  a.rbar = static_cast<float*>(workspace);
+  fc::conv_dispatch(1, d->l_in, d->l_edge, d->l_out, a, stream);
+  return check_launch("explicit-weight edge conv VJP");
+}
+
 fc_status fc_edge_conv_vjp_vjp(const fc_conv_desc* d, const fc_graph* g, const float* pos, const float* shift,
                                const float* x, const float* radial_w, const float* g_z, const float* v_x,
                                const float* v_pos, float* g_hat, float* x_hat, float* pos_hat,

@@ -20,6 +20,10 @@ struct ConvArgs {
   float* g_hat;
   // VJP: gradient of the radial weights W [8][P][C] (nullable)
   float* W_bar;
+  // explicit per-edge weights w [E][P][C] (replacing R W when non-null) and
+  // their gradient (VJP, nullable)
+  const float* w_edge;
+  float* w_edge_bar;
 };
 
 #include "generated/fc_conv_configs.h"

@@ -24,6 +24,8 @@ __host__ __device__ constexpr int fwd_budget(int nin) { return 200 - 2 * nin; }
 __host__ __device__ constexpr int vjp_budget(int nin, int ne) { return 200 - 2 * nin - ne; }
 // Channels of one VJP block: up to 4 waves (C <= 256).
 inline constexpr int kMaxVjpWaves = 4;
+// LDS one workgroup may hold on gfx950.
+inline constexpr size_t kLdsBytes = 160 * 1024;
 // Per-edge products |c| y[g] are broadcast from LDS when a configuration uses
 // at most this many; larger tables multiply inline from y.
 inline constexpr int kCYMax = 48;
@@ -68,7 +70,10 @@ struct EdgeProducts {
 
 // Receiver-sorted edge record: direction-tensor entries (or their coefficient
 // products), the eight radial values and the sender id of edge e into u.
-template <int LIN, int LEDGE, int LOUT>
+// With explicit per-edge weights (XW) the first radial slot holds 1 for an
+// edge of nonzero length and 0 otherwise (such an edge has no direction and
+// takes no part), and the radial basis is not evaluated.
+template <int LIN, int LEDGE, int LOUT, bool XW = false>
 __device__ __forceinline__ void recv_edge_record(int e, const int* __restrict__ sender, const float* __restrict__ pos,
                                                  const float* __restrict__ shift, float pux, float puy, float puz,
                                                  float rc, float* rec) {
@@ -83,17 +88,24 @@ __device__ __forceinline__ void recv_edge_record(int e, const int* __restrict__ 
   }
   const float r = sqrtf(rx * rx + ry * ry + rz * rz);
   const float inv = r > 0.f ? 1.f / r : 0.f;
-  float y[NE], R[kNB];
+  float y[NE];
   direction_tensors<LEDGE>(rx * inv, ry * inv, rz * inv, y);
-  radial<false>(r, rc, R, nullptr);
   EP::fill(y, rec);
-  static_for<kNB>([&](auto b) { rec[EP::NY + b] = R[b]; });
+  if constexpr (XW) {
+    rec[EP::NY] = r > 0.f ? 1.f : 0.f;
+  } else {
+    float R[kNB];
+    radial<false>(r, rc, R, nullptr);
+    static_for<kNB>([&](auto b) { rec[EP::NY + b] = R[b]; });
+  }
   rec[EP::NY + kNB] = __int_as_float(s);
 }
 
 // ============================================================== forward ====
 // One launch per path group G: z rows of G's paths for node u and 64 channels.
-template <int LIN, int LEDGE, int LOUT, int P0, int P1>
+// XW: the weights are given per edge, W = w [E][P][C] (receiver-sorted edge
+// order), instead of being formed from the radial basis and W [8][P][C].
+template <int LIN, int LEDGE, int LOUT, int P0, int P1, bool XW>
 __global__ __launch_bounds__(kWave) void conv_fwd_kernel(
     int N, int C, const int* __restrict__ rowptr, const int* __restrict__ sender,
     const float* __restrict__ pos, const float* __restrict__ shift,
@@ -113,11 +125,13 @@ __global__ __launch_bounds__(kWave) void conv_fwd_kernel(
   const int voff = kk * 4;
   const auto xr = make_rsrc(x, (uint32_t)((size_t)N * NIN * C * 4));
 
-  float Wr[kNB * G::NP];
-  static_for<kNB * G::NP>([&](auto i) {
-    constexpr int b = i / G::NP, p = i % G::NP;
-    Wr[i] = W[(size_t)(b * P + P0 + p) * C + kk];
-  });
+  float Wr[XW ? 1 : kNB * G::NP];
+  if constexpr (!XW) {
+    static_for<kNB * G::NP>([&](auto i) {
+      constexpr int b = i / G::NP, p = i % G::NP;
+      Wr[i] = W[(size_t)(b * P + P0 + p) * C + kk];
+    });
+  }
   float acc[G::NR];
   static_for<G::NR>([&](auto i) { acc[i] = 0.f; });
 
@@ -126,24 +140,45 @@ __global__ __launch_bounds__(kWave) void conv_fwd_kernel(
   for (int base = e0; base < e1; base += kWave) {
     const int cnt = min(kWave, e1 - base);
     if (lane < cnt)
-      recv_edge_record<LIN, LEDGE, LOUT>(base + lane, sender, pos, shift, pux, puy, puz, rc, geo + lane * REC);
+      recv_edge_record<LIN, LEDGE, LOUT, XW>(base + lane, sender, pos, shift, pux, puy, puz, rc, geo + lane * REC);
     __syncthreads();
+    // XW: the weights of edge j + 1 are requested after the gather of edge
+    // j, so that waiting for the gather leaves the prefetch in flight
+    float wn[XW ? G::NP : 1];
+    if constexpr (XW) {
+      if (cnt > 0) {
+        const float* wrow = W + (size_t)base * P * C + kk;
+        static_for<G::NP>([&](auto pi) { wn[pi] = wrow[(size_t)(P0 + pi) * C]; });
+      }
+    }
     for (int j = 0; j < cnt; ++j) {
       const float* rec = geo + j * REC;
       const int s = uniform_int(__float_as_int(rec[EP::NY + kNB]));
       const int sbase = s * NIN * C * 4;
       float xv[NIN];
       static_for<NIN>([&](auto c) { xv[c] = buf_load(xr, voff, sbase + c * C * 4); });
+      float we[XW ? G::NP : 1];
+      if constexpr (XW) {
+        static_for<G::NP>([&](auto pi) { we[pi] = rec[EP::NY] * wn[pi]; });
+        if (j + 1 < cnt) {
+          const float* wrow = W + (size_t)(base + j + 1) * P * C + kk;
+          static_for<G::NP>([&](auto pi) { wn[pi] = wrow[(size_t)(P0 + pi) * C]; });
+        }
+      }
       static_for<G::NP>([&](auto pi) {
         constexpr int p = P0 + pi;
         constexpr PathInfo PI = Cfg::paths[p];
         constexpr int n1 = ncomp(PI.l1), o1 = rank_off(PI.l1), o2 = rank_off(PI.l2);
         constexpr int lo = G::loff(p);
         float w = 0.f;
-        static_for<kNB>([&](auto b) {
-          constexpr int bb = b;
-          w = fmaf(rec[EP::NY + bb], Wr[bb * G::NP + pi], w);
-        });
+        if constexpr (XW) {
+          w = we[pi];
+        } else {
+          static_for<kNB>([&](auto b) {
+            constexpr int bb = b;
+            w = fmaf(rec[EP::NY + bb], Wr[bb * G::NP + pi], w);
+          });
+        }
         float xw[n1];
         static_for<n1>([&](auto c) { xw[c] = w * xv[o1 + c]; });
         constexpr int tb = tab::kTermBegin[PI.type], te = tab::kTermBegin[PI.type + 1];
@@ -175,8 +210,12 @@ void launch_fwd(const ConvArgs& a, hipStream_t st) {
   dim3 grid(a.N, (a.C + kWave - 1) / kWave);
   static_for<GS::n>([&](auto gi) {
     constexpr int p0 = GS::start[gi], p1 = GS::start[gi + 1];
-    hipLaunchKernelGGL((conv_fwd_kernel<LIN, LEDGE, LOUT, p0, p1>), grid, dim3(kWave), 0, st, a.N, a.C, a.rowptr,
-                       a.sender, a.pos, a.shift, a.x, a.W, a.z, a.rc);
+    if (a.w_edge)
+      hipLaunchKernelGGL((conv_fwd_kernel<LIN, LEDGE, LOUT, p0, p1, true>), grid, dim3(kWave), 0, st, a.N, a.C,
+                         a.rowptr, a.sender, a.pos, a.shift, a.x, a.w_edge, a.z, a.rc);
+    else
+      hipLaunchKernelGGL((conv_fwd_kernel<LIN, LEDGE, LOUT, p0, p1, false>), grid, dim3(kWave), 0, st, a.N, a.C,
+                         a.rowptr, a.sender, a.pos, a.shift, a.x, a.W, a.z, a.rc);
   });
 }
 
@@ -327,7 +366,7 @@ struct VjpShape {
   using EP = EdgeProducts<LIN, LEDGE, LOUT>;
   static constexpr int NE = nrank(LEDGE);
   static constexpr int NRED = NE + 1;                      // y_bar components, s
-  static constexpr int REC = EP::NY + 2 * kNB + 1;         // y / products, R, R', receiver
+  static constexpr int REC = EP::NY + 2 * kNB + 2;         // y / products, R, R', receiver, edge id
   static constexpr int budget = vjp_budget(nrank(LIN), NE) - (EP::kCXReg ? EP::CXt::n : 0);
   static constexpr size_t lds_bytes(int nw) {
     return sizeof(float) * ((size_t)kWave * REC + (size_t)nw * kWave * NRED * 4);
@@ -343,13 +382,17 @@ __device__ __forceinline__ float row_sum16(float v) {
   return v;
 }
 
-template <int LIN, int LEDGE, int LOUT, bool NEED_X, bool NEED_POS>
+// XW: explicit per-edge weights, W = w [E][P][C]; the radial term of the
+// position cotangent is absent (w is held fixed), the first radial slot of
+// the edge record flags an edge of nonzero length, and (wb_out non-null)
+// w_bar[e, p, k] = <g_p, f_p(x, y)> is stored per edge.
+template <int LIN, int LEDGE, int LOUT, bool NEED_X, bool NEED_POS, bool XW>
 __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
     int N, int C, const int* __restrict__ t_rowptr, const int* __restrict__ t_edge,
     const int* __restrict__ receiver, const float* __restrict__ pos,
     const float* __restrict__ shift, const float* __restrict__ x,
     const float* __restrict__ W, const float* __restrict__ g, float* __restrict__ x_out,
-    float* __restrict__ p_out, float* __restrict__ rbar, float rc) {
+    float* __restrict__ p_out, float* __restrict__ rbar, float* __restrict__ wb_out, float rc) {
   using Cfg = ConvCfg<LIN, LEDGE, LOUT>;
   using Sh = VjpShape<LIN, LEDGE, LOUT>;
   using EP = typename Sh::EP;
@@ -400,11 +443,13 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
     constexpr bool FIRST = gi == 0;
     // radial weights of this lane's channel for the group's paths (zero for
     // idle lanes, so their contributions to the sums over lanes vanish)
-    float Wr[kNB * G::NP];
-    static_for<kNB * G::NP>([&](auto i) {
-      constexpr int b = i / G::NP, pi = i % G::NP;
-      Wr[i] = act ? W[(size_t)(b * P + G::p0 + pi) * C + kk] : 0.f;
-    });
+    float Wr[XW ? 1 : kNB * G::NP];
+    if constexpr (!XW) {
+      static_for<kNB * G::NP>([&](auto i) {
+        constexpr int b = i / G::NP, pi = i % G::NP;
+        Wr[i] = act ? W[(size_t)(b * P + G::p0 + pi) * C + kk] : 0.f;
+      });
+    }
     for (int base = e0; base < e1; base += kWave) {
       const int cnt = min(kWave, e1 - base);
       if (wv == 0 && lane < cnt) {
@@ -418,18 +463,36 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
         }
         const float r = sqrtf(rx * rx + ry * ry + rz * rz);
         const float inv = r > 0.f ? 1.f / r : 0.f;
-        float y[NE], R[kNB], dR[kNB];
+        float y[NE];
         direction_tensors<LEDGE>(rx * inv, ry * inv, rz * inv, y);
-        radial<true>(r, rc, R, dR);
         float* rec = geo + lane * REC;
         EP::fill(y, rec);
-        static_for<kNB>([&](auto b) {
-          rec[NY + b] = R[b];
-          rec[NY + kNB + b] = dR[b];
-        });
+        if constexpr (XW) {
+          rec[NY] = r > 0.f ? 1.f : 0.f;
+        } else {
+          float R[kNB], dR[kNB];
+          radial<true>(r, rc, R, dR);
+          static_for<kNB>([&](auto b) {
+            rec[NY + b] = R[b];
+            rec[NY + kNB + b] = dR[b];
+          });
+        }
         rec[NY + 2 * kNB] = __int_as_float(u);
+        rec[NY + 2 * kNB + 1] = __int_as_float(e);
       }
       __syncthreads();
+      // XW: the weights of edge j + 1 are requested after the gather of
+      // edge j, so that waiting for the gather leaves the prefetch in flight
+      float wn[XW ? G::NP : 1];
+      auto w_row = [&](int jj) -> size_t {
+        return (size_t)uniform_int(__float_as_int(geo[jj * REC + NY + 2 * kNB + 1])) * P * C + kk;
+      };
+      if constexpr (XW) {
+        if (cnt > 0) {
+          const size_t r0 = w_row(0);
+          static_for<G::NP>([&](auto pi) { wn[pi] = W[r0 + (size_t)(G::p0 + pi) * C]; });
+        }
+      }
       for (int j = 0; j < cnt; ++j) {
         const float* rec = geo + j * REC;
         const int u = uniform_int(__float_as_int(rec[NY + 2 * kNB]));
@@ -442,6 +505,16 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
             gv[li] = buf_load(gr, voff, ubase + row * C * 4);
           });
         });
+        float we[XW ? G::NP : 1];
+        [[maybe_unused]] size_t erow = 0;
+        if constexpr (XW) {
+          erow = w_row(j);
+          static_for<G::NP>([&](auto pi) { we[pi] = act ? rec[NY] * wn[pi] : 0.f; });
+          if (j + 1 < cnt) {
+            const size_t rn = w_row(j + 1);
+            static_for<G::NP>([&](auto pi) { wn[pi] = W[rn + (size_t)(G::p0 + pi) * C]; });
+          }
+        }
         float yb[NE];
         static_for<NE>([&](auto c) { yb[c] = 0.f; });
         float sacc = 0.f;
@@ -453,10 +526,14 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
           constexpr int lo = G::loff(p);
           constexpr int tb = tab::kTermBegin[PI.type], te = tab::kTermBegin[PI.type + 1];
           float w = 0.f;
-          static_for<kNB>([&](auto b) {
-            constexpr int bb = b;
-            w = fmaf(rec[NY + bb], Wr[bb * G::NP + pi], w);
-          });
+          if constexpr (XW) {
+            w = we[pi];
+          } else {
+            static_for<kNB>([&](auto b) {
+              constexpr int bb = b;
+              w = fmaf(rec[NY + bb], Wr[bb * G::NP + pi], w);
+            });
+          }
           if constexpr (NEED_X) {
             // x_bar[b1] += sum_terms c y[b2] (w g[a])
             float gw[na];
@@ -467,7 +544,7 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
               xb[o1 + T.b1] = fmaf(EP::template cy<tt, o2 + T.b2>(rec), gw[T.a], xb[o1 + T.b1]);
             });
           }
-          if constexpr (NEED_POS) {
+          if (NEED_POS || (XW && wb_out)) {
             // v2[b2] = sum_terms c g[a] x[b1]  (VJP_2(g, x), unweighted)
             float v2[n2];
             static_for<te - tb>([&](auto ti) {
@@ -487,12 +564,16 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
               yb[o2 + c] = fmaf(w, v2[c], yb[o2 + c]);
               wbar = fmaf(v2[c], rec[o2 + c], wbar);
             });
-            float dw = 0.f;
-            static_for<kNB>([&](auto b) {
-              constexpr int bb = b;
-              dw = fmaf(rec[NY + kNB + bb], Wr[bb * G::NP + pi], dw);
-            });
-            sacc = fmaf(wbar, dw, sacc);
+            if constexpr (XW) {
+              if (wb_out && act) wb_out[erow + (size_t)p * C] = rec[NY] * wbar;
+            } else {
+              float dw = 0.f;
+              static_for<kNB>([&](auto b) {
+                constexpr int bb = b;
+                dw = fmaf(rec[NY + kNB + bb], Wr[bb * G::NP + pi], dw);
+              });
+              sacc = fmaf(wbar, dw, sacc);
+            }
           }
         });
         if constexpr (NEED_POS) {
@@ -596,21 +677,27 @@ void launch_vjp(const ConvArgs& a, hipStream_t st) {
   const bool nx = a.x_bar != nullptr, np = a.pos_bar != nullptr;
   const int nw = (a.C + kWave - 1) / kWave;
   const VjpWorkspace wsl(a.N, a.E, a.C, nrank(LIN), ConvCfg<LIN, LEDGE, LOUT>::P, true, a.rbar);
-  if (a.W_bar) launch_wgrad<LIN, LEDGE, LOUT>(a, wsl.w_part, st);
-  if (!nx && !np) return;
+  if (a.W_bar && !a.w_edge) launch_wgrad<LIN, LEDGE, LOUT>(a, wsl.w_part, st);
+  if (!nx && !np && !(a.w_edge && a.w_edge_bar)) return;
   float* xo = wsl.S == 1 ? a.x_bar : wsl.x_part;
   float* po = wsl.S == 1 ? a.pos_bar : wsl.p_part;
   dim3 grid(a.N, wsl.S), block(nw * kWave);
   const size_t lds = VjpShape<LIN, LEDGE, LOUT>::lds_bytes(np ? nw : 0);
-  if (nx && np)
-    hipLaunchKernelGGL((conv_vjp_sender_kernel<LIN, LEDGE, LOUT, true, true>), grid, block, lds, st, a.N, a.C,
-                       a.t_rowptr, a.t_edge, a.receiver, a.pos, a.shift, a.x, a.W, a.g, xo, po, wsl.rbar, a.rc);
-  else if (nx)
-    hipLaunchKernelGGL((conv_vjp_sender_kernel<LIN, LEDGE, LOUT, true, false>), grid, block, lds, st, a.N, a.C,
-                       a.t_rowptr, a.t_edge, a.receiver, a.pos, a.shift, a.x, a.W, a.g, xo, po, wsl.rbar, a.rc);
-  else
-    hipLaunchKernelGGL((conv_vjp_sender_kernel<LIN, LEDGE, LOUT, false, true>), grid, block, lds, st, a.N, a.C,
-                       a.t_rowptr, a.t_edge, a.receiver, a.pos, a.shift, a.x, a.W, a.g, xo, po, wsl.rbar, a.rc);
+#define FC_VJP(NX, NP, XW)                                                                                          \
+  hipLaunchKernelGGL((conv_vjp_sender_kernel<LIN, LEDGE, LOUT, NX, NP, XW>), grid, block, lds, st, a.N, a.C,        \
+                     a.t_rowptr, a.t_edge, a.receiver, a.pos, a.shift, a.x, XW ? a.w_edge : a.W, a.g, xo, po,        \
+                     wsl.rbar, a.w_edge_bar, a.rc)
+  if (a.w_edge) {
+    if (nx && np) FC_VJP(true, true, true);
+    else if (nx) FC_VJP(true, false, true);
+    else if (np) FC_VJP(false, true, true);
+    else FC_VJP(false, false, true);
+  } else {
+    if (nx && np) FC_VJP(true, true, false);
+    else if (nx) FC_VJP(true, false, false);
+    else FC_VJP(false, true, false);
+  }
+#undef FC_VJP
   launch_vjp_combine(a, wsl, nrank(LIN), st);
 }
 

@@ -350,12 +350,23 @@ struct VVShape {
   static constexpr int NRED = (HAS_VX ? 3 : 2) * NE + 3;
   static constexpr int REC = 2 * NE + 3 * kNB + 2;   // y, ydot, R, R', R'', nd, receiver
   static constexpr int budget = 200 - (HAS_VX ? 3 : 2) * (NIN + NE);
-  static constexpr size_t lds_bytes(int nw) {
-    return sizeof(float) * ((size_t)kWave * REC + (size_t)nw * kWave * NRED * 4);
+  // edge records of a chunk of ch edges plus the per-wave row sums
+  static constexpr size_t lds_bytes(int nw, int ch) {
+    return sizeof(float) * ((size_t)ch * REC + (size_t)nw * ch * NRED * 4);
   }
+  // edges per chunk: the largest of 64, 32, 16 whose LDS fits the 160 KB a
+  // workgroup may hold with the most channel waves (C = 256) and lets two
+  // blocks of two waves (C = 128) share a CU (LDS otherwise caps occupancy)
+  static constexpr bool fits(int ch) {
+    return lds_bytes(kMaxVjpWaves, ch) <= kLdsBytes && lds_bytes(2, ch) <= kLdsBytes / 2;
+  }
+  static constexpr int CH = fits(64) ? 64 : fits(32) ? 32 : 16;
+  static_assert(lds_bytes(kMaxVjpWaves, CH) <= kLdsBytes, "VJP-of-VJP chunk does not fit in LDS");
 };
 
-template <int LIN, int LEDGE, int LOUT, bool HAS_VX, bool NEED_X, bool NEED_POS>
+// CH: edges per chunk (64, or 32 when the per-wave row sums of 64 edges would
+// not fit in LDS: many channel waves at rank 4).
+template <int LIN, int LEDGE, int LOUT, bool HAS_VX, bool NEED_X, bool NEED_POS, int CH>
 __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vv_sender_kernel(
     int N, int C, const int* __restrict__ t_rowptr, const int* __restrict__ t_edge,
     const int* __restrict__ receiver, const float* __restrict__ pos, const float* __restrict__ shift,
@@ -370,7 +381,7 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vv_sender_kernel(
   constexpr int IYB = 0, IYD = NE, IYA = 2 * NE, IS = (HAS_VX ? 3 : 2) * NE;
   extern __shared__ float lds[];
   float* geo = lds;
-  float* part = lds + kWave * REC;
+  float* part = lds + CH * REC;
   const int NW = blockDim.x / kWave;
 
   const int v = blockIdx.x;
@@ -427,8 +438,8 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vv_sender_kernel(
       constexpr int b = i / G::NP, pi = i % G::NP;
       Wr[i] = act ? W[(size_t)(b * P + G::p0 + pi) * C + kk] : 0.f;
     });
-    for (int base = e0; base < e1; base += kWave) {
-      const int cnt = min(kWave, e1 - base);
+    for (int base = e0; base < e1; base += CH) {
+      const int cnt = min(CH, e1 - base);
       if (wv == 0 && lane < cnt) {
         const int e = t_edge[base + lane];
         const int u = receiver[e];
@@ -523,7 +534,7 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vv_sender_kernel(
           }
         });
         if constexpr (NEED_POS) {
-          float* dst = part + ((size_t)(wv * kWave + j) * NRED) * 4 + (lane >> 4);
+          float* dst = part + ((size_t)(wv * CH + j) * NRED) * 4 + (lane >> 4);
           static_for<NRED>([&](auto i) {
             if constexpr (i >= IS || ((MASK >> (i % NE)) & 1)) {
               const float t = row_sum16(red[i]);
@@ -540,7 +551,7 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vv_sender_kernel(
           float tot[NRED];
           static_for<NRED>([&](auto i) { tot[i] = 0.f; });
           for (int w2 = 0; w2 < NW; ++w2) {
-            const float4* src = reinterpret_cast<const float4*>(part + ((size_t)(w2 * kWave + lane) * NRED) * 4);
+            const float4* src = reinterpret_cast<const float4*>(part + ((size_t)(w2 * CH + lane) * NRED) * 4);
             static_for<NRED>([&](auto i) {
               if constexpr (i >= IS || ((MASK >> (i % NE)) & 1)) {
                 const float4 q = src[i];
@@ -629,9 +640,10 @@ void launch_vv_sender_vx(const ConvArgs& a, const VjpWorkspace& wsl, hipStream_t
   float* xo = wsl.S == 1 ? a.x_bar : wsl.x_part;
   float* po = wsl.S == 1 ? a.pos_bar : wsl.p_part;
   dim3 grid(a.N, wsl.S), block(nw * kWave);
-  const size_t lds = VVShape<LIN, LEDGE, LOUT, HAS_VX>::lds_bytes(np ? nw : 0);
-#define FC_VV(NX, NP)                                                                                         \
-  hipLaunchKernelGGL((conv_vv_sender_kernel<LIN, LEDGE, LOUT, HAS_VX, NX, NP>), grid, block, lds, st, a.N, a.C, \
+  using Sh = VVShape<LIN, LEDGE, LOUT, HAS_VX>;
+  const size_t lds = Sh::lds_bytes(np ? nw : 0, Sh::CH);
+#define FC_VV(NX, NP)                                                                                                 \
+  hipLaunchKernelGGL((conv_vv_sender_kernel<LIN, LEDGE, LOUT, HAS_VX, NX, NP, Sh::CH>), grid, block, lds, st, a.N, a.C, \
                      a.t_rowptr, a.t_edge, a.receiver, a.pos, a.shift, a.x, a.W, a.g, a.v_x, a.v_pos, xo, po,   \
                      wsl.rbar, a.rc)
   if (nx && np) FC_VV(true, true);

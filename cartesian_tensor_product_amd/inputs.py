@@ -61,12 +61,14 @@ def random_cloud(seed: int, n_nodes: int, k: int, box: float):
 
 def edge_conv_inputs(seed: int, n_nodes: int, k: int, box: float, channels: int,
                      n_in_rows: int, n_paths: int, n_out_rows: int,
-                     n_basis: int = 8, with_vpos: bool = False):
+                     n_basis: int = 8, with_vpos: bool = False, with_edge_w: bool = False):
     """Everything one edge-convolution call needs, drawn in the fixed order.
 
     Returns a dict with pos [N,3], rowptr [N+1], sender [E], shift None,
     x [N, n_in_rows, C] ~ N(0,1), W [n_basis, P, C] ~ N(0, 1/n_basis)
-    (variance), g [N, n_out_rows, C] ~ N(0,1) and optionally v_pos [N,3].
+    (variance), g [N, n_out_rows, C] ~ N(0,1), optionally v_pos [N,3] and,
+    last, explicit per-edge weights w [E, P, C] ~ N(0,1) for the interface
+    that takes them given (drawing them does not change the earlier draws).
     """
     rng, pos, rowptr, sender = random_cloud(seed, n_nodes, k, box)
     x = normal(rng, (n_nodes, n_in_rows, channels))
@@ -75,7 +77,20 @@ def edge_conv_inputs(seed: int, n_nodes: int, k: int, box: float, channels: int,
     out = dict(pos=pos, rowptr=rowptr, sender=sender, shift=None, x=x, W=W, g=g)
     if with_vpos:
         out["v_pos"] = normal(rng, (n_nodes, 3))
+    if with_edge_w:
+        out["w"] = edge_weights(rng, len(sender), n_paths, channels)
     return out
+
+
+def edge_weights(rng, n_edges: int, n_paths: int, channels: int) -> np.ndarray:
+    """Per-edge weights w [E, P, C] ~ N(0,1), drawn in edge-row blocks so that
+    large arrays never pass through a float64 copy of their full size."""
+    w = np.empty((n_edges, n_paths, channels), dtype=np.float32)
+    step = max(1, (1 << 22) // max(1, n_paths * channels))
+    for e0 in range(0, n_edges, step):
+        e1 = min(n_edges, e0 + step)
+        w[e0:e1] = rng.standard_normal((e1 - e0, n_paths, channels)).astype(np.float32)
+    return w
 
 
 # ----------------------------------------------------------------------------

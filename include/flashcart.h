@@ -149,6 +149,26 @@ fc_status fc_edge_conv_vjp(const fc_conv_desc* d, const fc_graph* g, const float
                            float* radial_w_grad, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
+/* Forward of Eq. 1 with the per-edge weights given, as the pages state it:
+ * w [E][P][C] in receiver-sorted edge order (w[e, eta, k] weights path eta,
+ * channel k of edge e) replaces the radial basis; r_cut and n_basis of d are
+ * not used.  An edge of zero length has no direction and takes no part.
+ * Other arguments and layouts as fc_edge_conv_fwd. */
+fc_status fc_edge_conv_fwd_w(const fc_conv_desc* d, const fc_graph* g, const float* pos,
+                             const float* shift, const float* x, const float* w, float* z,
+                             hipStream_t stream);
+
+/* VJP of L = <g_z, z> for fc_edge_conv_fwd_w with w held fixed (Eq. C1):
+ * x_grad [N][in_rows][C]; pos_grad [N][3] through the direction tensors
+ * only; w_grad [E][P][C] = <g_z[u_e, eta, k], f_eta(x[v_e, k], T(r_hat_e))>
+ * (0 for an edge of zero length).  Each output is written when non-NULL; at
+ * least one.  Needs the full graph (transpose included) and a workspace of
+ * fc_edge_conv_workspace_bytes(d, 1) bytes. */
+fc_status fc_edge_conv_vjp_w(const fc_conv_desc* d, const fc_graph* g, const float* pos,
+                             const float* shift, const float* x, const float* w,
+                             const float* g_z, float* x_grad, float* pos_grad, float* w_grad,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* VJP-of-VJP (Eq. C2 with the position derivatives of T_l and R_b): for
  * s = <v_x, x_grad> + <v_pos, pos_grad> (NULL cotangent = zero), writes
  * g_hat = ds/dg_z [N][out_rows][C], x_hat = ds/dx [N][in_rows][C],

@@ -36,6 +36,26 @@ def test_vjp_vjp_small(ranks, with_vx):
     assert_close("radial_w_hat", Wh.cpu().numpy(), Wo)
 
 
+@pytest.mark.parametrize("ranks", [(3, 3, 3), (4, 4, 4)])
+@pytest.mark.parametrize("with_vx", [False, True])
+def test_vjp_vjp_256_channels(ranks, with_vx):
+    """Four channel waves per sender block: the VJP-of-VJP then stages fewer
+    edges per chunk (32 or 16 at rank 4) so its row sums fit in LDS; senders
+    of about 40 edges span several chunks."""
+    spec = conv.ConvSpec(*ranks, 6.0)
+    C = 256
+    d = inputs.edge_conv_inputs(13, 60, 40, 5.0, C, spec.n_in, spec.n_paths, spec.n_out, with_vpos=True)
+    rng = np.random.default_rng(14)
+    v_x = inputs.normal(rng, d["x"].shape) if with_vx else None
+    gc = GpuConv(ranks, 6.0, d, C)
+    gh, xh, ph, _ = gc.vjp_vjp(v_x=v_x, v_pos=d["v_pos"])
+    torch.cuda.synchronize()
+    go, xo, po, _ = oracle_vv(spec, d, v_x, d["v_pos"])
+    assert_close("g_hat", gh.cpu().numpy(), go)
+    assert_close("x_hat", xh.cpu().numpy(), xo)
+    assert_close("pos_hat", ph.cpu().numpy(), po)
+
+
 @pytest.mark.parametrize("ranks", [(2, 2, 2), (4, 4, 4)])
 def test_radial_w_hat_ragged_receivers(ranks):
     """Receiver counts that leave the last four-receiver block partly empty,

@@ -180,9 +180,9 @@ def explicit_bytes(N, E, C, n_in, n_out, P):
 
 def grid(dev, steps):
     """The pages' microbenchmark grid (1024 nodes x {64, 128} neighbours x
-    {64, 128, 256} channels x ranks 1-4; rank 5 is not built here): forward,
-    VJP and VJP-of-VJP (position cotangent) with fused Bessel radial weights,
-    and forward + VJP with explicit per-edge weights drawn on the device."""
+    {64, 128, 256} channels x ranks 1-5): forward, VJP and VJP-of-VJP
+    (position cotangent; ranks <= 4) with fused Bessel radial weights, and
+    forward + VJP with explicit per-edge weights drawn on the device."""
     import torch
 
     from cartesian_tensor_product_amd import flashcart as fc
@@ -195,7 +195,7 @@ def grid(dev, steps):
         pos = t(pos_h)
         E = len(sender)
         for C in (64, 128, 256):
-            for l in (1, 2, 3, 4):
+            for l in (1, 2, 3, 4, 5):
                 desc = fc.conv_desc(N_NODES, E, C, l, l, l, R_CUT)
                 P, n_in, n_out = fc.fc_conv_layout(desc)
                 gen = torch.Generator(device=dev).manual_seed(1000 * k + 10 * C + l)
@@ -209,8 +209,9 @@ def grid(dev, steps):
                      "fwd_ms": timed(lambda: fc.fc_edge_conv_fwd(desc, graph, pos, None, x, W, z), steps),
                      "vjp_ms": timed(lambda: fc.fc_edge_conv_vjp(desc, graph, pos, None, x, W, g, xb, pb, None, ws),
                                      steps),
-                     "vjp_vjp_ms": timed(lambda: fc.fc_edge_conv_vjp_vjp(desc, graph, pos, None, x, W, g, None, vp,
-                                                                         z, xb, pb, None, ws), max(2, steps // 4))}
+                     "vjp_vjp_ms": (timed(lambda: fc.fc_edge_conv_vjp_vjp(desc, graph, pos, None, x, W, g, None, vp,
+                                                                          z, xb, pb, None, ws), max(2, steps // 4))
+                                    if l <= 4 else None)}
                 w = rn((E, P, C))
                 wb = torch.empty_like(w)
                 r["explicit_fwd_ms"] = timed(lambda: fc.fc_edge_conv_fwd_w(desc, graph, pos, None, x, w, z), steps)
@@ -257,7 +258,7 @@ def main():
     ap.add_argument("--conv-rank", type=int, default=0, metavar="L",
                     help="only run the 1024-node edge-conv workload at ranks <= L (3 or 4; for counter runs)")
     ap.add_argument("--grid", action="store_true",
-                    help="only run the pages' microbenchmark grid (ranks 1-4) and print it as one JSON line")
+                    help="only run the pages' microbenchmark grid (ranks 1-5) and print it as one JSON line")
     ap.add_argument("--copy-only", type=int, default=0, metavar="MB",
                     help="only run 5 device-to-device copies of MB megabytes (counter calibration)")
     args = ap.parse_args()

@@ -56,8 +56,8 @@ fc_status check_desc(const fc_conv_desc* d) {
   if (d->channels < 1) return fail(FC_ERR_INVALID_ARGUMENT, "channels must be >= 1 (got %d)", d->channels);
   if (d->l_in < 0 || d->l_edge < 0 || d->l_out < 0)
     return fail(FC_ERR_INVALID_ARGUMENT, "ranks must be >= 0");
-  if (d->l_in > 4 || d->l_edge > 4 || d->l_out > 4)
-    return fail(FC_ERR_UNSUPPORTED, "ranks above 4 are not supported (l_in=%d l_edge=%d l_out=%d)", d->l_in,
+  if (d->l_in > 5 || d->l_edge > 5 || d->l_out > 5)
+    return fail(FC_ERR_UNSUPPORTED, "ranks above 5 are not supported (l_in=%d l_edge=%d l_out=%d)", d->l_in,
                 d->l_edge, d->l_out);
   if (!(d->r_cut > 0.f) || !std::isfinite(d->r_cut))
     return fail(FC_ERR_INVALID_ARGUMENT, "r_cut must be positive and finite");
@@ -302,6 +302,9 @@ fc_status fc_edge_conv_vjp_vjp(const fc_conv_desc* d, const fc_graph* g, const f
                                float* radial_w_hat, void* workspace, size_t workspace_bytes,
                                hipStream_t stream) {
   if (fc_status s = check_desc(d)) return s;
+  if (!fc::conv_vv_supported(d->l_in, d->l_edge, d->l_out))
+    return fail(FC_ERR_UNSUPPORTED, "VJP-of-VJP is not instantiated for (l_in, l_edge, l_out) = (%d, %d, %d)",
+                d->l_in, d->l_edge, d->l_out);
   if (!g_hat && !x_hat && !pos_hat && !radial_w_hat)
     return fail(FC_ERR_INVALID_ARGUMENT, "VJP-of-VJP: no output requested");
   if (!g || !g->rowptr || (d->n_edges > 0 && !g->sender))

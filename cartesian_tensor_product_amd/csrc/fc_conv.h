@@ -29,6 +29,8 @@ struct ConvArgs {
 #include "generated/fc_conv_configs.h"
 
 bool conv_supported(int l_in, int l_edge, int l_out);
+// whether the VJP-of-VJP (op 2) is instantiated for these ranks
+bool conv_vv_supported(int l_in, int l_edge, int l_out);
 // op 0: forward (needs rowptr, sender, pos, shift, x, W, z);
 // op 1: VJP (additionally receiver, t_rowptr, t_edge, g, rbar, and x_bar
 //       and/or pos_bar);

@@ -360,7 +360,8 @@ void launch_wgrad(const ConvArgs& a, float* wpart, hipStream_t st) {
 //   r_bar_e = s_e r_hat + (I - r_hat r_hat^T)/r (sum_c y_bar_c grad_n y_c);
 // it is added to the sender and stored per edge for the combine pass.
 // The NE+1 per-edge sums over lanes use DPP row rotations (16 lanes) and the
-// four row totals of every wave are combined from LDS once per 64-edge chunk.
+// four row totals of every wave are combined from LDS once per chunk of
+// edges (64, or 32 where LDS would not hold 64 at rank 5).
 template <int LIN, int LEDGE, int LOUT>
 struct VjpShape {
   using EP = EdgeProducts<LIN, LEDGE, LOUT>;
@@ -368,9 +369,18 @@ struct VjpShape {
   static constexpr int NRED = NE + 1;                      // y_bar components, s
   static constexpr int REC = EP::NY + 2 * kNB + 2;         // y / products, R, R', receiver, edge id
   static constexpr int budget = vjp_budget(nrank(LIN), NE) - (EP::kCXReg ? EP::CXt::n : 0);
-  static constexpr size_t lds_bytes(int nw) {
-    return sizeof(float) * ((size_t)kWave * REC + (size_t)nw * kWave * NRED * 4);
+  // edge records of a chunk of ch edges plus the per-wave row sums
+  static constexpr size_t lds_bytes(int nw, int ch) {
+    return sizeof(float) * ((size_t)ch * REC + (size_t)nw * ch * NRED * 4);
   }
+  // edges per chunk: 64, or 32 where 64 would not fit the 160 KB of a
+  // workgroup at 256 channels or would keep two blocks of two waves (128
+  // channels) from sharing a CU
+  static constexpr bool fits(int ch) {
+    return lds_bytes(kMaxVjpWaves, ch) <= kLdsBytes && lds_bytes(2, ch) <= kLdsBytes / 2;
+  }
+  static constexpr int CH = fits(64) ? 64 : 32;
+  static_assert(lds_bytes(kMaxVjpWaves, CH) <= kLdsBytes, "VJP chunk does not fit in LDS");
 };
 
 __device__ __forceinline__ float row_sum16(float v) {
@@ -401,8 +411,9 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
   constexpr int REC = Sh::REC, NRED = Sh::NRED, NY = EP::NY;
   using GS = PathGroups<Cfg, Sh::budget>;
   extern __shared__ float lds[];
-  float* geo = lds;                      // [64][REC]
-  float* part = lds + kWave * REC;       // [NW][64 edges][NRED][4 rows]
+  float* geo = lds;                      // [CH][REC]
+  constexpr int CH = Sh::CH;
+  float* part = lds + CH * REC;          // [NW][CH edges][NRED][4 rows]
   const int NW = blockDim.x / kWave;
 
   const int v = blockIdx.x;
@@ -450,8 +461,8 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
         Wr[i] = act ? W[(size_t)(b * P + G::p0 + pi) * C + kk] : 0.f;
       });
     }
-    for (int base = e0; base < e1; base += kWave) {
-      const int cnt = min(kWave, e1 - base);
+    for (int base = e0; base < e1; base += CH) {
+      const int cnt = min(CH, e1 - base);
       if (wv == 0 && lane < cnt) {
         const int e = t_edge[base + lane];
         const int u = receiver[e];
@@ -577,7 +588,7 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
           }
         });
         if constexpr (NEED_POS) {
-          float* dst = part + ((size_t)(wv * kWave + j) * NRED) * 4 + (lane >> 4);
+          float* dst = part + ((size_t)(wv * CH + j) * NRED) * 4 + (lane >> 4);
           static_for<NE>([&](auto c) {
             if constexpr (G::uses_comp(c)) {
               const float t = row_sum16(yb[c]);
@@ -596,7 +607,7 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
           float tot[NRED];
           static_for<NRED>([&](auto i) { tot[i] = 0.f; });
           for (int w2 = 0; w2 < NW; ++w2) {
-            const float4* src = reinterpret_cast<const float4*>(part + ((size_t)(w2 * kWave + lane) * NRED) * 4);
+            const float4* src = reinterpret_cast<const float4*>(part + ((size_t)(w2 * CH + lane) * NRED) * 4);
             static_for<NRED>([&](auto i) {
               if constexpr (i == NE || G::uses_comp(i)) {
                 const float4 q = src[i];
@@ -682,7 +693,7 @@ void launch_vjp(const ConvArgs& a, hipStream_t st) {
   float* xo = wsl.S == 1 ? a.x_bar : wsl.x_part;
   float* po = wsl.S == 1 ? a.pos_bar : wsl.p_part;
   dim3 grid(a.N, wsl.S), block(nw * kWave);
-  const size_t lds = VjpShape<LIN, LEDGE, LOUT>::lds_bytes(np ? nw : 0);
+  const size_t lds = VjpShape<LIN, LEDGE, LOUT>::lds_bytes(np ? nw : 0, VjpShape<LIN, LEDGE, LOUT>::CH);
 #define FC_VJP(NX, NP, XW)                                                                                          \
   hipLaunchKernelGGL((conv_vjp_sender_kernel<LIN, LEDGE, LOUT, NX, NP, XW>), grid, block, lds, st, a.N, a.C,        \
                      a.t_rowptr, a.t_edge, a.receiver, a.pos, a.shift, a.x, XW ? a.w_edge : a.W, a.g, xo, po,        \

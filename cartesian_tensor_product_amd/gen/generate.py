@@ -37,7 +37,7 @@ import os
 import sys
 from fractions import Fraction
 
-MAX_RANK = 4
+MAX_RANK = 5
 
 
 # ----------------------------------------------------------------------------
@@ -378,17 +378,26 @@ def emit(path: str, max_rank=MAX_RANK) -> None:
     _write(path, "\n".join(lines) + "\n")
 
 
-# (l_in, l_edge, l_out) instantiated in the library: equal ranks 0..4 (the
+# (l_in, l_edge, l_out) instantiated in the library: equal ranks 0..5 (the
 # microbenchmark grid of the pages) and (l_prop, l_e, l_e) with
-# l_prop <= min(l_e, 3) (model blocks; the first convolution has scalar
-# senders, later ones propagate rank l_prop).
+# l_prop <= min(l_e, 3), l_e <= 4 (model blocks; the first convolution has
+# scalar senders, later ones propagate rank l_prop).  The VJP-of-VJP is
+# instantiated up to rank 4 (at rank 5 its path groups would need about 20
+# sweeps per sender).
+VV_MAX_RANK = 4
+
+
 def conv_configs():
     out = [(L, L, L) for L in range(MAX_RANK + 1)]
-    for le in range(1, MAX_RANK + 1):
+    for le in range(1, 5):
         for lp in range(0, 4):
             if lp <= le and (lp, le, le) not in out:
                 out.append((lp, le, le))
     return out
+
+
+def has_vv(cfg) -> bool:
+    return max(cfg) <= VV_MAX_RANK
 
 
 def emit_instances(gen_dir: str) -> list:
@@ -398,18 +407,21 @@ def emit_instances(gen_dir: str) -> list:
              "// (l_in, l_edge, l_out) instantiated in this build.", "#pragma once", "",
              "#define FC_CONV_CONFIGS(X) \\"]
     lines += [f"  X({a}, {b}, {c}) \\" for a, b, c in cfgs]
+    lines += ["", "", "// ... of which the VJP-of-VJP is instantiated for", "#define FC_CONV_VV_CONFIGS(X) \\"]
+    lines += [f"  X({a}, {b}, {c}) \\" for a, b, c in cfgs if has_vv((a, b, c))]
     lines += ["", ""]
     _write(os.path.join(gen_dir, "fc_conv_configs.h"), "\n".join(lines))
     files = []
     for a, b, c in cfgs:
+        vv = has_vv((a, b, c))
         src = (f"// Generated by cartesian_tensor_product_amd/gen/generate.py -- do not edit.\n"
-               f"#include \"../fc_conv_vv.h\"\n\n"
+               f"#include \"../{'fc_conv_vv.h' if vv else 'fc_conv_kernels.h'}\"\n\n"
                f"namespace fc {{\n\n"
                f"bool conv_run_{a}{b}{c}(int op, const ConvArgs& args, hipStream_t stream) {{\n"
                f"  if (op == 0) launch_fwd<{a}, {b}, {c}>(args, stream);\n"
                f"  else if (op == 1) launch_vjp<{a}, {b}, {c}>(args, stream);\n"
-               f"  else launch_vjp_vjp<{a}, {b}, {c}>(args, stream);\n"
-               f"  return true;\n}}\n\n}}  // namespace fc\n")
+               + (f"  else launch_vjp_vjp<{a}, {b}, {c}>(args, stream);\n" if vv else "  else return false;\n")
+               + f"  return true;\n}}\n\n}}  // namespace fc\n")
         f = os.path.join(gen_dir, f"conv_inst_{a}{b}{c}.hip")
         _write(f, src)
         files.append(f)

@@ -84,7 +84,9 @@ int32_t fc_abi_version(void);
 /* ------------------------------------------------------------------------
  * Edge convolution descriptor.
  * n_nodes >= 1, n_edges >= 0, 1 <= channels <= 256,
- * 0 <= l_in, l_edge, l_out <= 4 with at least one admissible path,
+ * 0 <= l_in, l_edge, l_out <= 5 with at least one admissible path and the
+ * rank set instantiated in the build: equal ranks 0..5, and (l_prop, l_e, l_e)
+ * with l_prop <= min(l_e, 3), l_e <= 4 (FC_ERR_UNSUPPORTED otherwise);
  * n_basis == 8, r_cut > 0, flags == 0 (natural parity, paths separate).
  * ---------------------------------------------------------------------- */
 typedef struct {
@@ -176,7 +178,8 @@ fc_status fc_edge_conv_vjp_w(const fc_conv_desc* d, const fc_graph* g, const flo
  * when non-NULL; at least one).  The weight cotangent of Eq. C2 is zero.
  * Needs g_z unless only g_hat is requested, the graph transpose for x_hat
  * and pos_hat, and a workspace of fc_edge_conv_workspace_bytes(d, 2) bytes
- * unless only g_hat is requested. */
+ * unless only g_hat is requested.  Instantiated for ranks <= 4
+ * (FC_ERR_UNSUPPORTED at rank 5). */
 fc_status fc_edge_conv_vjp_vjp(const fc_conv_desc* d, const fc_graph* g, const float* pos,
                                const float* shift, const float* x, const float* radial_w,
                                const float* g_z, const float* v_x, const float* v_pos,

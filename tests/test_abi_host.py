@@ -55,7 +55,8 @@ def test_layout_and_path_order_match_oracle(ranks):
     (dict(n_edges=-1), fc.FC_ERR_INVALID_ARGUMENT),
     (dict(channels=0), fc.FC_ERR_INVALID_ARGUMENT),
     (dict(channels=300), fc.FC_ERR_UNSUPPORTED),
-    (dict(l_in=5), fc.FC_ERR_UNSUPPORTED),
+    (dict(l_in=6), fc.FC_ERR_UNSUPPORTED),
+    (dict(l_in=5, l_edge=5, l_out=4), fc.FC_ERR_UNSUPPORTED),
     (dict(l_in=-1), fc.FC_ERR_INVALID_ARGUMENT),
     (dict(n_basis=6), fc.FC_ERR_UNSUPPORTED),
     (dict(r_cut=0.0), fc.FC_ERR_INVALID_ARGUMENT),

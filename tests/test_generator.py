@@ -12,12 +12,12 @@ from oracle import tensors as T
 
 @pytest.fixture(scope="module")
 def tables():
-    return G.build_tables(4)
+    return G.build_tables(5)
 
 
 def test_every_path_matches_oracle(tables):
     paths, terms, _ = tables
-    assert paths == [(a, b, c) for a in range(5) for b in range(5) for c in range(5) if T.admissible(a, b, c)]
+    assert paths == [(a, b, c) for a in range(6) for b in range(6) for c in range(6) if T.admissible(a, b, c)]
     for p in paths:
         K = np.zeros((2 * p[2] + 1, 2 * p[0] + 1, 2 * p[1] + 1))
         for a, b1, b2, c in terms[p]:
@@ -31,7 +31,7 @@ def test_direction_polynomials_match_oracle(tables):
     for _ in range(5):
         n = rng.standard_normal(3)
         n /= np.linalg.norm(n)
-        for l in range(5):
+        for l in range(6):
             v = [sum(float(c) * n[0] ** ex * n[1] ** ey * n[2] ** ez for (ex, ey, ez), c in poly.items())
                  for poly in tpoly[l]]
             assert np.allclose(v, T.direction_tensor(l, n), atol=1e-14)

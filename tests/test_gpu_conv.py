@@ -48,9 +48,9 @@ def test_tiny_workload():
     check_full((1, 1, 1), 6.0, d, 8)
 
 
-@pytest.mark.parametrize("ranks", [(0, 0, 0), (1, 1, 1), (2, 2, 2), (3, 3, 3), (4, 4, 4), (0, 1, 1), (0, 2, 2),
-                                   (1, 2, 2), (0, 3, 3), (1, 3, 3), (2, 3, 3), (0, 4, 4), (1, 4, 4), (2, 4, 4),
-                                   (3, 4, 4)])
+@pytest.mark.parametrize("ranks", [(0, 0, 0), (1, 1, 1), (2, 2, 2), (3, 3, 3), (4, 4, 4), (5, 5, 5), (0, 1, 1),
+                                   (0, 2, 2), (1, 2, 2), (0, 3, 3), (1, 3, 3), (2, 3, 3), (0, 4, 4), (1, 4, 4),
+                                   (2, 4, 4), (3, 4, 4)])
 def test_every_instantiated_config(ranks):
     _, d = tiny_inputs(ranks, 24, seed=11, n=40, k=12, box=5.0, rc=6.0)
     check_full(ranks, 6.0, d, 24)
@@ -173,3 +173,34 @@ def test_bitwise_determinism():
     torch.cuda.synchronize()
     for u, v in zip(a, b):
         assert torch.equal(u, v)
+
+
+def test_rank5_256_channels():
+    """Rank 5 with four channel waves per sender block: the VJP stages 32
+    edges per chunk there so its row sums fit in LDS; senders of about 40
+    edges span two chunks."""
+    _, d = tiny_inputs((5, 5, 5), 256, seed=21, n=50, k=40, box=6.0, rc=6.0)
+    check_full((5, 5, 5), 6.0, d, 256)
+
+
+def test_rank5_microbenchmark_sampled_and_no_vjp_vjp():
+    """Rank 5 (69 paths, 457 output rows per channel) at 1024 nodes x 64
+    neighbours x 64 channels, sampled nodes; the VJP-of-VJP is not
+    instantiated at rank 5 and says so."""
+    from cartesian_tensor_product_amd import flashcart as fc
+    ranks = (5, 5, 5)
+    spec = conv.ConvSpec(*ranks, 5.0)
+    d = inputs.edge_conv_inputs(2, 1024, 64, 20.0, 64, spec.n_in, spec.n_paths, spec.n_out)
+    gc = GpuConv(ranks, 5.0, d, 64)
+    z = gc.fwd()
+    xb, pb = gc.vjp()
+    torch.cuda.synchronize()
+    nodes = np.random.default_rng(97).choice(1024, size=6, replace=False)
+    edges = sample_edges(d["rowptr"], d["sender"], nodes)
+    zo, xo, po, _ = oracle_all(spec, d, edges=edges)
+    assert_close("z", z.cpu().numpy()[nodes], zo[nodes])
+    assert_close("x_grad", xb.cpu().numpy()[nodes], xo[nodes])
+    assert_close("pos_grad", pb.cpu().numpy()[nodes], po[nodes])
+    with pytest.raises(fc.FlashCartError) as ei:
+        gc.vjp_vjp(v_pos=np.zeros((1024, 3), np.float32))
+    assert ei.value.status == fc.FC_ERR_UNSUPPORTED

@@ -65,8 +65,8 @@ def small(ranks, C, seed=11, n=40, k=12, box=5.0, rc=6.0):
     return inputs.edge_conv_inputs(seed, n, k, box, C, spec.n_in, spec.n_paths, spec.n_out, with_edge_w=True)
 
 
-@pytest.mark.parametrize("ranks", [(0, 0, 0), (1, 1, 1), (2, 2, 2), (3, 3, 3), (4, 4, 4), (0, 3, 3), (1, 2, 2),
-                                   (2, 4, 4), (3, 4, 4)])
+@pytest.mark.parametrize("ranks", [(0, 0, 0), (1, 1, 1), (2, 2, 2), (3, 3, 3), (4, 4, 4), (5, 5, 5), (0, 3, 3),
+                                   (1, 2, 2), (2, 4, 4), (3, 4, 4)])
 def test_explicit_weights_every_rank_set(ranks):
     check(ranks, small(ranks, 24), 24)
 

@@ -93,10 +93,10 @@ class ConvSpec:
     """Ranks, paths and layouts of one edge-convolution problem."""
 
     def __init__(self, l_in: int, l_edge: int, l_out: int, r_cut: float,
-                 n_basis: int = 8):
+                 n_basis: int = 8, all_parities: bool = False):
         self.l_in, self.l_edge, self.l_out = l_in, l_edge, l_out
         self.r_cut, self.n_basis = r_cut, n_basis
-        self.paths = T.conv_paths(l_in, l_edge, l_out)
+        self.paths = T.conv_paths(l_in, l_edge, l_out, all_parities)
         self.rows, self.n_out = T.out_layout(self.paths, l_out)
         self.in_off = T.rank_offsets(l_in)
         self.n_in = self.in_off[-1]

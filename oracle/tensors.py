@@ -18,6 +18,8 @@ Potentials"):
   braces evaluated as an explicit sum over distinct index placements.
 * ``coupling_full``: (x (x) y)_L = N_path * STF_L(Sym_L(x .n. y)),
   n = (l1+l2-L)/2 contracted pairs (§2, App. B Eq. B1, App. C).
+* ``coupling_odd_full``: odd J = l1+l2+L, the Levi-Civita extension the pages
+  name without defining it (§7 "Limitations"): reading below.
 
 Reading of the pages (path normalisation).  The constant C_{l1 l2 l3} of
 Eq. B1 is defined only by reference to other work and is not printed.  The
@@ -30,6 +32,17 @@ and reproduces the one printed worked example, the (1,1)->2 xx component of
 equivariance, symmetry, tracelessness and exchange symmetry; path counts
 printed in App. C Table C1 and App. E.  Beyond the worked example the
 normalisation is a reading of the pages, not a value they print.
+
+Reading of the pages (odd parity).  The pages restrict the method to natural
+parity and only name Levi-Civita contractions as the way to odd J.  The
+oracle's odd-J coupling takes the plainest construction: contract
+n = (l1+l2-L-1)/2 index pairs between x and y, one more index of each through
+the Levi-Civita symbol (its third index free), symmetrise and remove traces;
+constant 1, so that (1,1)->1 is the cross product x × y.  Pins: the cross
+product; pseudo-tensor equivariance (a reflection flips the sign);
+antisymmetry under exchange of equal-rank operands; tracelessness; and the
+generator's exact-rational construction.  Beyond the cross product the
+normalisation is parity unpinned against the pages.
 """
 
 from __future__ import annotations
@@ -335,6 +348,42 @@ def admissible(l1: int, l2: int, L: int) -> bool:
     return abs(l1 - l2) <= L <= l1 + l2 and (l1 + l2 + L) % 2 == 0
 
 
+def triangle(l1: int, l2: int, L: int) -> bool:
+    """Triangle condition only: every path of either parity (the odd-J ones
+    are the Levi-Civita extension the pages name in §7)."""
+    return abs(l1 - l2) <= L <= l1 + l2
+
+
+def levi_civita() -> np.ndarray:
+    eps = np.zeros((3, 3, 3))
+    eps[0, 1, 2] = eps[1, 2, 0] = eps[2, 0, 1] = 1.0
+    eps[0, 2, 1] = eps[2, 1, 0] = eps[1, 0, 2] = -1.0
+    return eps
+
+
+def coupling_odd_full(l1: int, l2: int, L: int, xf, yf):
+    """Odd-J coupling of full tensors (reading, see the module notes):
+    STF_L(Sym_L(E)), E_{a.., b.., i} = eps_{i k j} x_{a.. c.. k} y_{c.. j b..}
+    with n = (l1+l2-L-1)/2 pairs c contracted between x and y and one more
+    index of each operand contracted through the Levi-Civita symbol, whose
+    third index stays free.  Constant 1: (1,1)->1 is the cross product."""
+    assert triangle(l1, l2, L) and (l1 + l2 + L) % 2 == 1
+    n = (l1 + l2 - L - 1) // 2
+    batch = np.broadcast_shapes(xf.shape[:-1], yf.shape[:-1])
+    xb = np.broadcast_to(xf, batch + (3 ** l1,)).reshape((-1,) + (3,) * l1)
+    yb = np.broadcast_to(yf, batch + (3 ** l2,)).reshape((-1,) + (3,) * l2)
+    letters = 'abcdefghijklmnopqrs'
+    fa = letters[:l1 - n - 1]                   # free indices of x
+    cc = letters[l1 - n - 1:l1 - 1]             # contracted pairs
+    k, j, i = 'x', 'y', 'w'
+    fb = letters[l1 - 1:l1 - 1 + l2 - n - 1]    # free indices of y
+    q = np.einsum(f'Z{fa}{cc}{k},Z{cc}{j}{fb},{i}{k}{j}->Z{fa}{fb}{i}', xb, yb, levi_civita())
+    q = q.reshape(q.shape[0], 3 ** L)
+    q = np.einsum('fg,zg->zf', sym_matrix(L), q)
+    q = stf(L, q)
+    return q.reshape(batch + (3 ** L,))
+
+
 def coupling_unnormalised(l1: int, l2: int, L: int, xf, yf):
     """STF_L(Sym_L(x .n. y)) for full tensors xf (..., 3^l1), yf (..., 3^l2)."""
     assert admissible(l1, l2, L)
@@ -370,7 +419,10 @@ def path_norm(l1: int, l2: int, L: int) -> float:
 
 
 def coupling_full(l1: int, l2: int, L: int, xf, yf):
-    """Normalised Cartesian coupling of full tensors."""
+    """Normalised Cartesian coupling of full tensors (odd J: the Levi-Civita
+    reading of ``coupling_odd_full``)."""
+    if (l1 + l2 + L) % 2 == 1:
+        return coupling_odd_full(l1, l2, L, xf, yf)
     return path_norm(l1, l2, L) * coupling_unnormalised(l1, l2, L, xf, yf)
 
 
@@ -397,17 +449,19 @@ def coupling_tensor(l1: int, l2: int, L: int) -> np.ndarray:
 # path lists and layouts
 # ----------------------------------------------------------------------------
 
-def conv_paths(l_in: int, l_edge: int, l_out: int) -> list:
-    """Admissible (l1, l2, L), l1 <= l_in, l2 <= l_edge, L <= l_out.
+def conv_paths(l_in: int, l_edge: int, l_out: int, all_parities: bool = False) -> list:
+    """Admissible (l1, l2, L), l1 <= l_in, l2 <= l_edge, L <= l_out (with
+    ``all_parities``: every triangle-allowed path, odd J included).
 
     Ordered by L, then (l1, l2) lexicographically (the pages leave the order
     within an output rank open).
     """
+    ok = triangle if all_parities else admissible
     out = []
     for L in range(l_out + 1):
         for l1 in range(l_in + 1):
             for l2 in range(l_edge + 1):
-                if admissible(l1, l2, L):
+                if ok(l1, l2, L):
                     out.append((l1, l2, L))
     return out
 
@@ -444,7 +498,7 @@ def out_layout(paths: list, l_out: int):
     return rows, acc
 
 
-def levi_civita_11_1(x, y):
+def levi_civita_11_1(x, y):  # noqa: D401
     """eps_ijk x_j y_k: the odd-J (1,1)->1 coupling (cross product).
 
     The pages restrict the method to natural-parity (even J) paths and name

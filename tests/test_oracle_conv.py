@@ -306,3 +306,41 @@ def test_explicit_weights_zero_length_edge():
     assert np.all(np.isfinite(z)) and np.all(np.isfinite(pb))
     assert np.abs(z - z2).max() == 0 and np.abs(xb - xb2).max() == 0 and np.abs(pb - pb2).max() < 1e-14
     assert np.all(wb[e0] == 0)
+
+
+# ----------------------------------------------------- odd parity (reading) --
+
+@pytest.mark.parametrize("l", [1, 2])
+def test_all_parity_convolution(l):
+    """Every triangle-allowed path (odd J through the Levi-Civita reading):
+    the probed forward equals the explicit full-tensor one; rotations act on
+    the odd paths' rows as on pseudo-tensors (a reflection flips their sign);
+    the VJP matches complex steps on x and on every position coordinate."""
+    spec = conv.ConvSpec(l, l, l, 6.0, all_parities=True)
+    d = inputs.edge_conv_inputs(0, 32, 8, 6.0, 3, spec.n_in, spec.n_paths, spec.n_out)
+    d = {k: (v.astype(np.float64) if isinstance(v, np.ndarray) and v.dtype == np.float32 else v) for k, v in d.items()}
+    args = (spec, d["pos"], d["rowptr"], d["sender"])
+    z = conv.edge_conv_fwd(*args, d["x"], d["W"])
+    assert np.abs(conv.edge_conv_fwd(*args, d["x"], d["W"], mode="explicit") - z).max() < 1e-12 * np.abs(z).max()
+    rng = np.random.default_rng(5)
+    for reflect in (False, True):
+        R = rand_rotation(rng, reflect)
+        xr = rotate_rows(in_rows(spec), d["x"], R)
+        zr = conv.edge_conv_fwd(spec, d["pos"] @ R.T, d["rowptr"], d["sender"], xr, d["W"])
+        want = rotate_rows(out_rows(spec), z, R)
+        for p, (l1, l2, L) in enumerate(spec.paths):
+            sign = np.linalg.det(R) if (l1 + l2 + L) % 2 else 1.0
+            assert np.abs(zr[:, spec.rows[p]] - sign * want[:, spec.rows[p]]).max() < 1e-10 * np.abs(z).max()
+    g = d["g"]
+    xb, pb, _ = conv.edge_conv_vjp(*args, d["x"], d["W"], g)
+    loss = lambda pos, x: np.sum(g * conv.edge_conv_fwd(spec, pos, d["rowptr"], d["sender"], x, d["W"]))
+    for i in range(d["pos"].shape[0]):
+        for j in range(3):
+            pc = d["pos"].astype(complex)
+            pc[i, j] += 1e-20j
+            assert abs(loss(pc, d["x"]).imag / 1e-20 - pb[i, j]) < 1e-9 * max(1, abs(pb).max())
+    for _ in range(6):
+        idx = tuple(rng.integers(0, s_) for s_ in d["x"].shape)
+        xc = d["x"].astype(complex)
+        xc[idx] += 1e-20j
+        assert loss(d["pos"], xc).imag / 1e-20 == pytest.approx(xb[idx], rel=1e-10, abs=1e-12)

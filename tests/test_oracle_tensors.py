@@ -243,3 +243,67 @@ def test_printed_counts():
     paths = T.conv_paths(lp["l_max"], lp["l_max"], lp["l_max"])
     assert sum(2 * L + 1 for (_, _, L) in paths) == lp["B_components_per_channel"]
     assert sum(2 * l + 1 for l in range(lp["l_max"] + 1)) == lp["mixed_components_per_channel"]
+
+
+# ------------------------------------------------- odd parity (reading) --
+
+ODD_PATHS = [(l1, l2, L) for l1 in range(4) for l2 in range(4) for L in range(4)
+             if T.triangle(l1, l2, L) and (l1 + l2 + L) % 2 == 1]
+
+
+def test_odd_11_1_is_the_cross_product():
+    rng = np.random.default_rng(31)
+    x, y = rng.standard_normal((5, 3)), rng.standard_normal((5, 3))
+    f = T.coupling(1, 1, 1, x, y)
+    # stored rank-1 components are (x, y, z)
+    assert np.allclose(f, np.cross(x, y), atol=1e-13)
+
+
+def test_odd_22_1_is_the_axial_vector_of_the_matrix_product():
+    """(2,2)->1: one pair contracted and one through eps: the axial vector of
+    X Y for symmetric traceless X, Y."""
+    rng = np.random.default_rng(32)
+    x, y = rng.standard_normal(5), rng.standard_normal(5)
+    X, Y = T.recon(2, x).reshape(3, 3), T.recon(2, y).reshape(3, 3)
+    M = X @ Y
+    want = np.array([M[1, 2] - M[2, 1], M[2, 0] - M[0, 2], M[0, 1] - M[1, 0]])
+    assert np.allclose(T.coupling(2, 2, 1, x, y), want, atol=1e-13)
+
+
+def test_odd_12_2_is_the_symmetric_part_of_columnwise_cross_products():
+    """(1,2)->2: E[b, i] = (x cross Y[:, b])_i; the coupling is its symmetric
+    part (already traceless for symmetric Y)."""
+    rng = np.random.default_rng(33)
+    x, y = rng.standard_normal(3), rng.standard_normal(5)
+    Y = T.recon(2, y).reshape(3, 3)
+    E = np.stack([np.cross(x, Y[:, b]) for b in range(3)])
+    want = 0.5 * (E + E.T)
+    assert abs(np.trace(want)) < 1e-13
+    assert np.allclose(T.coupling(1, 2, 2, x, y), T.select(2, want.reshape(9)), atol=1e-13)
+
+
+@pytest.mark.parametrize("path", ODD_PATHS)
+def test_odd_coupling_invariants(path):
+    """Traceless symmetric output; pseudo-tensor equivariance (a reflection
+    flips the sign); antisymmetry under exchange of the operands."""
+    l1, l2, L = path
+    rng = np.random.default_rng(hash(path) % 2 ** 32)
+    x, y = full_of(l1, rng), full_of(l2, rng)
+    f = T.coupling_full(l1, l2, L, x, y)
+    assert np.abs(f).max() > 1e-3
+    assert np.allclose(T.stf(L, f), f, atol=1e-12)
+    for reflect in (False, True):
+        R = rand_rotation(rng, reflect)
+        lhs = T.coupling_full(l1, l2, L, rotate_full(l1, x, R), rotate_full(l2, y, R))
+        assert np.allclose(lhs, np.linalg.det(R) * rotate_full(L, f, R), atol=1e-10)
+    assert np.allclose(T.coupling_full(l2, l1, L, y, x), -f, atol=1e-12)
+
+
+def test_all_parity_path_counts():
+    """With every triangle-allowed path: ranks <= 1 give the dot and cross
+    products of two vectors plus the scalar products (five paths); ranks <= 2
+    add to the 11 natural paths the odd (1,1)->1, (2,2)->1, (1,2)->2, (2,1)->2."""
+    assert T.conv_paths(1, 1, 1, all_parities=True) == [(0, 0, 0), (1, 1, 0), (0, 1, 1), (1, 0, 1), (1, 1, 1)]
+    odd = [p for p in T.conv_paths(2, 2, 2, all_parities=True) if not T.admissible(*p)]
+    assert odd == [(1, 1, 1), (2, 2, 1), (1, 2, 2), (2, 1, 2)]
+    assert len(T.conv_paths(2, 2, 2)) == 11

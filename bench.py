@@ -94,6 +94,30 @@ def extras(dev, only_ladder=False, conv_ranks=(3, 4), only_conv=False):
         r["fwd_plus_vjp_edge_channels_per_s"] = E * CHANNELS / ((r["fwd_ms"] + r["vjp_ms"]) * 1e-3)
         out[f"conv_rank{l}_1024n_128c_128nbr"] = r
         del z, xb, pb, gh, xh, ph, ws, Wb
+    # every triangle-allowed path (odd J through the Levi-Civita reading), the
+    # literal path sets of the microbenchmark configurations: ranks <= 2
+    # (15 paths), <= 3 (34), <= 4 (65; no VJP-of-VJP)
+    for l in (() if only_ladder else ((2, 3, 4) if not only_conv else ())):
+        desc = fc.conv_desc(N_NODES, N_NODES * K_NBR, CHANNELS, l, l, l, R_CUT, flags=fc.FC_CONV_ALL_PARITIES)
+        P, n_in, n_out = fc.fc_conv_layout(desc)
+        d = inputs.edge_conv_inputs(1 if l == 2 else 2, N_NODES, K_NBR, BOX, CHANNELS, n_in, P, n_out,
+                                    with_vpos=True)
+        graph = fc.DeviceGraph(d["rowptr"], d["sender"], N_NODES, device=dev)
+        pos, x, W, g, vp = t(d["pos"]), t(d["x"]), t(d["W"]), t(d["g"]), t(d["v_pos"])
+        z = torch.empty((N_NODES, n_out, CHANNELS), device=dev)
+        xb, pb = torch.empty_like(x), torch.empty((N_NODES, 3), device=dev)
+        ws = fc.workspace(fc.fc_edge_conv_workspace_bytes(desc, 2 if l <= 3 else 1), dev)
+        E = N_NODES * K_NBR
+        r = {"paths": P, "fwd_ms": timed(lambda: fc.fc_edge_conv_fwd(desc, graph, pos, None, x, W, z)),
+             "vjp_ms": timed(lambda: fc.fc_edge_conv_vjp(desc, graph, pos, None, x, W, g, xb, pb, None, ws))}
+        if l <= 3:
+            gh, xh, ph = torch.empty_like(z), torch.empty_like(x), torch.empty_like(pb)
+            r["vjp_vjp_ms"] = timed(lambda: fc.fc_edge_conv_vjp_vjp(desc, graph, pos, None, x, W, g, None, vp, gh, xh,
+                                                                    ph, None, ws), iters=5)
+            del gh, xh, ph
+        r["fwd_plus_vjp_edge_channels_per_s"] = E * CHANNELS / ((r["fwd_ms"] + r["vjp_ms"]) * 1e-3)
+        out[f"conv_all_parities_rank{l}_1024n_128c_128nbr"] = r
+        del z, xb, pb, ws
     # node-local ladder, 4096 nodes, 128 channels, ranks <= 3, order 4, both variants
     for name, var in (() if only_conv else (("full", fc.FC_LADDER_FULL), ("path_reduced", fc.FC_LADDER_PATH_REDUCED))):
         ld = fc.ladder_desc(4096, CHANNELS, 3, 3, 3, 4, var)

@@ -51,9 +51,13 @@ def _compile(src: str) -> str:
 
 
 def _weight(src: str) -> int:
+    """Rough compile cost, so that the largest units start first: the ranks
+    of a convolution unit conv_inst_<l_in><l_edge><l_out key>."""
     name = os.path.basename(src)
     if name.startswith("conv_inst_"):
-        return sum(int(c) for c in name[10:13]) * 10
+        digits = name[len("conv_inst_"):-len(".hip")]
+        a, b, key = int(digits[0]), int(digits[1]), int(digits[2:])
+        return (a + b + key % 8 + (4 if key >= 8 else 0)) * 10
     return 1
 
 

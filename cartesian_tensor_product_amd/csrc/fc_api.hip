@@ -41,11 +41,20 @@ fc_status check_launch(const char* what) {
 
 bool misaligned(const void* p, size_t a) { return p && (reinterpret_cast<uintptr_t>(p) % a) != 0; }
 
+bool all_parities(const fc_conv_desc* d) { return (d->flags & FC_CONV_ALL_PARITIES) != 0; }
+
+bool path_ok(const fc_conv_desc* d, int l1, int l2, int L) {
+  return all_parities(d) ? fc::triangle(l1, l2, L) : fc::admissible(l1, l2, L);
+}
+
+// output-rank key of the configuration (kAllParities set for every path)
+int lout_key(const fc_conv_desc* d) { return d->l_out + (all_parities(d) ? fc::kAllParities : 0); }
+
 int conv_paths_L(const fc_conv_desc* d, int L) {
   int c = 0;
   for (int l1 = 0; l1 <= d->l_in; ++l1)
     for (int l2 = 0; l2 <= d->l_edge; ++l2)
-      if (fc::admissible(l1, l2, L)) ++c;
+      if (path_ok(d, l1, l2, L)) ++c;
   return c;
 }
 
@@ -62,12 +71,13 @@ fc_status check_desc(const fc_conv_desc* d) {
   if (!(d->r_cut > 0.f) || !std::isfinite(d->r_cut))
     return fail(FC_ERR_INVALID_ARGUMENT, "r_cut must be positive and finite");
   if (d->n_basis != fc::kNB) return fail(FC_ERR_UNSUPPORTED, "n_basis must be 8 (got %d)", d->n_basis);
-  if (d->flags != 0) return fail(FC_ERR_UNSUPPORTED, "flags must be 0 (natural parity, paths separate)");
+  if ((d->flags & ~uint32_t(FC_CONV_ALL_PARITIES)) != 0)
+    return fail(FC_ERR_UNSUPPORTED, "flags other than FC_CONV_ALL_PARITIES are not supported (paths separate)");
   int P = 0;
   for (int L = 0; L <= d->l_out; ++L) P += conv_paths_L(d, L);
   if (P == 0) return fail(FC_ERR_INVALID_ARGUMENT, "no admissible path for these ranks");
   if (d->channels > 256) return fail(FC_ERR_UNSUPPORTED, "channels above 256 are not supported");
-  if (!fc::conv_supported(d->l_in, d->l_edge, d->l_out))
+  if (!fc::conv_supported(d->l_in, d->l_edge, lout_key(d)))
     return fail(FC_ERR_UNSUPPORTED, "(l_in, l_edge, l_out) = (%d, %d, %d) is not instantiated in this build",
                 d->l_in, d->l_edge, d->l_out);
   return FC_OK;
@@ -156,7 +166,7 @@ fc_status fc_conv_path(const fc_conv_desc* d, int32_t i, int32_t* l1, int32_t* l
   for (int LL = 0; LL <= d->l_out; ++LL)
     for (int a = 0; a <= d->l_in; ++a)
       for (int b = 0; b <= d->l_edge; ++b)
-        if (fc::admissible(a, b, LL)) {
+        if (path_ok(d, a, b, LL)) {
           if (idx == i) {
             if (l1) *l1 = a;
             if (l2) *l2 = b;
@@ -221,7 +231,7 @@ fc_status fc_edge_conv_fwd(const fc_conv_desc* d, const fc_graph* g, const float
     return fail(FC_ERR_INVALID_ARGUMENT, "forward: arrays must be 4-byte aligned");
   fc::ConvArgs a = make_args(d, g, pos, shift, x, radial_w);
   a.z = z;
-  fc::conv_dispatch(0, d->l_in, d->l_edge, d->l_out, a, stream);
+  fc::conv_dispatch(0, d->l_in, d->l_edge, lout_key(d), a, stream);
   return check_launch("edge conv forward");
 }
 
@@ -246,7 +256,7 @@ fc_status fc_edge_conv_vjp(const fc_conv_desc* d, const fc_graph* g, const float
   a.pos_bar = pos_grad;
   a.W_bar = radial_w_grad;
   a.rbar = static_cast<float*>(workspace);
-  fc::conv_dispatch(1, d->l_in, d->l_edge, d->l_out, a, stream);
+  fc::conv_dispatch(1, d->l_in, d->l_edge, lout_key(d), a, stream);
   return check_launch("edge conv VJP");
 }
 
@@ -266,7 +276,7 @@ fc_status fc_edge_conv_fwd_w(const fc_conv_desc* d, const fc_graph* g, const flo
     // no edge: z is zero (launch with a dummy weight pointer, nothing reads it)
     a.w_edge = x;
   }
-  fc::conv_dispatch(0, d->l_in, d->l_edge, d->l_out, a, stream);
+  fc::conv_dispatch(0, d->l_in, d->l_edge, lout_key(d), a, stream);
   return check_launch("explicit-weight edge conv forward");
 }
 
@@ -292,7 +302,7 @@ fc_status fc_edge_conv_vjp_w(const fc_conv_desc* d, const fc_graph* g, const flo
   a.x_bar = x_grad;
   a.pos_bar = pos_grad;
   a.rbar = static_cast<float*>(workspace);
-  fc::conv_dispatch(1, d->l_in, d->l_edge, d->l_out, a, stream);
+  fc::conv_dispatch(1, d->l_in, d->l_edge, lout_key(d), a, stream);
   return check_launch("explicit-weight edge conv VJP");
 }
 
@@ -302,7 +312,7 @@ fc_status fc_edge_conv_vjp_vjp(const fc_conv_desc* d, const fc_graph* g, const f
                                float* radial_w_hat, void* workspace, size_t workspace_bytes,
                                hipStream_t stream) {
   if (fc_status s = check_desc(d)) return s;
-  if (!fc::conv_vv_supported(d->l_in, d->l_edge, d->l_out))
+  if (!fc::conv_vv_supported(d->l_in, d->l_edge, lout_key(d)))
     return fail(FC_ERR_UNSUPPORTED, "VJP-of-VJP is not instantiated for (l_in, l_edge, l_out) = (%d, %d, %d)",
                 d->l_in, d->l_edge, d->l_out);
   if (!g_hat && !x_hat && !pos_hat && !radial_w_hat)
@@ -329,7 +339,7 @@ fc_status fc_edge_conv_vjp_vjp(const fc_conv_desc* d, const fc_graph* g, const f
   a.pos_bar = pos_hat;
   a.W_bar = radial_w_hat;
   a.rbar = static_cast<float*>(workspace);
-  fc::conv_dispatch(2, d->l_in, d->l_edge, d->l_out, a, stream);
+  fc::conv_dispatch(2, d->l_in, d->l_edge, lout_key(d), a, stream);
   return check_launch("edge conv VJP-of-VJP");
 }
 

@@ -40,6 +40,14 @@ __host__ __device__ constexpr bool admissible(int l1, int l2, int L) {
   int d = l1 > l2 ? l1 - l2 : l2 - l1;
   return d <= L && L <= l1 + l2 && ((l1 + l2 + L) % 2 == 0);
 }
+// every triangle-allowed path, odd J included (the Levi-Civita extension)
+__host__ __device__ constexpr bool triangle(int l1, int l2, int L) {
+  int d = l1 > l2 ? l1 - l2 : l2 - l1;
+  return d <= L && L <= l1 + l2;
+}
+// Key of the output rank of a configuration that keeps every triangle-allowed
+// path: l_out + kAllParities.
+inline constexpr int kAllParities = 8;
 __host__ __device__ constexpr int path_type(int l1, int l2, int L) {
   for (int t = 0; t < tab::kNumPathTypes; ++t)
     if (tab::kPathL1[t] == l1 && tab::kPathL2[t] == l2 && tab::kPathL[t] == L) return t;
@@ -53,17 +61,24 @@ struct PathInfo {
   int off;   // first row of the L block
 };
 
-// Paths (l1 <= LIN, l2 <= LEDGE, L <= LOUT), ordered by L then (l1, l2).
-template <int LIN, int LEDGE, int LOUT>
+// Paths (l1 <= LIN, l2 <= LEDGE, L <= LOUT), ordered by L then (l1, l2);
+// natural parity, or every triangle-allowed path when the output-rank key is
+// LOUT + kAllParities.
+template <int LIN, int LEDGE, int LOUT_KEY>
 struct ConvCfg {
+  static constexpr int LOUT = LOUT_KEY % kAllParities;
+  static constexpr bool ALL_PARITIES = LOUT_KEY >= kAllParities;
   static constexpr int NIN = nrank(LIN);
   static constexpr int NE = nrank(LEDGE);
+  static constexpr bool path_ok(int l1, int l2, int L) {
+    return ALL_PARITIES ? triangle(l1, l2, L) : admissible(l1, l2, L);
+  }
 
   static constexpr int count_L(int L) {
     int c = 0;
     for (int l1 = 0; l1 <= LIN; ++l1)
       for (int l2 = 0; l2 <= LEDGE; ++l2)
-        if (admissible(l1, l2, L)) ++c;
+        if (path_ok(l1, l2, L)) ++c;
     return c;
   }
   static constexpr int count_all() {
@@ -86,7 +101,7 @@ struct ConvCfg {
       int eta = 0;
       for (int l1 = 0; l1 <= LIN; ++l1)
         for (int l2 = 0; l2 <= LEDGE; ++l2)
-          if (admissible(l1, l2, L)) {
+          if (path_ok(l1, l2, L)) {
             a[i] = PathInfo{path_type(l1, l2, L), l1, l2, L, eta, count_L(L), off_L(L)};
             ++eta;
             ++i;

@@ -28,6 +28,8 @@ struct ConvArgs {
 
 #include "generated/fc_conv_configs.h"
 
+// l_out is the output-rank key: l_out + kAllParities keeps every
+// triangle-allowed path
 bool conv_supported(int l_in, int l_edge, int l_out);
 // whether the VJP-of-VJP (op 2) is instantiated for these ranks
 bool conv_vv_supported(int l_in, int l_edge, int l_out);

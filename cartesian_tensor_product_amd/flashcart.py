@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libflashcart.so")
 
 FC_OK, FC_ERR_INVALID_ARGUMENT, FC_ERR_UNSUPPORTED, FC_ERR_WORKSPACE, FC_ERR_HIP = range(5)
 FC_LADDER_FULL, FC_LADDER_PATH_REDUCED = 0, 1
+FC_CONV_ALL_PARITIES = 1   # descriptor flag: every triangle-allowed path (odd J too)
 
 
 class FlashCartError(RuntimeError):

@@ -1,7 +1,8 @@
 """Coupling-table generator for the HIP kernels.
 
 Expands every natural-parity Cartesian coupling path (l1, l2) -> L with
-l1, l2, L <= MAX_RANK into an exact bilinear polynomial over the 2l+1 stored
+l1, l2, L <= MAX_RANK (and every odd-J path up to ODD_MAX_RANK, through the
+Levi-Civita reading below) into an exact bilinear polynomial over the 2l+1 stored
 components of each operand, and every direction tensor T_l(n) into a
 polynomial in (n_x, n_y, n_z), using exact rational arithmetic (stdlib
 ``fractions``).  The result is emitted as constexpr C++ tables in
@@ -25,6 +26,10 @@ Mathematics (FlashCart paper, arXiv 2610.06409):
   x...x entry of T_L(e_x) is T_L : e_x^L = 1, which fixes the constant exactly.
 * direction tensors: App. B, T_l = (2l-1)!!/l! sum_m (-1)^m
   (2l-2m-1)!!/(2l-1)!! {n^(l-2m) (x) I^m}.
+* odd J (the Levi-Civita extension the pages name in §7, a reading): contract
+  (l1+l2-L-1)/2 index pairs and one more index of each operand through the
+  Levi-Civita symbol, symmetrise over the L free slots and remove traces with
+  the closed-form detracer; constant 1, so that (1,1)->1 is x × y.
 
 Run as a script to (re)write the header; ``build()`` in the package does so.
 """
@@ -38,6 +43,7 @@ import sys
 from fractions import Fraction
 
 MAX_RANK = 5
+ODD_MAX_RANK = 4     # odd-J (Levi-Civita) paths are tabulated up to this rank
 
 
 # ----------------------------------------------------------------------------
@@ -119,6 +125,79 @@ def matchings(slots):
 
 def admissible(l1, l2, L):
     return abs(l1 - l2) <= L <= l1 + l2 and (l1 + l2 + L) % 2 == 0
+
+
+def odd_path(l1, l2, L):
+    return abs(l1 - l2) <= L <= l1 + l2 and (l1 + l2 + L) % 2 == 1
+
+
+# ----------------------------------------------------------------------------
+# odd J: the Levi-Civita extension named in the pages' §7 (reading)
+# ----------------------------------------------------------------------------
+
+def levi(i, k, j):
+    return {(0, 1, 2): 1, (1, 2, 0): 1, (2, 0, 1): 1, (0, 2, 1): -1, (2, 1, 0): -1, (1, 0, 2): -1}.get((i, k, j), 0)
+
+
+def stf_entry(L, S, out_idx):
+    """Entry of the trace-free part of the symmetric rank-L tensor S (dict),
+    by the closed-form detracer: sum_m (-1)^m (2L-2m-1)!!/(2L-1)!! over the
+    placements of m Kronecker deltas among the L slots, times the m-fold
+    trace of S on the remaining slots."""
+    total = Fraction(0)
+    for m in range(L // 2 + 1):
+        coef = Fraction((-1) ** m * dfact(2 * L - 2 * m - 1), dfact(2 * L - 1))
+        for chosen in itertools.combinations(range(L), 2 * m):
+            rest = tuple(out_idx[s] for s in range(L) if s not in chosen)
+            for pairs in matchings(chosen):
+                if any(out_idx[a] != out_idx[b] for a, b in pairs):
+                    continue
+                tr = Fraction(0)
+                for c in itertools.product(range(3), repeat=m):
+                    tr += S[rest + tuple(v for cc in c for v in (cc, cc))]
+                total += coef * tr
+    return total
+
+
+def odd_entry(l1, l2, L, X, Y, out_idx):
+    """Entry ``out_idx`` of STF_L(Sym_L(E)) with
+    E_{a.., b.., i} = sum eps_{i k j} X_{a.. c.. k} Y_{c.. j b..},
+    n = (l1+l2-L-1)/2 contracted pairs c (constant 1)."""
+    n = (l1 + l2 - L - 1) // 2
+    fa, fb = l1 - n - 1, l2 - n - 1
+    E = {}
+    for idx in itertools.product(range(3), repeat=L):
+        a, b, i = idx[:fa], idx[fa:fa + fb], idx[L - 1]
+        v = Fraction(0)
+        for c in itertools.product(range(3), repeat=n):
+            for k in range(3):
+                for j in range(3):
+                    e = levi(i, k, j)
+                    if e:
+                        v += e * X[a + c + (k,)] * Y[c + (j,) + b]
+        E[idx] = v
+    perms = list(itertools.permutations(range(L)))
+    S = {}
+    for idx in itertools.product(range(3), repeat=L):
+        S[idx] = sum((E[tuple(idx[p] for p in perm)] for perm in perms), Fraction(0)) / len(perms)
+    return stf_entry(L, S, out_idx)
+
+
+def odd_coupling_terms(l1, l2, L):
+    """[(a, b1, b2, Fraction)] of the odd-J coupling (reading: constant 1)."""
+    n1, n2 = 2 * l1 + 1, 2 * l2 + 1
+    basis = lambda n, i: [Fraction(int(j == i)) for j in range(n)]
+    fullx = [full_tensor(l1, basis(n1, i)) for i in range(n1)]
+    fully = [full_tensor(l2, basis(n2, i)) for i in range(n2)]
+    terms = []
+    for a, p in enumerate(stored(L)):
+        oi = rep_index(p)
+        for b1 in range(n1):
+            for b2 in range(n2):
+                v = odd_entry(l1, l2, L, fullx[b1], fully[b2], oi)
+                if v != 0:
+                    terms.append((a, b1, b2, v))
+    return terms
 
 
 def b1_entry(l1, l2, L, X, Y, out_idx):
@@ -228,17 +307,23 @@ def coupling_terms(l1, l2, L):
     return terms
 
 
-def all_paths(max_rank=MAX_RANK):
-    return [(l1, l2, L) for l1 in range(max_rank + 1) for l2 in range(max_rank + 1)
-            for L in range(max_rank + 1) if admissible(l1, l2, L)]
+def all_paths(max_rank=MAX_RANK, odd_max_rank=ODD_MAX_RANK):
+    """Natural-parity path types (lexicographic), then the odd-J ones."""
+    nat = [(l1, l2, L) for l1 in range(max_rank + 1) for l2 in range(max_rank + 1)
+           for L in range(max_rank + 1) if admissible(l1, l2, L)]
+    odd = [(l1, l2, L) for l1 in range(odd_max_rank + 1) for l2 in range(odd_max_rank + 1)
+           for L in range(odd_max_rank + 1) if odd_path(l1, l2, L)]
+    return nat + odd
 
 
-def build_tables(max_rank=MAX_RANK):
-    paths = all_paths(max_rank)
+def build_tables(max_rank=MAX_RANK, odd_max_rank=ODD_MAX_RANK):
+    paths = all_paths(max_rank, odd_max_rank)
     cache = {}
     tables = {}
     for (l1, l2, L) in paths:
-        if (l2, l1, L) in cache:           # exchange symmetry: swap operands
+        if odd_path(l1, l2, L):
+            tables[(l1, l2, L)] = odd_coupling_terms(l1, l2, L)
+        elif (l2, l1, L) in cache:         # exchange symmetry: swap operands
             tables[(l1, l2, L)] = [(a, b2, b1, c) for (a, b1, b2, c) in cache[(l2, l1, L)]]
         else:
             cache[(l1, l2, L)] = coupling_terms(l1, l2, L)
@@ -279,8 +364,9 @@ def product_table(paths, tables, cfg, operand):
     index in the list (-1 when the path type is not part of the
     configuration, or for operand 1 when |c| = 1).
     """
-    l_in, l_edge, l_out = cfg
-    used = {p for p in paths if p[0] <= l_in and p[1] <= l_edge and p[2] <= l_out}
+    l_in, l_edge, l_out, allp = cfg_ranks(cfg)
+    used = {p for p in paths if p[0] <= l_in and p[1] <= l_edge and p[2] <= l_out
+            and (allp or admissible(*p))}
     keys, index = [], {}
     if operand == 2:
         for g in range((l_edge + 1) ** 2):
@@ -319,7 +405,7 @@ def emit(path: str, max_rank=MAX_RANK) -> None:
     w("struct Term { int a, b1, b2; float c; bool fa, f1, f2; };")
     w("struct Mono { int ex, ey, ez; float c; };")
     w("")
-    w("// coupling path types (l1, l2 -> L), natural parity, lexicographic")
+    w("// coupling path types (l1, l2 -> L): natural parity, lexicographic, then odd J")
     w(f"inline constexpr int kNumPathTypes = {len(paths)};")
     w("inline constexpr int kPathL1[] = {" + ", ".join(str(p[0]) for p in paths) + "};")
     w("inline constexpr int kPathL2[] = {" + ", ".join(str(p[1]) for p in paths) + "};")
@@ -378,13 +464,21 @@ def emit(path: str, max_rank=MAX_RANK) -> None:
     _write(path, "\n".join(lines) + "\n")
 
 
-# (l_in, l_edge, l_out) instantiated in the library: equal ranks 0..5 (the
-# microbenchmark grid of the pages) and (l_prop, l_e, l_e) with
+# (l_in, l_edge, l_out key) instantiated in the library: equal ranks 0..5
+# (the microbenchmark grid of the pages), (l_prop, l_e, l_e) with
 # l_prop <= min(l_e, 3), l_e <= 4 (model blocks; the first convolution has
-# scalar senders, later ones propagate rank l_prop).  The VJP-of-VJP is
-# instantiated up to rank 4 (at rank 5 its path groups would need about 20
-# sweeps per sender).
+# scalar senders, later ones propagate rank l_prop), and equal ranks 1..4 with
+# every triangle-allowed path (odd J included), keyed by l_out + ALL_PARITIES.
+# The VJP-of-VJP is instantiated up to rank 4 (natural parity) and 3 (every
+# path); beyond, its path groups would need about 20 sweeps per sender.
+ALL_PARITIES = 8
 VV_MAX_RANK = 4
+VV_MAX_RANK_ALL = 3
+
+
+def cfg_ranks(cfg):
+    """(l_in, l_edge, l_out, all parities) of a configuration key."""
+    return cfg[0], cfg[1], cfg[2] % ALL_PARITIES, cfg[2] >= ALL_PARITIES
 
 
 def conv_configs():
@@ -393,11 +487,13 @@ def conv_configs():
         for lp in range(0, 4):
             if lp <= le and (lp, le, le) not in out:
                 out.append((lp, le, le))
+    out += [(L, L, L + ALL_PARITIES) for L in range(1, ODD_MAX_RANK + 1)]
     return out
 
 
 def has_vv(cfg) -> bool:
-    return max(cfg) <= VV_MAX_RANK
+    li, le, lo, allp = cfg_ranks(cfg)
+    return max(li, le, lo) <= (VV_MAX_RANK_ALL if allp else VV_MAX_RANK)
 
 
 def emit_instances(gen_dir: str) -> list:

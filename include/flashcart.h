@@ -87,8 +87,15 @@ int32_t fc_abi_version(void);
  * 0 <= l_in, l_edge, l_out <= 5 with at least one admissible path and the
  * rank set instantiated in the build: equal ranks 0..5, and (l_prop, l_e, l_e)
  * with l_prop <= min(l_e, 3), l_e <= 4 (FC_ERR_UNSUPPORTED otherwise);
- * n_basis == 8, r_cut > 0, flags == 0 (natural parity, paths separate).
+ * n_basis == 8, r_cut > 0, flags == 0 (natural parity: even l1+l2+L, the
+ * pages' method) or FC_CONV_ALL_PARITIES (every triangle-allowed path: the
+ * odd-J couplings are STF_L(Sym_L(E)) with one index of each operand
+ * contracted through the Levi-Civita symbol, constant 1, so (1,1)->1 is the
+ * cross product x × y; instantiated for equal ranks 1..4, the VJP-of-VJP
+ * for 1..3).  Paths are kept separate either way.
  * ---------------------------------------------------------------------- */
+#define FC_CONV_ALL_PARITIES 1u
+
 typedef struct {
   int32_t n_nodes, n_edges, channels;
   int32_t l_in, l_edge, l_out;

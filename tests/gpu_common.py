@@ -23,14 +23,14 @@ def assert_close(name, got, want, floor=None):
 class GpuConv:
     """One edge-convolution problem on the GPU (forward + VJP)."""
 
-    def __init__(self, ranks, rc, d, channels, device="cuda"):
+    def __init__(self, ranks, rc, d, channels, device="cuda", flags=0):
         import torch
         from cartesian_tensor_product_amd import flashcart as fc
         self.fc, self.torch = fc, torch
         self.N = d["pos"].shape[0]
         self.E = int(len(d["sender"]))
         self.C = channels
-        self.desc = fc.conv_desc(self.N, self.E, channels, *ranks, rc)
+        self.desc = fc.conv_desc(self.N, self.E, channels, *ranks, rc, flags=flags)
         self.P, self.nin, self.nout = fc.fc_conv_layout(self.desc)
         self.graph = fc.DeviceGraph(d["rowptr"], d["sender"], self.N, device=device)
         t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(device)

@@ -39,10 +39,13 @@ def test_abi_version_and_status_strings():
     assert L.fc_status_string(3) == b"FC_ERR_WORKSPACE"
 
 
-@pytest.mark.parametrize("ranks", [(1, 1, 1), (2, 2, 2), (3, 3, 3), (4, 4, 4), (0, 3, 3), (2, 3, 3)])
-def test_layout_and_path_order_match_oracle(ranks):
-    spec = conv.ConvSpec(*ranks, 5.0)
-    d = fc.conv_desc(10, 20, 16, *ranks, 5.0)
+@pytest.mark.parametrize("ranks,allp", [((1, 1, 1), False), ((2, 2, 2), False), ((3, 3, 3), False),
+                                        ((4, 4, 4), False), ((5, 5, 5), False), ((0, 3, 3), False),
+                                        ((2, 3, 3), False), ((1, 1, 1), True), ((2, 2, 2), True),
+                                        ((3, 3, 3), True), ((4, 4, 4), True)])
+def test_layout_and_path_order_match_oracle(ranks, allp):
+    spec = conv.ConvSpec(*ranks, 5.0, all_parities=allp)
+    d = fc.conv_desc(10, 20, 16, *ranks, 5.0, flags=fc.FC_CONV_ALL_PARITIES if allp else 0)
     P, nin, nout = fc.fc_conv_layout(d)
     assert (P, nin, nout) == (spec.n_paths, spec.n_in, spec.n_out)
     assert [fc.fc_conv_path(d, i) for i in range(P)] == spec.paths
@@ -61,7 +64,8 @@ def test_layout_and_path_order_match_oracle(ranks):
     (dict(n_basis=6), fc.FC_ERR_UNSUPPORTED),
     (dict(r_cut=0.0), fc.FC_ERR_INVALID_ARGUMENT),
     (dict(r_cut=float("inf")), fc.FC_ERR_INVALID_ARGUMENT),
-    (dict(flags=1), fc.FC_ERR_UNSUPPORTED),
+    (dict(flags=2), fc.FC_ERR_UNSUPPORTED),
+    (dict(flags=1, l_in=0, l_edge=2, l_out=2), fc.FC_ERR_UNSUPPORTED),   # not instantiated
 ])
 def test_descriptor_errors(bad, status):
     kw = dict(n_nodes=4, n_edges=8, channels=8, l_in=1, l_edge=1, l_out=1, r_cut=5.0, n_basis=8, flags=0)

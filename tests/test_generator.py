@@ -1,8 +1,9 @@
 """The HIP path's generated coupling tables against the oracle.
 
-The generator evaluates Eq. B1 with exact rationals on stored components; the
-oracle builds full tensors, symmetrises by permutation averaging and projects
-out traces numerically.  The two constructions must agree."""
+The generator evaluates Eq. B1 (and, for odd J, the Levi-Civita reading) with
+exact rationals on stored components; the oracle builds full tensors,
+symmetrises by permutation averaging and projects out traces numerically.
+The two constructions must agree, natural and odd paths alike."""
 import numpy as np
 import pytest
 
@@ -17,7 +18,10 @@ def tables():
 
 def test_every_path_matches_oracle(tables):
     paths, terms, _ = tables
-    assert paths == [(a, b, c) for a in range(6) for b in range(6) for c in range(6) if T.admissible(a, b, c)]
+    nat = [(a, b, c) for a in range(6) for b in range(6) for c in range(6) if T.admissible(a, b, c)]
+    odd = [(a, b, c) for a in range(5) for b in range(5) for c in range(5)
+           if T.triangle(a, b, c) and not T.admissible(a, b, c)]
+    assert paths == nat + odd
     for p in paths:
         K = np.zeros((2 * p[2] + 1, 2 * p[0] + 1, 2 * p[1] + 1))
         for a, b1, b2, c in terms[p]:
@@ -39,7 +43,7 @@ def test_direction_polynomials_match_oracle(tables):
 
 def test_term_counts(tables):
     paths, terms, _ = tables
-    counts = {lm: sum(len(terms[p]) for p in paths if max(p) <= lm) for lm in range(1, 5)}
+    counts = {lm: sum(len(terms[p]) for p in paths if max(p) <= lm and T.admissible(*p)) for lm in range(1, 5)}
     assert counts == {1: 10, 2: 87, 3: 396, 4: 1500}
 
 

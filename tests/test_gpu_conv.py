@@ -24,9 +24,10 @@ def oracle_all(spec, d, edges=None, g=None):
     return z, xb, pb, Wb
 
 
-def check_full(ranks, rc, d, C):
-    spec = conv.ConvSpec(*ranks, rc)
-    gc = GpuConv(ranks, rc, d, C)
+def check_full(ranks, rc, d, C, allp=False):
+    from cartesian_tensor_product_amd import flashcart as fc
+    spec = conv.ConvSpec(*ranks, rc, all_parities=allp)
+    gc = GpuConv(ranks, rc, d, C, flags=fc.FC_CONV_ALL_PARITIES if allp else 0)
     z = gc.fwd()
     xb, pb, Wb = gc.vjp(want_W=True)
     torch.cuda.synchronize()
@@ -37,8 +38,8 @@ def check_full(ranks, rc, d, C):
     assert_close("radial_w_grad", Wb.cpu().numpy(), Wo)
 
 
-def tiny_inputs(ranks, C, seed=0, n=32, k=8, box=6.0, rc=6.0):
-    spec = conv.ConvSpec(*ranks, rc)
+def tiny_inputs(ranks, C, seed=0, n=32, k=8, box=6.0, rc=6.0, allp=False):
+    spec = conv.ConvSpec(*ranks, rc, all_parities=allp)
     return spec, inputs.edge_conv_inputs(seed, n, k, box, C, spec.n_in, spec.n_paths, spec.n_out)
 
 
@@ -54,6 +55,20 @@ def test_tiny_workload():
 def test_every_instantiated_config(ranks):
     _, d = tiny_inputs(ranks, 24, seed=11, n=40, k=12, box=5.0, rc=6.0)
     check_full(ranks, 6.0, d, 24)
+
+
+def test_tiny_workload_all_triangle_allowed_paths():
+    """The tiny workload with every triangle-allowed path of ranks <= 1:
+    the odd (1,1)->1 coupling (the cross product) joins the four natural
+    paths."""
+    _, d = tiny_inputs((1, 1, 1), 8, allp=True)
+    check_full((1, 1, 1), 6.0, d, 8, allp=True)
+
+
+@pytest.mark.parametrize("ranks", [(1, 1, 1), (2, 2, 2), (3, 3, 3), (4, 4, 4)])
+def test_all_parities_every_rank(ranks):
+    _, d = tiny_inputs(ranks, 40, seed=12, n=40, k=12, box=5.0, rc=6.0, allp=True)
+    check_full(ranks, 6.0, d, 40, allp=True)
 
 
 @pytest.mark.parametrize("C", [1, 63, 64, 65, 128, 200, 256])
@@ -204,3 +219,22 @@ def test_rank5_microbenchmark_sampled_and_no_vjp_vjp():
     with pytest.raises(fc.FlashCartError) as ei:
         gc.vjp_vjp(v_pos=np.zeros((1024, 3), np.float32))
     assert ei.value.status == fc.FC_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("ranks,seed", [((2, 2, 2), 1), ((3, 3, 3), 2)])
+def test_all_parities_microbenchmark_sampled(ranks, seed):
+    """1024 nodes x 128 neighbours x 128 channels with every triangle-allowed
+    path (15 at rank 2, 34 at rank 3), sampled nodes."""
+    from cartesian_tensor_product_amd import flashcart as fc
+    spec = conv.ConvSpec(*ranks, 5.0, all_parities=True)
+    d = inputs.edge_conv_inputs(seed, 1024, 128, 20.0, 128, spec.n_in, spec.n_paths, spec.n_out)
+    gc = GpuConv(ranks, 5.0, d, 128, flags=fc.FC_CONV_ALL_PARITIES)
+    z = gc.fwd()
+    xb, pb = gc.vjp()
+    torch.cuda.synchronize()
+    nodes = np.random.default_rng(96).choice(1024, size=8, replace=False)
+    edges = sample_edges(d["rowptr"], d["sender"], nodes)
+    zo, xo, po, _ = oracle_all(spec, d, edges=edges)
+    assert_close("z", z.cpu().numpy()[nodes], zo[nodes])
+    assert_close("x_grad", xb.cpu().numpy()[nodes], xo[nodes])
+    assert_close("pos_grad", pb.cpu().numpy()[nodes], po[nodes])

@@ -14,11 +14,11 @@ pytestmark = pytest.mark.gpu
 
 
 class GpuConvW:
-    def __init__(self, ranks, d, C, rc=6.0):
+    def __init__(self, ranks, d, C, rc=6.0, flags=0):
         from cartesian_tensor_product_amd import flashcart as fc
         self.fc = fc
         self.N, self.E, self.C = d["pos"].shape[0], int(len(d["sender"])), C
-        self.desc = fc.conv_desc(self.N, self.E, C, *ranks, rc)
+        self.desc = fc.conv_desc(self.N, self.E, C, *ranks, rc, flags=flags)
         self.P, self.nin, self.nout = fc.fc_conv_layout(self.desc)
         self.graph = fc.DeviceGraph(d["rowptr"], d["sender"], self.N, device="cuda")
         t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
@@ -46,9 +46,10 @@ def oracle(spec, d, edges=None):
     return z, xb, pb, wb
 
 
-def check(ranks, d, C, rc=6.0):
-    spec = conv.ConvSpec(*ranks, rc)
-    gc = GpuConvW(ranks, d, C, rc)
+def check(ranks, d, C, rc=6.0, allp=False):
+    from cartesian_tensor_product_amd import flashcart as fc
+    spec = conv.ConvSpec(*ranks, rc, all_parities=allp)
+    gc = GpuConvW(ranks, d, C, rc, flags=fc.FC_CONV_ALL_PARITIES if allp else 0)
     z = gc.fwd()
     xb, pb, wb = gc.vjp()
     torch.cuda.synchronize()
@@ -60,8 +61,8 @@ def check(ranks, d, C, rc=6.0):
     return gc
 
 
-def small(ranks, C, seed=11, n=40, k=12, box=5.0, rc=6.0):
-    spec = conv.ConvSpec(*ranks, rc)
+def small(ranks, C, seed=11, n=40, k=12, box=5.0, rc=6.0, allp=False):
+    spec = conv.ConvSpec(*ranks, rc, all_parities=allp)
     return inputs.edge_conv_inputs(seed, n, k, box, C, spec.n_in, spec.n_paths, spec.n_out, with_edge_w=True)
 
 
@@ -69,6 +70,11 @@ def small(ranks, C, seed=11, n=40, k=12, box=5.0, rc=6.0):
                                    (1, 2, 2), (2, 4, 4), (3, 4, 4)])
 def test_explicit_weights_every_rank_set(ranks):
     check(ranks, small(ranks, 24), 24)
+
+
+@pytest.mark.parametrize("ranks", [(1, 1, 1), (2, 2, 2), (4, 4, 4)])
+def test_explicit_weights_all_parities(ranks):
+    check(ranks, small(ranks, 24, allp=True), 24, allp=True)
 
 
 @pytest.mark.parametrize("C", [1, 65, 200])

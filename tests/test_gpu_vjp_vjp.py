@@ -36,6 +36,36 @@ def test_vjp_vjp_small(ranks, with_vx):
     assert_close("radial_w_hat", Wh.cpu().numpy(), Wo)
 
 
+@pytest.mark.parametrize("ranks", [(1, 1, 1), (2, 2, 2), (3, 3, 3)])
+@pytest.mark.parametrize("with_vx", [False, True])
+def test_vjp_vjp_all_parities(ranks, with_vx):
+    """Every triangle-allowed path (odd J through the Levi-Civita reading)."""
+    from cartesian_tensor_product_amd import flashcart as fc
+    spec = conv.ConvSpec(*ranks, 6.0, all_parities=True)
+    C = 24
+    d = inputs.edge_conv_inputs(7, 40, 12, 5.0, C, spec.n_in, spec.n_paths, spec.n_out, with_vpos=True)
+    rng = np.random.default_rng(8)
+    v_x = inputs.normal(rng, d["x"].shape) if with_vx else None
+    gc = GpuConv(ranks, 6.0, d, C, flags=fc.FC_CONV_ALL_PARITIES)
+    gh, xh, ph, Wh = gc.vjp_vjp(v_x=v_x, v_pos=d["v_pos"], want=("g", "x", "pos", "W"))
+    torch.cuda.synchronize()
+    go, xo, po, Wo = oracle_vv(spec, d, v_x, d["v_pos"])
+    assert_close("g_hat", gh.cpu().numpy(), go)
+    assert_close("x_hat", xh.cpu().numpy(), xo)
+    assert_close("pos_hat", ph.cpu().numpy(), po)
+    assert_close("radial_w_hat", Wh.cpu().numpy(), Wo)
+
+
+def test_vjp_vjp_all_parities_rank4_unsupported():
+    from cartesian_tensor_product_amd import flashcart as fc
+    spec = conv.ConvSpec(4, 4, 4, 6.0, all_parities=True)
+    d = inputs.edge_conv_inputs(7, 20, 6, 5.0, 8, spec.n_in, spec.n_paths, spec.n_out, with_vpos=True)
+    gc = GpuConv((4, 4, 4), 6.0, d, 8, flags=fc.FC_CONV_ALL_PARITIES)
+    with pytest.raises(fc.FlashCartError) as ei:
+        gc.vjp_vjp(v_pos=d["v_pos"])
+    assert ei.value.status == fc.FC_ERR_UNSUPPORTED
+
+
 @pytest.mark.parametrize("ranks", [(3, 3, 3), (4, 4, 4)])
 @pytest.mark.parametrize("with_vx", [False, True])
 def test_vjp_vjp_256_channels(ranks, with_vx):

@@ -293,11 +293,14 @@ CSTEP = 1e-20
 
 def edge_conv_vjp_vjp(spec: ConvSpec, pos, rowptr, sender, x, W, g, v_x=None,
                       v_pos=None, shift=None, edges=None, chunk: int = 4096,
-                      want_W: bool = False, outputs=("g", "x", "pos")):
-    """(g_hat, x_hat, pos_hat, W_hat) for s = <v_x, x_bar> + <v_pos, pos_bar>.
+                      want_W: bool = False, outputs=("g", "x", "pos"), v_W=None):
+    """(g_hat, x_hat, pos_hat, W_hat) for s = <v_x, x_bar> + <v_pos, pos_bar> + <v_W, W_bar>.
 
-    g_hat = d z / d eps and (x_hat, pos_hat, W_hat) = d (x_bar, pos_bar,
-    W_bar) / d eps at (x + eps v_x, pos + eps v_pos), by complex step.
+    App. C Eq. C2 (second-order term) with the weight cotangent carried
+    through w = R W: s is the derivative of <g, z> along (v_x, v_pos, v_W),
+    so g_hat = d z / d eps and (x_hat, pos_hat, W_hat) = d (x_bar, pos_bar,
+    W_bar) / d eps at (x + eps v_x, pos + eps v_pos, W + eps v_W), by
+    complex step.  Each missing cotangent is zero.
     """
     h = CSTEP
     xc = x.astype(np.complex128)
@@ -306,6 +309,8 @@ def edge_conv_vjp_vjp(spec: ConvSpec, pos, rowptr, sender, x, W, g, v_x=None,
         xc = xc + 1j * h * v_x
     if v_pos is not None:
         pc = pc + 1j * h * v_pos
+    if v_W is not None:
+        W = W.astype(np.complex128) + 1j * h * v_W
     g_hat = x_hat = pos_hat = W_hat = None
     if "g" in outputs:
         g_hat = edge_conv_fwd(spec, pc, rowptr, sender, xc, W, shift, edges, chunk).imag / h

@@ -236,6 +236,46 @@ def test_vjp_vjp_against_fd_and_symmetry():
     assert lhs == pytest.approx(rhs, rel=1e-10)
 
 
+def test_vjp_vjp_weight_cotangent():
+    """Eq. C2 with a cotangent v_W on the radial-weight gradient as well.
+
+    Pinned by central differences of the VJP and forward along (v_x, v_pos,
+    v_W), by the symmetry of the Hessian over all three blocks, and by the
+    linearity of z in W: with v_W alone, g_hat is the forward with W = v_W
+    and x_hat / pos_hat are the VJP with W = v_W, while W_bar does not
+    depend on W at all.
+    """
+    spec, d = tiny(2, channels=3)
+    rng = np.random.default_rng(23)
+    v_pos = rng.standard_normal(d["pos"].shape)
+    v_x = rng.standard_normal(d["x"].shape)
+    v_W = rng.standard_normal(d["W"].shape)
+    base = (spec, d["pos"], d["rowptr"], d["sender"], d["x"], d["W"], d["g"])
+    gh, xh, ph, Wh = conv.edge_conv_vjp_vjp(*base, v_x=v_x, v_pos=v_pos, v_W=v_W, want_W=True)
+    h = 1e-5
+    args = lambda sgn: (spec, d["pos"] + sgn * h * v_pos, d["rowptr"], d["sender"], d["x"] + sgn * h * v_x,
+                        d["W"] + sgn * h * v_W)
+    fp = conv.edge_conv_vjp(*args(1), d["g"], want_W=True)
+    fm = conv.edge_conv_vjp(*args(-1), d["g"], want_W=True)
+    for got, a, b in zip((xh, ph, Wh), fp, fm):
+        assert np.abs(got - (a - b) / (2 * h)).max() < 1e-6 * max(1.0, np.abs(got).max())
+    zd = (conv.edge_conv_fwd(*args(1)) - conv.edge_conv_fwd(*args(-1))) / (2 * h)
+    assert np.abs(gh - zd).max() < 1e-6 * np.abs(gh).max()
+    # Hessian symmetry over (x, pos, W)
+    u_pos, u_x, u_W = (rng.standard_normal(a.shape) for a in (d["pos"], d["x"], d["W"]))
+    _, xh2, ph2, Wh2 = conv.edge_conv_vjp_vjp(*base, v_x=u_x, v_pos=u_pos, v_W=u_W, want_W=True,
+                                              outputs=("x", "pos"))
+    lhs = np.sum(u_pos * ph) + np.sum(u_x * xh) + np.sum(u_W * Wh)
+    rhs = np.sum(v_pos * ph2) + np.sum(v_x * xh2) + np.sum(v_W * Wh2)
+    assert lhs == pytest.approx(rhs, rel=1e-10)
+    # linearity in W
+    g1, x1, p1, W1 = conv.edge_conv_vjp_vjp(*base, v_W=v_W, want_W=True)
+    assert np.allclose(g1, conv.edge_conv_fwd(spec, d["pos"], d["rowptr"], d["sender"], d["x"], v_W), atol=1e-12)
+    xb, pb, _ = conv.edge_conv_vjp(spec, d["pos"], d["rowptr"], d["sender"], d["x"], v_W, d["g"])
+    assert np.allclose(x1, xb, atol=1e-12) and np.allclose(p1, pb, atol=1e-12)
+    assert np.abs(W1).max() == 0.0
+
+
 # ---------------------------------------------------------------- diamond --
 
 def test_diamond_neighbour_counts():

@@ -87,10 +87,10 @@ def extras(dev, only_ladder=False, conv_ranks=(3, 4), only_conv=False):
              "vjp_ms": timed(lambda: fc.fc_edge_conv_vjp(desc, graph, pos, None, x, W, g, xb, pb, None, ws)),
              "radial_w_grad_ms": timed(lambda: fc.fc_edge_conv_vjp(desc, graph, pos, None, x, W, g, None, None, Wb,
                                                                    ws)),
-             "vjp_vjp_ms": timed(lambda: fc.fc_edge_conv_vjp_vjp(desc, graph, pos, None, x, W, g, None, vp, gh, xh,
+             "vjp_vjp_ms": timed(lambda: fc.fc_edge_conv_vjp_vjp(desc, graph, pos, None, x, W, g, None, vp, None, gh, xh,
                                                                  ph, None, ws), iters=5),
              "radial_w_hat_ms": timed(lambda: fc.fc_edge_conv_vjp_vjp(desc, graph, pos, None, x, W, g, None, vp,
-                                                                      None, None, None, Wb, ws), iters=5)}
+                                                                      None, None, None, None, Wb, ws), iters=5)}
         r["fwd_plus_vjp_edge_channels_per_s"] = E * CHANNELS / ((r["fwd_ms"] + r["vjp_ms"]) * 1e-3)
         out[f"conv_rank{l}_1024n_128c_128nbr"] = r
         del z, xb, pb, gh, xh, ph, ws, Wb
@@ -112,7 +112,7 @@ def extras(dev, only_ladder=False, conv_ranks=(3, 4), only_conv=False):
              "vjp_ms": timed(lambda: fc.fc_edge_conv_vjp(desc, graph, pos, None, x, W, g, xb, pb, None, ws))}
         if l <= 3:
             gh, xh, ph = torch.empty_like(z), torch.empty_like(x), torch.empty_like(pb)
-            r["vjp_vjp_ms"] = timed(lambda: fc.fc_edge_conv_vjp_vjp(desc, graph, pos, None, x, W, g, None, vp, gh, xh,
+            r["vjp_vjp_ms"] = timed(lambda: fc.fc_edge_conv_vjp_vjp(desc, graph, pos, None, x, W, g, None, vp, None, gh, xh,
                                                                     ph, None, ws), iters=5)
             del gh, xh, ph
         r["fwd_plus_vjp_edge_channels_per_s"] = E * CHANNELS / ((r["fwd_ms"] + r["vjp_ms"]) * 1e-3)
@@ -234,7 +234,7 @@ def grid(dev, steps):
                      "vjp_ms": timed(lambda: fc.fc_edge_conv_vjp(desc, graph, pos, None, x, W, g, xb, pb, None, ws),
                                      steps),
                      "vjp_vjp_ms": (timed(lambda: fc.fc_edge_conv_vjp_vjp(desc, graph, pos, None, x, W, g, None, vp,
-                                                                          z, xb, pb, None, ws), max(2, steps // 4))
+                                                                          None, z, xb, pb, None, ws), max(2, steps // 4))
                                     if l <= 4 else None)}
                 w = rn((E, P, C))
                 wb = torch.empty_like(w)

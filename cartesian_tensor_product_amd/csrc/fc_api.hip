@@ -209,11 +209,37 @@ fc_status fc_graph_validate(int32_t n_nodes, int32_t n_edges, const int32_t* h_r
   return ok();
 }
 
+namespace {
+// VJP-of-VJP workspace: the VJP workspace, then (weight cotangent given
+// with x / pos cotangents) the forward and VJP taken with the weight
+// cotangent as weights, [N][out_rows][C], [N][in_rows][C] and [N][3].
+struct VVWorkspace {
+  fc::VjpWorkspace vjp;
+  float *g_lin, *x_lin, *p_lin;
+  size_t bytes;
+  VVWorkspace(const fc_conv_desc* d, int P, int nin, int nout, void* base)
+      : vjp(d->n_nodes, d->n_edges, d->channels, nin, P, true, base) {
+    const size_t N = d->n_nodes, C = d->channels;
+    char* p = static_cast<char*>(base);
+    size_t off = vjp.bytes;
+    g_lin = reinterpret_cast<float*>(p + off);
+    off += fc::align256(N * nout * C * sizeof(float));
+    x_lin = reinterpret_cast<float*>(p + off);
+    off += fc::align256(N * nin * C * sizeof(float));
+    p_lin = reinterpret_cast<float*>(p + off);
+    off += fc::align256(N * 3 * sizeof(float));
+    bytes = off;
+    if (!base) g_lin = x_lin = p_lin = nullptr;
+  }
+};
+}  // namespace
+
 size_t fc_edge_conv_workspace_bytes(const fc_conv_desc* d, int32_t op) {
   if (check_desc(d) != FC_OK) return 0;
   if (op == 1 || op == 2) {
     int P, nin, nout;
     layout(d, &P, &nin, &nout);
+    if (op == 2) return VVWorkspace(d, P, nin, nout, nullptr).bytes;
     const fc::VjpWorkspace w(d->n_nodes, d->n_edges, d->channels, nin, P, true, nullptr);
     return w.bytes;
   }
@@ -308,8 +334,8 @@ fc_status fc_edge_conv_vjp_w(const fc_conv_desc* d, const fc_graph* g, const flo
 
 fc_status fc_edge_conv_vjp_vjp(const fc_conv_desc* d, const fc_graph* g, const float* pos, const float* shift,
                                const float* x, const float* radial_w, const float* g_z, const float* v_x,
-                               const float* v_pos, float* g_hat, float* x_hat, float* pos_hat,
-                               float* radial_w_hat, void* workspace, size_t workspace_bytes,
+                               const float* v_pos, const float* v_radial_w, float* g_hat, float* x_hat,
+                               float* pos_hat, float* radial_w_hat, void* workspace, size_t workspace_bytes,
                                hipStream_t stream) {
   if (fc_status s = check_desc(d)) return s;
   if (!fc::conv_vv_supported(d->l_in, d->l_edge, lout_key(d)))
@@ -324,22 +350,57 @@ fc_status fc_edge_conv_vjp_vjp(const fc_conv_desc* d, const fc_graph* g, const f
   if (!pos || !x || !radial_w || ((x_hat || pos_hat || radial_w_hat) && !g_z))
     return fail(FC_ERR_INVALID_ARGUMENT, "VJP-of-VJP: NULL pos, x, radial_w or g_z");
   if (misaligned(pos, 4) || misaligned(x, 4) || misaligned(radial_w, 4) || misaligned(g_z, 4) ||
-      misaligned(v_x, 4) || misaligned(v_pos, 4) || misaligned(g_hat, 4) || misaligned(x_hat, 4) ||
-      misaligned(pos_hat, 4) || misaligned(radial_w_hat, 4) || misaligned(shift, 4))
+      misaligned(v_x, 4) || misaligned(v_pos, 4) || misaligned(v_radial_w, 4) || misaligned(g_hat, 4) ||
+      misaligned(x_hat, 4) || misaligned(pos_hat, 4) || misaligned(radial_w_hat, 4) || misaligned(shift, 4))
     return fail(FC_ERR_INVALID_ARGUMENT, "VJP-of-VJP: arrays must be 4-byte aligned");
+  // second-order part (x / pos cotangents) and the part linear in the
+  // weight cotangent
+  const bool second = v_x || v_pos || !v_radial_w;
+  const bool lin = v_radial_w && (g_hat || x_hat || pos_hat);
   const size_t need = fc_edge_conv_workspace_bytes(d, 2);
-  if ((x_hat || pos_hat || radial_w_hat) && need > 0 && (!workspace || workspace_bytes < need))
+  if ((x_hat || pos_hat || radial_w_hat || (lin && second)) && need > 0 && (!workspace || workspace_bytes < need))
     return fail(FC_ERR_WORKSPACE, "VJP-of-VJP needs %zu workspace bytes", need);
-  fc::ConvArgs a = make_args(d, g, pos, shift, x, radial_w);
-  a.g = g_z;
-  a.v_x = v_x;
-  a.v_pos = v_pos;
-  a.g_hat = g_hat;
-  a.x_bar = x_hat;
-  a.pos_bar = pos_hat;
-  a.W_bar = radial_w_hat;
-  a.rbar = static_cast<float*>(workspace);
-  fc::conv_dispatch(2, d->l_in, d->l_edge, lout_key(d), a, stream);
+  int P, nin, nout;
+  layout(d, &P, &nin, &nout);
+  const VVWorkspace ws(d, P, nin, nout, workspace);
+  const size_t N = d->n_nodes, C = d->channels;
+  if (second) {
+    fc::ConvArgs a = make_args(d, g, pos, shift, x, radial_w);
+    a.g = g_z;
+    a.v_x = v_x;
+    a.v_pos = v_pos;
+    a.g_hat = g_hat;
+    a.x_bar = x_hat;
+    a.pos_bar = pos_hat;
+    a.W_bar = radial_w_hat;
+    a.rbar = static_cast<float*>(workspace);
+    fc::conv_dispatch(2, d->l_in, d->l_edge, lout_key(d), a, stream);
+  } else if (radial_w_hat) {
+    // W_bar does not depend on the radial weights: no x / pos cotangent, no W_hat
+    fc::launch_zero((size_t)d->n_basis * P * C, radial_w_hat, stream);
+  }
+  if (lin) {
+    // z, x_bar and pos_bar are linear in the radial weights: the weight
+    // cotangent adds the forward and the VJP taken with v_radial_w as the
+    // weights (written straight to the outputs when there is no
+    // second-order part, else added to it)
+    if (g_hat) {
+      fc::ConvArgs a = make_args(d, g, pos, shift, x, v_radial_w);
+      a.z = second ? ws.g_lin : g_hat;
+      fc::conv_dispatch(0, d->l_in, d->l_edge, lout_key(d), a, stream);
+      if (second) fc::launch_add(N * nout * C, ws.g_lin, g_hat, stream);
+    }
+    if (x_hat || pos_hat) {
+      fc::ConvArgs a = make_args(d, g, pos, shift, x, v_radial_w);
+      a.g = g_z;
+      a.x_bar = x_hat ? (second ? ws.x_lin : x_hat) : nullptr;
+      a.pos_bar = pos_hat ? (second ? ws.p_lin : pos_hat) : nullptr;
+      a.rbar = static_cast<float*>(workspace);
+      fc::conv_dispatch(1, d->l_in, d->l_edge, lout_key(d), a, stream);
+      if (second && x_hat) fc::launch_add(N * nin * C, ws.x_lin, x_hat, stream);
+      if (second && pos_hat) fc::launch_add(N * 3, ws.p_lin, pos_hat, stream);
+    }
+  }
   return check_launch("edge conv VJP-of-VJP");
 }
 

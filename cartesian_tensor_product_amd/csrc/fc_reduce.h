@@ -9,4 +9,10 @@ namespace fc {
 // depends only on nblk (bitwise reproducible).
 void launch_block_sum(int nblk, int n, const float* part, float* out, hipStream_t st);
 
+// dst[i] += src[i] for i < n.
+void launch_add(size_t n, const float* src, float* dst, hipStream_t st);
+
+// dst[i] = 0 for i < n (a kernel, so that it may sit in a captured graph).
+void launch_zero(size_t n, float* dst, hipStream_t st);
+
 }  // namespace fc

@@ -38,4 +38,29 @@ void launch_block_sum(int nblk, int n, const float* part, float* out, hipStream_
   hipLaunchKernelGGL(block_sum_kernel, dim3((n + kWave - 1) / kWave), dim3(4 * kWave), 0, st, nblk, n, part, out);
 }
 
+__global__ __launch_bounds__(256) void add_kernel(size_t n, const float* __restrict__ src, float* __restrict__ dst) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    dst[i] += src[i];
+}
+
+__global__ __launch_bounds__(256) void zero_kernel(size_t n, float* __restrict__ dst) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    dst[i] = 0.f;
+}
+
+static dim3 elementwise_grid(size_t n) {
+  const size_t b = (n + 255) / 256;
+  return dim3((unsigned)(b < 8192 ? b : 8192));
+}
+
+void launch_add(size_t n, const float* src, float* dst, hipStream_t st) {
+  if (n == 0) return;
+  hipLaunchKernelGGL(add_kernel, elementwise_grid(n), dim3(256), 0, st, n, src, dst);
+}
+
+void launch_zero(size_t n, float* dst, hipStream_t st) {
+  if (n == 0) return;
+  hipLaunchKernelGGL(zero_kernel, elementwise_grid(n), dim3(256), 0, st, n, dst);
+}
+
 }  // namespace fc

@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define FC_ABI_VERSION 1
+#define FC_ABI_VERSION 2
 
 typedef enum {
   FC_OK = 0,
@@ -179,20 +179,24 @@ fc_status fc_edge_conv_vjp_w(const fc_conv_desc* d, const fc_graph* g, const flo
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* VJP-of-VJP (Eq. C2 with the position derivatives of T_l and R_b): for
- * s = <v_x, x_grad> + <v_pos, pos_grad> (NULL cotangent = zero), writes
- * g_hat = ds/dg_z [N][out_rows][C], x_hat = ds/dx [N][in_rows][C],
- * pos_hat = ds/dpos [N][3] and radial_w_hat = ds/dradial_w [8][P][C] (each
- * when non-NULL; at least one).  The weight cotangent of Eq. C2 is zero.
- * Needs g_z unless only g_hat is requested, the graph transpose for x_hat
- * and pos_hat, and a workspace of fc_edge_conv_workspace_bytes(d, 2) bytes
- * unless only g_hat is requested.  Instantiated for ranks <= 4
- * (FC_ERR_UNSUPPORTED at rank 5). */
+ * s = <v_x, x_grad> + <v_pos, pos_grad> + <v_radial_w, radial_w_grad>
+ * (v_x [N][in_rows][C], v_pos [N][3], v_radial_w [8][P][C]; a NULL
+ * cotangent is zero), writes g_hat = ds/dg_z [N][out_rows][C],
+ * x_hat = ds/dx [N][in_rows][C], pos_hat = ds/dpos [N][3] and
+ * radial_w_hat = ds/dradial_w [8][P][C] (each when non-NULL; at least one).
+ * z is linear in radial_w, so the weight cotangent adds the forward and
+ * the VJP evaluated with v_radial_w as the weights to g_hat, x_hat and
+ * pos_hat and leaves radial_w_hat unchanged.  Needs g_z unless only g_hat
+ * is requested, the graph transpose for x_hat and pos_hat, and a workspace
+ * of fc_edge_conv_workspace_bytes(d, 2) bytes unless only g_hat is
+ * requested with v_radial_w NULL (or v_radial_w the only cotangent).
+ * Instantiated for ranks <= 4 (FC_ERR_UNSUPPORTED at rank 5). */
 fc_status fc_edge_conv_vjp_vjp(const fc_conv_desc* d, const fc_graph* g, const float* pos,
                                const float* shift, const float* x, const float* radial_w,
                                const float* g_z, const float* v_x, const float* v_pos,
-                               float* g_hat, float* x_hat, float* pos_hat,
-                               float* radial_w_hat, void* workspace, size_t workspace_bytes,
-                               hipStream_t stream);
+                               const float* v_radial_w, float* g_hat, float* x_hat,
+                               float* pos_hat, float* radial_w_hat, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Node-local correlation ladder (§5 Eq. 2; App. E "Path-reduced products").

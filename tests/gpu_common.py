@@ -44,7 +44,7 @@ class GpuConv:
         self.fc.fc_edge_conv_fwd(self.desc, self.graph, self.pos, self.shift, self.x, self.W, z)
         return z
 
-    def vjp_vjp(self, v_x=None, v_pos=None, want=("g", "x", "pos"), g=None):
+    def vjp_vjp(self, v_x=None, v_pos=None, want=("g", "x", "pos"), g=None, v_W=None):
         """(g_hat, x_hat, pos_hat, radial_w_hat); entries not in ``want`` are None."""
         t = self.torch
         dv = lambda a: None if a is None else t.from_numpy(np.ascontiguousarray(a)).to(self.device)
@@ -54,7 +54,8 @@ class GpuConv:
         Wh = t.empty_like(self.W) if "W" in want else None
         ws = self.fc.workspace(self.fc.fc_edge_conv_workspace_bytes(self.desc, 2), self.device)
         self.fc.fc_edge_conv_vjp_vjp(self.desc, self.graph, self.pos, self.shift, self.x, self.W,
-                                     self.g if g is None else dv(g), dv(v_x), dv(v_pos), gh, xh, ph, Wh, ws)
+                                     self.g if g is None else dv(g), dv(v_x), dv(v_pos), dv(v_W), gh, xh, ph, Wh,
+                                     ws)
         return gh, xh, ph, Wh
 
     def vjp(self, g=None, want_x=True, want_pos=True, want_W=False):

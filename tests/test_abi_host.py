@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert fc.fc_abi_version() == 1
+    assert fc.fc_abi_version() == 2
     L = fc.lib()
     assert L.fc_status_string(0) == b"FC_OK"
     assert L.fc_status_string(3) == b"FC_ERR_WORKSPACE"
@@ -104,3 +104,13 @@ def test_workspace_sizes():
     d = fc.conv_desc(1024, 131072, 128, 2, 2, 2, 5.0)
     assert fc.fc_edge_conv_workspace_bytes(d, 0) == 0
     assert fc.fc_edge_conv_workspace_bytes(d, 1) >= 131072 * 3 * 4
+
+
+def test_vjp_vjp_workspace_holds_weight_cotangent_terms():
+    """Op 2 adds room for the forward and VJP taken with the weight
+    cotangent as weights: [N][out_rows][C], [N][in_rows][C] and [N][3]."""
+    d = fc.conv_desc(1024, 131072, 128, 2, 2, 2, 5.0)
+    P, nin, nout = fc.fc_conv_layout(d)
+    w1 = fc.fc_edge_conv_workspace_bytes(d, 1)
+    w2 = fc.fc_edge_conv_workspace_bytes(d, 2)
+    assert w2 >= w1 + 4 * 1024 * 128 * (nout + nin) + 4 * 1024 * 3

@@ -11,11 +11,11 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 
-def oracle_vv(spec, d, v_x, v_pos, edges=None, g=None):
+def oracle_vv(spec, d, v_x, v_pos, edges=None, g=None, v_W=None):
     g = d["g"] if g is None else g
     return conv.edge_conv_vjp_vjp(spec, f64(d["pos"]), d["rowptr"], d["sender"], f64(d["x"]), f64(d["W"]),
                                   f64(g), v_x=f64(v_x), v_pos=f64(v_pos), shift=f64(d.get("shift")),
-                                  edges=edges, want_W=True)
+                                  edges=edges, want_W=True, v_W=f64(v_W))
 
 
 @pytest.mark.parametrize("ranks", [(1, 1, 1), (2, 2, 2), (3, 3, 3), (4, 4, 4), (0, 3, 3), (2, 3, 3)])
@@ -140,3 +140,56 @@ def test_vjp_vjp_periodic_and_subsets():
         out = gc.vjp_vjp(v_pos=vp, want=want)
         torch.cuda.synchronize()
         assert_close(want[0], out[idx].cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("ranks", [(1, 1, 1), (2, 2, 2), (3, 3, 3), (0, 3, 3)])
+@pytest.mark.parametrize("cot", ["W", "W+pos", "W+x+pos"])
+def test_vjp_vjp_weight_cotangent(ranks, cot):
+    """A cotangent on the radial-weight gradient, alone or with the x and
+    position cotangents (the linear part is then added to the second-order
+    part)."""
+    spec = conv.ConvSpec(*ranks, 6.0)
+    C = 40
+    d = inputs.edge_conv_inputs(17, 40, 12, 5.0, C, spec.n_in, spec.n_paths, spec.n_out, with_vpos=True)
+    rng = np.random.default_rng(18)
+    v_W = inputs.normal(rng, d["W"].shape)
+    v_x = inputs.normal(rng, d["x"].shape) if "x" in cot else None
+    v_pos = d["v_pos"] if "pos" in cot else None
+    gc = GpuConv(ranks, 6.0, d, C)
+    gh, xh, ph, Wh = gc.vjp_vjp(v_x=v_x, v_pos=v_pos, v_W=v_W, want=("g", "x", "pos", "W"))
+    torch.cuda.synchronize()
+    go, xo, po, Wo = oracle_vv(spec, d, v_x, v_pos, v_W=v_W)
+    assert_close("g_hat", gh.cpu().numpy(), go)
+    assert_close("x_hat", xh.cpu().numpy(), xo)
+    assert_close("pos_hat", ph.cpu().numpy(), po)
+    if cot == "W":
+        assert float(Wh.abs().max()) == 0.0 and np.abs(Wo).max() == 0.0
+    else:
+        assert_close("radial_w_hat", Wh.cpu().numpy(), Wo)
+
+
+@pytest.mark.parametrize("with_pos", [False, True])
+def test_vjp_vjp_weight_cotangent_subsets(with_pos):
+    """Each output requested on its own with the weight cotangent; g_hat
+    alone without a workspace when the weight cotangent is the only one."""
+    spec = conv.ConvSpec(2, 2, 2, 6.0)
+    C = 24
+    d = inputs.edge_conv_inputs(19, 36, 10, 5.0, C, spec.n_in, spec.n_paths, spec.n_out, with_vpos=True)
+    rng = np.random.default_rng(20)
+    v_W = inputs.normal(rng, d["W"].shape)
+    v_pos = d["v_pos"] if with_pos else None
+    gc = GpuConv((2, 2, 2), 6.0, d, C)
+    ref = oracle_vv(spec, d, None, v_pos, v_W=v_W)
+    for idx, want in enumerate(("g", "x", "pos", "W")):
+        out = gc.vjp_vjp(v_pos=v_pos, v_W=v_W, want=(want,))
+        torch.cuda.synchronize()
+        if want == "W" and not with_pos:
+            assert float(out[idx].abs().max()) == 0.0
+        else:
+            assert_close(want, out[idx].cpu().numpy(), ref[idx])
+    if not with_pos:
+        gh = torch.empty((gc.N, gc.nout, gc.C), device=gc.device)
+        gc.fc.fc_edge_conv_vjp_vjp(gc.desc, gc.graph, gc.pos, gc.shift, gc.x, gc.W, None, None, None,
+                                   torch.from_numpy(v_W).to(gc.device), gh, None, None, None, None)
+        torch.cuda.synchronize()
+        assert_close("g_hat", gh.cpu().numpy(), ref[0])

@@ -21,6 +21,11 @@ FlashCart paper:
   the same forward and VJP with w [E, P, C] given instead of formed from the
   radial basis; its gradient w_bar [E, P, C] is returned per edge and the
   position gradient runs through the direction tensors only (w held fixed).
+* path-summed outputs (ConvSpec(sum_paths=True)): the kernel option of
+  summing the outputs of all paths with the same output rank L into one
+  (2L+1)-row block instead of keeping them separate (App. D "Executing
+  Cartesian tensor products"; weights stay per path).  The VJPs read the same g
+  block for every path of rank L.
 * VJP-of-VJP: with s = <v_x, x_bar> + <v_pos, pos_bar>, g_hat = ds/dg is the
   directional derivative of the forward along (v_x, v_pos), and
   (x_hat, pos_hat, W_hat) is the directional derivative of the VJP along the
@@ -93,11 +98,16 @@ class ConvSpec:
     """Ranks, paths and layouts of one edge-convolution problem."""
 
     def __init__(self, l_in: int, l_edge: int, l_out: int, r_cut: float,
-                 n_basis: int = 8, all_parities: bool = False):
+                 n_basis: int = 8, all_parities: bool = False, sum_paths: bool = False):
         self.l_in, self.l_edge, self.l_out = l_in, l_edge, l_out
         self.r_cut, self.n_basis = r_cut, n_basis
         self.paths = T.conv_paths(l_in, l_edge, l_out, all_parities)
-        self.rows, self.n_out = T.out_layout(self.paths, l_out)
+        # path-separated rows (Eq. 1), or one block per output rank into which
+        # every path of that rank adds (the summed-output option); the
+        # forward adds each path into its rows and the VJPs read g from them,
+        # so both layouts run through the same code below
+        layout = T.summed_out_layout if sum_paths else T.out_layout
+        self.rows, self.n_out = layout(self.paths, l_out)
         self.in_off = T.rank_offsets(l_in)
         self.n_in = self.in_off[-1]
 

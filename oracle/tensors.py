@@ -498,6 +498,22 @@ def out_layout(paths: list, l_out: int):
     return rows, acc
 
 
+def summed_out_layout(paths: list, l_out: int):
+    """Rows of the path-summed output (the pages' kernel option of summing
+    the outputs of the coupling paths instead of keeping them separate, App.
+    D "Executing Cartesian tensor products"): every path with output rank L adds into the
+    single (2L+1)-row block of L; ranks without a path take no rows.
+    Returns (rows, n_rows) like out_layout.
+    """
+    off, acc = {}, 0
+    for L in range(l_out + 1):
+        if any(p[2] == L for p in paths):
+            off[L] = acc
+            acc += n_comp(L)
+    rows = [np.array([off[p[2]] + c for c in range(n_comp(p[2]))]) for p in paths]
+    return rows, acc
+
+
 def levi_civita_11_1(x, y):  # noqa: D401
     """eps_ijk x_j y_k: the odd-J (1,1)->1 coupling (cross product).
 

@@ -384,3 +384,116 @@ def test_all_parity_convolution(l):
         xc = d["x"].astype(complex)
         xc[idx] += 1e-20j
         assert loss(d["pos"], xc).imag / 1e-20 == pytest.approx(xb[idx], rel=1e-10, abs=1e-12)
+
+
+# ------------------------------------------------------- path-summed output --
+
+def summed_tiny(ranks, all_parities=False, seed=0, channels=3):
+    sep = conv.ConvSpec(*ranks, 6.0, all_parities=all_parities)
+    summ = conv.ConvSpec(*ranks, 6.0, all_parities=all_parities, sum_paths=True)
+    d = inputs.edge_conv_inputs(seed, 32, 8, 6.0, channels, sep.n_in, sep.n_paths, sep.n_out)
+    f = {k: (v.astype(np.float64) if isinstance(v, np.ndarray) and v.dtype == np.float32 else v)
+         for k, v in d.items()}
+    rng = np.random.default_rng(seed + 100)
+    f["g"] = rng.standard_normal((32, summ.n_out, channels))
+    return sep, summ, f
+
+
+def rank_blocks(paths, l_out):
+    """Per output rank present: (L, first summed row, [(path index, eta, P_L)]),
+    written from the two layouts' definitions (App. D Fig. D1 for the
+    separate rows: off(L) + c P_L + eta)."""
+    out, row = [], 0
+    for L in range(l_out + 1):
+        ps = [i for i, p in enumerate(paths) if p[2] == L]
+        if ps:
+            out.append((L, row, [(i, eta, len(ps)) for eta, i in enumerate(ps)]))
+            row += 2 * L + 1
+    return out, row
+
+
+@pytest.mark.parametrize("ranks,allp", [((2, 2, 2), False), ((1, 2, 2), False), ((0, 1, 2), False),
+                                        ((1, 1, 1), True)])
+def test_summed_output_is_rank_block_sum(ranks, allp):
+    """z_sum[L block, c] = sum over the paths eta -> L of the separate row
+    off(L) + c P_L + eta; an output rank with no path has no rows."""
+    sep, summ, d = summed_tiny(ranks, allp)
+    args = (d["pos"], d["rowptr"], d["sender"], d["x"], d["W"])
+    zs = conv.edge_conv_fwd(sep, *args)
+    zm = conv.edge_conv_fwd(summ, *args)
+    blocks, nrow = rank_blocks(sep.paths, ranks[2])
+    assert zm.shape[1] == nrow == summ.n_out
+    off_sep = {}
+    acc = 0
+    for L in range(ranks[2] + 1):
+        off_sep[L] = acc
+        acc += (2 * L + 1) * sum(1 for p in sep.paths if p[2] == L)
+    for L, r0, ps in blocks:
+        for c in range(2 * L + 1):
+            want = sum(zs[:, off_sep[L] + c * PL + eta, :] for _, eta, PL in ps)
+            assert np.abs(zm[:, r0 + c, :] - want).max() < 1e-12 * max(1.0, np.abs(want).max())
+
+
+def test_summed_output_one_path_per_rank_equals_separate():
+    """l_in = 0: one path per output rank, so both layouts coincide (and
+    l_out above l_edge leaves the top rank without rows)."""
+    for ranks in ((0, 2, 2), (0, 1, 2)):
+        sep, summ, d = summed_tiny(ranks)
+        args = (d["pos"], d["rowptr"], d["sender"], d["x"], d["W"])
+        assert summ.n_out == sep.n_out
+        assert np.array_equal(conv.edge_conv_fwd(sep, *args), conv.edge_conv_fwd(summ, *args))
+
+
+def test_summed_output_equivariance():
+    sep, summ, d = summed_tiny((2, 2, 2))
+    rng = np.random.default_rng(31)
+    rows = [(np.arange(r0, r0 + 2 * L + 1), L) for L, r0, _ in rank_blocks(summ.paths, 2)[0]]
+    for reflect in (False, True):
+        R = rand_rotation(rng, reflect)
+        z = conv.edge_conv_fwd(summ, d["pos"], d["rowptr"], d["sender"], d["x"], d["W"])
+        xr = rotate_rows(in_rows(summ), d["x"], R)
+        zr = conv.edge_conv_fwd(summ, d["pos"] @ R.T, d["rowptr"], d["sender"], xr, d["W"])
+        assert np.abs(zr - rotate_rows(rows, z, R)).max() < 1e-10 * np.abs(z).max()
+
+
+@pytest.mark.parametrize("ranks", [(1, 1, 1), (2, 2, 2)])
+def test_summed_vjp_against_complex_step_and_broadcast(ranks):
+    """The VJP of the summed output: complex step of <g, z_sum> in every
+    position coordinate and central differences in sampled x and W; and,
+    as the adjoint of the block sum, the separate VJP with g copied to
+    every path of the rank."""
+    sep, summ, d = summed_tiny(ranks)
+    g = d["g"]
+    xb, pb, Wb = conv.edge_conv_vjp(summ, d["pos"], d["rowptr"], d["sender"], d["x"], d["W"], g, want_W=True)
+    loss = lambda pos, x, W: np.sum(g * conv.edge_conv_fwd(summ, pos, d["rowptr"], d["sender"], x, W))
+    for i in range(d["pos"].shape[0]):
+        for j in range(3):
+            pc = d["pos"].astype(complex)
+            pc[i, j] += 1e-20j
+            assert abs(loss(pc, d["x"], d["W"]).imag / 1e-20 - pb[i, j]) < 1e-9 * max(1, abs(pb).max())
+    rng = np.random.default_rng(4)
+    h = 1e-6
+    for _ in range(6):
+        idx = tuple(rng.integers(0, s) for s in d["x"].shape)
+        xp, xm = d["x"].copy(), d["x"].copy()
+        xp[idx] += h
+        xm[idx] -= h
+        assert (loss(d["pos"], xp, d["W"]) - loss(d["pos"], xm, d["W"])) / (2 * h) == pytest.approx(
+            xb[idx], rel=1e-6, abs=1e-7)
+        idw = tuple(rng.integers(0, s) for s in d["W"].shape)
+        Wp, Wm = d["W"].copy(), d["W"].copy()
+        Wp[idw] += h
+        Wm[idw] -= h
+        assert (loss(d["pos"], d["x"], Wp) - loss(d["pos"], d["x"], Wm)) / (2 * h) == pytest.approx(
+            Wb[idw], rel=1e-6, abs=1e-7)
+    blocks, _ = rank_blocks(sep.paths, ranks[2])
+    gs = np.zeros((g.shape[0], sep.n_out, g.shape[2]))
+    acc = 0
+    for L, r0, ps in blocks:
+        for c in range(2 * L + 1):
+            for _, eta, PL in ps:
+                gs[:, acc + c * PL + eta, :] = g[:, r0 + c, :]
+        acc += (2 * L + 1) * len(ps)
+    xs, ps_, Ws = conv.edge_conv_vjp(sep, d["pos"], d["rowptr"], d["sender"], d["x"], d["W"], gs, want_W=True)
+    for a, b in ((xb, xs), (pb, ps_), (Wb, Ws)):
+        assert np.abs(a - b).max() < 1e-12 * max(1.0, np.abs(b).max())

@@ -118,6 +118,48 @@ def extras(dev, only_ladder=False, conv_ranks=(3, 4), only_conv=False):
         r["fwd_plus_vjp_edge_channels_per_s"] = E * CHANNELS / ((r["fwd_ms"] + r["vjp_ms"]) * 1e-3)
         out[f"conv_all_parities_rank{l}_1024n_128c_128nbr"] = r
         del z, xb, pb, ws
+    # path-summed outputs (one block per output rank): the micro workload at
+    # ranks 2, 3, 4; z and g shrink from sum_L (2L+1) P_L rows to (l+1)^2
+    for l in (() if only_ladder else ((2, 3, 4) if not only_conv else ())):
+        desc = fc.conv_desc(N_NODES, N_NODES * K_NBR, CHANNELS, l, l, l, R_CUT, flags=fc.FC_CONV_SUM_PATHS)
+        P, n_in, n_out = fc.fc_conv_layout(desc)
+        d = inputs.edge_conv_inputs(1 if l == 2 else 2, N_NODES, K_NBR, BOX, CHANNELS, n_in, P, n_out,
+                                    with_vpos=True)
+        graph = fc.DeviceGraph(d["rowptr"], d["sender"], N_NODES, device=dev)
+        pos, x, W, g, vp = t(d["pos"]), t(d["x"]), t(d["W"]), t(d["g"]), t(d["v_pos"])
+        z = torch.empty((N_NODES, n_out, CHANNELS), device=dev)
+        xb, pb = torch.empty_like(x), torch.empty((N_NODES, 3), device=dev)
+        ws = fc.workspace(fc.fc_edge_conv_workspace_bytes(desc, 2 if l <= 3 else 1), dev)
+        E = N_NODES * K_NBR
+        r = {"out_rows": n_out, "fwd_ms": timed(lambda: fc.fc_edge_conv_fwd(desc, graph, pos, None, x, W, z)),
+             "vjp_ms": timed(lambda: fc.fc_edge_conv_vjp(desc, graph, pos, None, x, W, g, xb, pb, None, ws))}
+        if l <= 3:
+            gh, xh, ph = torch.empty_like(z), torch.empty_like(x), torch.empty_like(pb)
+            r["vjp_vjp_ms"] = timed(lambda: fc.fc_edge_conv_vjp_vjp(desc, graph, pos, None, x, W, g, None, vp, None,
+                                                                    gh, xh, ph, None, ws), iters=5)
+            del gh, xh, ph
+        bf, bv = algorithmic_bytes(N_NODES, E, CHANNELS, n_in, n_out, P)
+        r["fwd_plus_vjp_edge_channels_per_s"] = E * CHANNELS / ((r["fwd_ms"] + r["vjp_ms"]) * 1e-3)
+        r["fwd_plus_vjp_frac_hbm"] = (bf + bv) / ((r["fwd_ms"] + r["vjp_ms"]) * 1e-3) / 1e9 / HBM_PEAK_GBS
+        out[f"conv_summed_rank{l}_1024n_128c_128nbr"] = r
+        del z, xb, pb, ws
+    # equivariant RMS normalisation of the ladder's node features (4096
+    # nodes, 128 channels, ranks <= 3): forward, and VJP with both gradients
+    if not only_conv:
+        nd = fc.norm_desc(4096, CHANNELS, 3, 1e-5)
+        rng = np.random.default_rng(5)
+        xn = t(inputs.normal(rng, (4096, 16, CHANNELS)))
+        gam = t(inputs.f32(1.0 + 0.1 * rng.standard_normal((4, CHANNELS))))
+        gy = t(inputs.normal(rng, (4096, 16, CHANNELS)))
+        yn, isn, xnb, gamb = torch.empty_like(xn), torch.empty(4096, device=dev), torch.empty_like(xn), torch.empty_like(gam)
+        wsn = fc.workspace(fc.fc_rms_norm_workspace_bytes(nd), dev)
+        fms = timed(lambda: fc.fc_rms_norm_fwd(nd, xn, gam, yn, isn))
+        vms = timed(lambda: fc.fc_rms_norm_vjp(nd, xn, gam, isn, gy, xnb, gamb, wsn))
+        nb = 4096 * 16 * CHANNELS * 4
+        out["rms_norm_4096n_128c_rank3"] = {"fwd_ms": fms, "vjp_ms": vms,
+                                            "fwd_GBs_alg": 2 * nb / (fms * 1e-3) / 1e9,
+                                            "vjp_GBs_alg": 3 * nb / (vms * 1e-3) / 1e9}
+        del xn, gy, yn, xnb, wsn
     # node-local ladder, 4096 nodes, 128 channels, ranks <= 3, order 4, both variants
     for name, var in (() if only_conv else (("full", fc.FC_LADDER_FULL), ("path_reduced", fc.FC_LADDER_PATH_REDUCED))):
         ld = fc.ladder_desc(4096, CHANNELS, 3, 3, 3, 4, var)

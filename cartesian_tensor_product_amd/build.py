@@ -57,7 +57,7 @@ def _weight(src: str) -> int:
     if name.startswith("conv_inst_"):
         digits = name[len("conv_inst_"):-len(".hip")]
         a, b, key = int(digits[0]), int(digits[1]), int(digits[2:])
-        return (a + b + key % 8 + (4 if key >= 8 else 0)) * 10
+        return (a + b + key % 8 + (4 if (key // 8) % 2 else 0)) * 10
     return 1
 
 

@@ -13,6 +13,7 @@
 #include "fc_graph.h"
 #include "fc_block.h"
 #include "fc_ladder.h"
+#include "fc_norm.h"
 
 namespace {
 
@@ -42,13 +43,17 @@ fc_status check_launch(const char* what) {
 bool misaligned(const void* p, size_t a) { return p && (reinterpret_cast<uintptr_t>(p) % a) != 0; }
 
 bool all_parities(const fc_conv_desc* d) { return (d->flags & FC_CONV_ALL_PARITIES) != 0; }
+bool sum_paths(const fc_conv_desc* d) { return (d->flags & FC_CONV_SUM_PATHS) != 0; }
 
 bool path_ok(const fc_conv_desc* d, int l1, int l2, int L) {
   return all_parities(d) ? fc::triangle(l1, l2, L) : fc::admissible(l1, l2, L);
 }
 
-// output-rank key of the configuration (kAllParities set for every path)
-int lout_key(const fc_conv_desc* d) { return d->l_out + (all_parities(d) ? fc::kAllParities : 0); }
+// output-rank key of the configuration (kAllParities set for every path,
+// kSumPaths for path-summed outputs)
+int lout_key(const fc_conv_desc* d) {
+  return d->l_out + (all_parities(d) ? fc::kAllParities : 0) + (sum_paths(d) ? fc::kSumPaths : 0);
+}
 
 int conv_paths_L(const fc_conv_desc* d, int L) {
   int c = 0;
@@ -71,15 +76,17 @@ fc_status check_desc(const fc_conv_desc* d) {
   if (!(d->r_cut > 0.f) || !std::isfinite(d->r_cut))
     return fail(FC_ERR_INVALID_ARGUMENT, "r_cut must be positive and finite");
   if (d->n_basis != fc::kNB) return fail(FC_ERR_UNSUPPORTED, "n_basis must be 8 (got %d)", d->n_basis);
-  if ((d->flags & ~uint32_t(FC_CONV_ALL_PARITIES)) != 0)
-    return fail(FC_ERR_UNSUPPORTED, "flags other than FC_CONV_ALL_PARITIES are not supported (paths separate)");
+  if ((d->flags & ~uint32_t(FC_CONV_ALL_PARITIES | FC_CONV_SUM_PATHS)) != 0)
+    return fail(FC_ERR_UNSUPPORTED, "unknown flags 0x%x (FC_CONV_ALL_PARITIES and FC_CONV_SUM_PATHS are defined)",
+                d->flags);
   int P = 0;
   for (int L = 0; L <= d->l_out; ++L) P += conv_paths_L(d, L);
   if (P == 0) return fail(FC_ERR_INVALID_ARGUMENT, "no admissible path for these ranks");
   if (d->channels > 256) return fail(FC_ERR_UNSUPPORTED, "channels above 256 are not supported");
   if (!fc::conv_supported(d->l_in, d->l_edge, lout_key(d)))
-    return fail(FC_ERR_UNSUPPORTED, "(l_in, l_edge, l_out) = (%d, %d, %d) is not instantiated in this build",
-                d->l_in, d->l_edge, d->l_out);
+    return fail(FC_ERR_UNSUPPORTED,
+                "(l_in, l_edge, l_out) = (%d, %d, %d) with flags 0x%x is not instantiated in this build", d->l_in,
+                d->l_edge, d->l_out, d->flags);
   return FC_OK;
 }
 
@@ -88,7 +95,7 @@ void layout(const fc_conv_desc* d, int* P, int* nin, int* nout) {
   for (int L = 0; L <= d->l_out; ++L) {
     const int c = conv_paths_L(d, L);
     p += c;
-    o += (2 * L + 1) * c;
+    o += (2 * L + 1) * (sum_paths(d) ? (c > 0 ? 1 : 0) : c);
   }
   *P = p;
   *nin = (d->l_in + 1) * (d->l_in + 1);
@@ -114,6 +121,19 @@ fc::ConvArgs make_args(const fc_conv_desc* d, const fc_graph* g, const float* po
   return a;
 }
 
+
+fc_status check_norm(const fc_norm_desc* d) {
+  if (!d) return fail(FC_ERR_INVALID_ARGUMENT, "norm descriptor is NULL");
+  if (d->n_nodes < 1) return fail(FC_ERR_INVALID_ARGUMENT, "norm: n_nodes must be >= 1 (got %d)", d->n_nodes);
+  if (d->channels < 1) return fail(FC_ERR_INVALID_ARGUMENT, "norm: channels must be >= 1 (got %d)", d->channels);
+  if (d->channels > fc::kNormMaxChannels)
+    return fail(FC_ERR_UNSUPPORTED, "norm: channels above %d are not supported", fc::kNormMaxChannels);
+  if (d->l_max < 0) return fail(FC_ERR_INVALID_ARGUMENT, "norm: l_max must be >= 0");
+  if (d->l_max > fc::kNormMaxRank) return fail(FC_ERR_UNSUPPORTED, "norm: l_max above 5 is not supported");
+  if (!(d->eps >= 0.f) || !std::isfinite(d->eps))
+    return fail(FC_ERR_INVALID_ARGUMENT, "norm: eps must be >= 0 and finite");
+  return FC_OK;
+}
 
 fc_status ladder_plan(const fc_ladder_desc* d, fc::LadderPlan* p) {
   if (!d) return fail(FC_ERR_INVALID_ARGUMENT, "ladder descriptor is NULL");
@@ -552,6 +572,38 @@ fc_status fc_block_energy_forces(const fc_conv_desc* cd, const fc_graph* g, cons
     fc::block_scale(forces, (size_t)N * 3, -1.f, stream);
   }
   return check_launch("block energy/forces");
+}
+
+fc_status fc_rms_norm_fwd(const fc_norm_desc* d, const float* x, const float* gamma, float* y, float* inv_scale,
+                          hipStream_t stream) {
+  if (fc_status s = check_norm(d)) return s;
+  if (!x || !y) return fail(FC_ERR_INVALID_ARGUMENT, "norm forward: NULL x or y");
+  if (misaligned(x, 4) || misaligned(gamma, 4) || misaligned(y, 4) || misaligned(inv_scale, 4))
+    return fail(FC_ERR_INVALID_ARGUMENT, "norm forward: arrays must be 4-byte aligned");
+  fc::launch_rms_norm_fwd(d->l_max, d->n_nodes, d->channels, d->eps, x, gamma, y, inv_scale, stream);
+  return check_launch("RMS norm forward");
+}
+
+size_t fc_rms_norm_workspace_bytes(const fc_norm_desc* d) {
+  if (check_norm(d) != FC_OK) return 0;
+  return (size_t)fc::rms_norm_vjp_blocks(d->n_nodes) * (d->l_max + 1) * d->channels * sizeof(float);
+}
+
+fc_status fc_rms_norm_vjp(const fc_norm_desc* d, const float* x, const float* gamma, const float* inv_scale,
+                          const float* g_y, float* x_grad, float* gamma_grad, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  if (fc_status s = check_norm(d)) return s;
+  if (!x || !inv_scale || !g_y) return fail(FC_ERR_INVALID_ARGUMENT, "norm VJP: NULL x, inv_scale or g_y");
+  if (!x_grad && !gamma_grad) return fail(FC_ERR_INVALID_ARGUMENT, "norm VJP: no output requested");
+  if (misaligned(x, 4) || misaligned(gamma, 4) || misaligned(inv_scale, 4) || misaligned(g_y, 4) ||
+      misaligned(x_grad, 4) || misaligned(gamma_grad, 4) || misaligned(workspace, 4))
+    return fail(FC_ERR_INVALID_ARGUMENT, "norm VJP: arrays must be 4-byte aligned");
+  const size_t need = fc_rms_norm_workspace_bytes(d);
+  if (gamma_grad && (!workspace || workspace_bytes < need))
+    return fail(FC_ERR_WORKSPACE, "norm VJP needs %zu workspace bytes for gamma_grad", need);
+  fc::launch_rms_norm_vjp(d->l_max, d->n_nodes, d->channels, x, gamma, inv_scale, g_y, x_grad,
+                          gamma_grad ? static_cast<float*>(workspace) : nullptr, gamma_grad, stream);
+  return check_launch("RMS norm VJP");
 }
 
 }  // extern "C"

@@ -45,9 +45,11 @@ __host__ __device__ constexpr bool triangle(int l1, int l2, int L) {
   int d = l1 > l2 ? l1 - l2 : l2 - l1;
   return d <= L && L <= l1 + l2;
 }
-// Key of the output rank of a configuration that keeps every triangle-allowed
-// path: l_out + kAllParities.
+// Output-rank key of a configuration: l_out, plus kAllParities to keep every
+// triangle-allowed path, plus kSumPaths to sum the outputs of the paths of
+// each output rank into one block.
 inline constexpr int kAllParities = 8;
+inline constexpr int kSumPaths = 16;
 __host__ __device__ constexpr int path_type(int l1, int l2, int L) {
   for (int t = 0; t < tab::kNumPathTypes; ++t)
     if (tab::kPathL1[t] == l1 && tab::kPathL2[t] == l2 && tab::kPathL[t] == L) return t;
@@ -62,12 +64,15 @@ struct PathInfo {
 };
 
 // Paths (l1 <= LIN, l2 <= LEDGE, L <= LOUT), ordered by L then (l1, l2);
-// natural parity, or every triangle-allowed path when the output-rank key is
-// LOUT + kAllParities.
+// natural parity, or every triangle-allowed path with kAllParities in the
+// output-rank key.  Output rows: path-separated (component c of path eta of
+// rank L at off(L) + c P_L + eta), or with kSumPaths one block of 2L+1 rows
+// per output rank that has a path, into which all its paths add.
 template <int LIN, int LEDGE, int LOUT_KEY>
 struct ConvCfg {
   static constexpr int LOUT = LOUT_KEY % kAllParities;
-  static constexpr bool ALL_PARITIES = LOUT_KEY >= kAllParities;
+  static constexpr bool ALL_PARITIES = (LOUT_KEY / kAllParities) % 2 == 1;
+  static constexpr bool SUM = LOUT_KEY >= kSumPaths;
   static constexpr int NIN = nrank(LIN);
   static constexpr int NE = nrank(LEDGE);
   static constexpr bool path_ok(int l1, int l2, int L) {
@@ -89,7 +94,7 @@ struct ConvCfg {
   static constexpr int P = count_all();
   static constexpr int off_L(int L) {
     int o = 0;
-    for (int l = 0; l < L; ++l) o += ncomp(l) * count_L(l);
+    for (int l = 0; l < L; ++l) o += SUM ? (count_L(l) > 0 ? ncomp(l) : 0) : ncomp(l) * count_L(l);
     return o;
   }
   static constexpr int NOUT = off_L(LOUT + 1);
@@ -111,7 +116,9 @@ struct ConvCfg {
   }
   static constexpr std::array<PathInfo, (P > 0 ? P : 1)> paths = build();
 
-  static constexpr int row(int p, int c) { return paths[p].off + c * paths[p].PL + paths[p].eta; }
+  static constexpr int row(int p, int c) {
+    return SUM ? paths[p].off + c : paths[p].off + c * paths[p].PL + paths[p].eta;
+  }
   static constexpr int first_path_of(int L) {
     int i = 0;
     for (int l = 0; l < L; ++l) i += count_L(l);
@@ -123,15 +130,29 @@ struct ConvCfg {
 // one kernel launch (forward) or one sweep over the edges (VJP).  The rows of
 // the group's paths are held path-major in registers: component c of path p
 // sits at loff(p) + c; its row in the node-feature layout is Cfg::row(p, c).
+// With summed outputs the paths of one rank share their registers (loff is
+// that of the group's first path of the rank, the owner), and a group whose
+// first rank began in an earlier group adds to that group's output (carry).
 template <class Cfg, int P0, int P1>
 struct PathGroup {
   static constexpr int p0 = P0, p1 = P1, NP = P1 - P0;
+  // first path of the group with this path's output rank
+  static constexpr bool owner(int p) { return !Cfg::SUM || p == P0 || Cfg::paths[p - 1].L != Cfg::paths[p].L; }
   static constexpr int loff(int p) {
     int o = 0;
-    for (int q = P0; q < p; ++q) o += ncomp(Cfg::paths[q].L);
+    for (int q = P0; q < p; ++q)
+      if (owner(q) && !(Cfg::SUM && Cfg::paths[q].L == Cfg::paths[p].L)) o += ncomp(Cfg::paths[q].L);
     return o;
   }
-  static constexpr int NR = loff(P1);
+  static constexpr int nregs() {
+    int o = 0;
+    for (int q = P0; q < P1; ++q)
+      if (owner(q)) o += ncomp(Cfg::paths[q].L);
+    return o;
+  }
+  static constexpr int NR = nregs();
+  // the rank block of path p was begun by an earlier group (summed outputs)
+  static constexpr bool carry(int p) { return Cfg::SUM && P0 > 0 && Cfg::paths[P0 - 1].L == Cfg::paths[p].L; }
   // whether some path of the group has edge rank l2
   static constexpr bool uses_l2(int l2) {
     for (int q = P0; q < P1; ++q)
@@ -154,21 +175,25 @@ struct PathGroup {
 };
 
 // Split of the paths into groups whose register cost stays within BUDGET:
-// every path costs its 2L+1 output rows plus its kNB radial weights.  Greedy
-// in path order; a group holds at least one path.
+// every path costs its 2L+1 output rows (with summed outputs only the first
+// path of each rank in the group) plus its kNB radial weights.  Greedy in
+// path order; a group holds at least one path.
 template <class Cfg, int BUDGET>
 struct PathGroups {
-  static constexpr int cost(int p) { return ncomp(Cfg::paths[p].L) + kNB; }
+  static constexpr int cost(int p, bool shares) { return (shares ? 0 : ncomp(Cfg::paths[p].L)) + kNB; }
   static constexpr std::array<int, Cfg::P + 1> build() {
     std::array<int, Cfg::P + 1> s{};
     int n = 0, used = 0;
     s[0] = 0;
     for (int p = 0; p < Cfg::P; ++p) {
-      if (p > s[n] && used + cost(p) > BUDGET) {
+      const bool shares = Cfg::SUM && p > s[n] && Cfg::paths[p - 1].L == Cfg::paths[p].L;
+      if (p > s[n] && used + cost(p, shares) > BUDGET) {
         s[++n] = p;
         used = 0;
+        used += cost(p, false);
+        continue;
       }
-      used += cost(p);
+      used += cost(p, shares);
     }
     s[++n] = Cfg::P;
     return s;

@@ -63,27 +63,27 @@ void launch_vjp_combine(const ConvArgs& a, const VjpWorkspace& w, int nin, hipSt
 FC_CONV_CONFIGS(FC_CONV_DECL)
 
 #define FC_CONV_CASE(A, B, Cc) \
-  case (A) * 256 + (B) * 16 + (Cc): return conv_run_##A##B##Cc(op, args, stream);
+  case (A) * 1024 + (B) * 32 + (Cc): return conv_run_##A##B##Cc(op, args, stream);
 
 #define FC_CONV_SUPPORTED(A, B, Cc) \
-  case (A) * 256 + (B) * 16 + (Cc): return true;
+  case (A) * 1024 + (B) * 32 + (Cc): return true;
 
 bool conv_supported(int l_in, int l_edge, int l_out) {
-  switch (l_in * 256 + l_edge * 16 + l_out) {
+  switch (l_in * 1024 + l_edge * 32 + l_out) {
     FC_CONV_CONFIGS(FC_CONV_SUPPORTED)
     default: return false;
   }
 }
 
 bool conv_vv_supported(int l_in, int l_edge, int l_out) {
-  switch (l_in * 256 + l_edge * 16 + l_out) {
+  switch (l_in * 1024 + l_edge * 32 + l_out) {
     FC_CONV_VV_CONFIGS(FC_CONV_SUPPORTED)
     default: return false;
   }
 }
 
 bool conv_dispatch(int op, int l_in, int l_edge, int l_out, const ConvArgs& args, hipStream_t stream) {
-  switch (l_in * 256 + l_edge * 16 + l_out) {
+  switch (l_in * 1024 + l_edge * 32 + l_out) {
     FC_CONV_CONFIGS(FC_CONV_CASE)
     default: return false;
   }

@@ -35,8 +35,8 @@ inline constexpr int kCXMax = 20;
 // Per-edge coefficient products of one configuration.
 template <int LIN, int LEDGE, int LOUT>
 struct EdgeProducts {
-  using CYt = tab::CY<LIN, LEDGE, LOUT>;
-  using CXt = tab::CX<LIN, LEDGE, LOUT>;
+  using CYt = tab::CY<LIN, LEDGE, LOUT % kSumPaths>;
+  using CXt = tab::CX<LIN, LEDGE, LOUT % kSumPaths>;
   static constexpr int NE = nrank(LEDGE);
   static constexpr bool kLDS = CYt::n <= kCYMax;
   static constexpr bool kCXReg = CXt::n <= kCXMax;
@@ -195,9 +195,11 @@ __global__ __launch_bounds__(kWave) void conv_fwd_kernel(
     float* zo = z + (size_t)u * NOUT * C + k;
     static_for<G::NP>([&](auto pi) {
       constexpr int p = P0 + pi;
+      if constexpr (!G::owner(p)) return;
       static_for<ncomp(Cfg::paths[p].L)>([&](auto c) {
         constexpr int row = Cfg::row(p, c), li = G::loff(p) + c;
-        zo[(size_t)row * C] = acc[li];
+        if constexpr (G::carry(p)) zo[(size_t)row * C] += acc[li];
+        else zo[(size_t)row * C] = acc[li];
       });
     });
   }
@@ -279,6 +281,7 @@ __global__ __launch_bounds__(kWgWaves * kWave) void conv_wgrad_kernel(
   float gv[G::NR];
   static_for<G::NP>([&](auto pi) {
     constexpr int p = P0 + pi;
+    if constexpr (!G::owner(p)) return;
     static_for<ncomp(Cfg::paths[p].L)>([&](auto c) {
       constexpr int row = Cfg::row(p, c), li = G::loff(p) + c;
       gv[li] = (act && has_u) ? g[((size_t)u * NOUT + row) * C + k] : 0.f;
@@ -511,6 +514,7 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
         float gv[G::NR];
         static_for<G::NP>([&](auto pi) {
           constexpr int p = G::p0 + pi;
+          if constexpr (!G::owner(p)) return;
           static_for<ncomp(Cfg::paths[p].L)>([&](auto c) {
             constexpr int row = Cfg::row(p, c), li = G::loff(p) + c;
             gv[li] = buf_load(gr, voff, ubase + row * C * 4);

@@ -167,9 +167,11 @@ __global__ __launch_bounds__(kWave) void conv_vv_recv_kernel(
     float* zo = g_hat + (size_t)u * NOUT * C + k;
     static_for<G::NP>([&](auto pi) {
       constexpr int p = P0 + pi;
+      if constexpr (!G::owner(p)) return;
       static_for<ncomp(Cfg::paths[p].L)>([&](auto c) {
         constexpr int row = Cfg::row(p, c), li = G::loff(p) + c;
-        zo[(size_t)row * C] = acc[li];
+        if constexpr (G::carry(p)) zo[(size_t)row * C] += acc[li];
+        else zo[(size_t)row * C] = acc[li];
       });
     });
   }
@@ -229,6 +231,7 @@ __global__ __launch_bounds__(kWgWaves * kWave) void conv_wgrad_vv_kernel(
   float gv[G::NR];
   static_for<G::NP>([&](auto pi) {
     constexpr int p = P0 + pi;
+    if constexpr (!G::owner(p)) return;
     static_for<ncomp(Cfg::paths[p].L)>([&](auto c) {
       constexpr int row = Cfg::row(p, c), li = G::loff(p) + c;
       gv[li] = (act && has_u) ? g[((size_t)u * NOUT + row) * C + k] : 0.f;
@@ -469,6 +472,7 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vv_sender_kernel(
         float gv[G::NR];
         static_for<G::NP>([&](auto pi) {
           constexpr int p = G::p0 + pi;
+          if constexpr (!G::owner(p)) return;
           static_for<ncomp(Cfg::paths[p].L)>([&](auto c) {
             constexpr int row = Cfg::row(p, c), li = G::loff(p) + c;
             gv[li] = buf_load(gr, voff, ubase + row * C * 4);

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libflashcart.so")
 FC_OK, FC_ERR_INVALID_ARGUMENT, FC_ERR_UNSUPPORTED, FC_ERR_WORKSPACE, FC_ERR_HIP = range(5)
 FC_LADDER_FULL, FC_LADDER_PATH_REDUCED = 0, 1
 FC_CONV_ALL_PARITIES = 1   # descriptor flag: every triangle-allowed path (odd J too)
+FC_CONV_SUM_PATHS = 2      # descriptor flag: outputs of the paths of each rank summed
 
 
 class FlashCartError(RuntimeError):
@@ -42,6 +43,11 @@ class LadderDesc(ctypes.Structure):
                 ("variant", ctypes.c_int32)]
 
 
+class NormDesc(ctypes.Structure):
+    _fields_ = [("n_nodes", ctypes.c_int32), ("channels", ctypes.c_int32), ("l_max", ctypes.c_int32),
+                ("eps", ctypes.c_float)]
+
+
 _lib = None
 _P = ctypes.c_void_p
 _I = ctypes.c_int32
@@ -49,6 +55,7 @@ _SZ = ctypes.c_size_t
 _PD = ctypes.POINTER(ConvDesc)
 _PL = ctypes.POINTER(LadderDesc)
 _PG = ctypes.POINTER(Graph)
+_PN = ctypes.POINTER(NormDesc)
 _PI = ctypes.POINTER(ctypes.c_int32)
 _PSZ = ctypes.POINTER(ctypes.c_size_t)
 
@@ -72,6 +79,9 @@ _SIGS = {
     "fc_ladder_weight_block": (_I, [_PL, _I, _PSZ, _PI, _PI, _PI]),
     "fc_node_ladder_fwd": (_I, [_PL, _P, _P, _P, _P, _P, _SZ, _P]),
     "fc_node_ladder_vjp": (_I, [_PL, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "fc_rms_norm_fwd": (_I, [_PN, _P, _P, _P, _P, _P]),
+    "fc_rms_norm_workspace_bytes": (_SZ, [_PN]),
+    "fc_rms_norm_vjp": (_I, [_PN, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "fc_block_workspace_bytes": (_SZ, [_PD, _PL]),
     "fc_block_energy_forces": (_I, [_PD, _PG, _P, _P, _P, _P, _PL, _P, ctypes.c_float, _P, _P, _P, _P, _SZ, _P]),
 }
@@ -139,6 +149,10 @@ def _stream(stream):
 
 def conv_desc(n_nodes, n_edges, channels, l_in, l_edge, l_out, r_cut, n_basis=8, flags=0) -> ConvDesc:
     return ConvDesc(n_nodes, n_edges, channels, l_in, l_edge, l_out, n_basis, r_cut, flags)
+
+
+def norm_desc(n_nodes, channels, l_max, eps) -> NormDesc:
+    return NormDesc(n_nodes, channels, l_max, eps)
 
 
 def ladder_desc(n_nodes, channels, l_a, l_prod, l_out, order, variant) -> LadderDesc:
@@ -288,6 +302,23 @@ def fc_node_ladder_vjp(d: LadderDesc, A, weights, saved, g_z, A_grad, weights_gr
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().fc_node_ladder_vjp(ctypes.byref(d), _f32(A), _f32(weights), _f32(saved), _f32(g_z),
                                     _f32(A_grad), _f32(weights_grad), _ptr(workspace), nbytes, _stream(stream)))
+
+
+# -------------------------------------------------------------------- norm --
+
+def fc_rms_norm_fwd(d: NormDesc, x, gamma, y, inv_scale, stream=None):
+    _check(lib().fc_rms_norm_fwd(ctypes.byref(d), _f32(x), _f32(gamma), _f32(y), _f32(inv_scale),
+                                 _stream(stream)))
+
+
+def fc_rms_norm_workspace_bytes(d: NormDesc) -> int:
+    return lib().fc_rms_norm_workspace_bytes(ctypes.byref(d))
+
+
+def fc_rms_norm_vjp(d: NormDesc, x, gamma, inv_scale, g_y, x_grad, gamma_grad, workspace, stream=None):
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().fc_rms_norm_vjp(ctypes.byref(d), _f32(x), _f32(gamma), _f32(inv_scale), _f32(g_y), _f32(x_grad),
+                                 _f32(gamma_grad), _ptr(workspace), nbytes, _stream(stream)))
 
 
 # ------------------------------------------------------------------- block --

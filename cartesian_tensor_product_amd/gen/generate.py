@@ -447,9 +447,12 @@ def emit(path: str, max_rank=MAX_RANK) -> None:
     w("// per configuration (l_in, l_edge, l_out): the distinct products |c| * y[g]")
     w("// (CY, g = l2^2 + b2; y itself first) and |c| * x[g] with |c| != 1")
     w("// (CX, g = l1^2 + b1) its paths use, and for every term the product's index")
+    w("// (a configuration with summed outputs uses the tables of its paths)")
     w("template <int LIN, int LEDGE, int LOUT> struct CY;")
     w("template <int LIN, int LEDGE, int LOUT> struct CX;")
     for cfg in conv_configs():
+        if cfg_summed(cfg):
+            continue
         for name, op in (("CY", 2), ("CX", 1)):
             keys, tidx = product_table(paths, tables, cfg, op)
             w(f"template <> struct {name}<{cfg[0]}, {cfg[1]}, {cfg[2]}> {{")
@@ -468,17 +471,26 @@ def emit(path: str, max_rank=MAX_RANK) -> None:
 # (the microbenchmark grid of the pages), (l_prop, l_e, l_e) with
 # l_prop <= min(l_e, 3), l_e <= 4 (model blocks; the first convolution has
 # scalar senders, later ones propagate rank l_prop), and equal ranks 1..4 with
-# every triangle-allowed path (odd J included), keyed by l_out + ALL_PARITIES.
+# every triangle-allowed path (odd J included), keyed by l_out + ALL_PARITIES,
+# and equal ranks 1..4 with path-summed outputs, keyed by l_out + SUM_PATHS.
 # The VJP-of-VJP is instantiated up to rank 4 (natural parity) and 3 (every
-# path); beyond, its path groups would need about 20 sweeps per sender.
+# path, or summed outputs); beyond, its path groups would need about 20
+# sweeps per sender.
 ALL_PARITIES = 8
+SUM_PATHS = 16
 VV_MAX_RANK = 4
 VV_MAX_RANK_ALL = 3
+VV_MAX_RANK_SUM = 3
+SUM_MAX_RANK = 4
 
 
 def cfg_ranks(cfg):
     """(l_in, l_edge, l_out, all parities) of a configuration key."""
-    return cfg[0], cfg[1], cfg[2] % ALL_PARITIES, cfg[2] >= ALL_PARITIES
+    return cfg[0], cfg[1], cfg[2] % ALL_PARITIES, (cfg[2] // ALL_PARITIES) % 2 == 1
+
+
+def cfg_summed(cfg) -> bool:
+    return cfg[2] >= SUM_PATHS
 
 
 def conv_configs():
@@ -488,11 +500,14 @@ def conv_configs():
             if lp <= le and (lp, le, le) not in out:
                 out.append((lp, le, le))
     out += [(L, L, L + ALL_PARITIES) for L in range(1, ODD_MAX_RANK + 1)]
+    out += [(L, L, L + SUM_PATHS) for L in range(1, SUM_MAX_RANK + 1)]
     return out
 
 
 def has_vv(cfg) -> bool:
     li, le, lo, allp = cfg_ranks(cfg)
+    if cfg_summed(cfg):
+        return max(li, le, lo) <= VV_MAX_RANK_SUM
     return max(li, le, lo) <= (VV_MAX_RANK_ALL if allp else VV_MAX_RANK)
 
 

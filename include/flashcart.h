@@ -87,14 +87,21 @@ int32_t fc_abi_version(void);
  * 0 <= l_in, l_edge, l_out <= 5 with at least one admissible path and the
  * rank set instantiated in the build: equal ranks 0..5, and (l_prop, l_e, l_e)
  * with l_prop <= min(l_e, 3), l_e <= 4 (FC_ERR_UNSUPPORTED otherwise);
- * n_basis == 8, r_cut > 0, flags == 0 (natural parity: even l1+l2+L, the
- * pages' method) or FC_CONV_ALL_PARITIES (every triangle-allowed path: the
- * odd-J couplings are STF_L(Sym_L(E)) with one index of each operand
- * contracted through the Levi-Civita symbol, constant 1, so (1,1)->1 is the
- * cross product x × y; instantiated for equal ranks 1..4, the VJP-of-VJP
- * for 1..3).  Paths are kept separate either way.
+ * n_basis == 8, r_cut > 0.  flags:
+ *   0: natural parity (even l1+l2+L, the pages' method), paths separate;
+ *   FC_CONV_ALL_PARITIES: every triangle-allowed path (the odd-J couplings
+ *     are STF_L(Sym_L(E)) with one index of each operand contracted through
+ *     the Levi-Civita symbol, constant 1, so (1,1)->1 is the cross product
+ *     x × y); instantiated for equal ranks 1..4, the VJP-of-VJP for 1..3;
+ *   FC_CONV_SUM_PATHS: the outputs of all paths with the same output rank L
+ *     are summed into one block of 2L+1 rows (App. D, "Executing Cartesian
+ *     tensor products": the kernel option of summing path outputs; weights
+ *     stay per path, and the cotangents g_z / g_hat use the same rows);
+ *     natural parity, instantiated for equal ranks 1..4, the VJP-of-VJP
+ *     for 1..3.
  * ---------------------------------------------------------------------- */
 #define FC_CONV_ALL_PARITIES 1u
+#define FC_CONV_SUM_PATHS 2u
 
 typedef struct {
   int32_t n_nodes, n_edges, channels;
@@ -114,7 +121,10 @@ typedef struct {
 
 /* Number of paths and row counts (in units of C floats) of x and z.
  * Implements the path enumeration of §2 "Irreducible Cartesian tensors"
- * (admissible = triangle + even J).  Host only. */
+ * (admissible = triangle + even J).  out_rows is sum_L (2L+1) P_L with paths
+ * separate, and the sum of 2L+1 over the ranks L that have a path with
+ * FC_CONV_SUM_PATHS: block L starts after the blocks of the lower ranks.
+ * Host only. */
 fc_status fc_conv_layout(const fc_conv_desc* d, int32_t* n_paths, int32_t* in_rows,
                          int32_t* out_rows);
 /* The i-th path (l1, l2, L) in storage order.  Host only. */
@@ -270,6 +280,38 @@ fc_status fc_block_energy_forces(const fc_conv_desc* conv, const fc_graph* g, co
                                  const fc_ladder_desc* lad, const float* ladder_w, float conv_scale,
                                  double* energy, float* e_atom, float* forces, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Equivariant RMS normalisation of node features (App. E "Model
+ * architecture": scalar invariants from the generated (l,l)->0 couplings,
+ * combined over ranks and channels into one scale per atom, no batch
+ * statistics).  The combination is read as the root mean square:
+ *   q[u,l,k] = f_(l,l)->0(x[u,l,k], x[u,l,k]),
+ *   s[u] = sqrt(sum_{l,k} q[u,l,k] / ((l_max+1) C) + eps),
+ *   y[u,l,k] = gamma[l,k] x[u,l,k] / s[u].
+ * x, y [N][(l_max+1)^2][C] (ranks 0..l_max, stored components);
+ * gamma [l_max+1][C] or NULL (all ones); inv_scale [N] = 1/s (written by
+ * the forward when non-NULL, read by the VJP).  Constraints: n_nodes >= 1,
+ * 1 <= channels <= 512, 0 <= l_max <= 5, eps >= 0 and finite (with eps = 0
+ * a node of zeros gives non-finite outputs).
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t n_nodes, channels, l_max;
+  float eps;
+} fc_norm_desc;
+
+fc_status fc_rms_norm_fwd(const fc_norm_desc* d, const float* x, const float* gamma, float* y,
+                          float* inv_scale, hipStream_t stream);
+
+/* VJP of L = <g_y, y> at the forward's inv_scale: x_grad [N][rows][C] and
+ * gamma_grad [l_max+1][C] (summed over nodes in a fixed order), each when
+ * non-NULL (at least one).  gamma_grad needs a workspace of
+ * fc_rms_norm_workspace_bytes(d) bytes. */
+size_t fc_rms_norm_workspace_bytes(const fc_norm_desc* d);
+fc_status fc_rms_norm_vjp(const fc_norm_desc* d, const float* x, const float* gamma,
+                          const float* inv_scale, const float* g_y, float* x_grad,
+                          float* gamma_grad, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -53,6 +53,17 @@ def test_layout_and_path_order_match_oracle(ranks, allp):
         fc.fc_conv_path(d, P)
 
 
+@pytest.mark.parametrize("ranks", [(1, 1, 1), (2, 2, 2), (3, 3, 3), (4, 4, 4)])
+def test_summed_layout_matches_oracle(ranks):
+    """FC_CONV_SUM_PATHS: one 2L+1-row block per output rank; the path order
+    (the order of the radial weights) is that of the separate layout."""
+    spec = conv.ConvSpec(*ranks, 5.0, sum_paths=True)
+    d = fc.conv_desc(10, 20, 16, *ranks, 5.0, flags=fc.FC_CONV_SUM_PATHS)
+    P, nin, nout = fc.fc_conv_layout(d)
+    assert (P, nin, nout) == (spec.n_paths, spec.n_in, spec.n_out) == (P, nin, (ranks[2] + 1) ** 2)
+    assert [fc.fc_conv_path(d, i) for i in range(P)] == spec.paths
+
+
 @pytest.mark.parametrize("bad,status", [
     (dict(n_nodes=0), fc.FC_ERR_INVALID_ARGUMENT),
     (dict(n_edges=-1), fc.FC_ERR_INVALID_ARGUMENT),
@@ -64,8 +75,10 @@ def test_layout_and_path_order_match_oracle(ranks, allp):
     (dict(n_basis=6), fc.FC_ERR_UNSUPPORTED),
     (dict(r_cut=0.0), fc.FC_ERR_INVALID_ARGUMENT),
     (dict(r_cut=float("inf")), fc.FC_ERR_INVALID_ARGUMENT),
-    (dict(flags=2), fc.FC_ERR_UNSUPPORTED),
+    (dict(flags=4), fc.FC_ERR_UNSUPPORTED),
     (dict(flags=1, l_in=0, l_edge=2, l_out=2), fc.FC_ERR_UNSUPPORTED),   # not instantiated
+    (dict(flags=2, l_in=0, l_edge=2, l_out=2), fc.FC_ERR_UNSUPPORTED),   # not instantiated
+    (dict(flags=3), fc.FC_ERR_UNSUPPORTED),                             # summed + all parities
 ])
 def test_descriptor_errors(bad, status):
     kw = dict(n_nodes=4, n_edges=8, channels=8, l_in=1, l_edge=1, l_out=1, r_cut=5.0, n_basis=8, flags=0)
@@ -114,3 +127,30 @@ def test_vjp_vjp_workspace_holds_weight_cotangent_terms():
     w1 = fc.fc_edge_conv_workspace_bytes(d, 1)
     w2 = fc.fc_edge_conv_workspace_bytes(d, 2)
     assert w2 >= w1 + 4 * 1024 * 128 * (nout + nin) + 4 * 1024 * 3
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(n_nodes=0), fc.FC_ERR_INVALID_ARGUMENT),
+    (dict(channels=0), fc.FC_ERR_INVALID_ARGUMENT),
+    (dict(channels=513), fc.FC_ERR_UNSUPPORTED),
+    (dict(l_max=-1), fc.FC_ERR_INVALID_ARGUMENT),
+    (dict(l_max=6), fc.FC_ERR_UNSUPPORTED),
+    (dict(eps=-1.0), fc.FC_ERR_INVALID_ARGUMENT),
+    (dict(eps=float("nan")), fc.FC_ERR_INVALID_ARGUMENT),
+])
+def test_norm_descriptor_errors(bad, status):
+    """The RMS norm rejects bad descriptors on the host (no GPU call)."""
+    kw = dict(n_nodes=4, channels=8, l_max=2, eps=1e-5)
+    kw.update(bad)
+    d = fc.norm_desc(**kw)
+    assert fc.fc_rms_norm_workspace_bytes(d) == 0
+    with pytest.raises(fc.FlashCartError) as ei:
+        fc.fc_rms_norm_fwd(d, None, None, None, None, stream=0)
+    assert ei.value.status == status
+
+
+def test_norm_workspace_size():
+    d = fc.norm_desc(4096, 128, 3, 1e-5)
+    assert fc.fc_rms_norm_workspace_bytes(d) == 1024 * 4 * 128 * 4
+    d = fc.norm_desc(10, 16, 1, 0.0)
+    assert fc.fc_rms_norm_workspace_bytes(d) == 3 * 2 * 16 * 4

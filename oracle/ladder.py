@@ -13,6 +13,8 @@ acts on every node independently).  Follows the FlashCart paper:
   z[L] = W_L (sum_q phi^q[L]) for L <= l_out.
 * VJP: the reverse of both recurrences by hand (transposed matmuls and the
   transposed bilinear forms of Eq. C1), giving dA and every weight gradient.
+* VJP-of-VJP: the complex-step derivative of the forward and of the VJP
+  along the cotangents (v_A, v_W) of (dA, weight gradients).
 
 Paths of step q: admissible (l1, l2, L) with l1 <= l_{q-1}, l2 <= l_a and
 L <= l_q, ordered by L and then (l1, l2) lexicographically; phi^1 keeps ranks
@@ -167,16 +169,17 @@ def ladder_vjp(spec: LadderSpec, A, ws, gz, nodes=None, chunk: int = 256):
     """(A_bar, [weight grads in flat order]) of L = <g_z, z>."""
     w = _weights(spec, ws)
     names = [s[0] for s in spec.weight_shapes()]
-    wb = {k: np.zeros(np.shape(v), dtype=np.result_type(A.dtype, gz.dtype, np.float64)) for k, v in w.items()}
+    dt = np.result_type(A.dtype, gz.dtype, np.float64, *[np.asarray(v).dtype for v in ws])
+    wb = {k: np.zeros(np.shape(v), dtype=dt) for k, v in w.items()}
     idx = np.arange(A.shape[0]) if nodes is None else np.asarray(nodes)
-    A_bar = np.zeros((len(idx),) + A.shape[1:], dtype=np.result_type(A.dtype, gz.dtype, np.float64))
+    A_bar = np.zeros((len(idx),) + A.shape[1:], dtype=dt)
     C = spec.C
     for i0 in range(0, len(idx), chunk):
         sel = idx[i0:i0 + chunk]
         Ac = _f64(A[sel])
         gc = _f64(gz[sel])
         z, phis, acc = _forward_chunk(spec, Ac, w, keep=True)
-        Ab = np.zeros_like(Ac)
+        Ab = np.zeros(Ac.shape, dtype=dt)
         # gradient of the output sum
         S_bar = {}
         for L in range(spec.l_out + 1):
@@ -230,3 +233,24 @@ def ladder_vjp(spec: LadderSpec, A, ws, gz, nodes=None, chunk: int = 256):
                 wb["a1"][l] += np.einsum('uck,uck->k', G, Al)
         A_bar[i0:i0 + len(sel)] = Ab
     return A_bar, [wb[k] for k in names]
+
+
+CSTEP = 1e-20
+
+
+def ladder_vjp_vjp(spec: LadderSpec, A, ws, gz, v_A=None, v_ws=None, nodes=None, chunk: int = 256):
+    """(g_hat, A_hat, [W_hat in flat order]) for the second-order term of
+    App. C Eq. C2 applied to the ladder: s = <v_A, A_bar> + sum <v_W, W_bar>.
+
+    s is the derivative of <g_z, z> along (v_A, v_W), so g_hat = dz/d eps
+    and (A_hat, W_hat) = d (A_bar, W_bar) / d eps at (A + eps v_A,
+    W + eps v_W), by complex step (exact to rounding for h = 1e-20).  A
+    missing cotangent is zero.
+    """
+    h = CSTEP
+    Ac = A.astype(np.complex128) + (0 if v_A is None else 1j * h * v_A)
+    wc = [np.asarray(w, dtype=np.complex128) + (0 if v_ws is None else 1j * h * v)
+          for w, v in zip(ws, v_ws if v_ws is not None else [None] * len(ws))]
+    g_hat = ladder_fwd(spec, Ac, wc, nodes=nodes, chunk=chunk).imag / h
+    Ab, Wb = ladder_vjp(spec, Ac, wc, gz, nodes=nodes, chunk=chunk)
+    return g_hat, Ab.imag / h, [b.imag / h for b in Wb]

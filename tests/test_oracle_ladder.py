@@ -128,3 +128,34 @@ def test_ladder_step_paths():
     spec = ladder.LadderSpec(3, 3, 0, 5, "reduced", 8)
     assert len(spec.paths[2]) == 23 and spec.lq[5] == 0
     assert [p for p in spec.paths[5]] == [(l, l, 0) for l in range(4)]
+
+
+@pytest.mark.parametrize("variant,l_out,order", [("full", 3, 4), ("reduced", 3, 4), ("full", 1, 3), ("full", 2, 1)])
+def test_ladder_vjp_vjp_fd_and_symmetry(variant, l_out, order):
+    """The ladder's VJP-of-VJP against central differences of its VJP and
+    forward along (v_A, v_W), and the symmetry of the Hessian of <g, z> over
+    (A, W) (both directions, both cotangents)."""
+    spec, A, ws, gz = make(3, 3, l_out, order, variant, 3, N=4, seed=11)
+    rng = np.random.default_rng(12)
+    vA = rng.standard_normal(A.shape)
+    vw = [rng.standard_normal(w.shape) for w in ws]
+    gh, Ah, Wh = ladder.ladder_vjp_vjp(spec, A, ws, gz, v_A=vA, v_ws=vw)
+    h = 1e-5
+    shift = lambda sg: (A + sg * h * vA, [w + sg * h * v for w, v in zip(ws, vw)])
+    (Ap, wp), (Am, wm) = shift(1), shift(-1)
+    zd = (ladder.ladder_fwd(spec, Ap, wp) - ladder.ladder_fwd(spec, Am, wm)) / (2 * h)
+    assert np.abs(gh - zd).max() < 1e-7 * max(1.0, np.abs(gh).max())
+    bp, bm = ladder.ladder_vjp(spec, Ap, wp, gz), ladder.ladder_vjp(spec, Am, wm, gz)
+    assert np.abs(Ah - (bp[0] - bm[0]) / (2 * h)).max() < 1e-7 * max(1.0, np.abs(Ah).max())
+    for got, a, b in zip(Wh, bp[1], bm[1]):
+        assert np.abs(got - (a - b) / (2 * h)).max() < 1e-7 * max(1.0, np.abs(got).max())
+    uA = rng.standard_normal(A.shape)
+    uw = [rng.standard_normal(w.shape) for w in ws]
+    _, Ah2, Wh2 = ladder.ladder_vjp_vjp(spec, A, ws, gz, v_A=uA, v_ws=uw)
+    lhs = np.sum(uA * Ah) + sum(np.sum(u * x) for u, x in zip(uw, Wh))
+    rhs = np.sum(vA * Ah2) + sum(np.sum(v * x) for v, x in zip(vw, Wh2))
+    assert lhs == pytest.approx(rhs, rel=1e-10)
+    # one cotangent at a time adds up to both (linearity in the direction)
+    g1, A1, W1 = ladder.ladder_vjp_vjp(spec, A, ws, gz, v_A=vA)
+    g2, A2, W2 = ladder.ladder_vjp_vjp(spec, A, ws, gz, v_ws=vw)
+    assert np.allclose(g1 + g2, gh, atol=1e-12) and np.allclose(A1 + A2, Ah, atol=1e-12)

@@ -461,6 +461,7 @@ fc_status fc_ladder_weight_block(const fc_ladder_desc* d, int32_t i, size_t* off
 size_t fc_ladder_workspace_bytes(const fc_ladder_desc* d, int32_t op) {
   fc::LadderPlan p;
   if (ladder_plan(d, &p) != FC_OK) return 0;
+  if (op == 2) return p.variant == FC_LADDER_FULL ? sizeof(float) * p.vv_ws_floats() : 0;
   return sizeof(float) * (op == 1 ? p.vjp_ws_floats() : p.fwd_ws_floats());
 }
 
@@ -495,6 +496,31 @@ fc_status fc_node_ladder_vjp(const fc_ladder_desc* d, const float* A, const floa
     return fail(FC_ERR_WORKSPACE, "ladder VJP needs %zu workspace bytes", need);
   fc::ladder_vjp(p, A, weights, saved, g_z, A_grad, weights_grad, static_cast<float*>(workspace), stream);
   return check_launch("ladder VJP");
+}
+
+fc_status fc_node_ladder_vjp_vjp(const fc_ladder_desc* d, const float* A, const float* weights, const float* saved,
+                                 const float* g_z, const float* v_A, const float* v_weights, float* g_hat,
+                                 float* A_hat, float* weights_hat, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  fc::LadderPlan p;
+  if (fc_status s = ladder_plan(d, &p)) return s;
+  if (p.variant != FC_LADDER_FULL)
+    return fail(FC_ERR_UNSUPPORTED, "ladder VJP-of-VJP is implemented for the full ladder only");
+  if (!g_hat && !A_hat && !weights_hat) return fail(FC_ERR_INVALID_ARGUMENT, "ladder VJP-of-VJP: no output requested");
+  if (!A || !weights || ((A_hat || weights_hat) && !g_z))
+    return fail(FC_ERR_INVALID_ARGUMENT, "ladder VJP-of-VJP: NULL A, weights or g_z");
+  if (p.order > 1 && !saved)
+    return fail(FC_ERR_INVALID_ARGUMENT, "ladder VJP-of-VJP: saved states required (order > 1)");
+  if (misaligned(A, 4) || misaligned(weights, 4) || misaligned(saved, 4) || misaligned(g_z, 4) ||
+      misaligned(v_A, 4) || misaligned(v_weights, 4) || misaligned(g_hat, 4) || misaligned(A_hat, 4) ||
+      misaligned(weights_hat, 4) || misaligned(workspace, 4))
+    return fail(FC_ERR_INVALID_ARGUMENT, "ladder VJP-of-VJP: arrays must be 4-byte aligned");
+  const size_t need = fc_ladder_workspace_bytes(d, 2);
+  if (!workspace || workspace_bytes < need)
+    return fail(FC_ERR_WORKSPACE, "ladder VJP-of-VJP needs %zu workspace bytes", need);
+  fc::ladder_vjp_vjp(p, A, weights, saved, g_z, v_A, v_weights, g_hat, A_hat, weights_hat,
+                     static_cast<float*>(workspace), stream);
+  return check_launch("ladder VJP-of-VJP");
 }
 
 }  // extern "C"

@@ -31,11 +31,13 @@ constexpr int kRedWaves = 4;   // waves per block of the path-reduced reverse ke
 
 // One step of the full ladder: B rows for all paths of ConvCfg<LP, LA, LQ>.
 // phi [N][phi_rows][C], A [N][a_rows][C]; B block of rank L starts at
-// N * off(L) * C floats, row (u (2L+1) + a), column (eta_L C + k).
+// N * off(L) * C floats, row (u (2L+1) + a), column (eta_L C + k).  With
+// acc the products are added to B (a tangent B' = prod(phi', A) +
+// prod(phi, A') takes two launches).
 template <int LP, int LA, int LQ>
 __global__ __launch_bounds__(kWave) void ladder_prod_kernel(int N, int C, const float* __restrict__ phi,
                                                             int phi_rows, const float* __restrict__ A,
-                                                            int a_rows, float* __restrict__ B) {
+                                                            int a_rows, float* __restrict__ B, int acc) {
   using Cfg = ConvCfg<LP, LA, LQ>;
   const int u = blockIdx.x;
   const int k = blockIdx.y * kWave + threadIdx.x;
@@ -57,7 +59,10 @@ __global__ __launch_bounds__(kWave) void ladder_prod_kernel(int N, int C, const 
     });
     float* dst = B + (size_t)N * PI.off * C + (size_t)PI.eta * C + k;
     const size_t ld = (size_t)PI.PL * C;
-    static_for<na>([&](auto a) { dst[((size_t)u * na + a) * ld] = t[a]; });
+    static_for<na>([&](auto a) {
+      float* d = dst + ((size_t)u * na + a) * ld;
+      *d = acc ? *d + t[a] : t[a];
+    });
   });
 }
 
@@ -137,13 +142,14 @@ __global__ __launch_bounds__(kWave) void ladder_reduced_kernel(int N, int C, int
 
 // Full ladder, reverse of one product step: given Bbar (layout of B),
 // phi^{q-1} and A, write G^{q-1} = g_z (ranks <= l_out) + sum_eta VJP1 and
-// add sum_eta VJP2 into A_bar.
+// add sum_eta VJP2 into A_bar.  acc_g adds to G^{q-1} instead (g_z unused);
+// A == nullptr drops the VJP1 term, Abar == nullptr the VJP2 term.
 template <int LP, int LA, int LQ>
 __global__ __launch_bounds__(kWave) void ladder_prod_vjp_kernel(int N, int C, const float* __restrict__ Bbar,
                                                                 const float* __restrict__ phi,
                                                                 const float* __restrict__ A,
                                                                 const float* __restrict__ gz, int gz_rows,
-                                                                float* __restrict__ Gprev,
+                                                                float* __restrict__ Gprev, int acc_g,
                                                                 float* __restrict__ Abar) {
   using Cfg = ConvCfg<LP, LA, LQ>;
   constexpr int NP = nrank(LP), NA = nrank(LA);
@@ -153,10 +159,11 @@ __global__ __launch_bounds__(kWave) void ladder_prod_vjp_kernel(int N, int C, co
   float x[NP], y[NA], gp[NP], ab[NA];
   static_for<NP>([&](auto c) {
     x[c] = phi[((size_t)u * NP + c) * C + k];
-    gp[c] = c < gz_rows ? gz[((size_t)u * gz_rows + c) * C + k] : 0.f;
+    gp[c] = acc_g ? Gprev[((size_t)u * NP + c) * C + k]
+                  : (c < gz_rows ? gz[((size_t)u * gz_rows + c) * C + k] : 0.f);
   });
   static_for<NA>([&](auto c) {
-    y[c] = A[((size_t)u * NA + c) * C + k];
+    y[c] = A ? A[((size_t)u * NA + c) * C + k] : 0.f;
     ab[c] = 0.f;
   });
   static_for<Cfg::P>([&](auto pc) {
@@ -176,7 +183,7 @@ __global__ __launch_bounds__(kWave) void ladder_prod_vjp_kernel(int N, int C, co
     });
   });
   static_for<NP>([&](auto c) { Gprev[((size_t)u * NP + c) * C + k] = gp[c]; });
-  static_for<NA>([&](auto c) { Abar[((size_t)u * NA + c) * C + k] += ab[c]; });
+  if (Abar) static_for<NA>([&](auto c) { Abar[((size_t)u * NA + c) * C + k] += ab[c]; });
 }
 
 // Path-reduced ladder, reverse of step q for a tile of nodes: G = dL/dphi^q
@@ -396,6 +403,27 @@ size_t LadderPlan::vjp_ws_floats() const {
   return 2 * (size_t)N * nr(lout) * C + 2 * st + (size_t)nblk * (pmax + lprod + 1) * C + part;
 }
 
+// B, B', B_bar, B_bar' (largest step), G and G' double buffers, phi'^q for
+// q < order, split-K partials of the weight gradients
+size_t LadderPlan::vv_ws_floats() const {
+  const size_t st = state_floats();
+  const size_t C2 = (size_t)C * C;
+  size_t b = 0, part = 0;
+  for (int q = 2; q <= order; ++q) {
+    b = std::max(b, (size_t)N * prod_rows(q) * C);
+    size_t g = 0;
+    for (int L = 0; L <= lq(q); ++L) {
+      const int P = paths(q, L);
+      if (P) g += (size_t)gemm_ksplit(C, P * C, N * (2 * L + 1), kSplitTarget) * P * C2;
+    }
+    part = std::max(part, g);
+  }
+  size_t g1 = 0;
+  for (int l = 0; l <= lq(1); ++l) g1 += (size_t)gemm_ksplit(C, C, N * (2 * l + 1), kSplitTarget) * C2;
+  part = std::max(part, g1);
+  return 4 * b + 4 * st + (size_t)(order - 1) * st + part;
+}
+
 // offset (floats) of W^q_L (full) in the flat weights
 size_t LadderPlan::w_full(int q, int L) const {
   const size_t C2 = (size_t)C * C;
@@ -424,29 +452,30 @@ size_t LadderPlan::w_final(int L) const {
 namespace {
 
 template <int LP, int LQ>
-void launch_prod(const LadderPlan& p, const float* phi, const float* A, float* B, hipStream_t st) {
+void launch_prod(const LadderPlan& p, const float* phi, const float* A, float* B, int acc, hipStream_t st) {
   dim3 grid(p.N, (p.C + kWave - 1) / kWave);
   hipLaunchKernelGGL((ladder_prod_kernel<LP, LP, LQ>), grid, dim3(kWave), 0, st, p.N, p.C, phi, nr(p.lprod), A,
-                     nr(p.la), B);
+                     nr(p.la), B, acc);
 }
 
 template <int LP>
-void dispatch_prod(const LadderPlan& p, int LQ, const float* phi, const float* A, float* B, hipStream_t st) {
+void dispatch_prod(const LadderPlan& p, int LQ, const float* phi, const float* A, float* B, int acc,
+                   hipStream_t st) {
   switch (LQ) {
-    case 0: launch_prod<LP, 0>(p, phi, A, B, st); break;
-    case 1: if constexpr (LP >= 1) launch_prod<LP, 1>(p, phi, A, B, st); break;
-    case 2: if constexpr (LP >= 2) launch_prod<LP, 2>(p, phi, A, B, st); break;
-    case 3: if constexpr (LP >= 3) launch_prod<LP, 3>(p, phi, A, B, st); break;
-    case 4: if constexpr (LP >= 4) launch_prod<LP, 4>(p, phi, A, B, st); break;
+    case 0: launch_prod<LP, 0>(p, phi, A, B, acc, st); break;
+    case 1: if constexpr (LP >= 1) launch_prod<LP, 1>(p, phi, A, B, acc, st); break;
+    case 2: if constexpr (LP >= 2) launch_prod<LP, 2>(p, phi, A, B, acc, st); break;
+    case 3: if constexpr (LP >= 3) launch_prod<LP, 3>(p, phi, A, B, acc, st); break;
+    case 4: if constexpr (LP >= 4) launch_prod<LP, 4>(p, phi, A, B, acc, st); break;
   }
 }
 
-void prod(const LadderPlan& p, int LQ, const float* phi, const float* A, float* B, hipStream_t st) {
+void prod(const LadderPlan& p, int LQ, const float* phi, const float* A, float* B, hipStream_t st, int acc = 0) {
   switch (p.lprod) {
-    case 1: dispatch_prod<1>(p, LQ, phi, A, B, st); break;
-    case 2: dispatch_prod<2>(p, LQ, phi, A, B, st); break;
-    case 3: dispatch_prod<3>(p, LQ, phi, A, B, st); break;
-    case 4: dispatch_prod<4>(p, LQ, phi, A, B, st); break;
+    case 1: dispatch_prod<1>(p, LQ, phi, A, B, acc, st); break;
+    case 2: dispatch_prod<2>(p, LQ, phi, A, B, acc, st); break;
+    case 3: dispatch_prod<3>(p, LQ, phi, A, B, acc, st); break;
+    case 4: dispatch_prod<4>(p, LQ, phi, A, B, acc, st); break;
   }
 }
 
@@ -566,10 +595,10 @@ namespace {
 
 template <int LP, int LQ>
 void launch_prod_vjp(const LadderPlan& p, const float* Bbar, const float* phi, const float* A, const float* gz,
-                     float* Gprev, float* Abar, hipStream_t st) {
+                     float* Gprev, float* Abar, hipStream_t st, int acc_g = 0) {
   dim3 grid(p.N, (p.C + kWave - 1) / kWave);
   hipLaunchKernelGGL((ladder_prod_vjp_kernel<LP, LP, LQ>), grid, dim3(kWave), 0, st, p.N, p.C, Bbar, phi, A, gz,
-                     nr(p.lout), Gprev, Abar);
+                     gz ? nr(p.lout) : 0, Gprev, acc_g, Abar);
 }
 
 template <int LP, int LQ>
@@ -784,6 +813,221 @@ void ladder_vjp(const LadderPlan& p, const float* A, const float* w, const float
     }
     G = Gprev;
     grows = rp;
+  }
+}
+
+// Full ladder, VJP-of-VJP by forward-over-reverse: every map of the ladder is
+// linear in each operand, so the tangent of a product step is two product
+// launches (prod(phi', A) + prod(phi, v_A)), the tangent of a GEMM two GEMMs
+// (X' W + X V), and the tangent of a reverse product step two reverse
+// launches (G' from VJP1(B_bar', A) + VJP1(B_bar, v_A), A_hat from
+// VJP2(B_bar', phi) + VJP2(B_bar, phi')).  The forward tangent gives
+// g_hat = z' and phi'^q; the reverse sweep recomputes G^q = dL/dphi^q beside
+// its tangent G'^q, and A_hat and w_hat collect the tangents of A_bar and
+// w_bar (zero-filled, then accumulated: the GEMM groups that add to the same
+// output run one after another).
+void ladder_vjp_vjp(const LadderPlan& p, const float* A, const float* w, const float* saved, const float* gz,
+                    const float* vA, const float* vw, float* g_hat, float* A_hat, float* w_hat, float* ws,
+                    hipStream_t st) {
+  const int C = p.C;
+  const int ra = nr(p.la), rp = nr(p.lprod), ro = nr(p.lout);
+  const size_t stf = p.state_floats();
+  size_t bmax = 0;
+  for (int q = 2; q <= p.order; ++q) bmax = std::max(bmax, (size_t)p.N * p.prod_rows(q) * C);
+  float* B = ws;
+  float* dB = B + bmax;
+  float* Bb = dB + bmax;
+  float* dBb = Bb + bmax;
+  float* Gb[2] = {dBb + bmax, dBb + bmax + stf};
+  float* dGb[2] = {Gb[1] + stf, Gb[1] + 2 * stf};
+  float* dphi = dGb[1] + stf;
+  float* part = dphi + (size_t)(p.order - 1) * stf;
+  auto phi_of = [&](int q) -> const float* { return saved + (size_t)(q - 1) * stf; };
+  auto dphi_of = [&](int q) -> float* { return q < p.order ? dphi + (size_t)(q - 1) * stf : nullptr; };
+  const bool rev = A_hat || w_hat;
+  if (A_hat) fill_zero(A_hat, (size_t)p.N * ra * C, st);
+  if (w_hat) fill_zero(w_hat, p.weight_floats(), st);
+  if (!vA && !vw) {   // zero cotangents
+    if (g_hat) fill_zero(g_hat, (size_t)p.N * ro * C, st);
+    return;
+  }
+
+  // ---- forward tangent: phi'^1 = W1 v_A + V1 A, phi'^q = W^q B' + V^q B
+  {
+    for (int pass = 0; pass < 2; ++pass) {
+      const float* X = pass == 0 ? vA : A;
+      const float* Wt = pass == 0 ? w : vw;
+      if (!X || !Wt) continue;
+      const int acc = (pass == 1 && vA) ? 1 : 0;
+      GemmGroup g{};
+      for (int L = 0; L <= p.lq(1); ++L) {
+        GemmProblem& pr = g.prob[g.count++];
+        pr.M = p.N * (2 * L + 1);
+        pr.N = C;
+        pr.K = C;
+        pr.alpha = 1.f;
+        pr.A = node_view(X, ra, L, C);
+        pr.Bt = plain_view(Wt + p.w_full(1, L), C);
+        pr.C = node_out(dphi_of(1), rp, L, C, acc);
+        pr.C2 = L <= p.lout ? node_out(g_hat, ro, L, C, acc) : no_out();
+      }
+      gemm_group(g, st);
+    }
+  }
+  for (int q = 2; q <= p.order; ++q) {
+    float* out = dphi_of(q);
+    if (!out && !g_hat) break;
+    const float* phi = phi_of(q - 1);
+    prod(p, p.lq(q), dphi_of(q - 1), A, dB, st, 0);
+    if (vA) prod(p, p.lq(q), phi, vA, dB, st, 1);
+    if (vw) prod(p, p.lq(q), phi, A, B, st, 0);
+    for (int pass = 0; pass < 2; ++pass) {
+      if (pass == 1 && !vw) continue;
+      const float* X = pass == 0 ? dB : B;
+      const float* Wt = pass == 0 ? w : vw;
+      GemmGroup g{};
+      size_t boff = 0;
+      for (int L = 0; L <= p.lq(q); ++L) {
+        const int P = p.paths(q, L);
+        if (P == 0) continue;
+        GemmProblem& pr = g.prob[g.count++];
+        pr.M = p.N * (2 * L + 1);
+        pr.N = C;
+        pr.K = P * C;
+        pr.alpha = 1.f;
+        pr.A = plain_view(X + boff, (long long)P * C);
+        pr.Bt = plain_view(Wt + p.w_full(q, L), (long long)P * C);
+        pr.C = node_out(out, rp, L, C, pass);
+        pr.C2 = L <= p.lout ? node_out(g_hat, ro, L, C, 1) : no_out();
+        boff += (size_t)p.N * (2 * L + 1) * P * C;
+      }
+      gemm_group(g, st);
+    }
+  }
+  if (!rev) return;
+
+  // ---- reverse sweep with tangents
+  const float* G = gz;
+  const float* dG = nullptr;
+  int grows = ro;
+  for (int q = p.order; q >= 2; --q) {
+    const float* phi = phi_of(q - 1);
+    const float* dph = dphi_of(q - 1);
+    prod(p, p.lq(q), phi, A, B, st, 0);
+    prod(p, p.lq(q), dph, A, dB, st, 0);
+    if (vA) prod(p, p.lq(q), phi, vA, dB, st, 1);
+    const bool have_dBb = dG || vw;
+    // B_bar = G W, B_bar' = G' W (+ G V below)
+    {
+      GemmGroup g{};
+      size_t boff = 0;
+      for (int L = 0; L <= p.lq(q); ++L) {
+        const int P = p.paths(q, L);
+        if (P == 0) continue;
+        const long long PC = (long long)P * C;
+        for (int t = 0; t < 2; ++t) {
+          const float* X = t == 0 ? G : dG;
+          if (!X) continue;
+          GemmProblem& b = g.prob[g.count++];
+          b.M = p.N * (2 * L + 1);
+          b.N = (int)PC;
+          b.K = C;
+          b.alpha = 1.f;
+          b.A = node_view(X, grows, L, C);
+          b.Bt = weight_t(w + p.w_full(q, L), PC);
+          b.C = plain_out((t == 0 ? Bb : dBb) + boff, PC, 0);
+          b.C2 = no_out();
+        }
+        boff += (size_t)p.N * (2 * L + 1) * PC;
+      }
+      gemm_group(g, st);
+    }
+    // B_bar' += G V;  w_hat^q += G^T B'  (then += G'^T B)
+    for (int pass = 0; pass < 2; ++pass) {
+      GemmGroup g{};
+      size_t boff = 0, poff = 0;
+      for (int L = 0; L <= p.lq(q); ++L) {
+        const int P = p.paths(q, L);
+        if (P == 0) continue;
+        const long long PC = (long long)P * C;
+        if (pass == 0 && vw) {
+          GemmProblem& b = g.prob[g.count++];
+          b.M = p.N * (2 * L + 1);
+          b.N = (int)PC;
+          b.K = C;
+          b.alpha = 1.f;
+          b.A = node_view(G, grows, L, C);
+          b.Bt = weight_t(vw + p.w_full(q, L), PC);
+          b.C = plain_out(dBb + boff, PC, dG ? 1 : 0);
+          b.C2 = no_out();
+        }
+        const float* Gx = pass == 0 ? G : dG;
+        const float* Bx = pass == 0 ? dB : B;
+        if (w_hat && Gx) {
+          GemmProblem& d = g.prob[g.count++];
+          d.M = C;
+          d.N = (int)PC;
+          d.K = p.N * (2 * L + 1);
+          d.alpha = 1.f;
+          d.A = node_view_t(Gx, grows, L, C);
+          d.Bt = weight_t(Bx + boff, PC);
+          d.C = plain_out(w_hat + p.w_full(q, L), PC, 1);
+          d.C2 = no_out();
+          d.ksplit = gemm_ksplit(d.M, d.N, d.K, kSplitTarget);
+          d.part = part + poff;
+          poff += (size_t)d.ksplit * d.M * d.N;
+        }
+        boff += (size_t)p.N * (2 * L + 1) * PC;
+      }
+      if (g.count) gemm_group(g, st);
+    }
+    float* Gn = Gb[q % 2];
+    float* dGn = dGb[q % 2];
+    by_ranks<ProdVjp>(p.lprod, p.lq(q), p, (const float*)Bb, phi, A, gz, Gn, (float*)nullptr, st, 0);
+    if (have_dBb)
+      by_ranks<ProdVjp>(p.lprod, p.lq(q), p, (const float*)dBb, phi, A, (const float*)nullptr, dGn, A_hat, st, 0);
+    by_ranks<ProdVjp>(p.lprod, p.lq(q), p, (const float*)Bb, dph, vA, (const float*)nullptr, dGn, A_hat, st,
+                      have_dBb ? 1 : 0);
+    G = Gn;
+    dG = dGn;
+    grows = rp;
+  }
+  // step 1: A_hat += G' W1 + G V1;  w_hat^1 += G^T v_A + G'^T A
+  for (int pass = 0; pass < 2; ++pass) {
+    GemmGroup g{};
+    size_t poff = 0;
+    for (int l = 0; l <= p.lq(1); ++l) {
+      const float* Gx = pass == 0 ? dG : G;
+      const float* Wt = pass == 0 ? w : vw;
+      if (A_hat && Gx && Wt) {
+        GemmProblem& b = g.prob[g.count++];
+        b.M = p.N * (2 * l + 1);
+        b.N = C;
+        b.K = C;
+        b.alpha = 1.f;
+        b.A = node_view(Gx, grows, l, C);
+        b.Bt = weight_t(Wt + p.w_full(1, l), C);
+        b.C = node_out(A_hat, ra, l, C, 1);
+        b.C2 = no_out();
+      }
+      const float* Gy = pass == 0 ? G : dG;
+      const float* Xy = pass == 0 ? vA : A;
+      if (w_hat && Gy && Xy) {
+        GemmProblem& d = g.prob[g.count++];
+        d.M = C;
+        d.N = C;
+        d.K = p.N * (2 * l + 1);
+        d.alpha = 1.f;
+        d.A = node_view_t(Gy, grows, l, C);
+        d.Bt = node_view_t(Xy, ra, l, C);
+        d.C = plain_out(w_hat + p.w_full(1, l), C, 1);
+        d.C2 = no_out();
+        d.ksplit = gemm_ksplit(d.M, d.N, d.K, kSplitTarget);
+        d.part = part + poff;
+        poff += (size_t)d.ksplit * d.M * d.N;
+      }
+    }
+    if (g.count) gemm_group(g, st);
   }
 }
 

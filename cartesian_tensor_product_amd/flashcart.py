@@ -79,6 +79,7 @@ _SIGS = {
     "fc_ladder_weight_block": (_I, [_PL, _I, _PSZ, _PI, _PI, _PI]),
     "fc_node_ladder_fwd": (_I, [_PL, _P, _P, _P, _P, _P, _SZ, _P]),
     "fc_node_ladder_vjp": (_I, [_PL, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "fc_node_ladder_vjp_vjp": (_I, [_PL, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "fc_rms_norm_fwd": (_I, [_PN, _P, _P, _P, _P, _P]),
     "fc_rms_norm_workspace_bytes": (_SZ, [_PN]),
     "fc_rms_norm_vjp": (_I, [_PN, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -319,6 +320,14 @@ def fc_rms_norm_vjp(d: NormDesc, x, gamma, inv_scale, g_y, x_grad, gamma_grad, w
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().fc_rms_norm_vjp(ctypes.byref(d), _f32(x), _f32(gamma), _f32(inv_scale), _f32(g_y), _f32(x_grad),
                                  _f32(gamma_grad), _ptr(workspace), nbytes, _stream(stream)))
+
+
+def fc_node_ladder_vjp_vjp(d: LadderDesc, A, weights, saved, g_z, v_A, v_weights, g_hat, A_hat, weights_hat,
+                           workspace, stream=None):
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().fc_node_ladder_vjp_vjp(ctypes.byref(d), _f32(A), _f32(weights), _f32(saved), _f32(g_z), _f32(v_A),
+                                        _f32(v_weights), _f32(g_hat), _f32(A_hat), _f32(weights_hat),
+                                        _ptr(workspace), nbytes, _stream(stream)))
 
 
 # ------------------------------------------------------------------- block --

@@ -240,7 +240,7 @@ typedef struct {
  * the forward fills for the VJP.  Host only. */
 fc_status fc_ladder_layout(const fc_ladder_desc* d, size_t* n_weight_floats,
                            size_t* n_saved_floats);
-size_t fc_ladder_workspace_bytes(const fc_ladder_desc* d, int32_t op /*0 fwd, 1 vjp*/);
+size_t fc_ladder_workspace_bytes(const fc_ladder_desc* d, int32_t op /*0 fwd, 1 vjp, 2 vjp-of-vjp*/);
 /* Block i (0-based, in flat order) of the weight buffer: its offset in
  * floats, its shape rows x cols, and kind 0 (a mixing matrix, fan-in =
  * cols) or 1 (per-rank or per-path channel weights a, shape [rows][C]).
@@ -261,6 +261,21 @@ fc_status fc_node_ladder_vjp(const fc_ladder_desc* d, const float* A, const floa
                              const float* saved, const float* g_z, float* A_grad,
                              float* weights_grad, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
+
+/* VJP-of-VJP of the full ladder (App. C Eq. C2 carried through Eq. 2): for
+ * s = <v_A, A_grad> + <v_weights, weights_grad> (NULL cotangent = zero),
+ * writes g_hat = ds/dg_z [N][(l_out+1)^2][C], A_hat = ds/dA and
+ * weights_hat = ds/dweights (flat weight layout), each when non-NULL (at
+ * least one).  Needs the forward's saved states (order > 1), g_z unless only
+ * g_hat is requested, and a workspace of fc_ladder_workspace_bytes(d, 2)
+ * bytes (op 2: the largest step's product buffer four times, four states,
+ * order - 1 tangent states and split-K partials).  FC_LADDER_PATH_REDUCED
+ * returns FC_ERR_UNSUPPORTED (op 2 workspace 0). */
+fc_status fc_node_ladder_vjp_vjp(const fc_ladder_desc* d, const float* A, const float* weights,
+                                 const float* saved, const float* g_z, const float* v_A,
+                                 const float* v_weights, float* g_hat, float* A_hat,
+                                 float* weights_hat, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * One message-passing block for energy and forces (App. E "Model

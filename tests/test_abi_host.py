@@ -154,3 +154,13 @@ def test_norm_workspace_size():
     assert fc.fc_rms_norm_workspace_bytes(d) == 1024 * 4 * 128 * 4
     d = fc.norm_desc(10, 16, 1, 0.0)
     assert fc.fc_rms_norm_workspace_bytes(d) == 3 * 2 * 16 * 4
+
+
+def test_ladder_vjp_vjp_workspace():
+    """Op 2 (VJP-of-VJP) of the full ladder holds four product buffers, four
+    states and order - 1 tangent states; the path-reduced ladder has none."""
+    full = fc.ladder_desc(4096, 128, 3, 3, 3, 4, fc.FC_LADDER_FULL)
+    red = fc.ladder_desc(4096, 128, 3, 3, 3, 4, fc.FC_LADDER_PATH_REDUCED)
+    st = 4096 * 16 * 128 * 4
+    assert fc.fc_ladder_workspace_bytes(full, 2) >= 4 * 4096 * 99 * 128 * 4 + 7 * st
+    assert fc.fc_ladder_workspace_bytes(red, 2) == 0

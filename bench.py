@@ -177,17 +177,16 @@ def extras(dev, only_ladder=False, conv_ranks=(3, 4), only_conv=False):
         r = {"fwd_ms": timed(lambda: fc.fc_node_ladder_fwd(ld, dA, dW, z, saved, wsf)),
              "vjp_ms": timed(lambda: fc.fc_node_ladder_vjp(ld, dA, dW, saved, dg, Ab, Wb, wsb))}
         r["node_channels_per_s_fwd"] = 4096 * CHANNELS / (r["fwd_ms"] * 1e-3)
-        if var == fc.FC_LADDER_FULL:
-            # VJP-of-VJP with the cotangent on A_grad only (zero weight-gradient
-            # cotangent, as the pages time it); its workspace is the extra memory
-            fc.fc_node_ladder_fwd(ld, dA, dW, z, saved, wsf)
-            vA = t(inputs.normal(np.random.default_rng(6), A.shape))
-            gh, Ah, Wh = torch.empty_like(z), torch.empty_like(dA), torch.empty_like(dW)
-            wsv = fc.workspace(fc.fc_ladder_workspace_bytes(ld, 2), dev)
-            r["vjp_vjp_ms"] = timed(lambda: fc.fc_node_ladder_vjp_vjp(ld, dA, dW, saved, dg, vA, None, gh, Ah, Wh,
-                                                                      wsv), iters=5)
-            r["vjp_vjp_workspace_bytes"] = fc.fc_ladder_workspace_bytes(ld, 2)
-            del vA, gh, Ah, Wh, wsv
+        # VJP-of-VJP with the cotangent on A_grad only (zero weight-gradient
+        # cotangent, as the pages time it); its workspace is the extra memory
+        fc.fc_node_ladder_fwd(ld, dA, dW, z, saved, wsf)
+        vA = t(inputs.normal(np.random.default_rng(6), A.shape))
+        gh, Ah, Wh = torch.empty_like(z), torch.empty_like(dA), torch.empty_like(dW)
+        wsv = fc.workspace(fc.fc_ladder_workspace_bytes(ld, 2), dev)
+        r["vjp_vjp_ms"] = timed(lambda: fc.fc_node_ladder_vjp_vjp(ld, dA, dW, saved, dg, vA, None, gh, Ah, Wh,
+                                                                  wsv), iters=5)
+        r["vjp_vjp_workspace_bytes"] = fc.fc_ladder_workspace_bytes(ld, 2)
+        del vA, gh, Ah, Wh, wsv
         out[f"ladder_{name}_4096n_128c_rank3_order4"] = r
         del saved, z, Ab, Wb, wsf, wsb
     if only_conv:

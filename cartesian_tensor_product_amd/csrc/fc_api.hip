@@ -461,7 +461,7 @@ fc_status fc_ladder_weight_block(const fc_ladder_desc* d, int32_t i, size_t* off
 size_t fc_ladder_workspace_bytes(const fc_ladder_desc* d, int32_t op) {
   fc::LadderPlan p;
   if (ladder_plan(d, &p) != FC_OK) return 0;
-  if (op == 2) return p.variant == FC_LADDER_FULL ? sizeof(float) * p.vv_ws_floats() : 0;
+  if (op == 2) return sizeof(float) * p.vv_ws_floats();
   return sizeof(float) * (op == 1 ? p.vjp_ws_floats() : p.fwd_ws_floats());
 }
 
@@ -504,8 +504,6 @@ fc_status fc_node_ladder_vjp_vjp(const fc_ladder_desc* d, const float* A, const 
                                  hipStream_t stream) {
   fc::LadderPlan p;
   if (fc_status s = ladder_plan(d, &p)) return s;
-  if (p.variant != FC_LADDER_FULL)
-    return fail(FC_ERR_UNSUPPORTED, "ladder VJP-of-VJP is implemented for the full ladder only");
   if (!g_hat && !A_hat && !weights_hat) return fail(FC_ERR_INVALID_ARGUMENT, "ladder VJP-of-VJP: no output requested");
   if (!A || !weights || ((A_hat || weights_hat) && !g_z))
     return fail(FC_ERR_INVALID_ARGUMENT, "ladder VJP-of-VJP: NULL A, weights or g_z");

@@ -20,7 +20,7 @@ struct LadderPlan {
   size_t state_floats() const;
   size_t fwd_ws_floats() const;
   size_t vjp_ws_floats() const;
-  size_t vv_ws_floats() const;         // VJP-of-VJP (full ladder)
+  size_t vv_ws_floats() const;         // VJP-of-VJP
   // offsets (floats) into the flat weight buffer
   size_t w_full(int q, int L) const;   // full: W1_L (q = 1) or W^q_L
   size_t w_a(int q) const;             // reduced: a1 (q = 1) or a^q
@@ -31,7 +31,7 @@ void ladder_forward(const LadderPlan& p, const float* A, const float* w, float* 
                     hipStream_t st);
 void ladder_vjp(const LadderPlan& p, const float* A, const float* w, const float* saved, const float* gz,
                 float* A_grad, float* w_grad, float* ws, hipStream_t st);
-// Full ladder: derivatives of s = <v_A, A_bar> + <v_w, w_bar> (cotangents
+// Derivatives of s = <v_A, A_bar> + <v_w, w_bar> (cotangents
 // nullable) with respect to g_z (g_hat), A (A_hat) and the weights (w_hat).
 void ladder_vjp_vjp(const LadderPlan& p, const float* A, const float* w, const float* saved, const float* gz,
                     const float* vA, const float* vw, float* g_hat, float* A_hat, float* w_hat, float* ws,

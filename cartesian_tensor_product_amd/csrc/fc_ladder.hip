@@ -306,6 +306,194 @@ __global__ __launch_bounds__(kWave) void ladder_reduced_first_kernel(int N, int 
   for (int l = 0; l <= lout; ++l) a1part[((size_t)blockIdx.x * (lout + 1) + l) * C + k] = acc[l];
 }
 
+// ---------------------------------- path-reduced steps on a product buffer --
+// The path-reduced VJP-of-VJP runs a step on the full ladder's product
+// buffer (layout of ladder_prod_kernel) with the per-path channel weights:
+//   mix:      out_L = s_L sum_{eta -> L} (a_eta X_eta + b_eta Y_eta)
+//   mix VJP:  B_bar_eta = s_L (a_eta X_L + b_eta Y_L)
+//   weights:  part[blk][eta][k] = s_L sum_{u in tile, c} (X_L B1_eta + Y_L B2_eta)
+// with s_L = P_L^{-1/2}, a, b [P][C] (either term nullable).
+
+// out (state rows `orows`, nullable) = or += the mix; dS (rows `srows`,
+// ranks <= lout, nullable) += or = it as well.
+template <int LP, int LA, int LQ>
+__global__ __launch_bounds__(kWave) void ladder_mix_kernel(int N, int C, const float* __restrict__ X,
+                                                           const float* __restrict__ a,
+                                                           const float* __restrict__ Y,
+                                                           const float* __restrict__ b, float* __restrict__ out,
+                                                           int orows, float* __restrict__ dS, int srows, int lout,
+                                                           int acc_s) {
+  using Cfg = ConvCfg<LP, LA, LQ>;
+  const int u = blockIdx.x;
+  const int k = blockIdx.y * kWave + threadIdx.x;
+  if (k >= C) return;
+  static_for<LQ + 1>([&](auto Lc) {
+    constexpr int L = Lc, PL = Cfg::count_L(L), na = ncomp(L);
+    if constexpr (PL > 0) {
+      constexpr int p0 = Cfg::first_path_of(L), off = Cfg::paths[p0].off;
+      const float sL = 1.0f / sqrtf(float(PL));
+      const size_t ld = (size_t)PL * C;
+      float t[na];
+      static_for<na>([&](auto c) { t[c] = 0.f; });
+      static_for<PL>([&](auto e) {
+        constexpr int eta = e;
+        const size_t base = (size_t)N * off * C + (size_t)eta * C + k;
+        if (X) {
+          const float w = a[(size_t)(p0 + eta) * C + k];
+          static_for<na>([&](auto c) { t[c] = fmaf(w, X[base + ((size_t)u * na + c) * ld], t[c]); });
+        }
+        if (Y) {
+          const float w = b[(size_t)(p0 + eta) * C + k];
+          static_for<na>([&](auto c) { t[c] = fmaf(w, Y[base + ((size_t)u * na + c) * ld], t[c]); });
+        }
+      });
+      static_for<na>([&](auto c) {
+        const float v = sL * t[c];
+        if (out) out[((size_t)u * orows + L * L + c) * C + k] = v;
+        if (dS && L <= lout) {
+          float* d = dS + ((size_t)u * srows + L * L + c) * C + k;
+          *d = acc_s ? *d + v : v;
+        }
+      });
+    }
+  });
+}
+
+template <int LP, int LA, int LQ>
+__global__ __launch_bounds__(kWave) void ladder_mix_vjp_kernel(int N, int C, const float* __restrict__ X, int xrows,
+                                                               const float* __restrict__ a,
+                                                               const float* __restrict__ Y, int yrows,
+                                                               const float* __restrict__ b,
+                                                               float* __restrict__ Bbar) {
+  using Cfg = ConvCfg<LP, LA, LQ>;
+  const int u = blockIdx.x;
+  const int k = blockIdx.y * kWave + threadIdx.x;
+  if (k >= C) return;
+  static_for<LQ + 1>([&](auto Lc) {
+    constexpr int L = Lc, PL = Cfg::count_L(L), na = ncomp(L);
+    if constexpr (PL > 0) {
+      constexpr int p0 = Cfg::first_path_of(L), off = Cfg::paths[p0].off;
+      const float sL = 1.0f / sqrtf(float(PL));
+      const size_t ld = (size_t)PL * C;
+      float xv[na], yv[na];
+      static_for<na>([&](auto c) {
+        xv[c] = X ? X[((size_t)u * xrows + L * L + c) * C + k] : 0.f;
+        yv[c] = Y ? Y[((size_t)u * yrows + L * L + c) * C + k] : 0.f;
+      });
+      static_for<PL>([&](auto e) {
+        constexpr int eta = e;
+        const float wa = X ? sL * a[(size_t)(p0 + eta) * C + k] : 0.f;
+        const float wb = Y ? sL * b[(size_t)(p0 + eta) * C + k] : 0.f;
+        float* dst = Bbar + (size_t)N * off * C + (size_t)eta * C + k;
+        static_for<na>([&](auto c) { dst[((size_t)u * na + c) * ld] = fmaf(wa, xv[c], wb * yv[c]); });
+      });
+    }
+  });
+}
+
+template <int LP, int LA, int LQ>
+__global__ __launch_bounds__(kWave) void ladder_mix_wgrad_kernel(int N, int C, int ntile,
+                                                                 const float* __restrict__ X, int xrows,
+                                                                 const float* __restrict__ B1,
+                                                                 const float* __restrict__ Y, int yrows,
+                                                                 const float* __restrict__ B2,
+                                                                 float* __restrict__ part) {
+  using Cfg = ConvCfg<LP, LA, LQ>;
+  const int k = blockIdx.y * kWave + threadIdx.x;
+  if (k >= C) return;
+  const int u0 = blockIdx.x * ntile, u1 = min(N, u0 + ntile);
+  static_for<LQ + 1>([&](auto Lc) {
+    constexpr int L = Lc, PL = Cfg::count_L(L), na = ncomp(L);
+    if constexpr (PL > 0) {
+      constexpr int p0 = Cfg::first_path_of(L), off = Cfg::paths[p0].off;
+      const float sL = 1.0f / sqrtf(float(PL));
+      const size_t ld = (size_t)PL * C;
+      float acc[PL];
+      static_for<PL>([&](auto e) { acc[e] = 0.f; });
+      for (int u = u0; u < u1; ++u) {
+        float xv[na], yv[na];
+        static_for<na>([&](auto c) {
+          xv[c] = X ? X[((size_t)u * xrows + L * L + c) * C + k] : 0.f;
+          yv[c] = Y ? Y[((size_t)u * yrows + L * L + c) * C + k] : 0.f;
+        });
+        static_for<PL>([&](auto e) {
+          constexpr int eta = e;
+          const size_t base = (size_t)N * off * C + (size_t)eta * C + k;
+          float t = acc[eta];
+          static_for<na>([&](auto c) {
+            if (X) t = fmaf(xv[c], B1[base + ((size_t)u * na + c) * ld], t);
+            if (Y) t = fmaf(yv[c], B2[base + ((size_t)u * na + c) * ld], t);
+          });
+          acc[eta] = t;
+        });
+      }
+      static_for<PL>([&](auto e) {
+        part[((size_t)blockIdx.x * Cfg::P + p0 + e) * C + k] = sL * acc[e];
+      });
+    }
+  });
+}
+
+// phi'^1 = a1 v_A + b1 A for ranks l <= lq1 (either term nullable) into the
+// state dphi (rows `prows`, nullable) and dS (ranks <= lout, stored).
+__global__ __launch_bounds__(kWave) void ladder_first_tangent_kernel(int N, int C, int lq1, int lout, int a_rows,
+                                                                     int prows, int srows,
+                                                                     const float* __restrict__ vA,
+                                                                     const float* __restrict__ a1,
+                                                                     const float* __restrict__ A,
+                                                                     const float* __restrict__ b1,
+                                                                     float* __restrict__ dphi,
+                                                                     float* __restrict__ dS) {
+  const int u = blockIdx.x;
+  const int k = blockIdx.y * kWave + threadIdx.x;
+  if (k >= C) return;
+  const int rows = (lq1 + 1) * (lq1 + 1);
+  for (int c = 0; c < rows; ++c) {
+    int l = 0;
+    while ((l + 1) * (l + 1) <= c) ++l;
+    float v = 0.f;
+    if (vA) v = a1[(size_t)l * C + k] * vA[((size_t)u * a_rows + c) * C + k];
+    if (b1) v = fmaf(b1[(size_t)l * C + k], A[((size_t)u * a_rows + c) * C + k], v);
+    if (dphi) dphi[((size_t)u * prows + c) * C + k] = v;
+    if (dS && l <= lout) dS[((size_t)u * srows + c) * C + k] = v;
+  }
+}
+
+// Reverse of phi^1 = a1 A with tangents: A_hat += a1 G' + b1 G (nullable
+// terms), part[blk][l][k] = sum_{u in tile, c} (G' A + G v_A).
+__global__ __launch_bounds__(kWave) void ladder_first_reverse_kernel(int N, int C, int ntile, int lq1, int a_rows,
+                                                                     int grows, const float* __restrict__ G,
+                                                                     const float* __restrict__ dG,
+                                                                     const float* __restrict__ A,
+                                                                     const float* __restrict__ vA,
+                                                                     const float* __restrict__ a1,
+                                                                     const float* __restrict__ b1,
+                                                                     float* __restrict__ A_hat,
+                                                                     float* __restrict__ part) {
+  const int k = blockIdx.y * kWave + threadIdx.x;
+  if (k >= C) return;
+  const int rows = (lq1 + 1) * (lq1 + 1);
+  float acc[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+  const int u0 = blockIdx.x * ntile, u1 = min(N, u0 + ntile);
+  for (int u = u0; u < u1; ++u)
+    for (int c = 0; c < rows; ++c) {
+      int l = 0;
+      while ((l + 1) * (l + 1) <= c) ++l;
+      const float g = G[((size_t)u * grows + c) * C + k];
+      const float dg = dG ? dG[((size_t)u * grows + c) * C + k] : 0.f;
+      if (A_hat) {
+        float h = a1[(size_t)l * C + k] * dg;
+        if (b1) h = fmaf(b1[(size_t)l * C + k], g, h);
+        A_hat[((size_t)u * a_rows + c) * C + k] += h;
+      }
+      float t = dg * A[((size_t)u * a_rows + c) * C + k];
+      if (vA) t = fmaf(g, vA[((size_t)u * a_rows + c) * C + k], t);
+      acc[l] += t;
+    }
+  if (part)
+    for (int l = 0; l <= lq1; ++l) part[((size_t)blockIdx.x * (lq1 + 1) + l) * C + k] = acc[l];
+}
+
 __global__ __launch_bounds__(256) void fill_zero_kernel(size_t n, float* __restrict__ p) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0.f;
@@ -409,6 +597,18 @@ size_t LadderPlan::vv_ws_floats() const {
   const size_t st = state_floats();
   const size_t C2 = (size_t)C * C;
   size_t b = 0, part = 0;
+  if (variant == 1) {   // + S, S', S_bar, S_bar' and the path-weight partials
+    const int nblk = (N + kNTile - 1) / kNTile;
+    int pmax = lq(1) + 1;
+    for (int q = 2; q <= order; ++q) {
+      b = std::max(b, (size_t)N * prod_rows(q) * C);
+      pmax = std::max(pmax, paths(q));
+    }
+    size_t g = 0;
+    for (int L = 0; L <= lout; ++L) g += (size_t)gemm_ksplit(C, C, N * (2 * L + 1), kSplitTarget) * C2;
+    part = std::max(g, (size_t)nblk * pmax * C);
+    return 4 * b + 4 * st + (size_t)(order - 1) * st + 4 * (size_t)N * nr(lout) * C + part;
+  }
   for (int q = 2; q <= order; ++q) {
     b = std::max(b, (size_t)N * prod_rows(q) * C);
     size_t g = 0;
@@ -644,6 +844,33 @@ struct RedVjp {
   template <class... A>
   static void run(A&&... a) { launch_red_vjp<LP, LQ>(a...); }
 };
+template <int LP, int LQ>
+struct Mix {
+  static void run(const LadderPlan& p, const float* X, const float* a, const float* Y, const float* b, float* out,
+                  float* dS, int acc_s, hipStream_t st) {
+    dim3 grid(p.N, (p.C + kWave - 1) / kWave);
+    hipLaunchKernelGGL((ladder_mix_kernel<LP, LP, LQ>), grid, dim3(kWave), 0, st, p.N, p.C, X, a, Y, b, out,
+                       nr(p.lprod), dS, nr(p.lout), p.lout, acc_s);
+  }
+};
+template <int LP, int LQ>
+struct MixVjp {
+  static void run(const LadderPlan& p, const float* X, int xrows, const float* a, const float* Y, int yrows,
+                  const float* b, float* Bbar, hipStream_t st) {
+    dim3 grid(p.N, (p.C + kWave - 1) / kWave);
+    hipLaunchKernelGGL((ladder_mix_vjp_kernel<LP, LP, LQ>), grid, dim3(kWave), 0, st, p.N, p.C, X, xrows, a, Y,
+                       yrows, b, Bbar);
+  }
+};
+template <int LP, int LQ>
+struct MixWgrad {
+  static void run(const LadderPlan& p, const float* X, int xrows, const float* B1, const float* Y, int yrows,
+                  const float* B2, float* part, hipStream_t st) {
+    dim3 grid((p.N + kNTile - 1) / kNTile, (p.C + kWave - 1) / kWave);
+    hipLaunchKernelGGL((ladder_mix_wgrad_kernel<LP, LP, LQ>), grid, dim3(kWave), 0, st, p.N, p.C, kNTile, X, xrows,
+                       B1, Y, yrows, B2, part);
+  }
+};
 
 void fill_zero(float* p, size_t n, hipStream_t st) {
   if (n) hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, n, p);
@@ -816,6 +1043,156 @@ void ladder_vjp(const LadderPlan& p, const float* A, const float* w, const float
   }
 }
 
+namespace {
+
+// Path-reduced ladder, VJP-of-VJP: the same forward-over-reverse scheme as
+// the full ladder below, with each step run on the product buffer (B, B')
+// and the channel-diagonal path weights a^q in place of the GEMM (the
+// register-fused kernels of the forward and VJP have no tangent form).
+void ladder_vjp_vjp_reduced(const LadderPlan& p, const float* A, const float* w, const float* saved,
+                            const float* gz, const float* vA, const float* vw, float* g_hat, float* A_hat,
+                            float* w_hat, float* ws, hipStream_t st) {
+  const int C = p.C;
+  const int ra = nr(p.la), rp = nr(p.lprod), ro = nr(p.lout);
+  const size_t stf = p.state_floats(), so = (size_t)p.N * ro * C;
+  size_t bmax = 0;
+  for (int q = 2; q <= p.order; ++q) bmax = std::max(bmax, (size_t)p.N * p.prod_rows(q) * C);
+  float* B = ws;
+  float* dB = B + bmax;
+  float* Bb = dB + bmax;
+  float* dBb = Bb + bmax;
+  float* Gb[2] = {dBb + bmax, dBb + bmax + stf};
+  float* dGb[2] = {Gb[1] + stf, Gb[1] + 2 * stf};
+  float* dphi = dGb[1] + stf;
+  float* S = dphi + (size_t)(p.order - 1) * stf;
+  float* dS = S + so;
+  float* Sb = dS + so;
+  float* dSb = Sb + so;
+  float* part = dSb + so;
+  auto phi_of = [&](int q) -> const float* { return saved + (size_t)(q - 1) * stf; };
+  auto dphi_of = [&](int q) -> float* { return q < p.order ? dphi + (size_t)(q - 1) * stf : nullptr; };
+  auto aw = [&](const float* base, int q) -> const float* { return base ? base + p.w_a(q) : nullptr; };
+  const int nblk = (p.N + kNTile - 1) / kNTile;
+  const dim3 ngrid(p.N, (C + kWave - 1) / kWave), tgrid(nblk, (C + kWave - 1) / kWave);
+  const bool rev = A_hat || w_hat;
+  if (A_hat) fill_zero(A_hat, (size_t)p.N * ra * C, st);
+  if (w_hat) fill_zero(w_hat, p.weight_floats(), st);
+  if (!vA && !vw) {
+    if (g_hat) fill_zero(g_hat, so, st);
+    return;
+  }
+  // ---- forward tangent: S' = sum_q Pi phi'^q
+  hipLaunchKernelGGL(ladder_first_tangent_kernel, ngrid, dim3(kWave), 0, st, p.N, C, p.lq(1), p.lout, ra, rp, ro,
+                     vA, aw(w, 1), A, aw(vw, 1), dphi_of(1), dS);
+  for (int q = 2; q <= p.order; ++q) {
+    const float* phi = phi_of(q - 1);
+    prod(p, p.lq(q), dphi_of(q - 1), A, dB, st, 0);
+    if (vA) prod(p, p.lq(q), phi, vA, dB, st, 1);
+    if (vw) prod(p, p.lq(q), phi, A, B, st, 0);
+    by_ranks<Mix>(p.lprod, p.lq(q), p, (const float*)dB, aw(w, q), vw ? (const float*)B : nullptr, aw(vw, q),
+                  dphi_of(q), dS, 1, st);
+  }
+  if (vw) {   // S, for the cotangent of the final maps
+    switch (p.lprod) {
+      case 1: dispatch_reduced<1>(p, A, w, S, nullptr, st); break;
+      case 2: dispatch_reduced<2>(p, A, w, S, nullptr, st); break;
+      case 3: dispatch_reduced<3>(p, A, w, S, nullptr, st); break;
+      case 4: dispatch_reduced<4>(p, A, w, S, nullptr, st); break;
+    }
+  }
+  // g_hat = W_L S'_L + V_L S_L
+  for (int pass = 0; g_hat && pass < 2; ++pass) {
+    if (pass == 1 && !vw) continue;
+    GemmGroup g{};
+    for (int L = 0; L <= p.lout; ++L) {
+      GemmProblem& pr = g.prob[g.count++];
+      pr.M = p.N * (2 * L + 1);
+      pr.N = C;
+      pr.K = C;
+      pr.alpha = 1.f;
+      pr.A = node_view(pass == 0 ? dS : S, ro, L, C);
+      pr.Bt = plain_view((pass == 0 ? w : vw) + p.w_final(L), C);
+      pr.C = node_out(g_hat, ro, L, C, pass);
+      pr.C2 = no_out();
+    }
+    gemm_group(g, st);
+  }
+  if (!rev) return;
+  // ---- reverse: S_bar = g W_L, S_bar' = g V_L;  w_hat(W_L) += g^T S'
+  {
+    GemmGroup g{};
+    for (int L = 0; L <= p.lout; ++L)
+      for (int t = 0; t < 2; ++t) {
+        if (t == 1 && !vw) continue;
+        GemmProblem& b = g.prob[g.count++];
+        b.M = p.N * (2 * L + 1);
+        b.N = C;
+        b.K = C;
+        b.alpha = 1.f;
+        b.A = node_view(gz, ro, L, C);
+        b.Bt = weight_t((t == 0 ? w : vw) + p.w_final(L), C);
+        b.C = node_out(t == 0 ? Sb : dSb, ro, L, C, 0);
+        b.C2 = no_out();
+      }
+    gemm_group(g, st);
+  }
+  if (w_hat) {
+    GemmGroup g{};
+    size_t poff = 0;
+    for (int L = 0; L <= p.lout; ++L) {
+      GemmProblem& d = g.prob[g.count++];
+      d.M = C;
+      d.N = C;
+      d.K = p.N * (2 * L + 1);
+      d.alpha = 1.f;
+      d.A = node_view_t(gz, ro, L, C);
+      d.Bt = node_view_t(dS, ro, L, C);
+      d.C = plain_out(w_hat + p.w_final(L), C, 1);
+      d.C2 = no_out();
+      d.ksplit = gemm_ksplit(d.M, d.N, d.K, kSplitTarget);
+      d.part = part + poff;
+      poff += (size_t)d.ksplit * d.M * d.N;
+    }
+    gemm_group(g, st);
+  }
+  const float* G = Sb;
+  const float* dG = vw ? dSb : nullptr;
+  const float* dSbar = vw ? dSb : nullptr;
+  int grows = ro;
+  for (int q = p.order; q >= 2; --q) {
+    const float* phi = phi_of(q - 1);
+    const float* dph = dphi_of(q - 1);
+    const float* aq = aw(w, q);
+    const float* vaq = aw(vw, q);
+    prod(p, p.lq(q), phi, A, B, st, 0);
+    prod(p, p.lq(q), dph, A, dB, st, 0);
+    if (vA) prod(p, p.lq(q), phi, vA, dB, st, 1);
+    by_ranks<MixVjp>(p.lprod, p.lq(q), p, G, grows, aq, (const float*)nullptr, 0, (const float*)nullptr, Bb, st);
+    const bool have_dBb = dG || vaq;
+    if (have_dBb)
+      by_ranks<MixVjp>(p.lprod, p.lq(q), p, dG, grows, aq, vaq ? G : nullptr, grows, vaq, dBb, st);
+    if (w_hat) {
+      by_ranks<MixWgrad>(p.lprod, p.lq(q), p, dG, grows, (const float*)B, G, grows, (const float*)dB, part, st);
+      block_sum(nblk, p.paths(q) * C, part, w_hat + p.w_a(q), st);
+    }
+    float* Gn = Gb[q % 2];
+    float* dGn = dGb[q % 2];
+    by_ranks<ProdVjp>(p.lprod, p.lq(q), p, (const float*)Bb, phi, A, (const float*)Sb, Gn, (float*)nullptr, st, 0);
+    if (have_dBb)
+      by_ranks<ProdVjp>(p.lprod, p.lq(q), p, (const float*)dBb, phi, A, dSbar, dGn, A_hat, st, 0);
+    by_ranks<ProdVjp>(p.lprod, p.lq(q), p, (const float*)Bb, dph, vA, have_dBb ? nullptr : dSbar, dGn, A_hat, st,
+                      have_dBb ? 1 : 0);
+    G = Gn;
+    dG = dGn;
+    grows = rp;
+  }
+  hipLaunchKernelGGL(ladder_first_reverse_kernel, tgrid, dim3(kWave), 0, st, p.N, C, kNTile, p.lq(1), ra, grows, G,
+                     dG, A, vA, aw(w, 1), aw(vw, 1), A_hat, w_hat ? part : nullptr);
+  if (w_hat) block_sum(nblk, (p.lq(1) + 1) * C, part, w_hat + p.w_a(1), st);
+}
+
+}  // namespace
+
 // Full ladder, VJP-of-VJP by forward-over-reverse: every map of the ladder is
 // linear in each operand, so the tangent of a product step is two product
 // launches (prod(phi', A) + prod(phi, v_A)), the tangent of a GEMM two GEMMs
@@ -829,6 +1206,10 @@ void ladder_vjp(const LadderPlan& p, const float* A, const float* w, const float
 void ladder_vjp_vjp(const LadderPlan& p, const float* A, const float* w, const float* saved, const float* gz,
                     const float* vA, const float* vw, float* g_hat, float* A_hat, float* w_hat, float* ws,
                     hipStream_t st) {
+  if (p.variant == 1) {
+    ladder_vjp_vjp_reduced(p, A, w, saved, gz, vA, vw, g_hat, A_hat, w_hat, ws, st);
+    return;
+  }
   const int C = p.C;
   const int ra = nr(p.la), rp = nr(p.lprod), ro = nr(p.lout);
   const size_t stf = p.state_floats();

@@ -262,15 +262,15 @@ fc_status fc_node_ladder_vjp(const fc_ladder_desc* d, const float* A, const floa
                              float* weights_grad, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
-/* VJP-of-VJP of the full ladder (App. C Eq. C2 carried through Eq. 2): for
+/* VJP-of-VJP of the ladder (App. C Eq. C2 carried through Eq. 2): for
  * s = <v_A, A_grad> + <v_weights, weights_grad> (NULL cotangent = zero),
  * writes g_hat = ds/dg_z [N][(l_out+1)^2][C], A_hat = ds/dA and
  * weights_hat = ds/dweights (flat weight layout), each when non-NULL (at
  * least one).  Needs the forward's saved states (order > 1), g_z unless only
  * g_hat is requested, and a workspace of fc_ladder_workspace_bytes(d, 2)
  * bytes (op 2: the largest step's product buffer four times, four states,
- * order - 1 tangent states and split-K partials).  FC_LADDER_PATH_REDUCED
- * returns FC_ERR_UNSUPPORTED (op 2 workspace 0). */
+ * order - 1 tangent states, split-K partials and, path-reduced, four
+ * output-sized sums).  Both variants. */
 fc_status fc_node_ladder_vjp_vjp(const fc_ladder_desc* d, const float* A, const float* weights,
                                  const float* saved, const float* g_z, const float* v_A,
                                  const float* v_weights, float* g_hat, float* A_hat,

@@ -157,10 +157,10 @@ def test_norm_workspace_size():
 
 
 def test_ladder_vjp_vjp_workspace():
-    """Op 2 (VJP-of-VJP) of the full ladder holds four product buffers, four
-    states and order - 1 tangent states; the path-reduced ladder has none."""
+    """Op 2 (VJP-of-VJP) holds four product buffers, four states and order - 1
+    tangent states; the path-reduced ladder also four output-sized sums."""
     full = fc.ladder_desc(4096, 128, 3, 3, 3, 4, fc.FC_LADDER_FULL)
     red = fc.ladder_desc(4096, 128, 3, 3, 3, 4, fc.FC_LADDER_PATH_REDUCED)
     st = 4096 * 16 * 128 * 4
     assert fc.fc_ladder_workspace_bytes(full, 2) >= 4 * 4096 * 99 * 128 * 4 + 7 * st
-    assert fc.fc_ladder_workspace_bytes(red, 2) == 0
+    assert fc.fc_ladder_workspace_bytes(red, 2) >= 4 * 4096 * 99 * 128 * 4 + 7 * st + 4 * st

@@ -1,5 +1,6 @@
-"""GPU parity of the full ladder's VJP-of-VJP (cotangents on A_grad and on
-the weight gradients) against the oracle's complex-step derivatives."""
+"""GPU parity of the ladder's VJP-of-VJP, full and path-reduced (cotangents
+on A_grad and on the weight gradients), against the oracle's complex-step
+derivatives."""
 import numpy as np
 import pytest
 
@@ -47,45 +48,40 @@ def cotangents(g, seed, with_A=True, with_w=True):
     return vA, vw
 
 
+@pytest.mark.parametrize("variant", ["full", "reduced"])
 @pytest.mark.parametrize("l,l_out,order", [(1, 1, 1), (1, 0, 3), (2, 2, 2), (2, 1, 4), (3, 3, 4), (3, 2, 1),
                                            (4, 4, 3)])
-def test_ladder_vjp_vjp_small(l, l_out, order):
-    g = GpuLadder(l, l_out, order, "full", C=64, N=37)
+def test_ladder_vjp_vjp_small(l, l_out, order, variant):
+    g = GpuLadder(l, l_out, order, variant, C=64, N=37)
     g.fwd()
     vA, vw = cotangents(g, 40 + order)
     check(g, vA, vw)
 
 
+@pytest.mark.parametrize("variant", ["full", "reduced"])
 @pytest.mark.parametrize("which", ["A", "w"])
-def test_ladder_vjp_vjp_one_cotangent(which):
-    g = GpuLadder(3, 3, 4, "full", C=32, N=29)
+def test_ladder_vjp_vjp_one_cotangent(which, variant):
+    g = GpuLadder(3, 3, 4, variant, C=32, N=29)
     g.fwd()
     vA, vw = cotangents(g, 7, with_A=which == "A", with_w=which == "w")
     check(g, vA, vw)
 
 
-def test_ladder_vjp_vjp_single_outputs():
-    g = GpuLadder(2, 2, 3, "full", C=32, N=21)
+@pytest.mark.parametrize("variant", ["full", "reduced"])
+def test_ladder_vjp_vjp_single_outputs(variant):
+    g = GpuLadder(2, 2, 3, variant, C=32, N=21)
     g.fwd()
     vA, vw = cotangents(g, 8)
     for want in (("g",), ("A",), ("W",)):
         check(g, vA, vw, want)
 
 
-def test_ladder_vjp_vjp_path_reduced_unsupported():
-    g = GpuLadder(2, 2, 2, "reduced", C=32, N=8)
-    g.fwd()
-    vA, _ = cotangents(g, 9, with_w=False)
-    with pytest.raises(g.fc.FlashCartError) as ei:
-        run_vv(g, vA, None)
-    assert ei.value.status == g.fc.FC_ERR_UNSUPPORTED
-
-
-def test_ladder_vjp_vjp_workload_sampled():
+@pytest.mark.parametrize("variant", ["full", "reduced"])
+def test_ladder_vjp_vjp_workload_sampled(variant):
     """4096 nodes, 128 channels, ranks <= 3, order 4 (the ladder workload),
     position-free training derivative with v_A only (as the pages time it);
     g_hat and A_hat compared on 24 sampled nodes (the ladder is node-local)."""
-    g = GpuLadder(3, 3, 4, "full", C=128, N=4096)
+    g = GpuLadder(3, 3, 4, variant, C=128, N=4096)
     g.fwd()
     vA, _ = cotangents(g, 10, with_w=False)
     gh, Ah, _ = run_vv(g, vA, None, want=("g", "A"))

@@ -143,6 +143,31 @@ def extras(dev, only_ladder=False, conv_ranks=(3, 4), only_conv=False):
         r["fwd_plus_vjp_frac_hbm"] = (bf + bv) / ((r["fwd_ms"] + r["vjp_ms"]) * 1e-3) / 1e9 / HBM_PEAK_GBS
         out[f"conv_summed_rank{l}_1024n_128c_128nbr"] = r
         del z, xb, pb, ws
+    # the pages' radial network (Chebyshev + envelope + bias-free SiLU MLP,
+    # MFMA output layer) weighting the rank-2 micro convolution
+    if not only_ladder and not only_conv:
+        desc = fc.conv_desc(N_NODES, N_NODES * K_NBR, CHANNELS, 2, 2, 2, R_CUT)
+        P, n_in, n_out = fc.fc_conv_layout(desc)
+        d = inputs.edge_conv_inputs(1, N_NODES, K_NBR, BOX, CHANNELS, n_in, P, n_out)
+        mlp = t(inputs.radial_mlp_weights(np.random.default_rng(51), P, CHANNELS))
+        graph = fc.DeviceGraph(d["rowptr"], d["sender"], N_NODES, device=dev)
+        pos, x, g = t(d["pos"]), t(d["x"]), t(d["g"])
+        E = N_NODES * K_NBR
+        w = torch.empty((E, P, CHANNELS), device=dev)
+        z = torch.empty((N_NODES, n_out, CHANNELS), device=dev)
+        xb, pb, mb = torch.empty_like(x), torch.empty((N_NODES, 3), device=dev), torch.empty_like(mlp)
+        ws0 = fc.workspace(fc.fc_edge_conv_mlp_workspace_bytes(desc, 0), dev)
+        ws1 = fc.workspace(fc.fc_edge_conv_mlp_workspace_bytes(desc, 1), dev)
+        rms = timed(lambda: fc.fc_radial_mlp(desc, graph, pos, None, mlp, w, ws0))
+        fms = timed(lambda: fc.fc_edge_conv_mlp_fwd(desc, graph, pos, None, x, mlp, z, ws0))
+        vms = timed(lambda: fc.fc_edge_conv_mlp_vjp(desc, graph, pos, None, x, mlp, g, xb, pb, None, ws1))
+        vwms = timed(lambda: fc.fc_edge_conv_mlp_vjp(desc, graph, pos, None, x, mlp, g, xb, pb, mb, ws1))
+        out["conv_radial_mlp_rank2_1024n_128c_128nbr"] = {
+            "radial_mlp_ms": rms, "fwd_ms": fms, "vjp_ms": vms, "vjp_with_mlp_grad_ms": vwms,
+            "output_layer_tflops_lower_bound": 2.0 * E * 64 * P * CHANNELS / (rms * 1e-3) / 1e12,
+            "w_bytes": E * P * CHANNELS * 4,
+            "fwd_plus_vjp_edge_channels_per_s": E * CHANNELS / ((fms + vms) * 1e-3)}
+        del w, z, xb, pb, mb, ws0, ws1, mlp
     # equivariant RMS normalisation of the ladder's node features (4096
     # nodes, 128 channels, ranks <= 3): forward, and VJP with both gradients
     if not only_conv:

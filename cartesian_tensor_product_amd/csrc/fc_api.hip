@@ -14,6 +14,7 @@
 #include "fc_block.h"
 #include "fc_ladder.h"
 #include "fc_norm.h"
+#include "fc_radial.h"
 
 namespace {
 
@@ -121,6 +122,42 @@ fc::ConvArgs make_args(const fc_conv_desc* d, const fc_graph* g, const float* po
   return a;
 }
 
+
+// Workspace of the convolution weighted by the radial network: (op 1) the
+// convolution's VJP workspace, then h2 [64][E], w [E][P C], (op 1) w_bar
+// [E][P C], the per-edge position terms [E][3] and the radial VJP scratch.
+struct MlpWorkspace {
+  size_t conv_bytes;
+  float *h2t, *w, *wbar, *q, *scratch;
+  size_t bytes;
+  MlpWorkspace(const fc_conv_desc* d, int op, void* base) {
+    int P, nin, nout;
+    layout(d, &P, &nin, &nout);
+    const size_t E = d->n_edges, PC = (size_t)P * d->channels;
+    conv_bytes = op == 1 ? fc::VjpWorkspace(d->n_nodes, d->n_edges, d->channels, nin, P, false, nullptr).bytes : 0;
+    char* p = static_cast<char*>(base);
+    size_t off = conv_bytes;
+    auto take = [&](size_t floats) {
+      float* r = reinterpret_cast<float*>(p + off);
+      off += fc::align256(floats * sizeof(float));
+      return r;
+    };
+    h2t = take(E * fc::kRadHidden);
+    w = take(E * PC);
+    wbar = op == 1 ? take(E * PC) : nullptr;
+    q = op == 1 ? take(E * 3) : nullptr;
+    scratch = op == 1 ? take(fc::radial_vjp_scratch_floats(d->n_edges, P, d->channels)) : nullptr;
+    bytes = off;
+  }
+};
+
+fc::RadialArgs radial_args(const fc_conv_desc* d, const fc_graph* g, const float* pos, const float* shift,
+                           const float* mlp_w) {
+  int P, nin, nout;
+  layout(d, &P, &nin, &nout);
+  return fc::RadialArgs{d->n_nodes, d->n_edges, P, d->channels, d->r_cut, g->rowptr, g->sender, g->receiver,
+                        g->t_rowptr, g->t_edge, pos, shift, mlp_w};
+}
 
 fc_status check_norm(const fc_norm_desc* d) {
   if (!d) return fail(FC_ERR_INVALID_ARGUMENT, "norm descriptor is NULL");
@@ -628,6 +665,89 @@ fc_status fc_rms_norm_vjp(const fc_norm_desc* d, const float* x, const float* ga
   fc::launch_rms_norm_vjp(d->l_max, d->n_nodes, d->channels, x, gamma, inv_scale, g_y, x_grad,
                           gamma_grad ? static_cast<float*>(workspace) : nullptr, gamma_grad, stream);
   return check_launch("RMS norm VJP");
+}
+
+size_t fc_radial_mlp_weight_floats(const fc_conv_desc* d) {
+  if (check_desc(d) != FC_OK) return 0;
+  int P, nin, nout;
+  layout(d, &P, &nin, &nout);
+  return fc::radial_weight_floats(P, d->channels);
+}
+
+size_t fc_edge_conv_mlp_workspace_bytes(const fc_conv_desc* d, int32_t op) {
+  if (check_desc(d) != FC_OK || (op != 0 && op != 1)) return 0;
+  return MlpWorkspace(d, op, nullptr).bytes;
+}
+
+fc_status fc_radial_mlp(const fc_conv_desc* d, const fc_graph* g, const float* pos, const float* shift,
+                        const float* mlp_w, float* w, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (fc_status s = check_desc(d)) return s;
+  if (!g || (d->n_edges > 0 && (!g->sender || !g->receiver)))
+    return fail(FC_ERR_INVALID_ARGUMENT, "radial MLP needs graph sender and receiver");
+  if (!pos || !mlp_w || (d->n_edges > 0 && !w))
+    return fail(FC_ERR_INVALID_ARGUMENT, "radial MLP: NULL pos, mlp_w or w");
+  if (misaligned(pos, 4) || misaligned(shift, 4) || misaligned(mlp_w, 4) || misaligned(w, 4))
+    return fail(FC_ERR_INVALID_ARGUMENT, "radial MLP: arrays must be 4-byte aligned");
+  const MlpWorkspace ws(d, 0, workspace);
+  if (!workspace || workspace_bytes < ws.bytes)
+    return fail(FC_ERR_WORKSPACE, "radial MLP needs %zu workspace bytes", ws.bytes);
+  const fc::RadialArgs ra = radial_args(d, g, pos, shift, mlp_w);
+  fc::launch_radial_hidden(ra, ws.h2t, stream);
+  fc::launch_radial_out(ra, ws.h2t, w, stream);
+  return check_launch("radial MLP");
+}
+
+fc_status fc_edge_conv_mlp_fwd(const fc_conv_desc* d, const fc_graph* g, const float* pos, const float* shift,
+                               const float* x, const float* mlp_w, float* z, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  if (fc_status s = check_desc(d)) return s;
+  if (!g || !g->rowptr || (d->n_edges > 0 && (!g->sender || !g->receiver)))
+    return fail(FC_ERR_INVALID_ARGUMENT, "MLP-weighted forward needs graph rowptr, sender and receiver");
+  if (!pos || !x || !mlp_w || !z) return fail(FC_ERR_INVALID_ARGUMENT, "MLP-weighted forward: NULL pos, x, mlp_w or z");
+  if (misaligned(pos, 4) || misaligned(shift, 4) || misaligned(x, 4) || misaligned(mlp_w, 4) || misaligned(z, 4))
+    return fail(FC_ERR_INVALID_ARGUMENT, "MLP-weighted forward: arrays must be 4-byte aligned");
+  const MlpWorkspace ws(d, 0, workspace);
+  if (!workspace || workspace_bytes < ws.bytes)
+    return fail(FC_ERR_WORKSPACE, "MLP-weighted forward needs %zu workspace bytes", ws.bytes);
+  const fc::RadialArgs ra = radial_args(d, g, pos, shift, mlp_w);
+  fc::launch_radial_hidden(ra, ws.h2t, stream);
+  fc::launch_radial_out(ra, ws.h2t, ws.w, stream);
+  fc::ConvArgs a = make_args(d, g, pos, shift, x, nullptr);
+  a.w_edge = d->n_edges > 0 ? ws.w : x;   // never read without edges
+  a.z = z;
+  fc::conv_dispatch(0, d->l_in, d->l_edge, lout_key(d), a, stream);
+  return check_launch("MLP-weighted edge conv forward");
+}
+
+fc_status fc_edge_conv_mlp_vjp(const fc_conv_desc* d, const fc_graph* g, const float* pos, const float* shift,
+                               const float* x, const float* mlp_w, const float* g_z, float* x_grad, float* pos_grad,
+                               float* mlp_w_grad, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (fc_status s = check_desc(d)) return s;
+  if (!g || !g->rowptr || !g->t_rowptr || (d->n_edges > 0 && (!g->sender || !g->receiver || !g->t_edge)))
+    return fail(FC_ERR_INVALID_ARGUMENT, "MLP-weighted VJP needs the full graph (run fc_graph_transpose first)");
+  if (!pos || !x || !mlp_w || !g_z)
+    return fail(FC_ERR_INVALID_ARGUMENT, "MLP-weighted VJP: NULL pos, x, mlp_w or g_z");
+  if (!x_grad && !pos_grad && !mlp_w_grad) return fail(FC_ERR_INVALID_ARGUMENT, "MLP-weighted VJP: no output requested");
+  if (misaligned(pos, 4) || misaligned(shift, 4) || misaligned(x, 4) || misaligned(mlp_w, 4) || misaligned(g_z, 4) ||
+      misaligned(x_grad, 4) || misaligned(pos_grad, 4) || misaligned(mlp_w_grad, 4))
+    return fail(FC_ERR_INVALID_ARGUMENT, "MLP-weighted VJP: arrays must be 4-byte aligned");
+  const MlpWorkspace ws(d, 1, workspace);
+  if (!workspace || workspace_bytes < ws.bytes)
+    return fail(FC_ERR_WORKSPACE, "MLP-weighted VJP needs %zu workspace bytes", ws.bytes);
+  const fc::RadialArgs ra = radial_args(d, g, pos, shift, mlp_w);
+  const bool radial = pos_grad || mlp_w_grad;
+  fc::launch_radial_hidden(ra, ws.h2t, stream);
+  fc::launch_radial_out(ra, ws.h2t, ws.w, stream);
+  fc::ConvArgs a = make_args(d, g, pos, shift, x, nullptr);
+  a.w_edge = d->n_edges > 0 ? ws.w : x;
+  a.w_edge_bar = (radial && d->n_edges > 0) ? ws.wbar : nullptr;
+  a.g = g_z;
+  a.x_bar = x_grad;
+  a.pos_bar = pos_grad;
+  a.rbar = static_cast<float*>(workspace);
+  if (x_grad || pos_grad || a.w_edge_bar) fc::conv_dispatch(1, d->l_in, d->l_edge, lout_key(d), a, stream);
+  if (radial) fc::launch_radial_vjp(ra, ws.h2t, ws.wbar, ws.q, pos_grad, mlp_w_grad, ws.scratch, stream);
+  return check_launch("MLP-weighted edge conv VJP");
 }
 
 }  // extern "C"

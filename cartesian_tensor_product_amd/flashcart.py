@@ -80,6 +80,11 @@ _SIGS = {
     "fc_node_ladder_fwd": (_I, [_PL, _P, _P, _P, _P, _P, _SZ, _P]),
     "fc_node_ladder_vjp": (_I, [_PL, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "fc_node_ladder_vjp_vjp": (_I, [_PL, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "fc_radial_mlp_weight_floats": (_SZ, [_PD]),
+    "fc_edge_conv_mlp_workspace_bytes": (_SZ, [_PD, _I]),
+    "fc_radial_mlp": (_I, [_PD, _PG, _P, _P, _P, _P, _P, _SZ, _P]),
+    "fc_edge_conv_mlp_fwd": (_I, [_PD, _PG, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "fc_edge_conv_mlp_vjp": (_I, [_PD, _PG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "fc_rms_norm_fwd": (_I, [_PN, _P, _P, _P, _P, _P]),
     "fc_rms_norm_workspace_bytes": (_SZ, [_PN]),
     "fc_rms_norm_vjp": (_I, [_PN, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -303,6 +308,36 @@ def fc_node_ladder_vjp(d: LadderDesc, A, weights, saved, g_z, A_grad, weights_gr
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().fc_node_ladder_vjp(ctypes.byref(d), _f32(A), _f32(weights), _f32(saved), _f32(g_z),
                                     _f32(A_grad), _f32(weights_grad), _ptr(workspace), nbytes, _stream(stream)))
+
+
+# ------------------------------------------------------------------ radial --
+
+def fc_radial_mlp_weight_floats(d: ConvDesc) -> int:
+    return lib().fc_radial_mlp_weight_floats(ctypes.byref(d))
+
+
+def fc_edge_conv_mlp_workspace_bytes(d: ConvDesc, op: int) -> int:
+    return lib().fc_edge_conv_mlp_workspace_bytes(ctypes.byref(d), op)
+
+
+def fc_radial_mlp(d: ConvDesc, graph: DeviceGraph, pos, shift, mlp_w, w, workspace, stream=None):
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().fc_radial_mlp(ctypes.byref(d), ctypes.byref(graph.struct), _f32(pos), _f32(shift), _f32(mlp_w),
+                               _f32(w), _ptr(workspace), nbytes, _stream(stream)))
+
+
+def fc_edge_conv_mlp_fwd(d: ConvDesc, graph: DeviceGraph, pos, shift, x, mlp_w, z, workspace, stream=None):
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().fc_edge_conv_mlp_fwd(ctypes.byref(d), ctypes.byref(graph.struct), _f32(pos), _f32(shift), _f32(x),
+                                      _f32(mlp_w), _f32(z), _ptr(workspace), nbytes, _stream(stream)))
+
+
+def fc_edge_conv_mlp_vjp(d: ConvDesc, graph: DeviceGraph, pos, shift, x, mlp_w, g_z, x_grad, pos_grad, mlp_w_grad,
+                         workspace, stream=None):
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().fc_edge_conv_mlp_vjp(ctypes.byref(d), ctypes.byref(graph.struct), _f32(pos), _f32(shift), _f32(x),
+                                      _f32(mlp_w), _f32(g_z), _f32(x_grad), _f32(pos_grad), _f32(mlp_w_grad),
+                                      _ptr(workspace), nbytes, _stream(stream)))
 
 
 # -------------------------------------------------------------------- norm --

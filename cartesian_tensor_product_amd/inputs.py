@@ -204,3 +204,12 @@ def diamond_inputs(channels: int = 128, r_cut: float = 5.0, rattle: float = 0.0,
     x = np.ascontiguousarray(np.broadcast_to(emb, (pos.shape[0], 1, channels)))
     return dict(pos=pos, box=box, rowptr=rowptr, sender=sender, shift=shift,
                 x=x, W=W, ladder_weights=ws)
+
+
+def radial_mlp_weights(rng, n_paths: int, channels: int) -> np.ndarray:
+    """Flat weights of the radial network, W1 [8, 64] ~ N(0, 1/8), then
+    W2 [64, 64] and W3 [64, P C] ~ N(0, 1/64) (variance 1/fan_in)."""
+    W1 = normal(rng, (8, 64), std=1.0 / np.sqrt(8))
+    W2 = normal(rng, (64, 64), std=1.0 / 8.0)
+    W3 = normal(rng, (64, n_paths * channels), std=1.0 / 8.0)
+    return np.concatenate([W1.ravel(), W2.ravel(), W3.ravel()])

@@ -209,6 +209,43 @@ fc_status fc_edge_conv_vjp_vjp(const fc_conv_desc* d, const fc_graph* g, const f
                                size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * The pages' radial network (App. E "Model architecture", the weights
+ * w_{eta k}(r) of Eq. E1; App. F "Model architecture and training"):
+ *   phi_n(r) = T_n(cos(pi r / r_cut)) u(r / r_cut), n = 0..7, with the p = 6
+ *   envelope u(d) = 1 - 28 d^6 + 48 d^7 - 21 d^8 (0 for d >= 1; value and
+ *   first two derivatives vanish at d = 1; the pages fix the property, this
+ *   polynomial is the reading),
+ *   w[e, eta, k] = (SiLU(SiLU(phi(r_e) W1) W2) W3)[eta C + k], bias-free.
+ * Flat weights mlp_w: W1 [8][64], W2 [64][64], W3 [64][P][C]
+ * (fc_radial_mlp_weight_floats(d) floats).  r_cut of d is r_max; n_basis
+ * must be 8 (the Chebyshev count).  An edge of zero length gets w = 0.
+ * ---------------------------------------------------------------------- */
+size_t fc_radial_mlp_weight_floats(const fc_conv_desc* d);
+/* Workspace of the calls below: op 0 forward (and fc_radial_mlp), op 1 VJP. */
+size_t fc_edge_conv_mlp_workspace_bytes(const fc_conv_desc* d, int32_t op);
+
+/* w [E][P][C] (receiver-sorted edges): the per-edge weights alone, for
+ * fc_edge_conv_fwd_w.  Needs sender and receiver of g. */
+fc_status fc_radial_mlp(const fc_conv_desc* d, const fc_graph* g, const float* pos,
+                        const float* shift, const float* mlp_w, float* w, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
+/* Eq. 1 / E1 with w from the radial network: z [N][out_rows][C].  Needs
+ * rowptr, sender and receiver of g. */
+fc_status fc_edge_conv_mlp_fwd(const fc_conv_desc* d, const fc_graph* g, const float* pos,
+                               const float* shift, const float* x, const float* mlp_w, float* z,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* VJP of L = <g_z, z> through the convolution and the radial network:
+ * x_grad [N][in_rows][C], pos_grad [N][3] (through the direction tensors
+ * and through w(r)), mlp_w_grad (flat, as mlp_w); each when non-NULL, at
+ * least one.  Needs the full graph. */
+fc_status fc_edge_conv_mlp_vjp(const fc_conv_desc* d, const fc_graph* g, const float* pos,
+                               const float* shift, const float* x, const float* mlp_w,
+                               const float* g_z, float* x_grad, float* pos_grad, float* mlp_w_grad,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Node-local correlation ladder (§5 Eq. 2; App. E "Path-reduced products").
  * A [N][(l_a+1)^2][C]; z [N][(l_out+1)^2][C].  Steps q = 1..order; the
  * product at step q >= 2 couples phi^{q-1} (ranks <= l_{q-1}) with A (ranks

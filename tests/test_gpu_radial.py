@@ -1,0 +1,128 @@
+"""GPU parity of the pages' radial network (Chebyshev features, envelope,
+bias-free SiLU MLP with an MFMA output layer) and of the convolution it
+weights (forward; VJP to features, positions and the network's weights)
+against the oracle."""
+import numpy as np
+import pytest
+
+from cartesian_tensor_product_amd import inputs
+from oracle import conv, radial
+from tests.gpu_common import assert_close, f64, sample_edges
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def split(flat, P, C):
+    W1 = flat[:512].reshape(8, 64)
+    W2 = flat[512:512 + 4096].reshape(64, 64)
+    W3 = flat[512 + 4096:].reshape(64, P * C)
+    return W1, W2, W3
+
+
+class GpuMlpConv:
+    def __init__(self, ranks, d, C, rc, mlp):
+        from cartesian_tensor_product_amd import flashcart as fc
+        self.fc = fc
+        self.N, self.E, self.C = d["pos"].shape[0], int(len(d["sender"])), C
+        self.desc = fc.conv_desc(self.N, self.E, C, *ranks, rc)
+        self.P, self.nin, self.nout = fc.fc_conv_layout(self.desc)
+        assert fc.fc_radial_mlp_weight_floats(self.desc) == mlp.size
+        self.graph = fc.DeviceGraph(d["rowptr"], d["sender"], self.N, device="cuda")
+        t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        self.pos, self.shift, self.x, self.g, self.mlp = t(d["pos"]), t(d.get("shift")), t(d["x"]), t(d["g"]), t(mlp)
+
+    def weights(self):
+        w = torch.empty((self.E, self.P, self.C), device="cuda")
+        ws = self.fc.workspace(self.fc.fc_edge_conv_mlp_workspace_bytes(self.desc, 0), "cuda")
+        self.fc.fc_radial_mlp(self.desc, self.graph, self.pos, self.shift, self.mlp, w, ws)
+        return w
+
+    def fwd(self):
+        z = torch.empty((self.N, self.nout, self.C), device="cuda")
+        ws = self.fc.workspace(self.fc.fc_edge_conv_mlp_workspace_bytes(self.desc, 0), "cuda")
+        self.fc.fc_edge_conv_mlp_fwd(self.desc, self.graph, self.pos, self.shift, self.x, self.mlp, z, ws)
+        return z
+
+    def vjp(self, want=("x", "pos", "w")):
+        xb = torch.empty_like(self.x) if "x" in want else None
+        pb = torch.empty((self.N, 3), device="cuda") if "pos" in want else None
+        wb = torch.empty_like(self.mlp) if "w" in want else None
+        ws = self.fc.workspace(self.fc.fc_edge_conv_mlp_workspace_bytes(self.desc, 1), "cuda")
+        self.fc.fc_edge_conv_mlp_vjp(self.desc, self.graph, self.pos, self.shift, self.x, self.mlp, self.g, xb, pb,
+                                     wb, ws)
+        return xb, pb, wb
+
+
+def setup(ranks, C, seed, n=40, k=12, box=5.0, rc=5.0):
+    spec = conv.ConvSpec(*ranks, rc)
+    d = inputs.edge_conv_inputs(seed, n, k, box, C, spec.n_in, spec.n_paths, spec.n_out)
+    mlp = inputs.radial_mlp_weights(np.random.default_rng(seed + 50), spec.n_paths, C)
+    return spec, d, mlp
+
+
+@pytest.mark.parametrize("ranks", [(1, 1, 1), (2, 2, 2), (0, 3, 3), (3, 3, 3)])
+def test_mlp_conv_full(ranks):
+    spec, d, mlp = setup(ranks, 40, 31)
+    gc = GpuMlpConv(ranks, d, 40, 5.0, mlp)
+    w = gc.weights()
+    z = gc.fwd()
+    xb, pb, wb = gc.vjp()
+    torch.cuda.synchronize()
+    W1, W2, W3 = split(f64(mlp), spec.n_paths, 40)
+    r, _ = radial.edge_lengths(f64(d["pos"]), d["rowptr"], d["sender"])
+    assert_close("w", w.cpu().numpy(), radial.radial_mlp(r, 5.0, W1, W2, W3, spec.n_paths, 40))
+    args = (spec, f64(d["pos"]), d["rowptr"], d["sender"], f64(d["x"]), W1, W2, W3)
+    assert_close("z", z.cpu().numpy(), radial.edge_conv_fwd_mlp(*args))
+    xo, po, W1b, W2b, W3b = radial.edge_conv_vjp_mlp(*args, f64(d["g"]))
+    assert_close("x_grad", xb.cpu().numpy(), xo)
+    assert_close("pos_grad", pb.cpu().numpy(), po)
+    wo = np.concatenate([W1b.ravel(), W2b.ravel(), W3b.ravel()])
+    assert_close("mlp_w_grad", wb.cpu().numpy(), wo)
+
+
+def test_mlp_conv_single_outputs_and_channel_tail():
+    spec, d, mlp = setup((2, 2, 2), 65, 32, n=30, k=9)
+    gc = GpuMlpConv((2, 2, 2), d, 65, 5.0, mlp)
+    W1, W2, W3 = split(f64(mlp), spec.n_paths, 65)
+    xo, po, W1b, W2b, W3b = radial.edge_conv_vjp_mlp(spec, f64(d["pos"]), d["rowptr"], d["sender"], f64(d["x"]), W1,
+                                                     W2, W3, f64(d["g"]))
+    for want, ref in ((("x",), xo), (("pos",), po), (("w",), np.concatenate([W1b.ravel(), W2b.ravel(), W3b.ravel()]))):
+        out = gc.vjp(want)
+        torch.cuda.synchronize()
+        got = out[("x", "pos", "w").index(want[0])]
+        assert_close(want[0], got.cpu().numpy(), ref)
+
+
+def subgraph(rowptr, sender, edges):
+    """The receiver-sorted graph of the given (sorted) edge ids over the same nodes."""
+    recv = np.repeat(np.arange(len(rowptr) - 1), np.diff(rowptr))
+    counts = np.bincount(recv[edges], minlength=len(rowptr) - 1)
+    return np.concatenate([[0], np.cumsum(counts)]).astype(rowptr.dtype), sender[edges]
+
+
+def test_mlp_conv_microbenchmark_sampled():
+    """1024 nodes x 128 neighbours x 128 channels, rank 2, r_max 5 A: the
+    weights of 2000 sampled edges; z, x_grad and pos_grad on 8 sampled nodes
+    (the oracle runs on the edges touching them, which is all these outputs
+    read); translation invariance of the forces at full size."""
+    spec, d, mlp = setup((2, 2, 2), 128, 1, n=1024, k=128, box=20.0, rc=5.0)
+    gc = GpuMlpConv((2, 2, 2), d, 128, 5.0, mlp)
+    w = gc.weights()
+    z = gc.fwd()
+    xb, pb, _ = gc.vjp(("x", "pos"))
+    torch.cuda.synchronize()
+    W1, W2, W3 = split(f64(mlp), spec.n_paths, 128)
+    r, _ = radial.edge_lengths(f64(d["pos"]), d["rowptr"], d["sender"])
+    es = np.random.default_rng(3).choice(len(r), size=2000, replace=False)
+    assert_close("w", w.cpu().numpy()[es], radial.radial_mlp(r[es], 5.0, W1, W2, W3, spec.n_paths, 128))
+    nodes = np.random.default_rng(4).choice(1024, size=8, replace=False)
+    rp, sd = subgraph(d["rowptr"], d["sender"], sample_edges(d["rowptr"], d["sender"], nodes))
+    args = (spec, f64(d["pos"]), rp, sd, f64(d["x"]), W1, W2, W3)
+    zo = radial.edge_conv_fwd_mlp(*args)
+    xo, po, _, _, _ = radial.edge_conv_vjp_mlp(*args, f64(d["g"]))
+    assert_close("z", z.cpu().numpy()[nodes], zo[nodes])
+    assert_close("x_grad", xb.cpu().numpy()[nodes], xo[nodes])
+    assert_close("pos_grad", pb.cpu().numpy()[nodes], po[nodes])
+    p = pb.double().cpu().numpy()
+    assert np.abs(p.sum(0)).max() < 1e-4 * np.abs(p).max() * np.sqrt(1024)

@@ -213,3 +213,22 @@ def radial_mlp_weights(rng, n_paths: int, channels: int) -> np.ndarray:
     W2 = normal(rng, (64, 64), std=1.0 / 8.0)
     W3 = normal(rng, (64, n_paths * channels), std=1.0 / 8.0)
     return np.concatenate([W1.ravel(), W2.ravel(), W3.ravel()])
+
+
+def block_weights(seed: int, entries: list) -> dict:
+    """Random weights of a message-passing block, drawn in the listed order
+    from one generator: ``entries`` holds (name, shape, kind, fan_in) with
+    kind 'normal' (N(0, 1/fan_in)), 'one_plus' (1 + 0.1 N(0,1)) or 'mlp' (the
+    radial network's flat weights; shape = (n_paths, channels))."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    for name, shape, kind, fan_in in entries:
+        if kind == "normal":
+            out[name] = normal(rng, shape, std=1.0 / np.sqrt(fan_in))
+        elif kind == "one_plus":
+            out[name] = f32(1.0 + 0.1 * rng.standard_normal(shape))
+        elif kind == "mlp":
+            out[name] = radial_mlp_weights(rng, shape[0], shape[1])
+        else:
+            raise ValueError(kind)
+    return out

@@ -15,6 +15,8 @@
 #include "fc_ladder.h"
 #include "fc_norm.h"
 #include "fc_radial.h"
+#include "fc_model.h"
+#include "fc_gemm.h"
 
 namespace {
 
@@ -589,6 +591,81 @@ fc_status block_layout(const fc_conv_desc* cd, const fc_ladder_desc* ld, BlockLa
   return FC_OK;
 }
 
+// A full message-passing block: flat weight offsets (floats) and workspace
+// (bytes), in the order
+//   radial network | M [l+1][C][C] | R0 [C][C] | gamma1 [l+1][C] |
+//   O [l+1][C][C] | ladder | R2 [C][C] | gamma2 [C] | Wr1 [C][64] |
+//   Wr2 [64][64] | wr3 [64]
+struct MsgLayout {
+  size_t w_mlp, w_M, w_R0, w_g1, w_O, w_lad, w_R2, w_g2, w_r1, w_r2, w_r3, n_weights;
+  size_t a, m, n, y, A, Ab, nb, mb, z, f, fb, ob, inv1, inv2, ea, saved, lws, cws, cws_bytes, parts, total;
+};
+
+fc_status msg_layout(const fc_conv_desc* cd, const fc_ladder_desc* ld, MsgLayout* L) {
+  if (fc_status s = check_desc(cd)) return s;
+  fc::LadderPlan p;
+  if (fc_status s = ladder_plan(ld, &p)) return s;
+  if (cd->l_in != 0 || cd->l_edge != cd->l_out || cd->flags != 0)
+    return fail(FC_ERR_UNSUPPORTED, "message block: the convolution needs scalar senders, l_edge == l_out, flags 0");
+  if (ld->l_a != cd->l_out || ld->l_out != 0 || ld->channels != cd->channels || ld->n_nodes != cd->n_nodes)
+    return fail(FC_ERR_INVALID_ARGUMENT,
+                "message block: ladder l_a must equal the conv l_out, ladder l_out 0, equal channels and nodes");
+  const size_t N = cd->n_nodes, C = cd->channels, le = cd->l_edge, R = (le + 1) * (le + 1);
+  const size_t C2 = C * C, H = fc::kReadoutHidden;
+  size_t o = 0;
+  L->w_mlp = o; o += fc::radial_weight_floats((int)le + 1, (int)C);
+  L->w_M = o;   o += (le + 1) * C2;
+  L->w_R0 = o;  o += C2;
+  L->w_g1 = o;  o += (le + 1) * C;
+  L->w_O = o;   o += (le + 1) * C2;
+  L->w_lad = o; o += p.weight_floats();
+  L->w_R2 = o;  o += C2;
+  L->w_g2 = o;  o += C;
+  L->w_r1 = o;  o += C * H;
+  L->w_r2 = o;  o += H * H;
+  L->w_r3 = o;  o += H;
+  L->n_weights = o;
+  auto al = [](size_t floats) { return (floats * 4 + 255) / 256 * 256; };
+  o = 0;
+  size_t* big[] = {&L->a, &L->m, &L->n, &L->y, &L->A, &L->Ab, &L->nb, &L->mb};
+  for (size_t* b : big) { *b = o; o += al(N * R * C); }
+  size_t* small[] = {&L->z, &L->f, &L->fb, &L->ob};
+  for (size_t* b : small) { *b = o; o += al(N * C); }
+  L->inv1 = o;  o += al(N);
+  L->inv2 = o;  o += al(N);
+  L->ea = o;    o += al(N);
+  L->saved = o; o += al(p.saved_floats());
+  L->lws = o;   o += al(std::max(p.fwd_ws_floats(), p.vjp_ws_floats()));
+  L->cws_bytes = std::max(fc_edge_conv_mlp_workspace_bytes(cd, 0), fc_edge_conv_mlp_workspace_bytes(cd, 1));
+  L->cws = o;   o += (L->cws_bytes + 255) / 256 * 256;
+  L->parts = o; o += (size_t)fc::block_energy_parts(cd->n_nodes) * 8;
+  L->total = o;
+  return FC_OK;
+}
+
+// Rank block l of [N][rows][C] as a GEMM view / output, and a [out][in]
+// channel matrix applied to it (y = M x) or its transpose (x_bar = M^T y_bar).
+fc::GView rank_view(const float* base, int rows, int l, int C) {
+  return fc::GView{base + (size_t)l * l * C, 2 * l + 1, (long long)rows * C, (long long)C, 1, 1, 0, 0, 0};
+}
+fc::GOut rank_out(float* base, int rows, int l, int C, int acc) {
+  return fc::GOut{base + (size_t)l * l * C, 2 * l + 1, (long long)rows * C, (long long)C, acc, 0};
+}
+fc::GemmProblem channel_map(int N, int C, const float* X, int xrows, int l, const float* Mat, bool transpose,
+                            float* Y, int yrows, int yl, int acc) {
+  fc::GemmProblem p{};
+  p.M = N * (2 * l + 1);
+  p.N = C;
+  p.K = C;
+  p.alpha = 1.f;
+  p.A = rank_view(X, xrows, l, C);
+  p.Bt = transpose ? fc::plain_view_t(Mat, C) : fc::plain_view(Mat, C);
+  p.C = rank_out(Y, yrows, yl, C, acc);
+  p.C2 = fc::no_out();
+  p.ksplit = 1;
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -748,6 +825,104 @@ fc_status fc_edge_conv_mlp_vjp(const fc_conv_desc* d, const fc_graph* g, const f
   if (x_grad || pos_grad || a.w_edge_bar) fc::conv_dispatch(1, d->l_in, d->l_edge, lout_key(d), a, stream);
   if (radial) fc::launch_radial_vjp(ra, ws.h2t, ws.wbar, ws.q, pos_grad, mlp_w_grad, ws.scratch, stream);
   return check_launch("MLP-weighted edge conv VJP");
+}
+
+size_t fc_message_block_weight_floats(const fc_conv_desc* conv, const fc_ladder_desc* lad) {
+  MsgLayout L;
+  return msg_layout(conv, lad, &L) == FC_OK ? L.n_weights : 0;
+}
+
+size_t fc_message_block_workspace_bytes(const fc_conv_desc* conv, const fc_ladder_desc* lad) {
+  MsgLayout L;
+  return msg_layout(conv, lad, &L) == FC_OK ? L.total : 0;
+}
+
+fc_status fc_message_block_energy_forces(const fc_conv_desc* cd, const fc_graph* g, const float* pos,
+                                         const float* shift, const float* h0, const fc_ladder_desc* ld,
+                                         const float* weights, float conv_scale, float eps, double* energy,
+                                         float* e_atom, float* forces, void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream) {
+  MsgLayout L;
+  if (fc_status s = msg_layout(cd, ld, &L)) return s;
+  if (!g || !energy || !weights || !h0 || !pos)
+    return fail(FC_ERR_INVALID_ARGUMENT, "message block: NULL graph, input or energy");
+  if (!(eps >= 0.f) || !std::isfinite(eps) || !std::isfinite(conv_scale))
+    return fail(FC_ERR_INVALID_ARGUMENT, "message block: eps must be >= 0 and finite");
+  if (misaligned(pos, 4) || misaligned(shift, 4) || misaligned(h0, 4) || misaligned(weights, 4) ||
+      misaligned(e_atom, 4) || misaligned(forces, 4) || misaligned(energy, 8))
+    return fail(FC_ERR_INVALID_ARGUMENT, "message block: misaligned array");
+  if (!workspace || workspace_bytes < L.total)
+    return fail(FC_ERR_WORKSPACE, "message block needs %zu workspace bytes", L.total);
+  if (forces && (!g->t_rowptr || (cd->n_edges > 0 && (!g->receiver || !g->t_edge))))
+    return fail(FC_ERR_INVALID_ARGUMENT, "message block: forces need the full graph (run fc_graph_transpose first)");
+  char* wb = static_cast<char*>(workspace);
+  auto buf = [&](size_t off) { return reinterpret_cast<float*>(wb + off); };
+  float *a = buf(L.a), *m = buf(L.m), *n = buf(L.n), *y = buf(L.y), *A = buf(L.A), *Ab = buf(L.Ab);
+  float *nb = buf(L.nb), *mb = buf(L.mb), *z = buf(L.z), *f = buf(L.f), *fb = buf(L.fb), *ob = buf(L.ob);
+  float *inv1 = buf(L.inv1), *inv2 = buf(L.inv2), *ea = buf(L.ea), *saved = buf(L.saved), *lws = buf(L.lws);
+  double* parts = reinterpret_cast<double*>(wb + L.parts);
+  const float* W = weights;
+  fc::LadderPlan p;
+  ladder_plan(ld, &p);
+  const int N = cd->n_nodes, C = cd->channels, le = cd->l_edge, R = (le + 1) * (le + 1);
+  const float* lw = W + L.w_lad;
+  auto chan = [&](const float* M, int l) { return M + (size_t)l * C * C; };
+
+  // ---- forward
+  if (fc_status s = fc_edge_conv_mlp_fwd(cd, g, pos, shift, h0, W + L.w_mlp, a, wb + L.cws, L.cws_bytes, stream))
+    return s;
+  fc::block_scale(a, (size_t)N * R * C, conv_scale, stream);
+  {
+    fc::GemmGroup gg{};
+    for (int l = 0; l <= le; ++l) gg.prob[gg.count++] = channel_map(N, C, a, R, l, chan(W + L.w_M, l), false, m, R, l, 0);
+    fc::gemm_group(gg, stream);
+    fc::GemmGroup gr{};
+    gr.prob[gr.count++] = channel_map(N, C, h0, 1, 0, W + L.w_R0, false, m, R, 0, 1);
+    fc::gemm_group(gr, stream);
+  }
+  fc::launch_rms_norm_fwd(le, N, C, eps, m, W + L.w_g1, n, inv1, stream);
+  fc::launch_gate_fwd(N, C, le, n, y, A, stream);
+  {
+    fc::GemmGroup gg{};
+    for (int l = 0; l <= le; ++l) gg.prob[gg.count++] = channel_map(N, C, y, R, l, chan(W + L.w_O, l), false, A, R, l, 1);
+    fc::gemm_group(gg, stream);
+  }
+  fc::ladder_forward(p, A, lw, z, saved, lws, stream);
+  {  // o = z + R2 A_0 (in place in z)
+    fc::GemmGroup gg{};
+    gg.prob[gg.count++] = channel_map(N, C, A, R, 0, W + L.w_R2, false, z, 1, 0, 1);
+    fc::gemm_group(gg, stream);
+  }
+  fc::launch_rms_norm_fwd(0, N, C, eps, z, W + L.w_g2, f, inv2, stream);
+  fc::launch_readout_fwd(N, C, f, W + L.w_r1, W + L.w_r2, W + L.w_r3, ea, stream);
+  fc::block_energy(ea, N, 1, 1, e_atom, parts, energy, stream);
+  if (!forces) return check_launch("message block energy");
+
+  // ---- backward for the forces
+  fc::launch_readout_vjp(N, C, f, W + L.w_r1, W + L.w_r2, W + L.w_r3, fb, stream);
+  fc::launch_rms_norm_vjp(0, N, C, z, W + L.w_g2, inv2, fb, ob, nullptr, nullptr, stream);
+  fc::ladder_vjp(p, A, lw, saved, ob, Ab, nullptr, lws, stream);
+  {  // A_bar_0 += R2^T o_bar;  y_bar_l = O_l^T A_bar_l (into y)
+    fc::GemmGroup gg{};
+    gg.prob[gg.count++] = channel_map(N, C, ob, 1, 0, W + L.w_R2, true, Ab, R, 0, 1);
+    fc::gemm_group(gg, stream);
+    fc::GemmGroup gy{};
+    for (int l = 0; l <= le; ++l) gy.prob[gy.count++] = channel_map(N, C, Ab, R, l, chan(W + L.w_O, l), true, y, R, l, 0);
+    fc::gemm_group(gy, stream);
+  }
+  fc::launch_gate_vjp(N, C, le, n, Ab, y, nb, stream);
+  fc::launch_rms_norm_vjp(le, N, C, m, W + L.w_g1, inv1, nb, mb, nullptr, nullptr, stream);
+  {  // a_bar_l = M_l^T m_bar_l (into a), times the convolution scale
+    fc::GemmGroup gg{};
+    for (int l = 0; l <= le; ++l) gg.prob[gg.count++] = channel_map(N, C, mb, R, l, chan(W + L.w_M, l), true, a, R, l, 0);
+    fc::gemm_group(gg, stream);
+  }
+  fc::block_scale(a, (size_t)N * R * C, conv_scale, stream);
+  if (fc_status s = fc_edge_conv_mlp_vjp(cd, g, pos, shift, h0, W + L.w_mlp, a, nullptr, forces, nullptr, wb + L.cws,
+                                         L.cws_bytes, stream))
+    return s;
+  fc::block_scale(forces, (size_t)N * 3, -1.f, stream);
+  return check_launch("message block energy/forces");
 }
 
 }  // extern "C"

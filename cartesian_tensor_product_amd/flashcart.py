@@ -88,6 +88,10 @@ _SIGS = {
     "fc_rms_norm_fwd": (_I, [_PN, _P, _P, _P, _P, _P]),
     "fc_rms_norm_workspace_bytes": (_SZ, [_PN]),
     "fc_rms_norm_vjp": (_I, [_PN, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "fc_message_block_weight_floats": (_SZ, [_PD, _PL]),
+    "fc_message_block_workspace_bytes": (_SZ, [_PD, _PL]),
+    "fc_message_block_energy_forces": (_I, [_PD, _PG, _P, _P, _P, _PL, _P, ctypes.c_float, ctypes.c_float, _P, _P,
+                                            _P, _P, _SZ, _P]),
     "fc_block_workspace_bytes": (_SZ, [_PD, _PL]),
     "fc_block_energy_forces": (_I, [_PD, _PG, _P, _P, _P, _P, _PL, _P, ctypes.c_float, _P, _P, _P, _P, _SZ, _P]),
 }
@@ -384,3 +388,22 @@ def fc_block_energy_forces(conv: ConvDesc, graph: DeviceGraph, pos, shift, x, ra
 def workspace(nbytes: int, device="cuda"):
     import torch
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def fc_message_block_weight_floats(conv: ConvDesc, lad: LadderDesc) -> int:
+    return lib().fc_message_block_weight_floats(ctypes.byref(conv), ctypes.byref(lad))
+
+
+def fc_message_block_workspace_bytes(conv: ConvDesc, lad: LadderDesc) -> int:
+    return lib().fc_message_block_workspace_bytes(ctypes.byref(conv), ctypes.byref(lad))
+
+
+def fc_message_block_energy_forces(conv: ConvDesc, graph: DeviceGraph, pos, shift, h0, lad: LadderDesc, weights,
+                                   conv_scale: float, eps: float, energy, e_atom, forces, workspace, stream=None):
+    import torch
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().fc_message_block_energy_forces(ctypes.byref(conv), ctypes.byref(graph.struct), _f32(pos),
+                                                _f32(shift), _f32(h0), ctypes.byref(lad), _f32(weights),
+                                                ctypes.c_float(conv_scale), ctypes.c_float(eps),
+                                                _ptr(energy, torch.float64), _f32(e_atom), _f32(forces),
+                                                _ptr(workspace), nbytes, _stream(stream)))

@@ -334,6 +334,40 @@ fc_status fc_block_energy_forces(const fc_conv_desc* conv, const fc_graph* g, co
                                  size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * A full message-passing block for energy and forces (App. E "Model
+ * architecture"; App. F for the radial network, SiLU gates and the readout
+ * width), one final block with scalar senders in and scalars out, with the
+ * caller's (random) weights.  Readings where the pages leave a step open:
+ *   a   = conv_scale * conv(h0), weights from the radial network (Eq. E1);
+ *   m_l = M_l a_l (rank-wise map of the paths and channels; one path per
+ *         rank with scalar senders), m_0 += R0 h0 (residual update);
+ *   n   = RMSnorm(m; gamma1, eps) (fc_rms_norm_fwd);
+ *   y_0 = SiLU(n_0), y_l = SiLU(n_0) n_l (scalar SiLU gates);
+ *   A_l = n_l + O_l y_l (the output map added to the gated layer's input);
+ *   z   = ladder(A) with l_out = 0;  o = z + R2 A_0 (residual update);
+ *   f   = RMSnorm(o; gamma2, eps);  E_u = SiLU(SiLU(f Wr1) Wr2) . wr3
+ *         (bias-free readout MLP C -> 64 -> 64 -> 1);
+ *   E   = sum_u E_u (fp64, fixed order), forces = -dE/dpos.
+ * Matrices act on channels as [out][in].  Flat weights, in order: radial
+ * network (fc_radial_mlp_weight_floats layout, P = l_edge + 1), M
+ * [l+1][C][C], R0 [C][C], gamma1 [l+1][C], O [l+1][C][C], ladder weights
+ * (fc_ladder_layout), R2 [C][C], gamma2 [C], Wr1 [C][64], Wr2 [64][64],
+ * wr3 [64] (fc_message_block_weight_floats floats).  conv: l_in = 0,
+ * l_edge = l_out = l, flags 0; lad: l_a = l_prod = l, l_out = 0, equal
+ * nodes and channels.  h0 [N][1][C]; energy: DEVICE double[1]; e_atom
+ * DEVICE float[N] or NULL; forces DEVICE float[N][3] or NULL (then no
+ * backward pass; otherwise the full graph is needed).
+ * ---------------------------------------------------------------------- */
+size_t fc_message_block_weight_floats(const fc_conv_desc* conv, const fc_ladder_desc* lad);
+size_t fc_message_block_workspace_bytes(const fc_conv_desc* conv, const fc_ladder_desc* lad);
+fc_status fc_message_block_energy_forces(const fc_conv_desc* conv, const fc_graph* g,
+                                         const float* pos, const float* shift, const float* h0,
+                                         const fc_ladder_desc* lad, const float* weights,
+                                         float conv_scale, float eps, double* energy, float* e_atom,
+                                         float* forces, void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Equivariant RMS normalisation of node features (App. E "Model
  * architecture": scalar invariants from the generated (l,l)->0 couplings,
  * combined over ranks and channels into one scale per atom, no batch

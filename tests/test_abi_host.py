@@ -164,3 +164,17 @@ def test_ladder_vjp_vjp_workspace():
     st = 4096 * 16 * 128 * 4
     assert fc.fc_ladder_workspace_bytes(full, 2) >= 4 * 4096 * 99 * 128 * 4 + 7 * st
     assert fc.fc_ladder_workspace_bytes(red, 2) >= 4 * 4096 * 99 * 128 * 4 + 7 * st + 4 * st
+
+
+def test_message_block_weight_count_matches_oracle():
+    from oracle import conv, ladder, model
+    for order, var in ((3, "reduced"), (5, "full")):
+        cspec = conv.ConvSpec(0, 3, 3, 5.0)
+        lspec = ladder.LadderSpec(3, 3, 0, order, var, 32)
+        n = sum(int(np.prod(s)) for _, s in model.block_weight_shapes(32, 3, cspec.n_paths, lspec))
+        cd = fc.conv_desc(216, 1000, 32, 0, 3, 3, 5.0)
+        ld = fc.ladder_desc(216, 32, 3, 3, 0, order, fc.FC_LADDER_FULL if var == "full" else fc.FC_LADDER_PATH_REDUCED)
+        assert fc.fc_message_block_weight_floats(cd, ld) == n
+        assert fc.fc_message_block_workspace_bytes(cd, ld) > 0
+    bad = fc.ladder_desc(216, 32, 3, 3, 1, 3, fc.FC_LADDER_PATH_REDUCED)   # ladder l_out must be 0
+    assert fc.fc_message_block_weight_floats(fc.conv_desc(216, 1000, 32, 0, 3, 3, 5.0), bad) == 0

@@ -561,6 +561,7 @@ size_t LadderPlan::fwd_ws_floats() const {
 
 namespace {
 constexpr int kNTile = 16;          // nodes per block in the path-reduced reverse kernels
+constexpr int kMixTile = 2;         // nodes per wave in the path-weight gradient on a product buffer
 constexpr int kSplitTarget = 512;   // blocks per split-K weight-gradient GEMM
 }  // namespace
 
@@ -598,7 +599,7 @@ size_t LadderPlan::vv_ws_floats() const {
   const size_t C2 = (size_t)C * C;
   size_t b = 0, part = 0;
   if (variant == 1) {   // + S, S', S_bar, S_bar' and the path-weight partials
-    const int nblk = (N + kNTile - 1) / kNTile;
+    const int nblk = (N + kMixTile - 1) / kMixTile;
     int pmax = lq(1) + 1;
     for (int q = 2; q <= order; ++q) {
       b = std::max(b, (size_t)N * prod_rows(q) * C);
@@ -866,8 +867,8 @@ template <int LP, int LQ>
 struct MixWgrad {
   static void run(const LadderPlan& p, const float* X, int xrows, const float* B1, const float* Y, int yrows,
                   const float* B2, float* part, hipStream_t st) {
-    dim3 grid((p.N + kNTile - 1) / kNTile, (p.C + kWave - 1) / kWave);
-    hipLaunchKernelGGL((ladder_mix_wgrad_kernel<LP, LP, LQ>), grid, dim3(kWave), 0, st, p.N, p.C, kNTile, X, xrows,
+    dim3 grid((p.N + kMixTile - 1) / kMixTile, (p.C + kWave - 1) / kWave);
+    hipLaunchKernelGGL((ladder_mix_wgrad_kernel<LP, LP, LQ>), grid, dim3(kWave), 0, st, p.N, p.C, kMixTile, X, xrows,
                        B1, Y, yrows, B2, part);
   }
 };
@@ -1173,7 +1174,7 @@ void ladder_vjp_vjp_reduced(const LadderPlan& p, const float* A, const float* w,
       by_ranks<MixVjp>(p.lprod, p.lq(q), p, dG, grows, aq, vaq ? G : nullptr, grows, vaq, dBb, st);
     if (w_hat) {
       by_ranks<MixWgrad>(p.lprod, p.lq(q), p, dG, grows, (const float*)B, G, grows, (const float*)dB, part, st);
-      block_sum(nblk, p.paths(q) * C, part, w_hat + p.w_a(q), st);
+      block_sum((p.N + kMixTile - 1) / kMixTile, p.paths(q) * C, part, w_hat + p.w_a(q), st);
     }
     float* Gn = Gb[q % 2];
     float* dGn = dGb[q % 2];

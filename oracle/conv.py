@@ -64,7 +64,7 @@ def segment_sum(vals: np.ndarray, seg: np.ndarray, nseg: int) -> np.ndarray:
     """out[s] = sum of vals[e] over e with seg[e] = s (sparse incidence matmul)."""
     E = vals.shape[0]
     m = sp.csr_matrix((np.ones(E), (seg, np.arange(E))), shape=(nseg, E))
-    flat = vals.reshape(E, -1)
+    flat = vals.reshape(E, int(np.prod(vals.shape[1:])))
     if np.iscomplexobj(flat):
         out = (m @ flat.real) + 1j * (m @ flat.imag)
     else:

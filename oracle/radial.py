@@ -75,7 +75,7 @@ def radial_mlp_vjp(r, r_max: float, W1, W2, W3, w_bar):
     h1 = silu(a1)
     a2 = h1 @ W2
     h2 = silu(a2)
-    wb = w_bar.reshape(E, -1)
+    wb = w_bar.reshape(E, W3.shape[1])
     W3b = h2.T @ wb
     a2b = (wb @ W3.T) * silu_grad(a2)
     W2b = h1.T @ a2b

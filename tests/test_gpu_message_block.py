@@ -53,3 +53,33 @@ def test_message_block_perfect_cell_and_energy_only():
     _, _, Fr = gpu_block(*block_setup(C=C, rattle=0.05), C, 3, "reduced")
     assert np.abs(F).max() < 1e-3 * np.abs(Fr).max()
     assert np.ptp(ea) < 1e-4 * np.abs(ea).max()
+
+
+def test_message_block_without_edges():
+    """r_cut below the nearest-neighbour distance: no edge, so the block is
+    node-local (residual, norms, gates, ladder, readout of the embedding);
+    the energy matches the oracle and the forces are zero."""
+    from cartesian_tensor_product_amd import inputs
+    C = 32
+    cspec, lspec, w, d, entries = block_setup(C=C)
+    d = inputs.diamond_inputs(channels=C, r_cut=1.0, rattle=0.05, ncell=3, n_paths=cspec.n_paths)
+    assert len(d["sender"]) == 0
+    from cartesian_tensor_product_amd import flashcart as fc
+    N = d["pos"].shape[0]
+    cd = fc.conv_desc(N, 0, C, 0, 3, 3, 1.0)
+    ld = fc.ladder_desc(N, C, 3, 3, 0, 3, fc.FC_LADDER_PATH_REDUCED)
+    flat = np.concatenate([w[name].astype(np.float32).ravel() for name, *_ in entries])
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    graph = fc.DeviceGraph(d["rowptr"], d["sender"], N, device="cuda")
+    en = torch.zeros(1, dtype=torch.float64, device="cuda")
+    F = torch.empty((N, 3), device="cuda")
+    ws = fc.workspace(fc.fc_message_block_workspace_bytes(cd, ld), "cuda")
+    fc.fc_message_block_energy_forces(cd, graph, t(d["pos"]), t(d["shift"]), t(d["x"]), ld, t(flat), 1.0, 1e-5, en,
+                                      None, F, ws)
+    torch.cuda.synchronize()
+    from oracle import conv as cv
+    cs1 = cv.ConvSpec(0, 3, 3, 1.0)
+    Eo, eao, Fo = model.block_energy_forces(cs1, lspec, w, d["pos"].astype(np.float64), d["rowptr"], d["sender"],
+                                            d["shift"].astype(np.float64), d["x"].astype(np.float64), 1.0)
+    assert abs(float(en.item()) - Eo) <= 1e-4 * np.abs(eao).sum()
+    assert float(F.abs().max()) == 0.0 and np.abs(Fo).max() == 0.0

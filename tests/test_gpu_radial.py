@@ -126,3 +126,21 @@ def test_mlp_conv_microbenchmark_sampled():
     assert_close("pos_grad", pb.cpu().numpy()[nodes], po[nodes])
     p = pb.double().cpu().numpy()
     assert np.abs(p.sum(0)).max() < 1e-4 * np.abs(p).max() * np.sqrt(1024)
+
+
+def test_mlp_conv_without_edges():
+    """No edge: z and the gradients are zero (the network's weight gradient
+    included)."""
+    from cartesian_tensor_product_amd import flashcart as fc
+    spec = conv.ConvSpec(2, 2, 2, 5.0)
+    N, C = 6, 24
+    d = dict(pos=inputs.normal(np.random.default_rng(1), (N, 3)), rowptr=np.zeros(N + 1, np.int32),
+             sender=np.zeros(0, np.int32), x=inputs.normal(np.random.default_rng(2), (N, spec.n_in, C)),
+             g=inputs.normal(np.random.default_rng(3), (N, spec.n_out, C)))
+    mlp = inputs.radial_mlp_weights(np.random.default_rng(4), spec.n_paths, C)
+    gc = GpuMlpConv((2, 2, 2), d, C, 5.0, mlp)
+    z = gc.fwd()
+    xb, pb, wb = gc.vjp()
+    torch.cuda.synchronize()
+    for name, a in (("z", z), ("x_grad", xb), ("pos_grad", pb), ("mlp_w_grad", wb)):
+        assert float(a.abs().max()) == 0.0, name

@@ -21,6 +21,19 @@ namespace fc {
 // group (gathered features, their weighted copies, accumulated cotangents)
 // are counted.
 __host__ __device__ constexpr int fwd_budget(int nin) { return 200 - 2 * nin; }
+
+// Whether output component a (resp. input component b1) occurs among the
+// terms [tb, te) of a path type.
+__host__ __device__ constexpr bool term_has_a(int tb, int te, int a) {
+  for (int t = tb; t < te; ++t)
+    if (tab::kTerms[t].a == a) return true;
+  return false;
+}
+__host__ __device__ constexpr bool term_has_b1(int tb, int te, int b) {
+  for (int t = tb; t < te; ++t)
+    if (tab::kTerms[t].b1 == b) return true;
+  return false;
+}
 __host__ __device__ constexpr int vjp_budget(int nin, int ne) { return 200 - 2 * nin - ne; }
 // Channels of one VJP block: up to 4 waves (C <= 256).
 inline constexpr int kMaxVjpWaves = 4;
@@ -179,14 +192,30 @@ __global__ __launch_bounds__(kWave) void conv_fwd_kernel(
             w = fmaf(rec[EP::NY + bb], Wr[bb * G::NP + pi], w);
           });
         }
-        float xw[n1];
-        static_for<n1>([&](auto c) { xw[c] = w * xv[o1 + c]; });
         constexpr int tb = tab::kTermBegin[PI.type], te = tab::kTermBegin[PI.type + 1];
-        static_for<te - tb>([&](auto ti) {
-          constexpr int tt = tb + ti;
-          constexpr tab::Term T = tab::kTerms[tt];
-          acc[lo + T.a] = fmaf(EP::template cy<tt, o2 + T.b2>(rec), xw[T.b1], acc[lo + T.a]);
-        });
+        constexpr int na = ncomp(PI.L);
+        if constexpr (na < n1) {
+          // fewer outputs than inputs: weight the 2L+1 products, not the 2l1+1 inputs
+          float t[na];
+          static_for<te - tb>([&](auto ti) {
+            constexpr int tt = tb + ti;
+            constexpr tab::Term T = tab::kTerms[tt];
+            const float cy = EP::template cy<tt, o2 + T.b2>(rec);
+            if constexpr (T.fa) t[T.a] = cy * xv[o1 + T.b1];
+            else t[T.a] = fmaf(cy, xv[o1 + T.b1], t[T.a]);
+          });
+          static_for<na>([&](auto a) {
+            if constexpr (term_has_a(tb, te, a)) acc[lo + a] = fmaf(w, t[a], acc[lo + a]);
+          });
+        } else {
+          float xw[n1];
+          static_for<n1>([&](auto c) { xw[c] = w * xv[o1 + c]; });
+          static_for<te - tb>([&](auto ti) {
+            constexpr int tt = tb + ti;
+            constexpr tab::Term T = tab::kTerms[tt];
+            acc[lo + T.a] = fmaf(EP::template cy<tt, o2 + T.b2>(rec), xw[T.b1], acc[lo + T.a]);
+          });
+        }
       });
     }
     __syncthreads();
@@ -550,14 +579,30 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
             });
           }
           if constexpr (NEED_X) {
-            // x_bar[b1] += sum_terms c y[b2] (w g[a])
-            float gw[na];
-            static_for<na>([&](auto a) { gw[a] = w * gv[lo + a]; });
-            static_for<te - tb>([&](auto ti) {
-              constexpr int tt = tb + ti;
-              constexpr tab::Term T = tab::kTerms[tt];
-              xb[o1 + T.b1] = fmaf(EP::template cy<tt, o2 + T.b2>(rec), gw[T.a], xb[o1 + T.b1]);
-            });
+            // x_bar[b1] += sum_terms c y[b2] (w g[a]); with fewer inputs than
+            // outputs the 2l1+1 sums are weighted instead of the 2L+1 g rows
+            constexpr int n1 = ncomp(PI.l1);
+            if constexpr (n1 < na) {
+              float u[n1];
+              static_for<te - tb>([&](auto ti) {
+                constexpr int tt = tb + ti;
+                constexpr tab::Term T = tab::kTerms[tt];
+                const float cy = EP::template cy<tt, o2 + T.b2>(rec);
+                if constexpr (T.f1) u[T.b1] = cy * gv[lo + T.a];
+                else u[T.b1] = fmaf(cy, gv[lo + T.a], u[T.b1]);
+              });
+              static_for<n1>([&](auto c) {
+                if constexpr (term_has_b1(tb, te, c)) xb[o1 + c] = fmaf(w, u[c], xb[o1 + c]);
+              });
+            } else {
+              float gw[na];
+              static_for<na>([&](auto a) { gw[a] = w * gv[lo + a]; });
+              static_for<te - tb>([&](auto ti) {
+                constexpr int tt = tb + ti;
+                constexpr tab::Term T = tab::kTerms[tt];
+                xb[o1 + T.b1] = fmaf(EP::template cy<tt, o2 + T.b2>(rec), gw[T.a], xb[o1 + T.b1]);
+              });
+            }
           }
           if (NEED_POS || (XW && wb_out)) {
             // v2[b2] = sum_terms c g[a] x[b1]  (VJP_2(g, x), unweighted)

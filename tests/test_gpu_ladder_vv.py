@@ -90,3 +90,14 @@ def test_ladder_vjp_vjp_workload_sampled(variant):
     go, Ao, _ = ladder.ladder_vjp_vjp(g.spec, f(g.A[nodes]), [f(w) for w in g.ws], f(g.gz[nodes]), v_A=f(vA[nodes]))
     assert_close("g_hat", gh.cpu().numpy()[nodes], go)
     assert_close("A_hat", Ah.cpu().numpy()[nodes], Ao)
+
+
+@pytest.mark.parametrize("variant", ["full", "reduced"])
+def test_ladder_vjp_vjp_bitwise_deterministic(variant):
+    g = GpuLadder(2, 2, 3, variant, C=32, N=300)
+    g.fwd()
+    vA, vw = cotangents(g, 13)
+    a = [x.cpu().numpy() for x in run_vv(g, vA, vw)]
+    b = [x.cpu().numpy() for x in run_vv(g, vA, vw)]
+    for p, q in zip(a, b):
+        assert np.array_equal(p, q)

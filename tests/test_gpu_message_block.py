@@ -83,3 +83,12 @@ def test_message_block_without_edges():
                                             d["shift"].astype(np.float64), d["x"].astype(np.float64), 1.0)
     assert abs(float(en.item()) - Eo) <= 1e-4 * np.abs(eao).sum()
     assert float(F.abs().max()) == 0.0 and np.abs(Fo).max() == 0.0
+
+
+def test_message_block_bitwise_deterministic():
+    """No floating-point atomics anywhere: two runs give the same bits."""
+    C = 32
+    cspec, lspec, w, d, entries = block_setup(C=C)
+    a = gpu_block(cspec, lspec, w, d, entries, C, 3, "reduced")
+    b = gpu_block(cspec, lspec, w, d, entries, C, 3, "reduced")
+    assert a[0] == b[0] and np.array_equal(a[1], b[1]) and np.array_equal(a[2], b[2])

@@ -58,3 +58,23 @@ def test_without_gamma_and_single_outputs():
     run(2, 25, 48, 0.1, 8, with_gamma=False)
     run(2, 25, 48, 0.1, 9, want=("x",))
     run(2, 25, 48, 0.1, 10, want=("gamma",))
+
+
+def test_norm_vjp_bitwise_deterministic():
+    from cartesian_tensor_product_amd import flashcart as fc
+    rng = np.random.default_rng(12)
+    N, C = 3000, 64
+    x = torch.from_numpy(inputs.normal(rng, (N, 9, C))).cuda()
+    g = torch.from_numpy(inputs.normal(rng, (N, 9, C))).cuda()
+    gam = torch.from_numpy(inputs.f32(1 + 0.1 * rng.standard_normal((3, C)))).cuda()
+    d = fc.norm_desc(N, C, 2, 1e-5)
+    y, s = torch.empty_like(x), torch.empty(N, device="cuda")
+    fc.fc_rms_norm_fwd(d, x, gam, y, s)
+    ws = fc.workspace(fc.fc_rms_norm_workspace_bytes(d), "cuda")
+    outs = []
+    for _ in range(2):
+        xb, gb = torch.empty_like(x), torch.empty_like(gam)
+        fc.fc_rms_norm_vjp(d, x, gam, s, g, xb, gb, ws)
+        torch.cuda.synchronize()
+        outs.append((xb.cpu().numpy(), gb.cpu().numpy()))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])

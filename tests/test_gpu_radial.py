@@ -144,3 +144,12 @@ def test_mlp_conv_without_edges():
     torch.cuda.synchronize()
     for name, a in (("z", z), ("x_grad", xb), ("pos_grad", pb), ("mlp_w_grad", wb)):
         assert float(a.abs().max()) == 0.0, name
+
+
+def test_mlp_conv_bitwise_deterministic():
+    spec, d, mlp = setup((2, 2, 2), 40, 33, n=60, k=20, box=6.0)
+    gc = GpuMlpConv((2, 2, 2), d, 40, 5.0, mlp)
+    r1 = [t.cpu().numpy() for t in gc.vjp()]
+    r2 = [t.cpu().numpy() for t in gc.vjp()]
+    for a, b in zip(r1, r2):
+        assert np.array_equal(a, b)

@@ -144,7 +144,7 @@ struct MlpWorkspace {
       off += fc::align256(floats * sizeof(float));
       return r;
     };
-    h2t = take(E * fc::kRadHidden);
+    h2t = take((size_t)fc::radial_ld(d->n_edges) * fc::kRadHidden);
     w = take(E * PC);
     wbar = op == 1 ? take(E * PC) : nullptr;
     q = op == 1 ? take(E * 3) : nullptr;
@@ -159,6 +159,40 @@ fc::RadialArgs radial_args(const fc_conv_desc* d, const fc_graph* g, const float
   layout(d, &P, &nin, &nout);
   return fc::RadialArgs{d->n_nodes, d->n_edges, P, d->channels, d->r_cut, g->rowptr, g->sender, g->receiver,
                         g->t_rowptr, g->t_edge, pos, shift, mlp_w};
+}
+
+// The convolution weighted by the radial network, forward and VJP, on a
+// workspace laid out by MlpWorkspace; with have_w the VJP reuses h2 and w
+// left in it by a forward on the same workspace (op 1 layout).
+void mlp_conv_forward(const fc_conv_desc* d, const fc_graph* g, const float* pos, const float* shift, const float* x,
+                      const float* mlp_w, float* z, const MlpWorkspace& ws, hipStream_t stream) {
+  const fc::RadialArgs ra = radial_args(d, g, pos, shift, mlp_w);
+  fc::launch_radial_hidden(ra, ws.h2t, stream);
+  fc::launch_radial_out(ra, ws.h2t, ws.w, stream);
+  fc::ConvArgs a = make_args(d, g, pos, shift, x, nullptr);
+  a.w_edge = d->n_edges > 0 ? ws.w : x;   // never read without edges
+  a.z = z;
+  fc::conv_dispatch(0, d->l_in, d->l_edge, lout_key(d), a, stream);
+}
+
+void mlp_conv_vjp(const fc_conv_desc* d, const fc_graph* g, const float* pos, const float* shift, const float* x,
+                  const float* mlp_w, const float* g_z, float* x_grad, float* pos_grad, float* mlp_w_grad,
+                  const MlpWorkspace& ws, void* conv_ws, bool have_w, hipStream_t stream) {
+  const fc::RadialArgs ra = radial_args(d, g, pos, shift, mlp_w);
+  const bool radial = pos_grad || mlp_w_grad;
+  if (!have_w) {
+    fc::launch_radial_hidden(ra, ws.h2t, stream);
+    fc::launch_radial_out(ra, ws.h2t, ws.w, stream);
+  }
+  fc::ConvArgs a = make_args(d, g, pos, shift, x, nullptr);
+  a.w_edge = d->n_edges > 0 ? ws.w : x;
+  a.w_edge_bar = (radial && d->n_edges > 0) ? ws.wbar : nullptr;
+  a.g = g_z;
+  a.x_bar = x_grad;
+  a.pos_bar = pos_grad;
+  a.rbar = static_cast<float*>(conv_ws);
+  if (x_grad || pos_grad || a.w_edge_bar) fc::conv_dispatch(1, d->l_in, d->l_edge, lout_key(d), a, stream);
+  if (radial) fc::launch_radial_vjp(ra, ws.h2t, ws.wbar, ws.q, pos_grad, mlp_w_grad, ws.scratch, stream);
 }
 
 fc_status check_norm(const fc_norm_desc* d) {
@@ -636,7 +670,7 @@ fc_status msg_layout(const fc_conv_desc* cd, const fc_ladder_desc* ld, MsgLayout
   L->ea = o;    o += al(N);
   L->saved = o; o += al(p.saved_floats());
   L->lws = o;   o += al(std::max(p.fwd_ws_floats(), p.vjp_ws_floats()));
-  L->cws_bytes = std::max(fc_edge_conv_mlp_workspace_bytes(cd, 0), fc_edge_conv_mlp_workspace_bytes(cd, 1));
+  L->cws_bytes = fc_edge_conv_mlp_workspace_bytes(cd, 1);   // the VJP reuses the forward's h2 and w in it
   L->cws = o;   o += (L->cws_bytes + 255) / 256 * 256;
   L->parts = o; o += (size_t)fc::block_energy_parts(cd->n_nodes) * 8;
   L->total = o;
@@ -786,13 +820,7 @@ fc_status fc_edge_conv_mlp_fwd(const fc_conv_desc* d, const fc_graph* g, const f
   const MlpWorkspace ws(d, 0, workspace);
   if (!workspace || workspace_bytes < ws.bytes)
     return fail(FC_ERR_WORKSPACE, "MLP-weighted forward needs %zu workspace bytes", ws.bytes);
-  const fc::RadialArgs ra = radial_args(d, g, pos, shift, mlp_w);
-  fc::launch_radial_hidden(ra, ws.h2t, stream);
-  fc::launch_radial_out(ra, ws.h2t, ws.w, stream);
-  fc::ConvArgs a = make_args(d, g, pos, shift, x, nullptr);
-  a.w_edge = d->n_edges > 0 ? ws.w : x;   // never read without edges
-  a.z = z;
-  fc::conv_dispatch(0, d->l_in, d->l_edge, lout_key(d), a, stream);
+  mlp_conv_forward(d, g, pos, shift, x, mlp_w, z, ws, stream);
   return check_launch("MLP-weighted edge conv forward");
 }
 
@@ -811,19 +839,7 @@ fc_status fc_edge_conv_mlp_vjp(const fc_conv_desc* d, const fc_graph* g, const f
   const MlpWorkspace ws(d, 1, workspace);
   if (!workspace || workspace_bytes < ws.bytes)
     return fail(FC_ERR_WORKSPACE, "MLP-weighted VJP needs %zu workspace bytes", ws.bytes);
-  const fc::RadialArgs ra = radial_args(d, g, pos, shift, mlp_w);
-  const bool radial = pos_grad || mlp_w_grad;
-  fc::launch_radial_hidden(ra, ws.h2t, stream);
-  fc::launch_radial_out(ra, ws.h2t, ws.w, stream);
-  fc::ConvArgs a = make_args(d, g, pos, shift, x, nullptr);
-  a.w_edge = d->n_edges > 0 ? ws.w : x;
-  a.w_edge_bar = (radial && d->n_edges > 0) ? ws.wbar : nullptr;
-  a.g = g_z;
-  a.x_bar = x_grad;
-  a.pos_bar = pos_grad;
-  a.rbar = static_cast<float*>(workspace);
-  if (x_grad || pos_grad || a.w_edge_bar) fc::conv_dispatch(1, d->l_in, d->l_edge, lout_key(d), a, stream);
-  if (radial) fc::launch_radial_vjp(ra, ws.h2t, ws.wbar, ws.q, pos_grad, mlp_w_grad, ws.scratch, stream);
+  mlp_conv_vjp(d, g, pos, shift, x, mlp_w, g_z, x_grad, pos_grad, mlp_w_grad, ws, workspace, false, stream);
   return check_launch("MLP-weighted edge conv VJP");
 }
 
@@ -868,9 +884,12 @@ fc_status fc_message_block_energy_forces(const fc_conv_desc* cd, const fc_graph*
   const float* lw = W + L.w_lad;
   auto chan = [&](const float* M, int l) { return M + (size_t)l * C * C; };
 
+  if (cd->n_edges > 0 && (!g->rowptr || !g->sender || !g->receiver))
+    return fail(FC_ERR_INVALID_ARGUMENT, "message block needs graph rowptr, sender and receiver");
+  const MlpWorkspace mws(cd, 1, wb + L.cws);
+
   // ---- forward
-  if (fc_status s = fc_edge_conv_mlp_fwd(cd, g, pos, shift, h0, W + L.w_mlp, a, wb + L.cws, L.cws_bytes, stream))
-    return s;
+  mlp_conv_forward(cd, g, pos, shift, h0, W + L.w_mlp, a, mws, stream);
   fc::block_scale(a, (size_t)N * R * C, conv_scale, stream);
   {
     fc::GemmGroup gg{};
@@ -918,9 +937,7 @@ fc_status fc_message_block_energy_forces(const fc_conv_desc* cd, const fc_graph*
     fc::gemm_group(gg, stream);
   }
   fc::block_scale(a, (size_t)N * R * C, conv_scale, stream);
-  if (fc_status s = fc_edge_conv_mlp_vjp(cd, g, pos, shift, h0, W + L.w_mlp, a, nullptr, forces, nullptr, wb + L.cws,
-                                         L.cws_bytes, stream))
-    return s;
+  mlp_conv_vjp(cd, g, pos, shift, h0, W + L.w_mlp, a, nullptr, forces, nullptr, mws, wb + L.cws, true, stream);
   fc::block_scale(forces, (size_t)N * 3, -1.f, stream);
   return check_launch("message block energy/forces");
 }

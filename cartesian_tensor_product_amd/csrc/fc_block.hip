@@ -46,10 +46,16 @@ __global__ __launch_bounds__(256) void atom_energy_kernel(int N, int rows, int C
   if (threadIdx.x == 0) part[blockIdx.x] = (s[0] + s[1]) + (s[2] + s[3]);
 }
 
-__global__ void energy_sum_kernel(int n, const double* __restrict__ part, double* __restrict__ energy) {
+// One wave: lane l sums part[l], part[l + 64], ... in order, then a butterfly
+// (fixed order, the same bits in every lane).
+__global__ __launch_bounds__(64) void energy_sum_kernel(int n, const double* __restrict__ part,
+                                                        double* __restrict__ energy) {
+  const int lane = threadIdx.x;
   double t = 0.0;
-  for (int i = 0; i < n; ++i) t += part[i];
-  *energy = t;
+  for (int i = lane; i < n; i += 64) t += part[i];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o);
+  if (lane == 0) *energy = t;
 }
 
 }  // namespace
@@ -69,7 +75,7 @@ void block_energy(const float* z, int N, int rows, int C, float* e_atom, double*
                   hipStream_t st) {
   const int nb = block_energy_parts(N);
   hipLaunchKernelGGL(atom_energy_kernel, dim3(nb), dim3(256), 0, st, N, rows, C, z, e_atom, part);
-  hipLaunchKernelGGL(energy_sum_kernel, dim3(1), dim3(1), 0, st, nb, (const double*)part, energy);
+  hipLaunchKernelGGL(energy_sum_kernel, dim3(1), dim3(64), 0, st, nb, (const double*)part, energy);
 }
 
 }  // namespace fc

@@ -24,7 +24,11 @@ struct RadialArgs {
   const float *pos, *shift, *weights;
 };
 
-// h2t [64][E] = second hidden layer, edge-minor.
+// Row stride of the edge-minor hidden layer: E rounded up to a multiple of 4
+// (128-bit loads of the GEMM operand).
+inline int radial_ld(int E) { return (E + 3) / 4 * 4; }
+
+// h2t [64][radial_ld(E)] = second hidden layer, edge-minor.
 void launch_radial_hidden(const RadialArgs& a, float* h2t, hipStream_t st);
 // w [E][P C] = h2 W3.
 void launch_radial_out(const RadialArgs& a, const float* h2t, float* w, hipStream_t st);

@@ -86,7 +86,8 @@ __global__ __launch_bounds__(kRadBlock) void radial_hidden_kernel(int E, float r
                                                                   const int* __restrict__ sender,
                                                                   const float* __restrict__ pos,
                                                                   const float* __restrict__ shift,
-                                                                  const float* __restrict__ W, float* __restrict__ h2t) {
+                                                                  const float* __restrict__ W, float* __restrict__ h2t,
+                                                                  int ld) {
   __shared__ float w1[kW1], w2[kW2];
   load_hidden_weights(W, w1, w2);
   const int e = blockIdx.x * kRadBlock + threadIdx.x;
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(kRadBlock) void radial_hidden_kernel(int E, float r
     float a = 0.f;
 #pragma unroll
     for (int j = 0; j < kRadHidden; ++j) a = fmaf(h1[j], w2[j * kRadHidden + j2], a);
-    h2t[(size_t)j2 * E + e] = silu(a);
+    h2t[(size_t)j2 * ld + e] = silu(a);
   }
 }
 
@@ -229,7 +230,7 @@ GemmProblem problem(int M, int N, int K, GView A, GView Bt, GOut C) {
 void launch_radial_hidden(const RadialArgs& a, float* h2t, hipStream_t st) {
   if (a.E == 0) return;
   hipLaunchKernelGGL(radial_hidden_kernel, dim3((a.E + kRadBlock - 1) / kRadBlock), dim3(kRadBlock), 0, st, a.E,
-                     a.r_max, a.receiver, a.sender, a.pos, a.shift, a.weights, h2t);
+                     a.r_max, a.receiver, a.sender, a.pos, a.shift, a.weights, h2t, radial_ld(a.E));
 }
 
 void launch_radial_out(const RadialArgs& a, const float* h2t, float* w, hipStream_t st) {
@@ -237,8 +238,15 @@ void launch_radial_out(const RadialArgs& a, const float* h2t, float* w, hipStrea
   const long long PC = (long long)a.P * a.C;
   const float* W3 = a.weights + kW1 + kW2;
   GemmGroup g{};
-  g.prob[g.count++] = problem(a.E, (int)PC, kRadHidden, plain_view_t(h2t, a.E), plain_view_t(W3, PC),
-                              plain_out(w, PC, 0));
+  // the first E4 = 4 floor(E / 4) edges with 128-bit operand loads, the rest
+  // (at most three) with scalar ones
+  const int ld = radial_ld(a.E), E4 = a.E / 4 * 4;
+  if (E4 > 0)
+    g.prob[g.count++] = problem(E4, (int)PC, kRadHidden, plain_view_t(h2t, ld), plain_view_t(W3, PC),
+                                plain_out(w, PC, 0));
+  if (a.E > E4)
+    g.prob[g.count++] = problem(a.E - E4, (int)PC, kRadHidden, plain_view_t(h2t + E4, ld), plain_view_t(W3, PC),
+                                plain_out(w + (size_t)E4 * PC, PC, 0));
   gemm_group(g, st);
 }
 
@@ -271,7 +279,7 @@ void launch_radial_vjp(const RadialArgs& a, const float* h2t, const float* w_bar
     g.prob[g.count++] = problem(E, kRadHidden, (int)PC, plain_view(w_bar, PC), plain_view(W3, PC),
                                 plain_out(hbar, kRadHidden, 0));
     if (w_grad) {
-      GemmProblem d = problem(kRadHidden, (int)PC, E, plain_view(h2t, E), plain_view_t(w_bar, PC),
+      GemmProblem d = problem(kRadHidden, (int)PC, E, plain_view(h2t, radial_ld(E)), plain_view_t(w_bar, PC),
                               plain_out(w_grad + kW1 + kW2, PC, 0));
       d.ksplit = gemm_ksplit(d.M, d.N, d.K, kRadSplitTarget);
       d.part = part;

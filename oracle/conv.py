@@ -330,3 +330,33 @@ def edge_conv_vjp_vjp(spec: ConvSpec, pos, rowptr, sender, x, W, g, v_x=None,
         x_hat, pos_hat = xb.imag / h, pb.imag / h
         W_hat = Wb.imag / h if want_W else None
     return g_hat, x_hat, pos_hat, W_hat
+
+
+def edge_conv_vjp_vjp_w(spec: ConvSpec, pos, rowptr, sender, x, w, g, v_x=None,
+                        v_pos=None, v_w=None, shift=None, edges=None, chunk: int = 4096,
+                        outputs=("g", "x", "pos", "w")):
+    """(g_hat, x_hat, pos_hat, w_hat) of the explicit-weight convolution for
+    s = <v_x, x_bar> + <v_pos, pos_bar> + <v_w, w_bar> (App. C Eq. C2 and
+    Alg. 3 with the per-edge weights as inputs; the direction cotangent of
+    Alg. 3 carried to the positions): g_hat = d z / d eps and (x_hat,
+    pos_hat, w_hat) = d (x_bar, pos_bar, w_bar) / d eps of edge_conv_fwd_w
+    and edge_conv_vjp_w at (x + eps v_x, pos + eps v_pos, w + eps v_w), by
+    complex step.  A missing cotangent is zero.
+    """
+    h = CSTEP
+    xc = x.astype(np.complex128)
+    pc = pos.astype(np.complex128)
+    wc = w.astype(np.complex128)
+    if v_x is not None:
+        xc = xc + 1j * h * v_x
+    if v_pos is not None:
+        pc = pc + 1j * h * v_pos
+    if v_w is not None:
+        wc = wc + 1j * h * v_w
+    g_hat = x_hat = pos_hat = w_hat = None
+    if "g" in outputs:
+        g_hat = edge_conv_fwd_w(spec, pc, rowptr, sender, xc, wc, shift, edges, chunk).imag / h
+    if "x" in outputs or "pos" in outputs or "w" in outputs:
+        xb, pb, wb = edge_conv_vjp_w(spec, pc, rowptr, sender, xc, wc, g, shift, edges, chunk)
+        x_hat, pos_hat, w_hat = xb.imag / h, pb.imag / h, wb.imag / h
+    return g_hat, x_hat, pos_hat, w_hat

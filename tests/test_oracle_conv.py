@@ -497,3 +497,46 @@ def test_summed_vjp_against_complex_step_and_broadcast(ranks):
     xs, ps_, Ws = conv.edge_conv_vjp(sep, d["pos"], d["rowptr"], d["sender"], d["x"], d["W"], gs, want_W=True)
     for a, b in ((xb, xs), (pb, ps_), (Wb, Ws)):
         assert np.abs(a - b).max() < 1e-12 * max(1.0, np.abs(b).max())
+
+
+def test_vjp_vjp_explicit_weights_fd_and_symmetry():
+    """The explicit-weight VJP-of-VJP (Alg. 3's interface with the direction
+    cotangent carried to the positions): central differences of the
+    explicit-weight VJP and forward along (v_x, v_pos, v_w), Hessian
+    symmetry over (x, pos, w), and the per-edge weight output against
+    Eq. C2's w_hat = <g, f(v_x, y) + f(x, v_y)> with v_y = J_y dv."""
+    spec, d = tiny(2, channels=3)
+    rng = np.random.default_rng(41)
+    E = len(d["sender"])
+    w = rng.standard_normal((E, spec.n_paths, 3))
+    v_x, v_pos, v_w = (rng.standard_normal(a.shape) for a in (d["x"], d["pos"], w))
+    base = (spec, d["pos"], d["rowptr"], d["sender"], d["x"], w, d["g"])
+    gh, xh, ph, wh = conv.edge_conv_vjp_vjp_w(*base, v_x=v_x, v_pos=v_pos, v_w=v_w)
+    h = 1e-5
+    arg = lambda sg: (spec, d["pos"] + sg * h * v_pos, d["rowptr"], d["sender"], d["x"] + sg * h * v_x, w + sg * h * v_w)
+    zd = (conv.edge_conv_fwd_w(*arg(1)) - conv.edge_conv_fwd_w(*arg(-1))) / (2 * h)
+    assert np.abs(gh - zd).max() < 1e-6 * np.abs(gh).max()
+    bp, bm = conv.edge_conv_vjp_w(*arg(1), d["g"]), conv.edge_conv_vjp_w(*arg(-1), d["g"])
+    for got, a, b in zip((xh, ph, wh), bp, bm):
+        assert np.abs(got - (a - b) / (2 * h)).max() < 1e-6 * max(1.0, np.abs(got).max())
+    # Eq. C2 edge by edge: w_hat = <g, f(v_x, y) + f(x, v_y)>, v_y = J_y dv
+    recv = conv.receivers(d["rowptr"])
+    for e in range(0, E, 7):
+        u, s_ = recv[e], d["sender"][e]
+        rv = d["pos"][s_] - d["pos"][u]
+        n = rv / np.linalg.norm(rv)
+        dv = v_pos[s_] - v_pos[u]
+        for p, (l1, l2, L) in enumerate(spec.paths):
+            K = T.coupling_tensor(l1, l2, L)
+            y = T.direction_tensor(l2, n[None, :])[0]
+            vy = T.direction_tensor_jac(l2, rv[None, :])[0] @ dv
+            xs = d["x"][s_, spec.in_off[l1]:spec.in_off[l1 + 1], :]
+            vxs = v_x[s_, spec.in_off[l1]:spec.in_off[l1 + 1], :]
+            gp = d["g"][u, spec.rows[p], :]
+            want = (np.einsum('abc,bk,c,ak->k', K, vxs, y, gp) + np.einsum('abc,bk,c,ak->k', K, xs, vy, gp))
+            assert np.allclose(wh[e, p], want, rtol=1e-8, atol=1e-10)
+    u_x, u_pos, u_w = (rng.standard_normal(a.shape) for a in (d["x"], d["pos"], w))
+    _, xh2, ph2, wh2 = conv.edge_conv_vjp_vjp_w(*base, v_x=u_x, v_pos=u_pos, v_w=u_w)
+    lhs = np.sum(u_x * xh) + np.sum(u_pos * ph) + np.sum(u_w * wh)
+    rhs = np.sum(v_x * xh2) + np.sum(v_pos * ph2) + np.sum(v_w * wh2)
+    assert lhs == pytest.approx(rhs, rel=1e-10)

@@ -507,7 +507,16 @@ def main():
             "fwd_GBs_alg": bw_f / (fw * 1e-3) / 1e9, "vjp_GBs_alg": bw_v / (vw * 1e-3) / 1e9,
             "fwd_plus_vjp_frac_hbm": (bw_f + bw_v) / ((fw + vw) * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "w_bytes": E * P * CHANNELS * 4}
-        del w_e, wb_e
+        # VJP-of-VJP with every cotangent (v_x, v_pos, v_w) and every output
+        # (g_hat, x_hat, pos_hat, w_hat); w, v_w and w_hat each move w_bytes
+        v_x = torch.randn(x.shape, device=dev, generator=gen)
+        v_pos = torch.randn(pos.shape, device=dev, generator=gen)
+        v_w = torch.randn((E, P, CHANNELS), device=dev, generator=gen)
+        gh, xh, ph = torch.empty_like(g), torch.empty_like(x), torch.empty_like(pos)
+        out["explicit_weights"]["vjp_vjp_ms"] = timed(
+            lambda: fc.fc_edge_conv_vjp_vjp_w(desc, graph, pos, None, x, w_e, g, v_x, v_pos, v_w, gh, xh, ph, wb_e,
+                                              ws))
+        del w_e, wb_e, v_w, v_x, v_pos, gh, xh, ph
         # the radial-weight gradient (optional VJP output, a receiver-sorted
         # pass of its own), timed alone and with the rest of the VJP
         Wb = torch.empty_like(W)

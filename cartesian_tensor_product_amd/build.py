@@ -52,12 +52,14 @@ def _compile(src: str) -> str:
 
 def _weight(src: str) -> int:
     """Rough compile cost, so that the largest units start first: the ranks
-    of a convolution unit conv_inst_<l_in><l_edge><l_out key>."""
+    of a convolution unit conv_inst_<l_in><l_edge><l_out key>[w]."""
     name = os.path.basename(src)
     if name.startswith("conv_inst_"):
         digits = name[len("conv_inst_"):-len(".hip")]
+        xw = digits.endswith("w")   # explicit-weight VJP-of-VJP unit
+        digits = digits.rstrip("w")
         a, b, key = int(digits[0]), int(digits[1]), int(digits[2:])
-        return (a + b + key % 8 + (4 if (key // 8) % 2 else 0)) * 10
+        return (a + b + key % 8 + (4 if (key // 8) % 2 else 0)) * (8 if xw else 10)
     return 1
 
 

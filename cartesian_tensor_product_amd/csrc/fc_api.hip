@@ -497,6 +497,46 @@ fc_status fc_edge_conv_vjp_vjp(const fc_conv_desc* d, const fc_graph* g, const f
   return check_launch("edge conv VJP-of-VJP");
 }
 
+fc_status fc_edge_conv_vjp_vjp_w(const fc_conv_desc* d, const fc_graph* g, const float* pos, const float* shift,
+                                 const float* x, const float* w, const float* g_z, const float* v_x,
+                                 const float* v_pos, const float* v_w, float* g_hat, float* x_hat, float* pos_hat,
+                                 float* w_hat, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (fc_status s = check_desc(d)) return s;
+  if (!fc::conv_vv_supported(d->l_in, d->l_edge, lout_key(d)))
+    return fail(FC_ERR_UNSUPPORTED, "VJP-of-VJP is not instantiated for (l_in, l_edge, l_out) = (%d, %d, %d)",
+                d->l_in, d->l_edge, d->l_out);
+  if (!g_hat && !x_hat && !pos_hat && !w_hat)
+    return fail(FC_ERR_INVALID_ARGUMENT, "explicit-weight VJP-of-VJP: no output requested");
+  if (!g || !g->rowptr || (d->n_edges > 0 && !g->sender))
+    return fail(FC_ERR_INVALID_ARGUMENT, "explicit-weight VJP-of-VJP needs graph rowptr and sender");
+  const bool back = x_hat || pos_hat || w_hat;
+  if (back && (!g->t_rowptr || (d->n_edges > 0 && (!g->receiver || !g->t_edge))))
+    return fail(FC_ERR_INVALID_ARGUMENT, "explicit-weight VJP-of-VJP: x_hat/pos_hat/w_hat need the graph transpose");
+  if (!pos || !x || (d->n_edges > 0 && !w) || (back && !g_z))
+    return fail(FC_ERR_INVALID_ARGUMENT, "explicit-weight VJP-of-VJP: NULL pos, x, w or g_z");
+  if (misaligned(pos, 4) || misaligned(x, 4) || misaligned(w, 4) || misaligned(g_z, 4) || misaligned(v_x, 4) ||
+      misaligned(v_pos, 4) || misaligned(v_w, 4) || misaligned(g_hat, 4) || misaligned(x_hat, 4) ||
+      misaligned(pos_hat, 4) || misaligned(w_hat, 4) || misaligned(shift, 4))
+    return fail(FC_ERR_INVALID_ARGUMENT, "explicit-weight VJP-of-VJP: arrays must be 4-byte aligned");
+  const size_t need = fc_edge_conv_workspace_bytes(d, 1);
+  if (back && need > 0 && (!workspace || workspace_bytes < need))
+    return fail(FC_ERR_WORKSPACE, "explicit-weight VJP-of-VJP needs %zu workspace bytes", need);
+  fc::ConvArgs a = make_args(d, g, pos, shift, x, nullptr);
+  const bool edges = d->n_edges > 0;
+  a.w_edge = edges ? w : x;   // never read without edges
+  a.v_w_edge = edges ? v_w : nullptr;
+  a.w_edge_bar = edges ? w_hat : nullptr;
+  a.g = g_z;
+  a.v_x = v_x;
+  a.v_pos = v_pos;
+  a.g_hat = g_hat;
+  a.x_bar = x_hat;
+  a.pos_bar = pos_hat;
+  a.rbar = static_cast<float*>(workspace);
+  fc::conv_vv_w_dispatch(d->l_in, d->l_edge, lout_key(d), a, stream);
+  return check_launch("explicit-weight edge conv VJP-of-VJP");
+}
+
 fc_status fc_ladder_layout(const fc_ladder_desc* d, size_t* n_weight_floats, size_t* n_saved_floats) {
   fc::LadderPlan p;
   if (fc_status s = ladder_plan(d, &p)) return s;

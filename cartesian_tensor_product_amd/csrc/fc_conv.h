@@ -24,6 +24,9 @@ struct ConvArgs {
   // their gradient (VJP, nullable)
   const float* w_edge;
   float* w_edge_bar;
+  // VJP-of-VJP with explicit weights: the weight cotangent [E][P][C]
+  // (nullable); w_hat reuses w_edge_bar
+  const float* v_w_edge;
 };
 
 #include "generated/fc_conv_configs.h"
@@ -78,5 +81,9 @@ struct VjpWorkspace {
 
 void launch_vjp_combine(const ConvArgs& a, const VjpWorkspace& w, int nin, hipStream_t st);
 bool conv_dispatch(int op, int l_in, int l_edge, int l_out, const ConvArgs& args, hipStream_t stream);
+// VJP-of-VJP with explicit per-edge weights (w_edge, v_w_edge; w_hat in
+// w_edge_bar); false when not instantiated (the configurations of
+// conv_vv_supported)
+bool conv_vv_w_dispatch(int l_in, int l_edge, int l_out, const ConvArgs& args, hipStream_t stream);
 
 }  // namespace fc

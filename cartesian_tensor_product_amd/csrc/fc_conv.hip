@@ -89,4 +89,19 @@ bool conv_dispatch(int op, int l_in, int l_edge, int l_out, const ConvArgs& args
   }
 }
 
+#define FC_CONV_W_DECL(A, B, Cc) void conv_run_w_##A##B##Cc(const ConvArgs& args, hipStream_t stream);
+FC_CONV_VV_CONFIGS(FC_CONV_W_DECL)
+
+#define FC_CONV_W_CASE(A, B, Cc)            \
+  case (A) * 1024 + (B) * 32 + (Cc):         \
+    conv_run_w_##A##B##Cc(args, stream);     \
+    return true;
+
+bool conv_vv_w_dispatch(int l_in, int l_edge, int l_out, const ConvArgs& args, hipStream_t stream) {
+  switch (l_in * 1024 + l_edge * 32 + l_out) {
+    FC_CONV_VV_CONFIGS(FC_CONV_W_CASE)
+    default: return false;
+  }
+}
+
 }  // namespace fc

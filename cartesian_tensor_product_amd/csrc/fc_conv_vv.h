@@ -56,11 +56,15 @@ __device__ __forceinline__ void vv_tensors(const VVGeo& G, float* y, float* yd) 
 // ------------------------------------------------------------ g_hat pass --
 __host__ __device__ constexpr int vv_recv_budget(int nin) { return 200 - 3 * nin; }
 
-template <int LIN, int LEDGE, int LOUT, int P0, int P1, bool HAS_VX>
+// XW: per-edge weights W = w [E][P][C] with the weight cotangent vw (same
+// layout, nullable) in place of the radial weights (Alg. 3's interface):
+// w_dot = vw instead of w'(r) nd, and an edge of zero length takes no part.
+template <int LIN, int LEDGE, int LOUT, int P0, int P1, bool HAS_VX, bool XW = false>
 __global__ __launch_bounds__(kWave) void conv_vv_recv_kernel(
     int N, int C, const int* __restrict__ rowptr, const int* __restrict__ sender, const float* __restrict__ pos,
     const float* __restrict__ shift, const float* __restrict__ x, const float* __restrict__ W,
-    const float* __restrict__ v_x, const float* __restrict__ v_pos, float* __restrict__ g_hat, float rc) {
+    const float* __restrict__ v_x, const float* __restrict__ v_pos, float* __restrict__ g_hat, float rc,
+    const float* __restrict__ vw = nullptr) {
   using Cfg = ConvCfg<LIN, LEDGE, LOUT>;
   using G = PathGroup<Cfg, P0, P1>;
   constexpr int NIN = Cfg::NIN, NE = Cfg::NE, P = Cfg::P, NOUT = Cfg::NOUT;
@@ -76,11 +80,13 @@ __global__ __launch_bounds__(kWave) void conv_vv_recv_kernel(
   const auto xr = make_rsrc(x, (uint32_t)((size_t)N * NIN * C * 4));
   const auto vr = make_rsrc(HAS_VX ? v_x : x, (uint32_t)((size_t)N * NIN * C * 4));
 
-  float Wr[kNB * G::NP];
-  static_for<kNB * G::NP>([&](auto i) {
-    constexpr int b = i / G::NP, p = i % G::NP;
-    Wr[i] = W[(size_t)(b * P + P0 + p) * C + kk];
-  });
+  float Wr[XW ? 1 : kNB * G::NP];
+  if constexpr (!XW) {
+    static_for<kNB * G::NP>([&](auto i) {
+      constexpr int b = i / G::NP, p = i % G::NP;
+      Wr[i] = W[(size_t)(b * P + P0 + p) * C + kk];
+    });
+  }
   float acc[G::NR];
   static_for<G::NR>([&](auto i) { acc[i] = 0.f; });
 
@@ -106,18 +112,23 @@ __global__ __launch_bounds__(kWave) void conv_vv_recv_kernel(
         dvz = v_pos[3 * s + 2] - vuz;
       }
       const VVGeo Gm = vv_geo(rx, ry, rz, dvx, dvy, dvz);
-      float y[NE], yd[NE], R[kNB], dR[kNB];
+      float y[NE], yd[NE];
       vv_tensors<LEDGE>(Gm, y, yd);
-      radial<true>(Gm.r, rc, R, dR);
       float* rec = geo + lane * REC;
       static_for<NE>([&](auto c) {
         rec[c] = y[c];
         rec[NE + c] = yd[c];
       });
-      static_for<kNB>([&](auto b) {
-        rec[2 * NE + b] = R[b];
-        rec[2 * NE + kNB + b] = dR[b];
-      });
+      if constexpr (XW) {
+        rec[2 * NE] = Gm.r > 0.f ? 1.f : 0.f;
+      } else {
+        float R[kNB], dR[kNB];
+        radial<true>(Gm.r, rc, R, dR);
+        static_for<kNB>([&](auto b) {
+          rec[2 * NE + b] = R[b];
+          rec[2 * NE + kNB + b] = dR[b];
+        });
+      }
       rec[2 * NE + 2 * kNB] = Gm.nd;
       rec[2 * NE + 2 * kNB + 1] = __int_as_float(s);
     }
@@ -130,24 +141,37 @@ __global__ __launch_bounds__(kWave) void conv_vv_recv_kernel(
       float xv[NIN], vx[HAS_VX ? NIN : 1];
       static_for<NIN>([&](auto c) { xv[c] = buf_load(xr, voff, sbase + c * C * 4); });
       if constexpr (HAS_VX) static_for<NIN>([&](auto c) { vx[c] = buf_load(vr, voff, sbase + c * C * 4); });
+      float we[XW ? G::NP : 1], wve[XW ? G::NP : 1];
+      if constexpr (XW) {
+        const float valid = rec[2 * NE];
+        const size_t erow = (size_t)(base + j) * P * C + kk;
+        static_for<G::NP>([&](auto pi) {
+          we[pi] = valid * W[erow + (size_t)(P0 + pi) * C];
+          wve[pi] = vw ? valid * vw[erow + (size_t)(P0 + pi) * C] : 0.f;
+        });
+      }
       static_for<G::NP>([&](auto pi) {
         constexpr int p = P0 + pi;
         constexpr PathInfo PI = Cfg::paths[p];
         constexpr int n1 = ncomp(PI.l1), o1 = rank_off(PI.l1), o2 = rank_off(PI.l2);
         constexpr int lo = G::loff(p);
         float w = 0.f, w1 = 0.f;
-        static_for<kNB>([&](auto b) {
-          constexpr int bb = b;
-          const float wb = Wr[bb * G::NP + pi];
-          w = fmaf(rec[2 * NE + bb], wb, w);
-          w1 = fmaf(rec[2 * NE + kNB + bb], wb, w1);
-        });
-        const float wd = w1 * nd;
-        float xw[n1], xd[n1], vw[HAS_VX ? n1 : 1];
+        if constexpr (XW) {
+          w = we[pi];
+        } else {
+          static_for<kNB>([&](auto b) {
+            constexpr int bb = b;
+            const float wb = Wr[bb * G::NP + pi];
+            w = fmaf(rec[2 * NE + bb], wb, w);
+            w1 = fmaf(rec[2 * NE + kNB + bb], wb, w1);
+          });
+        }
+        const float wd = XW ? wve[pi] : w1 * nd;
+        float xw[n1], xd[n1], vxw[HAS_VX ? n1 : 1];
         static_for<n1>([&](auto c) {
           xw[c] = w * xv[o1 + c];
           xd[c] = wd * xv[o1 + c];
-          if constexpr (HAS_VX) vw[c] = w * vx[o1 + c];
+          if constexpr (HAS_VX) vxw[c] = w * vx[o1 + c];
         });
         constexpr int tb = tab::kTermBegin[PI.type], te = tab::kTermBegin[PI.type + 1];
         static_for<te - tb>([&](auto ti) {
@@ -156,7 +180,7 @@ __global__ __launch_bounds__(kWave) void conv_vv_recv_kernel(
           const float cyd = T.c * rec[NE + o2 + T.b2];
           float a = fmaf(cy, xd[T.b1], acc[lo + T.a]);
           a = fmaf(cyd, xw[T.b1], a);
-          if constexpr (HAS_VX) a = fmaf(cy, vw[T.b1], a);
+          if constexpr (HAS_VX) a = fmaf(cy, vxw[T.b1], a);
           acc[lo + T.a] = a;
         });
       });
@@ -177,19 +201,22 @@ __global__ __launch_bounds__(kWave) void conv_vv_recv_kernel(
   }
 }
 
-template <int LIN, int LEDGE, int LOUT>
+template <int LIN, int LEDGE, int LOUT, bool XW = false>
 void launch_vv_recv(const ConvArgs& a, hipStream_t st) {
   using Cfg = ConvCfg<LIN, LEDGE, LOUT>;
   using GS = PathGroups<Cfg, vv_recv_budget(Cfg::NIN)>;
   dim3 grid(a.N, (a.C + kWave - 1) / kWave);
+  const float* Wt = XW ? a.w_edge : a.W;
   static_for<GS::n>([&](auto gi) {
     constexpr int p0 = GS::start[gi], p1 = GS::start[gi + 1];
     if (a.v_x)
-      hipLaunchKernelGGL((conv_vv_recv_kernel<LIN, LEDGE, LOUT, p0, p1, true>), grid, dim3(kWave), 0, st, a.N, a.C,
-                         a.rowptr, a.sender, a.pos, a.shift, a.x, a.W, a.v_x, a.v_pos, a.g_hat, a.rc);
+      hipLaunchKernelGGL((conv_vv_recv_kernel<LIN, LEDGE, LOUT, p0, p1, true, XW>), grid, dim3(kWave), 0, st, a.N,
+                         a.C, a.rowptr, a.sender, a.pos, a.shift, a.x, Wt, a.v_x, a.v_pos, a.g_hat, a.rc,
+                         a.v_w_edge);
     else
-      hipLaunchKernelGGL((conv_vv_recv_kernel<LIN, LEDGE, LOUT, p0, p1, false>), grid, dim3(kWave), 0, st, a.N,
-                         a.C, a.rowptr, a.sender, a.pos, a.shift, a.x, a.W, a.v_x, a.v_pos, a.g_hat, a.rc);
+      hipLaunchKernelGGL((conv_vv_recv_kernel<LIN, LEDGE, LOUT, p0, p1, false, XW>), grid, dim3(kWave), 0, st, a.N,
+                         a.C, a.rowptr, a.sender, a.pos, a.shift, a.x, Wt, a.v_x, a.v_pos, a.g_hat, a.rc,
+                         a.v_w_edge);
   });
 }
 
@@ -369,13 +396,18 @@ struct VVShape {
 
 // CH: edges per chunk (64, or 32 when the per-wave row sums of 64 edges would
 // not fit in LDS: many channel waves at rank 4).
-template <int LIN, int LEDGE, int LOUT, bool HAS_VX, bool NEED_X, bool NEED_POS, int CH>
+// XW: per-edge weights W = w [E][P][C] with the weight cotangent vw (nullable)
+// as in conv_vv_recv_kernel; w_dot = vw enters J_y^T with coefficient 1 (no
+// radial terms), and wh_out (nullable) receives the per-edge
+// w_hat = <g, f(v_x, y) + f(x, ydot)> = <alpha, y> + <beta, ydot> (Eq. C2).
+template <int LIN, int LEDGE, int LOUT, bool HAS_VX, bool NEED_X, bool NEED_POS, int CH, bool XW = false>
 __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vv_sender_kernel(
     int N, int C, const int* __restrict__ t_rowptr, const int* __restrict__ t_edge,
     const int* __restrict__ receiver, const float* __restrict__ pos, const float* __restrict__ shift,
     const float* __restrict__ x, const float* __restrict__ W, const float* __restrict__ g,
     const float* __restrict__ v_x, const float* __restrict__ v_pos, float* __restrict__ x_out,
-    float* __restrict__ p_out, float* __restrict__ qbar, float rc) {
+    float* __restrict__ p_out, float* __restrict__ qbar, float rc, const float* __restrict__ vw = nullptr,
+    float* __restrict__ wh_out = nullptr) {
   using Cfg = ConvCfg<LIN, LEDGE, LOUT>;
   using Sh = VVShape<LIN, LEDGE, LOUT, HAS_VX>;
   using GS = PathGroups<Cfg, Sh::budget>;
@@ -436,30 +468,38 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vv_sender_kernel(
     using G = typename GS::template group<gi>;
     constexpr bool FIRST = gi == 0;
     constexpr uint64_t MASK = G::comp_mask();
-    float Wr[kNB * G::NP];
-    static_for<kNB * G::NP>([&](auto i) {
-      constexpr int b = i / G::NP, pi = i % G::NP;
-      Wr[i] = act ? W[(size_t)(b * P + G::p0 + pi) * C + kk] : 0.f;
-    });
+    float Wr[XW ? 1 : kNB * G::NP];
+    if constexpr (!XW) {
+      static_for<kNB * G::NP>([&](auto i) {
+        constexpr int b = i / G::NP, pi = i % G::NP;
+        Wr[i] = act ? W[(size_t)(b * P + G::p0 + pi) * C + kk] : 0.f;
+      });
+    }
     for (int base = e0; base < e1; base += CH) {
       const int cnt = min(CH, e1 - base);
       if (wv == 0 && lane < cnt) {
         const int e = t_edge[base + lane];
         const int u = receiver[e];
         const VVGeo Gm = edge_geo(e, u);
-        float y[NE], yd[NE], R[kNB], dR[kNB], d2R[kNB];
+        float y[NE], yd[NE];
         vv_tensors<LEDGE>(Gm, y, yd);
-        radial2(Gm.r, rc, R, dR, d2R);
         float* rec = geo + lane * REC;
         static_for<NE>([&](auto c) {
           rec[c] = y[c];
           rec[NE + c] = yd[c];
         });
-        static_for<kNB>([&](auto b) {
-          rec[2 * NE + b] = R[b];
-          rec[2 * NE + kNB + b] = dR[b];
-          rec[2 * NE + 2 * kNB + b] = d2R[b];
-        });
+        if constexpr (XW) {
+          rec[2 * NE] = __int_as_float(e);
+          rec[2 * NE + 1] = Gm.r > 0.f ? 1.f : 0.f;
+        } else {
+          float R[kNB], dR[kNB], d2R[kNB];
+          radial2(Gm.r, rc, R, dR, d2R);
+          static_for<kNB>([&](auto b) {
+            rec[2 * NE + b] = R[b];
+            rec[2 * NE + kNB + b] = dR[b];
+            rec[2 * NE + 2 * kNB + b] = d2R[b];
+          });
+        }
         rec[2 * NE + 3 * kNB] = Gm.nd;
         rec[2 * NE + 3 * kNB + 1] = __int_as_float(u);
       }
@@ -480,6 +520,19 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vv_sender_kernel(
         });
         float red[NRED];
         static_for<NRED>([&](auto i) { red[i] = 0.f; });
+        float we[XW ? G::NP : 1], wve[XW ? G::NP : 1];
+        [[maybe_unused]] size_t erow = 0;
+        [[maybe_unused]] float valid = 1.f;
+        if constexpr (XW) {
+          // lanes past the last channel read channel 0 and must add nothing
+          // to the per-edge row sums
+          valid = act ? rec[2 * NE + 1] : 0.f;
+          erow = (size_t)uniform_int(__float_as_int(rec[2 * NE])) * P * C + kk;
+          static_for<G::NP>([&](auto pi) {
+            we[pi] = valid * W[erow + (size_t)(G::p0 + pi) * C];
+            wve[pi] = vw ? valid * vw[erow + (size_t)(G::p0 + pi) * C] : 0.f;
+          });
+        }
         static_for<G::NP>([&](auto pi) {
           constexpr int p = G::p0 + pi;
           constexpr PathInfo PI = Cfg::paths[p];
@@ -488,14 +541,19 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vv_sender_kernel(
           constexpr int lo = G::loff(p);
           constexpr int tb = tab::kTermBegin[PI.type], te = tab::kTermBegin[PI.type + 1];
           float w = 0.f, w1 = 0.f, w2 = 0.f;
-          static_for<kNB>([&](auto b) {
-            constexpr int bb = b;
-            const float wb = Wr[bb * G::NP + pi];
-            w = fmaf(rec[2 * NE + bb], wb, w);
-            w1 = fmaf(rec[2 * NE + kNB + bb], wb, w1);
-            if constexpr (NEED_POS) w2 = fmaf(rec[2 * NE + 2 * kNB + bb], wb, w2);
-          });
-          const float wd = w1 * nd;
+          if constexpr (XW) {
+            w = we[pi];
+            w1 = wve[pi];   // enters J_y^T with coefficient 1 (no nd factor)
+          } else {
+            static_for<kNB>([&](auto b) {
+              constexpr int bb = b;
+              const float wb = Wr[bb * G::NP + pi];
+              w = fmaf(rec[2 * NE + bb], wb, w);
+              w1 = fmaf(rec[2 * NE + kNB + bb], wb, w1);
+              if constexpr (NEED_POS) w2 = fmaf(rec[2 * NE + 2 * kNB + bb], wb, w2);
+            });
+          }
+          const float wd = XW ? w1 : w1 * nd;
           if constexpr (NEED_X) {
             // x_hat[b1] += sum c g[a] (w ydot[b2] + wdot y[b2])
             float gw[na], gd[na];
@@ -509,7 +567,7 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vv_sender_kernel(
               xh[o1 + T.b1] = fmaf(T.c * rec[o2 + T.b2], gd[T.a], t);
             });
           }
-          if constexpr (NEED_POS) {
+          if (NEED_POS || (XW && wh_out)) {
             float be[n2], al[HAS_VX ? n2 : 1];
             static_for<n2>([&](auto c) {
               be[c] = 0.f;
@@ -532,9 +590,13 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vv_sender_kernel(
                 red[IYA + o2 + c] = fmaf(w, al[c], red[IYA + o2 + c]);
               }
             });
-            red[IS] = fmaf(w1, ay + bd, red[IS]);
-            red[IS + 1] = fmaf(w2, by, red[IS + 1]);
-            red[IS + 2] = fmaf(w1, by, red[IS + 2]);
+            if constexpr (XW) {
+              if (wh_out && act) wh_out[erow + (size_t)p * C] = valid * (ay + bd);
+            } else {
+              red[IS] = fmaf(w1, ay + bd, red[IS]);
+              red[IS + 1] = fmaf(w2, by, red[IS + 1]);
+              red[IS + 2] = fmaf(w1, by, red[IS + 2]);
+            }
           }
         });
         if constexpr (NEED_POS) {
@@ -569,7 +631,7 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vv_sender_kernel(
             // J_y^T (Ya + nd Yd) = (gA - n (n.gA)) / r, gA = grad_n of (Ya + nd Yd) . y
             float cA[NE];
             static_for<NE>([&](auto c) {
-              cA[c] = Gm.nd * tot[IYD + c];
+              cA[c] = XW ? tot[IYD + c] : Gm.nd * tot[IYD + c];
               if constexpr (HAS_VX) cA[c] += tot[IYA + c];
             });
             float gA[3], HA[6], gB[3], HB[6];
@@ -637,7 +699,7 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vv_sender_kernel(
   }
 }
 
-template <int LIN, int LEDGE, int LOUT, bool HAS_VX>
+template <int LIN, int LEDGE, int LOUT, bool HAS_VX, bool XW = false>
 void launch_vv_sender_vx(const ConvArgs& a, const VjpWorkspace& wsl, hipStream_t st) {
   const bool nx = a.x_bar != nullptr, np = a.pos_bar != nullptr;
   const int nw = (a.C + kWave - 1) / kWave;
@@ -646,13 +708,14 @@ void launch_vv_sender_vx(const ConvArgs& a, const VjpWorkspace& wsl, hipStream_t
   dim3 grid(a.N, wsl.S), block(nw * kWave);
   using Sh = VVShape<LIN, LEDGE, LOUT, HAS_VX>;
   const size_t lds = Sh::lds_bytes(np ? nw : 0, Sh::CH);
-#define FC_VV(NX, NP)                                                                                                 \
-  hipLaunchKernelGGL((conv_vv_sender_kernel<LIN, LEDGE, LOUT, HAS_VX, NX, NP, Sh::CH>), grid, block, lds, st, a.N, a.C, \
-                     a.t_rowptr, a.t_edge, a.receiver, a.pos, a.shift, a.x, a.W, a.g, a.v_x, a.v_pos, xo, po,   \
-                     wsl.rbar, a.rc)
+#define FC_VV(NX, NP)                                                                                    \
+  hipLaunchKernelGGL((conv_vv_sender_kernel<LIN, LEDGE, LOUT, HAS_VX, NX, NP, Sh::CH, XW>), grid, block, lds, st, \
+                     a.N, a.C, a.t_rowptr, a.t_edge, a.receiver, a.pos, a.shift, a.x, XW ? a.w_edge : a.W, a.g,  \
+                     a.v_x, a.v_pos, xo, po, wsl.rbar, a.rc, a.v_w_edge, XW ? a.w_edge_bar : nullptr)
   if (nx && np) FC_VV(true, true);
   else if (nx) FC_VV(true, false);
-  else FC_VV(false, true);
+  else if (np || !XW) FC_VV(false, true);
+  else if constexpr (XW) FC_VV(false, false);   // w_hat alone
 #undef FC_VV
 }
 
@@ -666,6 +729,19 @@ void launch_vjp_vjp(const ConvArgs& a, hipStream_t st) {
   if (!a.x_bar && !a.pos_bar) return;
   if (a.v_x) launch_vv_sender_vx<LIN, LEDGE, LOUT, true>(a, wsl, st);
   else launch_vv_sender_vx<LIN, LEDGE, LOUT, false>(a, wsl, st);
+  launch_vjp_combine(a, wsl, nrank(LIN), st);
+}
+
+// Explicit per-edge weights w = a.w_edge [E][P][C] (receiver-sorted edge
+// order) with cotangent a.v_w_edge (nullable): g_hat, then x_hat / pos_hat
+// and w_hat (a.w_edge_bar), each when requested.  The workspace is the VJP's.
+template <int LIN, int LEDGE, int LOUT>
+void launch_vjp_vjp_w(const ConvArgs& a, hipStream_t st) {
+  if (a.g_hat) launch_vv_recv<LIN, LEDGE, LOUT, true>(a, st);
+  if (!a.x_bar && !a.pos_bar && !a.w_edge_bar) return;
+  const VjpWorkspace wsl(a.N, a.E, a.C, nrank(LIN), ConvCfg<LIN, LEDGE, LOUT>::P, true, a.rbar);
+  if (a.v_x) launch_vv_sender_vx<LIN, LEDGE, LOUT, true, true>(a, wsl, st);
+  else launch_vv_sender_vx<LIN, LEDGE, LOUT, false, true>(a, wsl, st);
   launch_vjp_combine(a, wsl, nrank(LIN), st);
 }
 

@@ -74,6 +74,7 @@ _SIGS = {
     "fc_edge_conv_vjp_vjp": (_I, [_PD, _PG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "fc_edge_conv_fwd_w": (_I, [_PD, _PG, _P, _P, _P, _P, _P, _P]),
     "fc_edge_conv_vjp_w": (_I, [_PD, _PG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "fc_edge_conv_vjp_vjp_w": (_I, [_PD, _PG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "fc_ladder_layout": (_I, [_PL, _PSZ, _PSZ]),
     "fc_ladder_workspace_bytes": (_SZ, [_PL, _I]),
     "fc_ladder_weight_block": (_I, [_PL, _I, _PSZ, _PI, _PI, _PI]),
@@ -298,6 +299,15 @@ def fc_edge_conv_vjp_vjp(d: ConvDesc, graph: DeviceGraph, pos, shift, x, radial_
                                       _f32(x), _f32(radial_w), _f32(g_z), _f32(v_x), _f32(v_pos),
                                       _f32(v_radial_w), _f32(g_hat), _f32(x_hat), _f32(pos_hat),
                                       _f32(radial_w_hat), _ptr(workspace), nbytes, _stream(stream)))
+
+
+def fc_edge_conv_vjp_vjp_w(d: ConvDesc, graph: DeviceGraph, pos, shift, x, w, g_z, v_x, v_pos, v_w,
+                           g_hat, x_hat, pos_hat, w_hat, workspace, stream=None):
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().fc_edge_conv_vjp_vjp_w(ctypes.byref(d), ctypes.byref(graph.struct), _f32(pos), _f32(shift),
+                                        _f32(x), _f32(w), _f32(g_z), _f32(v_x), _f32(v_pos), _f32(v_w),
+                                        _f32(g_hat), _f32(x_hat), _f32(pos_hat), _f32(w_hat), _ptr(workspace),
+                                        nbytes, _stream(stream)))
 
 
 # ------------------------------------------------------------------ ladder --

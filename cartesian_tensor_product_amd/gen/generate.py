@@ -536,6 +536,17 @@ def emit_instances(gen_dir: str) -> list:
         f = os.path.join(gen_dir, f"conv_inst_{a}{b}{c}.hip")
         _write(f, src)
         files.append(f)
+        if vv:
+            # the explicit-weight VJP-of-VJP in a unit of its own (compiles in parallel)
+            src = (f"// Generated by cartesian_tensor_product_amd/gen/generate.py -- do not edit.\n"
+                   f"#include \"../fc_conv_vv.h\"\n\n"
+                   f"namespace fc {{\n\n"
+                   f"void conv_run_w_{a}{b}{c}(const ConvArgs& args, hipStream_t stream) {{\n"
+                   f"  launch_vjp_vjp_w<{a}, {b}, {c}>(args, stream);\n"
+                   f"}}\n\n}}  // namespace fc\n")
+            f = os.path.join(gen_dir, f"conv_inst_{a}{b}{c}w.hip")
+            _write(f, src)
+            files.append(f)
     return files
 
 

@@ -208,6 +208,25 @@ fc_status fc_edge_conv_vjp_vjp(const fc_conv_desc* d, const fc_graph* g, const f
                                float* pos_hat, float* radial_w_hat, void* workspace,
                                size_t workspace_bytes, hipStream_t stream);
 
+/* VJP-of-VJP of the explicit-weight convolution (App. C Eq. C2; the inputs
+ * and outputs of Alg. 3, with the direction cotangent carried on to the
+ * positions): for s = <v_x, x_grad> + <v_pos, pos_grad> + <v_w, w_grad> of
+ * fc_edge_conv_vjp_w (v_x [N][in_rows][C], v_pos [N][3], v_w [E][P][C] in
+ * receiver-sorted edge order; a NULL cotangent is zero), writes
+ * g_hat = ds/dg_z [N][out_rows][C], x_hat = ds/dx [N][in_rows][C],
+ * pos_hat = ds/dpos [N][3] and w_hat = ds/dw [E][P][C], i.e.
+ * w_hat[e, eta, k] = <g_z[u_e], f_eta(v_x[v_e], y_e) + f_eta(x[v_e], J_y dv_e)>
+ * (each when non-NULL; at least one).  An edge of zero length takes no part
+ * (its w_hat is 0).  Needs g_z, the graph transpose and a workspace of
+ * fc_edge_conv_workspace_bytes(d, 1) bytes unless only g_hat is requested.
+ * Ranks as fc_edge_conv_vjp_vjp. */
+fc_status fc_edge_conv_vjp_vjp_w(const fc_conv_desc* d, const fc_graph* g, const float* pos,
+                                 const float* shift, const float* x, const float* w,
+                                 const float* g_z, const float* v_x, const float* v_pos,
+                                 const float* v_w, float* g_hat, float* x_hat, float* pos_hat,
+                                 float* w_hat, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * The pages' radial network (App. E "Model architecture", the weights
  * w_{eta k}(r) of Eq. E1; App. F "Model architecture and training"):

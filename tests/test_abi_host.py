@@ -178,3 +178,18 @@ def test_message_block_weight_count_matches_oracle():
         assert fc.fc_message_block_workspace_bytes(cd, ld) > 0
     bad = fc.ladder_desc(216, 32, 3, 3, 1, 3, fc.FC_LADDER_PATH_REDUCED)   # ladder l_out must be 0
     assert fc.fc_message_block_weight_floats(fc.conv_desc(216, 1000, 32, 0, 3, 3, 5.0), bad) == 0
+
+
+def test_vjp_vjp_w_argument_checks():
+    """The explicit-weight VJP-of-VJP rejects an uninstantiated rank set and
+    a call with no output on the host (no GPU call)."""
+    import ctypes
+    L = fc.lib()
+    g = fc.Graph()
+    d = fc.conv_desc(4, 8, 8, 5, 5, 5, 5.0)
+    st = L.fc_edge_conv_vjp_vjp_w(ctypes.byref(d), ctypes.byref(g), *([None] * 12), None, 0, None)
+    assert st == fc.FC_ERR_UNSUPPORTED
+    d = fc.conv_desc(4, 8, 8, 2, 2, 2, 5.0)
+    st = L.fc_edge_conv_vjp_vjp_w(ctypes.byref(d), ctypes.byref(g), *([None] * 12), None, 0, None)
+    assert st == fc.FC_ERR_INVALID_ARGUMENT
+    assert b"no output requested" in L.fc_last_error_message()

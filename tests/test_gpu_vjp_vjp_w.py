@@ -1,0 +1,169 @@
+"""GPU parity of the explicit-weight VJP-of-VJP (per-edge weights w [E, P, C]
+given, App. C Eq. C2 with the inputs and outputs of Alg. 3; the direction
+cotangent carried on to the positions) against the oracle's complex-step
+derivatives of the explicit-weight VJP."""
+import numpy as np
+import pytest
+
+from cartesian_tensor_product_amd import inputs
+from oracle import conv
+from tests.gpu_common import assert_close, f64, sample_edges
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+class GpuConvVVW:
+    def __init__(self, ranks, d, C, rc=6.0, flags=0):
+        from cartesian_tensor_product_amd import flashcart as fc
+        self.fc = fc
+        self.N, self.E, self.C = d["pos"].shape[0], int(len(d["sender"])), C
+        self.desc = fc.conv_desc(self.N, self.E, C, *ranks, rc, flags=flags)
+        self.P, self.nin, self.nout = fc.fc_conv_layout(self.desc)
+        self.graph = fc.DeviceGraph(d["rowptr"], d["sender"], self.N, device="cuda")
+        self.t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        self.pos, self.shift, self.x, self.w, self.g = (self.t(d["pos"]), self.t(d.get("shift")), self.t(d["x"]),
+                                                        self.t(d["w"]), self.t(d["g"]))
+        self.ws = fc.workspace(fc.fc_edge_conv_workspace_bytes(self.desc, 1), "cuda")
+
+    def vv(self, v_x=None, v_pos=None, v_w=None, want=("g", "x", "pos", "w"), g=None):
+        gh = torch.empty((self.N, self.nout, self.C), device="cuda") if "g" in want else None
+        xh = torch.empty_like(self.x) if "x" in want else None
+        ph = torch.empty((self.N, 3), device="cuda") if "pos" in want else None
+        wh = torch.empty_like(self.w) if "w" in want else None
+        self.fc.fc_edge_conv_vjp_vjp_w(self.desc, self.graph, self.pos, self.shift, self.x, self.w,
+                                       self.g if g is None else self.t(g), self.t(v_x), self.t(v_pos),
+                                       self.t(v_w), gh, xh, ph, wh, self.ws)
+        return gh, xh, ph, wh
+
+
+def oracle_vvw(spec, d, v_x, v_pos, v_w, edges=None):
+    return conv.edge_conv_vjp_vjp_w(spec, f64(d["pos"]), d["rowptr"], d["sender"], f64(d["x"]), d["w"],
+                                    f64(d["g"]), v_x=f64(v_x), v_pos=f64(v_pos), v_w=f64(v_w),
+                                    shift=f64(d.get("shift")), edges=edges)
+
+
+def cotangents(d, seed, with_vx=True, with_vpos=True, with_vw=True):
+    rng = np.random.default_rng(seed)
+    v_x = inputs.normal(rng, d["x"].shape) if with_vx else None
+    v_pos = inputs.normal(rng, d["pos"].shape) if with_vpos else None
+    v_w = inputs.edge_weights(rng, *d["w"].shape) if with_vw else None
+    return v_x, v_pos, v_w
+
+
+def small(ranks, C, seed=11, n=40, k=12, box=5.0, rc=6.0, **kw):
+    spec = conv.ConvSpec(*ranks, rc, **kw)
+    return spec, inputs.edge_conv_inputs(seed, n, k, box, C, spec.n_in, spec.n_paths, spec.n_out, with_edge_w=True)
+
+
+def check(spec, ranks, d, C, cots, flags=0, rc=6.0):
+    gc = GpuConvVVW(ranks, d, C, rc, flags)
+    out = gc.vv(*cots)
+    torch.cuda.synchronize()
+    ref = oracle_vvw(spec, d, *cots)
+    for name, a, b in zip(("g_hat", "x_hat", "pos_hat", "w_hat"), out, ref):
+        assert_close(name, a.cpu().numpy(), b)
+    return gc, ref
+
+
+@pytest.mark.parametrize("ranks", [(0, 0, 0), (1, 1, 1), (2, 2, 2), (3, 3, 3), (4, 4, 4), (0, 3, 3), (1, 2, 2),
+                                   (2, 4, 4), (3, 4, 4)])
+@pytest.mark.parametrize("with_vx", [False, True])
+def test_vjp_vjp_w_every_rank_set(ranks, with_vx):
+    spec, d = small(ranks, 24)
+    check(spec, ranks, d, 24, cotangents(d, 8, with_vx=with_vx))
+
+
+@pytest.mark.parametrize("ranks", [(1, 1, 1), (3, 3, 3)])
+def test_vjp_vjp_w_all_parities(ranks):
+    from cartesian_tensor_product_amd import flashcart as fc
+    spec, d = small(ranks, 24, all_parities=True)
+    check(spec, ranks, d, 24, cotangents(d, 9), flags=fc.FC_CONV_ALL_PARITIES)
+
+
+@pytest.mark.parametrize("ranks", [(2, 2, 2), (3, 3, 3)])
+def test_vjp_vjp_w_summed_paths(ranks):
+    from cartesian_tensor_product_amd import flashcart as fc
+    spec, d = small(ranks, 24, sum_paths=True)
+    check(spec, ranks, d, 24, cotangents(d, 10), flags=fc.FC_CONV_SUM_PATHS)
+
+
+@pytest.mark.parametrize("C", [1, 65, 256])
+def test_vjp_vjp_w_channel_tiles(C):
+    """One partial channel wave, a ragged second wave, four waves (the rank-4
+    sender then stages fewer edges per chunk); senders of about 40 edges."""
+    ranks = (4, 4, 4) if C == 256 else (2, 2, 2)
+    spec, d = small(ranks, C, seed=3, n=60, k=40, box=6.0)
+    check(spec, ranks, d, C, cotangents(d, 4))
+
+
+def test_vjp_vjp_w_zero_length_edge_and_subsets():
+    """Coincident atoms give an edge of zero length, which takes no part (its
+    w_hat is 0); each output on its own, and each cotangent on its own."""
+    ranks = (2, 2, 2)
+    spec, d = small(ranks, 32, seed=5)
+    recv = np.repeat(np.arange(40), np.diff(d["rowptr"]))
+    e0 = 7
+    d["pos"][d["sender"][e0]] = d["pos"][recv[e0]]
+    cots = cotangents(d, 6)
+    gc, ref = check(spec, ranks, d, 32, cots)
+    for want, i in ((("g",), 0), (("x",), 1), (("pos",), 2), (("w",), 3)):
+        out = gc.vv(*cots, want=want)
+        torch.cuda.synchronize()
+        assert_close(want[0], out[i].cpu().numpy(), ref[i])
+    assert float(gc.vv(*cots, want=("w",))[3][e0].abs().max()) == 0.0
+    for j in range(3):
+        one = [c if i == j else None for i, c in enumerate(cots)]
+        out = gc.vv(*one)
+        torch.cuda.synchronize()
+        r = oracle_vvw(spec, d, *one)
+        for name, a, b in zip(("g_hat", "x_hat", "pos_hat", "w_hat"), out, r):
+            assert_close(f"{name} (cotangent {j} alone)", a.cpu().numpy(), b)
+
+
+def test_vjp_vjp_w_matches_radial_form():
+    """With w = R(r) W and v_w = R'(r) (r_hat . dv) W (the weight cotangent
+    that the position cotangent induces through the radial basis), g_hat and
+    x_hat equal those of the radial-weight VJP-of-VJP (pos_hat differs by the
+    radial chain terms, which the explicit-weight form leaves to the caller)."""
+    ranks = (2, 2, 2)
+    spec = conv.ConvSpec(*ranks, 6.0)
+    d = inputs.edge_conv_inputs(12, 40, 12, 5.0, 16, spec.n_in, spec.n_paths, spec.n_out, with_vpos=True)
+    recv = np.repeat(np.arange(40), np.diff(d["rowptr"]))
+    r = d["pos"][d["sender"]] - d["pos"][recv]
+    rl = np.linalg.norm(r.astype(np.float64), axis=1)
+    R, dR = conv.radial(rl, 8, 6.0), conv.radial_deriv(rl, 8, 6.0)
+    d["w"] = np.einsum("eb,bpk->epk", R, d["W"].astype(np.float64)).astype(np.float32)
+    dv = d["v_pos"][d["sender"]] - d["v_pos"][recv]
+    nd = np.einsum("ei,ei->e", r / rl[:, None], dv)
+    v_w = np.einsum("eb,bpk->epk", dR * nd[:, None], d["W"].astype(np.float64)).astype(np.float32)
+    gc = GpuConvVVW(ranks, d, 16)
+    gh, xh, _, _ = gc.vv(v_pos=d["v_pos"], v_w=v_w)
+    torch.cuda.synchronize()
+    go, xo, _, _ = conv.edge_conv_vjp_vjp(spec, f64(d["pos"]), d["rowptr"], d["sender"], f64(d["x"]), f64(d["W"]),
+                                       f64(d["g"]), v_pos=f64(d["v_pos"]))
+    assert_close("g_hat", gh.cpu().numpy(), go)
+    assert_close("x_hat", xh.cpu().numpy(), xo)
+
+
+def test_vjp_vjp_w_microbenchmark_sampled():
+    """1024 nodes x 128 neighbours x 128 channels, ranks <= 2, every
+    cotangent: sampled nodes element by element and w_hat on every edge into
+    or out of them; a second call is bitwise equal."""
+    ranks = (2, 2, 2)
+    spec = conv.ConvSpec(*ranks, 5.0)
+    d = inputs.edge_conv_inputs(1, 1024, 128, 20.0, 128, spec.n_in, spec.n_paths, spec.n_out, with_edge_w=True)
+    cots = cotangents(d, 77)
+    gc = GpuConvVVW(ranks, d, 128, 5.0)
+    out = gc.vv(*cots)
+    torch.cuda.synchronize()
+    nodes = np.random.default_rng(99).choice(1024, size=8, replace=False)
+    edges = sample_edges(d["rowptr"], d["sender"], nodes)
+    ref = oracle_vvw(spec, d, *cots, edges=edges)
+    for name, a, b in zip(("g_hat", "x_hat", "pos_hat"), out[:3], ref[:3]):
+        assert_close(name, a.cpu().numpy()[nodes], b[nodes])
+    assert_close("w_hat", out[3][torch.from_numpy(edges).cuda()].cpu().numpy(), ref[3][edges])
+    again = gc.vv(*cots)
+    torch.cuda.synchronize()
+    for u, v in zip(again, out):
+        assert torch.equal(u, v)

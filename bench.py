@@ -282,6 +282,17 @@ def ladder_gemm_gflop(N, C, l, order):
     return f / 1e9
 
 
+def copy_bandwidth(mb=1024, iters=20):
+    """Device-to-device copy rate (read + write bytes per second, GB/s) of a
+    plain copy of mb MiB: the bandwidth a streaming kernel can reach here."""
+    import torch
+    src = torch.ones(mb * (1 << 20) // 4, device="cuda:0")
+    dst = torch.empty_like(src)
+    ms = timed(lambda: dst.copy_(src), iters)
+    del src, dst
+    return 2 * mb * (1 << 20) / (ms * 1e-3) / 1e9
+
+
 def algorithmic_bytes(N, E, C, n_in, n_out, P):
     """Bytes each launch must move if every per-edge gather goes to memory.
 
@@ -491,8 +502,17 @@ def main():
         "breakdown": {"fwd_ms": f_mean, "vjp_ms": v_mean, "fwd_GBs_alg": b_fwd / (f_mean * 1e-3) / 1e9,
                       "vjp_GBs_alg": b_vjp / (v_mean * 1e-3) / 1e9,
                       "fwd_plus_vjp_frac_hbm": (b_fwd + b_vjp) / ((f_mean + v_mean) * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                      "wall_s": wall},
+                      "wall_s": wall,
+                      "fwd_ms_p10_p50_p90": [float(np.percentile(t_fwd, q)) for q in (10, 50, 90)],
+                      "vjp_ms_p10_p50_p90": [float(np.percentile(t_vjp, q)) for q in (10, 50, 90)],
+                      "vjp_workspace_bytes": fc.fc_edge_conv_workspace_bytes(desc, 1),
+                      # the byte model of a receiver-sorted VJP with atomic x_bar
+                      # updates (gather x and add into x_bar per edge-channel)
+                      "vjp_bytes_receiver_atomics_model": 2 * E * CHANNELS * n_in * 4 + N_NODES * n_out * CHANNELS * 4},
     }
+    cbw = copy_bandwidth()
+    out["breakdown"]["copy_GBs_measured"] = cbw
+    out["breakdown"]["fwd_plus_vjp_frac_copy"] = (b_fwd + b_vjp) / ((f_mean + v_mean) * 1e-3) / 1e9 / cbw
     if not args.no_extras:
         # explicit per-edge weights w [E, P, C] (the pages' own interface),
         # same workload; w drawn on the device from a seeded generator

@@ -460,38 +460,54 @@ __global__ __launch_bounds__(kWave) void ladder_first_tangent_kernel(int N, int 
 }
 
 // Reverse of phi^1 = a1 A with tangents: A_hat += a1 G' + b1 G (nullable
-// terms), part[blk][l][k] = sum_{u in tile, c} (G' A + G v_A).
-__global__ __launch_bounds__(kWave) void ladder_first_reverse_kernel(int N, int C, int ntile, int lq1, int a_rows,
-                                                                     int grows, const float* __restrict__ G,
-                                                                     const float* __restrict__ dG,
-                                                                     const float* __restrict__ A,
-                                                                     const float* __restrict__ vA,
-                                                                     const float* __restrict__ a1,
-                                                                     const float* __restrict__ b1,
-                                                                     float* __restrict__ A_hat,
-                                                                     float* __restrict__ part) {
-  const int k = blockIdx.y * kWave + threadIdx.x;
-  if (k >= C) return;
+// terms), part[blk][l][k] = sum_{u in tile, c} (G' A + G v_A).  Eight waves
+// per block share the rows of a tile of nodes (wave w takes rows w, w + 8,
+// ...), each walking the tile's nodes with independent loads; the per-rank
+// sums meet in LDS in a fixed order.
+constexpr int kRevWaves = 8;
+__global__ __launch_bounds__(kRevWaves * kWave) void ladder_first_reverse_kernel(
+    int N, int C, int ntile, int lq1, int a_rows, int grows, const float* __restrict__ G,
+    const float* __restrict__ dG, const float* __restrict__ A, const float* __restrict__ vA,
+    const float* __restrict__ a1, const float* __restrict__ b1, float* __restrict__ A_hat, float* __restrict__ part) {
+  __shared__ float red[kRevWaves][5][kWave];
+  const int wv = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int k = blockIdx.y * kWave + lane;
+  const bool act = k < C;
   const int rows = (lq1 + 1) * (lq1 + 1);
   float acc[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
   const int u0 = blockIdx.x * ntile, u1 = min(N, u0 + ntile);
-  for (int u = u0; u < u1; ++u)
-    for (int c = 0; c < rows; ++c) {
+  if (act) {
+    for (int c = wv; c < rows; c += kRevWaves) {
       int l = 0;
       while ((l + 1) * (l + 1) <= c) ++l;
-      const float g = G[((size_t)u * grows + c) * C + k];
-      const float dg = dG ? dG[((size_t)u * grows + c) * C + k] : 0.f;
-      if (A_hat) {
-        float h = a1[(size_t)l * C + k] * dg;
-        if (b1) h = fmaf(b1[(size_t)l * C + k], g, h);
-        A_hat[((size_t)u * a_rows + c) * C + k] += h;
+      const float al = a1[(size_t)l * C + k];
+      const float bl = b1 ? b1[(size_t)l * C + k] : 0.f;
+      float t = 0.f;
+#pragma unroll 4
+      for (int u = u0; u < u1; ++u) {
+        const size_t gi = ((size_t)u * grows + c) * C + k, ai = ((size_t)u * a_rows + c) * C + k;
+        const float g = G[gi];
+        const float dg = dG ? dG[gi] : 0.f;
+        if (A_hat) A_hat[ai] += fmaf(bl, g, al * dg);
+        float tt = dg * A[ai];
+        if (vA) tt = fmaf(g, vA[ai], tt);
+        t += tt;
       }
-      float t = dg * A[((size_t)u * a_rows + c) * C + k];
-      if (vA) t = fmaf(g, vA[((size_t)u * a_rows + c) * C + k], t);
-      acc[l] += t;
+#pragma unroll
+      for (int li = 0; li < 5; ++li)
+        if (li == l) acc[li] += t;
     }
-  if (part)
-    for (int l = 0; l <= lq1; ++l) part[((size_t)blockIdx.x * (lq1 + 1) + l) * C + k] = acc[l];
+  }
+  if (!part) return;
+#pragma unroll
+  for (int li = 0; li < 5; ++li) red[wv][li][lane] = acc[li];
+  __syncthreads();
+  if (wv == 0 && act)
+    for (int l = 0; l <= lq1; ++l) {
+      float s = 0.f;
+      for (int w = 0; w < kRevWaves; ++w) s += red[w][l][lane];
+      part[((size_t)blockIdx.x * (lq1 + 1) + l) * C + k] = s;
+    }
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(size_t n, float* __restrict__ p) {
@@ -1187,7 +1203,7 @@ void ladder_vjp_vjp_reduced(const LadderPlan& p, const float* A, const float* w,
     dG = dGn;
     grows = rp;
   }
-  hipLaunchKernelGGL(ladder_first_reverse_kernel, tgrid, dim3(kWave), 0, st, p.N, C, kNTile, p.lq(1), ra, grows, G,
+  hipLaunchKernelGGL(ladder_first_reverse_kernel, tgrid, dim3(kRevWaves * kWave), 0, st, p.N, C, kNTile, p.lq(1), ra, grows, G,
                      dG, A, vA, aw(w, 1), aw(vw, 1), A_hat, w_hat ? part : nullptr);
   if (w_hat) block_sum(nblk, (p.lq(1) + 1) * C, part, w_hat + p.w_a(1), st);
 }

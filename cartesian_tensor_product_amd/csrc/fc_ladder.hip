@@ -576,7 +576,17 @@ size_t LadderPlan::fwd_ws_floats() const {
 }
 
 namespace {
-constexpr int kNTile = 16;          // nodes per block in the path-reduced reverse kernels
+// Nodes per block of the path-reduced reverse kernels: a power of two from 16
+// down to the waves per block, the largest for which about 512 blocks (two
+// waves per SIMD) still cover the nodes and channel tiles.  A larger tile
+// amortises the per-block path weights and partial sums; a smaller one keeps
+// a small graph spread over the chip.
+int red_ntile(int N, int C) {
+  const int ct = (C + kWave - 1) / kWave;
+  int t = 16;
+  while (t > kRedWaves && (long long)((N + t - 1) / t) * ct < 512) t /= 2;
+  return t;
+}
 constexpr int kMixTile = 2;         // nodes per wave in the path-weight gradient on a product buffer
 constexpr int kSplitTarget = 512;   // blocks per split-K weight-gradient GEMM
 }  // namespace
@@ -601,7 +611,8 @@ size_t LadderPlan::vjp_ws_floats() const {
     part = std::max(part, g1);
     return 2 * b + 2 * st + part;
   }
-  const int nblk = (N + kNTile - 1) / kNTile;
+  const int nt = red_ntile(N, C);
+  const int nblk = (N + nt - 1) / nt;
   int pmax = 0;
   for (int q = 2; q <= order; ++q) pmax = std::max(pmax, paths(q));
   for (int L = 0; L <= lout; ++L) part += (size_t)gemm_ksplit(C, C, N * (2 * L + 1), kSplitTarget) * C2;
@@ -822,12 +833,13 @@ template <int LP, int LQ>
 void launch_red_vjp(const LadderPlan& p, bool first, const float* G, int g_rows, const float* phi, const float* A,
                     const float* Sbar, const float* aw, const float* a1, float* Gprev, float* Abar, float* apart,
                     float* a1part, hipStream_t st) {
-  dim3 grid((p.N + kNTile - 1) / kNTile, (p.C + kWave - 1) / kWave);
+  const int nt = red_ntile(p.N, p.C);
+  dim3 grid((p.N + nt - 1) / nt, (p.C + kWave - 1) / kWave);
   if (first)
-    hipLaunchKernelGGL((ladder_reduced_vjp_kernel<LP, LP, LQ, true>), grid, dim3(kRedWaves * kWave), 0, st, p.N, p.C, kNTile,
+    hipLaunchKernelGGL((ladder_reduced_vjp_kernel<LP, LP, LQ, true>), grid, dim3(kRedWaves * kWave), 0, st, p.N, p.C, nt,
                        G, g_rows, phi, A, Sbar, nr(p.lout), aw, a1, Gprev, Abar, apart, a1part);
   else
-    hipLaunchKernelGGL((ladder_reduced_vjp_kernel<LP, LP, LQ, false>), grid, dim3(kRedWaves * kWave), 0, st, p.N, p.C, kNTile,
+    hipLaunchKernelGGL((ladder_reduced_vjp_kernel<LP, LP, LQ, false>), grid, dim3(kRedWaves * kWave), 0, st, p.N, p.C, nt,
                        G, g_rows, phi, A, Sbar, nr(p.lout), aw, a1, Gprev, Abar, apart, a1part);
 }
 
@@ -993,7 +1005,8 @@ void ladder_vjp(const LadderPlan& p, const float* A, const float* w, const float
   float* S = ws;
   float* Sbar = S + (size_t)p.N * ro * C;
   float* Gbuf[2] = {Sbar + (size_t)p.N * ro * C, Sbar + (size_t)p.N * ro * C + stf};
-  const int nblk = (p.N + kNTile - 1) / kNTile;
+  const int ntile = red_ntile(p.N, p.C);
+  const int nblk = (p.N + ntile - 1) / ntile;
   int pmax = 0;
   for (int q = 2; q <= p.order; ++q) pmax = std::max(pmax, p.paths(q));
   float* apart = Gbuf[1] + stf;
@@ -1039,7 +1052,7 @@ void ladder_vjp(const LadderPlan& p, const float* A, const float* w, const float
   const float* a1 = w + p.w_a(1);
   if (p.order == 1) {
     dim3 grid(nblk, (C + kWave - 1) / kWave);
-    hipLaunchKernelGGL(ladder_reduced_first_kernel, grid, dim3(kWave), 0, st, p.N, C, kNTile, p.lout, ra,
+    hipLaunchKernelGGL(ladder_reduced_first_kernel, grid, dim3(kWave), 0, st, p.N, C, ntile, p.lout, ra,
                        (const float*)Sbar, A, a1, A_grad, a1part);
     if (w_grad) block_sum(nblk, (p.lout + 1) * C, a1part, w_grad + p.w_a(1), st);
     return;
@@ -1089,7 +1102,8 @@ void ladder_vjp_vjp_reduced(const LadderPlan& p, const float* A, const float* w,
   auto phi_of = [&](int q) -> const float* { return saved + (size_t)(q - 1) * stf; };
   auto dphi_of = [&](int q) -> float* { return q < p.order ? dphi + (size_t)(q - 1) * stf : nullptr; };
   auto aw = [&](const float* base, int q) -> const float* { return base ? base + p.w_a(q) : nullptr; };
-  const int nblk = (p.N + kNTile - 1) / kNTile;
+  const int ntile = red_ntile(p.N, p.C);
+  const int nblk = (p.N + ntile - 1) / ntile;
   const dim3 ngrid(p.N, (C + kWave - 1) / kWave), tgrid(nblk, (C + kWave - 1) / kWave);
   const bool rev = A_hat || w_hat;
   if (A_hat) fill_zero(A_hat, (size_t)p.N * ra * C, st);
@@ -1203,7 +1217,7 @@ void ladder_vjp_vjp_reduced(const LadderPlan& p, const float* A, const float* w,
     dG = dGn;
     grows = rp;
   }
-  hipLaunchKernelGGL(ladder_first_reverse_kernel, tgrid, dim3(kRevWaves * kWave), 0, st, p.N, C, kNTile, p.lq(1), ra, grows, G,
+  hipLaunchKernelGGL(ladder_first_reverse_kernel, tgrid, dim3(kRevWaves * kWave), 0, st, p.N, C, ntile, p.lq(1), ra, grows, G,
                      dG, A, vA, aw(w, 1), aw(vw, 1), A_hat, w_hat ? part : nullptr);
   if (w_hat) block_sum(nblk, (p.lq(1) + 1) * C, part, w_hat + p.w_a(1), st);
 }

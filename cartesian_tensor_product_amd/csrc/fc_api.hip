@@ -639,7 +639,8 @@ fc_status fc_node_ladder_vjp_vjp(const fc_ladder_desc* d, const float* A, const 
 namespace {
 
 struct BlockLayout {
-  size_t A, z, saved, lws, gz, Ab, cws, parts, total;   // byte offsets / total
+  size_t A, z, saved, lws, gz, Ab, wsc, cws, parts, total;   // byte offsets / total
+  size_t n_w;   // radial weight floats (wsc holds a scaled and a negated copy)
 };
 
 fc_status block_layout(const fc_conv_desc* cd, const fc_ladder_desc* ld, BlockLayout* L) {
@@ -659,6 +660,10 @@ fc_status block_layout(const fc_conv_desc* cd, const fc_ladder_desc* ld, BlockLa
   L->lws = o;    o += al(std::max(p.fwd_ws_floats(), p.vjp_ws_floats()) * 4);
   L->gz = o;     o += al(N * nz * C * 4);
   L->Ab = o;     o += al(N * nA * C * 4);
+  int P, nin, nout;
+  layout(cd, &P, &nin, &nout);
+  L->n_w = (size_t)cd->n_basis * P * C;
+  L->wsc = o;    o += al(2 * L->n_w * 4);
   L->cws = o;    o += al(fc_edge_conv_workspace_bytes(cd, 1));
   L->parts = o;  o += al((size_t)fc::block_energy_parts(cd->n_nodes) * 8);
   L->total = o;
@@ -769,19 +774,22 @@ fc_status fc_block_energy_forces(const fc_conv_desc* cd, const fc_graph* g, cons
   fc::LadderPlan p;
   ladder_plan(ld, &p);
   const int N = cd->n_nodes, C = cd->channels;
-  const int nA = (cd->l_out + 1) * (cd->l_out + 1), nz = (ld->l_out + 1) * (ld->l_out + 1);
-  if (fc_status s = fc_edge_conv_fwd(cd, g, pos, shift, x, radial_w, A, stream)) return s;
-  fc::block_scale(A, (size_t)N * nA * C, conv_scale, stream);
+  const int nz = (ld->l_out + 1) * (ld->l_out + 1);
+  // the convolution is linear in its radial weights: the scale (and, for
+  // the backward pass, the sign of F = -dE/dpos) goes into a copy of them
+  float* Wpos = reinterpret_cast<float*>(w + L.wsc);
+  float* Wneg = Wpos + L.n_w;
+  if (!radial_w) return fail(FC_ERR_INVALID_ARGUMENT, "block: NULL radial weights");
+  fc::block_scaled_weights(radial_w, L.n_w, conv_scale, Wpos, forces ? Wneg : nullptr, stream);
+  if (fc_status s = fc_edge_conv_fwd(cd, g, pos, shift, x, Wpos, A, stream)) return s;
   fc::ladder_forward(p, A, ladder_w, z, saved, lws, stream);
   fc::block_energy(z, N, nz, C, e_atom, parts, energy, stream);
   if (forces) {
     fc::block_unit_cotangent(gz, N, nz, C, stream);
     fc::ladder_vjp(p, A, ladder_w, saved, gz, Ab, nullptr, lws, stream);
-    fc::block_scale(Ab, (size_t)N * nA * C, conv_scale, stream);
-    if (fc_status s = fc_edge_conv_vjp(cd, g, pos, shift, x, radial_w, Ab, nullptr, forces, nullptr,
+    if (fc_status s = fc_edge_conv_vjp(cd, g, pos, shift, x, Wneg, Ab, nullptr, forces, nullptr,
                                        w + L.cws, L.parts - L.cws, stream))
       return s;
-    fc::block_scale(forces, (size_t)N * 3, -1.f, stream);
   }
   return check_launch("block energy/forces");
 }

@@ -5,8 +5,9 @@
 // rank-0 outputs; §2: F_u = -dE/dr_u).  Residual updates, normalisation,
 // gates and the readout carry trained weights and are not part of it.
 //
-// Small kernels used by the composition: in-place scaling, a deterministic
-// fp64 energy reduction, the unit cotangent of the energy, and negation.
+// Small kernels used by the composition: scaling (in place, and of the
+// radial weights into a scaled and a negated copy), a deterministic fp64
+// energy reduction and the unit cotangent of the energy.
 #include <hip/hip_runtime.h>
 
 #include "fc_block.h"
@@ -18,6 +19,18 @@ namespace {
 __global__ __launch_bounds__(256) void scale_kernel(size_t n, float a, float* __restrict__ p) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] *= a;
+}
+
+// pos_w = a W and neg_w = -a W (nullable): the radial weights with the
+// convolution scale folded in, for the forward and (negated, so that the
+// VJP to the positions is the force) for the backward pass.
+__global__ __launch_bounds__(256) void scaled_pair_kernel(size_t n, float a, const float* __restrict__ W,
+                                                          float* __restrict__ pos_w, float* __restrict__ neg_w) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float v = a * W[i];
+  pos_w[i] = v;
+  if (neg_w) neg_w[i] = -v;
 }
 
 // dE/dz: 1 on the rank-0 rows, 0 elsewhere.
@@ -62,6 +75,12 @@ __global__ __launch_bounds__(64) void energy_sum_kernel(int n, const double* __r
 
 void block_scale(float* p, size_t n, float a, hipStream_t st) {
   if (n) hipLaunchKernelGGL(scale_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, n, a, p);
+}
+
+void block_scaled_weights(const float* W, size_t n, float a, float* pos_w, float* neg_w, hipStream_t st) {
+  if (n)
+    hipLaunchKernelGGL(scaled_pair_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, n, a, W, pos_w,
+                       neg_w);
 }
 
 void block_unit_cotangent(float* g, int N, int rows, int C, hipStream_t st) {

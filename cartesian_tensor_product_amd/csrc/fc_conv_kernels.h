@@ -39,6 +39,17 @@ __host__ __device__ constexpr int vjp_budget(int nin, int ne) { return 200 - 2 *
 inline constexpr int kMaxVjpWaves = 4;
 // LDS one workgroup may hold on gfx950.
 inline constexpr size_t kLdsBytes = 160 * 1024;
+
+// Node of the block with x index b in a grid whose x extent is N.  The
+// dispatcher deals consecutive workgroups to the chip's eight XCDs in turn,
+// so block b runs on XCD b % 8; this numbering gives each XCD one contiguous
+// range of nodes, so that when the nodes are numbered in space (a lattice, a
+// sorted cell list) the neighbour rows an XCD gathers meet in its own L2.
+// A bijection of [0, N) for any N.
+__device__ __forceinline__ int xcd_node(int b, int N) {
+  const int q = N >> 3, r = N & 7, k = b & 7;
+  return k * q + (k < r ? k : r) + (b >> 3);
+}
 // Per-edge products |c| y[g] are broadcast from LDS when a configuration uses
 // at most this many; larger tables multiply inline from y.
 inline constexpr int kCYMax = 48;
@@ -130,7 +141,7 @@ __global__ __launch_bounds__(kWave) void conv_fwd_kernel(
   constexpr int REC = EP::NY + kNB + 1;
   __shared__ float geo[kWave * REC];
 
-  const int u = blockIdx.x;
+  const int u = xcd_node(blockIdx.x, N);
   const int lane = threadIdx.x;
   const int k = blockIdx.y * kWave + lane;
   const bool act = k < C;
@@ -428,7 +439,9 @@ __device__ __forceinline__ float row_sum16(float v) {
 // position cotangent is absent (w is held fixed), the first radial slot of
 // the edge record flags an edge of nonzero length, and (wb_out non-null)
 // w_bar[e, p, k] = <g_p, f_p(x, y)> is stored per edge.
-template <int LIN, int LEDGE, int LOUT, bool NEED_X, bool NEED_POS, bool XW>
+// CH: edges staged per chunk (the shape's default, or 32 for short slices,
+// which halves the block's LDS).
+template <int LIN, int LEDGE, int LOUT, bool NEED_X, bool NEED_POS, bool XW, int CH = VjpShape<LIN, LEDGE, LOUT>::CH>
 __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
     int N, int C, const int* __restrict__ t_rowptr, const int* __restrict__ t_edge,
     const int* __restrict__ receiver, const float* __restrict__ pos,
@@ -444,11 +457,10 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
   using GS = PathGroups<Cfg, Sh::budget>;
   extern __shared__ float lds[];
   float* geo = lds;                      // [CH][REC]
-  constexpr int CH = Sh::CH;
   float* part = lds + CH * REC;          // [NW][CH edges][NRED][4 rows]
   const int NW = blockDim.x / kWave;
 
-  const int v = blockIdx.x;
+  const int v = xcd_node(blockIdx.x, N);
   const int S = gridDim.y, sl = blockIdx.y;   // slice sl of S of v's outgoing edges
   const int tid = threadIdx.x;
   const int wv = tid / kWave, lane = tid % kWave;
@@ -742,11 +754,27 @@ void launch_vjp(const ConvArgs& a, hipStream_t st) {
   float* xo = wsl.S == 1 ? a.x_bar : wsl.x_part;
   float* po = wsl.S == 1 ? a.pos_bar : wsl.p_part;
   dim3 grid(a.N, wsl.S), block(nw * kWave);
-  const size_t lds = VjpShape<LIN, LEDGE, LOUT>::lds_bytes(np ? nw : 0, VjpShape<LIN, LEDGE, LOUT>::CH);
-#define FC_VJP(NX, NP, XW)                                                                                          \
-  hipLaunchKernelGGL((conv_vjp_sender_kernel<LIN, LEDGE, LOUT, NX, NP, XW>), grid, block, lds, st, a.N, a.C,        \
-                     a.t_rowptr, a.t_edge, a.receiver, a.pos, a.shift, a.x, XW ? a.w_edge : a.W, a.g, xo, po,        \
-                     wsl.rbar, a.w_edge_bar, a.rc)
+  using Sh = VjpShape<LIN, LEDGE, LOUT>;
+  // slices of at most 32 edges on average (e.g. 128 or fewer neighbours in
+  // four slices) stage 32 edges per chunk when the block's LDS at 64 would
+  // keep four blocks from sharing a CU (it then holds half as much; at ranks
+  // <= 2 the registers, not the LDS, limit the blocks per CU)
+  const bool short_slices = (long long)a.E <= 32LL * a.N * wsl.S &&
+                            Sh::lds_bytes(np ? nw : 0, Sh::CH) > kLdsBytes / 4;
+#define FC_VJP_CH(NX, NP, XW, CHV)                                                                                   \
+  hipLaunchKernelGGL((conv_vjp_sender_kernel<LIN, LEDGE, LOUT, NX, NP, XW, CHV>), grid, block,                      \
+                     Sh::lds_bytes(np ? nw : 0, CHV), st, a.N, a.C, a.t_rowptr, a.t_edge, a.receiver, a.pos,         \
+                     a.shift, a.x, XW ? a.w_edge : a.W, a.g, xo, po, wsl.rbar, a.w_edge_bar, a.rc)
+#define FC_VJP(NX, NP, XW)                          \
+  do {                                              \
+    if constexpr (Sh::CH > 32) {                    \
+      if (short_slices) {                           \
+        FC_VJP_CH(NX, NP, XW, 32);                  \
+        break;                                      \
+      }                                             \
+    }                                               \
+    FC_VJP_CH(NX, NP, XW, Sh::CH);                  \
+  } while (0)
   if (a.w_edge) {
     if (nx && np) FC_VJP(true, true, true);
     else if (nx) FC_VJP(true, false, true);
@@ -758,6 +786,7 @@ void launch_vjp(const ConvArgs& a, hipStream_t st) {
     else FC_VJP(false, true, false);
   }
 #undef FC_VJP
+#undef FC_VJP_CH
   launch_vjp_combine(a, wsl, nrank(LIN), st);
 }
 

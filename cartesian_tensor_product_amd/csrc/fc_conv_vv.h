@@ -71,7 +71,7 @@ __global__ __launch_bounds__(kWave) void conv_vv_recv_kernel(
   constexpr int REC = 2 * NE + 2 * kNB + 2;   // y, ydot, R, R', nd, sender
   __shared__ float geo[kWave * REC];
 
-  const int u = blockIdx.x;
+  const int u = xcd_node(blockIdx.x, N);
   const int lane = threadIdx.x;
   const int k = blockIdx.y * kWave + lane;
   const bool act = k < C;
@@ -419,7 +419,7 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vv_sender_kernel(
   float* part = lds + CH * REC;
   const int NW = blockDim.x / kWave;
 
-  const int v = blockIdx.x;
+  const int v = xcd_node(blockIdx.x, N);
   const int S = gridDim.y, sl = blockIdx.y;
   const int tid = threadIdx.x;
   const int wv = tid / kWave, lane = tid % kWave;

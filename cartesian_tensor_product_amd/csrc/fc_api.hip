@@ -88,7 +88,7 @@ fc_status check_desc(const fc_conv_desc* d) {
   if (d->channels > 256) return fail(FC_ERR_UNSUPPORTED, "channels above 256 are not supported");
   if (!fc::conv_supported(d->l_in, d->l_edge, lout_key(d)))
     return fail(FC_ERR_UNSUPPORTED,
-                "(l_in, l_edge, l_out) = (%d, %d, %d) with flags 0x%x is not instantiated in this build", d->l_in,
+                "(l_in, l_edge, l_out) = (%d, %d, %d) with flags 0x%x is not instantiated in this library", d->l_in,
                 d->l_edge, d->l_out, d->flags);
   return FC_OK;
 }
@@ -219,7 +219,7 @@ fc_status ladder_plan(const fc_ladder_desc* d, fc::LadderPlan* p) {
   if (d->order > 8) return fail(FC_ERR_UNSUPPORTED, "ladder: order above 8 is not supported");
   if (d->l_a < 0 || d->l_prod < 0 || d->l_out < 0) return fail(FC_ERR_INVALID_ARGUMENT, "ladder: negative rank");
   if (d->l_a != d->l_prod || d->l_prod < 1 || d->l_prod > 4 || d->l_out > d->l_prod)
-    return fail(FC_ERR_UNSUPPORTED, "ladder: this build needs l_a == l_prod in 1..4 and l_out <= l_prod");
+    return fail(FC_ERR_UNSUPPORTED, "ladder: the library needs l_a == l_prod in 1..4 and l_out <= l_prod");
   *p = fc::LadderPlan{d->n_nodes, d->channels, d->l_a, d->l_prod, d->l_out, d->order, d->variant};
   return FC_OK;
 }

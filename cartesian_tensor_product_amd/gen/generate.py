@@ -515,7 +515,7 @@ def emit_instances(gen_dir: str) -> list:
     """One translation unit per convolution configuration, plus the list."""
     cfgs = conv_configs()
     lines = ["// Generated by cartesian_tensor_product_amd/gen/generate.py -- do not edit.",
-             "// (l_in, l_edge, l_out) instantiated in this build.", "#pragma once", "",
+             "// (l_in, l_edge, l_out) instantiated in the library.", "#pragma once", "",
              "#define FC_CONV_CONFIGS(X) \\"]
     lines += [f"  X({a}, {b}, {c}) \\" for a, b, c in cfgs]
     lines += ["", "", "// ... of which the VJP-of-VJP is instantiated for", "#define FC_CONV_VV_CONFIGS(X) \\"]

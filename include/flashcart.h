@@ -69,7 +69,7 @@ extern "C" {
 typedef enum {
   FC_OK = 0,
   FC_ERR_INVALID_ARGUMENT = 1, /* bad descriptor, NULL required pointer, bad size */
-  FC_ERR_UNSUPPORTED = 2,      /* valid request this build does not implement    */
+  FC_ERR_UNSUPPORTED = 2,      /* valid request the library does not implement   */
   FC_ERR_WORKSPACE = 3,        /* workspace NULL or smaller than required        */
   FC_ERR_HIP = 4               /* a HIP runtime call or launch failed            */
 } fc_status;

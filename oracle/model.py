@@ -58,7 +58,7 @@ def energy(cspec, lspec, pos, rowptr, sender, shift, x, W, lws, n_bar: float):
 #
 # The block as the pages describe it, with random weights, for one final block
 # (scalar senders in, scalars out).  Readings where the pages leave a step
-# open (each listed in the design doc):
+# open:
 #   a   = N_bar^{-1/2} conv(h0) with the radial network's weights (Eq. E1);
 #   m_l = M_l a_l (rank-wise map of the paths -- one per rank with scalar
 #         senders -- and channels), m_0 += R0 h0 (residual: a learned linear

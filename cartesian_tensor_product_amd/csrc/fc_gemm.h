@@ -49,6 +49,11 @@ inline constexpr int kMaxGemmGroup = 10;
 
 struct GemmGroup {
   int count;
+  // optional scratch (floats): a group of fewer than 64 tiles splits its
+  // unsplit problems' K over up to four blocks with partials here (set by the
+  // caller; zero-initialised groups have none)
+  float* scratch;
+  size_t scratch_floats;
   int tiles_m[kMaxGemmGroup];
   int tiles_n[kMaxGemmGroup];
   int kchunk[kMaxGemmGroup];
@@ -63,6 +68,10 @@ void gemm_group(const GemmGroup& g, hipStream_t st);
 
 // Split count for a long reduction: about `target` blocks in total.
 int gemm_ksplit(int M, int N, int K, int target);
+
+// Scratch floats that lets a group of these problems (M, N per problem)
+// split when small: four partial tiles per problem.
+inline size_t gemm_small_split_floats(size_t sum_MN) { return 4 * sum_MN; }
 
 inline GView plain_view(const float* p, long long ld) { return GView{p, 1, ld, 0, 1, 1, 0, 0, 0}; }
 // element (r, k) = p[k * ld + r] (a transposed plain matrix)

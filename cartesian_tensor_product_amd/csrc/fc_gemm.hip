@@ -388,6 +388,34 @@ int gemm_ksplit(int M, int N, int K, int target) {
 
 void gemm_group(const GemmGroup& g0, hipStream_t st) {
   GemmGroup g = g0;
+  // A group too small to fill the chip (e.g. a 1000-row map: 8 tiles) splits
+  // K over up to four blocks when the caller lent scratch for the partials:
+  // four times the blocks, each a quarter of the products, summed in split
+  // order by split_reduce_kernel.
+  if (g.scratch && g.scratch_floats) {
+    long long tiles = 0;
+    for (int i = 0; i < g.count; ++i) {
+      const GemmProblem& P = g.prob[i];
+      tiles += (long long)((P.M + BM - 1) / BM) * ((P.N + BN - 1) / BN) * (P.ksplit > 1 ? P.ksplit : 1);
+    }
+    if (tiles > 0 && tiles < 64) {
+      size_t used = 0;
+      for (int i = 0; i < g.count; ++i) {
+        GemmProblem& P = g.prob[i];
+        if (P.ksplit > 1) continue;
+        const long long kt = (P.K + BK - 1) / BK;
+        long long sp = 128 / tiles;
+        if (sp > 4) sp = 4;
+        if (sp > kt) sp = kt;
+        const size_t need = (size_t)sp * P.M * P.N;
+        if (sp > 1 && used + need <= g.scratch_floats) {
+          P.ksplit = (int)sp;
+          P.part = g.scratch + used;
+          used += need;
+        }
+      }
+    }
+  }
   int total = 0;
   for (int i = 0; i < g.count; ++i) {
     GemmProblem& P = g.prob[i];

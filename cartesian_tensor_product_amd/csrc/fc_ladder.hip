@@ -564,12 +564,16 @@ size_t LadderPlan::weight_floats() const {
   return n;
 }
 
-size_t LadderPlan::saved_floats() const { return (size_t)(order - 1) * N * nr(lprod) * C; }
+// the states phi^1 .. phi^(order-1) and, path-reduced, the final state S
+// that the output maps read (kept so that the VJP need not recompute it)
+size_t LadderPlan::saved_floats() const {
+  return (size_t)(order - 1) * N * nr(lprod) * C + (variant == 1 ? (size_t)N * nr(lout) * C : 0);
+}
 
 size_t LadderPlan::state_floats() const { return (size_t)N * nr(lprod) * C; }
 
 size_t LadderPlan::fwd_ws_floats() const {
-  if (variant == 1) return (size_t)N * nr(lout) * C;
+  if (variant == 1) return (size_t)N * nr(lout) * C + gemm_small_split_floats((size_t)N * nr(lout) * C);
   size_t b = 0;
   for (int q = 2; q <= order; ++q) b = std::max(b, (size_t)N * prod_rows(q) * C);
   return b + 2 * state_floats();
@@ -616,7 +620,8 @@ size_t LadderPlan::vjp_ws_floats() const {
   int pmax = 0;
   for (int q = 2; q <= order; ++q) pmax = std::max(pmax, paths(q));
   for (int L = 0; L <= lout; ++L) part += (size_t)gemm_ksplit(C, C, N * (2 * L + 1), kSplitTarget) * C2;
-  return 2 * (size_t)N * nr(lout) * C + 2 * st + (size_t)nblk * (pmax + lprod + 1) * C + part;
+  return 2 * (size_t)N * nr(lout) * C + 2 * st + (size_t)nblk * (pmax + lprod + 1) * C + part +
+         gemm_small_split_floats((size_t)N * nr(lout) * C);
 }
 
 // B, B', B_bar, B_bar' (largest step), G and G' double buffers, phi'^q for
@@ -748,7 +753,7 @@ void ladder_forward(const LadderPlan& p, const float* A, const float* w, float* 
   const int C = p.C;
   const int ra = nr(p.la), rp = nr(p.lprod), ro = nr(p.lout);
   if (p.variant == 1) {
-    float* S = ws;
+    float* S = saved ? saved + (size_t)(p.order - 1) * p.state_floats() : ws;
     switch (p.lprod) {
       case 1: dispatch_reduced<1>(p, A, w, S, saved, st); break;
       case 2: dispatch_reduced<2>(p, A, w, S, saved, st); break;
@@ -756,6 +761,13 @@ void ladder_forward(const LadderPlan& p, const float* A, const float* w, float* 
       case 4: dispatch_reduced<4>(p, A, w, S, saved, st); break;
     }
     GemmGroup g{};
+    if (S != ws) {   // the final state went to the saved states: ws is free
+      g.scratch = ws;
+      g.scratch_floats = p.fwd_ws_floats();
+    } else {
+      g.scratch = ws + (size_t)p.N * ro * C;
+      g.scratch_floats = gemm_small_split_floats((size_t)p.N * ro * C);
+    }
     for (int L = 0; L <= p.lout; ++L) {
       GemmProblem& pr = g.prob[g.count++];
       pr.M = p.N * (2 * L + 1);
@@ -1012,15 +1024,25 @@ void ladder_vjp(const LadderPlan& p, const float* A, const float* w, const float
   float* apart = Gbuf[1] + stf;
   float* a1part = apart + (size_t)nblk * pmax * C;
   float* part = a1part + (size_t)nblk * (p.lprod + 1) * C;
-  switch (p.lprod) {
-    case 1: dispatch_reduced<1>(p, A, w, S, nullptr, st); break;
-    case 2: dispatch_reduced<2>(p, A, w, S, nullptr, st); break;
-    case 3: dispatch_reduced<3>(p, A, w, S, nullptr, st); break;
-    case 4: dispatch_reduced<4>(p, A, w, S, nullptr, st); break;
+  // the final state the output maps read: kept by the forward in the saved
+  // states, else (order 1 without them) recomputed
+  const float* Sf = S;
+  if (saved) {
+    Sf = saved + (size_t)(p.order - 1) * stf;
+  } else {
+    switch (p.lprod) {
+      case 1: dispatch_reduced<1>(p, A, w, S, nullptr, st); break;
+      case 2: dispatch_reduced<2>(p, A, w, S, nullptr, st); break;
+      case 3: dispatch_reduced<3>(p, A, w, S, nullptr, st); break;
+      case 4: dispatch_reduced<4>(p, A, w, S, nullptr, st); break;
+    }
   }
   {
     GemmGroup g{};
-    size_t poff = 0;
+    size_t poff = 0, pfl = 0;
+    for (int L = 0; L <= p.lout; ++L) pfl += (size_t)gemm_ksplit(C, C, p.N * (2 * L + 1), kSplitTarget) * C * C;
+    g.scratch = part + pfl;
+    g.scratch_floats = gemm_small_split_floats((size_t)p.N * ro * C);
     for (int L = 0; L <= p.lout; ++L) {
       const float* WL = w + p.w_final(L);
       GemmProblem& b = g.prob[g.count++];
@@ -1039,7 +1061,7 @@ void ladder_vjp(const LadderPlan& p, const float* A, const float* w, const float
         d.K = p.N * (2 * L + 1);
         d.alpha = 1.f;
         d.A = node_view_t(gz, ro, L, C);
-        d.Bt = node_view_t(S, ro, L, C);
+        d.Bt = node_view_t(Sf, ro, L, C);
         d.C = plain_out(w_grad + p.w_final(L), C, 0);
         d.C2 = no_out();
         d.ksplit = gemm_ksplit(d.M, d.N, d.K, kSplitTarget);

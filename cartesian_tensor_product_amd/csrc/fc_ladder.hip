@@ -200,7 +200,7 @@ __global__ __launch_bounds__(kRedWaves * kWave) void ladder_reduced_vjp_kernel(
     int N, int C, int ntile, const float* __restrict__ G, int g_rows, const float* __restrict__ phi,
     const float* __restrict__ A, const float* __restrict__ Sbar, int s_rows, const float* __restrict__ aw,
     const float* __restrict__ a1, float* __restrict__ Gprev, float* __restrict__ Abar,
-    float* __restrict__ apart, float* __restrict__ a1part) {
+    float* __restrict__ apart, float* __restrict__ a1part, int acc_abar) {
   using Cfg = ConvCfg<LP, LA, LQ>;
   constexpr int NP = nrank(LP), NA = nrank(LA), NQ = nrank(LQ);
   constexpr int NR = Cfg::P + (FIRST ? LP + 1 : 0);   // partial sums per lane
@@ -264,7 +264,10 @@ __global__ __launch_bounds__(kRedWaves * kWave) void ladder_reduced_vjp_kernel(
     } else {
       static_for<NP>([&](auto c) { Gprev[((size_t)u * NP + c) * C + k] = gp[c]; });
     }
-    static_for<NA>([&](auto c) { Abar[((size_t)u * NA + c) * C + k] += ab[c]; });
+    static_for<NA>([&](auto c) {
+      float* d = Abar + ((size_t)u * NA + c) * C + k;
+      *d = acc_abar ? *d + ab[c] : ab[c];
+    });
   }
   if (wave > 0) {
     static_for<Cfg::P>([&](auto i) { red[wave - 1][i][lane] = aacc[i]; });
@@ -844,15 +847,15 @@ void launch_prod_vjp(const LadderPlan& p, const float* Bbar, const float* phi, c
 template <int LP, int LQ>
 void launch_red_vjp(const LadderPlan& p, bool first, const float* G, int g_rows, const float* phi, const float* A,
                     const float* Sbar, const float* aw, const float* a1, float* Gprev, float* Abar, float* apart,
-                    float* a1part, hipStream_t st) {
+                    float* a1part, int acc_abar, hipStream_t st) {
   const int nt = red_ntile(p.N, p.C);
   dim3 grid((p.N + nt - 1) / nt, (p.C + kWave - 1) / kWave);
   if (first)
     hipLaunchKernelGGL((ladder_reduced_vjp_kernel<LP, LP, LQ, true>), grid, dim3(kRedWaves * kWave), 0, st, p.N, p.C, nt,
-                       G, g_rows, phi, A, Sbar, nr(p.lout), aw, a1, Gprev, Abar, apart, a1part);
+                       G, g_rows, phi, A, Sbar, nr(p.lout), aw, a1, Gprev, Abar, apart, a1part, acc_abar);
   else
     hipLaunchKernelGGL((ladder_reduced_vjp_kernel<LP, LP, LQ, false>), grid, dim3(kRedWaves * kWave), 0, st, p.N, p.C, nt,
-                       G, g_rows, phi, A, Sbar, nr(p.lout), aw, a1, Gprev, Abar, apart, a1part);
+                       G, g_rows, phi, A, Sbar, nr(p.lout), aw, a1, Gprev, Abar, apart, a1part, acc_abar);
 }
 
 // dispatch (lprod, LQ) -> F<LP, LQ>
@@ -931,7 +934,9 @@ void ladder_vjp(const LadderPlan& p, const float* A, const float* w, const float
   const int C = p.C;
   const int ra = nr(p.la), rp = nr(p.lprod), ro = nr(p.lout);
   const size_t stf = p.state_floats();
-  fill_zero(A_grad, (size_t)p.N * ra * C, st);
+  // the path-reduced steps store A_grad at the first reverse step (q = order)
+  // and add to it after; the other paths accumulate from zero
+  if (p.variant == 0 || p.order == 1) fill_zero(A_grad, (size_t)p.N * ra * C, st);
   if (p.variant == 0) {
     size_t bmax = 0;
     for (int q = 2; q <= p.order; ++q) bmax = std::max(bmax, (size_t)p.N * p.prod_rows(q) * C);
@@ -1085,7 +1090,7 @@ void ladder_vjp(const LadderPlan& p, const float* A, const float* w, const float
     const float* phi = saved + (size_t)(q - 2) * stf;
     float* Gprev = Gbuf[q % 2];
     by_ranks<RedVjp>(p.lprod, p.lq(q), p, q == 2, G, grows, phi, A, (const float*)Sbar,
-                     (const float*)(w + p.w_a(q)), a1, Gprev, A_grad, apart, a1part, st);
+                     (const float*)(w + p.w_a(q)), a1, Gprev, A_grad, apart, a1part, q != p.order, st);
     if (w_grad) {
       block_sum(nblk, p.paths(q) * C, apart, w_grad + p.w_a(q), st);
       if (q == 2) block_sum(nblk, (p.lprod + 1) * C, a1part, w_grad + p.w_a(1), st);

@@ -124,3 +124,22 @@ def test_ladder_channel_tiles(l, l_out, order, variant, C):
     assert_close("A_grad", Ab.cpu().numpy(), Ao)
     for i, (got, want) in enumerate(zip(g.split(Wb.cpu().numpy()), Wo)):
         assert_close(f"w_grad[{i}]", got, want)
+
+
+@pytest.mark.parametrize("l,l_out", [(2, 2), (3, 1)])
+def test_ladder_reduced_order1_without_saved_states(l, l_out):
+    """Order 1 needs no saved states: without them the path-reduced VJP forms
+    the final state again instead of reading the forward's copy."""
+    g = GpuLadder(l, l_out, 1, "reduced", C=64, N=37)
+    g.fc.fc_node_ladder_fwd(g.desc, g.dA, g.dW, g.z, None, g.wsf)
+    dg = torch.from_numpy(np.ascontiguousarray(g.gz)).to("cuda")
+    Ab, Wb = torch.empty_like(g.dA), torch.empty_like(g.dW)
+    g.fc.fc_node_ladder_vjp(g.desc, g.dA, g.dW, None, dg, Ab, Wb, g.wsb)
+    torch.cuda.synchronize()
+    f = lambda a: a.astype(np.float64)
+    zo = ladder.ladder_fwd(g.spec, f(g.A), [f(w) for w in g.ws])
+    Ao, Wo = ladder.ladder_vjp(g.spec, f(g.A), [f(w) for w in g.ws], f(g.gz))
+    assert_close("z", g.z.cpu().numpy(), zo)
+    assert_close("A_grad", Ab.cpu().numpy(), Ao)
+    for i, (got, want) in enumerate(zip(g.split(Wb.cpu().numpy()), Wo)):
+        assert_close(f"w_grad[{i}]", got, want)

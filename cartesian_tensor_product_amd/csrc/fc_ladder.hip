@@ -32,19 +32,26 @@ constexpr int kRedWaves = 4;   // waves per block of the path-reduced reverse ke
 // One step of the full ladder: B rows for all paths of ConvCfg<LP, LA, LQ>.
 // phi [N][phi_rows][C], A [N][a_rows][C]; B block of rank L starts at
 // N * off(L) * C floats, row (u (2L+1) + a), column (eta_L C + k).  With
-// acc the products are added to B (a tangent B' = prod(phi', A) +
-// prod(phi, A') takes two launches).
-template <int LP, int LA, int LQ>
+// acc the products are added to B.  TWO: B gets prod(phi, A) +
+// prod(phi2, A2) in one pass (a tangent B' = prod(phi', A) + prod(phi, A')
+// without writing and re-reading B' in between).
+template <int LP, int LA, int LQ, bool TWO>
 __global__ __launch_bounds__(kWave) void ladder_prod_kernel(int N, int C, const float* __restrict__ phi,
                                                             int phi_rows, const float* __restrict__ A,
-                                                            int a_rows, float* __restrict__ B, int acc) {
+                                                            int a_rows, float* __restrict__ B, int acc,
+                                                            const float* __restrict__ phi2,
+                                                            const float* __restrict__ A2) {
   using Cfg = ConvCfg<LP, LA, LQ>;
   const int u = blockIdx.x;
   const int k = blockIdx.y * kWave + threadIdx.x;
   if (k >= C) return;
-  float x[nrank(LP)], y[nrank(LA)];
+  float x[nrank(LP)], y[nrank(LA)], x2[TWO ? nrank(LP) : 1], y2[TWO ? nrank(LA) : 1];
   static_for<nrank(LP)>([&](auto c) { x[c] = phi[((size_t)u * phi_rows + c) * C + k]; });
   static_for<nrank(LA)>([&](auto c) { y[c] = A[((size_t)u * a_rows + c) * C + k]; });
+  if constexpr (TWO) {
+    static_for<nrank(LP)>([&](auto c) { x2[c] = phi2[((size_t)u * phi_rows + c) * C + k]; });
+    static_for<nrank(LA)>([&](auto c) { y2[c] = A2[((size_t)u * a_rows + c) * C + k]; });
+  }
   static_for<Cfg::P>([&](auto pc) {
     constexpr int p = pc;
     constexpr PathInfo PI = Cfg::paths[p];
@@ -54,6 +61,7 @@ __global__ __launch_bounds__(kWave) void ladder_prod_kernel(int N, int C, const 
     static_for<te - tb>([&](auto ti) {
       constexpr tab::Term T = tab::kTerms[tb + ti];
       float xy = x[o1 + T.b1] * y[o2 + T.b2];
+      if constexpr (TWO) xy = fmaf(x2[o1 + T.b1], y2[o2 + T.b2], xy);
       if constexpr (T.fa) t[T.a] = T.c * xy;
       else t[T.a] = fmaf(T.c, xy, t[T.a]);
     });
@@ -688,30 +696,37 @@ size_t LadderPlan::w_final(int L) const {
 namespace {
 
 template <int LP, int LQ>
-void launch_prod(const LadderPlan& p, const float* phi, const float* A, float* B, int acc, hipStream_t st) {
+void launch_prod(const LadderPlan& p, const float* phi, const float* A, float* B, int acc, const float* phi2,
+                 const float* A2, hipStream_t st) {
   dim3 grid(p.N, (p.C + kWave - 1) / kWave);
-  hipLaunchKernelGGL((ladder_prod_kernel<LP, LP, LQ>), grid, dim3(kWave), 0, st, p.N, p.C, phi, nr(p.lprod), A,
-                     nr(p.la), B, acc);
+  if (phi2)
+    hipLaunchKernelGGL((ladder_prod_kernel<LP, LP, LQ, true>), grid, dim3(kWave), 0, st, p.N, p.C, phi,
+                       nr(p.lprod), A, nr(p.la), B, acc, phi2, A2);
+  else
+    hipLaunchKernelGGL((ladder_prod_kernel<LP, LP, LQ, false>), grid, dim3(kWave), 0, st, p.N, p.C, phi,
+                       nr(p.lprod), A, nr(p.la), B, acc, (const float*)nullptr, (const float*)nullptr);
 }
 
 template <int LP>
 void dispatch_prod(const LadderPlan& p, int LQ, const float* phi, const float* A, float* B, int acc,
-                   hipStream_t st) {
+                   const float* phi2, const float* A2, hipStream_t st) {
   switch (LQ) {
-    case 0: launch_prod<LP, 0>(p, phi, A, B, acc, st); break;
-    case 1: if constexpr (LP >= 1) launch_prod<LP, 1>(p, phi, A, B, acc, st); break;
-    case 2: if constexpr (LP >= 2) launch_prod<LP, 2>(p, phi, A, B, acc, st); break;
-    case 3: if constexpr (LP >= 3) launch_prod<LP, 3>(p, phi, A, B, acc, st); break;
-    case 4: if constexpr (LP >= 4) launch_prod<LP, 4>(p, phi, A, B, acc, st); break;
+    case 0: launch_prod<LP, 0>(p, phi, A, B, acc, phi2, A2, st); break;
+    case 1: if constexpr (LP >= 1) launch_prod<LP, 1>(p, phi, A, B, acc, phi2, A2, st); break;
+    case 2: if constexpr (LP >= 2) launch_prod<LP, 2>(p, phi, A, B, acc, phi2, A2, st); break;
+    case 3: if constexpr (LP >= 3) launch_prod<LP, 3>(p, phi, A, B, acc, phi2, A2, st); break;
+    case 4: if constexpr (LP >= 4) launch_prod<LP, 4>(p, phi, A, B, acc, phi2, A2, st); break;
   }
 }
 
-void prod(const LadderPlan& p, int LQ, const float* phi, const float* A, float* B, hipStream_t st, int acc = 0) {
+// B (=, or += with acc) prod(phi, A) [+ prod(phi2, A2) when phi2 is given]
+void prod(const LadderPlan& p, int LQ, const float* phi, const float* A, float* B, hipStream_t st, int acc = 0,
+          const float* phi2 = nullptr, const float* A2 = nullptr) {
   switch (p.lprod) {
-    case 1: dispatch_prod<1>(p, LQ, phi, A, B, acc, st); break;
-    case 2: dispatch_prod<2>(p, LQ, phi, A, B, acc, st); break;
-    case 3: dispatch_prod<3>(p, LQ, phi, A, B, acc, st); break;
-    case 4: dispatch_prod<4>(p, LQ, phi, A, B, acc, st); break;
+    case 1: dispatch_prod<1>(p, LQ, phi, A, B, acc, phi2, A2, st); break;
+    case 2: dispatch_prod<2>(p, LQ, phi, A, B, acc, phi2, A2, st); break;
+    case 3: dispatch_prod<3>(p, LQ, phi, A, B, acc, phi2, A2, st); break;
+    case 4: dispatch_prod<4>(p, LQ, phi, A, B, acc, phi2, A2, st); break;
   }
 }
 
@@ -1144,8 +1159,7 @@ void ladder_vjp_vjp_reduced(const LadderPlan& p, const float* A, const float* w,
                      vA, aw(w, 1), A, aw(vw, 1), dphi_of(1), dS);
   for (int q = 2; q <= p.order; ++q) {
     const float* phi = phi_of(q - 1);
-    prod(p, p.lq(q), dphi_of(q - 1), A, dB, st, 0);
-    if (vA) prod(p, p.lq(q), phi, vA, dB, st, 1);
+    prod(p, p.lq(q), dphi_of(q - 1), A, dB, st, 0, vA ? phi : nullptr, vA);
     if (vw) prod(p, p.lq(q), phi, A, B, st, 0);
     by_ranks<Mix>(p.lprod, p.lq(q), p, (const float*)dB, aw(w, q), vw ? (const float*)B : nullptr, aw(vw, q),
                   dphi_of(q), dS, 1, st);
@@ -1223,8 +1237,7 @@ void ladder_vjp_vjp_reduced(const LadderPlan& p, const float* A, const float* w,
     const float* aq = aw(w, q);
     const float* vaq = aw(vw, q);
     prod(p, p.lq(q), phi, A, B, st, 0);
-    prod(p, p.lq(q), dph, A, dB, st, 0);
-    if (vA) prod(p, p.lq(q), phi, vA, dB, st, 1);
+    prod(p, p.lq(q), dph, A, dB, st, 0, vA ? phi : nullptr, vA);
     by_ranks<MixVjp>(p.lprod, p.lq(q), p, G, grows, aq, (const float*)nullptr, 0, (const float*)nullptr, Bb, st);
     const bool have_dBb = dG || vaq;
     if (have_dBb)
@@ -1317,8 +1330,7 @@ void ladder_vjp_vjp(const LadderPlan& p, const float* A, const float* w, const f
     float* out = dphi_of(q);
     if (!out && !g_hat) break;
     const float* phi = phi_of(q - 1);
-    prod(p, p.lq(q), dphi_of(q - 1), A, dB, st, 0);
-    if (vA) prod(p, p.lq(q), phi, vA, dB, st, 1);
+    prod(p, p.lq(q), dphi_of(q - 1), A, dB, st, 0, vA ? phi : nullptr, vA);
     if (vw) prod(p, p.lq(q), phi, A, B, st, 0);
     for (int pass = 0; pass < 2; ++pass) {
       if (pass == 1 && !vw) continue;
@@ -1353,8 +1365,7 @@ void ladder_vjp_vjp(const LadderPlan& p, const float* A, const float* w, const f
     const float* phi = phi_of(q - 1);
     const float* dph = dphi_of(q - 1);
     prod(p, p.lq(q), phi, A, B, st, 0);
-    prod(p, p.lq(q), dph, A, dB, st, 0);
-    if (vA) prod(p, p.lq(q), phi, vA, dB, st, 1);
+    prod(p, p.lq(q), dph, A, dB, st, 0, vA ? phi : nullptr, vA);
     const bool have_dBb = dG || vw;
     // B_bar = G W, B_bar' = G' W (+ G V below)
     {

@@ -938,10 +938,12 @@ fc_status fc_message_block_energy_forces(const fc_conv_desc* cd, const fc_graph*
 
   // ---- forward
   mlp_conv_forward(cd, g, pos, shift, h0, W + L.w_mlp, a, mws, stream);
-  fc::block_scale(a, (size_t)N * R * C, conv_scale, stream);
-  {
+  {  // m_l = conv_scale M_l a_l (the scale rides on the GEMM) + R0 h0 for l = 0
     fc::GemmGroup gg{};
-    for (int l = 0; l <= le; ++l) gg.prob[gg.count++] = channel_map(N, C, a, R, l, chan(W + L.w_M, l), false, m, R, l, 0);
+    for (int l = 0; l <= le; ++l) {
+      gg.prob[gg.count] = channel_map(N, C, a, R, l, chan(W + L.w_M, l), false, m, R, l, 0);
+      gg.prob[gg.count++].alpha = conv_scale;
+    }
     fc::gemm_group(gg, stream);
     fc::GemmGroup gr{};
     gr.prob[gr.count++] = channel_map(N, C, h0, 1, 0, W + L.w_R0, false, m, R, 0, 1);
@@ -979,14 +981,16 @@ fc_status fc_message_block_energy_forces(const fc_conv_desc* cd, const fc_graph*
   }
   fc::launch_gate_vjp(N, C, le, n, Ab, y, nb, stream);
   fc::launch_rms_norm_vjp(le, N, C, m, W + L.w_g1, inv1, nb, mb, nullptr, nullptr, stream);
-  {  // a_bar_l = M_l^T m_bar_l (into a), times the convolution scale
+  {  // a_bar_l = conv_scale M_l^T m_bar_l (into a), negated: the convolution's
+     // VJP is linear in its cotangent, so its position gradient is then the force
     fc::GemmGroup gg{};
-    for (int l = 0; l <= le; ++l) gg.prob[gg.count++] = channel_map(N, C, mb, R, l, chan(W + L.w_M, l), true, a, R, l, 0);
+    for (int l = 0; l <= le; ++l) {
+      gg.prob[gg.count] = channel_map(N, C, mb, R, l, chan(W + L.w_M, l), true, a, R, l, 0);
+      gg.prob[gg.count++].alpha = -conv_scale;
+    }
     fc::gemm_group(gg, stream);
   }
-  fc::block_scale(a, (size_t)N * R * C, conv_scale, stream);
   mlp_conv_vjp(cd, g, pos, shift, h0, W + L.w_mlp, a, nullptr, forces, nullptr, mws, wb + L.cws, true, stream);
-  fc::block_scale(forces, (size_t)N * 3, -1.f, stream);
   return check_launch("message block energy/forces");
 }
 

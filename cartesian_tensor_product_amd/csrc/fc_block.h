@@ -8,7 +8,6 @@
 
 namespace fc {
 
-void block_scale(float* p, size_t n, float a, hipStream_t st);
 // pos_w = a W, neg_w = -a W (neg_w nullable), n floats each
 void block_scaled_weights(const float* W, size_t n, float a, float* pos_w, float* neg_w, hipStream_t st);
 void block_unit_cotangent(float* g, int N, int rows, int C, hipStream_t st);

@@ -16,11 +16,6 @@ namespace fc {
 
 namespace {
 
-__global__ __launch_bounds__(256) void scale_kernel(size_t n, float a, float* __restrict__ p) {
-  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] *= a;
-}
-
 // pos_w = a W and neg_w = -a W (nullable): the radial weights with the
 // convolution scale folded in, for the forward and (negated, so that the
 // VJP to the positions is the force) for the backward pass.
@@ -72,10 +67,6 @@ __global__ __launch_bounds__(64) void energy_sum_kernel(int n, const double* __r
 }
 
 }  // namespace
-
-void block_scale(float* p, size_t n, float a, hipStream_t st) {
-  if (n) hipLaunchKernelGGL(scale_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, n, a, p);
-}
 
 void block_scaled_weights(const float* W, size_t n, float a, float* pos_w, float* neg_w, hipStream_t st) {
   if (n)

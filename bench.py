@@ -62,6 +62,47 @@ def timed(fn, iters=10, warmup=2):
     return a.elapsed_time(b) / iters
 
 
+def message_blocks(dev, cases=((8, "path_reduced"), (8, "full"), (5, "path_reduced"))):
+    """One full message-passing block (radial network, rank-wise map,
+    residuals, RMS norms, SiLU gates, ladder of order 5, readout) for energy
+    and forces on diamond cells of ncell^3 conventional cells, random weights."""
+    import torch
+
+    from cartesian_tensor_product_amd import flashcart as fc
+    from cartesian_tensor_product_amd import inputs as inp
+    out = {}
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    en = torch.zeros(1, dtype=torch.float64, device=dev)
+    variants = {"path_reduced": fc.FC_LADDER_PATH_REDUCED, "full": fc.FC_LADDER_FULL}
+    for ncell, vname in cases:
+        var = variants[vname]
+        dm = inp.diamond_inputs(channels=CHANNELS, r_cut=5.0, rattle=0.05, ncell=ncell, n_paths=4)
+        Nm, Em = dm["pos"].shape[0], len(dm["sender"])
+        cdm = fc.conv_desc(Nm, Em, CHANNELS, 0, 3, 3, 5.0)
+        ldm = fc.ladder_desc(Nm, CHANNELS, 3, 3, 0, 5, var)
+        C2 = CHANNELS
+        entries = [("mlp", (4, C2), "mlp", 1), ("M", (4, C2, C2), "normal", C2), ("R0", (C2, C2), "normal", C2),
+                   ("gamma1", (4, C2), "one_plus", 1), ("O", (4, C2, C2), "normal", C2)]
+        entries += [(f"ladder{i}", (r_, c_), "normal" if k_ == 0 else "one_plus", c_)
+                    for i, (_, r_, c_, k_) in enumerate(fc.ladder_weight_blocks(ldm))]
+        entries += [("R2", (C2, C2), "normal", C2), ("gamma2", (1, C2), "one_plus", 1),
+                    ("Wr1", (C2, 64), "normal", C2), ("Wr2", (64, 64), "normal", 64), ("wr3", (64,), "normal", 64)]
+        wdict = inp.block_weights(8, entries)
+        flat = t(np.concatenate([wdict[e[0]].ravel() for e in entries]))
+        assert flat.numel() == fc.fc_message_block_weight_floats(cdm, ldm)
+        gm = fc.DeviceGraph(dm["rowptr"], dm["sender"], Nm, device=dev)
+        wsm = fc.workspace(fc.fc_message_block_workspace_bytes(cdm, ldm), dev)
+        Fm = torch.empty((Nm, 3), device=dev)
+        am = (cdm, gm, t(dm["pos"]), t(dm["shift"]), t(dm["x"]), ldm, flat, 1.0 / np.sqrt(Em / Nm), 1e-5)
+        msm = timed(lambda: fc.fc_message_block_energy_forces(*am, en, None, Fm, wsm), iters=5)
+        mse = timed(lambda: fc.fc_message_block_energy_forces(*am, en, None, None, wsm), iters=5)
+        out[f"message_block_diamond_{Nm}_atoms_{vname}_order5"] = {
+            "energy_forces_ms": msm, "us_per_atom": msm * 1e3 / Nm, "energy_only_ms": mse, "edges": Em,
+            "workspace_bytes": fc.fc_message_block_workspace_bytes(cdm, ldm)}
+        del wsm, gm, flat
+    return out
+
+
 def extras(dev, only_ladder=False, conv_ranks=(3, 4), only_conv=False):
     """Secondary workloads (reported beside the headline, not part of it)."""
     import torch
@@ -238,35 +279,7 @@ def extras(dev, only_ladder=False, conv_ranks=(3, 4), only_conv=False):
     ms = timed(lambda: fc.fc_block_energy_forces(*args, en, None, F, wsd))
     out["diamond_1000_atoms_energy_forces"] = {"ms": ms, "us_per_atom": ms * 1e3 / Nd, "edges": Ed}
     del wsd
-    # one full message-passing block (radial network, rank-wise map,
-    # residuals, RMS norms, SiLU gates, ladder of order 5, readout) for energy
-    # and forces on diamond cells, random weights
-    for ncell, var, vname in ((8, fc.FC_LADDER_PATH_REDUCED, "path_reduced"), (8, fc.FC_LADDER_FULL, "full"),
-                              (5, fc.FC_LADDER_PATH_REDUCED, "path_reduced")):
-        dm = inp.diamond_inputs(channels=CHANNELS, r_cut=5.0, rattle=0.05, ncell=ncell, n_paths=4)
-        Nm, Em = dm["pos"].shape[0], len(dm["sender"])
-        cdm = fc.conv_desc(Nm, Em, CHANNELS, 0, 3, 3, 5.0)
-        ldm = fc.ladder_desc(Nm, CHANNELS, 3, 3, 0, 5, var)
-        C2 = CHANNELS
-        entries = [("mlp", (4, C2), "mlp", 1), ("M", (4, C2, C2), "normal", C2), ("R0", (C2, C2), "normal", C2),
-                   ("gamma1", (4, C2), "one_plus", 1), ("O", (4, C2, C2), "normal", C2)]
-        entries += [(f"ladder{i}", (r_, c_), "normal" if k_ == 0 else "one_plus", c_)
-                    for i, (_, r_, c_, k_) in enumerate(fc.ladder_weight_blocks(ldm))]
-        entries += [("R2", (C2, C2), "normal", C2), ("gamma2", (1, C2), "one_plus", 1),
-                    ("Wr1", (C2, 64), "normal", C2), ("Wr2", (64, 64), "normal", 64), ("wr3", (64,), "normal", 64)]
-        wdict = inp.block_weights(8, entries)
-        flat = t(np.concatenate([wdict[e[0]].ravel() for e in entries]))
-        assert flat.numel() == fc.fc_message_block_weight_floats(cdm, ldm)
-        gm = fc.DeviceGraph(dm["rowptr"], dm["sender"], Nm, device=dev)
-        wsm = fc.workspace(fc.fc_message_block_workspace_bytes(cdm, ldm), dev)
-        Fm = torch.empty((Nm, 3), device=dev)
-        am = (cdm, gm, t(dm["pos"]), t(dm["shift"]), t(dm["x"]), ldm, flat, 1.0 / np.sqrt(Em / Nm), 1e-5)
-        msm = timed(lambda: fc.fc_message_block_energy_forces(*am, en, None, Fm, wsm), iters=5)
-        mse = timed(lambda: fc.fc_message_block_energy_forces(*am, en, None, None, wsm), iters=5)
-        out[f"message_block_diamond_{Nm}_atoms_{vname}_order5"] = {
-            "energy_forces_ms": msm, "us_per_atom": msm * 1e3 / Nm, "energy_only_ms": mse, "edges": Em,
-            "workspace_bytes": fc.fc_message_block_workspace_bytes(cdm, ldm)}
-        del wsm, gm, flat
+    out.update(message_blocks(dev))
     return out
 
 
@@ -399,6 +412,8 @@ def main():
                     help="only run the 4096-node ladder workloads (for counter runs) and print their timings")
     ap.add_argument("--conv-rank", type=int, default=0, metavar="L",
                     help="only run the 1024-node edge-conv workload at ranks <= L (3 or 4; for counter runs)")
+    ap.add_argument("--message-block-only", action="store_true",
+                    help="only time the path-reduced message block on the 4096-atom diamond cell")
     ap.add_argument("--grid", action="store_true",
                     help="only run the pages' microbenchmark grid (ranks 1-5) and print it as one JSON line")
     ap.add_argument("--copy-only", type=int, default=0, metavar="MB",
@@ -429,6 +444,9 @@ def main():
         return
     if args.grid:
         print(json.dumps({"grid": grid(dev, 10)}), flush=True)
+        return
+    if args.message_block_only:
+        print(json.dumps(message_blocks(dev, ((8, "path_reduced"),))), flush=True)
         return
     if args.conv_rank:
         print(json.dumps(extras(dev, conv_ranks=(args.conv_rank,), only_conv=True)), flush=True)

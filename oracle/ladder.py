@@ -29,7 +29,10 @@ Parity pins (tests/test_oracle_ladder.py): with nu = 1 the ladder is W1 A;
 the recurrence equals the explicit tensor-train contraction of App. E
 Eqs. E2-E4 on a tiny width; path-reduced with a = 1, nu = 2 is a sum of
 couplings over sqrt(P); O(3) equivariance; finite differences of the VJP;
-the product count "99 d components mixed down to 16 d" of App. E.
+the product count "99 d components mixed down to 16 d" of App. E; order 3
+at ranks <= 2 with path weights a != 1 (and the full variant's W^q column
+order) against a hand expansion in explicit 3 x 3 tensor algebra
+(tests/test_oracle_hand.py).
 """
 
 from __future__ import annotations

@@ -16,7 +16,10 @@ rattled cell.
 The full message-passing block at the end of this file adds the pages'
 radial network, the rank-wise path/channel map, residual updates, the
 equivariant RMS normalisation, scalar SiLU gates with their output map and
-a readout MLP (random weights); its pins are the same three properties.
+a readout MLP (random weights); its pins are the same three properties,
+plus a two-atom walkthrough (one channel, ranks <= 3, ladder of order 2)
+whose energy is evaluated step by step in scalar code and whose forces are
+central differences of that energy (tests/test_oracle_hand.py).
 """
 
 from __future__ import annotations

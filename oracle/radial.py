@@ -23,7 +23,9 @@ Parity pins (tests/test_oracle_radial.py): the Chebyshev features against
 cos(n theta); the envelope's value and derivatives at 0 and r_max; the
 pages' statement that w and its first two r-derivatives vanish at r_max;
 the hand-written MLP VJP and the convolution VJP against complex-step
-derivatives.
+derivatives; the network on one edge with sparse weights against a closed
+form in scalar code (layer order, both SiLUs, the path-major output column
+order; tests/test_oracle_hand.py).
 """
 
 from __future__ import annotations

@@ -220,6 +220,11 @@ fc_status ladder_plan(const fc_ladder_desc* d, fc::LadderPlan* p) {
   if (d->l_a < 0 || d->l_prod < 0 || d->l_out < 0) return fail(FC_ERR_INVALID_ARGUMENT, "ladder: negative rank");
   if (d->l_a != d->l_prod || d->l_prod < 1 || d->l_prod > 4 || d->l_out > d->l_prod)
     return fail(FC_ERR_UNSUPPORTED, "ladder: the library needs l_a == l_prod in 1..4 and l_out <= l_prod");
+  // the mixing GEMMs index node rows n (2l + 1) + c, divided exactly by
+  // 2l + 1 with a multiply-high reciprocal, which holds below 2^26
+  if ((int64_t)d->n_nodes * (2 * d->l_prod + 1) >= (int64_t(1) << 26))
+    return fail(FC_ERR_UNSUPPORTED, "ladder: n_nodes * (2 l_prod + 1) = %lld reaches 2^26, the GEMM row index range",
+                (long long)d->n_nodes * (2 * d->l_prod + 1));
   *p = fc::LadderPlan{d->n_nodes, d->channels, d->l_a, d->l_prod, d->l_out, d->order, d->variant};
   return FC_OK;
 }

@@ -380,6 +380,14 @@ __device__ __forceinline__ int uniform_int(int v) { return __builtin_amdgcn_read
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
+// Descriptor of one node's rows ([row_floats] floats) of a node array.  The
+// base is formed in 64 bits from a wave-uniform node index, so node arrays
+// may exceed the 2 GiB reach of a 32-bit buffer offset; row offsets inside
+// the node (at most n_rows * C * 4 bytes) stay small.  Loads past the node's
+// rows (lanes beyond the last channel of the last row) return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t node_rsrc(const float* base, int u, int row_floats) {
+  return make_rsrc(base + (size_t)u * (size_t)row_floats, (uint32_t)row_floats * 4u);
+}
 __device__ __forceinline__ float buf_load(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }

@@ -147,7 +147,6 @@ __global__ __launch_bounds__(kWave) void conv_fwd_kernel(
   const bool act = k < C;
   const int kk = act ? k : 0;
   const int voff = kk * 4;
-  const auto xr = make_rsrc(x, (uint32_t)((size_t)N * NIN * C * 4));
 
   float Wr[XW ? 1 : kNB * G::NP];
   if constexpr (!XW) {
@@ -178,9 +177,9 @@ __global__ __launch_bounds__(kWave) void conv_fwd_kernel(
     for (int j = 0; j < cnt; ++j) {
       const float* rec = geo + j * REC;
       const int s = uniform_int(__float_as_int(rec[EP::NY + kNB]));
-      const int sbase = s * NIN * C * 4;
+      const auto xs = node_rsrc(x, s, NIN * C);
       float xv[NIN];
-      static_for<NIN>([&](auto c) { xv[c] = buf_load(xr, voff, sbase + c * C * 4); });
+      static_for<NIN>([&](auto c) { xv[c] = buf_load(xs, voff, c * C * 4); });
       float we[XW ? G::NP : 1];
       if constexpr (XW) {
         static_for<G::NP>([&](auto pi) { we[pi] = rec[EP::NY] * wn[pi]; });
@@ -315,7 +314,6 @@ __global__ __launch_bounds__(kWgWaves * kWave) void conv_wgrad_kernel(
   const bool act = k < C;
   const int kk = act ? k : 0;
   const int voff = kk * 4;
-  const auto xr = make_rsrc(x, (uint32_t)((size_t)N * NIN * C * 4));
   float* geo = lds + wv * kWave * REC;
 
   float gv[G::NR];
@@ -345,9 +343,9 @@ __global__ __launch_bounds__(kWgWaves * kWave) void conv_wgrad_kernel(
     for (int j = 0; j < cnt; ++j) {
       const float* rec = geo + j * REC;
       const int s = uniform_int(__float_as_int(rec[EP::NY + kNB]));
-      const int sbase = s * NIN * C * 4;
+      const auto xs = node_rsrc(x, s, NIN * C);
       float xv[NIN];
-      static_for<NIN>([&](auto c) { xv[c] = buf_load(xr, voff, sbase + c * C * 4); });
+      static_for<NIN>([&](auto c) { xv[c] = buf_load(xs, voff, c * C * 4); });
       static_for<G::NP>([&](auto pi) {
         constexpr int p = P0 + pi;
         constexpr PathInfo PI = Cfg::paths[p];
@@ -468,7 +466,6 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
   const bool act = k < C;
   const int kk = act ? k : 0;
   const int voff = kk * 4;
-  const auto gr = make_rsrc(g, (uint32_t)((size_t)N * NOUT * C * 4));
 
   float xv[NIN];
   {
@@ -551,14 +548,14 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
       for (int j = 0; j < cnt; ++j) {
         const float* rec = geo + j * REC;
         const int u = uniform_int(__float_as_int(rec[NY + 2 * kNB]));
-        const int ubase = u * NOUT * C * 4;
+        const auto gu = node_rsrc(g, u, NOUT * C);
         float gv[G::NR];
         static_for<G::NP>([&](auto pi) {
           constexpr int p = G::p0 + pi;
           if constexpr (!G::owner(p)) return;
           static_for<ncomp(Cfg::paths[p].L)>([&](auto c) {
             constexpr int row = Cfg::row(p, c), li = G::loff(p) + c;
-            gv[li] = buf_load(gr, voff, ubase + row * C * 4);
+            gv[li] = buf_load(gu, voff, row * C * 4);
           });
         });
         float we[XW ? G::NP : 1];

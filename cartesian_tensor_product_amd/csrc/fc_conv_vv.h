@@ -77,8 +77,6 @@ __global__ __launch_bounds__(kWave) void conv_vv_recv_kernel(
   const bool act = k < C;
   const int kk = act ? k : 0;
   const int voff = kk * 4;
-  const auto xr = make_rsrc(x, (uint32_t)((size_t)N * NIN * C * 4));
-  const auto vr = make_rsrc(HAS_VX ? v_x : x, (uint32_t)((size_t)N * NIN * C * 4));
 
   float Wr[XW ? 1 : kNB * G::NP];
   if constexpr (!XW) {
@@ -137,10 +135,11 @@ __global__ __launch_bounds__(kWave) void conv_vv_recv_kernel(
       const float* rec = geo + j * REC;
       const int s = uniform_int(__float_as_int(rec[2 * NE + 2 * kNB + 1]));
       const float nd = rec[2 * NE + 2 * kNB];
-      const int sbase = s * NIN * C * 4;
+      const auto xs = node_rsrc(x, s, NIN * C);
+      const auto vs = node_rsrc(HAS_VX ? v_x : x, s, NIN * C);
       float xv[NIN], vx[HAS_VX ? NIN : 1];
-      static_for<NIN>([&](auto c) { xv[c] = buf_load(xr, voff, sbase + c * C * 4); });
-      if constexpr (HAS_VX) static_for<NIN>([&](auto c) { vx[c] = buf_load(vr, voff, sbase + c * C * 4); });
+      static_for<NIN>([&](auto c) { xv[c] = buf_load(xs, voff, c * C * 4); });
+      if constexpr (HAS_VX) static_for<NIN>([&](auto c) { vx[c] = buf_load(vs, voff, c * C * 4); });
       float we[XW ? G::NP : 1], wve[XW ? G::NP : 1];
       if constexpr (XW) {
         const float valid = rec[2 * NE];
@@ -251,8 +250,6 @@ __global__ __launch_bounds__(kWgWaves * kWave) void conv_wgrad_vv_kernel(
   const bool act = k < C;
   const int kk = act ? k : 0;
   const int voff = kk * 4;
-  const auto xr = make_rsrc(x, (uint32_t)((size_t)N * NIN * C * 4));
-  const auto vr = make_rsrc(HAS_VX ? v_x : x, (uint32_t)((size_t)N * NIN * C * 4));
   float* geo = lds + wv * kWhChunk * REC;
 
   float gv[G::NR];
@@ -311,10 +308,11 @@ __global__ __launch_bounds__(kWgWaves * kWave) void conv_wgrad_vv_kernel(
     for (int j = 0; j < cnt; ++j) {
       const float* rec = geo + j * REC;
       const int s = uniform_int(__float_as_int(rec[2 * NE + 2 * kNB]));
-      const int sbase = s * NIN * C * 4;
+      const auto xs = node_rsrc(x, s, NIN * C);
+      const auto vs = node_rsrc(HAS_VX ? v_x : x, s, NIN * C);
       float xv[NIN], vx[HAS_VX ? NIN : 1];
-      static_for<NIN>([&](auto c) { xv[c] = buf_load(xr, voff, sbase + c * C * 4); });
-      if constexpr (HAS_VX) static_for<NIN>([&](auto c) { vx[c] = buf_load(vr, voff, sbase + c * C * 4); });
+      static_for<NIN>([&](auto c) { xv[c] = buf_load(xs, voff, c * C * 4); });
+      if constexpr (HAS_VX) static_for<NIN>([&](auto c) { vx[c] = buf_load(vs, voff, c * C * 4); });
       static_for<G::NP>([&](auto pi) {
         constexpr int p = P0 + pi;
         constexpr PathInfo PI = Cfg::paths[p];
@@ -427,7 +425,6 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vv_sender_kernel(
   const bool act = k < C;
   const int kk = act ? k : 0;
   const int voff = kk * 4;
-  const auto gr = make_rsrc(g, (uint32_t)((size_t)N * NOUT * C * 4));
 
   float xv[NIN], vx[HAS_VX ? NIN : 1];
   {
@@ -508,14 +505,14 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vv_sender_kernel(
         const float* rec = geo + j * REC;
         const int u = uniform_int(__float_as_int(rec[2 * NE + 3 * kNB + 1]));
         const float nd = rec[2 * NE + 3 * kNB];
-        const int ubase = u * NOUT * C * 4;
+        const auto gu = node_rsrc(g, u, NOUT * C);
         float gv[G::NR];
         static_for<G::NP>([&](auto pi) {
           constexpr int p = G::p0 + pi;
           if constexpr (!G::owner(p)) return;
           static_for<ncomp(Cfg::paths[p].L)>([&](auto c) {
             constexpr int row = Cfg::row(p, c), li = G::loff(p) + c;
-            gv[li] = buf_load(gr, voff, ubase + row * C * 4);
+            gv[li] = buf_load(gu, voff, row * C * 4);
           });
         });
         float red[NRED];

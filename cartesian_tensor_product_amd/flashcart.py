@@ -244,7 +244,17 @@ class DeviceGraph:
     """
 
     def __init__(self, rowptr, sender, n_nodes: int, device="cuda", stream=None):
+        import numpy as np
         import torch
+        # the device calls do not check graph contents: validate the host
+        # copy (an out-of-range sender would make the transpose write out of
+        # bounds)
+        h_rowptr = np.ascontiguousarray(torch.as_tensor(rowptr).cpu().numpy(), dtype=np.int32)
+        h_sender = np.ascontiguousarray(torch.as_tensor(sender).cpu().numpy(), dtype=np.int32)
+        if h_rowptr.shape != (n_nodes + 1,):
+            raise FlashCartError(FC_ERR_INVALID_ARGUMENT,
+                                 f"rowptr has {h_rowptr.size} entries, expected n_nodes + 1 = {n_nodes + 1}")
+        fc_graph_validate(n_nodes, int(h_sender.size), h_rowptr, h_sender)
         self.n_nodes = n_nodes
         self.rowptr = torch.as_tensor(rowptr, dtype=torch.int32, device=device).contiguous()
         self.sender = torch.as_tensor(sender, dtype=torch.int32, device=device).contiguous()

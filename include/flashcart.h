@@ -27,6 +27,14 @@
  *   reproducible for fixed inputs and launch configuration.
  * Errors: every call returns an fc_status; fc_last_error_message() gives a
  *   thread-local detail string for the last failing call on this thread.
+ * Sizes: node and edge counts are int32.  Every kernel forms node and edge
+ *   offsets in 64 bits, so arrays may exceed 2 GiB (e.g. [N][230][128] at
+ *   rank 4 beyond 18 k nodes).  The correlation ladder, and the blocks that
+ *   contain it, need n_nodes * (2 l_prod + 1) < 2^26 (the row index range of
+ *   its matrix-core GEMMs); larger requests return FC_ERR_UNSUPPORTED.
+ * Graph contents are not checked by the device calls: a graph must satisfy
+ *   fc_graph_validate (rowptr monotone from 0 to E, senders in [0, N)),
+ *   otherwise kernels read and write out of bounds.
  *
  * Layouts (row-major, channels contiguous)
  * ----------------------------------------

@@ -113,6 +113,36 @@ def test_graph_validate():
         assert ei.value.status == fc.FC_ERR_INVALID_ARGUMENT
 
 
+def test_device_graph_rejects_bad_graph_before_upload():
+    """The device calls trust the graph; the binding validates the host copy
+    first (an out-of-range sender, a short rowptr)."""
+    for rp, sd, n in [([0, 2, 3, 4], [1, 2, 0, 3], 3), ([0, 2, 3], [1, 2, 0], 3)]:
+        with pytest.raises(fc.FlashCartError) as ei:
+            fc.DeviceGraph(np.array(rp, np.int32), np.array(sd, np.int32), n, device="cpu")
+        assert ei.value.status == fc.FC_ERR_INVALID_ARGUMENT
+
+
+def test_large_node_arrays_are_accepted():
+    """Node arrays past 2 GiB (rank 4, 128 channels, 20 000 nodes: g is
+    2.36 GB) are within the kernels' 64-bit offsets, so the descriptor and
+    the workspace queries accept them."""
+    d = fc.conv_desc(20000, 80000, 128, 4, 4, 4, 5.0)
+    P, nin, nout = fc.fc_conv_layout(d)
+    assert 20000 * nout * 128 * 4 > 2 ** 31
+    assert fc.fc_edge_conv_workspace_bytes(d, 1) > 0
+    assert fc.fc_edge_conv_workspace_bytes(d, 2) > 20000 * nout * 128 * 4
+
+
+def test_ladder_row_index_limit():
+    """The ladder's GEMM row index n (2l + 1) + c must stay below 2^26."""
+    ok = fc.ladder_desc(7_000_000, 32, 4, 4, 4, 2, fc.FC_LADDER_PATH_REDUCED)
+    fc.fc_ladder_layout(ok)
+    big = fc.ladder_desc(7_500_000, 32, 4, 4, 4, 2, fc.FC_LADDER_PATH_REDUCED)
+    with pytest.raises(fc.FlashCartError) as ei:
+        fc.fc_ladder_layout(big)
+    assert ei.value.status == fc.FC_ERR_UNSUPPORTED
+
+
 def test_workspace_sizes():
     d = fc.conv_desc(1024, 131072, 128, 2, 2, 2, 5.0)
     assert fc.fc_edge_conv_workspace_bytes(d, 0) == 0

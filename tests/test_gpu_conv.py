@@ -133,6 +133,34 @@ def test_graph_transpose_matches_stable_sort():
                           np.concatenate([[0], np.cumsum(np.bincount(d["sender"], minlength=300))]))
 
 
+def test_graph_transpose_skewed_degrees():
+    """One sender feeds every receiver, a tenth of the nodes send nothing,
+    and senders are unsorted within a receiver: the transpose lists each
+    sender's edge ids in ascending order whatever the scatter did."""
+    from cartesian_tensor_product_amd import flashcart as fc
+    rng = np.random.default_rng(23)
+    N = 700
+    quiet = rng.choice(np.arange(1, N), size=N // 10, replace=False)
+    pool = np.setdiff1d(np.arange(N), quiet)
+    rows = []
+    for u in range(N):
+        k = int(rng.integers(0, 60))
+        s = rng.choice(pool[pool != u], size=k, replace=False)
+        if u != 0:
+            s = np.concatenate([s[s != 0], [0]])
+        rows.append(rng.permutation(s))
+    rowptr = np.concatenate([[0], np.cumsum([len(r) for r in rows])]).astype(np.int32)
+    sender = np.concatenate(rows).astype(np.int32)
+    g = fc.DeviceGraph(rowptr, sender, N)
+    torch.cuda.synchronize()
+    recv = np.repeat(np.arange(N), np.diff(rowptr))
+    assert np.count_nonzero(sender == 0) == N - 1
+    assert np.array_equal(g.receiver.cpu().numpy(), recv)
+    assert np.array_equal(g.t_edge.cpu().numpy(), np.argsort(sender, kind="stable"))
+    assert np.array_equal(g.t_rowptr.cpu().numpy(),
+                          np.concatenate([[0], np.cumsum(np.bincount(sender, minlength=N))]))
+
+
 def test_periodic_shifts_diamond():
     """The diamond cell's convolution (scalar senders, ranks <= 3, shifts)."""
     spec = conv.ConvSpec(0, 3, 3, 5.0)

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/flashcart.h"
@@ -17,6 +18,13 @@
 #include "fc_radial.h"
 #include "fc_model.h"
 #include "fc_gemm.h"
+
+// Scratch of the allocation-free VJP (fc_edge_conv_vjp_noalloc): the VJP
+// workspace of one call, in device memory the library owns.  Each GPU the
+// library runs on holds its own copy from module load until the process
+// ends; all calls on one GPU share it.
+constexpr size_t kNoAllocScratchBytes = FC_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 namespace {
 
@@ -229,6 +237,64 @@ fc_status ladder_plan(const fc_ladder_desc* d, fc::LadderPlan* p) {
   return FC_OK;
 }
 
+fc_status check_vjp_args(const fc_conv_desc* d, const fc_graph* g, const float* pos, const float* shift,
+                         const float* x, const float* radial_w, const float* g_z, const float* x_grad,
+                         const float* pos_grad, const float* radial_w_grad) {
+  if (fc_status s = check_desc(d)) return s;
+  if (!g || !g->rowptr || !g->t_rowptr || (d->n_edges > 0 && (!g->sender || !g->receiver || !g->t_edge)))
+    return fail(FC_ERR_INVALID_ARGUMENT, "VJP needs the full graph (run fc_graph_transpose first)");
+  if (!pos || !x || !radial_w || !g_z) return fail(FC_ERR_INVALID_ARGUMENT, "VJP: NULL pos, x, radial_w or g_z");
+  if (!x_grad && !pos_grad && !radial_w_grad) return fail(FC_ERR_INVALID_ARGUMENT, "VJP: no output requested");
+  if (misaligned(pos, 4) || misaligned(x, 4) || misaligned(radial_w, 4) || misaligned(g_z, 4) ||
+      misaligned(x_grad, 4) || misaligned(pos_grad, 4) || misaligned(radial_w_grad, 4) || misaligned(shift, 4))
+    return fail(FC_ERR_INVALID_ARGUMENT, "VJP: arrays must be 4-byte aligned");
+  return FC_OK;
+}
+
+// The VJP launches on a checked request; `workspace` holds at least the
+// VjpWorkspace layout (its radial-weight partials only when radial_w_grad is
+// requested).  The kernels write every workspace slot they later read, so
+// its initial contents do not matter.
+fc_status run_vjp(const fc_conv_desc* d, const fc_graph* g, const float* pos, const float* shift, const float* x,
+                  const float* radial_w, const float* g_z, float* x_grad, float* pos_grad, float* radial_w_grad,
+                  void* workspace, hipStream_t stream) {
+  fc::ConvArgs a = make_args(d, g, pos, shift, x, radial_w);
+  a.g = g_z;
+  a.x_bar = x_grad;
+  a.pos_bar = pos_grad;
+  a.W_bar = radial_w_grad;
+  a.rbar = static_cast<float*>(workspace);
+  fc::conv_dispatch(1, d->l_in, d->l_edge, lout_key(d), a, stream);
+  return check_launch("edge conv VJP");
+}
+
+// Device address of this GPU's copy of `scratch`, looked up once per device
+// (with that device current) and kept.  In host code the array's name is
+// only a stand-in for the symbol: kernels get this address, never the name.
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+fc_status device_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FC_ERR_HIP, "allocation-free VJP: hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(FC_ERR_UNSUPPORTED, "allocation-free VJP: device %d is beyond the %d the library tracks", dev,
+                kMaxScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(FC_ERR_HIP, "allocation-free VJP: hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -363,25 +429,31 @@ fc_status fc_edge_conv_vjp(const fc_conv_desc* d, const fc_graph* g, const float
                            const float* x, const float* radial_w, const float* g_z, float* x_grad,
                            float* pos_grad, float* radial_w_grad, void* workspace, size_t workspace_bytes,
                            hipStream_t stream) {
-  if (fc_status s = check_desc(d)) return s;
-  if (!g || !g->rowptr || !g->t_rowptr || (d->n_edges > 0 && (!g->sender || !g->receiver || !g->t_edge)))
-    return fail(FC_ERR_INVALID_ARGUMENT, "VJP needs the full graph (run fc_graph_transpose first)");
-  if (!pos || !x || !radial_w || !g_z) return fail(FC_ERR_INVALID_ARGUMENT, "VJP: NULL pos, x, radial_w or g_z");
-  if (!x_grad && !pos_grad && !radial_w_grad) return fail(FC_ERR_INVALID_ARGUMENT, "VJP: no output requested");
-  if (misaligned(pos, 4) || misaligned(x, 4) || misaligned(radial_w, 4) || misaligned(g_z, 4) ||
-      misaligned(x_grad, 4) || misaligned(pos_grad, 4) || misaligned(radial_w_grad, 4) || misaligned(shift, 4))
-    return fail(FC_ERR_INVALID_ARGUMENT, "VJP: arrays must be 4-byte aligned");
+  if (fc_status s = check_vjp_args(d, g, pos, shift, x, radial_w, g_z, x_grad, pos_grad, radial_w_grad)) return s;
   const size_t need = fc_edge_conv_workspace_bytes(d, 1);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(FC_ERR_WORKSPACE, "VJP needs %zu workspace bytes", need);
-  fc::ConvArgs a = make_args(d, g, pos, shift, x, radial_w);
-  a.g = g_z;
-  a.x_bar = x_grad;
-  a.pos_bar = pos_grad;
-  a.W_bar = radial_w_grad;
-  a.rbar = static_cast<float*>(workspace);
-  fc::conv_dispatch(1, d->l_in, d->l_edge, lout_key(d), a, stream);
-  return check_launch("edge conv VJP");
+  return run_vjp(d, g, pos, shift, x, radial_w, g_z, x_grad, pos_grad, radial_w_grad, workspace, stream);
+}
+
+fc_status fc_edge_conv_vjp_noalloc(const fc_conv_desc* d, const fc_graph* g, const float* pos, const float* shift,
+                                   const float* x, const float* radial_w, const float* g_z, float* x_grad,
+                                   float* pos_grad, float* radial_w_grad, hipStream_t stream) {
+  if (fc_status s = check_vjp_args(d, g, pos, shift, x, radial_w, g_z, x_grad, pos_grad, radial_w_grad)) return s;
+  int P, nin, nout;
+  layout(d, &P, &nin, &nout);
+  // the partial radial-weight gradients come last in the layout: without
+  // radial_w_grad the call needs only the part before them
+  const size_t need = fc::VjpWorkspace(d->n_nodes, d->n_edges, d->channels, nin, P, radial_w_grad != nullptr,
+                                       nullptr).bytes;
+  if (need > kNoAllocScratchBytes)
+    return fail(FC_ERR_WORKSPACE,
+                "allocation-free VJP: this call needs %zu scratch bytes, above the %zu bytes the library holds per "
+                "GPU (use fc_edge_conv_vjp with a caller workspace)",
+                need, kNoAllocScratchBytes);
+  void* ptr = nullptr;
+  if (fc_status s = device_scratch(&ptr)) return s;
+  return run_vjp(d, g, pos, shift, x, radial_w, g_z, x_grad, pos_grad, radial_w_grad, ptr, stream);
 }
 
 fc_status fc_edge_conv_fwd_w(const fc_conv_desc* d, const fc_graph* g, const float* pos, const float* shift,

@@ -71,6 +71,7 @@ _SIGS = {
     "fc_edge_conv_workspace_bytes": (_SZ, [_PD, _I]),
     "fc_edge_conv_fwd": (_I, [_PD, _PG, _P, _P, _P, _P, _P, _P]),
     "fc_edge_conv_vjp": (_I, [_PD, _PG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "fc_edge_conv_vjp_noalloc": (_I, [_PD, _PG, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "fc_edge_conv_vjp_vjp": (_I, [_PD, _PG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "fc_edge_conv_fwd_w": (_I, [_PD, _PG, _P, _P, _P, _P, _P, _P]),
     "fc_edge_conv_vjp_w": (_I, [_PD, _PG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -287,6 +288,14 @@ def fc_edge_conv_vjp(d: ConvDesc, graph: DeviceGraph, pos, shift, x, radial_w, g
     _check(lib().fc_edge_conv_vjp(ctypes.byref(d), ctypes.byref(graph.struct), _f32(pos), _f32(shift), _f32(x),
                                   _f32(radial_w), _f32(g_z), _f32(x_grad), _f32(pos_grad), _f32(radial_w_grad),
                                   _ptr(workspace), nbytes, _stream(stream)))
+
+
+def fc_edge_conv_vjp_noalloc(d: ConvDesc, graph: DeviceGraph, pos, shift, x, radial_w, g_z, x_grad, pos_grad,
+                             radial_w_grad, stream=None):
+    """fc_edge_conv_vjp with the library's own per-GPU scratch (no workspace)."""
+    _check(lib().fc_edge_conv_vjp_noalloc(ctypes.byref(d), ctypes.byref(graph.struct), _f32(pos), _f32(shift),
+                                          _f32(x), _f32(radial_w), _f32(g_z), _f32(x_grad), _f32(pos_grad),
+                                          _f32(radial_w_grad), _stream(stream)))
 
 
 def fc_edge_conv_fwd_w(d: ConvDesc, graph: DeviceGraph, pos, shift, x, w, z, stream=None):

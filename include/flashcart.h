@@ -176,6 +176,28 @@ fc_status fc_edge_conv_vjp(const fc_conv_desc* d, const fc_graph* g, const float
                            float* radial_w_grad, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * VJP as fc_edge_conv_vjp (same kernels, same results) with its workspace
+ * taken from a device array the library owns, FC_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) on each GPU it runs on, held until the process ends.  The call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine);
+ * the caller still passes inputs and outputs.  A call needs the VJP
+ * workspace of fc_edge_conv_workspace_bytes(d, 1), less its per-block
+ * radial-weight partials when radial_w_grad is NULL (at 1024 nodes x 128
+ * neighbours x 128 channels, ranks <= 2: 20.5 MB, or 32.0 MB with
+ * radial_w_grad; ranks <= 3: 35.2 MB / 59.3 MB); a larger request returns
+ * FC_ERR_WORKSPACE before any launch.  All calls on one GPU share its array
+ * and leave the last call's partial sums in it (nothing in it needs to start
+ * at zero): calls that overlap on one GPU (different streams or threads)
+ * race, so order them on one stream or with events.  The first call on a
+ * device looks up that device's copy of the array with the device current. */
+#define FC_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+fc_status fc_edge_conv_vjp_noalloc(const fc_conv_desc* d, const fc_graph* g, const float* pos,
+                                   const float* shift, const float* x, const float* radial_w,
+                                   const float* g_z, float* x_grad, float* pos_grad,
+                                   float* radial_w_grad, hipStream_t stream);
+
 /* Forward of Eq. 1 with the per-edge weights given, as the pages state it:
  * w [E][P][C] in receiver-sorted edge order (w[e, eta, k] weights path eta,
  * channel k of edge e) replaces the radial basis; r_cut and n_basis of d are

@@ -92,3 +92,83 @@ def test_message_block_bitwise_deterministic():
     a = gpu_block(cspec, lspec, w, d, entries, C, 3, "reduced")
     b = gpu_block(cspec, lspec, w, d, entries, C, 3, "reduced")
     assert a[0] == b[0] and np.array_equal(a[1], b[1]) and np.array_equal(a[2], b[2])
+
+
+# ------------------------------------------ the timed width, order and size --
+
+_ORACLE = {}
+
+
+def oracle_1000(variant, rattle):
+    """The oracle's energies and forces of the 1000-atom cell at 128
+    channels and order 5 (kept: two tests use the rattled cell)."""
+    key = (variant, rattle)
+    if key not in _ORACLE:
+        cspec, lspec, w, d, _ = block_setup(C=128, order=5, variant=variant, rattle=rattle, ncell=5)
+        _ORACLE[key] = model.block_energy_forces(*args(cspec, lspec, w, d))
+    return _ORACLE[key]
+
+@pytest.mark.parametrize("variant", ["reduced", "full"])
+def test_message_block_1000_atoms_128_channels_order5(variant):
+    """1000 atoms (5 x 5 x 5 cells), 128 channels, ladder order 5: every
+    atom's energy and force against the oracle."""
+    C, order = 128, 5
+    cspec, lspec, w, d, entries = block_setup(C=C, order=order, variant=variant, ncell=5)
+    E, ea, F = gpu_block(cspec, lspec, w, d, entries, C, order, variant)
+    Eo, eao, Fo = oracle_1000(variant, 0.05)
+    assert abs(E - Eo) <= 1e-4 * np.abs(eao).sum()
+    assert_close("e_atom", ea, eao)
+    assert_close("forces", F, Fo)
+
+
+def test_message_block_perfect_cell_against_oracle():
+    """Perfect 1000-atom cell (zero forces by symmetry, up to the fp32
+    rounding of the positions): forces against the oracle with the rattled
+    cell's force scale as the floor, energies element by element."""
+    C, order = 128, 5
+    cspec, lspec, w, d, entries = block_setup(C=C, order=order, rattle=0.0, ncell=5)
+    E, ea, F = gpu_block(cspec, lspec, w, d, entries, C, order, "reduced")
+    Eo, eao, Fo = oracle_1000("reduced", 0.0)
+    _, _, Fr = oracle_1000("reduced", 0.05)
+    assert_close("e_atom", ea, eao)
+    assert_close("forces", F, Fo, floor=np.abs(Fr).max())
+
+
+def local_block_problem(d, nodes):
+    """The edges into ``nodes`` and their neighbours, renumbered: an atom's
+    energy depends on its incoming edges only and an atom's force on the
+    energies of itself and its neighbours, so the sampled atoms' energies and
+    forces on this subgraph equal those of the whole cell (the convolution
+    scale is the whole cell's)."""
+    N = d["pos"].shape[0]
+    rowptr, sender = d["rowptr"], d["sender"]
+    recv = np.repeat(np.arange(N), np.diff(rowptr))
+    near = np.unique(np.concatenate([nodes, sender[np.isin(recv, nodes)], recv[np.isin(sender, nodes)]]))
+    e = np.nonzero(np.isin(recv, near))[0]
+    ids = np.unique(np.concatenate([near, sender[e]]))
+    r2, s2 = np.searchsorted(ids, recv[e]), np.searchsorted(ids, sender[e])
+    rp = np.concatenate([[0], np.cumsum(np.bincount(r2, minlength=len(ids)))]).astype(np.int32)
+    sub = dict(pos=d["pos"][ids], rowptr=rp, sender=s2.astype(np.int32), shift=d["shift"][e], x=d["x"][ids])
+    return ids, sub
+
+
+@pytest.mark.parametrize("variant", ["reduced", "full"])
+def test_message_block_4096_atoms_sampled(variant):
+    """The benchmarked block: 4096 atoms (8 x 8 x 8 cells), 128 channels,
+    order 5, in the launch configuration the benchmark times; four atoms'
+    energies and forces against the oracle on their local subgraph."""
+    C, order = 128, 5
+    cspec, lspec, w, d, entries = block_setup(C=C, order=order, variant=variant, ncell=8)
+    N = d["pos"].shape[0]
+    assert N == 4096
+    E, ea, F = gpu_block(cspec, lspec, w, d, entries, C, order, variant)
+    nodes = np.array([0, 1337, 2900, 4095])
+    ids, sub = local_block_problem(d, nodes)
+    n_bar = len(d["sender"]) / N
+    _, eao, Fo = model.block_energy_forces(cspec, lspec, w, sub["pos"].astype(np.float64), sub["rowptr"],
+                                           sub["sender"], sub["shift"].astype(np.float64),
+                                           sub["x"].astype(np.float64), n_bar)
+    at = np.searchsorted(ids, nodes)
+    assert_close("e_atom", ea[nodes], eao[at])
+    assert_close("forces", F[nodes], Fo[at])
+    assert np.abs(F.astype(np.float64).sum(0)).max() < 1e-4 * np.abs(F).max() * np.sqrt(N)

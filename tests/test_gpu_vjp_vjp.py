@@ -103,12 +103,15 @@ def test_radial_w_hat_ragged_receivers(ranks):
 
 
 @pytest.mark.parametrize("ranks", [(3, 3, 3), (4, 4, 4)])
-def test_vjp_vjp_microbenchmark_sampled(ranks):
+@pytest.mark.parametrize("rc", [5.0, 35.0])
+def test_vjp_vjp_microbenchmark_sampled(ranks, rc):
     """1024 nodes x 128 neighbours x 128 channels, position cotangent only
-    (v_x = 0), 10 sampled nodes compared element by element."""
-    spec = conv.ConvSpec(*ranks, 5.0)
+    (v_x = 0), 10 sampled nodes compared element by element; r_c = 35 A
+    keeps every edge of the 20 A cube inside the cutoff (at 5 A about 95 %
+    of them carry zero weight)."""
+    spec = conv.ConvSpec(*ranks, rc)
     d = inputs.edge_conv_inputs(2, 1024, 128, 20.0, 128, spec.n_in, spec.n_paths, spec.n_out, with_vpos=True)
-    gc = GpuConv(ranks, 5.0, d, 128)
+    gc = GpuConv(ranks, rc, d, 128)
     gh, xh, ph, _ = gc.vjp_vjp(v_pos=d["v_pos"])
     # radial_w_hat through a cotangent that vanishes off the sampled
     # receivers: only their incoming edges contribute

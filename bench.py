@@ -92,7 +92,8 @@ def message_blocks(dev, cases=((8, "path_reduced"), (8, "full"), (5, "path_reduc
         cdm = fc.conv_desc(Nm, Em, CHANNELS, 0, 3, 3, 5.0)
         ldm = fc.ladder_desc(Nm, CHANNELS, 3, 3, 0, 5, var)
         C2 = CHANNELS
-        entries = [("mlp", (4, C2), "mlp", 1), ("M", (4, C2, C2), "normal", C2), ("R0", (C2, C2), "normal", C2),
+        entries = [("mlp", (4, C2), "mlp", 1), ("Mpre", (C2, C2), "normal", C2), ("M", (4, C2, C2), "normal", C2),
+                   ("R0", (C2, C2), "normal", C2),
                    ("gamma1", (4, C2), "one_plus", 1), ("O", (4, C2, C2), "normal", C2)]
         entries += [(f"ladder{i}", (r_, c_), "normal" if k_ == 0 else "one_plus", c_)
                     for i, (_, r_, c_, k_) in enumerate(fc.ladder_weight_blocks(ldm))]
@@ -148,7 +149,7 @@ def extras(dev, only_ladder=False, conv_ranks=(3, 4), only_conv=False):
         del z, xb, pb, gh, xh, ph, ws, Wb
     # every triangle-allowed path (odd J through the Levi-Civita reading), the
     # literal path sets of the microbenchmark configurations: ranks <= 2
-    # (15 paths), <= 3 (34), <= 4 (65; no VJP-of-VJP)
+    # (15 paths), <= 3 (34), <= 4 (65)
     for l in (() if only_ladder else ((2, 3, 4) if not only_conv else ())):
         desc = fc.conv_desc(N_NODES, N_NODES * K_NBR, CHANNELS, l, l, l, R_CUT, flags=fc.FC_CONV_ALL_PARITIES)
         P, n_in, n_out = fc.fc_conv_layout(desc)
@@ -158,15 +159,14 @@ def extras(dev, only_ladder=False, conv_ranks=(3, 4), only_conv=False):
         pos, x, W, g, vp = t(d["pos"]), t(d["x"]), t(d["W"]), t(d["g"]), t(d["v_pos"])
         z = torch.empty((N_NODES, n_out, CHANNELS), device=dev)
         xb, pb = torch.empty_like(x), torch.empty((N_NODES, 3), device=dev)
-        ws = fc.workspace(fc.fc_edge_conv_workspace_bytes(desc, 2 if l <= 3 else 1), dev)
+        ws = fc.workspace(fc.fc_edge_conv_workspace_bytes(desc, 2), dev)
         E = N_NODES * K_NBR
         r = {"paths": P, "fwd_ms": timed(lambda: fc.fc_edge_conv_fwd(desc, graph, pos, None, x, W, z)),
              "vjp_ms": timed(lambda: fc.fc_edge_conv_vjp(desc, graph, pos, None, x, W, g, xb, pb, None, ws))}
-        if l <= 3:
-            gh, xh, ph = torch.empty_like(z), torch.empty_like(x), torch.empty_like(pb)
-            r["vjp_vjp_ms"] = timed(lambda: fc.fc_edge_conv_vjp_vjp(desc, graph, pos, None, x, W, g, None, vp, None, gh, xh,
-                                                                    ph, None, ws), iters=5)
-            del gh, xh, ph
+        gh, xh, ph = torch.empty_like(z), torch.empty_like(x), torch.empty_like(pb)
+        r["vjp_vjp_ms"] = timed(lambda: fc.fc_edge_conv_vjp_vjp(desc, graph, pos, None, x, W, g, None, vp, None, gh, xh,
+                                                                ph, None, ws), iters=5)
+        del gh, xh, ph
         r["fwd_plus_vjp_edge_channels_per_s"] = E * CHANNELS / ((r["fwd_ms"] + r["vjp_ms"]) * 1e-3)
         out[f"conv_all_parities_rank{l}_1024n_128c_128nbr"] = r
         del z, xb, pb, ws
@@ -181,15 +181,14 @@ def extras(dev, only_ladder=False, conv_ranks=(3, 4), only_conv=False):
         pos, x, W, g, vp = t(d["pos"]), t(d["x"]), t(d["W"]), t(d["g"]), t(d["v_pos"])
         z = torch.empty((N_NODES, n_out, CHANNELS), device=dev)
         xb, pb = torch.empty_like(x), torch.empty((N_NODES, 3), device=dev)
-        ws = fc.workspace(fc.fc_edge_conv_workspace_bytes(desc, 2 if l <= 3 else 1), dev)
+        ws = fc.workspace(fc.fc_edge_conv_workspace_bytes(desc, 2), dev)
         E = N_NODES * K_NBR
         r = {"out_rows": n_out, "fwd_ms": timed(lambda: fc.fc_edge_conv_fwd(desc, graph, pos, None, x, W, z)),
              "vjp_ms": timed(lambda: fc.fc_edge_conv_vjp(desc, graph, pos, None, x, W, g, xb, pb, None, ws))}
-        if l <= 3:
-            gh, xh, ph = torch.empty_like(z), torch.empty_like(x), torch.empty_like(pb)
-            r["vjp_vjp_ms"] = timed(lambda: fc.fc_edge_conv_vjp_vjp(desc, graph, pos, None, x, W, g, None, vp, None,
-                                                                    gh, xh, ph, None, ws), iters=5)
-            del gh, xh, ph
+        gh, xh, ph = torch.empty_like(z), torch.empty_like(x), torch.empty_like(pb)
+        r["vjp_vjp_ms"] = timed(lambda: fc.fc_edge_conv_vjp_vjp(desc, graph, pos, None, x, W, g, None, vp, None,
+                                                                gh, xh, ph, None, ws), iters=5)
+        del gh, xh, ph
         r["fwd_plus_vjp_edge_channels_per_s"] = E * CHANNELS / ((r["fwd_ms"] + r["vjp_ms"]) * 1e-3)
         out[f"conv_summed_rank{l}_1024n_128c_128nbr"] = r
         del z, xb, pb, ws
@@ -350,7 +349,7 @@ def compulsory_bytes(N, E, C, n_in, n_out, P, explicit=False):
 def grid(dev, steps):
     """The pages' microbenchmark grid (1024 nodes x {64, 128} neighbours x
     {64, 128, 256} channels x ranks 1-5): forward, VJP and VJP-of-VJP
-    (position cotangent; ranks <= 4) with fused Bessel radial weights, and
+    (position cotangent) with fused Bessel radial weights, and
     forward + VJP with explicit per-edge weights drawn on the device."""
     import torch
 
@@ -378,9 +377,8 @@ def grid(dev, steps):
                      "fwd_ms": timed(lambda: fc.fc_edge_conv_fwd(desc, graph, pos, None, x, W, z), steps),
                      "vjp_ms": timed(lambda: fc.fc_edge_conv_vjp(desc, graph, pos, None, x, W, g, xb, pb, None, ws),
                                      steps),
-                     "vjp_vjp_ms": (timed(lambda: fc.fc_edge_conv_vjp_vjp(desc, graph, pos, None, x, W, g, None, vp,
-                                                                          None, z, xb, pb, None, ws), max(2, steps // 4))
-                                    if l <= 4 else None)}
+                     "vjp_vjp_ms": timed(lambda: fc.fc_edge_conv_vjp_vjp(desc, graph, pos, None, x, W, g, None, vp,
+                                                                         None, z, xb, pb, None, ws), max(2, steps // 4))}
                 w = rn((E, P, C))
                 wb = torch.empty_like(w)
                 r["explicit_fwd_ms"] = timed(lambda: fc.fc_edge_conv_fwd_w(desc, graph, pos, None, x, w, z), steps)

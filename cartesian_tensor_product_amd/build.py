@@ -50,14 +50,22 @@ def _compile(src: str) -> str:
     return f"{os.path.basename(src)} {time.time() - t:.1f}s"
 
 
+# relative cost of the separately compiled VJP-of-VJP passes at the highest
+# ranks (the sender pass with a feature cotangent is the longest unit)
+_PART_WEIGHT = {"vx": 400, "vs": 160, "vr": 40, "vg": 40}
+
+
 def _weight(src: str) -> int:
     """Rough compile cost, so that the largest units start first: the ranks
-    of a convolution unit conv_inst_<l_in><l_edge><l_out key>[w]."""
+    of a convolution unit conv_inst_<l_in><l_edge><l_out key>[w | vr | vg |
+    vs | vx]."""
     name = os.path.basename(src)
     if name.startswith("conv_inst_"):
-        digits = name[len("conv_inst_"):-len(".hip")]
-        xw = digits.endswith("w")   # explicit-weight VJP-of-VJP unit
-        digits = digits.rstrip("w")
+        stem = name[len("conv_inst_"):-len(".hip")]
+        if stem[-2:] in _PART_WEIGHT:
+            return _PART_WEIGHT[stem[-2:]]
+        xw = stem.endswith("w")   # explicit-weight VJP-of-VJP unit
+        digits = stem.rstrip("w")
         a, b, key = int(digits[0]), int(digits[1]), int(digits[2:])
         return (a + b + key % 8 + (4 if (key // 8) % 2 else 0)) * (8 if xw else 10)
     return 1

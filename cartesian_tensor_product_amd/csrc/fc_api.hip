@@ -579,7 +579,7 @@ fc_status fc_edge_conv_vjp_vjp_w(const fc_conv_desc* d, const fc_graph* g, const
                                  const float* v_pos, const float* v_w, float* g_hat, float* x_hat, float* pos_hat,
                                  float* w_hat, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (fc_status s = check_desc(d)) return s;
-  if (!fc::conv_vv_supported(d->l_in, d->l_edge, lout_key(d)))
+  if (!fc::conv_vv_w_supported(d->l_in, d->l_edge, lout_key(d)))
     return fail(FC_ERR_UNSUPPORTED, "VJP-of-VJP is not instantiated for (l_in, l_edge, l_out) = (%d, %d, %d)",
                 d->l_in, d->l_edge, d->l_out);
   if (!g_hat && !x_hat && !pos_hat && !w_hat)
@@ -749,12 +749,12 @@ fc_status block_layout(const fc_conv_desc* cd, const fc_ladder_desc* ld, BlockLa
 
 // A full message-passing block: flat weight offsets (floats) and workspace
 // (bytes), in the order
-//   radial network | M [l+1][C][C] | R0 [C][C] | gamma1 [l+1][C] |
-//   O [l+1][C][C] | ladder | R2 [C][C] | gamma2 [C] | Wr1 [C][64] |
-//   Wr2 [64][64] | wr3 [64]
+//   radial network | Mpre [C][C] | M [l+1][C][C] | R0 [C][C] |
+//   gamma1 [l+1][C] | O [l+1][C][C] | ladder | R2 [C][C] | gamma2 [C] |
+//   Wr1 [C][64] | Wr2 [64][64] | wr3 [64]
 struct MsgLayout {
-  size_t w_mlp, w_M, w_R0, w_g1, w_O, w_lad, w_R2, w_g2, w_r1, w_r2, w_r3, n_weights;
-  size_t a, m, n, y, A, Ab, nb, mb, z, f, fb, ob, inv1, inv2, ea, saved, lws, cws, cws_bytes, parts, total;
+  size_t w_mlp, w_pre, w_M, w_R0, w_g1, w_O, w_lad, w_R2, w_g2, w_r1, w_r2, w_r3, n_weights;
+  size_t a, m, n, y, A, Ab, nb, mb, hb, z, f, fb, ob, inv1, inv2, ea, saved, lws, cws, cws_bytes, parts, total;
 };
 
 fc_status msg_layout(const fc_conv_desc* cd, const fc_ladder_desc* ld, MsgLayout* L) {
@@ -770,6 +770,7 @@ fc_status msg_layout(const fc_conv_desc* cd, const fc_ladder_desc* ld, MsgLayout
   const size_t C2 = C * C, H = fc::kReadoutHidden;
   size_t o = 0;
   L->w_mlp = o; o += fc::radial_weight_floats((int)le + 1, (int)C);
+  L->w_pre = o; o += C2;
   L->w_M = o;   o += (le + 1) * C2;
   L->w_R0 = o;  o += C2;
   L->w_g1 = o;  o += (le + 1) * C;
@@ -785,7 +786,7 @@ fc_status msg_layout(const fc_conv_desc* cd, const fc_ladder_desc* ld, MsgLayout
   o = 0;
   size_t* big[] = {&L->a, &L->m, &L->n, &L->y, &L->A, &L->Ab, &L->nb, &L->mb};
   for (size_t* b : big) { *b = o; o += al(N * R * C); }
-  size_t* small[] = {&L->z, &L->f, &L->fb, &L->ob};
+  size_t* small[] = {&L->hb, &L->z, &L->f, &L->fb, &L->ob};
   for (size_t* b : small) { *b = o; o += al(N * C); }
   L->inv1 = o;  o += al(N);
   L->inv2 = o;  o += al(N);
@@ -999,7 +1000,8 @@ fc_status fc_message_block_energy_forces(const fc_conv_desc* cd, const fc_graph*
   char* wb = static_cast<char*>(workspace);
   auto buf = [&](size_t off) { return reinterpret_cast<float*>(wb + off); };
   float *a = buf(L.a), *m = buf(L.m), *n = buf(L.n), *y = buf(L.y), *A = buf(L.A), *Ab = buf(L.Ab);
-  float *nb = buf(L.nb), *mb = buf(L.mb), *z = buf(L.z), *f = buf(L.f), *fb = buf(L.fb), *ob = buf(L.ob);
+  float *nb = buf(L.nb), *mb = buf(L.mb), *hb = buf(L.hb), *z = buf(L.z), *f = buf(L.f), *fb = buf(L.fb);
+  float* ob = buf(L.ob);
   float *inv1 = buf(L.inv1), *inv2 = buf(L.inv2), *ea = buf(L.ea), *saved = buf(L.saved), *lws = buf(L.lws);
   double* parts = reinterpret_cast<double*>(wb + L.parts);
   const float* W = weights;
@@ -1014,7 +1016,12 @@ fc_status fc_message_block_energy_forces(const fc_conv_desc* cd, const fc_graph*
   const MlpWorkspace mws(cd, 1, wb + L.cws);
 
   // ---- forward
-  mlp_conv_forward(cd, g, pos, shift, h0, W + L.w_mlp, a, mws, stream);
+  {  // hb = Mpre h0: the channel map of the sender features before the convolution
+    fc::GemmGroup gg{};
+    gg.prob[gg.count++] = channel_map(N, C, h0, 1, 0, W + L.w_pre, false, hb, 1, 0, 0);
+    fc::gemm_group(gg, stream);
+  }
+  mlp_conv_forward(cd, g, pos, shift, hb, W + L.w_mlp, a, mws, stream);
   {  // m_l = conv_scale M_l a_l (the scale rides on the GEMM) + R0 h0 for l = 0
     fc::GemmGroup gg{};
     for (int l = 0; l <= le; ++l) {
@@ -1067,7 +1074,7 @@ fc_status fc_message_block_energy_forces(const fc_conv_desc* cd, const fc_graph*
     }
     fc::gemm_group(gg, stream);
   }
-  mlp_conv_vjp(cd, g, pos, shift, h0, W + L.w_mlp, a, nullptr, forces, nullptr, mws, wb + L.cws, true, stream);
+  mlp_conv_vjp(cd, g, pos, shift, hb, W + L.w_mlp, a, nullptr, forces, nullptr, mws, wb + L.cws, true, stream);
   return check_launch("message block energy/forces");
 }
 

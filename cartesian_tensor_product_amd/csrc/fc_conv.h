@@ -29,8 +29,6 @@ struct ConvArgs {
   const float* v_w_edge;
 };
 
-#include "generated/fc_conv_configs.h"
-
 // l_out is the output-rank key: l_out + kAllParities keeps every
 // triangle-allowed path
 bool conv_supported(int l_in, int l_edge, int l_out);
@@ -80,10 +78,23 @@ struct VjpWorkspace {
 };
 
 void launch_vjp_combine(const ConvArgs& a, const VjpWorkspace& w, int nin, hipStream_t st);
+
+// The launch sequences of one configuration's VJP-of-VJP passes (g_hat,
+// W_hat, and the sender pass without / with a feature cotangent).
+struct VVParts {
+  void (*recv)(const ConvArgs&, hipStream_t);
+  void (*wgrad)(const ConvArgs&, hipStream_t);
+  void (*sender)(const ConvArgs&, hipStream_t);
+  void (*sender_vx)(const ConvArgs&, hipStream_t);
+};
+// g_hat, W_hat (args.W_bar), then x_hat / pos_hat with the combine pass,
+// each when requested; nin input rows and P paths size the workspace.
+void run_vjp_vjp(const VVParts& parts, int nin, int P, const ConvArgs& a, hipStream_t st);
 bool conv_dispatch(int op, int l_in, int l_edge, int l_out, const ConvArgs& args, hipStream_t stream);
 // VJP-of-VJP with explicit per-edge weights (w_edge, v_w_edge; w_hat in
 // w_edge_bar); false when not instantiated (the configurations of
 // conv_vv_supported)
 bool conv_vv_w_dispatch(int l_in, int l_edge, int l_out, const ConvArgs& args, hipStream_t stream);
+bool conv_vv_w_supported(int l_in, int l_edge, int l_out);
 
 }  // namespace fc

@@ -2,6 +2,7 @@
 // in its own generated translation unit (generated/conv_inst_*.hip) so that
 // the heavily unrolled kernels compile in parallel.
 #include "fc_conv.h"
+#include "generated/fc_conv_configs.h"
 
 namespace fc {
 
@@ -89,8 +90,25 @@ bool conv_dispatch(int op, int l_in, int l_edge, int l_out, const ConvArgs& args
   }
 }
 
+void run_vjp_vjp(const VVParts& parts, int nin, int P, const ConvArgs& a, hipStream_t st) {
+  if (a.g_hat) parts.recv(a, st);
+  if (a.W_bar) parts.wgrad(a, st);
+  if (!a.x_bar && !a.pos_bar) return;
+  if (a.v_x) parts.sender_vx(a, st);
+  else parts.sender(a, st);
+  const VjpWorkspace wsl(a.N, a.E, a.C, nin, P, true, a.rbar);
+  launch_vjp_combine(a, wsl, nin, st);
+}
+
+bool conv_vv_w_supported(int l_in, int l_edge, int l_out) {
+  switch (l_in * 1024 + l_edge * 32 + l_out) {
+    FC_CONV_VV_W_CONFIGS(FC_CONV_SUPPORTED)
+    default: return false;
+  }
+}
+
 #define FC_CONV_W_DECL(A, B, Cc) void conv_run_w_##A##B##Cc(const ConvArgs& args, hipStream_t stream);
-FC_CONV_VV_CONFIGS(FC_CONV_W_DECL)
+FC_CONV_VV_W_CONFIGS(FC_CONV_W_DECL)
 
 #define FC_CONV_W_CASE(A, B, Cc)            \
   case (A) * 1024 + (B) * 32 + (Cc):         \
@@ -99,7 +117,7 @@ FC_CONV_VV_CONFIGS(FC_CONV_W_DECL)
 
 bool conv_vv_w_dispatch(int l_in, int l_edge, int l_out, const ConvArgs& args, hipStream_t stream) {
   switch (l_in * 1024 + l_edge * 32 + l_out) {
-    FC_CONV_VV_CONFIGS(FC_CONV_W_CASE)
+    FC_CONV_VV_W_CONFIGS(FC_CONV_W_CASE)
     default: return false;
   }
 }

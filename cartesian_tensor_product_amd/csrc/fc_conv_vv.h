@@ -716,17 +716,33 @@ void launch_vv_sender_vx(const ConvArgs& a, const VjpWorkspace& wsl, hipStream_t
 #undef FC_VV
 }
 
+// The passes of the VJP-of-VJP, each a separate launch sequence (the
+// g_hat pass, the W_hat pass, the sender pass for x_hat and the per-edge
+// position terms without and with a feature cotangent); at the highest
+// ranks each is instantiated in a unit of its own and composed by
+// run_vjp_vjp.
+template <int LIN, int LEDGE, int LOUT>
+void vv_part_recv(const ConvArgs& a, hipStream_t st) {
+  launch_vv_recv<LIN, LEDGE, LOUT>(a, st);
+}
+template <int LIN, int LEDGE, int LOUT>
+void vv_part_wgrad(const ConvArgs& a, hipStream_t st) {
+  const VjpWorkspace wsl(a.N, a.E, a.C, nrank(LIN), ConvCfg<LIN, LEDGE, LOUT>::P, true, a.rbar);
+  launch_wgrad_vv<LIN, LEDGE, LOUT>(a, wsl.w_part, st);
+}
+template <int LIN, int LEDGE, int LOUT, bool HAS_VX>
+void vv_part_sender(const ConvArgs& a, hipStream_t st) {
+  const VjpWorkspace wsl(a.N, a.E, a.C, nrank(LIN), ConvCfg<LIN, LEDGE, LOUT>::P, true, a.rbar);
+  launch_vv_sender_vx<LIN, LEDGE, LOUT, HAS_VX>(a, wsl, st);
+}
+
 // g_hat, W_hat (W_bar of the arguments), then x_hat / pos_hat, each when
 // requested.
 template <int LIN, int LEDGE, int LOUT>
 void launch_vjp_vjp(const ConvArgs& a, hipStream_t st) {
-  if (a.g_hat) launch_vv_recv<LIN, LEDGE, LOUT>(a, st);
-  const VjpWorkspace wsl(a.N, a.E, a.C, nrank(LIN), ConvCfg<LIN, LEDGE, LOUT>::P, true, a.rbar);
-  if (a.W_bar) launch_wgrad_vv<LIN, LEDGE, LOUT>(a, wsl.w_part, st);
-  if (!a.x_bar && !a.pos_bar) return;
-  if (a.v_x) launch_vv_sender_vx<LIN, LEDGE, LOUT, true>(a, wsl, st);
-  else launch_vv_sender_vx<LIN, LEDGE, LOUT, false>(a, wsl, st);
-  launch_vjp_combine(a, wsl, nrank(LIN), st);
+  run_vjp_vjp(VVParts{vv_part_recv<LIN, LEDGE, LOUT>, vv_part_wgrad<LIN, LEDGE, LOUT>,
+                      vv_part_sender<LIN, LEDGE, LOUT, false>, vv_part_sender<LIN, LEDGE, LOUT, true>},
+              nrank(LIN), ConvCfg<LIN, LEDGE, LOUT>::P, a, st);
 }
 
 // Explicit per-edge weights w = a.w_edge [E][P][C] (receiver-sorted edge

@@ -478,9 +478,14 @@ def emit(path: str, max_rank=MAX_RANK) -> None:
 # sweeps per sender.
 ALL_PARITIES = 8
 SUM_PATHS = 16
-VV_MAX_RANK = 4
-VV_MAX_RANK_ALL = 3
-VV_MAX_RANK_SUM = 3
+VV_MAX_RANK = 5
+VV_MAX_RANK_ALL = 4
+VV_MAX_RANK_SUM = 4
+VV_W_MAX_RANK = 4        # explicit-weight VJP-of-VJP, natural parity and paths separate
+VV_W_MAX_RANK_OTHER = 3  # ... with every parity or summed paths
+# from these ranks each VJP-of-VJP pass is compiled in a unit of its own
+VV_SPLIT_RANK = 5
+VV_SPLIT_RANK_OTHER = 4
 SUM_MAX_RANK = 4
 
 
@@ -511,6 +516,25 @@ def has_vv(cfg) -> bool:
     return max(li, le, lo) <= (VV_MAX_RANK_ALL if allp else VV_MAX_RANK)
 
 
+def has_vv_w(cfg) -> bool:
+    li, le, lo, allp = cfg_ranks(cfg)
+    other = allp or cfg_summed(cfg)
+    return has_vv(cfg) and max(li, le, lo) <= (VV_W_MAX_RANK_OTHER if other else VV_W_MAX_RANK)
+
+
+def vv_split(cfg) -> bool:
+    li, le, lo, allp = cfg_ranks(cfg)
+    other = allp or cfg_summed(cfg)
+    return has_vv(cfg) and max(li, le, lo) >= (VV_SPLIT_RANK_OTHER if other else VV_SPLIT_RANK)
+
+
+# the passes of a split VJP-of-VJP: unit suffix, function, body
+VV_PARTS = [("vr", "recv", "vv_part_recv<{r}>(a, st);"),
+            ("vg", "wgrad", "vv_part_wgrad<{r}>(a, st);"),
+            ("vs", "send", "vv_part_sender<{r}, false>(a, st);"),
+            ("vx", "sendvx", "vv_part_sender<{r}, true>(a, st);")]
+
+
 def emit_instances(gen_dir: str) -> list:
     """One translation unit per convolution configuration, plus the list."""
     cfgs = conv_configs()
@@ -520,23 +544,41 @@ def emit_instances(gen_dir: str) -> list:
     lines += [f"  X({a}, {b}, {c}) \\" for a, b, c in cfgs]
     lines += ["", "", "// ... of which the VJP-of-VJP is instantiated for", "#define FC_CONV_VV_CONFIGS(X) \\"]
     lines += [f"  X({a}, {b}, {c}) \\" for a, b, c in cfgs if has_vv((a, b, c))]
+    lines += ["", "", "// ... and the VJP-of-VJP with explicit per-edge weights for", "#define FC_CONV_VV_W_CONFIGS(X) \\"]
+    lines += [f"  X({a}, {b}, {c}) \\" for a, b, c in cfgs if has_vv_w((a, b, c))]
     lines += ["", ""]
     _write(os.path.join(gen_dir, "fc_conv_configs.h"), "\n".join(lines))
     files = []
+    head = "// Generated by cartesian_tensor_product_amd/gen/generate.py -- do not edit.\n"
     for a, b, c in cfgs:
-        vv = has_vv((a, b, c))
-        src = (f"// Generated by cartesian_tensor_product_amd/gen/generate.py -- do not edit.\n"
-               f"#include \"../{'fc_conv_vv.h' if vv else 'fc_conv_kernels.h'}\"\n\n"
-               f"namespace fc {{\n\n"
-               f"bool conv_run_{a}{b}{c}(int op, const ConvArgs& args, hipStream_t stream) {{\n"
-               f"  if (op == 0) launch_fwd<{a}, {b}, {c}>(args, stream);\n"
-               f"  else if (op == 1) launch_vjp<{a}, {b}, {c}>(args, stream);\n"
-               + (f"  else launch_vjp_vjp<{a}, {b}, {c}>(args, stream);\n" if vv else "  else return false;\n")
+        vv, split = has_vv((a, b, c)), vv_split((a, b, c))
+        key, r = f"{a}{b}{c}", f"{a}, {b}, {c}"
+        if split:
+            # the VJP-of-VJP passes are compiled in units of their own (in
+            # parallel) and composed here
+            decl = "".join(f"void conv_vv{key}_{fn}(const ConvArgs& a, hipStream_t st);\n" for _, fn, _ in VV_PARTS)
+            vv_line = (f"  else run_vjp_vjp(VVParts{{{', '.join(f'conv_vv{key}_{fn}' for _, fn, _ in VV_PARTS)}}},"
+                       f" nrank({a}), ConvCfg<{r}>::P, args, stream);\n")
+            for suf, fn, body in VV_PARTS:
+                f = os.path.join(gen_dir, f"conv_inst_{key}{suf}.hip")
+                _write(f, head + "#include \"../fc_conv_vv.h\"\n\nnamespace fc {\n\n"
+                       f"void conv_vv{key}_{fn}(const ConvArgs& a, hipStream_t st) {{ {body.format(r=r)} }}\n\n"
+                       "}  // namespace fc\n")
+                files.append(f)
+        else:
+            decl = ""
+            vv_line = f"  else launch_vjp_vjp<{r}>(args, stream);\n" if vv else "  else return false;\n"
+        src = (head + f"#include \"../{'fc_conv_vv.h' if vv and not split else 'fc_conv_kernels.h'}\"\n\n"
+               f"namespace fc {{\n\n" + decl + ("\n" if decl else "") +
+               f"bool conv_run_{key}(int op, const ConvArgs& args, hipStream_t stream) {{\n"
+               f"  if (op == 0) launch_fwd<{r}>(args, stream);\n"
+               f"  else if (op == 1) launch_vjp<{r}>(args, stream);\n"
+               + vv_line
                + f"  return true;\n}}\n\n}}  // namespace fc\n")
         f = os.path.join(gen_dir, f"conv_inst_{a}{b}{c}.hip")
         _write(f, src)
         files.append(f)
-        if vv:
+        if has_vv_w((a, b, c)):
             # the explicit-weight VJP-of-VJP in a unit of its own (compiles in parallel)
             src = (f"// Generated by cartesian_tensor_product_amd/gen/generate.py -- do not edit.\n"
                    f"#include \"../fc_conv_vv.h\"\n\n"

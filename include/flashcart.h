@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define FC_ABI_VERSION 2
+#define FC_ABI_VERSION 3
 
 typedef enum {
   FC_OK = 0,
@@ -387,7 +387,9 @@ fc_status fc_block_energy_forces(const fc_conv_desc* conv, const fc_graph* g, co
  * architecture"; App. F for the radial network, SiLU gates and the readout
  * width), one final block with scalar senders in and scalars out, with the
  * caller's (random) weights.  Readings where the pages leave a step open:
- *   a   = conv_scale * conv(h0), weights from the radial network (Eq. E1);
+ *   hb  = Mpre h0 (the d x d channel map of the sender features before the
+ *         convolution; one rank with scalar senders);
+ *   a   = conv_scale * conv(hb), weights from the radial network (Eq. E1);
  *   m_l = M_l a_l (rank-wise map of the paths and channels; one path per
  *         rank with scalar senders), m_0 += R0 h0 (residual update);
  *   n   = RMSnorm(m; gamma1, eps) (fc_rms_norm_fwd);
@@ -398,8 +400,8 @@ fc_status fc_block_energy_forces(const fc_conv_desc* conv, const fc_graph* g, co
  *         (bias-free readout MLP C -> 64 -> 64 -> 1);
  *   E   = sum_u E_u (fp64, fixed order), forces = -dE/dpos.
  * Matrices act on channels as [out][in].  Flat weights, in order: radial
- * network (fc_radial_mlp_weight_floats layout, P = l_edge + 1), M
- * [l+1][C][C], R0 [C][C], gamma1 [l+1][C], O [l+1][C][C], ladder weights
+ * network (fc_radial_mlp_weight_floats layout, P = l_edge + 1), Mpre
+ * [C][C], M [l+1][C][C], R0 [C][C], gamma1 [l+1][C], O [l+1][C][C], ladder weights
  * (fc_ladder_layout), R2 [C][C], gamma2 [C], Wr1 [C][64], Wr2 [64][64],
  * wr3 [64] (fc_message_block_weight_floats floats).  conv: l_in = 0,
  * l_edge = l_out = l, flags 0; lad: l_a = l_prod = l, l_out = 0, equal

@@ -14,7 +14,8 @@ symmetry); complex-step derivatives of E reproduce the forces on the
 rattled cell.
 
 The full message-passing block at the end of this file adds the pages'
-radial network, the rank-wise path/channel map, residual updates, the
+channel map before the convolution, the radial network, the rank-wise
+path/channel map, residual updates, the
 equivariant RMS normalisation, scalar SiLU gates with their output map and
 a readout MLP (random weights); its pins are the same three properties,
 plus a two-atom walkthrough (one channel, ranks <= 3, ladder of order 2)
@@ -62,7 +63,9 @@ def energy(cspec, lspec, pos, rowptr, sender, shift, x, W, lws, n_bar: float):
 # The block as the pages describe it, with random weights, for one final block
 # (scalar senders in, scalars out).  Readings where the pages leave a step
 # open:
-#   a   = N_bar^{-1/2} conv(h0) with the radial network's weights (Eq. E1);
+#   hb  = Mpre h0 (the d x d channel map applied to the sender features of
+#         each rank before the convolution; scalars only here);
+#   a   = N_bar^{-1/2} conv(hb) with the radial network's weights (Eq. E1);
 #   m_l = M_l a_l (rank-wise map of the paths -- one per rank with scalar
 #         senders -- and channels), m_0 += R0 h0 (residual: a learned linear
 #         map of the block input);
@@ -78,7 +81,7 @@ BLOCK_HIDDEN = 64
 
 def block_weight_shapes(C: int, l_e: int, n_paths: int, lspec):
     """(name, shape) of the block's flat weights, in order."""
-    out = [("mlp", (8 * 64 + 64 * 64 + 64 * n_paths * C,)), ("M", (l_e + 1, C, C)), ("R0", (C, C)),
+    out = [("mlp", (8 * 64 + 64 * 64 + 64 * n_paths * C,)), ("Mpre", (C, C)), ("M", (l_e + 1, C, C)), ("R0", (C, C)),
            ("gamma1", (l_e + 1, C)), ("O", (l_e + 1, C, C))]
     out += [(f"ladder{i}", s[1]) for i, s in enumerate(lspec.weight_shapes())]
     out += [("R2", (C, C)), ("gamma2", (1, C)), ("Wr1", (C, BLOCK_HIDDEN)), ("Wr2", (BLOCK_HIDDEN, BLOCK_HIDDEN)),
@@ -111,7 +114,8 @@ def _block_forward(cspec, lspec, w, pos, rowptr, sender, shift, h0, n_bar, eps):
     mlp = w["mlp"]
     W1, W2, W3 = mlp[:512].reshape(8, 64), mlp[512:4608].reshape(64, 64), mlp[4608:].reshape(64, P * C)
     s = 1.0 / np.sqrt(n_bar)
-    a = s * radial.edge_conv_fwd_mlp(cspec, pos, rowptr, sender, h0, W1, W2, W3, shift=shift)
+    hb = np.einsum('uk,jk->uj', h0[:, 0, :], w["Mpre"])[:, None, :]
+    a = s * radial.edge_conv_fwd_mlp(cspec, pos, rowptr, sender, hb, W1, W2, W3, shift=shift)
     m = _rank_map(a, w["M"], l_e)
     m[:, 0, :] = m[:, 0, :] + np.einsum('uk,jk->uj', h0[:, 0, :], w["R0"])
     n, _ = norm.rms_norm_fwd(m, l_e, eps, w["gamma1"])
@@ -127,7 +131,8 @@ def _block_forward(cspec, lspec, w, pos, rowptr, sender, shift, h0, n_bar, eps):
     h1 = radial.silu(f[:, 0, :] @ w["Wr1"])
     h2 = radial.silu(h1 @ w["Wr2"])
     e_atom = h2 @ w["wr3"]
-    return dict(a=a, m=m, n=n, sg=sg, y=y, A=A, z=z, o=o, f=f, h1=h1, e_atom=e_atom, W=(W1, W2, W3), lws=lws)
+    return dict(hb=hb, a=a, m=m, n=n, sg=sg, y=y, A=A, z=z, o=o, f=f, h1=h1, e_atom=e_atom, W=(W1, W2, W3),
+                lws=lws)
 
 
 def block_energy(cspec, lspec, w, pos, rowptr, sender, shift, h0, n_bar, eps=1e-5):
@@ -162,5 +167,5 @@ def block_energy_forces(cspec, lspec, w, pos, rowptr, sender, shift, h0, n_bar, 
     ab = _rank_map_t(mb, w["M"], l_e)
     s = 1.0 / np.sqrt(n_bar)
     W1, W2, W3 = st["W"]
-    _, pb, _, _, _ = radial.edge_conv_vjp_mlp(cspec, pos, rowptr, sender, h0, W1, W2, W3, s * ab, shift=shift)
+    _, pb, _, _, _ = radial.edge_conv_vjp_mlp(cspec, pos, rowptr, sender, st["hb"], W1, W2, W3, s * ab, shift=shift)
     return float(np.sum(st["e_atom"])), st["e_atom"], -pb

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert fc.fc_abi_version() == 2
+    assert fc.fc_abi_version() == 3
     L = fc.lib()
     assert L.fc_status_string(0) == b"FC_OK"
     assert L.fc_status_string(3) == b"FC_ERR_WORKSPACE"
@@ -223,3 +223,18 @@ def test_vjp_vjp_w_argument_checks():
     st = L.fc_edge_conv_vjp_vjp_w(ctypes.byref(d), ctypes.byref(g), *([None] * 12), None, 0, None)
     assert st == fc.FC_ERR_INVALID_ARGUMENT
     assert b"no output requested" in L.fc_last_error_message()
+
+
+def test_vjp_vjp_instantiation_limits():
+    """The fused-weight VJP-of-VJP covers rank 5 (its passes compiled as
+    separate units); the explicit-weight one stops at rank 4 and says so
+    before any launch."""
+    import ctypes
+    L = fc.lib()
+    assert L.fc_edge_conv_workspace_bytes(ctypes.byref(fc.conv_desc(10, 20, 16, 5, 5, 5, 5.0)), 2) > 0
+    d = fc.conv_desc(10, 20, 16, 5, 5, 5, 5.0)
+    g = fc.Graph()
+    st = L.fc_edge_conv_vjp_vjp_w(ctypes.byref(d), ctypes.byref(g), None, None, None, None, None, None, None, None,
+                                  None, None, None, None, None, 0, None)
+    assert st == fc.FC_ERR_UNSUPPORTED
+    assert b"not instantiated" in L.fc_last_error_message()

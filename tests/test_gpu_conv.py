@@ -226,27 +226,31 @@ def test_rank5_256_channels():
     check_full((5, 5, 5), 6.0, d, 256)
 
 
-def test_rank5_microbenchmark_sampled_and_no_vjp_vjp():
+def test_rank5_microbenchmark_sampled():
     """Rank 5 (69 paths, 457 output rows per channel) at 1024 nodes x 64
-    neighbours x 64 channels, sampled nodes; the VJP-of-VJP is not
-    instantiated at rank 5 and says so."""
-    from cartesian_tensor_product_amd import flashcart as fc
+    neighbours x 64 channels (r_c = 35 A: every edge inside the cutoff),
+    sampled nodes: forward, VJP and the VJP-of-VJP with a position
+    cotangent, whose passes (g_hat, x_hat and the position terms) run as
+    separate launches at this rank."""
     ranks = (5, 5, 5)
-    spec = conv.ConvSpec(*ranks, 5.0)
-    d = inputs.edge_conv_inputs(2, 1024, 64, 20.0, 64, spec.n_in, spec.n_paths, spec.n_out)
-    gc = GpuConv(ranks, 5.0, d, 64)
+    spec = conv.ConvSpec(*ranks, 35.0)
+    d = inputs.edge_conv_inputs(2, 1024, 64, 20.0, 64, spec.n_in, spec.n_paths, spec.n_out, with_vpos=True)
+    gc = GpuConv(ranks, 35.0, d, 64)
     z = gc.fwd()
     xb, pb = gc.vjp()
+    gh, xh, ph, _ = gc.vjp_vjp(v_pos=d["v_pos"])
     torch.cuda.synchronize()
-    nodes = np.random.default_rng(97).choice(1024, size=6, replace=False)
+    nodes = np.random.default_rng(97).choice(1024, size=4, replace=False)
     edges = sample_edges(d["rowptr"], d["sender"], nodes)
     zo, xo, po, _ = oracle_all(spec, d, edges=edges)
     assert_close("z", z.cpu().numpy()[nodes], zo[nodes])
     assert_close("x_grad", xb.cpu().numpy()[nodes], xo[nodes])
     assert_close("pos_grad", pb.cpu().numpy()[nodes], po[nodes])
-    with pytest.raises(fc.FlashCartError) as ei:
-        gc.vjp_vjp(v_pos=np.zeros((1024, 3), np.float32))
-    assert ei.value.status == fc.FC_ERR_UNSUPPORTED
+    go, xho, pho, _ = conv.edge_conv_vjp_vjp(spec, f64(d["pos"]), d["rowptr"], d["sender"], f64(d["x"]),
+                                             f64(d["W"]), f64(d["g"]), v_pos=f64(d["v_pos"]), edges=edges)
+    assert_close("g_hat", gh.cpu().numpy()[nodes], go[nodes])
+    assert_close("x_hat", xh.cpu().numpy()[nodes], xho[nodes])
+    assert_close("pos_hat", ph.cpu().numpy()[nodes], pho[nodes])
 
 
 @pytest.mark.parametrize("ranks,seed", [((2, 2, 2), 1), ((3, 3, 3), 2)])

@@ -18,7 +18,7 @@ def oracle_vv(spec, d, v_x, v_pos, edges=None, g=None, v_W=None):
                                   edges=edges, want_W=True, v_W=f64(v_W))
 
 
-@pytest.mark.parametrize("ranks", [(1, 1, 1), (2, 2, 2), (3, 3, 3), (4, 4, 4), (0, 3, 3), (2, 3, 3)])
+@pytest.mark.parametrize("ranks", [(1, 1, 1), (2, 2, 2), (3, 3, 3), (4, 4, 4), (5, 5, 5), (0, 3, 3), (2, 3, 3)])
 @pytest.mark.parametrize("with_vx", [False, True])
 def test_vjp_vjp_small(ranks, with_vx):
     spec = conv.ConvSpec(*ranks, 6.0)
@@ -36,7 +36,7 @@ def test_vjp_vjp_small(ranks, with_vx):
     assert_close("radial_w_hat", Wh.cpu().numpy(), Wo)
 
 
-@pytest.mark.parametrize("ranks", [(1, 1, 1), (2, 2, 2), (3, 3, 3)])
+@pytest.mark.parametrize("ranks", [(1, 1, 1), (2, 2, 2), (3, 3, 3), (4, 4, 4)])
 @pytest.mark.parametrize("with_vx", [False, True])
 def test_vjp_vjp_all_parities(ranks, with_vx):
     """Every triangle-allowed path (odd J through the Levi-Civita reading)."""
@@ -54,16 +54,6 @@ def test_vjp_vjp_all_parities(ranks, with_vx):
     assert_close("x_hat", xh.cpu().numpy(), xo)
     assert_close("pos_hat", ph.cpu().numpy(), po)
     assert_close("radial_w_hat", Wh.cpu().numpy(), Wo)
-
-
-def test_vjp_vjp_all_parities_rank4_unsupported():
-    from cartesian_tensor_product_amd import flashcart as fc
-    spec = conv.ConvSpec(4, 4, 4, 6.0, all_parities=True)
-    d = inputs.edge_conv_inputs(7, 20, 6, 5.0, 8, spec.n_in, spec.n_paths, spec.n_out, with_vpos=True)
-    gc = GpuConv((4, 4, 4), 6.0, d, 8, flags=fc.FC_CONV_ALL_PARITIES)
-    with pytest.raises(fc.FlashCartError) as ei:
-        gc.vjp_vjp(v_pos=d["v_pos"])
-    assert ei.value.status == fc.FC_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("ranks", [(3, 3, 3), (4, 4, 4)])

@@ -167,3 +167,4 @@ def test_vjp_vjp_w_microbenchmark_sampled():
     torch.cuda.synchronize()
     for u, v in zip(again, out):
         assert torch.equal(u, v)
+

@@ -21,7 +21,7 @@ def block_setup(C=8, order=3, variant="reduced", rattle=0.05, ncell=3, l_e=3, se
             ls = lspec.weight_shapes()[int(name[6:])]
             entries.append((name, ls[1], ls[2], ls[3]))
         else:
-            entries.append((name, shape, "normal", shape[-1] if name in ("M", "R0", "O", "R2") else shape[0]))
+            entries.append((name, shape, "normal", shape[-1] if name in ("Mpre", "M", "R0", "O", "R2") else shape[0]))
     w = {k: v.astype(np.float64) for k, v in inputs.block_weights(seed, entries).items()}
     d = inputs.diamond_inputs(channels=C, r_cut=5.0, rattle=rattle, ncell=ncell, n_paths=cspec.n_paths)
     return cspec, lspec, w, d, entries

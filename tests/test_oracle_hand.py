@@ -257,7 +257,8 @@ def hand_block_energy(pos, h0, w, r_cut, eps):
     (C = 1, ranks <= 3, path-reduced ladder of order 2, l_out = 0), each step
     written out in the order of App. E "Model architecture":
 
-      a_u    = sum_{v} w_l(r_uv) h0_v T_l(r_hat_uv)         (Eq. E1, N_bar = 1)
+      hb_v   = Mpre h0_v                                     (channel map before the convolution)
+      a_u    = sum_{v} w_l(r_uv) hb_v T_l(r_hat_uv)         (Eq. E1, N_bar = 1)
       m_l    = M_l a_l,  m_0 += R0 h0_u                      (rank-wise map, residual)
       n      = gamma1 m / s,  s = sqrt(sum_l q_l / 4 + eps)  (RMS norm, q = (l,l)->0)
       y_0    = SiLU(n_0),  y_l = SiLU(n_0) n_l               (gates)
@@ -281,7 +282,7 @@ def hand_block_energy(pos, h0, w, r_cut, eps):
         h1 = [silu(sum(feat[i] * W1[i, j] for i in range(8))) for j in range(64)]
         h2 = [silu(sum(h1[i] * W2[i, j] for i in range(64))) for j in range(64)]
         wl = [sum(h2[i] * W3[i, l] for i in range(64)) for l in range(4)]
-        a = {l: wl[l] * h0[v] * t_dir(l, n_hat) for l in range(4)}
+        a = {l: wl[l] * (w["Mpre"][0, 0] * h0[v]) * t_dir(l, n_hat) for l in range(4)}
         m = {l: w["M"][l, 0, 0] * a[l] for l in range(4)}
         m[0] = m[0] + w["R0"][0, 0] * h0[u]
         s = math.sqrt(sum(self_invariant(l, m[l]) for l in range(4)) / 4.0 + eps)
@@ -303,7 +304,7 @@ def hand_block_energy(pos, h0, w, r_cut, eps):
     return E
 
 
-def _two_atom_block(seed=21):
+def _two_atom_block(seed=35):
     from oracle import conv
     C, r_cut, eps = 1, 5.0, 1e-5
     cspec = conv.ConvSpec(0, 3, 3, r_cut)
@@ -331,7 +332,8 @@ def _two_atom_block(seed=21):
 
 def test_block_two_atoms_hand_walkthrough():
     """The oracle's block energy equals the step-by-step scalar evaluation,
-    and its forces equal central differences of that scalar energy."""
+    and its forces equal fourth-order central differences of that scalar
+    energy."""
     cspec, lspec, w, pos, rowptr, sender, h0, r_cut, eps = _two_atom_block()
     x = h0.reshape(2, 1, 1)
     E, e_atom = model.block_energy(cspec, lspec, w, pos, rowptr, sender, None, x, 1.0, eps)
@@ -340,12 +342,15 @@ def test_block_two_atoms_hand_walkthrough():
     assert E == pytest.approx(want, rel=1e-12)
     E2, _, F = model.block_energy_forces(cspec, lspec, w, pos, rowptr, sender, None, x, 1.0, eps)
     assert E2 == pytest.approx(want, rel=1e-12)
-    h = 1e-5
+    # fourth-order central differences (truncation O(h^4))
+    h = 5e-4
     for i in range(2):
         for j in range(3):
-            pp, pm = pos.copy(), pos.copy()
-            pp[i, j] += h
-            pm[i, j] -= h
-            fd = -(hand_block_energy(pp, h0, w, r_cut, eps) - hand_block_energy(pm, h0, w, r_cut, eps)) / (2 * h)
-            assert F[i, j] == pytest.approx(fd, rel=1e-6, abs=1e-9 * np.abs(F).max())
-    assert np.abs(F).max() > 1e-3
+            e = {}
+            for k in (-2, -1, 1, 2):
+                pk = pos.copy()
+                pk[i, j] += k * h
+                e[k] = hand_block_energy(pk, h0, w, r_cut, eps)
+            fd = -(-e[2] + 8 * e[1] - 8 * e[-1] + e[-2]) / (12 * h)
+            assert F[i, j] == pytest.approx(fd, rel=1e-7, abs=1e-8 * np.abs(F).max())
+    assert np.abs(F).max() > 1e-2

@@ -73,10 +73,12 @@ def timed(fn, iters=10, warmup=2):
     return a.elapsed_time(b) / iters
 
 
-def message_blocks(dev, cases=((8, "path_reduced"), (8, "full"), (5, "path_reduced"))):
+def message_blocks(dev, cases=((8, "path_reduced"), (8, "full"), (5, "path_reduced"), (8, "path_reduced", "fused"))):
     """One full message-passing block (radial network, rank-wise map,
     residuals, RMS norms, SiLU gates, ladder of order 5, readout) for energy
-    and forces on diamond cells of ncell^3 conventional cells, random weights."""
+    and forces on diamond cells of ncell^3 conventional cells, random weights;
+    the radial network's output layer as the library chooses (materialised
+    for this convolution), or (a third case entry) "fused" / "materialized"."""
     import torch
 
     from cartesian_tensor_product_amd import flashcart as fc
@@ -85,11 +87,13 @@ def message_blocks(dev, cases=((8, "path_reduced"), (8, "full"), (5, "path_reduc
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     en = torch.zeros(1, dtype=torch.float64, device=dev)
     variants = {"path_reduced": fc.FC_LADDER_PATH_REDUCED, "full": fc.FC_LADDER_FULL}
-    for ncell, vname in cases:
+    for case in cases:
+        ncell, vname, radial = (*case, "default")[:3]
         var = variants[vname]
         dm = inp.diamond_inputs(channels=CHANNELS, r_cut=5.0, rattle=0.05, ncell=ncell, n_paths=4)
         Nm, Em = dm["pos"].shape[0], len(dm["sender"])
-        cdm = fc.conv_desc(Nm, Em, CHANNELS, 0, 3, 3, 5.0)
+        flags = {"default": 0, "fused": fc.FC_CONV_MLP_FUSE, "materialized": fc.FC_CONV_MLP_MATERIALIZE}[radial]
+        cdm = fc.conv_desc(Nm, Em, CHANNELS, 0, 3, 3, 5.0, flags=flags)
         ldm = fc.ladder_desc(Nm, CHANNELS, 3, 3, 0, 5, var)
         C2 = CHANNELS
         entries = [("mlp", (4, C2), "mlp", 1), ("Mpre", (C2, C2), "normal", C2), ("M", (4, C2, C2), "normal", C2),
@@ -108,10 +112,63 @@ def message_blocks(dev, cases=((8, "path_reduced"), (8, "full"), (5, "path_reduc
         am = (cdm, gm, t(dm["pos"]), t(dm["shift"]), t(dm["x"]), ldm, flat, 1.0 / np.sqrt(Em / Nm), 1e-5)
         msm = timed(lambda: fc.fc_message_block_energy_forces(*am, en, None, Fm, wsm), iters=5)
         mse = timed(lambda: fc.fc_message_block_energy_forces(*am, en, None, None, wsm), iters=5)
-        out[f"message_block_diamond_{Nm}_atoms_{vname}_order5"] = {
+        out[f"message_block_diamond_{Nm}_atoms_{vname}_order5" + ("" if radial == "default" else f"_radial_{radial}")] = {
             "energy_forces_ms": msm, "us_per_atom": msm * 1e3 / Nm, "energy_only_ms": mse, "edges": Em,
             "workspace_bytes": fc.fc_message_block_workspace_bytes(cdm, ldm)}
         del wsm, gm, flat
+    return out
+
+
+def radial_mlp_workload(dev):
+    """The pages' radial network (Chebyshev + envelope + bias-free SiLU MLP)
+    weighting the rank-2 micro convolution: its output layer fused into the
+    convolution's lanes against w stored by an MFMA GEMM and streamed."""
+    import torch
+
+    from cartesian_tensor_product_amd import flashcart as fc
+    from cartesian_tensor_product_amd import inputs
+    out = {}
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    desc = fc.conv_desc(N_NODES, N_NODES * K_NBR, CHANNELS, 2, 2, 2, R_CUT)
+    P, n_in, n_out = fc.fc_conv_layout(desc)
+    d = inputs.edge_conv_inputs(1, N_NODES, K_NBR, BOX, CHANNELS, n_in, P, n_out)
+    mlp = t(inputs.radial_mlp_weights(np.random.default_rng(51), P, CHANNELS))
+    graph = fc.DeviceGraph(d["rowptr"], d["sender"], N_NODES, device=dev)
+    pos, x, g = t(d["pos"]), t(d["x"]), t(d["g"])
+    E = N_NODES * K_NBR
+    w = torch.empty((E, P, CHANNELS), device=dev)
+    z = torch.empty((N_NODES, n_out, CHANNELS), device=dev)
+    xb, pb, mb = torch.empty_like(x), torch.empty((N_NODES, 3), device=dev), torch.empty_like(mlp)
+    from cartesian_tensor_product_amd.opcount import conv_fma_per_edge_channel
+    ops64 = conv_fma_per_edge_channel(2, 2, 2, n_basis=64)
+    r = {"w_bytes": E * P * CHANNELS * 4, "fused_fma_per_edge_channel": ops64}
+    for mode, flags in (("fused", fc.FC_CONV_MLP_FUSE), ("materialized", fc.FC_CONV_MLP_MATERIALIZE)):
+        dm = fc.conv_desc(N_NODES, E, CHANNELS, 2, 2, 2, R_CUT, flags=flags)
+        ws0 = fc.workspace(fc.fc_edge_conv_mlp_workspace_bytes(dm, 0), dev)
+        ws2 = fc.workspace(fc.fc_edge_conv_mlp_workspace_bytes(dm, 2), dev)
+        fms = timed(lambda: fc.fc_edge_conv_mlp_fwd(dm, graph, pos, None, x, mlp, z, ws0))
+        vms = timed(lambda: fc.fc_edge_conv_mlp_vjp(dm, graph, pos, None, x, mlp, g, xb, pb, None, ws2))
+        r[mode] = {"fwd_ms": fms, "vjp_x_pos_ms": vms,
+                   "fwd_plus_vjp_edge_channels_per_s": E * CHANNELS / ((fms + vms) * 1e-3),
+                   # fused: FMAs per edge-channel with the 64 hidden units as the basis
+                   "fwd_alu_frac": (2.0 * ops64["fwd"] * E * CHANNELS / (fms * 1e-3) / 1e12 / VALU_F32_PEAK_TFS
+                                    if mode == "fused" else None),
+                   "vjp_alu_frac": (2.0 * ops64["vjp"] * E * CHANNELS / (vms * 1e-3) / 1e12 / VALU_F32_PEAK_TFS
+                                    if mode == "fused" else None),
+                   "workspace_bytes_fwd": fc.fc_edge_conv_mlp_workspace_bytes(dm, 0),
+                   "workspace_bytes_vjp": fc.fc_edge_conv_mlp_workspace_bytes(dm, 2)}
+        del ws0, ws2
+    ws1 = fc.workspace(fc.fc_edge_conv_mlp_workspace_bytes(desc, 1), dev)
+    rms = timed(lambda: fc.fc_radial_mlp(desc, graph, pos, None, mlp, w, ws1))
+    r["radial_mlp_w_only_ms"] = rms
+    r["output_layer_tflops_lower_bound"] = 2.0 * E * 64 * P * CHANNELS / (rms * 1e-3) / 1e12
+    r["vjp_with_mlp_grad_ms"] = timed(lambda: fc.fc_edge_conv_mlp_vjp(desc, graph, pos, None, x, mlp, g, xb, pb, mb,
+                                                                      ws1))
+    r["fused_speedup_fwd_plus_vjp"] = ((r["materialized"]["fwd_ms"] + r["materialized"]["vjp_x_pos_ms"]) /
+                                      (r["fused"]["fwd_ms"] + r["fused"]["vjp_x_pos_ms"]))
+    r["default"] = "fused (forward and VJP at these ranks)"
+    out["conv_radial_mlp_rank2_1024n_128c_128nbr"] = r
+    del w, z, xb, pb, mb, ws1, mlp
     return out
 
 
@@ -192,31 +249,8 @@ def extras(dev, only_ladder=False, conv_ranks=(3, 4), only_conv=False):
         r["fwd_plus_vjp_edge_channels_per_s"] = E * CHANNELS / ((r["fwd_ms"] + r["vjp_ms"]) * 1e-3)
         out[f"conv_summed_rank{l}_1024n_128c_128nbr"] = r
         del z, xb, pb, ws
-    # the pages' radial network (Chebyshev + envelope + bias-free SiLU MLP,
-    # MFMA output layer) weighting the rank-2 micro convolution
     if not only_ladder and not only_conv:
-        desc = fc.conv_desc(N_NODES, N_NODES * K_NBR, CHANNELS, 2, 2, 2, R_CUT)
-        P, n_in, n_out = fc.fc_conv_layout(desc)
-        d = inputs.edge_conv_inputs(1, N_NODES, K_NBR, BOX, CHANNELS, n_in, P, n_out)
-        mlp = t(inputs.radial_mlp_weights(np.random.default_rng(51), P, CHANNELS))
-        graph = fc.DeviceGraph(d["rowptr"], d["sender"], N_NODES, device=dev)
-        pos, x, g = t(d["pos"]), t(d["x"]), t(d["g"])
-        E = N_NODES * K_NBR
-        w = torch.empty((E, P, CHANNELS), device=dev)
-        z = torch.empty((N_NODES, n_out, CHANNELS), device=dev)
-        xb, pb, mb = torch.empty_like(x), torch.empty((N_NODES, 3), device=dev), torch.empty_like(mlp)
-        ws0 = fc.workspace(fc.fc_edge_conv_mlp_workspace_bytes(desc, 0), dev)
-        ws1 = fc.workspace(fc.fc_edge_conv_mlp_workspace_bytes(desc, 1), dev)
-        rms = timed(lambda: fc.fc_radial_mlp(desc, graph, pos, None, mlp, w, ws0))
-        fms = timed(lambda: fc.fc_edge_conv_mlp_fwd(desc, graph, pos, None, x, mlp, z, ws0))
-        vms = timed(lambda: fc.fc_edge_conv_mlp_vjp(desc, graph, pos, None, x, mlp, g, xb, pb, None, ws1))
-        vwms = timed(lambda: fc.fc_edge_conv_mlp_vjp(desc, graph, pos, None, x, mlp, g, xb, pb, mb, ws1))
-        out["conv_radial_mlp_rank2_1024n_128c_128nbr"] = {
-            "radial_mlp_ms": rms, "fwd_ms": fms, "vjp_ms": vms, "vjp_with_mlp_grad_ms": vwms,
-            "output_layer_tflops_lower_bound": 2.0 * E * 64 * P * CHANNELS / (rms * 1e-3) / 1e12,
-            "w_bytes": E * P * CHANNELS * 4,
-            "fwd_plus_vjp_edge_channels_per_s": E * CHANNELS / ((fms + vms) * 1e-3)}
-        del w, z, xb, pb, mb, ws0, ws1, mlp
+        out.update(radial_mlp_workload(dev))
     # equivariant RMS normalisation of the ladder's node features (4096
     # nodes, 128 channels, ranks <= 3): forward, and VJP with both gradients
     if not only_conv:
@@ -516,6 +550,8 @@ def main():
                     help="only run the 4096-node ladder workloads (for counter runs) and print their timings")
     ap.add_argument("--conv-rank", type=int, default=0, metavar="L",
                     help="only run the 1024-node edge-conv workload at ranks <= L (3 or 4; for counter runs)")
+    ap.add_argument("--mlp-only", action="store_true",
+                    help="only run the radial-network convolution workload (fused and materialised)")
     ap.add_argument("--message-block-only", action="store_true",
                     help="only time the path-reduced message block on the 4096-atom diamond cell")
     ap.add_argument("--grid", action="store_true",
@@ -551,6 +587,9 @@ def main():
         return
     if args.message_block_only:
         print(json.dumps(message_blocks(dev, ((8, "path_reduced"),))), flush=True)
+        return
+    if args.mlp_only:
+        print(json.dumps(radial_mlp_workload(dev)), flush=True)
         return
     if args.conv_rank:
         print(json.dumps(extras(dev, conv_ranks=(args.conv_rank,), only_conv=True)), flush=True)
@@ -668,6 +707,12 @@ def main():
     }
     cbw = copy_bandwidth()
     out["breakdown"]["copy_GBs_measured"] = cbw
+    # the sender-sorted transpose of the graph (rebuilt whenever the
+    # neighbour list changes; outside the timed step), rewritten in place
+    # with the same values
+    out["breakdown"]["graph_transpose_ms"] = timed(
+        lambda: fc.fc_graph_transpose(N_NODES, E, graph.rowptr, graph.sender, graph.receiver, graph.t_rowptr,
+                                      graph.t_edge, graph._ws))
     if not args.no_extras:
         # explicit per-edge weights w [E, P, C] (the pages' own interface),
         # same workload; w drawn on the device from a seeded generator

@@ -57,14 +57,16 @@ _PART_WEIGHT = {"vx": 400, "vs": 160, "vr": 40, "vg": 40}
 
 def _weight(src: str) -> int:
     """Rough compile cost, so that the largest units start first: the ranks
-    of a convolution unit conv_inst_<l_in><l_edge><l_out key>[w | vr | vg |
-    vs | vx]."""
+    of a convolution unit conv_inst_<l_in><l_edge><l_out key>[w | m | vr |
+    vg | vs | vx]."""
     name = os.path.basename(src)
     if name.startswith("conv_inst_"):
         stem = name[len("conv_inst_"):-len(".hip")]
         if stem[-2:] in _PART_WEIGHT:
             return _PART_WEIGHT[stem[-2:]]
         xw = stem.endswith("w")   # explicit-weight VJP-of-VJP unit
+        if stem.endswith("m"):    # fused radial network: forward and VJP
+            return 5 * (int(stem[0]) + int(stem[1]) + int(stem[2:-1]))
         digits = stem.rstrip("w")
         a, b, key = int(digits[0]), int(digits[1]), int(digits[2:])
         return (a + b + key % 8 + (4 if (key // 8) % 2 else 0)) * (8 if xw else 10)

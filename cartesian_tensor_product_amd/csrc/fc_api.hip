@@ -87,9 +87,12 @@ fc_status check_desc(const fc_conv_desc* d) {
   if (!(d->r_cut > 0.f) || !std::isfinite(d->r_cut))
     return fail(FC_ERR_INVALID_ARGUMENT, "r_cut must be positive and finite");
   if (d->n_basis != fc::kNB) return fail(FC_ERR_UNSUPPORTED, "n_basis must be 8 (got %d)", d->n_basis);
-  if ((d->flags & ~uint32_t(FC_CONV_ALL_PARITIES | FC_CONV_SUM_PATHS)) != 0)
-    return fail(FC_ERR_UNSUPPORTED, "unknown flags 0x%x (FC_CONV_ALL_PARITIES and FC_CONV_SUM_PATHS are defined)",
-                d->flags);
+  if ((d->flags & ~uint32_t(FC_CONV_ALL_PARITIES | FC_CONV_SUM_PATHS | FC_CONV_MLP_MATERIALIZE | FC_CONV_MLP_FUSE)) != 0)
+    return fail(FC_ERR_UNSUPPORTED,
+                "unknown flags 0x%x (FC_CONV_ALL_PARITIES, FC_CONV_SUM_PATHS, FC_CONV_MLP_MATERIALIZE and "
+                "FC_CONV_MLP_FUSE are defined)", d->flags);
+  if ((d->flags & FC_CONV_MLP_MATERIALIZE) && (d->flags & FC_CONV_MLP_FUSE))
+    return fail(FC_ERR_INVALID_ARGUMENT, "FC_CONV_MLP_MATERIALIZE and FC_CONV_MLP_FUSE exclude each other");
   int P = 0;
   for (int L = 0; L <= d->l_out; ++L) P += conv_paths_L(d, L);
   if (P == 0) return fail(FC_ERR_INVALID_ARGUMENT, "no admissible path for these ranks");
@@ -133,18 +136,40 @@ fc::ConvArgs make_args(const fc_conv_desc* d, const fc_graph* g, const float* po
 }
 
 
-// Workspace of the convolution weighted by the radial network: (op 1) the
-// convolution's VJP workspace, then h2 [64][E], w [E][P C], (op 1) w_bar
-// [E][P C], the per-edge position terms [E][3] and the radial VJP scratch.
+// Where the radial network's output layer runs fused in the convolution's
+// lanes (w = h2 W3 never stored): the forward wherever the rank set is
+// instantiated for it; the VJP where the rank set's own VJP work makes it
+// the faster choice, or with FC_CONV_MLP_FUSE; neither with
+// FC_CONV_MLP_MATERIALIZE.
+bool mlp_fuse_fwd(const fc_conv_desc* d) {
+  return !(d->flags & FC_CONV_MLP_MATERIALIZE) && fc::conv_mlp_supported(d->l_in, d->l_edge, lout_key(d));
+}
+bool mlp_fuse_vjp(const fc_conv_desc* d) {
+  return mlp_fuse_fwd(d) &&
+         ((d->flags & FC_CONV_MLP_FUSE) || fc::conv_mlp_vjp_fused(d->l_in, d->l_edge, lout_key(d)));
+}
+
+// Workspace of the convolution weighted by the radial network, for op 0
+// (forward), 1 (VJP, any outputs) or 2 (VJP without the network's weight
+// gradient; a forward on this layout follows the VJP's choice, so that the
+// VJP can reuse what it leaves).  Fused (op 0 where mlp_fuse_fwd, op 2
+// where mlp_fuse_vjp): (op 2) the
+// convolution's VJP workspace, then the per-edge hidden rows hh [E][2][64].
+// Materialised: (ops 1, 2) the VJP workspace, then h2 [64][E], w [E][P C],
+// (ops 1, 2) w_bar [E][P C], the per-edge position terms [E][3] and the
+// radial VJP scratch.
 struct MlpWorkspace {
+  bool fused;
   size_t conv_bytes;
-  float *h2t, *w, *wbar, *q, *scratch;
+  float *hh, *h2t, *w, *wbar, *q, *scratch;
   size_t bytes;
   MlpWorkspace(const fc_conv_desc* d, int op, void* base) {
     int P, nin, nout;
     layout(d, &P, &nin, &nout);
     const size_t E = d->n_edges, PC = (size_t)P * d->channels;
-    conv_bytes = op == 1 ? fc::VjpWorkspace(d->n_nodes, d->n_edges, d->channels, nin, P, false, nullptr).bytes : 0;
+    fused = op == 0 ? mlp_fuse_fwd(d) : op == 2 && mlp_fuse_vjp(d);
+    const bool vjp = op != 0;
+    conv_bytes = vjp ? fc::VjpWorkspace(d->n_nodes, d->n_edges, d->channels, nin, P, false, nullptr).bytes : 0;
     char* p = static_cast<char*>(base);
     size_t off = conv_bytes;
     auto take = [&](size_t floats) {
@@ -152,14 +177,24 @@ struct MlpWorkspace {
       off += fc::align256(floats * sizeof(float));
       return r;
     };
-    h2t = take((size_t)fc::radial_ld(d->n_edges) * fc::kRadHidden);
-    w = take(E * PC);
-    wbar = op == 1 ? take(E * PC) : nullptr;
-    q = op == 1 ? take(E * 3) : nullptr;
-    scratch = op == 1 ? take(fc::radial_vjp_scratch_floats(d->n_edges, P, d->channels)) : nullptr;
+    hh = h2t = w = wbar = q = scratch = nullptr;
+    if (fused) {
+      // (at least h2 [64][E] of fc_radial_mlp, which takes the op 0 bytes)
+      hh = take(std::max(E * fc::kRadRow, (size_t)fc::radial_ld(d->n_edges) * fc::kRadHidden));
+    } else {
+      h2t = take((size_t)fc::radial_ld(d->n_edges) * fc::kRadHidden);
+      w = take(E * PC);
+      wbar = vjp ? take(E * PC) : nullptr;
+      q = vjp ? take(E * 3) : nullptr;
+      scratch = vjp ? take(fc::radial_vjp_scratch_floats(d->n_edges, P, d->channels)) : nullptr;
+    }
     bytes = off;
   }
 };
+
+const float* mlp_w3(const float* mlp_w) {
+  return mlp_w + (size_t)fc::kRadFeat * fc::kRadHidden + (size_t)fc::kRadHidden * fc::kRadHidden;
+}
 
 fc::RadialArgs radial_args(const fc_conv_desc* d, const fc_graph* g, const float* pos, const float* shift,
                            const float* mlp_w) {
@@ -170,11 +205,21 @@ fc::RadialArgs radial_args(const fc_conv_desc* d, const fc_graph* g, const float
 }
 
 // The convolution weighted by the radial network, forward and VJP, on a
-// workspace laid out by MlpWorkspace; with have_w the VJP reuses h2 and w
-// left in it by a forward on the same workspace (op 1 layout).
+// workspace laid out by MlpWorkspace; with have_w the VJP reuses the hidden
+// rows (fused) or h2 and w (materialised) left in it by a forward on the
+// same workspace.  The fused VJP gives no network weight gradient (the
+// caller asks for the op 1 layout, which is materialised, to get one).
 void mlp_conv_forward(const fc_conv_desc* d, const fc_graph* g, const float* pos, const float* shift, const float* x,
                       const float* mlp_w, float* z, const MlpWorkspace& ws, hipStream_t stream) {
   const fc::RadialArgs ra = radial_args(d, g, pos, shift, mlp_w);
+  if (ws.fused) {
+    fc::launch_radial_hidden_rows(ra, ws.hh, stream);
+    fc::ConvArgs a = make_args(d, g, pos, shift, x, mlp_w3(mlp_w));
+    a.mlp_h = ws.hh;
+    a.z = z;
+    fc::conv_mlp_dispatch(0, d->l_in, d->l_edge, lout_key(d), a, stream);
+    return;
+  }
   fc::launch_radial_hidden(ra, ws.h2t, stream);
   fc::launch_radial_out(ra, ws.h2t, ws.w, stream);
   fc::ConvArgs a = make_args(d, g, pos, shift, x, nullptr);
@@ -187,6 +232,17 @@ void mlp_conv_vjp(const fc_conv_desc* d, const fc_graph* g, const float* pos, co
                   const float* mlp_w, const float* g_z, float* x_grad, float* pos_grad, float* mlp_w_grad,
                   const MlpWorkspace& ws, void* conv_ws, bool have_w, hipStream_t stream) {
   const fc::RadialArgs ra = radial_args(d, g, pos, shift, mlp_w);
+  if (ws.fused) {
+    if (!have_w) fc::launch_radial_hidden_rows(ra, ws.hh, stream);
+    fc::ConvArgs a = make_args(d, g, pos, shift, x, mlp_w3(mlp_w));
+    a.mlp_h = ws.hh;
+    a.g = g_z;
+    a.x_bar = x_grad;
+    a.pos_bar = pos_grad;
+    a.rbar = static_cast<float*>(conv_ws);
+    fc::conv_mlp_dispatch(1, d->l_in, d->l_edge, lout_key(d), a, stream);
+    return;
+  }
   const bool radial = pos_grad || mlp_w_grad;
   if (!have_w) {
     fc::launch_radial_hidden(ra, ws.h2t, stream);
@@ -761,8 +817,10 @@ fc_status msg_layout(const fc_conv_desc* cd, const fc_ladder_desc* ld, MsgLayout
   if (fc_status s = check_desc(cd)) return s;
   fc::LadderPlan p;
   if (fc_status s = ladder_plan(ld, &p)) return s;
-  if (cd->l_in != 0 || cd->l_edge != cd->l_out || cd->flags != 0)
-    return fail(FC_ERR_UNSUPPORTED, "message block: the convolution needs scalar senders, l_edge == l_out, flags 0");
+  if (cd->l_in != 0 || cd->l_edge != cd->l_out ||
+      (cd->flags & ~uint32_t(FC_CONV_MLP_MATERIALIZE | FC_CONV_MLP_FUSE)) != 0)
+    return fail(FC_ERR_UNSUPPORTED,
+                "message block: the convolution needs scalar senders, l_edge == l_out, natural parity, paths apart");
   if (ld->l_a != cd->l_out || ld->l_out != 0 || ld->channels != cd->channels || ld->n_nodes != cd->n_nodes)
     return fail(FC_ERR_INVALID_ARGUMENT,
                 "message block: ladder l_a must equal the conv l_out, ladder l_out 0, equal channels and nodes");
@@ -793,7 +851,7 @@ fc_status msg_layout(const fc_conv_desc* cd, const fc_ladder_desc* ld, MsgLayout
   L->ea = o;    o += al(N);
   L->saved = o; o += al(p.saved_floats());
   L->lws = o;   o += al(std::max(p.fwd_ws_floats(), p.vjp_ws_floats()));
-  L->cws_bytes = fc_edge_conv_mlp_workspace_bytes(cd, 1);   // the VJP reuses the forward's h2 and w in it
+  L->cws_bytes = fc_edge_conv_mlp_workspace_bytes(cd, 2);   // the VJP reuses the forward's rows in it
   L->cws = o;   o += (L->cws_bytes + 255) / 256 * 256;
   L->parts = o; o += (size_t)fc::block_energy_parts(cd->n_nodes) * 8;
   L->total = o;
@@ -912,7 +970,7 @@ size_t fc_radial_mlp_weight_floats(const fc_conv_desc* d) {
 }
 
 size_t fc_edge_conv_mlp_workspace_bytes(const fc_conv_desc* d, int32_t op) {
-  if (check_desc(d) != FC_OK || (op != 0 && op != 1)) return 0;
+  if (check_desc(d) != FC_OK || op < 0 || op > 2) return 0;
   return MlpWorkspace(d, op, nullptr).bytes;
 }
 
@@ -925,12 +983,14 @@ fc_status fc_radial_mlp(const fc_conv_desc* d, const fc_graph* g, const float* p
     return fail(FC_ERR_INVALID_ARGUMENT, "radial MLP: NULL pos, mlp_w or w");
   if (misaligned(pos, 4) || misaligned(shift, 4) || misaligned(mlp_w, 4) || misaligned(w, 4))
     return fail(FC_ERR_INVALID_ARGUMENT, "radial MLP: arrays must be 4-byte aligned");
-  const MlpWorkspace ws(d, 0, workspace);
-  if (!workspace || workspace_bytes < ws.bytes)
-    return fail(FC_ERR_WORKSPACE, "radial MLP needs %zu workspace bytes", ws.bytes);
+  // h2 [64][E] at the start of the workspace (within the op 0 size, fused or not)
+  const size_t need = fc::align256((size_t)fc::radial_ld(d->n_edges) * fc::kRadHidden * sizeof(float));
+  if (!workspace || workspace_bytes < need)
+    return fail(FC_ERR_WORKSPACE, "radial MLP needs %zu workspace bytes", need);
+  float* h2t = static_cast<float*>(workspace);
   const fc::RadialArgs ra = radial_args(d, g, pos, shift, mlp_w);
-  fc::launch_radial_hidden(ra, ws.h2t, stream);
-  fc::launch_radial_out(ra, ws.h2t, w, stream);
+  fc::launch_radial_hidden(ra, h2t, stream);
+  fc::launch_radial_out(ra, h2t, w, stream);
   return check_launch("radial MLP");
 }
 
@@ -962,9 +1022,11 @@ fc_status fc_edge_conv_mlp_vjp(const fc_conv_desc* d, const fc_graph* g, const f
   if (misaligned(pos, 4) || misaligned(shift, 4) || misaligned(x, 4) || misaligned(mlp_w, 4) || misaligned(g_z, 4) ||
       misaligned(x_grad, 4) || misaligned(pos_grad, 4) || misaligned(mlp_w_grad, 4))
     return fail(FC_ERR_INVALID_ARGUMENT, "MLP-weighted VJP: arrays must be 4-byte aligned");
-  const MlpWorkspace ws(d, 1, workspace);
+  const int op = mlp_w_grad ? 1 : 2;
+  const MlpWorkspace ws(d, op, workspace);
   if (!workspace || workspace_bytes < ws.bytes)
-    return fail(FC_ERR_WORKSPACE, "MLP-weighted VJP needs %zu workspace bytes", ws.bytes);
+    return fail(FC_ERR_WORKSPACE, "MLP-weighted VJP needs %zu workspace bytes (fc_edge_conv_mlp_workspace_bytes op %d)",
+                ws.bytes, op);
   mlp_conv_vjp(d, g, pos, shift, x, mlp_w, g_z, x_grad, pos_grad, mlp_w_grad, ws, workspace, false, stream);
   return check_launch("MLP-weighted edge conv VJP");
 }
@@ -1013,7 +1075,7 @@ fc_status fc_message_block_energy_forces(const fc_conv_desc* cd, const fc_graph*
 
   if (cd->n_edges > 0 && (!g->rowptr || !g->sender || !g->receiver))
     return fail(FC_ERR_INVALID_ARGUMENT, "message block needs graph rowptr, sender and receiver");
-  const MlpWorkspace mws(cd, 1, wb + L.cws);
+  const MlpWorkspace mws(cd, 2, wb + L.cws);
 
   // ---- forward
   {  // hb = Mpre h0: the channel map of the sender features before the convolution

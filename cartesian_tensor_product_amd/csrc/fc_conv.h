@@ -27,6 +27,10 @@ struct ConvArgs {
   // VJP-of-VJP with explicit weights: the weight cotangent [E][P][C]
   // (nullable); w_hat reuses w_edge_bar
   const float* v_w_edge;
+  // radial network fused into the lanes (conv_mlp_dispatch): the second
+  // hidden layer and its r-derivative per edge, [E][2][64]; W is then W3
+  // [64][P][C]
+  const float* mlp_h;
 };
 
 // l_out is the output-rank key: l_out + kAllParities keeps every
@@ -96,5 +100,14 @@ bool conv_dispatch(int op, int l_in, int l_edge, int l_out, const ConvArgs& args
 // conv_vv_supported)
 bool conv_vv_w_dispatch(int l_in, int l_edge, int l_out, const ConvArgs& args, hipStream_t stream);
 bool conv_vv_w_supported(int l_in, int l_edge, int l_out);
+// The convolution weighted by the radial network with its output layer
+// fused into the lanes (args.W = W3, args.mlp_h): op 0 forward (z), op 1
+// VJP (x_bar and/or pos_bar, the latter through w(r) as well); false when
+// not instantiated for these ranks.
+bool conv_mlp_dispatch(int op, int l_in, int l_edge, int l_out, const ConvArgs& args, hipStream_t stream);
+bool conv_mlp_supported(int l_in, int l_edge, int l_out);
+// whether the fused VJP is the default for these ranks (the convolution's
+// own VJP work is at least a third of the 64 P FMAs that form w)
+bool conv_mlp_vjp_fused(int l_in, int l_edge, int l_out);
 
 }  // namespace fc

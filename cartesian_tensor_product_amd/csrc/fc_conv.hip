@@ -122,4 +122,33 @@ bool conv_vv_w_dispatch(int l_in, int l_edge, int l_out, const ConvArgs& args, h
   }
 }
 
+#define FC_CONV_MLP_DECL(A, B, Cc) void conv_run_mlp_##A##B##Cc(int op, const ConvArgs& args, hipStream_t stream);
+FC_CONV_MLP_CONFIGS(FC_CONV_MLP_DECL)
+
+#define FC_CONV_MLP_CASE(A, B, Cc)            \
+  case (A) * 1024 + (B) * 32 + (Cc):           \
+    conv_run_mlp_##A##B##Cc(op, args, stream); \
+    return true;
+
+bool conv_mlp_dispatch(int op, int l_in, int l_edge, int l_out, const ConvArgs& args, hipStream_t stream) {
+  switch (l_in * 1024 + l_edge * 32 + l_out) {
+    FC_CONV_MLP_CONFIGS(FC_CONV_MLP_CASE)
+    default: return false;
+  }
+}
+
+bool conv_mlp_supported(int l_in, int l_edge, int l_out) {
+  switch (l_in * 1024 + l_edge * 32 + l_out) {
+    FC_CONV_MLP_CONFIGS(FC_CONV_SUPPORTED)
+    default: return false;
+  }
+}
+
+bool conv_mlp_vjp_fused(int l_in, int l_edge, int l_out) {
+  switch (l_in * 1024 + l_edge * 32 + l_out) {
+    FC_CONV_MLP_VJP_FUSED_CONFIGS(FC_CONV_SUPPORTED)
+    default: return false;
+  }
+}
+
 }  // namespace fc

@@ -13,6 +13,7 @@
 #pragma once
 
 #include "fc_conv.h"
+#include "fc_radial.h"
 
 namespace fc {
 
@@ -34,7 +35,18 @@ __host__ __device__ constexpr bool term_has_b1(int tb, int te, int b) {
     if (tab::kTerms[t].b1 == b) return true;
   return false;
 }
-__host__ __device__ constexpr int vjp_budget(int nin, int ne) { return 200 - 2 * nin - ne; }
+// Register budget of one VJP path group (2L+1 cotangent rows plus the radial
+// weights of each path).  With natural-parity, path-separated outputs and
+// senders of rank 3 or 4 it is sized so that the sender kernel stays within
+// the 256 registers of two waves per SIMD: one wave per SIMD had cost
+// 1.67 / 5.44 ms where two take 1.15 / 4.22 ms at the micro workload (ranks
+// 3 / 4), despite more sweeps per sender (the formula is fitted there).  The
+// same budgets made the every-parity and summed-path kernels slower (more
+// paths per rank, more repeated sums per sweep); they and the other ranks
+// keep the wider groups.
+__host__ __device__ constexpr int vjp_budget(int nin, int ne, bool natural_separate) {
+  return natural_separate && nin >= 16 && nin <= 25 && ne <= 25 ? 190 - 3 * nin - 2 * ne : 200 - 2 * nin - ne;
+}
 // Channels of one VJP block: up to 4 waves (C <= 256).
 inline constexpr int kMaxVjpWaves = 4;
 // LDS one workgroup may hold on gfx950.
@@ -92,6 +104,98 @@ struct EdgeProducts {
   }
 };
 
+// ------------------------------------------------ fused radial network ----
+// With the radial network's output layer fused into the convolution (MLP),
+// w[e, p, k] = sum_h h2[e, h] W3[h, p, k] (and, for the VJP, dw/dr from the
+// r-derivatives of h2) is formed per lane (channel k) for a batch of B
+// consecutive edges of a chunk: the edges' 64 activations are staged in LDS
+// (rows of kMlpRow floats, or kMlpRow2 with the derivatives) and read as
+// broadcasts, the W3 entries of the lane's channel are read from the cache
+// once per batch, and w never leaves the registers.
+inline constexpr int kMlpRow = kRadHidden + 4;        // padded: the lanes' row stores spread over the banks
+inline constexpr int kMlpRow2 = 2 * kRadHidden + 4;   // h2, then dh2/dr
+// Edges per batch for a path group of np paths: each W3 entry read serves
+// one FMA per edge of the batch (two in the VJP: w and dw/dr), so the batch
+// is as large as the registers allow: the forward holds 16 np weights (np
+// <= 6) or 8 np; the VJP holds 2 np per edge within 66 registers (3 edges
+// at the 11 paths of ranks <= 2, whose four would take the kernel past the
+// 256 registers of two waves per SIMD; 8 for four paths).
+#ifndef FC_MLP_VJP_CAP
+#define FC_MLP_VJP_CAP 8
+#endif
+#ifndef FC_MLP_FWD_REGS
+#define FC_MLP_FWD_REGS 96
+#endif
+__host__ __device__ constexpr int mlp_batch_fwd(int np) {
+  int b = 16;
+  while (b > 1 && b * np > FC_MLP_FWD_REGS) b /= 2;
+  return b;
+}
+__host__ __device__ constexpr int mlp_batch_vjp(int np) {
+  return np >= 33 ? 1 : (33 / np > FC_MLP_VJP_CAP ? FC_MLP_VJP_CAP : 33 / np);
+}
+inline constexpr int kMlpBatchVjpMax = 8;
+static_assert(FC_MLP_VJP_CAP <= kMlpBatchVjpMax, "LDS rows past the chunk");
+// edges per chunk of the fused forward: 32 keep its LDS (records and
+// activation rows) low enough for two one-wave blocks per SIMD
+inline constexpr int kMlpChunkFwd = 32;
+static_assert(kMlpChunkFwd % 16 == 0, "forward batches tile the chunk");
+
+// w[b NP + i] = sum_h hs[b HR + h] w3[h ldw + i C] for b < B (and, with D,
+// dw from the derivative rows at hs + b HR + kRadHidden).  HS hidden units
+// (2 or 4) per step; the W3 entries of step h + HS are requested before the
+// products of step h, so that their latency overlaps the FMAs (the last
+// step requests its own entries again, unused).
+template <int B, int NP, bool D, int HR, int HS>
+__device__ __forceinline__ void mlp_batch_weights(const float* hs, const float* __restrict__ w3, size_t ldw, int C,
+                                                  float* w, float* dw) {
+  static_assert(HS == 2 || HS == 4, "2 or 4 hidden units per step");
+  using V = typename std::conditional<HS == 4, float4, float2>::type;
+  static_for<B * NP>([&](auto i) {
+    w[i] = 0.f;
+    if constexpr (D) dw[i] = 0.f;
+  });
+  auto fetch = [&](float* dst, int h) {
+    static_for<HS * NP>([&](auto i) {
+      constexpr int q = i / NP, pi = i % NP;
+      dst[i] = w3[(size_t)(h + q) * ldw + (size_t)pi * C];
+    });
+  };
+  float wv[HS * NP];
+  fetch(wv, 0);
+#pragma unroll 2
+  for (int h = 0; h < kRadHidden; h += HS) {
+    float wn[HS * NP];
+    fetch(wn, min(h + HS, kRadHidden - HS));
+    auto madd = [&](const V& v, float* acc, auto pi, int o) {
+      acc[o] = fmaf(v.x, wv[pi], acc[o]);
+      acc[o] = fmaf(v.y, wv[NP + pi], acc[o]);
+      if constexpr (HS == 4) {
+        acc[o] = fmaf(v.z, wv[2 * NP + pi], acc[o]);
+        acc[o] = fmaf(v.w, wv[3 * NP + pi], acc[o]);
+      }
+    };
+    static_for<B>([&](auto b) {
+      constexpr int bb = b;
+      const V hv = *reinterpret_cast<const V*>(hs + bb * HR + h);
+      static_for<NP>([&](auto pi) { madd(hv, w, pi, bb * NP + pi); });
+      if constexpr (D) {
+        const V dv = *reinterpret_cast<const V*>(hs + bb * HR + kRadHidden + h);
+        static_for<NP>([&](auto pi) { madd(dv, dw, pi, bb * NP + pi); });
+      }
+    });
+    static_for<HS * NP>([&](auto i) { wv[i] = wn[i]; });
+  }
+}
+
+// Copies n floats (a multiple of 4) from global src to LDS dst.
+template <int NF>
+__device__ __forceinline__ void copy_row(const float* __restrict__ src, float* dst) {
+  static_for<NF / 4>([&](auto q) {
+    reinterpret_cast<float4*>(dst)[q] = reinterpret_cast<const float4*>(src)[q];
+  });
+}
+
 // Receiver-sorted edge record: direction-tensor entries (or their coefficient
 // products), the eight radial values and the sender id of edge e into u.
 // With explicit per-edge weights (XW) the first radial slot holds 1 for an
@@ -129,17 +233,23 @@ __device__ __forceinline__ void recv_edge_record(int e, const int* __restrict__ 
 // One launch per path group G: z rows of G's paths for node u and 64 channels.
 // XW: the weights are given per edge, W = w [E][P][C] (receiver-sorted edge
 // order), instead of being formed from the radial basis and W [8][P][C].
-template <int LIN, int LEDGE, int LOUT, int P0, int P1, bool XW>
+// MLP: W = W3 [64][P][C] and hh [E][2][64] the second hidden layer of the
+// radial network per edge (and its r-derivative, unused here); w = h2 W3 is
+// formed in the lanes.
+template <int LIN, int LEDGE, int LOUT, int P0, int P1, bool XW, bool MLP = false>
 __global__ __launch_bounds__(kWave) void conv_fwd_kernel(
     int N, int C, const int* __restrict__ rowptr, const int* __restrict__ sender,
     const float* __restrict__ pos, const float* __restrict__ shift,
-    const float* __restrict__ x, const float* __restrict__ W, float* __restrict__ z, float rc) {
+    const float* __restrict__ x, const float* __restrict__ W, float* __restrict__ z, float rc,
+    const float* __restrict__ hh) {
   using Cfg = ConvCfg<LIN, LEDGE, LOUT>;
   using G = PathGroup<Cfg, P0, P1>;
   using EP = EdgeProducts<LIN, LEDGE, LOUT>;
   constexpr int NIN = Cfg::NIN, NE = Cfg::NE, P = Cfg::P, NOUT = Cfg::NOUT;
   constexpr int REC = EP::NY + kNB + 1;
-  __shared__ float geo[kWave * REC];
+  constexpr int MB = mlp_batch_fwd(G::NP), CHF = MLP ? kMlpChunkFwd : kWave;
+  __shared__ float geo[CHF * REC];
+  __shared__ __align__(16) float hsh[MLP ? CHF * kMlpRow : 4];
 
   const int u = xcd_node(blockIdx.x, N);
   const int lane = threadIdx.x;
@@ -148,8 +258,8 @@ __global__ __launch_bounds__(kWave) void conv_fwd_kernel(
   const int kk = act ? k : 0;
   const int voff = kk * 4;
 
-  float Wr[XW ? 1 : kNB * G::NP];
-  if constexpr (!XW) {
+  float Wr[XW || MLP ? 1 : kNB * G::NP];
+  if constexpr (!XW && !MLP) {
     static_for<kNB * G::NP>([&](auto i) {
       constexpr int b = i / G::NP, p = i % G::NP;
       Wr[i] = W[(size_t)(b * P + P0 + p) * C + kk];
@@ -160,10 +270,13 @@ __global__ __launch_bounds__(kWave) void conv_fwd_kernel(
 
   const int e0 = rowptr[u], e1 = rowptr[u + 1];
   const float pux = pos[3 * u], puy = pos[3 * u + 1], puz = pos[3 * u + 2];
-  for (int base = e0; base < e1; base += kWave) {
-    const int cnt = min(kWave, e1 - base);
-    if (lane < cnt)
-      recv_edge_record<LIN, LEDGE, LOUT, XW>(base + lane, sender, pos, shift, pux, puy, puz, rc, geo + lane * REC);
+  for (int base = e0; base < e1; base += CHF) {
+    const int cnt = min(CHF, e1 - base);
+    if (lane < cnt) {
+      recv_edge_record<LIN, LEDGE, LOUT, XW || MLP>(base + lane, sender, pos, shift, pux, puy, puz, rc,
+                                                     geo + lane * REC);
+      if constexpr (MLP) copy_row<kRadHidden>(hh + (size_t)(base + lane) * kRadRow, hsh + lane * kMlpRow);
+    }
     __syncthreads();
     // XW: the weights of edge j + 1 are requested after the gather of edge
     // j, so that waiting for the gather leaves the prefetch in flight
@@ -174,7 +287,8 @@ __global__ __launch_bounds__(kWave) void conv_fwd_kernel(
         static_for<G::NP>([&](auto pi) { wn[pi] = wrow[(size_t)(P0 + pi) * C]; });
       }
     }
-    for (int j = 0; j < cnt; ++j) {
+    // one edge; wm(pi) gives the fused network's weight of path P0 + pi
+    auto edge = [&](int j, auto wm) {
       const float* rec = geo + j * REC;
       const int s = uniform_int(__float_as_int(rec[EP::NY + kNB]));
       const auto xs = node_rsrc(x, s, NIN * C);
@@ -196,6 +310,8 @@ __global__ __launch_bounds__(kWave) void conv_fwd_kernel(
         float w = 0.f;
         if constexpr (XW) {
           w = we[pi];
+        } else if constexpr (MLP) {
+          w = wm(pi);
         } else {
           static_for<kNB>([&](auto b) {
             constexpr int bb = b;
@@ -227,6 +343,19 @@ __global__ __launch_bounds__(kWave) void conv_fwd_kernel(
           });
         }
       });
+    };
+    if constexpr (MLP) {
+      for (int jb = 0; jb < cnt; jb += MB) {
+        float wb[MB * G::NP];
+        mlp_batch_weights<MB, G::NP, false, kMlpRow, 2>(hsh + jb * kMlpRow, W + (size_t)P0 * C + kk, (size_t)P * C, C,
+                                                    wb, nullptr);
+        static_for<MB>([&](auto bi) {
+          constexpr int b = bi;
+          if (jb + b < cnt) edge(jb + b, [&](auto pi) { return wb[b * G::NP + pi]; });
+        });
+      }
+    } else {
+      for (int j = 0; j < cnt; ++j) edge(j, [](auto) { return 0.f; });
     }
     __syncthreads();
   }
@@ -253,10 +382,23 @@ void launch_fwd(const ConvArgs& a, hipStream_t st) {
     constexpr int p0 = GS::start[gi], p1 = GS::start[gi + 1];
     if (a.w_edge)
       hipLaunchKernelGGL((conv_fwd_kernel<LIN, LEDGE, LOUT, p0, p1, true>), grid, dim3(kWave), 0, st, a.N, a.C,
-                         a.rowptr, a.sender, a.pos, a.shift, a.x, a.w_edge, a.z, a.rc);
+                         a.rowptr, a.sender, a.pos, a.shift, a.x, a.w_edge, a.z, a.rc, nullptr);
     else
       hipLaunchKernelGGL((conv_fwd_kernel<LIN, LEDGE, LOUT, p0, p1, false>), grid, dim3(kWave), 0, st, a.N, a.C,
-                         a.rowptr, a.sender, a.pos, a.shift, a.x, a.W, a.z, a.rc);
+                         a.rowptr, a.sender, a.pos, a.shift, a.x, a.W, a.z, a.rc, nullptr);
+  });
+}
+
+// Forward with the radial network fused (a.W = W3, a.mlp_h = h2 [E][64]).
+template <int LIN, int LEDGE, int LOUT>
+void launch_fwd_mlp(const ConvArgs& a, hipStream_t st) {
+  using Cfg = ConvCfg<LIN, LEDGE, LOUT>;
+  using GS = PathGroups<Cfg, fwd_budget(Cfg::NIN)>;
+  dim3 grid(a.N, (a.C + kWave - 1) / kWave);
+  static_for<GS::n>([&](auto gi) {
+    constexpr int p0 = GS::start[gi], p1 = GS::start[gi + 1];
+    hipLaunchKernelGGL((conv_fwd_kernel<LIN, LEDGE, LOUT, p0, p1, false, true>), grid, dim3(kWave), 0, st, a.N, a.C,
+                       a.rowptr, a.sender, a.pos, a.shift, a.x, a.W, a.z, a.rc, a.mlp_h);
   });
 }
 
@@ -409,7 +551,7 @@ struct VjpShape {
   static constexpr int NE = nrank(LEDGE);
   static constexpr int NRED = NE + 1;                      // y_bar components, s
   static constexpr int REC = EP::NY + 2 * kNB + 2;         // y / products, R, R', receiver, edge id
-  static constexpr int budget = vjp_budget(nrank(LIN), NE) - (EP::kCXReg ? EP::CXt::n : 0);
+  static constexpr int budget = vjp_budget(nrank(LIN), NE, LOUT < kAllParities) - (EP::kCXReg ? EP::CXt::n : 0);
   // edge records of a chunk of ch edges plus the per-wave row sums
   static constexpr size_t lds_bytes(int nw, int ch) {
     return sizeof(float) * ((size_t)ch * REC + (size_t)nw * ch * NRED * 4);
@@ -439,13 +581,18 @@ __device__ __forceinline__ float row_sum16(float v) {
 // w_bar[e, p, k] = <g_p, f_p(x, y)> is stored per edge.
 // CH: edges staged per chunk (the shape's default, or 32 for short slices,
 // which halves the block's LDS).
-template <int LIN, int LEDGE, int LOUT, bool NEED_X, bool NEED_POS, bool XW, int CH = VjpShape<LIN, LEDGE, LOUT>::CH>
+// MLP: W = W3 [64][P][C] and hh [E][2][64] the second hidden layer of the
+// radial network and its r-derivative per edge; w and dw/dr are formed in
+// the lanes for batches of mlp_batch_vjp(paths of the group) edges.
+template <int LIN, int LEDGE, int LOUT, bool NEED_X, bool NEED_POS, bool XW, int CH = VjpShape<LIN, LEDGE, LOUT>::CH,
+          bool MLP = false>
 __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
     int N, int C, const int* __restrict__ t_rowptr, const int* __restrict__ t_edge,
     const int* __restrict__ receiver, const float* __restrict__ pos,
     const float* __restrict__ shift, const float* __restrict__ x,
     const float* __restrict__ W, const float* __restrict__ g, float* __restrict__ x_out,
-    float* __restrict__ p_out, float* __restrict__ rbar, float* __restrict__ wb_out, float rc) {
+    float* __restrict__ p_out, float* __restrict__ rbar, float* __restrict__ wb_out, float rc,
+    const float* __restrict__ hh) {
   using Cfg = ConvCfg<LIN, LEDGE, LOUT>;
   using Sh = VjpShape<LIN, LEDGE, LOUT>;
   using EP = typename Sh::EP;
@@ -457,6 +604,10 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
   float* geo = lds;                      // [CH][REC]
   float* part = lds + CH * REC;          // [NW][CH edges][NRED][4 rows]
   const int NW = blockDim.x / kWave;
+  // MLP: [CH + kMlpBatchVjpMax][HR] activations (and their derivatives) of
+  // the chunk's edges (a last batch may read rows past the chunk; unused)
+  constexpr int HR = NEED_POS ? kMlpRow2 : kMlpRow;
+  float* hsh = part + (NEED_POS ? NW : 0) * CH * NRED * 4;
 
   const int v = xcd_node(blockIdx.x, N);
   const int S = gridDim.y, sl = blockIdx.y;   // slice sl of S of v's outgoing edges
@@ -495,8 +646,8 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
     constexpr bool FIRST = gi == 0;
     // radial weights of this lane's channel for the group's paths (zero for
     // idle lanes, so their contributions to the sums over lanes vanish)
-    float Wr[XW ? 1 : kNB * G::NP];
-    if constexpr (!XW) {
+    float Wr[XW || MLP ? 1 : kNB * G::NP];
+    if constexpr (!XW && !MLP) {
       static_for<kNB * G::NP>([&](auto i) {
         constexpr int b = i / G::NP, pi = i % G::NP;
         Wr[i] = act ? W[(size_t)(b * P + G::p0 + pi) * C + kk] : 0.f;
@@ -521,6 +672,8 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
         EP::fill(y, rec);
         if constexpr (XW) {
           rec[NY] = r > 0.f ? 1.f : 0.f;
+        } else if constexpr (MLP) {
+          copy_row<NEED_POS ? kRadRow : kRadHidden>(hh + (size_t)e * kRadRow, hsh + lane * HR);
         } else {
           float R[kNB], dR[kNB];
           radial<true>(r, rc, R, dR);
@@ -545,7 +698,9 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
           static_for<G::NP>([&](auto pi) { wn[pi] = W[r0 + (size_t)(G::p0 + pi) * C]; });
         }
       }
-      for (int j = 0; j < cnt; ++j) {
+      // one edge; wm(pi) / dwm(pi) give the fused network's weight of path
+      // p0 + pi and its r-derivative
+      auto edge = [&](int j, auto wm, auto dwm) {
         const float* rec = geo + j * REC;
         const int u = uniform_int(__float_as_int(rec[NY + 2 * kNB]));
         const auto gu = node_rsrc(g, u, NOUT * C);
@@ -581,6 +736,8 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
           float w = 0.f;
           if constexpr (XW) {
             w = we[pi];
+          } else if constexpr (MLP) {
+            w = wm(pi);
           } else {
             static_for<kNB>([&](auto b) {
               constexpr int bb = b;
@@ -637,10 +794,14 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
               if (wb_out && act) wb_out[erow + (size_t)p * C] = rec[NY] * wbar;
             } else {
               float dw = 0.f;
-              static_for<kNB>([&](auto b) {
-                constexpr int bb = b;
-                dw = fmaf(rec[NY + kNB + bb], Wr[bb * G::NP + pi], dw);
-              });
+              if constexpr (MLP) {
+                dw = dwm(pi);
+              } else {
+                static_for<kNB>([&](auto b) {
+                  constexpr int bb = b;
+                  dw = fmaf(rec[NY + kNB + bb], Wr[bb * G::NP + pi], dw);
+                });
+              }
               sacc = fmaf(wbar, dw, sacc);
             }
           }
@@ -656,6 +817,28 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
           const float t = row_sum16(sacc);
           if ((lane & 15) == 0) dst[NE * 4] = t;
         }
+      };
+      if constexpr (MLP) {
+        constexpr int MB = mlp_batch_vjp(G::NP);
+        for (int jb = 0; jb < cnt; jb += MB) {
+          float wb[MB * G::NP], dwb[MB * G::NP];
+          mlp_batch_weights<MB, G::NP, NEED_POS, HR, 2>(hsh + jb * HR, W + (size_t)G::p0 * C + kk, (size_t)P * C, C, wb,
+                                                     dwb);
+          // idle lanes carry weight 0 (their products must not reach the sums over lanes)
+          if (!act) {
+            static_for<MB * G::NP>([&](auto i) {
+              wb[i] = 0.f;
+              dwb[i] = 0.f;
+            });
+          }
+          static_for<MB>([&](auto bi) {
+            constexpr int b = bi;
+            if (jb + b < cnt)
+              edge(jb + b, [&](auto pi) { return wb[b * G::NP + pi]; }, [&](auto pi) { return dwb[b * G::NP + pi]; });
+          });
+        }
+      } else {
+        for (int j = 0; j < cnt; ++j) edge(j, [](auto) { return 0.f; }, [](auto) { return 0.f; });
       }
       __syncthreads();
       if constexpr (NEED_POS) {
@@ -761,7 +944,7 @@ void launch_vjp(const ConvArgs& a, hipStream_t st) {
 #define FC_VJP_CH(NX, NP, XW, CHV)                                                                                   \
   hipLaunchKernelGGL((conv_vjp_sender_kernel<LIN, LEDGE, LOUT, NX, NP, XW, CHV>), grid, block,                      \
                      Sh::lds_bytes(np ? nw : 0, CHV), st, a.N, a.C, a.t_rowptr, a.t_edge, a.receiver, a.pos,         \
-                     a.shift, a.x, XW ? a.w_edge : a.W, a.g, xo, po, wsl.rbar, a.w_edge_bar, a.rc)
+                     a.shift, a.x, XW ? a.w_edge : a.W, a.g, xo, po, wsl.rbar, a.w_edge_bar, a.rc, nullptr)
 #define FC_VJP(NX, NP, XW)                          \
   do {                                              \
     if constexpr (Sh::CH > 32) {                    \
@@ -784,6 +967,34 @@ void launch_vjp(const ConvArgs& a, hipStream_t st) {
   }
 #undef FC_VJP
 #undef FC_VJP_CH
+  launch_vjp_combine(a, wsl, nrank(LIN), st);
+}
+
+// VJP with the radial network fused (a.W = W3, a.mlp_h = [E][2][64] h2 and
+// dh2/dr): x_bar and/or pos_bar, the latter with the radial term through
+// w(r); 32 edges per chunk keep the activation rows within a quarter of
+// the LDS at 128 channels.
+template <int LIN, int LEDGE, int LOUT>
+void launch_vjp_mlp(const ConvArgs& a, hipStream_t st) {
+  const bool nx = a.x_bar != nullptr, np = a.pos_bar != nullptr;
+  if (!nx && !np) return;
+  const int nw = (a.C + kWave - 1) / kWave;
+  const VjpWorkspace wsl(a.N, a.E, a.C, nrank(LIN), ConvCfg<LIN, LEDGE, LOUT>::P, false, a.rbar);
+  float* xo = wsl.S == 1 ? a.x_bar : wsl.x_part;
+  float* po = wsl.S == 1 ? a.pos_bar : wsl.p_part;
+  dim3 grid(a.N, wsl.S), block(nw * kWave);
+  using Sh = VjpShape<LIN, LEDGE, LOUT>;
+  constexpr int CHM = 32;
+  // activation rows of the chunk's edges, plus the rows a last partial batch reads past its end
+  const size_t lds = Sh::lds_bytes(np ? nw : 0, CHM) + sizeof(float) * (CHM + kMlpBatchVjpMax) * (np ? kMlpRow2 : kMlpRow);
+#define FC_VJP_MLP(NX, NP)                                                                                          \
+  hipLaunchKernelGGL((conv_vjp_sender_kernel<LIN, LEDGE, LOUT, NX, NP, false, CHM, true>), grid, block, lds, st, a.N, \
+                     a.C, a.t_rowptr, a.t_edge, a.receiver, a.pos, a.shift, a.x, a.W, a.g, xo, po, wsl.rbar, nullptr,  \
+                     a.rc, a.mlp_h)
+  if (nx && np) FC_VJP_MLP(true, true);
+  else if (nx) FC_VJP_MLP(true, false);
+  else FC_VJP_MLP(false, true);
+#undef FC_VJP_MLP
   launch_vjp_combine(a, wsl, nrank(LIN), st);
 }
 

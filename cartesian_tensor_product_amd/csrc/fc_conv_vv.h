@@ -377,7 +377,12 @@ struct VVShape {
   // reductions: Yb, Yd, [Ya], S1, S2, S3
   static constexpr int NRED = (HAS_VX ? 3 : 2) * NE + 3;
   static constexpr int REC = 2 * NE + 3 * kNB + 2;   // y, ydot, R, R', R'', nd, receiver
-  static constexpr int budget = 200 - (HAS_VX ? 3 : 2) * (NIN + NE);
+  // register budget of one path group; with natural-parity, path-separated
+  // rank-3 senders capped at 100 (3.68 -> 3.44 ms for the micro workload's
+  // VJP-of-VJP; smaller groups were slower at rank 4, where each sweep
+  // repeats 2 NE + 3 sums per edge, and with every parity)
+  static constexpr int base_budget = 200 - (HAS_VX ? 3 : 2) * (NIN + NE);
+  static constexpr int budget = LOUT < kAllParities && NIN == 16 && base_budget > 100 ? 100 : base_budget;
   // edge records of a chunk of ch edges plus the per-wave row sums
   static constexpr size_t lds_bytes(int nw, int ch) {
     return sizeof(float) * ((size_t)ch * REC + (size_t)nw * ch * NRED * 4);

@@ -11,6 +11,7 @@ namespace fc {
 
 inline constexpr int kRadFeat = 8;     // Chebyshev functions
 inline constexpr int kRadHidden = 64;  // width of both hidden layers
+inline constexpr int kRadRow = 2 * kRadHidden;  // floats per edge of launch_radial_hidden_rows: h2, dh2/dr
 
 // Flat weights: W1 [8][64], W2 [64][64], W3 [64][P C].
 inline size_t radial_weight_floats(int P, int C) {
@@ -32,6 +33,10 @@ inline int radial_ld(int E) { return (E + 3) / 4 * 4; }
 void launch_radial_hidden(const RadialArgs& a, float* h2t, hipStream_t st);
 // w [E][P C] = h2 W3.
 void launch_radial_out(const RadialArgs& a, const float* h2t, float* w, hipStream_t st);
+// hh [E][2][64]: the second hidden layer of every edge and its derivative
+// with respect to the edge length (edge-major rows, for the convolution
+// with the output layer fused into its lanes).
+void launch_radial_hidden_rows(const RadialArgs& a, float* hh, hipStream_t st);
 // Backward from w_bar [E][P C]: q [E][3] = dL/dr_vec per edge, then
 // pos_grad[v] += sum_{e out of v} q_e - sum_{e into v} q_e; with w_grad
 // (flat layout) the weight gradients.  Scratch: hbar [E][64], then (w_grad)

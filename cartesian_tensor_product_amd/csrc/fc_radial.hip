@@ -111,6 +111,53 @@ __global__ __launch_bounds__(kRadBlock) void radial_hidden_kernel(int E, float r
   }
 }
 
+// Row e of hh: h2 (64 floats), then dh2/dr (64 floats), by forward-mode
+// differentiation of the two hidden layers along the edge length.
+__global__ __launch_bounds__(kRadBlock) void radial_hidden_rows_kernel(int E, float rmax,
+                                                                       const int* __restrict__ receiver,
+                                                                       const int* __restrict__ sender,
+                                                                       const float* __restrict__ pos,
+                                                                       const float* __restrict__ shift,
+                                                                       const float* __restrict__ W,
+                                                                       float* __restrict__ hh) {
+  __shared__ float w1[kW1], w2[kW2];
+  load_hidden_weights(W, w1, w2);
+  const int e = blockIdx.x * kRadBlock + threadIdx.x;
+  if (e >= E) return;   // no barrier below
+  float rv[3], phi[kRadFeat], dphi[kRadFeat];
+  edge_vec(e, receiver, sender, pos, shift, rv);
+  features(sqrtf(rv[0] * rv[0] + rv[1] * rv[1] + rv[2] * rv[2]), rmax, phi, dphi);
+  float h1[kRadHidden], dh1[kRadHidden];
+#pragma unroll
+  for (int j = 0; j < kRadHidden; ++j) {
+    float a = 0.f, da = 0.f;
+#pragma unroll
+    for (int n = 0; n < kRadFeat; ++n) {
+      a = fmaf(phi[n], w1[n * kRadHidden + j], a);
+      da = fmaf(dphi[n], w1[n * kRadHidden + j], da);
+    }
+    h1[j] = silu(a);
+    dh1[j] = silu_grad(a) * da;
+  }
+  float4* row = reinterpret_cast<float4*>(hh + (size_t)e * kRadRow);
+  for (int j4 = 0; j4 < kRadHidden; j4 += 4) {
+    float h[4], dh[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float a = 0.f, da = 0.f;
+#pragma unroll
+      for (int j = 0; j < kRadHidden; ++j) {
+        a = fmaf(h1[j], w2[j * kRadHidden + j4 + q], a);
+        da = fmaf(dh1[j], w2[j * kRadHidden + j4 + q], da);
+      }
+      h[q] = silu(a);
+      dh[q] = silu_grad(a) * da;
+    }
+    row[j4 / 4] = make_float4(h[0], h[1], h[2], h[3]);
+    row[(kRadHidden + j4) / 4] = make_float4(dh[0], dh[1], dh[2], dh[3]);
+  }
+}
+
 // Backward of the hidden layers for one edge from h2_bar = hbar[e][:]:
 // q_e = (sum_n phi_bar_n dphi_n / dr) r_hat and, with a2bt, the operands of
 // the W2 / W1 gradients (a2_bar, h1, a1_bar edge-minor; phi edge-minor).
@@ -248,6 +295,12 @@ void launch_radial_out(const RadialArgs& a, const float* h2t, float* w, hipStrea
     g.prob[g.count++] = problem(a.E - E4, (int)PC, kRadHidden, plain_view_t(h2t + E4, ld), plain_view_t(W3, PC),
                                 plain_out(w + (size_t)E4 * PC, PC, 0));
   gemm_group(g, st);
+}
+
+void launch_radial_hidden_rows(const RadialArgs& a, float* hh, hipStream_t st) {
+  if (a.E == 0) return;
+  hipLaunchKernelGGL(radial_hidden_rows_kernel, dim3((a.E + kRadBlock - 1) / kRadBlock), dim3(kRadBlock), 0, st,
+                     a.E, a.r_max, a.receiver, a.sender, a.pos, a.shift, a.weights, hh);
 }
 
 size_t radial_vjp_scratch_floats(int E, int P, int C) {

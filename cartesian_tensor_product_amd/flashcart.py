@@ -18,6 +18,8 @@ FC_OK, FC_ERR_INVALID_ARGUMENT, FC_ERR_UNSUPPORTED, FC_ERR_WORKSPACE, FC_ERR_HIP
 FC_LADDER_FULL, FC_LADDER_PATH_REDUCED = 0, 1
 FC_CONV_ALL_PARITIES = 1   # descriptor flag: every triangle-allowed path (odd J too)
 FC_CONV_SUM_PATHS = 2      # descriptor flag: outputs of the paths of each rank summed
+FC_CONV_MLP_MATERIALIZE = 4  # descriptor flag: radial-network calls store w [E][P][C] instead of fusing it
+FC_CONV_MLP_FUSE = 8         # descriptor flag: radial-network calls form w in the convolution's lanes
 
 
 class FlashCartError(RuntimeError):

@@ -487,6 +487,7 @@ VV_W_MAX_RANK_OTHER = 3  # ... with every parity or summed paths
 VV_SPLIT_RANK = 5
 VV_SPLIT_RANK_OTHER = 4
 SUM_MAX_RANK = 4
+MLP_MAX_RANK = 3         # convolution with the radial network fused into its lanes
 
 
 def cfg_ranks(cfg):
@@ -528,6 +529,28 @@ def vv_split(cfg) -> bool:
     return has_vv(cfg) and max(li, le, lo) >= (VV_SPLIT_RANK_OTHER if other else VV_SPLIT_RANK)
 
 
+def has_mlp(cfg) -> bool:
+    """Whether the convolution with the radial network's output layer fused
+    into its lanes is instantiated (natural parity, paths kept apart)."""
+    li, le, lo, allp = cfg_ranks(cfg)
+    return not allp and not cfg_summed(cfg) and max(li, le, lo) <= MLP_MAX_RANK
+
+
+def mlp_vjp_fused(cfg) -> bool:
+    """Whether the VJP weighted by the radial network runs fused by default:
+    when the convolution's own VJP work per edge and channel (2 T + sum
+    min(2l1+1, 2L+1) + 2 sum (2l2+1) FMAs over the paths) is at least a
+    third of the 64 P FMAs that form w from the 64 hidden units.  Below that
+    the fused VJP spends its issue slots on w and dw/dr, which the
+    materialised path gives to the matrix cores (measured: rank 2, ratio
+    0.38, fused 1.24 ms vs 1.42 ms; the (0, 3, 3) block convolution, ratio
+    0.27, fused slower)."""
+    li, le, lo, _ = cfg_ranks(cfg)
+    paths = [(a, b, L) for L in range(lo + 1) for a in range(li + 1) for b in range(le + 1) if admissible(a, b, L)]
+    core = sum(2 * len(coupling_terms(a, b, L)) + min(2 * a + 1, 2 * L + 1) + 2 * (2 * b + 1) for a, b, L in paths)
+    return 3 * core >= 64 * len(paths)
+
+
 # the passes of a split VJP-of-VJP: unit suffix, function, body
 VV_PARTS = [("vr", "recv", "vv_part_recv<{r}>(a, st);"),
             ("vg", "wgrad", "vv_part_wgrad<{r}>(a, st);"),
@@ -546,6 +569,11 @@ def emit_instances(gen_dir: str) -> list:
     lines += [f"  X({a}, {b}, {c}) \\" for a, b, c in cfgs if has_vv((a, b, c))]
     lines += ["", "", "// ... and the VJP-of-VJP with explicit per-edge weights for", "#define FC_CONV_VV_W_CONFIGS(X) \\"]
     lines += [f"  X({a}, {b}, {c}) \\" for a, b, c in cfgs if has_vv_w((a, b, c))]
+    lines += ["", "", "// ... and the convolution with the radial network's output layer fused for",
+              "#define FC_CONV_MLP_CONFIGS(X) \\"]
+    lines += [f"  X({a}, {b}, {c}) \\" for a, b, c in cfgs if has_mlp((a, b, c))]
+    lines += ["", "", "// ... of which the VJP runs fused by default for", "#define FC_CONV_MLP_VJP_FUSED_CONFIGS(X) \\"]
+    lines += [f"  X({a}, {b}, {c}) \\" for a, b, c in cfgs if has_mlp((a, b, c)) and mlp_vjp_fused((a, b, c))]
     lines += ["", ""]
     _write(os.path.join(gen_dir, "fc_conv_configs.h"), "\n".join(lines))
     files = []
@@ -587,6 +615,17 @@ def emit_instances(gen_dir: str) -> list:
                    f"  launch_vjp_vjp_w<{a}, {b}, {c}>(args, stream);\n"
                    f"}}\n\n}}  // namespace fc\n")
             f = os.path.join(gen_dir, f"conv_inst_{a}{b}{c}w.hip")
+            _write(f, src)
+            files.append(f)
+        if has_mlp((a, b, c)):
+            src = (f"// Generated by cartesian_tensor_product_amd/gen/generate.py -- do not edit.\n"
+                   f"#include \"../fc_conv_kernels.h\"\n\n"
+                   f"namespace fc {{\n\n"
+                   f"void conv_run_mlp_{a}{b}{c}(int op, const ConvArgs& args, hipStream_t stream) {{\n"
+                   f"  if (op == 0) launch_fwd_mlp<{a}, {b}, {c}>(args, stream);\n"
+                   f"  else launch_vjp_mlp<{a}, {b}, {c}>(args, stream);\n"
+                   f"}}\n\n}}  // namespace fc\n")
+            f = os.path.join(gen_dir, f"conv_inst_{a}{b}{c}m.hip")
             _write(f, src)
             files.append(f)
     return files

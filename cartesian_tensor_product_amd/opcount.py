@@ -19,6 +19,10 @@ VJP:
     y_bar += w_p v;  <g, f_p> = <v, y>      2 n2  (the radial derivative
                                             takes <g, f_p> from v)
 
+With the radial network's output layer fused into the convolution the
+basis is its 64 second-layer units (n_basis = 64): w_p = sum_h h2_h W3[h, p]
+and dw_p/dr from dh2/dr, per edge and channel.
+
 The products c y_b2 are formed once per edge and shared by all channels;
 such per-edge work (geometry, direction tensors, the chain rule of y_bar to
 the position) and the sums over lanes are not counted.  A flop is half an

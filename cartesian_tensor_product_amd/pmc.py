@@ -4,7 +4,8 @@
         per-kernel mean of every counter in the runs' *_counter_collection.csv
 
     python -m cartesian_tensor_product_amd.pmc stats DIR
-        per-kernel durations from a ``--kernel-trace --stats`` run (markdown)
+        per-kernel durations from a ``--kernel-trace --stats`` run (its stats
+        CSV, or its SQLite database) as markdown
 
     python -m cartesian_tensor_product_amd.pmc issue DIR [DIR ...]
         per-kernel instruction mix from runs holding SQ_WAVES, SQ_INSTS_VALU,
@@ -116,16 +117,31 @@ def kernel_name(raw: str) -> str:
     return raw.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
 
 
-def stats(run_dir: str) -> str:
+def _stats_rows(run_dir: str):
+    """(name, calls, avg ns, min ns, max ns, % time) per kernel, from the run's
+    *kernel_stats.csv or, where rocprofv3 wrote its SQLite database
+    (*_results.db), from the database's kernel dispatches."""
     files = glob.glob(os.path.join(run_dir, "**", "*kernel_stats.csv"), recursive=True)
-    if not files:
-        raise FileNotFoundError(f"no *kernel_stats.csv under {run_dir}")
+    if files:
+        with open(files[0]) as fh:
+            return [(r["Name"], int(r["Calls"]), float(r["AverageNs"]), float(r["MinNs"]), float(r["MaxNs"]),
+                     float(r["Percentage"])) for r in csv.DictReader(fh)]
+    dbs = glob.glob(os.path.join(run_dir, "**", "*_results.db"), recursive=True)
+    if not dbs:
+        raise FileNotFoundError(f"no *kernel_stats.csv or *_results.db under {run_dir}")
+    import sqlite3
+    con = sqlite3.connect(dbs[0])
+    rows = con.execute("select name, count(*), avg(duration), min(duration), max(duration), sum(duration) "
+                       "from kernels group by name order by sum(duration) desc").fetchall()
+    total = sum(r[5] for r in rows) or 1.0
+    return [(n, c, a, lo, hi, 100.0 * t / total) for n, c, a, lo, hi, t in rows]
+
+
+def stats(run_dir: str) -> str:
     out = ["| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
-    with open(files[0]) as fh:
-        for r in csv.DictReader(fh):
-            out.append(f"| `{kernel_name(r['Name'])[:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
-                       f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
-                       f"{float(r['Percentage']):.2f} |")
+    for name, calls, avg, lo, hi, pct in _stats_rows(run_dir):
+        out.append(f"| `{kernel_name(name)[:90]}` | {calls} | {avg / 1e3:.1f} | {lo / 1e3:.1f} | {hi / 1e3:.1f} | "
+                   f"{pct:.2f} |")
     return "\n".join(out)
 
 

@@ -110,6 +110,14 @@ int32_t fc_abi_version(void);
  * ---------------------------------------------------------------------- */
 #define FC_CONV_ALL_PARITIES 1u
 #define FC_CONV_SUM_PATHS 2u
+/* FC_CONV_MLP_MATERIALIZE / FC_CONV_MLP_FUSE (exclusive): how the calls
+ * weighted by the radial network (fc_edge_conv_mlp_*, the message blocks)
+ * apply its output layer -- materialised (w [E][P][C] written by an MFMA
+ * GEMM and streamed through the explicit-weight kernels) or fused into the
+ * convolution's lanes (see fc_edge_conv_mlp_workspace_bytes for the
+ * default); every other call ignores them. */
+#define FC_CONV_MLP_MATERIALIZE 4u
+#define FC_CONV_MLP_FUSE 8u
 
 typedef struct {
   int32_t n_nodes, n_edges, channels;
@@ -270,7 +278,21 @@ fc_status fc_edge_conv_vjp_vjp_w(const fc_conv_desc* d, const fc_graph* g, const
  * must be 8 (the Chebyshev count).  An edge of zero length gets w = 0.
  * ---------------------------------------------------------------------- */
 size_t fc_radial_mlp_weight_floats(const fc_conv_desc* d);
-/* Workspace of the calls below: op 0 forward (and fc_radial_mlp), op 1 VJP. */
+/* How w is applied.  Fused: a pre-pass stores each edge's second hidden
+ * layer and its r-derivative (512 bytes per edge), and the convolution's
+ * lanes form w = h2 W3 (and dw/dr) for batches of edges without storing
+ * them; available for natural parity, paths apart and ranks <= 3, in the
+ * forward and in a VJP without mlp_w_grad.  Materialised: w [E][P][C] is
+ * written to the workspace by an MFMA GEMM and streamed through the
+ * explicit-weight kernels, and the VJP carries w_bar back through the
+ * network.  Default: the forward fused wherever available; the VJP fused
+ * where the convolution's own VJP work per edge and channel is at least a
+ * third of the 64 P FMAs that form w (ranks (2,2,2), (1,3,3), (2,3,3),
+ * (3,3,3)), materialised elsewhere (there the matrix cores form w faster);
+ * FC_CONV_MLP_FUSE / FC_CONV_MLP_MATERIALIZE override.  A forward on an op 2
+ * workspace (the message blocks) follows the VJP's choice.
+ * Workspace of the calls below: op 0 forward (and fc_radial_mlp), op 1 VJP
+ * with mlp_w_grad, op 2 VJP without it (op 1 bytes serve both VJPs). */
 size_t fc_edge_conv_mlp_workspace_bytes(const fc_conv_desc* d, int32_t op);
 
 /* w [E][P][C] (receiver-sorted edges): the per-edge weights alone, for

@@ -12,10 +12,14 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 
-def gpu_block(cspec, lspec, w, d, entries, C, order, variant, forces=True):
+def gpu_block(cspec, lspec, w, d, entries, C, order, variant, forces=True, radial="default"):
+    """Energy, atom energies and forces of the block; the radial network's
+    output layer as the library chooses (materialised for this scalar-sender
+    convolution), "fused" into the convolution or "materialized"."""
     from cartesian_tensor_product_amd import flashcart as fc
     N, E = d["pos"].shape[0], len(d["sender"])
-    cd = fc.conv_desc(N, E, C, 0, cspec.l_edge, cspec.l_edge, 5.0)
+    flags = {"default": 0, "fused": fc.FC_CONV_MLP_FUSE, "materialized": fc.FC_CONV_MLP_MATERIALIZE}[radial]
+    cd = fc.conv_desc(N, E, C, 0, cspec.l_edge, cspec.l_edge, 5.0, flags=flags)
     ld = fc.ladder_desc(N, C, cspec.l_edge, cspec.l_edge, 0, order,
                         fc.FC_LADDER_FULL if variant == "full" else fc.FC_LADDER_PATH_REDUCED)
     flat = np.concatenate([w[name].astype(np.float32).ravel() for name, *_ in entries])
@@ -32,12 +36,14 @@ def gpu_block(cspec, lspec, w, d, entries, C, order, variant, forces=True):
     return float(en.item()), ea.cpu().numpy(), None if F is None else F.cpu().numpy()
 
 
-@pytest.mark.parametrize("variant,order,C", [("reduced", 3, 32), ("full", 3, 32), ("reduced", 5, 32),
-                                             ("reduced", 3, 96)])
-def test_message_block_rattled(variant, order, C):
+@pytest.mark.parametrize("variant,order,C,radial", [("reduced", 3, 32, "default"), ("full", 3, 32, "default"),
+                                                    ("reduced", 5, 32, "default"), ("reduced", 3, 96, "default"),
+                                                    ("reduced", 3, 32, "fused"), ("reduced", 3, 96, "fused"),
+                                                    ("full", 3, 32, "materialized")])
+def test_message_block_rattled(variant, order, C, radial):
     """C = 32 and 96 leave lanes of the readout's channel chunks idle."""
     cspec, lspec, w, d, entries = block_setup(C=C, order=order, variant=variant)
-    E, ea, F = gpu_block(cspec, lspec, w, d, entries, C, order, variant)
+    E, ea, F = gpu_block(cspec, lspec, w, d, entries, C, order, variant, radial=radial)
     Eo, eao, Fo = model.block_energy_forces(*args(cspec, lspec, w, d))
     assert abs(E - Eo) <= 1e-4 * np.abs(eao).sum()
     assert_close("e_atom", ea, eao)
@@ -108,13 +114,13 @@ def oracle_1000(variant, rattle):
         _ORACLE[key] = model.block_energy_forces(*args(cspec, lspec, w, d))
     return _ORACLE[key]
 
-@pytest.mark.parametrize("variant", ["reduced", "full"])
-def test_message_block_1000_atoms_128_channels_order5(variant):
+@pytest.mark.parametrize("variant,radial", [("reduced", "default"), ("full", "default"), ("reduced", "fused")])
+def test_message_block_1000_atoms_128_channels_order5(variant, radial):
     """1000 atoms (5 x 5 x 5 cells), 128 channels, ladder order 5: every
     atom's energy and force against the oracle."""
     C, order = 128, 5
     cspec, lspec, w, d, entries = block_setup(C=C, order=order, variant=variant, ncell=5)
-    E, ea, F = gpu_block(cspec, lspec, w, d, entries, C, order, variant)
+    E, ea, F = gpu_block(cspec, lspec, w, d, entries, C, order, variant, radial=radial)
     Eo, eao, Fo = oracle_1000(variant, 0.05)
     assert abs(E - Eo) <= 1e-4 * np.abs(eao).sum()
     assert_close("e_atom", ea, eao)
@@ -152,8 +158,8 @@ def local_block_problem(d, nodes):
     return ids, sub
 
 
-@pytest.mark.parametrize("variant", ["reduced", "full"])
-def test_message_block_4096_atoms_sampled(variant):
+@pytest.mark.parametrize("variant,radial", [("reduced", "default"), ("full", "default"), ("reduced", "fused")])
+def test_message_block_4096_atoms_sampled(variant, radial):
     """The benchmarked block: 4096 atoms (8 x 8 x 8 cells), 128 channels,
     order 5, in the launch configuration the benchmark times; four atoms'
     energies and forces against the oracle on their local subgraph."""
@@ -161,7 +167,7 @@ def test_message_block_4096_atoms_sampled(variant):
     cspec, lspec, w, d, entries = block_setup(C=C, order=order, variant=variant, ncell=8)
     N = d["pos"].shape[0]
     assert N == 4096
-    E, ea, F = gpu_block(cspec, lspec, w, d, entries, C, order, variant)
+    E, ea, F = gpu_block(cspec, lspec, w, d, entries, C, order, variant, radial=radial)
     nodes = np.array([0, 1337, 2900, 4095])
     ids, sub = local_block_problem(d, nodes)
     n_bar = len(d["sender"]) / N

@@ -1,7 +1,9 @@
 """GPU parity of the pages' radial network (Chebyshev features, envelope,
 bias-free SiLU MLP with an MFMA output layer) and of the convolution it
 weights (forward; VJP to features, positions and the network's weights)
-against the oracle."""
+against the oracle, with the output layer fused into the convolution's
+lanes (FC_CONV_MLP_FUSE), with w [E][P][C] stored and streamed
+(FC_CONV_MLP_MATERIALIZE), and with the default choice."""
 import numpy as np
 import pytest
 
@@ -20,12 +22,17 @@ def split(flat, P, C):
     return W1, W2, W3
 
 
+MODES = ["fused", "materialized"]
+FLAGS = {"fused": "FC_CONV_MLP_FUSE", "materialized": "FC_CONV_MLP_MATERIALIZE", "default": None}
+
+
 class GpuMlpConv:
-    def __init__(self, ranks, d, C, rc, mlp):
+    def __init__(self, ranks, d, C, rc, mlp, mode="fused"):
         from cartesian_tensor_product_amd import flashcart as fc
         self.fc = fc
         self.N, self.E, self.C = d["pos"].shape[0], int(len(d["sender"])), C
-        self.desc = fc.conv_desc(self.N, self.E, C, *ranks, rc)
+        flags = getattr(fc, FLAGS[mode]) if FLAGS[mode] else 0
+        self.desc = fc.conv_desc(self.N, self.E, C, *ranks, rc, flags=flags)
         self.P, self.nin, self.nout = fc.fc_conv_layout(self.desc)
         assert fc.fc_radial_mlp_weight_floats(self.desc) == mlp.size
         self.graph = fc.DeviceGraph(d["rowptr"], d["sender"], self.N, device="cuda")
@@ -48,7 +55,8 @@ class GpuMlpConv:
         xb = torch.empty_like(self.x) if "x" in want else None
         pb = torch.empty((self.N, 3), device="cuda") if "pos" in want else None
         wb = torch.empty_like(self.mlp) if "w" in want else None
-        ws = self.fc.workspace(self.fc.fc_edge_conv_mlp_workspace_bytes(self.desc, 1), "cuda")
+        op = 1 if "w" in want else 2
+        ws = self.fc.workspace(self.fc.fc_edge_conv_mlp_workspace_bytes(self.desc, op), "cuda")
         self.fc.fc_edge_conv_mlp_vjp(self.desc, self.graph, self.pos, self.shift, self.x, self.mlp, self.g, xb, pb,
                                      wb, ws)
         return xb, pb, wb
@@ -61,13 +69,18 @@ def setup(ranks, C, seed, n=40, k=12, box=5.0, rc=5.0):
     return spec, d, mlp
 
 
-@pytest.mark.parametrize("ranks", [(1, 1, 1), (2, 2, 2), (0, 3, 3), (3, 3, 3)])
-def test_mlp_conv_full(ranks):
+@pytest.mark.parametrize("mode", MODES + ["default"])
+@pytest.mark.parametrize("ranks", [(1, 1, 1), (2, 2, 2), (0, 3, 3), (1, 2, 2), (3, 3, 3)])
+def test_mlp_conv_full(ranks, mode):
+    """The forward and the VJP to x and positions (fused unless
+    materialised), then the VJP with the network's weight gradient (which
+    stores w in both modes)."""
     spec, d, mlp = setup(ranks, 40, 31)
-    gc = GpuMlpConv(ranks, d, 40, 5.0, mlp)
+    gc = GpuMlpConv(ranks, d, 40, 5.0, mlp, mode)
     w = gc.weights()
     z = gc.fwd()
-    xb, pb, wb = gc.vjp()
+    xb, pb, _ = gc.vjp(("x", "pos"))
+    xb2, pb2, wb = gc.vjp()
     torch.cuda.synchronize()
     W1, W2, W3 = split(f64(mlp), spec.n_paths, 40)
     r, _ = radial.edge_lengths(f64(d["pos"]), d["rowptr"], d["sender"])
@@ -77,13 +90,18 @@ def test_mlp_conv_full(ranks):
     xo, po, W1b, W2b, W3b = radial.edge_conv_vjp_mlp(*args, f64(d["g"]))
     assert_close("x_grad", xb.cpu().numpy(), xo)
     assert_close("pos_grad", pb.cpu().numpy(), po)
+    assert_close("x_grad (with the weight gradient)", xb2.cpu().numpy(), xo)
+    assert_close("pos_grad (with the weight gradient)", pb2.cpu().numpy(), po)
     wo = np.concatenate([W1b.ravel(), W2b.ravel(), W3b.ravel()])
     assert_close("mlp_w_grad", wb.cpu().numpy(), wo)
 
 
-def test_mlp_conv_single_outputs_and_channel_tail():
+@pytest.mark.parametrize("mode", MODES)
+def test_mlp_conv_single_outputs_and_channel_tail(mode):
+    """C = 65: the second wave has one live lane (the idle lanes must add
+    nothing to the per-edge sums over lanes)."""
     spec, d, mlp = setup((2, 2, 2), 65, 32, n=30, k=9)
-    gc = GpuMlpConv((2, 2, 2), d, 65, 5.0, mlp)
+    gc = GpuMlpConv((2, 2, 2), d, 65, 5.0, mlp, mode)
     W1, W2, W3 = split(f64(mlp), spec.n_paths, 65)
     xo, po, W1b, W2b, W3b = radial.edge_conv_vjp_mlp(spec, f64(d["pos"]), d["rowptr"], d["sender"], f64(d["x"]), W1,
                                                      W2, W3, f64(d["g"]))
@@ -101,13 +119,14 @@ def subgraph(rowptr, sender, edges):
     return np.concatenate([[0], np.cumsum(counts)]).astype(rowptr.dtype), sender[edges]
 
 
-def test_mlp_conv_microbenchmark_sampled():
+@pytest.mark.parametrize("mode", MODES)
+def test_mlp_conv_microbenchmark_sampled(mode):
     """1024 nodes x 128 neighbours x 128 channels, rank 2, r_max 5 A: the
     weights of 2000 sampled edges; z, x_grad and pos_grad on 8 sampled nodes
     (the oracle runs on the edges touching them, which is all these outputs
     read); translation invariance of the forces at full size."""
     spec, d, mlp = setup((2, 2, 2), 128, 1, n=1024, k=128, box=20.0, rc=5.0)
-    gc = GpuMlpConv((2, 2, 2), d, 128, 5.0, mlp)
+    gc = GpuMlpConv((2, 2, 2), d, 128, 5.0, mlp, mode)
     w = gc.weights()
     z = gc.fwd()
     xb, pb, _ = gc.vjp(("x", "pos"))
@@ -128,7 +147,8 @@ def test_mlp_conv_microbenchmark_sampled():
     assert np.abs(p.sum(0)).max() < 1e-4 * np.abs(p).max() * np.sqrt(1024)
 
 
-def test_mlp_conv_without_edges():
+@pytest.mark.parametrize("mode", MODES)
+def test_mlp_conv_without_edges(mode):
     """No edge: z and the gradients are zero (the network's weight gradient
     included)."""
     from cartesian_tensor_product_amd import flashcart as fc
@@ -138,18 +158,40 @@ def test_mlp_conv_without_edges():
              sender=np.zeros(0, np.int32), x=inputs.normal(np.random.default_rng(2), (N, spec.n_in, C)),
              g=inputs.normal(np.random.default_rng(3), (N, spec.n_out, C)))
     mlp = inputs.radial_mlp_weights(np.random.default_rng(4), spec.n_paths, C)
-    gc = GpuMlpConv((2, 2, 2), d, C, 5.0, mlp)
+    gc = GpuMlpConv((2, 2, 2), d, C, 5.0, mlp, mode)
     z = gc.fwd()
     xb, pb, wb = gc.vjp()
+    xf, pf, _ = gc.vjp(("x", "pos"))
     torch.cuda.synchronize()
-    for name, a in (("z", z), ("x_grad", xb), ("pos_grad", pb), ("mlp_w_grad", wb)):
+    for name, a in (("z", z), ("x_grad", xb), ("pos_grad", pb), ("mlp_w_grad", wb), ("x_grad", xf), ("pos_grad", pf)):
         assert float(a.abs().max()) == 0.0, name
 
 
-def test_mlp_conv_bitwise_deterministic():
+@pytest.mark.parametrize("want", [("x", "pos", "w"), ("x", "pos")])
+def test_mlp_conv_bitwise_deterministic(want):
     spec, d, mlp = setup((2, 2, 2), 40, 33, n=60, k=20, box=6.0)
     gc = GpuMlpConv((2, 2, 2), d, 40, 5.0, mlp)
-    r1 = [t.cpu().numpy() for t in gc.vjp()]
-    r2 = [t.cpu().numpy() for t in gc.vjp()]
+    r1 = [t.cpu().numpy() for t in gc.vjp(want) if t is not None]
+    r2 = [t.cpu().numpy() for t in gc.vjp(want) if t is not None]
+    assert len(r1) == len(want)
     for a, b in zip(r1, r2):
         assert np.array_equal(a, b)
+
+
+def test_mlp_workspace_sizes():
+    """The fused layouts are small (hidden rows, 512 bytes per edge); the
+    VJP with the network's weight gradient takes the materialised layout,
+    whose size also covers the fused VJP; a VJP asking for the weight
+    gradient with the smaller op 2 workspace is refused."""
+    from cartesian_tensor_product_amd import flashcart as fc
+    spec, d, mlp = setup((2, 2, 2), 128, 1, n=200, k=32, box=10.0)
+    gc = GpuMlpConv((2, 2, 2), d, 128, 5.0, mlp)
+    E = gc.E
+    b0, b1, b2 = (fc.fc_edge_conv_mlp_workspace_bytes(gc.desc, op) for op in (0, 1, 2))
+    mat = fc.conv_desc(gc.N, E, 128, 2, 2, 2, 5.0, flags=fc.FC_CONV_MLP_MATERIALIZE)
+    m0 = fc.fc_edge_conv_mlp_workspace_bytes(mat, 0)
+    assert b0 < E * 600 and m0 > E * gc.P * 128 * 4 and b2 < b1
+    ws = fc.workspace(b2, "cuda")
+    with pytest.raises(fc.FlashCartError):
+        fc.fc_edge_conv_mlp_vjp(gc.desc, gc.graph, gc.pos, gc.shift, gc.x, gc.mlp, gc.g, None, None,
+                                torch.empty_like(gc.mlp), ws)

@@ -47,6 +47,14 @@ __host__ __device__ constexpr bool term_has_b1(int tb, int te, int b) {
 __host__ __device__ constexpr int vjp_budget(int nin, int ne, bool natural_separate) {
   return natural_separate && nin >= 16 && nin <= 25 && ne <= 25 ? 190 - 3 * nin - 2 * ne : 200 - 2 * nin - ne;
 }
+// With one wave per sender (C <= 64) each extra sweep's records and
+// per-edge sums serve half as many channels: at rank 4 the wider groups
+// are faster there (1.62 / 2.64 ms against 2.02 / 3.49 ms at 64 / 128
+// neighbours); at rank 3 the narrower ones still win (0.51 / 0.71 ms
+// against 0.50 / 0.81 ms).
+__host__ __device__ constexpr bool vjp_wide_when_narrow(int nin, int ne, bool natural_separate) {
+  return natural_separate && nin == 25 && ne == 25;
+}
 // Channels of one VJP block: up to 4 waves (C <= 256).
 inline constexpr int kMaxVjpWaves = 4;
 // LDS one workgroup may hold on gfx950.
@@ -552,6 +560,8 @@ struct VjpShape {
   static constexpr int NRED = NE + 1;                      // y_bar components, s
   static constexpr int REC = EP::NY + 2 * kNB + 2;         // y / products, R, R', receiver, edge id
   static constexpr int budget = vjp_budget(nrank(LIN), NE, LOUT < kAllParities) - (EP::kCXReg ? EP::CXt::n : 0);
+  static constexpr int wide_budget = vjp_budget(nrank(LIN), NE, false) - (EP::kCXReg ? EP::CXt::n : 0);
+  static constexpr bool wide_when_narrow = vjp_wide_when_narrow(nrank(LIN), NE, LOUT < kAllParities);
   // edge records of a chunk of ch edges plus the per-wave row sums
   static constexpr size_t lds_bytes(int nw, int ch) {
     return sizeof(float) * ((size_t)ch * REC + (size_t)nw * ch * NRED * 4);
@@ -584,8 +594,9 @@ __device__ __forceinline__ float row_sum16(float v) {
 // MLP: W = W3 [64][P][C] and hh [E][2][64] the second hidden layer of the
 // radial network and its r-derivative per edge; w and dw/dr are formed in
 // the lanes for batches of mlp_batch_vjp(paths of the group) edges.
+// WIDE: the wider path groups of vjp_budget(.., false) (one-wave blocks at rank 4).
 template <int LIN, int LEDGE, int LOUT, bool NEED_X, bool NEED_POS, bool XW, int CH = VjpShape<LIN, LEDGE, LOUT>::CH,
-          bool MLP = false>
+          bool MLP = false, bool WIDE = false>
 __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
     int N, int C, const int* __restrict__ t_rowptr, const int* __restrict__ t_edge,
     const int* __restrict__ receiver, const float* __restrict__ pos,
@@ -599,7 +610,7 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
   using CXt = typename EP::CXt;
   constexpr int NIN = Cfg::NIN, NE = Cfg::NE, P = Cfg::P, NOUT = Cfg::NOUT;
   constexpr int REC = Sh::REC, NRED = Sh::NRED, NY = EP::NY;
-  using GS = PathGroups<Cfg, Sh::budget>;
+  using GS = PathGroups<Cfg, WIDE ? Sh::wide_budget : Sh::budget>;
   extern __shared__ float lds[];
   float* geo = lds;                      // [CH][REC]
   float* part = lds + CH * REC;          // [NW][CH edges][NRED][4 rows]
@@ -960,6 +971,22 @@ void launch_vjp(const ConvArgs& a, hipStream_t st) {
     else if (nx) FC_VJP(true, false, true);
     else if (np) FC_VJP(false, true, true);
     else FC_VJP(false, false, true);
+  } else if constexpr (Sh::wide_when_narrow) {
+    // (32-edge chunks, as the wide groups were measured with)
+#define FC_VJP_WIDE(NX, NP)                                                                                         \
+  hipLaunchKernelGGL((conv_vjp_sender_kernel<LIN, LEDGE, LOUT, NX, NP, false, 32, false, true>), grid, block,        \
+                     Sh::lds_bytes(np ? nw : 0, 32), st, a.N, a.C, a.t_rowptr, a.t_edge, a.receiver, a.pos, a.shift,   \
+                     a.x, a.W, a.g, xo, po, wsl.rbar, nullptr, a.rc, nullptr)
+    if (nw == 1) {
+      if (nx && np) FC_VJP_WIDE(true, true);
+      else if (nx) FC_VJP_WIDE(true, false);
+      else FC_VJP_WIDE(false, true);
+    } else {
+      if (nx && np) FC_VJP(true, true, false);
+      else if (nx) FC_VJP(true, false, false);
+      else FC_VJP(false, true, false);
+    }
+#undef FC_VJP_WIDE
   } else {
     if (nx && np) FC_VJP(true, true, false);
     else if (nx) FC_VJP(true, false, false);

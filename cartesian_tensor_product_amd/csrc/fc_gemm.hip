@@ -2,7 +2,9 @@
 //
 // Block tile 128 (M) x 128 (N) x 32 (K), four waves in a 2 x 2 grid; each
 // wave owns a 64 x 64 sub-tile held as 2 x 2 accumulators of
-// v_mfma_f32_32x32x2f32.  Operand layout of that instruction: lane l
+// v_mfma_f32_32x32x2f32.  Problems with N <= 64 take a narrow layout
+// instead: four waves stacked along M, each 32 x 64 (1 x 2 accumulators),
+// so that no wave computes columns past N.  Operand layout of that instruction: lane l
 // supplies A[l % 32][l / 32] and B[l / 32][l % 32]; the sixteen accumulator
 // registers r of lane l hold D[8 (r / 4) + 4 (l / 32) + r % 4][l % 32].
 //
@@ -36,6 +38,7 @@ constexpr int TPAD = BN + 4;     // epilogue tile row length (floats)
 static_assert(BM * TPAD <= 4 * SMEM, "the epilogue tile reuses the operand buffers");
 
 enum StageMode { kK = 0, kR = 1, kG = 2 };
+constexpr int kNarrow = 16;   // added to a problem's mode: N <= 64, narrow wave layout
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
@@ -203,18 +206,21 @@ __device__ __forceinline__ void store_out(const GOut& o, int m, int n, float val
   else *dst = val;
 }
 
-template <int MA, int MB>
+// NI: 32-row accumulator blocks per wave, 2 (2 x 2 waves of 64 x 64) or 1
+// (narrow: 4 x 1 waves of 32 x 64, for N <= 64).
+template <int MA, int MB, int NI>
 __device__ __forceinline__ void gemm_tile(const GemmProblem& P, int m0, int n0, int k_lo, int k_hi, int ks, float* As,
                                           float* Bs, bool vec_out) {
   const int wv = threadIdx.x / 64, lane = threadIdx.x % 64;
-  const int wm = wv % 2, wn = wv / 2;
+  const int wm = NI == 2 ? wv % 2 : wv, wn = NI == 2 ? wv / 2 : 0;
+  const int row0 = wm * 32 * NI;   // first row of the wave's sub-tile
   Stager<MA> sa;
   Stager<MB> sb;
   sa.init(P.A, P.M, m0);
   sb.init(P.Bt, P.N, n0);
-  floatx16 acc[2][2];
+  floatx16 acc[NI][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -239,16 +245,15 @@ __device__ __forceinline__ void gemm_tile(const GemmProblem& P, int m0, int n0, 
   for (int k0 = k_lo; k0 < k_hi; k0 += BK) {
     const float* Ac = As + buf * SMEM;
     const float* Bc = Bs + buf * SMEM;
-    float a[2][16], b[2][16];
+    float a[NI][16], b[2][16];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      fetch<MA>(Ac, wm * 64 + i * 32, lane, a[i]);
-      fetch<MB>(Bc, wn * 64 + i * 32, lane, b[i]);
-    }
+    for (int i = 0; i < NI; ++i) fetch<MA>(Ac, row0 + i * 32, lane, a[i]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) fetch<MB>(Bc, wn * 64 + j * 32, lane, b[j]);
 #pragma unroll
     for (int s = 0; s < 16; ++s)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][s], b[j][s], acc[i][j], 0, 0, 0);
     if (k0 + BK < k_hi) {
@@ -270,12 +275,12 @@ __device__ __forceinline__ void gemm_tile(const GemmProblem& P, int m0, int n0, 
   // per element, and whole 512-byte row segments per wave.
   float* T = As;   // [BM][TPAD]
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = wm * 64 + i * 32 + 8 * (r / 4) + 4 * (lane / 32) + r % 4;
+        const int row = row0 + i * 32 + 8 * (r / 4) + 4 * (lane / 32) + r % 4;
         T[row * TPAD + wn * 64 + j * 32 + lane % 32] = acc[i][j][r];
       }
   __syncthreads();
@@ -331,11 +336,16 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(GemmGroup g) {
   const int k_hi = min(P.K, k_lo + g.kchunk[pi]);
   const bool vec_out = g.vec_out[pi] != 0;
   switch (g.mode[pi]) {
-    case kK * 3 + kK: gemm_tile<kK, kK>(P, m0, n0, k_lo, k_hi, ks, As, Bs, vec_out); break;
-    case kK * 3 + kR: gemm_tile<kK, kR>(P, m0, n0, k_lo, k_hi, ks, As, Bs, vec_out); break;
-    case kR * 3 + kR: gemm_tile<kR, kR>(P, m0, n0, k_lo, k_hi, ks, As, Bs, vec_out); break;
-    case kR * 3 + kK: gemm_tile<kR, kK>(P, m0, n0, k_lo, k_hi, ks, As, Bs, vec_out); break;
-    default: gemm_tile<kG, kG>(P, m0, n0, k_lo, k_hi, ks, As, Bs, vec_out); break;
+    case kK * 3 + kK: gemm_tile<kK, kK, 2>(P, m0, n0, k_lo, k_hi, ks, As, Bs, vec_out); break;
+    case kK * 3 + kR: gemm_tile<kK, kR, 2>(P, m0, n0, k_lo, k_hi, ks, As, Bs, vec_out); break;
+    case kR * 3 + kR: gemm_tile<kR, kR, 2>(P, m0, n0, k_lo, k_hi, ks, As, Bs, vec_out); break;
+    case kR * 3 + kK: gemm_tile<kR, kK, 2>(P, m0, n0, k_lo, k_hi, ks, As, Bs, vec_out); break;
+    case kNarrow + kK * 3 + kK: gemm_tile<kK, kK, 1>(P, m0, n0, k_lo, k_hi, ks, As, Bs, vec_out); break;
+    case kNarrow + kK * 3 + kR: gemm_tile<kK, kR, 1>(P, m0, n0, k_lo, k_hi, ks, As, Bs, vec_out); break;
+    case kNarrow + kR * 3 + kR: gemm_tile<kR, kR, 1>(P, m0, n0, k_lo, k_hi, ks, As, Bs, vec_out); break;
+    case kNarrow + kR * 3 + kK: gemm_tile<kR, kK, 1>(P, m0, n0, k_lo, k_hi, ks, As, Bs, vec_out); break;
+    case kNarrow + kG * 3 + kG: gemm_tile<kG, kG, 1>(P, m0, n0, k_lo, k_hi, ks, As, Bs, vec_out); break;
+    default: gemm_tile<kG, kG, 2>(P, m0, n0, k_lo, k_hi, ks, As, Bs, vec_out); break;
   }
 }
 
@@ -431,7 +441,7 @@ void gemm_group(const GemmGroup& g0, hipStream_t st) {
     P.C.mdiv = magic(P.C.div);
     P.C2.mdiv = magic(P.C2.div);
     const int ma = stage_mode(P.A, P.M, P.K), mb = stage_mode(P.Bt, P.N, P.K);
-    g.mode[i] = (ma == kG || mb == kG) ? kG * 3 + kG : ma * 3 + mb;
+    g.mode[i] = ((ma == kG || mb == kG) ? kG * 3 + kG : ma * 3 + mb) + (P.N <= BN / 2 ? kNarrow : 0);
     auto out_vec = [&](const GOut& o) {
       return !o.p || (aligned16(o.p) && o.s1 % 4 == 0 && (o.div == 1 || o.s2 % 4 == 0));
     };

@@ -728,6 +728,13 @@ def main():
             "fwd_GBs_compulsory": cw_f / (fw * 1e-3) / 1e9, "vjp_GBs_compulsory": cw_v / (vw * 1e-3) / 1e9,
             "fwd_plus_vjp_frac_hbm_compulsory": (cw_f + cw_v) / ((fw + vw) * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "w_bytes": E * P * CHANNELS * 4}
+        # without x_grad the VJP runs receiver-side: w read, w_bar written,
+        # each cotangent row read once (compulsory: w, w_bar, g, x, graph,
+        # the per-edge position terms written and summed)
+        vr = timed(lambda: fc.fc_edge_conv_vjp_w(desc, graph, pos, None, x, w_e, g, None, pb, wb_e, ws))
+        cr = 2 * E * P * CHANNELS * 4 + N_NODES * (n_in + n_out) * CHANNELS * 4 + E * 4 * 2 + E * 12 * 3
+        out["explicit_weights"]["vjp_pos_w_only_ms"] = vr
+        out["explicit_weights"]["vjp_pos_w_only_GBs_compulsory"] = cr / (vr * 1e-3) / 1e9
         # VJP-of-VJP with every cotangent (v_x, v_pos, v_w) and every output
         # (g_hat, x_hat, pos_hat, w_hat); w, v_w and w_hat each move w_bytes
         v_x = torch.randn(x.shape, device=dev, generator=gen)

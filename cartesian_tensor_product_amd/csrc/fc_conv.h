@@ -82,6 +82,9 @@ struct VjpWorkspace {
 };
 
 void launch_vjp_combine(const ConvArgs& a, const VjpWorkspace& w, int nin, hipStream_t st);
+// pos_bar[v] = sum over v's out-edges of rbar - sum over its in-edges (the
+// receiver-side VJP's position gradient; needs rowptr, t_rowptr, t_edge)
+void launch_pos_from_edges(const ConvArgs& a, const float* rbar, hipStream_t st);
 
 // The launch sequences of one configuration's VJP-of-VJP passes (g_hat,
 // W_hat, and the sender pass without / with a feature cotangent).

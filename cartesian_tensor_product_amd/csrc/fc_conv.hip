@@ -54,6 +54,44 @@ __global__ __launch_bounds__(256) void conv_vjp_combine_kernel(int S, int row, c
   }
 }
 
+// pos_bar[v] = sum_{e out of v} r_bar_e - sum_{e into v} r_bar_e, one wave
+// per node, fixed order (after the receiver-side VJP, which stores r_bar per
+// edge only).
+__global__ __launch_bounds__(kWave) void conv_pos_from_edges_kernel(int N, const int* __restrict__ rowptr,
+                                                                    const int* __restrict__ t_rowptr,
+                                                                    const int* __restrict__ t_edge,
+                                                                    const float* __restrict__ rbar,
+                                                                    float* __restrict__ pos_bar) {
+  const int v = blockIdx.x, lane = threadIdx.x;
+  float s[3] = {0.f, 0.f, 0.f};
+  for (int i = t_rowptr[v] + lane; i < t_rowptr[v + 1]; i += kWave) {
+    const size_t e = (size_t)t_edge[i];
+    s[0] += rbar[3 * e];
+    s[1] += rbar[3 * e + 1];
+    s[2] += rbar[3 * e + 2];
+  }
+  for (int e = rowptr[v] + lane; e < rowptr[v + 1]; e += kWave) {
+    s[0] -= rbar[3 * (size_t)e];
+    s[1] -= rbar[3 * (size_t)e + 1];
+    s[2] -= rbar[3 * (size_t)e + 2];
+  }
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s[i] += __shfl_xor(s[i], o);
+  }
+  if (lane == 0) {
+    pos_bar[3 * (size_t)v] = s[0];
+    pos_bar[3 * (size_t)v + 1] = s[1];
+    pos_bar[3 * (size_t)v + 2] = s[2];
+  }
+}
+
+void launch_pos_from_edges(const ConvArgs& a, const float* rbar, hipStream_t st) {
+  hipLaunchKernelGGL(conv_pos_from_edges_kernel, dim3(a.N), dim3(kWave), 0, st, a.N, a.rowptr, a.t_rowptr, a.t_edge,
+                     rbar, a.pos_bar);
+}
+
 void launch_vjp_combine(const ConvArgs& a, const VjpWorkspace& w, int nin, hipStream_t st) {
   if (w.S == 1 && !a.pos_bar) return;
   hipLaunchKernelGGL(conv_vjp_combine_kernel, dim3(a.N), dim3(256), 0, st, w.S, nin * a.C, a.rowptr, w.rbar,

@@ -935,6 +935,199 @@ __global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_sender_kernel(
   }
 }
 
+// ==================================================== receiver-side VJP ====
+// Without x_bar (the message blocks ask for the forces and w_bar only) the
+// VJP needs no sender order: a block of NW = ceil(C/64) waves holds all
+// channels of receiver u with its cotangent rows g[u] in registers and
+// walks u's incoming edges like the forward, gathering the senders' x.  Per
+// edge and path it forms v2 = VJP2_p(g, x) per lane and
+//   y_bar_e        = sum_{p,k} w_p v2_p        (over lanes, DPP rows + LDS)
+//   w_bar[e, p, k] = <v2_p, y>                 (stored when wb_out)
+// and the edge lane turns y_bar_e into r_bar_e = (I - r_hat r_hat^T)/r
+// grad_n(y_bar . y), stored per edge; launch_pos_from_edges then sums the
+// out-edges minus the in-edges of every node in a fixed order.  Each row of
+// g is read once per receiver instead of once per incoming edge in sender
+// order, where the rows of the receivers in flight on an XCD outgrow its L2.
+// Explicit per-edge weights only (the weights w [E][P][C] are read in edge
+// order, w_bar written in edge order).
+template <int LIN, int LEDGE, int LOUT, bool NEED_POS, int CH>
+__global__ __launch_bounds__(kMaxVjpWaves * kWave) void conv_vjp_recv_kernel(
+    int N, int C, const int* __restrict__ rowptr, const int* __restrict__ sender,
+    const float* __restrict__ pos, const float* __restrict__ shift, const float* __restrict__ x,
+    const float* __restrict__ W, const float* __restrict__ g, float* __restrict__ rbar,
+    float* __restrict__ wb_out) {
+  using Cfg = ConvCfg<LIN, LEDGE, LOUT>;
+  using Sh = VjpShape<LIN, LEDGE, LOUT>;
+  using EP = typename Sh::EP;
+  constexpr int NIN = Cfg::NIN, NE = Cfg::NE, P = Cfg::P, NOUT = Cfg::NOUT;
+  constexpr int REC = Sh::REC, NRED = Sh::NRED, NY = EP::NY;
+  using GS = PathGroups<Cfg, Sh::budget>;
+  extern __shared__ float lds[];
+  float* geo = lds;                      // [CH][REC]
+  float* part = lds + CH * REC;          // [NW][CH edges][NRED][4 rows]
+
+  const int NW = blockDim.x / kWave;
+  const int u = xcd_node(blockIdx.x, N);
+  const int tid = threadIdx.x;
+  const int wv = tid / kWave, lane = tid % kWave;
+  const int k = tid;
+  const bool act = k < C;
+  const int kk = act ? k : 0;
+  const int voff = kk * 4;
+  const int e0 = rowptr[u], e1 = rowptr[u + 1];
+  const float pux = pos[3 * u], puy = pos[3 * u + 1], puz = pos[3 * u + 2];
+
+  // one sweep over u's edges per path group; the groups' parts of each
+  // edge's position term are added in group order
+  static_for<GS::n>([&](auto gi) {
+    using G = typename GS::template group<gi>;
+    constexpr bool FIRST = gi == 0;
+    float gv[G::NR];
+    {
+      const float* gu = g + (size_t)u * NOUT * C + kk;
+      static_for<G::NP>([&](auto pi) {
+        constexpr int p = G::p0 + pi;
+        if constexpr (!G::owner(p)) return;
+        static_for<ncomp(Cfg::paths[p].L)>([&](auto c) {
+          constexpr int row = Cfg::row(p, c), li = G::loff(p) + c;
+          gv[li] = gu[(size_t)row * C];
+        });
+      });
+    }
+    for (int base = e0; base < e1; base += CH) {
+      const int cnt = min(CH, e1 - base);
+      if (wv == 0 && lane < cnt) {
+        const int e = base + lane;
+        const int s = sender[e];
+        float rx = pos[3 * s] - pux, ry = pos[3 * s + 1] - puy, rz = pos[3 * s + 2] - puz;
+        if (shift) {
+          rx += shift[3 * e];
+          ry += shift[3 * e + 1];
+          rz += shift[3 * e + 2];
+        }
+        const float r = sqrtf(rx * rx + ry * ry + rz * rz);
+        const float inv = r > 0.f ? 1.f / r : 0.f;
+        float y[NE];
+        direction_tensors<LEDGE>(rx * inv, ry * inv, rz * inv, y);
+        float* rec = geo + lane * REC;
+        EP::fill(y, rec);
+        rec[NY] = r > 0.f ? 1.f : 0.f;   // an edge without a direction takes no part
+        rec[NY + 2 * kNB] = __int_as_float(s);
+      }
+      __syncthreads();
+      // the weights of edge j + 1 are requested after the gather of edge j
+      float wn[G::NP];
+      if (cnt > 0) {
+        const float* wrow = W + (size_t)base * P * C + kk;
+        static_for<G::NP>([&](auto pi) { wn[pi] = wrow[(size_t)(G::p0 + pi) * C]; });
+      }
+      for (int j = 0; j < cnt; ++j) {
+        const float* rec = geo + j * REC;
+        const int s = uniform_int(__float_as_int(rec[NY + 2 * kNB]));
+        const auto xs = node_rsrc(x, s, NIN * C);
+        float xv[NIN];
+        static_for<NIN>([&](auto c) { xv[c] = buf_load(xs, voff, c * C * 4); });
+        float we[G::NP];
+        static_for<G::NP>([&](auto pi) { we[pi] = act ? rec[NY] * wn[pi] : 0.f; });
+        if (j + 1 < cnt) {
+          const float* wrow = W + (size_t)(base + j + 1) * P * C + kk;
+          static_for<G::NP>([&](auto pi) { wn[pi] = wrow[(size_t)(G::p0 + pi) * C]; });
+        }
+        float yb[NE];
+        static_for<NE>([&](auto c) { yb[c] = 0.f; });
+        static_for<G::NP>([&](auto pi) {
+          constexpr int p = G::p0 + pi;
+          constexpr PathInfo PI = Cfg::paths[p];
+          constexpr int n2 = ncomp(PI.l2), o1 = rank_off(PI.l1), o2 = rank_off(PI.l2);
+          constexpr int lo = G::loff(p);
+          constexpr int tb = tab::kTermBegin[PI.type], te = tab::kTermBegin[PI.type + 1];
+          // v2[b2] = sum_terms c g[a] x[b1]  (VJP_2(g, x))
+          float v2[n2];
+          static_for<te - tb>([&](auto ti) {
+            constexpr int tt = tb + ti;
+            constexpr tab::Term T = tab::kTerms[tt];
+            constexpr float ac = T.c < 0.f ? -T.c : T.c;
+            float cx = ac == 1.f ? xv[o1 + T.b1] : ac * xv[o1 + T.b1];
+            if constexpr (T.c < 0.f) cx = -cx;
+            if constexpr (T.f2) v2[T.b2] = gv[lo + T.a] * cx;
+            else v2[T.b2] = fmaf(gv[lo + T.a], cx, v2[T.b2]);
+          });
+          float wbar = 0.f;
+          static_for<n2>([&](auto c) {
+            if constexpr (NEED_POS) yb[o2 + c] = fmaf(we[pi], v2[c], yb[o2 + c]);
+            wbar = fmaf(v2[c], rec[o2 + c], wbar);
+          });
+          if (wb_out && act) wb_out[(size_t)(base + j) * P * C + (size_t)p * C + k] = rec[NY] * wbar;
+        });
+        if constexpr (NEED_POS) {
+          float* dst = part + ((size_t)(wv * CH + j) * NRED) * 4 + (lane >> 4);
+          static_for<NE>([&](auto c) {
+            if constexpr (G::uses_comp(c)) {
+              const float t = row_sum16(yb[c]);
+              if ((lane & 15) == 0) dst[c * 4] = t;
+            }
+          });
+        }
+      }
+      __syncthreads();
+      if constexpr (NEED_POS) {
+        if (wv == 0 && lane < cnt) {
+          const int e = base + lane;
+          const int s = sender[e];
+          float tot[NE];
+          static_for<NE>([&](auto i) { tot[i] = 0.f; });
+          for (int w2 = 0; w2 < NW; ++w2) {
+            const float4* src = reinterpret_cast<const float4*>(part + ((size_t)(w2 * CH + lane) * NRED) * 4);
+            static_for<NE>([&](auto i) {
+              if constexpr (G::uses_comp(i)) {
+                const float4 q = src[i];
+                tot[i] += (q.x + q.y) + (q.z + q.w);
+              }
+            });
+          }
+          float rx = pos[3 * s] - pux, ry = pos[3 * s + 1] - puy, rz = pos[3 * s + 2] - puz;
+          if (shift) {
+            rx += shift[3 * e];
+            ry += shift[3 * e + 1];
+            rz += shift[3 * e + 2];
+          }
+          const float r = sqrtf(rx * rx + ry * ry + rz * rz);
+          float ox = 0.f, oy = 0.f, oz = 0.f;
+          if (r > 0.f) {
+            const float inv = 1.f / r;
+            const float nx = rx * inv, ny = ry * inv, nz = rz * inv;
+            float dy[3 * NE];
+            direction_tensor_grads<LEDGE>(nx, ny, nz, dy);
+            float gx = 0.f, gy = 0.f, gz = 0.f;
+            static_for<NE>([&](auto c) {
+              if constexpr (G::uses_comp(c)) {
+                gx = fmaf(tot[c], dy[3 * c], gx);
+                gy = fmaf(tot[c], dy[3 * c + 1], gy);
+                gz = fmaf(tot[c], dy[3 * c + 2], gz);
+              }
+            });
+            const float gn = gx * nx + gy * ny + gz * nz;
+            ox = (gx - gn * nx) * inv;
+            oy = (gy - gn * ny) * inv;
+            oz = (gz - gn * nz) * inv;
+          }
+          float* re = rbar + 3 * (size_t)e;
+          if constexpr (FIRST) {
+            re[0] = ox;
+            re[1] = oy;
+            re[2] = oz;
+          } else {
+            re[0] += ox;
+            re[1] += oy;
+            re[2] += oz;
+          }
+        }
+        __syncthreads();
+      }
+    }
+  });
+}
+
 template <int LIN, int LEDGE, int LOUT>
 void launch_vjp(const ConvArgs& a, hipStream_t st) {
   const bool nx = a.x_bar != nullptr, np = a.pos_bar != nullptr;
@@ -942,10 +1135,28 @@ void launch_vjp(const ConvArgs& a, hipStream_t st) {
   const VjpWorkspace wsl(a.N, a.E, a.C, nrank(LIN), ConvCfg<LIN, LEDGE, LOUT>::P, true, a.rbar);
   if (a.W_bar && !a.w_edge) launch_wgrad<LIN, LEDGE, LOUT>(a, wsl.w_part, st);
   if (!nx && !np && !(a.w_edge && a.w_edge_bar)) return;
+  using Sh = VjpShape<LIN, LEDGE, LOUT>;
+  if (a.w_edge && !nx) {
+    // explicit weights without x_bar: receiver order (each g row read once)
+    const int ch = Sh::CH > 32 && Sh::lds_bytes(np ? nw : 0, Sh::CH) > kLdsBytes / 4 ? 32 : Sh::CH;
+#define FC_VJP_RECV(NP, CHV)                                                                                         \
+  hipLaunchKernelGGL((conv_vjp_recv_kernel<LIN, LEDGE, LOUT, NP, CHV>), dim3(a.N), dim3(nw * kWave),                   \
+                     Sh::lds_bytes(NP ? nw : 0, CHV), st, a.N, a.C, a.rowptr, a.sender, a.pos, a.shift, a.x, a.w_edge,  \
+                     a.g, wsl.rbar, a.w_edge_bar)
+    if (ch == 32) {
+      if (np) FC_VJP_RECV(true, 32);
+      else FC_VJP_RECV(false, 32);
+    } else if constexpr (Sh::CH > 32) {
+      if (np) FC_VJP_RECV(true, Sh::CH);
+      else FC_VJP_RECV(false, Sh::CH);
+    }
+#undef FC_VJP_RECV
+    if (np) launch_pos_from_edges(a, wsl.rbar, st);
+    return;
+  }
   float* xo = wsl.S == 1 ? a.x_bar : wsl.x_part;
   float* po = wsl.S == 1 ? a.pos_bar : wsl.p_part;
   dim3 grid(a.N, wsl.S), block(nw * kWave);
-  using Sh = VjpShape<LIN, LEDGE, LOUT>;
   // slices of at most 32 edges on average (e.g. 128 or fewer neighbours in
   // four slices) stage 32 edges per chunk when the block's LDS at 64 would
   // keep four blocks from sharing a CU (it then holds half as much; at ranks

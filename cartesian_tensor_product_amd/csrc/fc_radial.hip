@@ -76,6 +76,58 @@ __device__ __forceinline__ void features(float r, float rmax, float* phi, float*
   }
 }
 
+// acc[i] = sum_j h[j] w2[j][j0 + i] for i < NJ (j ascending, as a dot product
+// per output would add them): the loop over j is outside, so that every
+// 128-bit LDS read of a W2 row segment feeds four accumulators instead of one
+// scalar read per FMA.
+template <int NJ>
+__device__ __forceinline__ void layer2(const float* h, const float* w2, int j0, float* acc) {
+#pragma unroll
+  for (int i = 0; i < NJ; ++i) acc[i] = 0.f;
+#pragma unroll
+  for (int j = 0; j < kRadHidden; ++j) {
+    const float4* row = reinterpret_cast<const float4*>(w2 + j * kRadHidden + j0);
+#pragma unroll
+    for (int q = 0; q < NJ / 4; ++q) {
+      const float4 w = row[q];
+      acc[4 * q] = fmaf(h[j], w.x, acc[4 * q]);
+      acc[4 * q + 1] = fmaf(h[j], w.y, acc[4 * q + 1]);
+      acc[4 * q + 2] = fmaf(h[j], w.z, acc[4 * q + 2]);
+      acc[4 * q + 3] = fmaf(h[j], w.w, acc[4 * q + 3]);
+    }
+  }
+}
+
+// h1 = SiLU(phi W1) (and its r-derivative with dphi), W1 rows read as float4.
+template <bool D>
+__device__ __forceinline__ void layer1(const float* phi, const float* dphi, const float* w1, float* h1, float* dh1) {
+  float a[kRadHidden], da[D ? kRadHidden : 1];
+#pragma unroll
+  for (int j = 0; j < kRadHidden; ++j) {
+    a[j] = 0.f;
+    if constexpr (D) da[j] = 0.f;
+  }
+#pragma unroll
+  for (int n = 0; n < kRadFeat; ++n) {
+    const float4* row = reinterpret_cast<const float4*>(w1 + n * kRadHidden);
+#pragma unroll
+    for (int q = 0; q < kRadHidden / 4; ++q) {
+      const float4 w = row[q];
+      const float wq[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        a[4 * q + t] = fmaf(phi[n], wq[t], a[4 * q + t]);
+        if constexpr (D) da[4 * q + t] = fmaf(dphi[n], wq[t], da[4 * q + t]);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kRadHidden; ++j) {
+    h1[j] = silu(a[j]);
+    if constexpr (D) dh1[j] = silu_grad(a[j]) * da[j];
+  }
+}
+
 __device__ __forceinline__ void load_hidden_weights(const float* __restrict__ W, float* w1, float* w2) {
   for (int i = threadIdx.x; i < kW1; i += blockDim.x) w1[i] = W[i];
   for (int i = threadIdx.x; i < kW2; i += blockDim.x) w2[i] = W[kW1 + i];
@@ -96,19 +148,11 @@ __global__ __launch_bounds__(kRadBlock) void radial_hidden_kernel(int E, float r
   edge_vec(e, receiver, sender, pos, shift, rv);
   features(sqrtf(rv[0] * rv[0] + rv[1] * rv[1] + rv[2] * rv[2]), rmax, phi, dphi);
   float h1[kRadHidden];
+  layer1<false>(phi, dphi, w1, h1, nullptr);
+  float a2[kRadHidden];
+  layer2<kRadHidden>(h1, w2, 0, a2);
 #pragma unroll
-  for (int j = 0; j < kRadHidden; ++j) {
-    float a = 0.f;
-#pragma unroll
-    for (int n = 0; n < kRadFeat; ++n) a = fmaf(phi[n], w1[n * kRadHidden + j], a);
-    h1[j] = silu(a);
-  }
-  for (int j2 = 0; j2 < kRadHidden; ++j2) {
-    float a = 0.f;
-#pragma unroll
-    for (int j = 0; j < kRadHidden; ++j) a = fmaf(h1[j], w2[j * kRadHidden + j2], a);
-    h2t[(size_t)j2 * ld + e] = silu(a);
-  }
+  for (int j2 = 0; j2 < kRadHidden; ++j2) h2t[(size_t)j2 * ld + e] = silu(a2[j2]);
 }
 
 // Row e of hh: h2 (64 floats), then dh2/dr (64 floats), by forward-mode
@@ -128,33 +172,25 @@ __global__ __launch_bounds__(kRadBlock) void radial_hidden_rows_kernel(int E, fl
   edge_vec(e, receiver, sender, pos, shift, rv);
   features(sqrtf(rv[0] * rv[0] + rv[1] * rv[1] + rv[2] * rv[2]), rmax, phi, dphi);
   float h1[kRadHidden], dh1[kRadHidden];
-#pragma unroll
-  for (int j = 0; j < kRadHidden; ++j) {
-    float a = 0.f, da = 0.f;
-#pragma unroll
-    for (int n = 0; n < kRadFeat; ++n) {
-      a = fmaf(phi[n], w1[n * kRadHidden + j], a);
-      da = fmaf(dphi[n], w1[n * kRadHidden + j], da);
-    }
-    h1[j] = silu(a);
-    dh1[j] = silu_grad(a) * da;
-  }
+  layer1<true>(phi, dphi, w1, h1, dh1);
   float4* row = reinterpret_cast<float4*>(hh + (size_t)e * kRadRow);
-  for (int j4 = 0; j4 < kRadHidden; j4 += 4) {
-    float h[4], dh[4];
+  // the second layer and its derivative in quarters of 16 outputs (registers)
+#pragma unroll 1
+  for (int part = 0; part < 4; ++part) {
+    float a[16], da[16];
+    layer2<16>(h1, w2, 16 * part, a);
+    layer2<16>(dh1, w2, 16 * part, da);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      float a = 0.f, da = 0.f;
+      float h[4], dh[4];
 #pragma unroll
-      for (int j = 0; j < kRadHidden; ++j) {
-        a = fmaf(h1[j], w2[j * kRadHidden + j4 + q], a);
-        da = fmaf(dh1[j], w2[j * kRadHidden + j4 + q], da);
+      for (int t = 0; t < 4; ++t) {
+        h[t] = silu(a[4 * q + t]);
+        dh[t] = silu_grad(a[4 * q + t]) * da[4 * q + t];
       }
-      h[q] = silu(a);
-      dh[q] = silu_grad(a) * da;
+      row[4 * part + q] = make_float4(h[0], h[1], h[2], h[3]);
+      row[(kRadHidden + 16 * part) / 4 + q] = make_float4(dh[0], dh[1], dh[2], dh[3]);
     }
-    row[j4 / 4] = make_float4(h[0], h[1], h[2], h[3]);
-    row[(kRadHidden + j4) / 4] = make_float4(dh[0], dh[1], dh[2], dh[3]);
   }
 }
 
@@ -178,22 +214,23 @@ __global__ __launch_bounds__(kRadBlock) void radial_back_kernel(
   float ab2[kRadHidden];
   {
     float h1[kRadHidden];
+    layer1<false>(phi, dphi, w1, h1, nullptr);
+    if (a1bt) {
 #pragma unroll
-    for (int j = 0; j < kRadHidden; ++j) {
-      float a = 0.f;
-#pragma unroll
-      for (int n = 0; n < kRadFeat; ++n) a = fmaf(phi[n], w1[n * kRadHidden + j], a);
-      h1[j] = silu(a);
-      if (a1bt) h1t[(size_t)j * E + e] = h1[j];
+      for (int j = 0; j < kRadHidden; ++j) h1t[(size_t)j * E + e] = h1[j];
     }
-    const float* hb = hbar + (size_t)e * kRadHidden;
+    layer2<kRadHidden>(h1, w2, 0, ab2);
+    const float4* hb = reinterpret_cast<const float4*>(hbar + (size_t)e * kRadHidden);
 #pragma unroll
-    for (int j2 = 0; j2 < kRadHidden; ++j2) {
-      float a = 0.f;
+    for (int q = 0; q < kRadHidden / 4; ++q) {
+      const float4 h = hb[q];
+      const float hq[4] = {h.x, h.y, h.z, h.w};
 #pragma unroll
-      for (int j = 0; j < kRadHidden; ++j) a = fmaf(h1[j], w2[j * kRadHidden + j2], a);
-      ab2[j2] = hb[j2] * silu_grad(a);
-      if (a2bt) a2bt[(size_t)j2 * E + e] = ab2[j2];
+      for (int t = 0; t < 4; ++t) ab2[4 * q + t] = hq[t] * silu_grad(ab2[4 * q + t]);
+    }
+    if (a2bt) {
+#pragma unroll
+      for (int j2 = 0; j2 < kRadHidden; ++j2) a2bt[(size_t)j2 * E + e] = ab2[j2];
     }
   }
   // pass 2, one hidden unit j at a time: h1_bar_j = a2_bar . W2[j, :],

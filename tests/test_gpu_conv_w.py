@@ -99,6 +99,35 @@ def test_explicit_weights_zero_length_edge_and_partial_outputs():
         assert_close(want[0], out[i].cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("ranks,C,mode", [((0, 0, 0), 24, ""), ((1, 1, 1), 24, ""), ((0, 3, 3), 24, ""),
+                                          ((3, 3, 3), 24, ""), ((4, 4, 4), 24, ""), ((5, 5, 5), 16, ""),
+                                          ((2, 2, 2), 65, ""), ((2, 2, 2), 200, ""), ((2, 2, 2), 24, "allp"),
+                                          ((3, 3, 3), 24, "summed")])
+def test_explicit_weights_receiver_side_vjp(ranks, C, mode):
+    """Without x_grad the VJP walks each receiver's incoming edges (its
+    cotangent rows read once) and sums the per-edge position terms per node
+    afterwards: positions and w_grad together and each alone, against the
+    oracle."""
+    from cartesian_tensor_product_amd import flashcart as fc
+    allp, summed = mode == "allp", mode == "summed"
+    spec = conv.ConvSpec(*ranks, 6.0, all_parities=allp, sum_paths=summed)
+    d = inputs.edge_conv_inputs(13, 50, 20, 5.5, C, spec.n_in, spec.n_paths, spec.n_out, with_edge_w=True)
+    flags = fc.FC_CONV_ALL_PARITIES if allp else (fc.FC_CONV_SUM_PATHS if summed else 0)
+    gc = GpuConvW(ranks, d, C, 6.0, flags=flags)
+    _, _, po, wo = oracle(spec, d)
+    _, pb, wb = gc.vjp(("pos", "w"))
+    torch.cuda.synchronize()
+    assert_close("pos_grad", pb.cpu().numpy(), po)
+    assert_close("w_grad", wb.cpu().numpy(), wo)
+    for want, ref, i in ((("pos",), po, 1), (("w",), wo, 2)):
+        out = gc.vjp(want)
+        torch.cuda.synchronize()
+        assert_close(want[0], out[i].cpu().numpy(), ref)
+    again = gc.vjp(("pos", "w"))
+    torch.cuda.synchronize()
+    assert torch.equal(again[1], pb) and torch.equal(again[2], wb)
+
+
 def test_explicit_weights_microbenchmark_sampled():
     """1024 nodes x 128 neighbours x 128 channels, ranks <= 2, w [E, 11, 128]
     (738 MB): sampled nodes element by element, and the per-edge weight
@@ -117,6 +146,11 @@ def test_explicit_weights_microbenchmark_sampled():
     assert_close("x_grad", xb.cpu().numpy()[nodes], xo[nodes])
     assert_close("pos_grad", pb.cpu().numpy()[nodes], po[nodes])
     assert_close("w_grad", wb[torch.from_numpy(edges).cuda()].cpu().numpy(), wo[edges])
+    # the receiver-side VJP (no x_grad) at the same size
+    _, pr, wr = gc.vjp(("pos", "w"))
+    torch.cuda.synchronize()
+    assert_close("pos_grad (receiver side)", pr.cpu().numpy()[nodes], po[nodes])
+    assert_close("w_grad (receiver side)", wr[torch.from_numpy(edges).cuda()].cpu().numpy(), wo[edges])
     a = [gc.fwd(), *gc.vjp()]
     torch.cuda.synchronize()
     for u, v in zip(a, [z, xb, pb, wb]):

@@ -166,7 +166,7 @@ def radial_mlp_workload(dev):
                                                                       ws1))
     r["fused_speedup_fwd_plus_vjp"] = ((r["materialized"]["fwd_ms"] + r["materialized"]["vjp_x_pos_ms"]) /
                                       (r["fused"]["fwd_ms"] + r["fused"]["vjp_x_pos_ms"]))
-    r["default"] = "fused (forward and VJP at these ranks)"
+    r["default"] = "forward fused, VJP materialised (at these ranks)"
     out["conv_radial_mlp_rank2_1024n_128c_128nbr"] = r
     del w, z, xb, pb, mb, ws1, mlp
     return out

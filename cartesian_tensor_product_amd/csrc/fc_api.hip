@@ -137,17 +137,18 @@ fc::ConvArgs make_args(const fc_conv_desc* d, const fc_graph* g, const float* po
 
 
 // Where the radial network's output layer runs fused in the convolution's
-// lanes (w = h2 W3 never stored): the forward wherever the rank set is
-// instantiated for it; the VJP where the rank set's own VJP work makes it
-// the faster choice, or with FC_CONV_MLP_FUSE; neither with
+// lanes (w = h2 W3 never stored), for rank sets instantiated for it: the
+// forward where it was measured faster (conv_mlp_fwd_fused) or with
+// FC_CONV_MLP_FUSE; the VJP with FC_CONV_MLP_FUSE only; neither with
 // FC_CONV_MLP_MATERIALIZE.
-bool mlp_fuse_fwd(const fc_conv_desc* d) {
+bool mlp_fusable(const fc_conv_desc* d) {
   return !(d->flags & FC_CONV_MLP_MATERIALIZE) && fc::conv_mlp_supported(d->l_in, d->l_edge, lout_key(d));
 }
-bool mlp_fuse_vjp(const fc_conv_desc* d) {
-  return mlp_fuse_fwd(d) &&
-         ((d->flags & FC_CONV_MLP_FUSE) || fc::conv_mlp_vjp_fused(d->l_in, d->l_edge, lout_key(d)));
+bool mlp_fuse_fwd(const fc_conv_desc* d) {
+  return mlp_fusable(d) &&
+         ((d->flags & FC_CONV_MLP_FUSE) || fc::conv_mlp_fwd_fused(d->l_in, d->l_edge, lout_key(d)));
 }
+bool mlp_fuse_vjp(const fc_conv_desc* d) { return mlp_fusable(d) && (d->flags & FC_CONV_MLP_FUSE); }
 
 // Workspace of the convolution weighted by the radial network, for op 0
 // (forward), 1 (VJP, any outputs) or 2 (VJP without the network's weight

@@ -109,8 +109,8 @@ bool conv_vv_w_supported(int l_in, int l_edge, int l_out);
 // not instantiated for these ranks.
 bool conv_mlp_dispatch(int op, int l_in, int l_edge, int l_out, const ConvArgs& args, hipStream_t stream);
 bool conv_mlp_supported(int l_in, int l_edge, int l_out);
-// whether the fused VJP is the default for these ranks (the convolution's
-// own VJP work is at least a third of the 64 P FMAs that form w)
-bool conv_mlp_vjp_fused(int l_in, int l_edge, int l_out);
+// whether the fused forward is the default for these ranks (measured faster
+// than the materialised one; the VJP is materialised by default)
+bool conv_mlp_fwd_fused(int l_in, int l_edge, int l_out);
 
 }  // namespace fc

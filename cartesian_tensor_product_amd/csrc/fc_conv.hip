@@ -182,9 +182,9 @@ bool conv_mlp_supported(int l_in, int l_edge, int l_out) {
   }
 }
 
-bool conv_mlp_vjp_fused(int l_in, int l_edge, int l_out) {
+bool conv_mlp_fwd_fused(int l_in, int l_edge, int l_out) {
   switch (l_in * 1024 + l_edge * 32 + l_out) {
-    FC_CONV_MLP_VJP_FUSED_CONFIGS(FC_CONV_SUPPORTED)
+    FC_CONV_MLP_FWD_FUSED_CONFIGS(FC_CONV_SUPPORTED)
     default: return false;
   }
 }

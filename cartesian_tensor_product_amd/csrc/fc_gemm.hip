@@ -39,6 +39,7 @@ static_assert(BM * TPAD <= 4 * SMEM, "the epilogue tile reuses the operand buffe
 
 enum StageMode { kK = 0, kR = 1, kG = 2 };
 constexpr int kNarrow = 16;   // added to a problem's mode: N <= 64, narrow wave layout
+constexpr int kNLoop = 32;    // added to a problem's mode: K <= 2 BK, one block walks every N tile
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
@@ -317,16 +318,114 @@ __device__ __forceinline__ void gemm_tile(const GemmProblem& P, int m0, int n0, 
   }
 }
 
+// Short reductions (K <= 2 BK, e.g. the radial network's output layer,
+// K = 64) with several N tiles: one block per M tile keeps its A tile (both
+// K tiles) in LDS and walks every N tile; after a tile's products it loads
+// the next tile's B operand, and stores the result straight from the
+// accumulators (two 128-byte row segments per wave store) while those loads
+// are in flight.  Plain outputs only (one row stride, no accumulation, no
+// second output).  The general path's per-tile prologue and LDS epilogue
+// dominated there: two K tiles of products per block.
+template <int MA, int MB>
+__device__ __forceinline__ void gemm_tile_nloop(const GemmProblem& P, int m0, int ntiles, float* As, float* Bs) {
+  const int wv = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int wm = wv % 2, wn = wv / 2;
+  const int nkt = (P.K + BK - 1) / BK;   // 1 or 2
+  {
+    Stager<MA> sa;
+    sa.init(P.A, P.M, m0);
+    for (int kt = 0; kt < nkt; ++kt) {
+      sa.load(P.A, P.M, m0, kt * BK, P.K);
+      sa.store(As + kt * SMEM);
+    }
+  }
+  {
+    Stager<MB> sb;
+    sb.init(P.Bt, P.N, 0);
+    for (int kt = 0; kt < nkt; ++kt) {
+      sb.load(P.Bt, P.N, 0, kt * BK, P.K);
+      sb.store(Bs + kt * SMEM);
+    }
+  }
+  __syncthreads();
+  for (int tn = 0; tn < ntiles; ++tn) {
+    const int n0 = tn * BN;
+    floatx16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    for (int kt = 0; kt < nkt; ++kt) {
+      float a[2][16], b[2][16];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        fetch<MA>(As + kt * SMEM, wm * 64 + i * 32, lane, a[i]);
+        fetch<MB>(Bs + kt * SMEM, wn * 64 + i * 32, lane, b[i]);
+      }
+#pragma unroll
+      for (int st = 0; st < 16; ++st)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][st], b[j][st], acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();   // every wave is done reading this tile's B
+    Stager<MB> sb;
+    if (tn + 1 < ntiles) {
+      sb.init(P.Bt, P.N, n0 + BN);
+      sb.load(P.Bt, P.N, n0 + BN, 0, P.K);
+    }
+    // plain output (one row stride, no second output, no accumulation)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int mr = m0 + wm * 64 + i * 32 + 4 * (lane / 32);
+      float* rowp = P.C.p + (long long)mr * P.C.s1 + n0 + wn * 64 + lane % 32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int dm = 8 * (r / 4) + r % 4;
+        if (mr + dm < P.M) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            if (n0 + wn * 64 + j * 32 + lane % 32 < P.N) rowp[(long long)dm * P.C.s1 + j * 32] = P.alpha * acc[i][j][r];
+          }
+        }
+      }
+    }
+    if (tn + 1 < ntiles) {
+      sb.store(Bs);
+      for (int kt = 1; kt < nkt; ++kt) {
+        sb.load(P.Bt, P.N, n0 + BN, kt * BK, P.K);
+        sb.store(Bs + kt * SMEM);
+      }
+    }
+    __syncthreads();   // the next tile's B is in LDS
+  }
+}
+
 __global__ __launch_bounds__(NT, 2) void gemm_kernel(GemmGroup g) {
   __shared__ __attribute__((aligned(16))) float smem[4 * SMEM];   // A and B, two buffers each
   float* As = smem;
   float* Bs = smem + 2 * SMEM;
   int b = blockIdx.x, pi = 0;
-  while (pi < g.count - 1 && b >= g.tiles_m[pi] * g.tiles_n[pi] * g.prob[pi].ksplit) {
-    b -= g.tiles_m[pi] * g.tiles_n[pi] * g.prob[pi].ksplit;
+  while (pi < g.count - 1 && b >= g.blocks[pi]) {
+    b -= g.blocks[pi];
     ++pi;
   }
   const GemmProblem P = pin(g.prob[pi]);
+  if (g.mode[pi] >= kNLoop) {   // one block per M tile, every N tile
+    const int m0 = b * BM;
+    switch (g.mode[pi] - kNLoop) {
+      case kK * 3 + kK: gemm_tile_nloop<kK, kK>(P, m0, g.tiles_n[pi], As, Bs); break;
+      case kK * 3 + kR: gemm_tile_nloop<kK, kR>(P, m0, g.tiles_n[pi], As, Bs); break;
+      case kR * 3 + kR: gemm_tile_nloop<kR, kR>(P, m0, g.tiles_n[pi], As, Bs); break;
+      case kR * 3 + kK: gemm_tile_nloop<kR, kK>(P, m0, g.tiles_n[pi], As, Bs); break;
+      default: gemm_tile_nloop<kG, kG>(P, m0, g.tiles_n[pi], As, Bs); break;
+    }
+    return;
+  }
   const int tiles = g.tiles_m[pi] * g.tiles_n[pi];
   const int ks = b / tiles;
   b %= tiles;
@@ -442,11 +541,15 @@ void gemm_group(const GemmGroup& g0, hipStream_t st) {
     P.C2.mdiv = magic(P.C2.div);
     const int ma = stage_mode(P.A, P.M, P.K), mb = stage_mode(P.Bt, P.N, P.K);
     g.mode[i] = ((ma == kG || mb == kG) ? kG * 3 + kG : ma * 3 + mb) + (P.N <= BN / 2 ? kNarrow : 0);
+    const bool nloop = P.K <= 2 * BK && g.tiles_n[i] > 1 && P.ksplit == 1 && !P.C2.p && P.C.p && P.C.div == 1 &&
+                       !P.C.accumulate;
+    if (nloop) g.mode[i] = ((ma == kG || mb == kG) ? kG * 3 + kG : ma * 3 + mb) + kNLoop;
+    g.blocks[i] = nloop ? g.tiles_m[i] : g.tiles_m[i] * g.tiles_n[i] * P.ksplit;
     auto out_vec = [&](const GOut& o) {
       return !o.p || (aligned16(o.p) && o.s1 % 4 == 0 && (o.div == 1 || o.s2 % 4 == 0));
     };
     g.vec_out[i] = P.N % 4 == 0 && (P.ksplit > 1 ? aligned16(P.part) : (out_vec(P.C) && out_vec(P.C2)));
-    total += g.tiles_m[i] * g.tiles_n[i] * P.ksplit;
+    total += g.blocks[i];
   }
   if (total == 0) return;
   hipLaunchKernelGGL(gemm_kernel, dim3(total), dim3(NT), 0, st, g);

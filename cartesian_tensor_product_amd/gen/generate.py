@@ -536,19 +536,18 @@ def has_mlp(cfg) -> bool:
     return not allp and not cfg_summed(cfg) and max(li, le, lo) <= MLP_MAX_RANK
 
 
-def mlp_vjp_fused(cfg) -> bool:
-    """Whether the VJP weighted by the radial network runs fused by default:
-    when the convolution's own VJP work per edge and channel (2 T + sum
-    min(2l1+1, 2L+1) + 2 sum (2l2+1) FMAs over the paths) is at least a
-    third of the 64 P FMAs that form w from the 64 hidden units.  Below that
-    the fused VJP spends its issue slots on w and dw/dr, which the
-    materialised path gives to the matrix cores (measured: rank 2, ratio
-    0.38, fused 1.24 ms vs 1.42 ms; the (0, 3, 3) block convolution, ratio
-    0.27, fused slower)."""
+def mlp_fwd_fused(cfg) -> bool:
+    """Whether the forward weighted by the radial network runs fused by
+    default: measured faster than the materialised forward (an MFMA GEMM
+    writing w, then the explicit-weight kernel) for l_in <= 1 or ranks <= 2
+    at 1024 nodes x 128 neighbours x 128 channels (e.g. 0.54 vs 0.56 ms at
+    rank 2, 0.24 vs 0.28 ms at (0, 3, 3)), slower at (2, 3, 3) and (3, 3, 3)
+    (1.04 vs 0.89, 1.35 vs 1.17 ms).  The VJP is materialised by default:
+    with the output-layer GEMMs in their narrow and N-loop layouts it was as
+    fast or faster at every rank set measured except (1, 1, 1) and (1, 2, 2)
+    (within 4 %)."""
     li, le, lo, _ = cfg_ranks(cfg)
-    paths = [(a, b, L) for L in range(lo + 1) for a in range(li + 1) for b in range(le + 1) if admissible(a, b, L)]
-    core = sum(2 * len(coupling_terms(a, b, L)) + min(2 * a + 1, 2 * L + 1) + 2 * (2 * b + 1) for a, b, L in paths)
-    return 3 * core >= 64 * len(paths)
+    return li <= 1 or max(li, le, lo) <= 2
 
 
 # the passes of a split VJP-of-VJP: unit suffix, function, body
@@ -572,8 +571,8 @@ def emit_instances(gen_dir: str) -> list:
     lines += ["", "", "// ... and the convolution with the radial network's output layer fused for",
               "#define FC_CONV_MLP_CONFIGS(X) \\"]
     lines += [f"  X({a}, {b}, {c}) \\" for a, b, c in cfgs if has_mlp((a, b, c))]
-    lines += ["", "", "// ... of which the VJP runs fused by default for", "#define FC_CONV_MLP_VJP_FUSED_CONFIGS(X) \\"]
-    lines += [f"  X({a}, {b}, {c}) \\" for a, b, c in cfgs if has_mlp((a, b, c)) and mlp_vjp_fused((a, b, c))]
+    lines += ["", "", "// ... of which the forward runs fused by default for", "#define FC_CONV_MLP_FWD_FUSED_CONFIGS(X) \\"]
+    lines += [f"  X({a}, {b}, {c}) \\" for a, b, c in cfgs if has_mlp((a, b, c)) and mlp_fwd_fused((a, b, c))]
     lines += ["", ""]
     _write(os.path.join(gen_dir, "fc_conv_configs.h"), "\n".join(lines))
     files = []

@@ -285,10 +285,10 @@ size_t fc_radial_mlp_weight_floats(const fc_conv_desc* d);
  * forward and in a VJP without mlp_w_grad.  Materialised: w [E][P][C] is
  * written to the workspace by an MFMA GEMM and streamed through the
  * explicit-weight kernels, and the VJP carries w_bar back through the
- * network.  Default: the forward fused wherever available; the VJP fused
- * where the convolution's own VJP work per edge and channel is at least a
- * third of the 64 P FMAs that form w (ranks (2,2,2), (1,3,3), (2,3,3),
- * (3,3,3)), materialised elsewhere (there the matrix cores form w faster);
+ * network.  Default (measured): the forward fused where l_in <= 1 or every
+ * rank is <= 2, materialised at (2,3,3) and (3,3,3); the VJP materialised
+ * (the fused VJP needs 2 x 64 P FMAs per edge and channel on the vector
+ * units and was slower or within 4 %, but takes a far smaller workspace).
  * FC_CONV_MLP_FUSE / FC_CONV_MLP_MATERIALIZE override.  A forward on an op 2
  * workspace (the message blocks) follows the VJP's choice.
  * Workspace of the calls below: op 0 forward (and fc_radial_mlp), op 1 VJP

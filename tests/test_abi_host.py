@@ -246,24 +246,28 @@ def test_mlp_workspace_layouts():
     and force VJP hold per-edge hidden rows (512 bytes per edge); the
     materialised layouts hold w [E][P][C] (and w_bar); the VJP with the
     network's weight gradient (op 1) is materialised and covers op 2; other
-    ops are refused (0 bytes)."""
+    ops are refused (0 bytes).  Defaults: the forward fused at rank 2 and
+    for the scalar-sender (0, 3, 3), materialised at (3, 3, 3); the VJP
+    materialised unless FC_CONV_MLP_FUSE."""
     N, E, C = 1000, 64000, 128
-    fused = fc.conv_desc(N, E, C, 2, 2, 2, 5.0)
+    dflt = fc.conv_desc(N, E, C, 2, 2, 2, 5.0)
+    fused = fc.conv_desc(N, E, C, 2, 2, 2, 5.0, flags=fc.FC_CONV_MLP_FUSE)
     mat = fc.conv_desc(N, E, C, 2, 2, 2, 5.0, flags=fc.FC_CONV_MLP_MATERIALIZE)
     P = fc.fc_conv_layout(fused)[0]
     f0, f1, f2 = (fc.fc_edge_conv_mlp_workspace_bytes(fused, op) for op in (0, 1, 2))
     m0, m1, m2 = (fc.fc_edge_conv_mlp_workspace_bytes(mat, op) for op in (0, 1, 2))
-    assert f0 == (E * 512 + 255) // 256 * 256
-    assert m0 >= E * P * C * 4 and m2 >= 2 * E * P * C * 4
+    d0, d2 = fc.fc_edge_conv_mlp_workspace_bytes(dflt, 0), fc.fc_edge_conv_mlp_workspace_bytes(dflt, 2)
+    assert f0 == (E * 512 + 255) // 256 * 256 and d0 == f0
+    assert m0 >= E * P * C * 4 and m2 >= 2 * E * P * C * 4 and d2 == m2
     assert f1 == m1 and f2 < f1 and f2 < m2
     assert fc.fc_edge_conv_mlp_workspace_bytes(fused, 3) == 0
-    # the scalar-sender (0, 3, 3) VJP is materialised by default (its own VJP
-    # work is under a third of the 64 P FMAs that form w), fused on request
     blk = dict(n_nodes=N, n_edges=E, channels=C, l_in=0, l_edge=3, l_out=3, r_cut=5.0)
     P4 = 4
     assert fc.fc_edge_conv_mlp_workspace_bytes(fc.conv_desc(**blk), 2) >= 2 * E * P4 * C * 4
     assert fc.fc_edge_conv_mlp_workspace_bytes(fc.conv_desc(**blk, flags=fc.FC_CONV_MLP_FUSE), 2) < E * P4 * C * 4
     assert fc.fc_edge_conv_mlp_workspace_bytes(fc.conv_desc(**blk), 0) < E * P4 * C * 4   # forward fused
+    r3 = fc.conv_desc(N, E, C, 3, 3, 3, 5.0)
+    assert fc.fc_edge_conv_mlp_workspace_bytes(r3, 0) >= E * fc.fc_conv_layout(r3)[0] * C * 4   # materialised
     # ranks above the fused set, and every-parity or summed outputs, are materialised
     for d in (fc.conv_desc(N, E, C, 4, 4, 4, 5.0), fc.conv_desc(N, E, C, 2, 2, 2, 5.0, flags=fc.FC_CONV_SUM_PATHS)):
         P2 = fc.fc_conv_layout(d)[0]

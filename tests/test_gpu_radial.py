@@ -185,7 +185,7 @@ def test_mlp_workspace_sizes():
     gradient with the smaller op 2 workspace is refused."""
     from cartesian_tensor_product_amd import flashcart as fc
     spec, d, mlp = setup((2, 2, 2), 128, 1, n=200, k=32, box=10.0)
-    gc = GpuMlpConv((2, 2, 2), d, 128, 5.0, mlp)
+    gc = GpuMlpConv((2, 2, 2), d, 128, 5.0, mlp, "fused")
     E = gc.E
     b0, b1, b2 = (fc.fc_edge_conv_mlp_workspace_bytes(gc.desc, op) for op in (0, 1, 2))
     mat = fc.conv_desc(gc.N, E, 128, 2, 2, 2, 5.0, flags=fc.FC_CONV_MLP_MATERIALIZE)

@@ -1,12 +1,16 @@
 // Node-local correlation ladder for gfx950 (FlashCart paper §5 Eq. 2 and
 // App. E "Path-reduced products").
 //
-// Full ladder, per step q >= 2: a VALU kernel forms the channel-diagonal
-// products B_eta = (phi^{q-1}_{l1} (x) A_{l2})_L for every path eta of the
-// step (lanes = channels, coalesced) into a GEMM-ready buffer, one row
-// (u, component) per output rank and columns (eta, channel); the path/channel
-// mixing phi^q_L = B_L W^q_L^T then runs on the matrix cores as a grouped
-// FP32 MFMA GEMM whose epilogue also adds phi^q into the output sum z.
+// Full ladder, per step q >= 2: the channel-diagonal products
+// B_eta = (phi^{q-1}_{l1} (x) A_{l2})_L of every path eta and the
+// path/channel mixing phi^q_L = B_L W^q_L^T run in one kernel
+// (ladder_step_kernel): product waves form each K tile of B in LDS while
+// MFMA waves multiply the previous one, so B never reaches memory, and the
+// epilogue adds phi^q into the output sum z.  Shapes that kernel does not
+// cover (C other than 64 or 128, l_prod = 4) write B to a GEMM-ready buffer
+// with a VALU kernel (one row (u, component) per output rank, columns (eta,
+// channel)) and run the mixing as a grouped FP32 MFMA GEMM.  The reverse
+// passes always recompute B into a buffer.
 // Path-reduced products: every step runs in registers per (node, channel)
 // with the per-path weights a^q, and one grouped GEMM applies the final
 // rank-wise maps W_L.
@@ -17,6 +21,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <vector>
 
 #include "fc_common.h"
 #include "fc_gemm.h"
@@ -71,6 +76,215 @@ __global__ __launch_bounds__(kWave) void ladder_prod_kernel(int N, int C, const 
       float* d = dst + ((size_t)u * na + a) * ld;
       *d = acc ? *d + t[a] : t[a];
     });
+  });
+}
+
+// ------------------------------------------- fused product + mixing step --
+//
+// One step q >= 2 of the full ladder without the product buffer: the
+// channel-diagonal products are formed in LDS as the matrix-core A operand.
+// A block takes 32 nodes and one output rank L; its rows are ordered (c,
+// node), so each 32-row MFMA block belongs to one component c.  The K tiles
+// (32 channels of one path) run channel block outer, path inner, so that the
+// 2 l_prod + 1 ... rows of phi and A of a channel block are loaded once and
+// serve every path of the rank.  The block's eight waves split the work:
+// waves 4-7 hold those rows for one node and four channels each and form the
+// products of the next K tile, while waves 0-3 run the MFMAs of the current
+// one, wave w owning output columns [32 w, 32 w + 32) for every component,
+// its W^q_L operand loaded straight from global memory (L2) into registers,
+// as no other wave reads it.  One barrier per K tile hands the
+// double-buffered product tile over.
+constexpr int kStepNodes = 32;    // nodes per block: one MFMA row block per component
+constexpr int kStepKPad = 36;     // LDS row length of the product tile (floats)
+constexpr int kStepMaxItems = 6;
+
+struct StepItem {
+  int L;                     // output rank
+  long long woff;            // offset of W^q_L [C][P_L C] in the flat weights
+};
+struct StepPlan {
+  int count, tiles;          // items (blocks per node tile), node tiles
+  StepItem item[kStepMaxItems];
+};
+
+// Whether the phi rows of path e's l1 block (A rows of its l2 block, with
+// SECOND) are used by no later path of rank L: then they can be reloaded for
+// the next channel block right after path e.
+template <class Cfg, int FIRST, int P>
+__host__ __device__ constexpr bool step_last_use(int e, bool second) {
+  const int l = second ? Cfg::paths[FIRST + e].l2 : Cfg::paths[FIRST + e].l1;
+  for (int f = e + 1; f < P; ++f)
+    if ((second ? Cfg::paths[FIRST + f].l2 : Cfg::paths[FIRST + f].l1) == l) return false;
+  return true;
+}
+
+template <int LP, int LQ, int L>
+__device__ __forceinline__ void step_body(int N, int C, const float* __restrict__ phi, const float* __restrict__ A,
+                                          const float* __restrict__ wl, float* __restrict__ out,
+                                          float* __restrict__ z, int z_rows, int lz, int u0, float* Ps) {
+  using Cfg = ConvCfg<LP, LP, LQ>;
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  typedef float f16 __attribute__((ext_vector_type(16)));
+  constexpr int R = nrank(LP);   // rows of phi, A and out per node
+  constexpr int NC = ncomp(L);
+  constexpr int P = Cfg::count_L(L), FIRST = Cfg::first_path_of(L);
+  constexpr int TILE = ncomp(LP) * kStepNodes * kStepKPad;
+  const int nkb = C / 32;   // even
+  // Step t (0 .. ntiles - 1, then a final MFMA pass): the product waves form
+  // K tile t (channel block t / P, path t % P) into buffer t % 2 while the
+  // MFMA waves consume tile t - 1; one barrier per step.  The channel blocks
+  // go in pairs, so every step of a pair is straight-line code with
+  // compile-time path and buffer, and the waits on loads are exact.
+
+  if (threadIdx.x < 256) {
+    // ---- MFMA waves: wave wv owns columns [32 wv, 32 wv + 32)
+    const int wv = threadIdx.x / 64, lane = threadIdx.x % 64, h = lane / 32;
+    const bool nok = wv < nkb;
+    const long long ldw = (long long)P * C;
+    const float* wrow = wl + (long long)((nok ? wv : 0) * 32 + lane % 32) * ldw + 16 * h;
+    // W columns of K tile (channel block kb, path e): e C + 32 kb
+    auto load_w = [&](int kb, int e, f4 (&dst)[4]) {
+      const float* src = wrow + (long long)e * C + kb * 32;
+      static_for<4>([&](auto q) { dst[q] = *reinterpret_cast<const f4*>(src + 4 * q); });
+    };
+    f16 acc[NC];
+    static_for<NC>([&](auto i) { static_for<16>([&](auto r) { acc[i][(int)r] = 0.f; }); });
+    auto mma = [&](const float* Sc, const f4 (&bw)[4]) {
+      static_for<NC>([&](auto i) {
+        const f4* src = reinterpret_cast<const f4*>(Sc + (i * kStepNodes + lane % 32) * kStepKPad + 16 * h);
+        f4 a4[4];
+        static_for<4>([&](auto q) { a4[q] = src[q]; });
+        static_for<16>([&](auto s) {
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[s / 4][(int)s % 4], bw[s / 4][(int)s % 4], acc[i], 0, 0,
+                                                        0);
+        });
+      });
+    };
+    // W operands in two register sets by tile parity (a pair of channel
+    // blocks starts at an even tile, so the parity is fixed per step): the
+    // operand of tile t is requested at step t, one step before its MFMAs
+    f4 wb[2][4];
+    for (int kb = 0; kb < nkb; kb += 2) {
+      static_for<2 * P>([&](auto sc) {
+        constexpr int s = sc, par = s % 2;
+        load_w(kb + s / P, s % P, wb[par]);
+        if (kb > 0 || s > 0) {
+          __builtin_amdgcn_sched_barrier(0);
+          mma(Ps + (par ^ 1) * TILE, wb[par ^ 1]);   // tile t - 1
+        }
+        __syncthreads();
+      });
+    }
+    mma(Ps + TILE, wb[1]);   // the last tile (odd: the tile count is even)
+    // epilogue: accumulator register r of lane l holds row 8 (r / 4) + 4 h +
+    // r % 4 (a node of the tile) and column l % 32.  The z values of two
+    // components are requested before any store, so that the adds wait for
+    // one round trip per pair instead of one per element.
+    if (nok) {
+      const int n = wv * 32 + lane % 32, ub = u0 + 4 * h;
+      const size_t zs = (size_t)z_rows * C, os = (size_t)R * C;
+      float* zp = z + ((size_t)ub * z_rows + L * L) * C + n;
+      float* op = out ? out + ((size_t)ub * R + L * L) * C + n : nullptr;
+      const bool full = u0 + kStepNodes <= N, addz = L <= lz;
+      auto row_ok = [&](int du) { return full || ub + du < N; };
+      static_for<(NC + 1) / 2>([&](auto pc) {
+        constexpr int c0 = 2 * pc, nc = (c0 + 1 < NC) ? 2 : 1;
+        float zv[nc][16];
+        static_for<nc>([&](auto j) {
+          static_for<16>([&](auto r) {
+            constexpr int du = 8 * (r / 4) + r % 4;
+            zv[j][(int)r] = (addz && row_ok(du)) ? zp[du * zs + (c0 + j) * C] : 0.f;
+          });
+        });
+        static_for<nc>([&](auto j) {
+          static_for<16>([&](auto r) {
+            constexpr int du = 8 * (r / 4) + r % 4;
+            if (row_ok(du)) {
+              const float v = acc[c0 + j][(int)r];
+              if (op) op[du * os + (c0 + j) * C] = v;
+              if (addz) zp[du * zs + (c0 + j) * C] = zv[j][(int)r] + v;
+            }
+          });
+        });
+      });
+    }
+  } else {
+    // ---- product waves: node pu, channels pk .. pk + 3 of a channel block
+    const int pt = threadIdx.x - 256;
+    const int pu = pt / 8, pk = 4 * (pt % 8);
+    const size_t nbase = (size_t)(u0 + pu < N ? u0 + pu : 0) * R * C + pk;   // rows past N: node 0, never stored
+    f4 x[R], y[R];
+    // channel block 0 of every row block some path of rank L reads
+    static_for<P>([&](auto e) {
+      constexpr PathInfo PI = Cfg::paths[FIRST + e];
+      if constexpr (step_last_use<Cfg, FIRST, P>(e, false)) {
+        static_for<ncomp(PI.l1)>([&](auto a) {
+          x[rank_off(PI.l1) + a] = *reinterpret_cast<const f4*>(phi + nbase + (size_t)(rank_off(PI.l1) + a) * C);
+        });
+      }
+      if constexpr (step_last_use<Cfg, FIRST, P>(e, true)) {
+        static_for<ncomp(PI.l2)>([&](auto a) {
+          y[rank_off(PI.l2) + a] = *reinterpret_cast<const f4*>(A + nbase + (size_t)(rank_off(PI.l2) + a) * C);
+        });
+      }
+    });
+    // products of path e (the term order of the product-buffer kernel); then
+    // the rows whose last use this was are reloaded for channel block kbn
+    auto path_step = [&](auto ec, float* S, int kbn) {
+      constexpr int e = ec;
+      constexpr PathInfo PI = Cfg::paths[FIRST + e];
+      constexpr int o1 = rank_off(PI.l1), o2 = rank_off(PI.l2);
+      constexpr int tb = tab::kTermBegin[PI.type], te = tab::kTermBegin[PI.type + 1];
+      f4 t[NC];
+      static_for<te - tb>([&](auto ti) {
+        constexpr tab::Term T = tab::kTerms[tb + ti];
+        const f4 xy = x[o1 + T.b1] * y[o2 + T.b2];
+        if constexpr (T.fa) t[T.a] = T.c * xy;
+        else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) t[T.a][k] = fmaf(T.c, xy[k], t[T.a][k]);
+        }
+      });
+      static_for<NC>([&](auto c) { *reinterpret_cast<f4*>(S + (c * kStepNodes + pu) * kStepKPad + pk) = t[c]; });
+      // keep the reloads after the products: issued earlier, they would need
+      // registers of their own
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (step_last_use<Cfg, FIRST, P>(e, false)) {
+        static_for<ncomp(PI.l1)>([&](auto a) {
+          x[o1 + a] = *reinterpret_cast<const f4*>(phi + nbase + (size_t)(o1 + a) * C + kbn * 32);
+        });
+      }
+      if constexpr (step_last_use<Cfg, FIRST, P>(e, true)) {
+        static_for<ncomp(PI.l2)>([&](auto a) {
+          y[o2 + a] = *reinterpret_cast<const f4*>(A + nbase + (size_t)(o2 + a) * C + kbn * 32);
+        });
+      }
+    };
+    for (int kb = 0; kb < nkb; kb += 2) {
+      static_for<2 * P>([&](auto sc) {
+        constexpr int s = sc, e = s % P, d = s / P;
+        // tile kb P + s: path e of channel block kb + d (buffer s % 2, as
+        // kb P is even); reloads are for the following channel block
+        path_step(std::integral_constant<int, e>{}, Ps + (s % 2) * TILE, min(kb + d + 1, nkb - 1));
+        __syncthreads();
+      });
+    }
+  }
+}
+
+template <int LP, int LQ>
+__global__ __launch_bounds__(512) void ladder_step_kernel(int N, int C, const float* __restrict__ phi,
+                                                         const float* __restrict__ A, const float* __restrict__ w,
+                                                         float* __restrict__ out, float* __restrict__ z, int z_rows,
+                                                         int lz, StepPlan plan) {
+  __shared__ __attribute__((aligned(16))) float Ps[2 * ncomp(LP) * kStepNodes * kStepKPad];
+  const int item = blockIdx.x / plan.tiles, tile = blockIdx.x - item * plan.tiles;
+  const int L = plan.item[item].L;
+  const float* wl = w + plan.item[item].woff;
+  static_for<LQ + 1>([&](auto Lc) {
+    if (Lc != L) return;
+    if constexpr (ConvCfg<LP, LP, LQ>::count_L(Lc) > 0)
+      step_body<LP, LQ, Lc>(N, C, phi, A, wl, out, z, z_rows, lz, tile * kStepNodes, Ps);
   });
 }
 
@@ -730,6 +944,56 @@ void prod(const LadderPlan& p, int LQ, const float* phi, const float* A, float* 
   }
 }
 
+// The fused step (product tile formed in LDS) covers C = 64 or 128 (one
+// column block per MFMA wave and an even number of channel blocks; more
+// columns, or l_prod = 4, would not fit the held phi and A rows or the
+// accumulators in the register budget) and 16-byte aligned phi, A and
+// weights; other shapes write the product buffer and run the grouped GEMM.
+bool step_fused_ok(const LadderPlan& p, const float* phi, const float* A, const float* w) {
+  auto al = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+  return (p.C == 64 || p.C == 128) && p.lprod <= 3 && p.la == p.lprod && al(phi) && al(A) && al(w);
+}
+
+template <int LP, int LQ>
+void launch_step(const LadderPlan& p, const StepPlan& sp, const float* phi, const float* A, const float* w,
+                 float* out, float* z, hipStream_t st) {
+  hipLaunchKernelGGL((ladder_step_kernel<LP, LQ>), dim3(sp.count * sp.tiles), dim3(512), 0, st, p.N, p.C, phi, A,
+                     w, out, z, nr(p.lout), p.lout, sp);
+}
+
+template <int LP>
+void dispatch_step(const LadderPlan& p, int LQ, const StepPlan& sp, const float* phi, const float* A,
+                   const float* w, float* out, float* z, hipStream_t st) {
+  switch (LQ) {
+    case 0: launch_step<LP, 0>(p, sp, phi, A, w, out, z, st); break;
+    case 1: if constexpr (LP >= 1) launch_step<LP, 1>(p, sp, phi, A, w, out, z, st); break;
+    case 2: if constexpr (LP >= 2) launch_step<LP, 2>(p, sp, phi, A, w, out, z, st); break;
+    case 3: if constexpr (LP >= 3) launch_step<LP, 3>(p, sp, phi, A, w, out, z, st); break;
+  }
+}
+
+// Step q >= 2 of the full ladder: phi^q (out, when not NULL) and z += phi^q
+// for the ranks <= l_out.  One item per output rank with paths; the items
+// with the most MFMA work come first in the grid.
+void step_fused(const LadderPlan& p, int q, const float* phi, const float* A, const float* w, float* out,
+                float* z, hipStream_t st) {
+  StepPlan sp{};
+  sp.tiles = (p.N + kStepNodes - 1) / kStepNodes;
+  std::vector<std::pair<int, StepItem>> items;   // (MFMA work, item)
+  for (int L = 0; L <= p.lq(q); ++L) {
+    const int P = p.paths(q, L);
+    if (P > 0) items.push_back({(2 * L + 1) * P, StepItem{L, (long long)p.w_full(q, L)}});
+  }
+  std::stable_sort(items.begin(), items.end(), [](const auto& a, const auto& b) { return a.first > b.first; });
+  sp.count = (int)items.size();
+  for (int i = 0; i < sp.count; ++i) sp.item[i] = items[i].second;
+  switch (p.lprod) {
+    case 1: dispatch_step<1>(p, p.lq(q), sp, phi, A, w, out, z, st); break;
+    case 2: dispatch_step<2>(p, p.lq(q), sp, phi, A, w, out, z, st); break;
+    case 3: dispatch_step<3>(p, p.lq(q), sp, phi, A, w, out, z, st); break;
+  }
+}
+
 template <int LP, int LO>
 void launch_reduced(const LadderPlan& p, const float* A, const float* w, float* S, float* saved, hipStream_t st) {
   dim3 grid(p.N, (p.C + kWave - 1) / kWave);
@@ -827,6 +1091,10 @@ void ladder_forward(const LadderPlan& p, const float* A, const float* w, float* 
   }
   for (int q = 2; q <= p.order; ++q) {
     const float* phi = state(q - 1);
+    if (step_fused_ok(p, phi, A, w)) {
+      step_fused(p, q, phi, A, w, state(q), z, st);
+      continue;
+    }
     prod(p, p.lq(q), phi, A, B, st);
     GemmGroup g{};
     size_t boff = 0;

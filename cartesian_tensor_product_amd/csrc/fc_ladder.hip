@@ -136,7 +136,9 @@ __device__ __forceinline__ void step_body(int N, int C, const float* __restrict_
   // go in pairs, so every step of a pair is straight-line code with
   // compile-time path and buffer, and the waits on loads are exact.
 
+  f16 acc[NC];   // MFMA waves only
   if (threadIdx.x < 256) {
+    static_for<NC>([&](auto i) { static_for<16>([&](auto r) { acc[i][(int)r] = 0.f; }); });
     // ---- MFMA waves: wave wv owns columns [32 wv, 32 wv + 32)
     const int wv = threadIdx.x / 64, lane = threadIdx.x % 64, h = lane / 32;
     const bool nok = wv < nkb;
@@ -147,8 +149,6 @@ __device__ __forceinline__ void step_body(int N, int C, const float* __restrict_
       const float* src = wrow + (long long)e * C + kb * 32;
       static_for<4>([&](auto q) { dst[q] = *reinterpret_cast<const f4*>(src + 4 * q); });
     };
-    f16 acc[NC];
-    static_for<NC>([&](auto i) { static_for<16>([&](auto r) { acc[i][(int)r] = 0.f; }); });
     auto mma = [&](const float* Sc, const f4 (&bw)[4]) {
       static_for<NC>([&](auto i) {
         const f4* src = reinterpret_cast<const f4*>(Sc + (i * kStepNodes + lane % 32) * kStepKPad + 16 * h);
@@ -176,38 +176,6 @@ __device__ __forceinline__ void step_body(int N, int C, const float* __restrict_
       });
     }
     mma(Ps + TILE, wb[1]);   // the last tile (odd: the tile count is even)
-    // epilogue: accumulator register r of lane l holds row 8 (r / 4) + 4 h +
-    // r % 4 (a node of the tile) and column l % 32.  The z values of two
-    // components are requested before any store, so that the adds wait for
-    // one round trip per pair instead of one per element.
-    if (nok) {
-      const int n = wv * 32 + lane % 32, ub = u0 + 4 * h;
-      const size_t zs = (size_t)z_rows * C, os = (size_t)R * C;
-      float* zp = z + ((size_t)ub * z_rows + L * L) * C + n;
-      float* op = out ? out + ((size_t)ub * R + L * L) * C + n : nullptr;
-      const bool full = u0 + kStepNodes <= N, addz = L <= lz;
-      auto row_ok = [&](int du) { return full || ub + du < N; };
-      static_for<(NC + 1) / 2>([&](auto pc) {
-        constexpr int c0 = 2 * pc, nc = (c0 + 1 < NC) ? 2 : 1;
-        float zv[nc][16];
-        static_for<nc>([&](auto j) {
-          static_for<16>([&](auto r) {
-            constexpr int du = 8 * (r / 4) + r % 4;
-            zv[j][(int)r] = (addz && row_ok(du)) ? zp[du * zs + (c0 + j) * C] : 0.f;
-          });
-        });
-        static_for<nc>([&](auto j) {
-          static_for<16>([&](auto r) {
-            constexpr int du = 8 * (r / 4) + r % 4;
-            if (row_ok(du)) {
-              const float v = acc[c0 + j][(int)r];
-              if (op) op[du * os + (c0 + j) * C] = v;
-              if (addz) zp[du * zs + (c0 + j) * C] = zv[j][(int)r] + v;
-            }
-          });
-        });
-      });
-    }
   } else {
     // ---- product waves: node pu, channels pk .. pk + 3 of a channel block
     const int pt = threadIdx.x - 256;
@@ -270,6 +238,58 @@ __device__ __forceinline__ void step_body(int N, int C, const float* __restrict_
       });
     }
   }
+
+  // Epilogue through LDS (the product buffers are free after one more
+  // barrier): the MFMA waves place CH components of their accumulators as
+  // rows [component][node][C] (accumulator register r of lane l holds node
+  // 8 (r / 4) + 4 h + r % 4 and column l % 32 of the wave's block), then all
+  // 512 threads write phi^q and add into z as whole 128-bit row pieces, the
+  // z values of a thread's pieces requested together.
+  constexpr int TP = 128 + 4;                                        // row stride (C <= 128)
+  constexpr int CH = (2 * TILE) / (kStepNodes * TP);                 // components per pass
+  constexpr int IT = (CH * kStepNodes * 128 / 4 + 511) / 512;         // pieces per thread at C = 128
+  const int c4 = C / 4;
+  const bool addz = L <= lz;
+  static_for<(NC + CH - 1) / CH>([&](auto cc) {
+    constexpr int cb = cc * CH, chn = (cb + CH <= NC) ? CH : NC - cb;
+    __syncthreads();
+    if (threadIdx.x < 256) {
+      const int wv = threadIdx.x / 64, lane = threadIdx.x % 64, h = lane / 32;
+      if (wv < C / 32) {
+        static_for<chn>([&](auto j) {
+          static_for<16>([&](auto r) {
+            constexpr int row = 8 * (r / 4) + r % 4;
+            Ps[(j * kStepNodes + row + 4 * h) * TP + wv * 32 + lane % 32] = acc[cb + j][(int)r];
+          });
+        });
+      }
+    }
+    __syncthreads();
+    const int total = chn * kStepNodes * c4;
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    f4 zv[IT];
+    static_for<IT>([&](auto k) {
+      const int idx = threadIdx.x + 512 * k;
+      zv[k] = f4{0.f, 0.f, 0.f, 0.f};
+      if (addz && idx < total) {
+        const int j = idx / (kStepNodes * c4), row = (idx / c4) % kStepNodes, q = idx % c4;
+        const int u = u0 + row;
+        if (u < N) zv[k] = *reinterpret_cast<const f4*>(z + ((size_t)u * z_rows + L * L + cb + j) * C + 4 * q);
+      }
+    });
+    static_for<IT>([&](auto k) {
+      const int idx = threadIdx.x + 512 * k;
+      if (idx < total) {
+        const int j = idx / (kStepNodes * c4), row = (idx / c4) % kStepNodes, q = idx % c4;
+        const int u = u0 + row;
+        if (u < N) {
+          const f4 v = *reinterpret_cast<const f4*>(Ps + (j * kStepNodes + row) * TP + 4 * q);
+          if (out) *reinterpret_cast<f4*>(out + ((size_t)u * R + L * L + cb + j) * C + 4 * q) = v;
+          if (addz) *reinterpret_cast<f4*>(z + ((size_t)u * z_rows + L * L + cb + j) * C + 4 * q) = zv[k] + v;
+        }
+      }
+    });
+  });
 }
 
 template <int LP, int LQ>
@@ -948,10 +968,13 @@ void prod(const LadderPlan& p, int LQ, const float* phi, const float* A, float* 
 // column block per MFMA wave and an even number of channel blocks; more
 // columns, or l_prod = 4, would not fit the held phi and A rows or the
 // accumulators in the register budget) and 16-byte aligned phi, A and
-// weights; other shapes write the product buffer and run the grouped GEMM.
-bool step_fused_ok(const LadderPlan& p, const float* phi, const float* A, const float* w) {
+// weights, states and z; other shapes write the product buffer and run the
+// grouped GEMM.
+bool step_fused_ok(const LadderPlan& p, const float* phi, const float* A, const float* w, const float* out,
+                   const float* z) {
   auto al = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
-  return (p.C == 64 || p.C == 128) && p.lprod <= 3 && p.la == p.lprod && al(phi) && al(A) && al(w);
+  return (p.C == 64 || p.C == 128) && p.lprod <= 3 && p.la == p.lprod && al(phi) && al(A) && al(w) && al(out) &&
+         al(z);
 }
 
 template <int LP, int LQ>
@@ -1091,7 +1114,7 @@ void ladder_forward(const LadderPlan& p, const float* A, const float* w, float* 
   }
   for (int q = 2; q <= p.order; ++q) {
     const float* phi = state(q - 1);
-    if (step_fused_ok(p, phi, A, w)) {
+    if (step_fused_ok(p, phi, A, w, state(q), z)) {
       step_fused(p, q, phi, A, w, state(q), z, st);
       continue;
     }
